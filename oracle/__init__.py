@@ -1,0 +1,155 @@
+"""fp64 CPU oracle for the gated delta rule -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The GPU library under ``linear_attention_token_gdn_amd``
+never imports it and shares no code with it.
+
+The arithmetic lives in ``gdn_oracle.c`` (plain token-by-token recurrence of
+Eq. (1) on the explainer page "論文解説: Qwen3.8-Next の設計", ta-paperlens.web.app,
+section "GDNの中身").  This module only builds that file with gcc, loads it
+with ctypes and marshals numpy arrays.
+
+Inputs are the stored values: fp32 arrays, or bf16 values widened exactly to
+fp32.  Outputs are fp64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB = os.path.join(_HERE, "libgdn_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile gdn_oracle.c into libgdn_oracle.so (gcc, OpenMP, no fast-math)."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
+           "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build(force=False)
+            lib = ctypes.CDLL(_LIB)
+            f32p = ctypes.POINTER(ctypes.c_float)
+            f64p = ctypes.POINTER(ctypes.c_double)
+            i64p = ctypes.POINTER(ctypes.c_int64)
+            lib.gdn_oracle_run.argtypes = [f32p, f32p, f32p, f32p, f32p, f64p,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_double, i64p, ctypes.c_int64,
+                                           f64p, f64p, ctypes.c_int]
+            lib.gdn_oracle_run.restype = ctypes.c_int
+            lib.gdn_oracle_decode_step.argtypes = [f32p, f32p, f32p, f32p, f32p, f64p,
+                                                   f64p, ctypes.c_int, ctypes.c_int,
+                                                   ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                   ctypes.c_double, ctypes.c_int]
+            lib.gdn_oracle_decode_step.restype = ctypes.c_int
+            lib.gdn_oracle_max_threads.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _f32(a, shape):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if a.shape != tuple(shape):
+        raise ValueError("expected shape %s, got %s" % (tuple(shape), a.shape))
+    return a
+
+
+def _ptr(a, ctype):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def max_threads() -> int:
+    return int(_load().gdn_oracle_max_threads())
+
+
+def run(q, k, v, beta, g, s0=None, scale=1.0, chains=None, nthreads=0,
+        want_state=True):
+    """Recurrence of Eq. (1) over all T tokens.
+
+    q, k: [B,T,Hk,dk]; v: [B,T,Hv,dv]; beta, g: [B,T,Hv] (g = log alpha);
+    s0: [B,Hv,dk,dv] (any float dtype, widened to fp64) or None.  ``chains`` lists chain ids b*Hv+hv (None = all).
+    Returns (o [n,T,dv] fp64, sT [n,dk,dv] fp64 or None), n = number of chains.
+    With chains=None the results are reshaped to o [B,T,Hv,dv] and sT [B,Hv,dk,dv].
+    """
+    lib = _load()
+    B, T, Hk, dk = np.shape(q)
+    Hv, dv = np.shape(v)[2], np.shape(v)[3]
+    q = _f32(q, (B, T, Hk, dk))
+    k = _f32(k, (B, T, Hk, dk))
+    v = _f32(v, (B, T, Hv, dv))
+    beta = _f32(beta, (B, T, Hv))
+    g = _f32(g, (B, T, Hv))
+    if s0 is not None:
+        s0 = np.ascontiguousarray(s0, dtype=np.float64)
+        if s0.shape != (B, Hv, dk, dv):
+            raise ValueError("s0 must have shape %s" % ((B, Hv, dk, dv),))
+    if chains is None:
+        n = B * Hv
+        ch = None
+    else:
+        ch = np.ascontiguousarray(np.asarray(chains, dtype=np.int64).ravel())
+        n = ch.size
+    o = np.empty((n, T, dv), dtype=np.float64)
+    sT = np.empty((n, dk, dv), dtype=np.float64) if want_state else None
+    rc = lib.gdn_oracle_run(_ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float),
+                            _ptr(v, ctypes.c_float), _ptr(beta, ctypes.c_float),
+                            _ptr(g, ctypes.c_float), _ptr(s0, ctypes.c_double),
+                            B, T, Hk, Hv, dk, dv, float(scale),
+                            _ptr(ch, ctypes.c_int64), n,
+                            _ptr(o, ctypes.c_double), _ptr(sT, ctypes.c_double),
+                            int(nthreads))
+    if rc != 0:
+        raise RuntimeError("gdn_oracle_run failed with code %d" % rc)
+    if chains is None:
+        o = o.reshape(B, Hv, T, dv).transpose(0, 2, 1, 3)
+        if sT is not None:
+            sT = sT.reshape(B, Hv, dk, dv)
+    return o, sT
+
+
+def decode_step(q, k, v, beta, g, state, scale=1.0, nthreads=0):
+    """One token of Eq. (1) applied in place to ``state`` (fp64 [B,Hv,dk,dv]).
+
+    q, k: [B,Hk,dk]; v: [B,Hv,dv]; beta, g: [B,Hv].  Returns o [B,Hv,dv] fp64.
+    """
+    lib = _load()
+    B, Hk, dk = np.shape(q)
+    Hv, dv = np.shape(v)[1], np.shape(v)[2]
+    if not (isinstance(state, np.ndarray) and state.dtype == np.float64
+            and state.flags.c_contiguous and state.shape == (B, Hv, dk, dv)):
+        raise ValueError("state must be a C-contiguous float64 array [B,Hv,dk,dv]")
+    q = _f32(q, (B, Hk, dk))
+    k = _f32(k, (B, Hk, dk))
+    v = _f32(v, (B, Hv, dv))
+    beta = _f32(beta, (B, Hv))
+    g = _f32(g, (B, Hv))
+    o = np.empty((B, Hv, dv), dtype=np.float64)
+    rc = lib.gdn_oracle_decode_step(_ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float),
+                                    _ptr(v, ctypes.c_float), _ptr(beta, ctypes.c_float),
+                                    _ptr(g, ctypes.c_float), _ptr(state, ctypes.c_double),
+                                    _ptr(o, ctypes.c_double), B, Hk, Hv, dk, dv,
+                                    float(scale), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("gdn_oracle_decode_step failed with code %d" % rc)
+    return o

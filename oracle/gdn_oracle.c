@@ -1,0 +1,210 @@
+/*
+ * gdn_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, fp64 CPU implementation of the gated delta rule.  It exists
+ * so that tests, the smoke check and the benchmark's CPU-baseline leg can
+ * check and time the GPU library against an independent definition.  The GPU
+ * product path never links, loads or calls anything in this directory, and
+ * this file includes nothing from the GPU library.
+ *
+ * What it computes (source: the explainer page "論文解説: Qwen3.8-Next の設計"
+ * on ta-paperlens.web.app, section "GDNの中身: 足すのではなく、消してから書く",
+ * Eq. (1) and the concept code that follows it):
+ *
+ *   each head keeps a matrix state S (dk x dv) mapping keys to values;
+ *   per token t:   S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
+ *                  o_t = scale * S_t^T q_t          (read after the update)
+ *
+ * Readings where the page leaves a step open (each one pinned by a test):
+ *   - S is dk x dv, stored row-major with dv contiguous; the read-out contracts
+ *     over dk (Eq. (1) writes k v^T, so rows are indexed by the key).
+ *   - alpha multiplies the whole product (Eq. (1)); the concept code's line
+ *     order, which takes the difference from the undecayed state, is not used.
+ *   - alpha is passed in log space: alpha_t = exp(g_t), evaluated here in fp64.
+ *   - q/k heads are shared by groups of G = Hv/Hk consecutive value heads:
+ *     value head hv reads q/k head hv / G.  beta and g are per value head.
+ *   - a NULL initial state means zeros; the output state is the state after
+ *     the last token.
+ *
+ * Arithmetic: every input value (fp32, or bf16 widened exactly to fp32 by the
+ * caller) is widened to double; sums run over the contracted index in
+ * ascending order; nothing is blocked, fused or reordered.  Build without
+ * -ffast-math and with -ffp-contract=off.
+ *
+ * Parity status: pinned by the CPU tests (closed forms for beta = 0 and
+ * beta = 1, orthonormal-key retrieval, exact rational brute force on tiny
+ * sizes, dense transition-matrix products, an independently derived chunked
+ * form, linearity, split/resume and GQA equivalence).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Apply one token of Eq. (1) to the state S (dk x dv, row-major) and write
+ * o = scale * S^T q for the updated state.  e and f are dv-long scratch. */
+static void gdn_oracle_token(double *S, const float *q, const float *k,
+                             const float *v, double alpha, double beta,
+                             double scale, int dk, int dv, double *e,
+                             double *f, double *o)
+{
+    /* e = S^T k : what the state currently stores under key k. */
+    for (int j = 0; j < dv; ++j)
+        e[j] = 0.0;
+    for (int i = 0; i < dk; ++i) {
+        const double ki = (double)k[i];
+        const double *row = S + (size_t)i * dv;
+        for (int j = 0; j < dv; ++j)
+            e[j] += ki * row[j];
+    }
+    /* S = alpha * (S - beta k e^T) + beta k v^T  ==  alpha (I - beta k k^T) S + beta k v^T */
+    for (int i = 0; i < dk; ++i) {
+        const double ki = (double)k[i];
+        double *row = S + (size_t)i * dv;
+        for (int j = 0; j < dv; ++j)
+            row[j] = alpha * (row[j] - beta * ki * e[j]) + beta * ki * (double)v[j];
+    }
+    /* o = scale * S^T q, read from the updated state. */
+    for (int j = 0; j < dv; ++j)
+        f[j] = 0.0;
+    for (int i = 0; i < dk; ++i) {
+        const double qi = (double)q[i];
+        const double *row = S + (size_t)i * dv;
+        for (int j = 0; j < dv; ++j)
+            f[j] += qi * row[j];
+    }
+    for (int j = 0; j < dv; ++j)
+        o[j] = scale * f[j];
+}
+
+static int gdn_oracle_dims_ok(int B, int T, int Hk, int Hv, int dk, int dv)
+{
+    if (B < 0 || T < 0 || Hk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0)
+        return 0;
+    if (Hv % Hk != 0)
+        return 0;
+    return 1;
+}
+
+/*
+ * Run the recurrence over T tokens for the chains listed in `chains`
+ * (chain id = b * Hv + hv; NULL means all B*Hv chains in order).
+ *
+ * Layouts (row-major, innermost last):
+ *   q, k  [B, T, Hk, dk]      v    [B, T, Hv, dv]
+ *   beta, g [B, T, Hv]        s0   [B, Hv, dk, dv] fp64, or NULL (zeros)
+ *   o     [n_chains, T, dv]   sT   [n_chains, dk, dv] or NULL (not written)
+ * Returns 0 on success, -1 on bad arguments, -2 on allocation failure.
+ */
+int gdn_oracle_run(const float *q, const float *k, const float *v,
+                   const float *beta, const float *g, const double *s0,
+                   int B, int T, int Hk, int Hv, int dk, int dv, double scale,
+                   const int64_t *chains, int64_t n_chains, double *o,
+                   double *sT, int nthreads)
+{
+    if (!gdn_oracle_dims_ok(B, T, Hk, Hv, dk, dv))
+        return -1;
+    if (chains == NULL)
+        n_chains = (int64_t)B * Hv;
+    if (n_chains < 0)
+        return -1;
+    if (T > 0 && (q == NULL || k == NULL || v == NULL || beta == NULL ||
+                  g == NULL || o == NULL))
+        return -1;
+    for (int64_t c = 0; chains != NULL && c < n_chains; ++c)
+        if (chains[c] < 0 || chains[c] >= (int64_t)B * Hv)
+            return -1;
+    const int G = Hv / Hk;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : failed)
+#endif
+    for (int64_t c = 0; c < n_chains; ++c) {
+        const int64_t id = chains ? chains[c] : c;
+        const int b = (int)(id / Hv), hv = (int)(id % Hv), hq = hv / G;
+        double *S = (double *)malloc(sizeof(double) * (size_t)dk * dv);
+        double *e = (double *)malloc(sizeof(double) * (size_t)dv);
+        double *f = (double *)malloc(sizeof(double) * (size_t)dv);
+        if (!S || !e || !f) {
+            free(S); free(e); free(f);
+            failed = 1;
+            continue;
+        }
+        const size_t ssz = (size_t)dk * dv;
+        if (s0) {
+            memcpy(S, s0 + ((size_t)b * Hv + hv) * ssz, sizeof(double) * ssz);
+        } else {
+            memset(S, 0, sizeof(double) * ssz);
+        }
+        for (int t = 0; t < T; ++t) {
+            const size_t bt = (size_t)b * T + t;
+            const float *qt = q + (bt * Hk + hq) * dk;
+            const float *kt = k + (bt * Hk + hq) * dk;
+            const float *vt = v + (bt * Hv + hv) * dv;
+            const double alpha = exp((double)g[bt * Hv + hv]);
+            const double bet = (double)beta[bt * Hv + hv];
+            double *ot = o + ((size_t)c * T + t) * dv;
+            gdn_oracle_token(S, qt, kt, vt, alpha, bet, scale, dk, dv, e, f, ot);
+        }
+        if (sT)
+            memcpy(sT + (size_t)c * ssz, S, sizeof(double) * ssz);
+        free(S); free(e); free(f);
+    }
+    return failed ? -2 : 0;
+}
+
+/*
+ * One decode step: apply one token of Eq. (1) to every state in place.
+ *   q, k [B, Hk, dk]   v [B, Hv, dv]   beta, g [B, Hv]
+ *   state [B, Hv, dk, dv] (fp64, updated in place)   o [B, Hv, dv]
+ */
+int gdn_oracle_decode_step(const float *q, const float *k, const float *v,
+                           const float *beta, const float *g, double *state,
+                           double *o, int B, int Hk, int Hv, int dk, int dv,
+                           double scale, int nthreads)
+{
+    if (!gdn_oracle_dims_ok(B, 1, Hk, Hv, dk, dv))
+        return -1;
+    if (B > 0 && (!q || !k || !v || !beta || !g || !state || !o))
+        return -1;
+    const int G = Hv / Hk;
+    const int64_t n = (int64_t)B * Hv;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(static) num_threads(nthreads) reduction(| : failed)
+#endif
+    for (int64_t id = 0; id < n; ++id) {
+        const int b = (int)(id / Hv), hv = (int)(id % Hv), hq = hv / G;
+        double *e = (double *)malloc(sizeof(double) * (size_t)dv);
+        double *f = (double *)malloc(sizeof(double) * (size_t)dv);
+        if (!e || !f) {
+            free(e); free(f);
+            failed = 1;
+            continue;
+        }
+        gdn_oracle_token(state + (size_t)id * dk * dv,
+                         q + ((size_t)b * Hk + hq) * dk,
+                         k + ((size_t)b * Hk + hq) * dk,
+                         v + (size_t)id * dv, exp((double)g[id]),
+                         (double)beta[id], scale, dk, dv, e, f,
+                         o + (size_t)id * dv);
+        free(e); free(f);
+    }
+    return failed ? -2 : 0;
+}
+
+int gdn_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

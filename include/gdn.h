@@ -1,0 +1,117 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet token-mixer library (libgdn.so).
+ *
+ * The operation (explainer page "論文解説: Qwen3.8-Next の設計", ta-paperlens.web.app,
+ * section "GDNの中身: 足すのではなく、消してから書く", Eq. (1)): every head keeps a
+ * matrix state S of dk x dv fp32 values that maps keys to values.  For each token t
+ *
+ *     S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t                      (read from the updated state)
+ *
+ * alpha_t in (0,1] is the decay gate that scales the whole memory, passed in log space
+ * as g_t = log(alpha_t) <= 0; beta_t in [0,1] is the write strength.  q and k are
+ * expected to be L2-normalised by the caller (the library does not renormalise).
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are dense, row-major (innermost index last), in device memory, and
+ *     16-byte aligned.  B = batch, T = tokens, Hk = q/k heads, Hv = value heads,
+ *     dk = key/query head size, dv = value head size.
+ *   - Grouped heads: Hv must be a multiple of Hk; value head hv reads q/k head
+ *     hv / (Hv/Hk) (groups of consecutive value heads share one q/k head).  beta and
+ *     g are per value head.
+ *   - The state layout is [B, Hv, dk, dv] fp32 (dv contiguous): S[b][hv][i][j] is the
+ *     entry for key coordinate i and value coordinate j.
+ *   - Ownership: the caller owns every buffer.  No call allocates device memory,
+ *     keeps state between calls, or synchronises the host; every call only enqueues
+ *     kernels on `stream` (a hipStream_t; NULL = the null stream) and returns.
+ *   - Errors: arguments are validated on the host before anything is enqueued; on an
+ *     error nothing is launched and no output is touched.  Faults inside a kernel
+ *     surface at the caller's next synchronisation of the stream.  NaN and Inf in the
+ *     inputs propagate; they are not checked.
+ *   - Results are deterministic: the same inputs, sizes and stream give bit-identical
+ *     outputs (no atomics are used).
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARG = 1, /* null required pointer, negative size, misalignment, Hv % Hk != 0,
+                                o aliasing an input, workspace too small */
+    GDN_ERR_UNSUPPORTED = 2, /* valid but not implemented: head sizes, chunk size or dtype pair */
+    GDN_ERR_HIP = 3          /* the HIP runtime refused a launch */
+} gdn_status_t;
+
+typedef enum gdn_dtype {
+    GDN_F32 = 0,
+    GDN_BF16 = 1
+} gdn_dtype_t;
+
+/* Returns GDN_ABI_VERSION of the built library. */
+int gdn_abi_version(void);
+
+/* Returns a static, human-readable name for a status code (never NULL). */
+const char *gdn_status_string(gdn_status_t status);
+
+/*
+ * Bytes of device workspace gdn_chunk_fwd needs for these sizes (0 means none; pass
+ * workspace = NULL then).  Returns 0 for sizes gdn_chunk_fwd would reject.
+ */
+size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
+                                    gdn_dtype_t in_dtype);
+
+/*
+ * Prefill: run Eq. (1) over T tokens for every (b, hv) chain, chunk by chunk.
+ *
+ *   q, k           [B, T, Hk, dk]  in_dtype     (read only; q may equal k)
+ *   v              [B, T, Hv, dv]  in_dtype
+ *   beta, g        [B, T, Hv]      in_dtype     beta in [0,1]; g = log(alpha) <= 0
+ *   initial_state  [B, Hv, dk, dv] fp32, or NULL for a zero state
+ *   o              [B, T, Hv, dv]  out_dtype    fully overwritten; must not overlap any input
+ *   final_state    [B, Hv, dk, dv] fp32, or NULL to skip; may be the same pointer as
+ *                  initial_state (updated in place); fully overwritten when given
+ *   chunk          tokens per chunk of the chunk-parallel form: 16, 32 or 64 (the result
+ *                  does not depend on it beyond rounding); T need not be a multiple
+ *   scale          multiplies every output (1.0 for the plain rule)
+ *   in_dtype       GDN_F32 or GDN_BF16;  out_dtype  GDN_F32 or GDN_BF16
+ *   workspace      device buffer of at least gdn_chunk_fwd_workspace_size(...) bytes
+ *
+ * Supported: dk, dv in {16, 32, 64, 128}.  T = 0 writes final_state = initial_state
+ * (or zeros) and nothing else.  B = 0 is a no-op.
+ */
+gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v, const void *beta,
+                           const void *g, const float *initial_state, void *o,
+                           float *final_state, int B, int T, int Hk, int Hv, int dk, int dv,
+                           int chunk, float scale, gdn_dtype_t in_dtype, gdn_dtype_t out_dtype,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Decode: apply one token of Eq. (1) to every state in place and read it out.
+ *
+ *   q, k      [B, Hk, dk]      in_dtype
+ *   v         [B, Hv, dv]      in_dtype
+ *   beta, g   [B, Hv]          in_dtype
+ *   state     [B, Hv, dk, dv]  fp32, read and overwritten with the updated state
+ *   o         [B, Hv, dv]      out_dtype, o = scale * S_new^T q; must not overlap any input
+ *
+ * Each state is read once and written once (a streaming, memory-bound update).
+ * Supported: dk, dv in {16, 32, 64, 128}.  B = 0 is a no-op.
+ */
+gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v, const void *beta,
+                             const void *g, float *state, void *o, int B, int Hk, int Hv,
+                             int dk, int dv, float scale, gdn_dtype_t in_dtype,
+                             gdn_dtype_t out_dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

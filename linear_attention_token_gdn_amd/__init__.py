@@ -1,0 +1,184 @@
+"""MI355X-native Gated DeltaNet token mixer: Python face of libgdn.so.
+
+The gated delta rule (explainer page "論文解説: Qwen3.8-Next の設計", ta-paperlens.web.app,
+section "GDNの中身: 足すのではなく、消してから書く", Eq. (1)):
+
+    S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,   o_t = scale * S_t^T q_t
+
+with g_t = log(alpha_t).  Every step runs in the HIP kernels of ``libgdn.so`` (built with
+``python -m linear_attention_token_gdn_amd.build``); this module only checks tensor
+properties, allocates outputs with torch and passes raw pointers and the current torch
+stream through ctypes.  There is no CPU fallback: without the built library every call raises.
+
+The C entry points are exposed unchanged as ``gdn_chunk_fwd``, ``gdn_decode_step``,
+``gdn_chunk_fwd_workspace_size``, ``gdn_status_string`` and ``gdn_abi_version``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libgdn.so")
+
+GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
+GDN_F32, GDN_BF16 = 0, 1
+EXPORTED_SYMBOLS = ("gdn_abi_version", "gdn_status_string", "gdn_chunk_fwd_workspace_size",
+                    "gdn_chunk_fwd", "gdn_decode_step")
+
+_lib = None
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__("%s failed: %s" % (where, status_string(status)))
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgdn.so and declare the C signatures.  Raises if the library is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libgdn.so is not built (%s); run "
+                           "`python -m linear_attention_token_gdn_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.gdn_abi_version.argtypes = []
+    lib.gdn_abi_version.restype = i
+    lib.gdn_status_string.argtypes = [i]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_chunk_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i, i]
+    lib.gdn_chunk_fwd_workspace_size.restype = sz
+    lib.gdn_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i,
+                                  vp, sz, vp]
+    lib.gdn_chunk_fwd.restype = i
+    lib.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    lib.gdn_decode_step.restype = i
+    _lib = lib
+    return lib
+
+
+# ------------------------------------------------------------------ raw C entry points
+def gdn_abi_version() -> int:
+    return int(load_library().gdn_abi_version())
+
+
+def gdn_status_string(status: int) -> str:
+    return load_library().gdn_status_string(int(status)).decode()
+
+
+status_string = gdn_status_string
+
+
+def gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, chunk, in_dtype) -> int:
+    return int(load_library().gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, chunk, in_dtype))
+
+
+def gdn_chunk_fwd(q, k, v, beta, g, initial_state, o, final_state, B, T, Hk, Hv, dk, dv, chunk,
+                  scale, in_dtype, out_dtype, workspace, workspace_bytes, stream) -> int:
+    """Raw call: pointer arguments are ints (device addresses) or None."""
+    return int(load_library().gdn_chunk_fwd(q, k, v, beta, g, initial_state, o, final_state, B, T,
+                                            Hk, Hv, dk, dv, chunk, scale, in_dtype, out_dtype,
+                                            workspace, workspace_bytes, stream))
+
+
+def gdn_decode_step(q, k, v, beta, g, state, o, B, Hk, Hv, dk, dv, scale, in_dtype, out_dtype,
+                    stream) -> int:
+    """Raw call: pointer arguments are ints (device addresses) or None."""
+    return int(load_library().gdn_decode_step(q, k, v, beta, g, state, o, B, Hk, Hv, dk, dv, scale,
+                                              in_dtype, out_dtype, stream))
+
+
+# ------------------------------------------------------------------ torch-facing wrappers
+def _dtype_code(t):
+    import torch
+    if t == torch.float32:
+        return GDN_F32
+    if t == torch.bfloat16:
+        return GDN_BF16
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check(t, name, shape, dtype, device):
+    if t.shape != tuple(shape):
+        raise ValueError("%s: expected shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s: expected %s, got %s" % (name, dtype, t.dtype))
+    if t.device != device:
+        raise ValueError("%s: expected device %s, got %s" % (name, device, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def chunk_fwd(q, k, v, beta, g, initial_state=None, output_final_state=True, chunk=64,
+              scale=1.0, out_dtype=None, final_state=None, o=None, workspace=None):
+    """Prefill over T tokens.
+
+    q, k: [B,T,Hk,dk]; v: [B,T,Hv,dv]; beta, g: [B,T,Hv] (all float32 or all bfloat16, same
+    device); initial_state: [B,Hv,dk,dv] float32 or None.  ``final_state`` may be passed (it
+    may be ``initial_state`` itself for an in-place update).  Returns (o, final_state or None);
+    o is float32 unless ``out_dtype`` says otherwise.
+    """
+    import torch
+    lib = load_library()
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dev, dt = q.device, q.dtype
+    for t, n, s in ((q, "q", (B, T, Hk, dk)), (k, "k", (B, T, Hk, dk)), (v, "v", (B, T, Hv, dv)),
+                    (beta, "beta", (B, T, Hv)), (g, "g", (B, T, Hv))):
+        _check(t, n, s, dt, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (B, Hv, dk, dv), torch.float32, dev)
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((B, T, Hv, dv), dtype=out_dtype, device=dev)
+    else:
+        _check(o, "o", (B, T, Hv, dv), out_dtype, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check(final_state, "final_state", (B, Hv, dk, dv), torch.float32, dev)
+    in_code, out_code = _dtype_code(dt), _dtype_code(out_dtype)
+    need = int(lib.gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, chunk, in_code))
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(initial_state),
+                           _ptr(o), _ptr(final_state), B, T, Hk, Hv, dk, dv, chunk, float(scale),
+                           in_code, out_code, _ptr(workspace), ws_bytes, stream)
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_chunk_fwd")
+    return o, final_state
+
+
+def decode_step(q, k, v, beta, g, state, scale=1.0, out_dtype=None, o=None):
+    """One token per sequence.  q, k: [B,Hk,dk]; v: [B,Hv,dv]; beta, g: [B,Hv];
+    state: [B,Hv,dk,dv] float32, updated in place.  Returns o [B,Hv,dv]."""
+    import torch
+    lib = load_library()
+    B, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    dev, dt = q.device, q.dtype
+    for t, n, s in ((q, "q", (B, Hk, dk)), (k, "k", (B, Hk, dk)), (v, "v", (B, Hv, dv)),
+                    (beta, "beta", (B, Hv)), (g, "g", (B, Hv))):
+        _check(t, n, s, dt, dev)
+    _check(state, "state", (B, Hv, dk, dv), torch.float32, dev)
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((B, Hv, dv), dtype=out_dtype, device=dev)
+    else:
+        _check(o, "o", (B, Hv, dv), out_dtype, dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(state), _ptr(o),
+                             B, Hk, Hv, dk, dv, float(scale), _dtype_code(dt),
+                             _dtype_code(out_dtype), stream)
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_decode_step")
+    return o

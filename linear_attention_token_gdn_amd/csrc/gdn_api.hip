@@ -1,0 +1,157 @@
+// gdn_api.hip -- the C ABI of libgdn.so (declared in include/gdn.h): host-side argument
+// validation and dispatch to the kernels.  Nothing here allocates device memory, keeps state
+// between calls or synchronises the host.
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "gdn_internal.h"
+
+namespace {
+
+bool dim_supported(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool dtype_known(gdn_dtype_t t) { return t == GDN_F32 || t == GDN_BF16; }
+size_t dtype_bytes(gdn_dtype_t t) { return t == GDN_F32 ? 4 : 2; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Half-open byte ranges [p, p + n) overlap.
+bool overlap(const void *p, size_t n, const void *r, size_t m) {
+    if (p == nullptr || r == nullptr || n == 0 || m == 0) return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(r);
+    return a < b + m && b < a + n;
+}
+
+// "variant" override for A/B measurements: GDN_FORCE_VARIANT=recurrent routes bf16 prefill
+// to the token-by-token kernel.
+bool force_recurrent() {
+    const char *s = getenv("GDN_FORCE_VARIANT");
+    return s != nullptr && strcmp(s, "recurrent") == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char *gdn_status_string(gdn_status_t s) {
+    switch (s) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_INVALID_ARG: return "GDN_ERR_INVALID_ARG";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP";
+    }
+    return "GDN_ERR_UNKNOWN";
+}
+
+static gdn_status_t check_prefill(const gdn::PrefillArgs &a) {
+    if (a.B < 0 || a.T < 0 || a.Hk <= 0 || a.Hv <= 0 || a.dk <= 0 || a.dv <= 0)
+        return GDN_ERR_INVALID_ARG;
+    if (a.Hv % a.Hk != 0) return GDN_ERR_INVALID_ARG;
+    if (!dtype_known(a.in_dt) || !dtype_known(a.out_dt)) return GDN_ERR_UNSUPPORTED;
+    if (!dim_supported(a.dk) || !dim_supported(a.dv)) return GDN_ERR_UNSUPPORTED;
+    if (a.chunk != 16 && a.chunk != 32 && a.chunk != 64) return GDN_ERR_UNSUPPORTED;
+    const size_t B = a.B, T = a.T, Hk = a.Hk, Hv = a.Hv, dk = a.dk, dv = a.dv;
+    const size_t ib = dtype_bytes(a.in_dt), ob = dtype_bytes(a.out_dt);
+    const size_t nq = B * T * Hk * dk * ib, nv = B * T * Hv * dv * ib, ng = B * T * Hv * ib;
+    const size_t no = B * T * Hv * dv * ob, ns = B * Hv * dk * dv * sizeof(float);
+    if (B * T > 0) {
+        if (!a.q || !a.k || !a.v || !a.beta || !a.g || !a.o) return GDN_ERR_INVALID_ARG;
+        if (!aligned(a.q, 16) || !aligned(a.k, 16) || !aligned(a.v, 16) || !aligned(a.o, 16))
+            return GDN_ERR_INVALID_ARG;
+        if (!aligned(a.beta, ib) || !aligned(a.g, ib)) return GDN_ERR_INVALID_ARG;
+        if (overlap(a.o, no, a.q, nq) || overlap(a.o, no, a.k, nq) || overlap(a.o, no, a.v, nv) ||
+            overlap(a.o, no, a.beta, ng) || overlap(a.o, no, a.g, ng) ||
+            overlap(a.o, no, a.s0, ns) || overlap(a.o, no, a.sT, ns))
+            return GDN_ERR_INVALID_ARG;
+    }
+    if ((a.s0 && !aligned(a.s0, 16)) || (a.sT && !aligned(a.sT, 16))) return GDN_ERR_INVALID_ARG;
+    if (a.sT && a.sT != a.s0 && overlap(a.sT, ns, a.s0, ns)) return GDN_ERR_INVALID_ARG;
+    if (a.sT && B * T > 0 &&
+        (overlap(a.sT, ns, a.q, nq) || overlap(a.sT, ns, a.k, nq) || overlap(a.sT, ns, a.v, nv)))
+        return GDN_ERR_INVALID_ARG;
+    return GDN_OK;
+}
+
+static bool use_chunk_kernel(const gdn::PrefillArgs &a) {
+    return a.in_dt == GDN_BF16 && !force_recurrent() && gdn::chunk_mfma_supports(a);
+}
+
+size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
+                                    gdn_dtype_t in_dtype) {
+    gdn::PrefillArgs a = {};
+    a.B = B; a.T = T; a.Hk = Hk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.chunk = chunk;
+    a.in_dt = in_dtype; a.out_dt = GDN_F32;
+    if (B < 0 || T < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk != 0 || !dim_supported(dk) ||
+        !dim_supported(dv) || (chunk != 16 && chunk != 32 && chunk != 64) || !dtype_known(in_dtype))
+        return 0;
+    if (B == 0 || T == 0 || !use_chunk_kernel(a)) return 0;
+    return gdn::chunk_mfma_workspace(a);
+}
+
+gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v, const void *beta,
+                           const void *g, const float *initial_state, void *o,
+                           float *final_state, int B, int T, int Hk, int Hv, int dk, int dv,
+                           int chunk, float scale, gdn_dtype_t in_dtype, gdn_dtype_t out_dtype,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+    gdn::PrefillArgs a;
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g;
+    a.s0 = initial_state; a.o = o; a.sT = final_state;
+    a.B = B; a.T = T; a.Hk = Hk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.chunk = chunk;
+    a.scale = scale; a.in_dt = in_dtype; a.out_dt = out_dtype;
+    a.ws = workspace; a.ws_bytes = workspace_bytes;
+    a.stream = static_cast<hipStream_t>(stream);
+    gdn_status_t st = check_prefill(a);
+    if (st != GDN_OK) return st;
+    if (B == 0) return GDN_OK;
+    if (T == 0) {
+        if (!final_state) return GDN_OK;
+        const size_t n = static_cast<size_t>(B) * Hv * dk * dv;
+        return gdn::launch_state_init(initial_state, final_state, n, a.stream) == hipSuccess
+                   ? GDN_OK
+                   : GDN_ERR_HIP;
+    }
+    hipError_t e;
+    if (use_chunk_kernel(a)) {
+        const size_t need = gdn::chunk_mfma_workspace(a);
+        if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+            return GDN_ERR_INVALID_ARG;
+        e = gdn::launch_chunk_mfma(a);
+    } else {
+        e = gdn::launch_recurrent(a);
+    }
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v, const void *beta,
+                             const void *g, float *state, void *o, int B, int Hk, int Hv,
+                             int dk, int dv, float scale, gdn_dtype_t in_dtype,
+                             gdn_dtype_t out_dtype, void *stream) {
+    if (B < 0 || Hk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || Hv % Hk != 0)
+        return GDN_ERR_INVALID_ARG;
+    if (!dtype_known(in_dtype) || !dtype_known(out_dtype)) return GDN_ERR_UNSUPPORTED;
+    if (!dim_supported(dk) || !dim_supported(dv)) return GDN_ERR_UNSUPPORTED;
+    if (B == 0) return GDN_OK;
+    if (!q || !k || !v || !beta || !g || !state || !o) return GDN_ERR_INVALID_ARG;
+    const size_t ib = dtype_bytes(in_dtype), ob = dtype_bytes(out_dtype);
+    if (!aligned(q, ib) || !aligned(k, ib) || !aligned(v, ib) || !aligned(beta, ib) ||
+        !aligned(g, ib) || !aligned(o, ob) || !aligned(state, 16))
+        return GDN_ERR_INVALID_ARG;
+    const size_t nq = size_t(B) * Hk * dk * ib, nv = size_t(B) * Hv * dv * ib;
+    const size_t ng = size_t(B) * Hv * ib, no = size_t(B) * Hv * dv * ob;
+    const size_t ns = size_t(B) * Hv * dk * dv * sizeof(float);
+    if (overlap(o, no, q, nq) || overlap(o, no, k, nq) || overlap(o, no, v, nv) ||
+        overlap(o, no, beta, ng) || overlap(o, no, g, ng) || overlap(o, no, state, ns) ||
+        overlap(state, ns, q, nq) || overlap(state, ns, k, nq) || overlap(state, ns, v, nv) ||
+        overlap(state, ns, beta, ng) || overlap(state, ns, g, ng))
+        return GDN_ERR_INVALID_ARG;
+    gdn::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g; a.state = state; a.o = o;
+    a.B = B; a.Hk = Hk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.scale = scale;
+    a.in_dt = in_dtype; a.out_dt = out_dtype;
+    a.stream = static_cast<hipStream_t>(stream);
+    return gdn::launch_decode(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // extern "C"

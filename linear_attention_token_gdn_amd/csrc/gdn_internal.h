@@ -1,0 +1,80 @@
+// gdn_internal.h -- launch interfaces and small device helpers shared by the kernels of
+// libgdn.so.  Not part of the public ABI (include/gdn.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/gdn.h"
+
+namespace gdn {
+
+struct PrefillArgs {
+    const void *q, *k, *v, *beta, *g;
+    const float *s0;  // may be null (zero state)
+    void *o;
+    float *sT;        // may be null (not written); may equal s0
+    int B, T, Hk, Hv, dk, dv, chunk;
+    float scale;
+    gdn_dtype_t in_dt, out_dt;
+    void *ws;
+    size_t ws_bytes;
+    hipStream_t stream;
+};
+
+struct DecodeArgs {
+    const void *q, *k, *v, *beta, *g;
+    float *state;
+    void *o;
+    int B, Hk, Hv, dk, dv;
+    float scale;
+    gdn_dtype_t in_dt, out_dt;
+    hipStream_t stream;
+};
+
+// Token-by-token kernel: every (dk, dv) in {16,32,64,128}^2, both dtypes.  It is the fp32
+// path and the fallback of the chunked kernel.
+hipError_t launch_recurrent(const PrefillArgs &a);
+
+// Chunk-parallel MFMA kernel for bf16 inputs.  supports() says whether the sizes are handled.
+bool chunk_mfma_supports(const PrefillArgs &a);
+size_t chunk_mfma_workspace(const PrefillArgs &a);
+hipError_t launch_chunk_mfma(const PrefillArgs &a);
+
+// One streaming pass over the decode state.
+hipError_t launch_decode(const DecodeArgs &a);
+
+// final_state = initial_state (or zeros) -- the whole result of a T = 0 prefill.
+hipError_t launch_state_init(const float *s0, float *sT, size_t n, hipStream_t stream);
+
+// ---------------------------------------------------------------------------------------
+// device helpers
+
+typedef uint16_t bf16_t;  // raw bf16 storage
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t x) {
+    return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+// Round to nearest even; NaN stays NaN (quiet bit set).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float load_f32(const T *p);
+template <> __device__ __forceinline__ float load_f32<float>(const float *p) { return *p; }
+template <> __device__ __forceinline__ float load_f32<bf16_t>(const bf16_t *p) {
+    return bf16_to_f32(*p);
+}
+
+template <typename T> __device__ __forceinline__ void store_f32(T *p, float x);
+template <> __device__ __forceinline__ void store_f32<float>(float *p, float x) { *p = x; }
+template <> __device__ __forceinline__ void store_f32<bf16_t>(bf16_t *p, float x) {
+    *p = f32_to_bf16(x);
+}
+
+}  // namespace gdn

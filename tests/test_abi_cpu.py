@@ -1,0 +1,130 @@
+"""CPU-side checks of the C ABI: the built library loads, exports every function that
+include/gdn.h declares, and rejects bad arguments on the host before launching anything
+(no call here reaches a kernel, so no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_token_gdn_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.LIB_PATH):
+        from linear_attention_token_gdn_amd import build
+        build.build()
+    return gdn.load_library()
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(gdn.EXPORTED_SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr), name
+
+
+def test_version_and_status_strings(lib):
+    assert gdn.gdn_abi_version() == 1
+    assert gdn.gdn_status_string(0) == "GDN_OK"
+    assert gdn.gdn_status_string(1) == "GDN_ERR_INVALID_ARG"
+    assert gdn.gdn_status_string(2) == "GDN_ERR_UNSUPPORTED"
+    assert gdn.gdn_status_string(3) == "GDN_ERR_HIP"
+    assert gdn.gdn_status_string(99) == "GDN_ERR_UNKNOWN"
+
+
+def test_workspace_size_rejects_bad_sizes(lib):
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 64, 2, 3, 16, 16, 16, gdn.GDN_BF16) == 0
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 64, 2, 2, 48, 16, 16, gdn.GDN_BF16) == 0
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 64, 2, 2, 16, 16, 24, gdn.GDN_BF16) == 0
+    assert gdn.gdn_chunk_fwd_workspace_size(0, 64, 2, 2, 16, 16, 16, gdn.GDN_BF16) == 0
+
+
+# fake, well-aligned, non-overlapping device addresses: validation must reject the call
+# before anything dereferences them
+BASE = 1 << 40
+P = {n: BASE + i * (1 << 32) for i, n in enumerate(["q", "k", "v", "beta", "g", "s0", "o", "sT"])}
+
+
+def prefill(**kw):
+    a = dict(q=P["q"], k=P["k"], v=P["v"], beta=P["beta"], g=P["g"], initial_state=P["s0"],
+             o=P["o"], final_state=P["sT"], B=1, T=64, Hk=2, Hv=2, dk=16, dv=16, chunk=16,
+             scale=1.0, in_dtype=gdn.GDN_BF16, out_dtype=gdn.GDN_F32, workspace=None,
+             workspace_bytes=0, stream=None)
+    a.update(kw)
+    return gdn.gdn_chunk_fwd(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hv=3), gdn.GDN_ERR_INVALID_ARG),
+    (dict(B=-1), gdn.GDN_ERR_INVALID_ARG),
+    (dict(T=-5), gdn.GDN_ERR_INVALID_ARG),
+    (dict(Hk=0), gdn.GDN_ERR_INVALID_ARG),
+    (dict(dk=48), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(dv=256), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(chunk=24), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(in_dtype=7), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(out_dtype=7), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(q=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(o=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(g=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(q=P["q"] + 2), gdn.GDN_ERR_INVALID_ARG),         # misaligned
+    (dict(initial_state=P["s0"] + 4), gdn.GDN_ERR_INVALID_ARG),
+    (dict(o=P["q"] + 64), gdn.GDN_ERR_INVALID_ARG),        # o overlaps q
+    (dict(o=P["s0"]), gdn.GDN_ERR_INVALID_ARG),            # o overlaps a state
+    (dict(final_state=P["s0"] + 1024), gdn.GDN_ERR_INVALID_ARG),  # partial state overlap
+])
+def test_prefill_validation(lib, kw, status):
+    assert prefill(**kw) == status
+
+
+def test_prefill_empty_batch_is_noop(lib):
+    assert prefill(B=0, q=None, k=None, v=None, beta=None, g=None, o=None) == gdn.GDN_OK
+
+
+def decode(**kw):
+    a = dict(q=P["q"], k=P["k"], v=P["v"], beta=P["beta"], g=P["g"], state=P["s0"], o=P["o"],
+             B=4, Hk=2, Hv=4, dk=16, dv=32, scale=1.0, in_dtype=gdn.GDN_BF16,
+             out_dtype=gdn.GDN_F32, stream=None)
+    a.update(kw)
+    return gdn.gdn_decode_step(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hv=3), gdn.GDN_ERR_INVALID_ARG),
+    (dict(B=-1), gdn.GDN_ERR_INVALID_ARG),
+    (dict(dk=8), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(in_dtype=5), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(state=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(state=P["s0"] + 8), gdn.GDN_ERR_INVALID_ARG),
+    (dict(o=P["v"]), gdn.GDN_ERR_INVALID_ARG),
+    (dict(state=P["q"]), gdn.GDN_ERR_INVALID_ARG),
+])
+def test_decode_validation(lib, kw, status):
+    assert decode(**kw) == status
+
+
+def test_decode_empty_batch_is_noop(lib):
+    assert decode(B=0) == gdn.GDN_OK
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    saved = gdn._lib
+    gdn._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="not built"):
+            gdn.load_library(str(tmp_path / "missing.so"))
+    finally:
+        gdn._lib = saved

@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet hot path on one MI355X.
+
+One step = one gdn_chunk_fwd over the prefill workload (default: B=1, T=4096, 16 heads,
+dk=dv=128, chunk 64, bf16 inputs, fp32 output and state) followed by one gdn_decode_step over
+the decode workload (B=256 sequences, 32 heads, dk=dv=128, fp32 state [256,32,128,128]
+updated in place; the 64 pre-drawn decode tokens are used in turn).  Inputs are seeded
+synthetic tensors (gdn_inputs.py), resident in HBM before the timed region.
+
+Prints ONE JSON line:  value = prefill tokens/s (B*T / mean prefill launch time), with the
+decode state GB/s, both kernels' rooflines (algorithmic bytes / measured launch time,
+against 8 TB/s HBM and 2.5 PFLOP/s dense fp16/bf16 MFMA), and the fp64 oracle's throughput
+on the host cores as a reported CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, vendor figure
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "prefill": os.path.join(ROOT, "linear_attention_token_gdn_amd", "csrc", "chunk_mfma.hip"),
+    "decode": os.path.join(ROOT, "linear_attention_token_gdn_amd", "csrc", "decode.hip"),
+}
+
+
+# ------------------------------------------------------------------ algorithmic counts
+def prefill_flops(B, T, Hk, Hv, dk, dv, C):
+    """Algorithmic FLOPs of the chunk-parallel form: only the needed triangles, KK^T and QK^T
+    once per q/k head; multiply-add = 2."""
+    total = 0
+    for t0 in range(0, T, C):
+        L = min(C, T - t0)
+        qk = 2 * L * L * dk                                   # lower KK^T (strict) + QK^T (incl)
+        v = ((L ** 3 - L) // 3 + L * (L - 1) * (dk + dv)       # inverse, U, W
+             + L * (L + 1) * dv + 6 * L * dk * dv)             # P Delta, W S, Q S, K^T Delta
+        total += Hk * qk + Hv * v
+    return B * total
+
+
+def prefill_bytes(B, T, Hk, Hv, dk, dv, in_bytes=2, out_bytes=4, has_s0=False):
+    rd = B * T * (2 * Hk * dk + Hv * dv + 2 * Hv) * in_bytes
+    if has_s0:
+        rd += B * Hv * dk * dv * 4
+    wr = B * T * Hv * dv * out_bytes + B * Hv * dk * dv * 4
+    return rd + wr
+
+
+def decode_bytes(B, Hk, Hv, dk, dv, in_bytes=2, out_bytes=4):
+    state = 2 * B * Hv * dk * dv * 4
+    other = B * (2 * Hk * dk + Hv * dv + 2 * Hv) * in_bytes + B * Hv * dv * out_bytes
+    return state, state + other
+
+
+def source_hash(path):
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None when absent or
+    taken on a different version of the kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------------ CPU baseline (oracle)
+def cpu_baseline(pre_inp, dec_inp, budget_s=30.0):
+    import numpy as np
+    import oracle
+    threads = min(16, len(os.sched_getaffinity(0)))
+    B, T, Hk, Hv = pre_inp.q.shape[0], pre_inp.q.shape[1], pre_inp.q.shape[2], pre_inp.v.shape[2]
+    reps, t = 0, time.perf_counter()
+    while True:  # repeat the whole workload until a few seconds of CPU time are sampled
+        oracle.run(pre_inp.q, pre_inp.k, pre_inp.v, pre_inp.beta, pre_inp.g, s0=pre_inp.s0,
+                   nthreads=threads, want_state=True)
+        reps += 1
+        if time.perf_counter() - t >= min(5.0, budget_s) or reps >= 50:
+            break
+    pre_s = (time.perf_counter() - t) / reps
+    # decode: one step of the decode workload (all 8192 states, fp64)
+    st = dec_inp.s0.astype(np.float64)
+    t = time.perf_counter()
+    oracle.decode_step(dec_inp.q[:, 0], dec_inp.k[:, 0], dec_inp.v[:, 0], dec_inp.beta[:, 0],
+                       dec_inp.g[:, 0], st, nthreads=threads)
+    dec_s = time.perf_counter() - t
+    Bd, Hvd, dk, dv = dec_inp.s0.shape
+    state_bytes_f32 = 2 * Bd * Hvd * dk * dv * 4
+    return {
+        "value": B * T / pre_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "sample": ("whole prefill workload (B=%d, T=%d, %d heads, fp64 token-by-token "
+                   "recurrence, %d independent chains), mean of %d runs: %.3f s each; plus one "
+                   "decode step of the decode workload in %.3f s" % (B, T, Hv, B * Hv, reps,
+                                                                      pre_s, dec_s)),
+        "decode_state_GBps_fp32_equiv": state_bytes_f32 / dec_s / 1e9,
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--prefill-config", type=int, default=1, choices=[1, 2, 3],
+                    help="prefill workload: 1 = B1 T4096 H16 (default), 2 = B8 T8192 Hk16/Hv32, "
+                         "3 = B1 T262144 H16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the Gated DeltaNet path here has no multi-GPU "
+              "mode (--gpus %d requested); run with --gpus 1" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    import linear_attention_token_gdn_amd as gdn
+    from gdn_inputs import CONFIGS, config_inputs
+
+    dev = torch.device("cuda:0")
+    gdn.load_library()
+
+    pc = CONFIGS[args.prefill_config]
+    dc = CONFIGS[4]
+    pre_inp = config_inputs(args.prefill_config)
+    dec_inp = config_inputs(4)
+
+    # ---- inputs resident in HBM
+    pt = pre_inp.to_torch(dev)
+    B, T, Hk, Hv, dk, dv, C = pc["B"], pc["T"], pc["Hk"], pc["Hv"], pc["dk"], pc["dv"], pc["chunk"]
+    o = torch.empty((B, T, Hv, dv), dtype=torch.float32, device=dev)
+    fs = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+    dt = dec_inp.to_torch(dev)
+    nsteps_dec = dc["T"]
+    dq = dt["q"].transpose(0, 1).contiguous()      # [64, B, H, d]: step s is a contiguous slice
+    dk_ = dt["k"].transpose(0, 1).contiguous()
+    dv_ = dt["v"].transpose(0, 1).contiguous()
+    db = dt["beta"].transpose(0, 1).contiguous()
+    dg = dt["g"].transpose(0, 1).contiguous()
+    state = dt["s0"].clone()
+    do = torch.empty((dc["B"], dc["Hv"], dc["dv"]), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def prefill():
+        gdn.chunk_fwd(pt["q"], pt["k"], pt["v"], pt["beta"], pt["g"], initial_state=pt["s0"],
+                      chunk=C, o=o, final_state=fs)
+
+    def decode(s):
+        i = s % nsteps_dec
+        gdn.decode_step(dq[i], dk_[i], dv_[i], db[i], dg[i], state, o=do)
+
+    for s in range(args.warmup):
+        prefill()
+        if not args.no_decode:
+            decode(s)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        e = ev[s]
+        e[0].record(stream)
+        prefill()
+        e[1].record(stream)
+        if not args.no_decode:
+            e[2].record(stream)
+            decode(args.warmup + s)
+            e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    pre_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    pre_mean = sum(pre_ms) / len(pre_ms)
+    flops = prefill_flops(B, T, Hk, Hv, dk, dv, C)
+    pbytes = prefill_bytes(B, T, Hk, Hv, dk, dv, has_s0=pre_inp.s0 is not None)
+    pre_tflops = flops / (pre_mean * 1e-3) / 1e12
+    pre_gbs = pbytes / (pre_mean * 1e-3) / 1e9
+    rooflines = {
+        "prefill": {
+            "kernel": "chunk_kernel<128,128,64,float>", "bound": "hbm",
+            "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(pre_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("prefill"),
+            "algorithmic_bytes": pbytes, "algorithmic_flops": flops,
+            "mean_launch_ms": round(pre_mean, 4),
+            "mfma_TFLOPs": round(pre_tflops, 2),
+            "frac_bf16_mfma_peak": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        }
+    }
+    dom = "prefill"
+    result_decode = None
+    if not args.no_decode:
+        dec_ms = [e[2].elapsed_time(e[3]) for e in ev]
+        dec_mean = sum(dec_ms) / len(dec_ms)
+        sbytes, tbytes = decode_bytes(dc["B"], dc["Hk"], dc["Hv"], dc["dk"], dc["dv"])
+        st_gbs = sbytes / (dec_mean * 1e-3) / 1e9
+        tot_gbs = tbytes / (dec_mean * 1e-3) / 1e9
+        rooflines["decode"] = {
+            "kernel": "decode_kernel<128,128,bf16,float>", "bound": "hbm",
+            "achieved": round(tot_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(tot_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode"),
+            "algorithmic_bytes": tbytes, "mean_launch_ms": round(dec_mean, 4),
+        }
+        result_decode = {
+            "state_GBps": round(st_gbs, 1), "frac_hbm_peak": round(st_gbs / HBM_PEAK_GBS, 4),
+            "us_per_step": round(dec_mean * 1e3, 2), "tokens_per_s": round(dc["B"] / (dec_mean * 1e-3), 1),
+            "state_bytes_per_step": sbytes,
+        }
+        if dec_mean > pre_mean:
+            dom = "decode"
+
+    line = {
+        "metric": "GDN prefill tokens/s + % bf16 MFMA peak; decode state GB/s % HBM peak",
+        "value": round(B * T / (pre_mean * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 in, fp16 MFMA operands, fp32 accumulate/state",
+        "data": "synthetic (seeded, gdn_inputs recipe v1)",
+        "config": {
+            "workload": pc["name"] + ("" if args.no_decode else " + " + dc["name"]),
+            "prefill": {k_: pc[k_] for k_ in ("B", "T", "Hk", "Hv", "dk", "dv", "chunk", "dtype")},
+            "decode": None if args.no_decode else
+            {k_: dc[k_] for k_ in ("B", "Hk", "Hv", "dk", "dv", "dtype")},
+        },
+        "prefill": {"tokens_per_s": round(B * T / (pre_mean * 1e-3), 1),
+                    "ms": round(pre_mean, 4), "TFLOPs": round(pre_tflops, 2),
+                    "frac_bf16_mfma_peak": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "GBps": round(pre_gbs, 1), "frac_hbm_peak": round(pre_gbs / HBM_PEAK_GBS, 4)},
+        "decode": result_decode,
+        "roofline": dict(rooflines[dom], kernel_role=dom),
+        "rooflines": rooflines,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(pre_inp, dec_inp)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

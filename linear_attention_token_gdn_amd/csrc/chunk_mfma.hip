@@ -8,27 +8,32 @@
 //
 //   gamma_r = sum_{s<=r} g_s (chunk-local),  D_rs = exp(gamma_r - gamma_s)  (s <= r)
 //   A       = strictly_lower(diag(beta) (K K^T o D))           (o = elementwise product)
-//   T       = (I + A)^-1                                         (unit lower triangular)
-//   U       = T diag(beta) V,     W = T diag(beta exp(gamma)) K  (independent of S)
+//   U       = (I + A)^-1 diag(beta) V                            } independent of S: the
+//   W       = (I + A)^-1 diag(beta exp(gamma)) K                 } "WY/UT" transform
 //   Delta   = U - W S                                            (rows are d_r)
 //   O       = scale (diag(exp(gamma)) Q S + (lower(Q K^T) o D) Delta)
 //   S_next  = exp(gamma_last) S + K^T diag(exp(gamma_last - gamma)) Delta
 //
 // Only ratios exp(gamma_r - gamma_s) <= 1 appear, so no factor can overflow.
 //
-// Design (one workgroup of 4 wavefronts per (b, hv) chain, the chunks walked in order):
-//   * the dk x dv fp32 state lives in MFMA accumulator registers for the whole sequence:
-//     wavefront w owns value columns [w*DV/4, (w+1)*DV/4);
-//   * Q, K, V of a chunk are staged in LDS once, converted bf16 -> fp16 (exact for the
-//     normalised q/k; v must stay inside the fp16 range);
-//   * KK^T and QK^T use exact fp16 inputs on v_mfma_f32_16x16x32_f16 with fp32 accumulation;
-//   * the unit-lower-triangular inverse is done in fp32: 16x16 diagonal blocks by forward
-//     substitution, off-diagonal blocks by block substitution on v_mfma_f32_16x16x4_f32;
-//   * operands derived in fp32 (T, W, S, Delta, P) are rounded to fp16 for the 16x16x32 MFMAs
-//     and every sum is accumulated in fp32 -- the fp32 state itself is never rounded;
-//   * the accumulator layout of S and Delta (lane l holds rows 4(l/16)..4(l/16)+3 of column
-//     l%16) is fed straight back as the B operand of the next product, with the k index of
-//     the A operand permuted to match, so the state never leaves registers.
+// Design: one workgroup of D/16 wavefronts per (b, hv) chain walks the chunks in order.
+//   * The D x D fp32 state lives in MFMA accumulator registers for the whole sequence;
+//     wavefront w owns value columns [16w, 16w + 16).
+//   * Q, K, V of the next chunk are prefetched into registers while the current chunk runs,
+//     then staged in LDS as fp16 (exact for normalised q/k; v must stay inside fp16 range).
+//   * KK^T and QK^T: v_mfma_f32_16x16x32_f16 on exact inputs, fp32 accumulation.
+//   * (I + A)^-1 is never formed: the 16x16 diagonal blocks are inverted in fp32 by forward
+//     substitution, and U, W come from a blocked forward substitution over 16-row blocks,
+//     X_a = T_aa (R_a - sum_{c<a} A_ac X_c), on v_mfma_f32_16x16x16_f16 -- every wavefront
+//     solves its own two 16-column panels (of diag(beta) V and diag(beta e^gamma) K), so the
+//     solve needs no barrier.
+//   * Derived fp32 operands (W, S, Delta, P, X) are rounded to fp16 for the MFMAs; every sum
+//     accumulates in fp32 and the fp32 state itself is never rounded.
+//   * The accumulator layout (lane l holds rows 4(l/16)..4(l/16)+3 of column l%16) is fed
+//     straight back as a B operand, with the k index of the A operand permuted to match, so
+//     the state and the solve panels never leave registers.
+//   * O is staged in LDS and written with coalesced 16-byte stores at the top of the next
+//     chunk, before the next prefetch is issued (the vector-memory counter is in-order).
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -39,51 +44,62 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ f32x4 mma16(f16x8 a, f16x8 b, f32x4 c) {
+__device__ __forceinline__ f32x4 mma_k32(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mma32(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mma_k16(f16x4 a, f16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f16x8 cat(f16x4 lo, f16x4 hi) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+__device__ __forceinline__ f16x4 to_f16x4(f32x4 x) {
+    return f16x4{f16(x[0]), f16(x[1]), f16(x[2]), f16(x[3])};
+}
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-constexpr int NW = 4;     // wavefronts per workgroup
-constexpr int NT = 64 * NW;
+// Workgroup barrier that waits only for this wave's LDS traffic.  __syncthreads() also waits
+// for every outstanding global load and store, which would stall each chunk on the prefetch of
+// the next chunk and on the output stores; nothing here reads global memory written by another
+// wave, so LDS completion is all a barrier has to guarantee.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
-template <int DK, int DV, int C> struct Cfg {
-    static constexpr int NR = C / 16;        // 16-row tiles of a chunk
-    static constexpr int NI = DK / 16;       // 16-row tiles of the state (key index)
-    static constexpr int NJ = DV / 16 / NW;  // 16-column state tiles per wavefront
-    static constexpr int NIW = NI / NW;      // 16-column tiles of W per wavefront
-    static constexpr int KD = DK / 32;       // k-steps over the key index
-    static constexpr int KC = C / 32;        // k-steps over the chunk
-    static constexpr int PD = DK + 8;        // padded LDS pitches (halves / floats)
-    static constexpr int PV = DV + 8;
+template <int D, int C> struct Cfg {
+    static constexpr int NW = D / 16;       // wavefronts: one 16-column state tile each
+    static constexpr int NT = 64 * NW;
+    static constexpr int NR = C / 16;       // 16-row blocks of a chunk
+    static constexpr int NI = D / 16;       // 16-row tiles of the state (key index)
+    static constexpr int KD = D / 32;       // 32-wide k-steps over the key index
+    static constexpr int KC = C / 32;       // 32-wide k-steps over the chunk
+    static constexpr int PD = D + 8;        // padded LDS pitches (halves)
     static constexpr int PC = C + 8;
-    static constexpr int PF = C + 4;
-    static_assert(DK % 64 == 0 && DV % 64 == 0 && C % 32 == 0, "unsupported chunk kernel shape");
-    static_assert(NJ >= 1 && NIW >= 1, "unsupported chunk kernel shape");
+    static constexpr int PO = D + 4;        // output staging pitch (floats)
+    static constexpr int NQ = C * D / 8 / NT;  // 16-byte pieces of q (or k, v) per thread
+    static constexpr int NO = C * D / 4 / NT;  // 16-byte pieces of o per thread
+    static_assert((D == 64 || D == 128) && (C == 32 || C == 64), "chunk kernel shape");
+    static_assert(NQ >= 1 && (C * D / 8) % NT == 0 && (C * D / 4) % NT == 0, "tiling");
 };
 
-template <int DK, int DV, int C> struct Smem {
-    using F = Cfg<DK, DV, C>;
-    f16 q[C][F::PD];      // Q rows
-    f16 k[C][F::PD];      // K rows
-    f16 kt[DK][F::PC];    // K^T
-    f16 v[C][F::PV];      // V rows
-    f16 tb[C][F::PC];     // T diag(beta)
-    f16 tbg[C][F::PC];    // T diag(beta exp(gamma))
-    f16 p[C][F::PC];      // lower(Q K^T) o D
-    f16 wn[C][F::PD];     // -W
-    float a[C][F::PF];    // A (strict lower); then T: diagonal blocks in place, off-diagonal
-                          // blocks T[r][s] (r > s) stored transposed at a[s][r]
-    float gam[C];         // gamma (chunk-local cumulative log-gate)
-    float Gam[C];         // exp(gamma)
-    float dec[C];         // exp(gamma_last - gamma)
-    float bet[C];         // beta
+template <int D, int C> struct Smem {
+    using F = Cfg<D, C>;
+    f16 q[C][F::PD];          // Q rows
+    f16 k[C][F::PD];          // K rows
+    f16 kt[D][F::PC];         // K^T
+    f16 v[C][F::PD];          // V rows
+    f16 p[C][F::PC];          // lower(Q K^T) o D
+    f16 wn[C][F::PD];         // -W
+    f16 an[C][F::PC];         // -A, off-diagonal 16x16 blocks (lower)
+    f16 td[F::NR][16][24];    // inverses of the diagonal blocks of I + A, fp16
+    float ad[F::NR][16][20];  // diagonal blocks of A, fp32
+    float gam[C];             // gamma (chunk-local cumulative log-gate)
+    float Gam[C];             // exp(gamma)
+    float dec[C];             // exp(gamma_last - gamma)
+    float bet[C];             // beta
+    float ost[C][F::PO];      // scaled output of the chunk, waiting to be stored
 };
 
 // Block -> chain order that keeps the G value heads sharing one q/k head on one XCD
@@ -94,72 +110,68 @@ __device__ __forceinline__ int chain_of_block(int blk, int nblk, int G) {
     return ((m / G) * 8 + x) * G + (m % G);
 }
 
-template <int DK, int DV, int C, typename TO>
-__global__ void __launch_bounds__(NT)
+template <typename TO> __device__ __forceinline__ void store4(TO *p, f32x4 x);
+template <> __device__ __forceinline__ void store4<float>(float *p, f32x4 x) {
+    *reinterpret_cast<f32x4 *>(p) = x;
+}
+template <> __device__ __forceinline__ void store4<bf16_t>(bf16_t *p, f32x4 x) {
+    *reinterpret_cast<u16x4 *>(p) =
+        u16x4{f32_to_bf16(x[0]), f32_to_bf16(x[1]), f32_to_bf16(x[2]), f32_to_bf16(x[3])};
+}
+
+template <int D, int C, typename TO>
+__global__ void __launch_bounds__((Cfg<D, C>::NT))
 chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
              const bf16_t *__restrict__ v, const bf16_t *__restrict__ beta,
              const bf16_t *__restrict__ g, const float *__restrict__ s0, TO *__restrict__ o,
              float *__restrict__ sT, int T, int Hk, int Hv, float scale) {
-    using F = Cfg<DK, DV, C>;
+    using F = Cfg<D, C>;
+    constexpr int NT = F::NT, NR = F::NR;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-    Smem<DK, DV, C> &sm = *reinterpret_cast<Smem<DK, DV, C> *>(smem_raw);
+    Smem<D, C> &sm = *reinterpret_cast<Smem<D, C> *>(smem_raw);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 15, lg = lane >> 4;
     const int G = Hv / Hk;
     const int chain = chain_of_block(blockIdx.x, gridDim.x, G);
     const int b = chain / Hv, hv = chain - b * Hv, hq = hv / G;
+    const int col = 16 * wave + li;  // the state column this lane holds
 
-    // lower(QK^T) tiles above the diagonal are never written: clear them once
-    for (int idx = tid; idx < C * F::PC; idx += NT) (&sm.p[0][0])[idx] = f16(0.f);
-
-    // ---- the state: tile (it, jt) holds rows 16it + 4lg + r, column colj(jt)
-    f32x4 S[F::NI][F::NJ];
-    const size_t sbase = static_cast<size_t>(chain) * DK * DV;
+    // ---- the state: tile it holds rows 16it + 4lg + r of column `col`
+    f32x4 S[F::NI];
+    const size_t sbase = static_cast<size_t>(chain) * D * D;
 #pragma unroll
     for (int it = 0; it < F::NI; ++it)
 #pragma unroll
-        for (int jt = 0; jt < F::NJ; ++jt) {
-            const int col = (wave * F::NJ + jt) * 16 + li;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                S[it][jt][r] = s0 ? s0[sbase + static_cast<size_t>(16 * it + 4 * lg + r) * DV + col]
-                                  : 0.f;
-        }
+        for (int r = 0; r < 4; ++r)
+            S[it][r] = s0 ? s0[sbase + static_cast<size_t>(16 * it + 4 * lg + r) * D + col] : 0.f;
 
-    // ---- raw inputs of the next chunk, prefetched into registers while the current chunk
-    // is being computed (16-byte pieces; rows past the end of the sequence read as zero)
-    constexpr int NQ = C * DK / 8 / NT, NV = C * DV / 8 / NT;
-    static_assert(NQ >= 1 && NV >= 1 && C * DK / 8 % NT == 0 && C * DV / 8 % NT == 0, "tiling");
-    u16x8 pq[NQ], pk[NQ], pv[NV];
-    float pgv = 0.f, pbv = 0.f;
+    // ---- raw inputs of the next chunk, prefetched into registers (rows past T read as 0)
+    u16x8 pq[F::NQ], pk[F::NQ], pv[F::NQ];
+    bf16_t pg = 0, pb = 0;
     auto prefetch = [&](int cidx) {
         const int tt = cidx * C, L = min(C, T - tt);
 #pragma unroll
-        for (int n = 0; n < NQ; ++n) {
-            const int idx = tid + n * NT, r = idx / (DK / 8), cc = idx - r * (DK / 8);
+        for (int n = 0; n < F::NQ; ++n) {
+            const int idx = tid + n * NT, r = idx / (D / 8), cc = idx - r * (D / 8);
             pq[n] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
             pk[n] = pq[n];
+            pv[n] = pq[n];
             if (r < L) {
-                const size_t off = ((static_cast<size_t>(b) * T + tt + r) * Hk + hq) * DK + cc * 8;
-                pq[n] = *reinterpret_cast<const u16x8 *>(q + off);
-                pk[n] = *reinterpret_cast<const u16x8 *>(k + off);
+                const size_t row = static_cast<size_t>(b) * T + tt + r;
+                const size_t oq = (row * Hk + hq) * D + cc * 8, ov = (row * Hv + hv) * D + cc * 8;
+                pq[n] = *reinterpret_cast<const u16x8 *>(q + oq);
+                pk[n] = *reinterpret_cast<const u16x8 *>(k + oq);
+                pv[n] = *reinterpret_cast<const u16x8 *>(v + ov);
             }
         }
-#pragma unroll
-        for (int n = 0; n < NV; ++n) {
-            const int idx = tid + n * NT, r = idx / (DV / 8), cc = idx - r * (DV / 8);
-            pv[n] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            if (r < L)
-                pv[n] = *reinterpret_cast<const u16x8 *>(
-                    v + ((static_cast<size_t>(b) * T + tt + r) * Hv + hv) * DV + cc * 8);
-        }
-        pgv = 0.f;
-        pbv = 0.f;
+        pg = 0;
+        pb = 0;
         if (tid < L) {
             const size_t gi = (static_cast<size_t>(b) * T + tt + tid) * Hv + hv;
-            pgv = bf16_to_f32(g[gi]);
-            pbv = bf16_to_f32(beta[gi]);
+            pg = g[gi];
+            pb = beta[gi];
         }
     };
 
@@ -167,305 +179,254 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     if (nchunks > 0) prefetch(0);
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = c * C;
-        const int Lc = min(C, T - t0);
-        __syncthreads();  // the previous chunk is done with every LDS buffer
+        lds_barrier();  // the previous chunk is done with every LDS buffer
 
-        // ---- stage 0: this chunk's Q, K, V rows (bf16 -> fp16) and gates into LDS
+        // ---- stage 0: stage this chunk in LDS, store the previous chunk's output, prefetch
 #pragma unroll
-        for (int n = 0; n < NQ; ++n) {
-            const int idx = tid + n * NT, r = idx / (DK / 8), cc = idx - r * (DK / 8);
-            f16x8 qh, kh;
+        for (int n = 0; n < F::NQ; ++n) {
+            const int idx = tid + n * NT, r = idx / (D / 8), cc = idx - r * (D / 8);
+            f16x8 qh, kh, vh;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 qh[e] = f16(bf16_to_f32(pq[n][e]));
                 kh[e] = f16(bf16_to_f32(pk[n][e]));
+                vh[e] = f16(bf16_to_f32(pv[n][e]));
             }
             *reinterpret_cast<f16x8 *>(&sm.q[r][cc * 8]) = qh;
             *reinterpret_cast<f16x8 *>(&sm.k[r][cc * 8]) = kh;
-        }
-#pragma unroll
-        for (int n = 0; n < NV; ++n) {
-            const int idx = tid + n * NT, r = idx / (DV / 8), cc = idx - r * (DV / 8);
-            f16x8 vh;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vh[e] = f16(bf16_to_f32(pv[n][e]));
             *reinterpret_cast<f16x8 *>(&sm.v[r][cc * 8]) = vh;
         }
-        if (tid < 64) {
-            float gv = pgv;
+        if (wave == 0) {
+            float gv = bf16_to_f32(pg);
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {  // inclusive prefix sum over the chunk
                 const float y = __shfl_up(gv, off);
                 if (lane >= off) gv += y;
             }
             const float glast = __shfl(gv, C - 1);
-            if (tid < C) {
-                sm.gam[tid] = gv;
-                sm.Gam[tid] = expf(gv);
-                sm.dec[tid] = expf(glast - gv);
-                sm.bet[tid] = pbv;
+            if (lane < C) {
+                sm.gam[lane] = gv;
+                sm.Gam[lane] = __expf(gv);
+                sm.dec[lane] = __expf(glast - gv);
+                sm.bet[lane] = bf16_to_f32(pb);
+            }
+        }
+        if (c > 0) {
+            const int tp = t0 - C;  // the previous chunk is always a full one
+#pragma unroll
+            for (int n = 0; n < F::NO; ++n) {
+                const int idx = tid + n * NT, r = idx / (D / 4), cc = idx - r * (D / 4);
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(&sm.ost[r][cc * 4]);
+                store4<TO>(o + ((static_cast<size_t>(b) * T + tp + r) * Hv + hv) * D + cc * 4, x);
             }
         }
         if (c + 1 < nchunks) prefetch(c + 1);
-        __syncthreads();
+        lds_barrier();
 
-        // ---- stage 0b: K^T
-        for (int idx = tid; idx < DK * (C / 8); idx += NT) {
-            const int i = idx % DK, s8 = idx / DK;
+        // ---- stage 1: KK^T -> A, QK^T -> P (lower-triangular 16x16 tiles), and K^T
+        for (int job = wave; job < 2 * NR; job += F::NW) {
+            const bool isq = job >= NR;
+            const int rt = isq ? job - NR : job;
+            const f16 *arow = isq ? &sm.q[16 * rt + li][0] : &sm.k[16 * rt + li][0];
+            f16x8 af[F::KD];
+#pragma unroll
+            for (int kk = 0; kk < F::KD; ++kk)
+                af[kk] = *reinterpret_cast<const f16x8 *>(arow + 32 * kk + 8 * lg);
+            float gr[4], br[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                gr[rr] = sm.gam[16 * rt + 4 * lg + rr];
+                br[rr] = sm.bet[16 * rt + 4 * lg + rr];
+            }
+#pragma unroll
+            for (int st = 0; st < NR; ++st) {
+                if (st > rt) break;
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int kk = 0; kk < F::KD; ++kk)
+                    acc = mma_k32(af[kk],
+                                  *reinterpret_cast<const f16x8 *>(&sm.k[16 * st + li][32 * kk + 8 * lg]),
+                                  acc);
+                const int s = 16 * st + li;
+                const float gs = sm.gam[s];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int r = 16 * rt + 4 * lg + rr;
+                    const float d = (s <= r) ? __expf(gr[rr] - gs) : 0.f;
+                    if (isq) {
+                        sm.p[r][s] = f16(acc[rr] * d);
+                    } else {
+                        const float av = (s < r) ? br[rr] * d * acc[rr] : 0.f;
+                        if (st == rt)
+                            sm.ad[rt][4 * lg + rr][li] = av;
+                        else
+                            sm.an[r][s] = f16(-av);
+                    }
+                }
+            }
+            if (isq && rt + 1 < NR) {  // the tile right of the diagonal is read by P Delta
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) sm.p[16 * rt + 4 * lg + rr][16 * (rt + 1) + li] = f16(0.f);
+            }
+        }
+        for (int idx = tid; idx < D * (C / 8); idx += NT) {
+            const int i = idx % D, s8 = idx / D;
             f16x8 x;
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = sm.k[s8 * 8 + e][i];
             *reinterpret_cast<f16x8 *>(&sm.kt[i][s8 * 8]) = x;
         }
+        lds_barrier();
 
-        // ---- stage 1: KK^T -> A (fp32), QK^T -> P (fp16); lower-triangular tiles only
-        {
-            constexpr int NTRI = F::NR * (F::NR + 1) / 2;
-            for (int pidx = wave; pidx < 2 * NTRI; pidx += NW) {
-                const bool isP = pidx >= NTRI;
-                const int pp = isP ? pidx - NTRI : pidx;
-                int rt = 0;
-                while ((rt + 1) * (rt + 2) / 2 <= pp) ++rt;
-                const int st = pp - rt * (rt + 1) / 2;
-                const f16 *arow = isP ? &sm.q[16 * rt + li][0] : &sm.k[16 * rt + li][0];
-                const f16 *brow = &sm.k[16 * st + li][0];
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < F::KD; ++kk)
-                    acc = mma16(*reinterpret_cast<const f16x8 *>(arow + 32 * kk + 8 * lg),
-                                *reinterpret_cast<const f16x8 *>(brow + 32 * kk + 8 * lg), acc);
-                const int s = 16 * st + li;
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int r = 16 * rt + 4 * lg + rr;
-                    const float d = (s <= r) ? expf(sm.gam[r] - sm.gam[s]) : 0.f;
-                    if (isP)
-                        sm.p[r][s] = f16(acc[rr] * d);
-                    else
-                        sm.a[r][s] = (s < r) ? sm.bet[r] * d * acc[rr] : 0.f;
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- stage 2a: inverse of each 16x16 diagonal block of I + A (forward substitution)
-        if (wave < F::NR && lane < 16) {
-            const int base = 16 * wave;
+        // ---- stage 2: inverse of each 16x16 diagonal block of I + A (forward substitution)
+        if (wave < NR && lane < 16) {
             float x[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float acc = (r == lane) ? 1.f : 0.f;
 #pragma unroll
-                for (int s = 0; s < r; ++s) acc -= sm.a[base + r][base + s] * x[s];
+                for (int s = 0; s < r; ++s) acc -= sm.ad[wave][r][s] * x[s];
                 x[r] = acc;
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sm.a[base + r][base + lane] = x[r];
+            for (int r = 0; r < 16; ++r) sm.td[wave][r][lane] = f16(x[r]);
         }
-        __syncthreads();
+        lds_barrier();
 
-        // ---- stage 2b: off-diagonal blocks, T_ab = -T_aa sum_{b<=c<a} A_ac T_cb, by distance
-        for (int d = 1; d < F::NR; ++d) {
-            if (wave < F::NR - d) {
-                const int bb = wave, aa = wave + d;
-                f32x4 X = {0.f, 0.f, 0.f, 0.f};
-                for (int cc = bb; cc < aa; ++cc) {
+        // ---- stage 3: blocked forward substitution for this wave's panels,
+        //      U[:, 16w..] = (I+A)^-1 diag(beta) V[:, 16w..]  (kept in registers)
+        //      W[:, 16w..] = (I+A)^-1 diag(beta e^gamma) K[:, 16w..]  (-W to LDS)
+        f32x4 U[NR], Wp[NR];
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        const int kx = 4 * ks + lg;
-                        const float av = sm.a[16 * aa + li][16 * cc + kx];  // A_ac[m][k]
-                        const float bv = (cc == bb) ? sm.a[16 * bb + kx][16 * bb + li]
-                                                    : sm.a[16 * bb + li][16 * cc + kx];  // T_cb[k][n]
-                        X = mma32(av, bv, X);
-                    }
-                }
-                f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+        for (int a = 0; a < NR; ++a) {
+            const f16x4 kv4 = *reinterpret_cast<const f16x4 *>(&sm.kt[col][16 * a + 4 * lg]);
+            f32x4 yu, yw;
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                    Y = mma32(sm.a[16 * aa + li][16 * aa + 4 * lg + rr], X[rr], Y);  // T_aa X
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) sm.a[16 * bb + li][16 * aa + 4 * lg + rr] = -Y[rr];
-            }
-            __syncthreads();
-        }
-
-        // ---- stage 2c: T diag(beta) and T diag(beta exp(gamma)) in fp16
-        for (int idx = tid; idx < C * C; idx += NT) {
-            const int r = idx / C, s = idx - r * C;
-            float tv = 0.f;
-            if (s <= r) tv = ((r >> 4) == (s >> 4)) ? sm.a[r][s] : sm.a[s][r];
-            const float tb = tv * sm.bet[s];
-            sm.tb[r][s] = f16(tb);
-            sm.tbg[r][s] = f16(tb * sm.Gam[s]);
-        }
-        __syncthreads();
-
-        // ---- stage 3: U = T diag(beta) V (kept in registers), -W to LDS
-        f32x4 U[F::NR][F::NJ];
-#pragma unroll
-        for (int rt = 0; rt < F::NR; ++rt)
-#pragma unroll
-            for (int jt = 0; jt < F::NJ; ++jt) U[rt][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int jt = 0; jt < F::NJ; ++jt) {
-            const int col = (wave * F::NJ + jt) * 16 + li;
-#pragma unroll
-            for (int kk = 0; kk < F::KC; ++kk) {
-                f16x8 bv;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) bv[e] = sm.v[32 * kk + 8 * lg + e][col];
-#pragma unroll
-                for (int rt = 0; rt < F::NR; ++rt)
-                    if (32 * kk <= 16 * rt + 15)
-                        U[rt][jt] = mma16(
-                            *reinterpret_cast<const f16x8 *>(&sm.tb[16 * rt + li][32 * kk + 8 * lg]),
-                            bv, U[rt][jt]);
-            }
-        }
-#pragma unroll
-        for (int iw = 0; iw < F::NIW; ++iw) {
-            const int icol = (wave * F::NIW + iw) * 16 + li;
-            f32x4 Wt[F::NR];
-#pragma unroll
-            for (int rt = 0; rt < F::NR; ++rt) Wt[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < F::KC; ++kk) {
-                const f16x8 bk = *reinterpret_cast<const f16x8 *>(&sm.kt[icol][32 * kk + 8 * lg]);
-#pragma unroll
-                for (int rt = 0; rt < F::NR; ++rt)
-                    if (32 * kk <= 16 * rt + 15)
-                        Wt[rt] = mma16(
-                            *reinterpret_cast<const f16x8 *>(&sm.tbg[16 * rt + li][32 * kk + 8 * lg]),
-                            bk, Wt[rt]);
+            for (int rr = 0; rr < 4; ++rr) {
+                const int r = 16 * a + 4 * lg + rr;
+                const float br = sm.bet[r];
+                yu[rr] = br * float(sm.v[r][col]);
+                yw[rr] = br * sm.Gam[r] * float(kv4[rr]);
             }
 #pragma unroll
-            for (int rt = 0; rt < F::NR; ++rt)
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) sm.wn[16 * rt + 4 * lg + rr][icol] = f16(-Wt[rt][rr]);
+            for (int cb = 0; cb < a; ++cb) {
+                const f16x4 an = *reinterpret_cast<const f16x4 *>(&sm.an[16 * a + li][16 * cb + 4 * lg]);
+                yu = mma_k16(an, to_f16x4(U[cb]), yu);
+                yw = mma_k16(an, to_f16x4(Wp[cb]), yw);
+            }
+            const f16x4 td = *reinterpret_cast<const f16x4 *>(&sm.td[a][li][4 * lg]);
+            U[a] = mma_k16(td, to_f16x4(yu), zero4());
+            Wp[a] = mma_k16(td, to_f16x4(yw), zero4());
         }
-        __syncthreads();
+#pragma unroll
+        for (int a = 0; a < NR; ++a)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) sm.wn[16 * a + 4 * lg + rr][col] = f16(-Wp[a][rr]);
+        lds_barrier();
 
         // ---- stage 4 (sequential part): Delta, O, next state
         // S as fp16 B operands over the key index: slot e < 4 -> tile 2kk row 4lg+e,
         // slot e >= 4 -> tile 2kk+1 row 4lg+e-4.  A operands read the matching k indices.
-        f16x8 bS[F::KD][F::NJ];
+        f16x8 bS[F::KD];
 #pragma unroll
         for (int kk = 0; kk < F::KD; ++kk)
 #pragma unroll
-            for (int jt = 0; jt < F::NJ; ++jt)
+            for (int e = 0; e < 4; ++e) {
+                bS[kk][e] = f16(S[2 * kk][e]);
+                bS[kk][4 + e] = f16(S[2 * kk + 1][e]);
+            }
+        // Delta = U + (-W) S   (accumulated onto U);  O = diag(e^gamma) Q S
+        f32x4 O[NR];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    bS[kk][jt][e] = f16(S[2 * kk][jt][e]);
-                    bS[kk][jt][4 + e] = f16(S[2 * kk + 1][jt][e]);
-                }
-        // Delta = U + (-W) S   (accumulated onto U)
-#pragma unroll
-        for (int rt = 0; rt < F::NR; ++rt)
+        for (int rt = 0; rt < NR; ++rt) {
+            O[rt] = zero4();
 #pragma unroll
             for (int kk = 0; kk < F::KD; ++kk) {
                 const f16 *wr = &sm.wn[16 * rt + li][32 * kk + 4 * lg];
-                const f16x8 a = cat(*reinterpret_cast<const f16x4 *>(wr),
-                                    *reinterpret_cast<const f16x4 *>(wr + 16));
-#pragma unroll
-                for (int jt = 0; jt < F::NJ; ++jt) U[rt][jt] = mma16(a, bS[kk][jt], U[rt][jt]);
-            }
-        // O = diag(exp(gamma)) Q S + P Delta
-        f32x4 O[F::NR][F::NJ];
-#pragma unroll
-        for (int rt = 0; rt < F::NR; ++rt) {
-#pragma unroll
-            for (int jt = 0; jt < F::NJ; ++jt) O[rt][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < F::KD; ++kk) {
                 const f16 *qr = &sm.q[16 * rt + li][32 * kk + 4 * lg];
-                const f16x8 a = cat(*reinterpret_cast<const f16x4 *>(qr),
-                                    *reinterpret_cast<const f16x4 *>(qr + 16));
-#pragma unroll
-                for (int jt = 0; jt < F::NJ; ++jt) O[rt][jt] = mma16(a, bS[kk][jt], O[rt][jt]);
+                const f16x8 aw = cat(*reinterpret_cast<const f16x4 *>(wr),
+                                     *reinterpret_cast<const f16x4 *>(wr + 16));
+                const f16x8 aq = cat(*reinterpret_cast<const f16x4 *>(qr),
+                                     *reinterpret_cast<const f16x4 *>(qr + 16));
+                U[rt] = mma_k32(aw, bS[kk], U[rt]);
+                O[rt] = mma_k32(aq, bS[kk], O[rt]);
             }
 #pragma unroll
-            for (int jt = 0; jt < F::NJ; ++jt)
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) O[rt][jt][rr] *= sm.Gam[16 * rt + 4 * lg + rr];
+            for (int rr = 0; rr < 4; ++rr) O[rt][rr] *= sm.Gam[16 * rt + 4 * lg + rr];
         }
         // Delta as fp16 B operands over the chunk index, plain and decayed to the chunk end
-        f16x8 bD[F::KC][F::NJ], bDs[F::KC][F::NJ];
+        f16x8 bD[F::KC], bDs[F::KC];
 #pragma unroll
         for (int kk = 0; kk < F::KC; ++kk)
 #pragma unroll
-            for (int jt = 0; jt < F::NJ; ++jt)
+            for (int e = 0; e < 4; ++e) {
+                const int s0i = 32 * kk + 4 * lg + e, s1i = s0i + 16;
+                const float d0 = U[2 * kk][e], d1 = U[2 * kk + 1][e];
+                bD[kk][e] = f16(d0);
+                bD[kk][4 + e] = f16(d1);
+                bDs[kk][e] = f16(d0 * sm.dec[s0i]);
+                bDs[kk][4 + e] = f16(d1 * sm.dec[s1i]);
+            }
+        // O += P Delta, staged for the store at the top of the next chunk
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int s0i = 32 * kk + 4 * lg + e, s1i = s0i + 16;
-                    const float d0 = U[2 * kk][jt][e], d1 = U[2 * kk + 1][jt][e];
-                    bD[kk][jt][e] = f16(d0);
-                    bD[kk][jt][4 + e] = f16(d1);
-                    bDs[kk][jt][e] = f16(d0 * sm.dec[s0i]);
-                    bDs[kk][jt][4 + e] = f16(d1 * sm.dec[s1i]);
-                }
-#pragma unroll
-        for (int rt = 0; rt < F::NR; ++rt)
+        for (int rt = 0; rt < NR; ++rt) {
 #pragma unroll
             for (int kk = 0; kk < F::KC; ++kk)
                 if (32 * kk <= 16 * rt + 15) {
                     const f16 *pr = &sm.p[16 * rt + li][32 * kk + 4 * lg];
-                    const f16x8 a = cat(*reinterpret_cast<const f16x4 *>(pr),
-                                        *reinterpret_cast<const f16x4 *>(pr + 16));
-#pragma unroll
-                    for (int jt = 0; jt < F::NJ; ++jt) O[rt][jt] = mma16(a, bD[kk][jt], O[rt][jt]);
+                    O[rt] = mma_k32(cat(*reinterpret_cast<const f16x4 *>(pr),
+                                        *reinterpret_cast<const f16x4 *>(pr + 16)),
+                                    bD[kk], O[rt]);
                 }
 #pragma unroll
-        for (int rt = 0; rt < F::NR; ++rt)
-#pragma unroll
-            for (int jt = 0; jt < F::NJ; ++jt) {
-                const int col = (wave * F::NJ + jt) * 16 + li;
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int r = 16 * rt + 4 * lg + rr;
-                    if (r < Lc)
-                        store_f32(o + ((static_cast<size_t>(b) * T + t0 + r) * Hv + hv) * DV + col,
-                                  scale * O[rt][jt][rr]);
-                }
-            }
-        // S = exp(gamma_last) S + K^T diag(exp(gamma_last - gamma)) Delta
+            for (int rr = 0; rr < 4; ++rr) sm.ost[16 * rt + 4 * lg + rr][col] = scale * O[rt][rr];
+        }
+        // S = e^gamma_last S + K^T diag(e^(gamma_last - gamma)) Delta
         const float GC = sm.Gam[C - 1];
 #pragma unroll
         for (int it = 0; it < F::NI; ++it) {
-#pragma unroll
-            for (int jt = 0; jt < F::NJ; ++jt) S[it][jt] *= GC;
+            S[it] *= GC;
 #pragma unroll
             for (int kk = 0; kk < F::KC; ++kk) {
                 const f16 *kr = &sm.kt[16 * it + li][32 * kk + 4 * lg];
-                const f16x8 a = cat(*reinterpret_cast<const f16x4 *>(kr),
-                                    *reinterpret_cast<const f16x4 *>(kr + 16));
-#pragma unroll
-                for (int jt = 0; jt < F::NJ; ++jt) S[it][jt] = mma16(a, bDs[kk][jt], S[it][jt]);
+                S[it] = mma_k32(cat(*reinterpret_cast<const f16x4 *>(kr),
+                                    *reinterpret_cast<const f16x4 *>(kr + 16)),
+                                bDs[kk], S[it]);
             }
         }
     }
 
+    // ---- the last chunk's output (rows past T are not stored) and the final state
+    lds_barrier();
+    if (nchunks > 0) {
+        const int tp = (nchunks - 1) * C, L = T - tp;
+#pragma unroll
+        for (int n = 0; n < F::NO; ++n) {
+            const int idx = tid + n * NT, r = idx / (D / 4), cc = idx - r * (D / 4);
+            if (r < L) {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(&sm.ost[r][cc * 4]);
+                store4<TO>(o + ((static_cast<size_t>(b) * T + tp + r) * Hv + hv) * D + cc * 4, x);
+            }
+        }
+    }
     if (sT) {
 #pragma unroll
         for (int it = 0; it < F::NI; ++it)
 #pragma unroll
-            for (int jt = 0; jt < F::NJ; ++jt) {
-                const int col = (wave * F::NJ + jt) * 16 + li;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sT[sbase + static_cast<size_t>(16 * it + 4 * lg + r) * DV + col] = S[it][jt][r];
-            }
+            for (int r = 0; r < 4; ++r)
+                sT[sbase + static_cast<size_t>(16 * it + 4 * lg + r) * D + col] = S[it][r];
     }
 }
 
-template <int DK, int DV, int C, typename TO> hipError_t launch_typed(const PrefillArgs &a) {
-    auto kern = chunk_kernel<DK, DV, C, TO>;
-    const size_t lds = sizeof(Smem<DK, DV, C>);
+template <int D, int C, typename TO> hipError_t launch_typed(const PrefillArgs &a) {
+    auto kern = chunk_kernel<D, C, TO>;
+    const size_t lds = sizeof(Smem<D, C>);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
     const unsigned nblk = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.Hv);
-    hipLaunchKernelGGL(kern, dim3(nblk), dim3(NT), lds, a.stream,
+    hipLaunchKernelGGL(kern, dim3(nblk), dim3(Cfg<D, C>::NT), lds, a.stream,
                        static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
                        static_cast<const bf16_t *>(a.v), static_cast<const bf16_t *>(a.beta),
                        static_cast<const bf16_t *>(a.g), a.s0, static_cast<TO *>(a.o), a.sT, a.T,
@@ -473,19 +434,18 @@ template <int DK, int DV, int C, typename TO> hipError_t launch_typed(const Pref
     return hipGetLastError();
 }
 
-template <int DK, int DV, int C> hipError_t launch_out(const PrefillArgs &a) {
-    return a.out_dt == GDN_F32 ? launch_typed<DK, DV, C, float>(a)
-                               : launch_typed<DK, DV, C, bf16_t>(a);
+template <int D, int C> hipError_t launch_out(const PrefillArgs &a) {
+    return a.out_dt == GDN_F32 ? launch_typed<D, C, float>(a) : launch_typed<D, C, bf16_t>(a);
 }
 
-template <int DK, int DV> hipError_t launch_chunk(const PrefillArgs &a) {
-    return a.chunk == 64 ? launch_out<DK, DV, 64>(a) : launch_out<DK, DV, 32>(a);
+template <int D> hipError_t launch_chunk(const PrefillArgs &a) {
+    return a.chunk == 64 ? launch_out<D, 64>(a) : launch_out<D, 32>(a);
 }
 
 }  // namespace
 
 bool chunk_mfma_supports(const PrefillArgs &a) {
-    return a.in_dt == GDN_BF16 && (a.dk == 64 || a.dk == 128) && (a.dv == 64 || a.dv == 128) &&
+    return a.in_dt == GDN_BF16 && a.dk == a.dv && (a.dk == 64 || a.dk == 128) &&
            (a.chunk == 32 || a.chunk == 64);
 }
 
@@ -493,9 +453,7 @@ size_t chunk_mfma_workspace(const PrefillArgs &) { return 0; }
 
 hipError_t launch_chunk_mfma(const PrefillArgs &a) {
     if (!chunk_mfma_supports(a)) return hipErrorNotSupported;
-    if (a.dk == 128)
-        return a.dv == 128 ? launch_chunk<128, 128>(a) : launch_chunk<128, 64>(a);
-    return a.dv == 128 ? launch_chunk<64, 128>(a) : launch_chunk<64, 64>(a);
+    return a.dk == 128 ? launch_chunk<128>(a) : launch_chunk<64>(a);
 }
 
 }  // namespace gdn

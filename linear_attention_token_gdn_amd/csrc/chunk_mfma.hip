@@ -141,11 +141,16 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     // ---- the state: tile it holds rows 16it + 4lg + r of column `col`
     f32x4 S[F::NI];
     const size_t sbase = static_cast<size_t>(chain) * D * D;
+    if (s0 != nullptr) {  // one branch, so that all loads are in flight together
 #pragma unroll
-    for (int it = 0; it < F::NI; ++it)
+        for (int it = 0; it < F::NI; ++it)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            S[it][r] = s0 ? s0[sbase + static_cast<size_t>(16 * it + 4 * lg + r) * D + col] : 0.f;
+            for (int r = 0; r < 4; ++r)
+                S[it][r] = s0[sbase + static_cast<size_t>(16 * it + 4 * lg + r) * D + col];
+    } else {
+#pragma unroll
+        for (int it = 0; it < F::NI; ++it) S[it] = zero4();
+    }
 
     // ---- raw inputs of the next chunk, prefetched into registers (rows past T read as 0)
     u16x8 pq[F::NQ], pk[F::NQ], pv[F::NQ];

@@ -1,0 +1,518 @@
+// chunk_split.hip -- two-kernel chunk-parallel prefill for shapes with few (b, hv) chains.
+//
+// Same exact rewriting of Eq. (1) of the explainer page "論文解説: Qwen3.8-Next の設計"
+// (ta-paperlens.web.app, section "GDNの中身") as chunk_mfma.hip:
+//
+//   gamma = cumsum(g) within a chunk,  D_rs = exp(gamma_r - gamma_s) (s <= r)
+//   A = strictly_lower(diag(beta) (K K^T o D)),   U = (I + A)^-1 diag(beta) V,
+//   W = (I + A)^-1 diag(beta e^gamma) K,          Delta = U - W S,
+//   O = scale (diag(e^gamma) Q S + (lower(Q K^T) o D) Delta),
+//   S_next = e^gamma_last S + K^T diag(e^(gamma_last - gamma)) Delta.
+//
+// Everything that does not depend on the state S is computed by prep_kernel, fully in
+// parallel over (chunk, chain), one wavefront each; scan_kernel then walks the chunks of one
+// chain in order for one 16-column tile of the state.  This trades extra HBM traffic (the
+// per-chunk operands go through a workspace) for parallelism: a chain of T/C chunks no longer
+// waits for the per-chunk triangular solve, which is what bounds a single-pass kernel when
+// there are fewer chains than compute units.
+//
+// The workspace holds, per (chain, chunk), the scan kernel's MFMA operands already in
+// fragment order -- for every 16x16x32 A operand one 1 KiB block, lane-major, 16 bytes per
+// lane -- so each operand reaches the scan kernel's registers with one coalesced 16-byte load
+// per lane and no LDS.  The prep kernel produces them without any transpose through LDS:
+// multiplying a row fragment by a 0/1 selection matrix on the matrix cores yields the tile in
+// the accumulator (column) layout, and a product whose left factor is the transpose of an
+// accumulator-layout tile takes that tile's registers as its A operand unchanged.
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mma_f16_k32(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_bf16_k32(u16x8 a, u16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_f16_k16(f16x4 a, f16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x4 h4(f32x4 x) {
+    return f16x4{f16(x[0]), f16(x[1]), f16(x[2]), f16(x[3])};
+}
+__device__ __forceinline__ f16x8 cat(f16x4 lo, f16x4 hi) {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+template <int D, int C> struct SplitCfg {
+    static constexpr int NR = C / 16;  // 16-row blocks of a chunk
+    static constexpr int NI = D / 16;  // 16-wide tiles of a head dimension
+    static constexpr int KD = D / 32;  // 32-wide k-steps over a head dimension
+    static constexpr int KC = C / 32;  // 32-wide k-steps over the chunk
+    // fragment-ordered workspace record of one (chain, chunk), in 16-byte units per lane
+    static constexpr size_t FRAG = 64 * 16;            // one A-operand fragment: 1 KiB
+    static constexpr size_t OFF_W = 0;                 // -W         [NR][KD]
+    static constexpr size_t OFF_Q = OFF_W + NR * KD * FRAG;   // e^gamma Q  [NR][KD]
+    static constexpr size_t OFF_K = OFF_Q + NR * KD * FRAG;   // K^T dec    [NI][KC]
+    static constexpr size_t OFF_P = OFF_K + NI * KC * FRAG;   // P          [NR][KC]
+    static constexpr size_t OFF_U = OFF_P + NR * KC * FRAG;   // U          [NI][NR] x 512 B
+    static constexpr size_t REC = OFF_U + NI * NR * 64 * 8;   // bytes per (chain, chunk)
+    static_assert((D == 64 || D == 128) && (C == 32 || C == 64), "split kernel shape");
+};
+
+// ---------------------------------------------------------------------------------------
+// prep_kernel: one wavefront per (chain, chunk)
+template <int D, int C>
+__global__ void __launch_bounds__(64)
+prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
+            const bf16_t *__restrict__ v, const bf16_t *__restrict__ beta,
+            const bf16_t *__restrict__ g, unsigned char *__restrict__ ws,
+            float *__restrict__ gchunk, int T, int Hk, int Hv, int nchunks) {
+    using F = SplitCfg<D, C>;
+    constexpr int NR = F::NR, KD = F::KD;
+    __shared__ float s_gam[C], s_Gam[C], s_dec[C], s_bet[C];
+    __shared__ float s_ad[NR][16][20];          // diagonal blocks of A (fp32)
+    __shared__ __attribute__((aligned(16))) f16 s_td[NR][16][20];  // their inverses (fp16)
+
+    const int lane = threadIdx.x, li = lane & 15, lg = lane >> 4;
+    const int chain = blockIdx.x / nchunks, c = blockIdx.x - chain * nchunks;
+    const int G = Hv / Hk;
+    const int b = chain / Hv, hv = chain - b * Hv, hq = hv / G;
+    const int t0 = c * C, L = min(C, T - t0);
+    unsigned char *rec = ws + (static_cast<size_t>(chain) * nchunks + c) * F::REC;
+
+    // ---- row fragments of K, Q, V (lane: row 16a + li, columns 32kk + 8lg .. +7), bf16
+    u16x8 Kf[NR][KD], Qf[NR][KD], Vf[NR][KD];
+#pragma unroll
+    for (int a = 0; a < NR; ++a) {
+        const int r = 16 * a + li;
+        const size_t row = static_cast<size_t>(b) * T + t0 + r;
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) {
+            Kf[a][kk] = Qf[a][kk] = Vf[a][kk] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            if (r < L) {
+                const size_t oq = (row * Hk + hq) * D + 32 * kk + 8 * lg;
+                Kf[a][kk] = *reinterpret_cast<const u16x8 *>(k + oq);
+                Qf[a][kk] = *reinterpret_cast<const u16x8 *>(q + oq);
+                Vf[a][kk] = *reinterpret_cast<const u16x8 *>(v + (row * Hv + hv) * D + 32 * kk + 8 * lg);
+            }
+        }
+    }
+    // ---- gates: chunk-local inclusive cumulative sum of g (rows past T: g = beta = 0)
+    {
+        float gv = 0.f, bv = 0.f;
+        if (lane < L) {
+            const size_t gi = (static_cast<size_t>(b) * T + t0 + lane) * Hv + hv;
+            gv = bf16_to_f32(g[gi]);
+            bv = bf16_to_f32(beta[gi]);
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(gv, off);
+            if (lane >= off) gv += y;
+        }
+        const float glast = __shfl(gv, C - 1);
+        if (lane < C) {
+            s_gam[lane] = gv;
+            s_Gam[lane] = __expf(gv);
+            s_dec[lane] = __expf(glast - gv);
+            s_bet[lane] = bv;
+        }
+        if (lane == 0) gchunk[static_cast<size_t>(chain) * nchunks + c] = __expf(glast);
+    }
+    __syncthreads();
+
+    // ---- KK^T: tile (m-block cb, n-block a) in accumulator layout holds
+    //      KK^T[16a + li][16cb + 4lg + rr] (the product is symmetric), i.e. exactly the
+    //      A-operand fragment of -A_{a,cb} for the substitution below.
+    f16x4 anf[NR][NR];
+#pragma unroll
+    for (int a = 0; a < NR; ++a) {
+        const int r = 16 * a + li;
+        const float gr = s_gam[r], br = s_bet[r];
+#pragma unroll
+        for (int cb = 0; cb <= a; ++cb) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < KD; ++kk) acc = mma_bf16_k32(Kf[cb][kk], Kf[a][kk], acc);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int s = 16 * cb + 4 * lg + rr;
+                const float av = (s < r) ? br * __expf(gr - s_gam[s]) * acc[rr] : 0.f;
+                if (cb == a)
+                    s_ad[a][li][4 * lg + rr] = av;  // A[r][s] of the diagonal block
+                else
+                    anf[a][cb][rr] = f16(-av);
+            }
+        }
+    }
+    // ---- P = lower(Q K^T) o D, computed as K Q^T so that the accumulator layout is the
+    //      scan kernel's A-operand fragment: lane holds P[16rt + li][16st + 4lg + rr]
+#pragma unroll
+    for (int rt = 0; rt < NR; ++rt) {
+        const int r = 16 * rt + li;
+        const float gr = s_gam[r];
+#pragma unroll
+        for (int kc = 0; kc < F::KC; ++kc) {
+            f16x4 half[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int st = 2 * kc + h;
+                half[h] = f16x4{f16(0.f), f16(0.f), f16(0.f), f16(0.f)};
+                if (st <= rt) {
+                    f32x4 acc = zero4();
+#pragma unroll
+                    for (int kk = 0; kk < KD; ++kk) acc = mma_bf16_k32(Kf[st][kk], Qf[rt][kk], acc);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int s = 16 * st + 4 * lg + rr;
+                        half[h][rr] = f16((s <= r) ? __expf(gr - s_gam[s]) * acc[rr] : 0.f);
+                    }
+                }
+            }
+            *reinterpret_cast<f16x8 *>(rec + F::OFF_P + ((rt * F::KC + kc) * 64 + lane) * 16) =
+                cat(half[0], half[1]);
+        }
+    }
+    __syncthreads();
+
+    // ---- inverses of the 16x16 diagonal blocks of I + A: lane (li, lg) solves column li of
+    //      block lg by forward substitution in fp32
+    {
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = (r == li) ? 1.f : 0.f;
+        if (lg < NR) {
+#pragma unroll
+            for (int s = 0; s < 16; ++s)
+#pragma unroll
+                for (int r = s + 1; r < 16; ++r) x[r] -= s_ad[lg][r][s] * x[s];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s_td[lg][r][li] = f16(x[r]);
+        }
+    }
+    __syncthreads();
+    f16x4 tf[NR];  // row li, columns 4lg..4lg+3 of each inverse block
+#pragma unroll
+    for (int a = 0; a < NR; ++a) tf[a] = *reinterpret_cast<const f16x4 *>(&s_td[a][li][4 * lg]);
+
+    // ---- 0/1 selection fragment: B[k][n] = (k == 16h + n), and as an A operand
+    //      A[m][k] = (k == 16h + m); both have the same register content
+    u16x8 sel[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sel[h][e] = (8 * lg + e == 16 * h + li) ? 0x3f80 : 0;
+
+    // per-lane row scalings (rows 16a + 4lg + rr of the accumulator layout)
+    // ---- panels: for every 16-column panel p = 2kk + h of the head dimension, the blocked
+    //      forward substitution X_a = T_aa (R_a - sum_{cb<a} A_{a,cb} X_cb) for U (R =
+    //      diag(beta) V) and W (R = diag(beta e^gamma) K), plus the scan kernel's Q and K^T
+    //      operands
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk) {
+        f16x4 wq[NR][2], qq[NR][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int p = 2 * kk + h;
+            f32x4 Ux[NR], Wx[NR];
+            f16x4 kt[NR];
+#pragma unroll
+            for (int a = 0; a < NR; ++a) {
+                const f32x4 Kt = mma_bf16_k32(Kf[a][kk], sel[h], zero4());  // K[16a+4lg+rr][16p+li]
+                const f32x4 Vt = mma_bf16_k32(Vf[a][kk], sel[h], zero4());  // V[16a+4lg+rr][16p+li]
+                const f32x4 Qt = mma_bf16_k32(sel[h], Qf[a][kk], zero4());  // Q[16a+li][16p+4lg+rr]
+                f32x4 yu, yw;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int s = 16 * a + 4 * lg + rr;
+                    const float bs = s_bet[s];
+                    yu[rr] = bs * Vt[rr];
+                    yw[rr] = bs * s_Gam[s] * Kt[rr];
+                    kt[a][rr] = f16(s_dec[s] * Kt[rr]);
+                }
+                const float gq = s_Gam[16 * a + li];
+                qq[a][h] = f16x4{f16(gq * Qt[0]), f16(gq * Qt[1]), f16(gq * Qt[2]), f16(gq * Qt[3])};
+#pragma unroll
+                for (int cb = 0; cb < a; ++cb) {
+                    yu = mma_f16_k16(anf[a][cb], h4(Ux[cb]), yu);
+                    yw = mma_f16_k16(anf[a][cb], h4(Wx[cb]), yw);
+                }
+                const f16x4 yu16 = h4(yu), yw16 = h4(yw);
+                Ux[a] = mma_f16_k16(tf[a], yu16, zero4());
+                Wx[a] = mma_f16_k16(tf[a], yw16, zero4());
+                // (T_aa Y)^T = Y^T T_aa^T: lane holds W[16a + li][16p + 4lg + rr]
+                const f32x4 WxT = mma_f16_k16(yw16, tf[a], zero4());
+                wq[a][h] = f16x4{f16(-WxT[0]), f16(-WxT[1]), f16(-WxT[2]), f16(-WxT[3])};
+                // U in accumulator layout: the scan kernel's initial Delta accumulator
+                *reinterpret_cast<f16x4 *>(rec + F::OFF_U + ((p * NR + a) * 64 + lane) * 8) = h4(Ux[a]);
+            }
+            // K^T diag(dec) fragments of row tile p: slots e<4 -> block 2kc, e>=4 -> 2kc+1
+#pragma unroll
+            for (int kc = 0; kc < F::KC; ++kc)
+                *reinterpret_cast<f16x8 *>(rec + F::OFF_K + ((p * F::KC + kc) * 64 + lane) * 16) =
+                    cat(kt[2 * kc], kt[2 * kc + 1]);
+        }
+#pragma unroll
+        for (int a = 0; a < NR; ++a) {
+            *reinterpret_cast<f16x8 *>(rec + F::OFF_W + ((a * KD + kk) * 64 + lane) * 16) =
+                cat(wq[a][0], wq[a][1]);
+            *reinterpret_cast<f16x8 *>(rec + F::OFF_Q + ((a * KD + kk) * 64 + lane) * 16) =
+                cat(qq[a][0], qq[a][1]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// scan_kernel: one wavefront per (chain, 16-column tile of the state), chunks in order.
+//
+// The operands of chunk c + 1 are copied global -> LDS by the asynchronous LDS-DMA path
+// (global_load_lds_dwordx4: 1 KiB per instruction, no registers) while chunk c is computed
+// from the other LDS buffer.  The compiler does not track these copies, so the kernel waits
+// for them itself (s_waitcnt vmcnt(0) at the top of every chunk: by then the copy and the
+// previous chunk's output stores have had a whole chunk of compute to complete).
+
+// One 16-byte-per-lane asynchronous copy global -> LDS: lane i's 16 bytes land at
+// lds_dst + 16 i (lds_dst must be the same for the whole wave).  The address-space cast the
+// builtin needs only exists in the device pass.
+__device__ __forceinline__ void lds_copy16(const void *src, void *lds_dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_dst, 16, 0,
+                                     0);
+#endif
+}
+
+// Wait for every outstanding vector-memory operation of this wave; also a compiler barrier
+// for memory accesses, so no LDS read of the freshly copied buffer moves above it.
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Tiles of one chain on one XCD (blocks i and i + 8 share an XCD), so that the chain's
+// workspace records are fetched from HBM once and then served from that XCD's L2.
+__device__ __forceinline__ void scan_block_map(int blk, int nblk, int ntile, int &chain, int &tile) {
+    if ((nblk / ntile) % 8 == 0) {
+        chain = (blk & 7) + 8 * (blk / (8 * ntile));
+        tile = (blk >> 3) % ntile;
+    } else {
+        chain = blk / ntile;
+        tile = blk - chain * ntile;
+    }
+}
+
+template <int D, int C, typename TO>
+__global__ void __launch_bounds__(64)
+scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchunk,
+            const float *__restrict__ s0, TO *__restrict__ o, float *__restrict__ sT, int T,
+            int Hv, int nchunks, float scale) {
+    using F = SplitCfg<D, C>;
+    constexpr int NR = F::NR, NI = F::NI, KD = F::KD, KC = F::KC;
+    constexpr int NFRAG = static_cast<int>(F::OFF_U / F::FRAG);  // 1 KiB operand blocks
+    constexpr int NUFR = NR * 64 * 8 / 1024;                       // this tile's U, 1 KiB blocks
+    constexpr size_t BUF = F::OFF_U + NUFR * 1024;                 // per-chunk LDS buffer
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];  // 2 x BUF
+    const int lane = threadIdx.x, li = lane & 15, lg = lane >> 4;
+    int chain, jt;
+    scan_block_map(blockIdx.x, gridDim.x, NI, chain, jt);
+    const int b = chain / Hv, hv = chain - b * Hv;
+    const int col = 16 * jt + li;
+
+    f32x4 S[NI];  // rows 16it + 4lg + rr of column col
+    const size_t sbase = static_cast<size_t>(chain) * D * D;
+    if (s0 != nullptr) {  // one branch, so that all loads are in flight together
+#pragma unroll
+        for (int it = 0; it < NI; ++it)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                S[it][rr] = s0[sbase + static_cast<size_t>(16 * it + 4 * lg + rr) * D + col];
+    } else {
+#pragma unroll
+        for (int it = 0; it < NI; ++it) S[it] = zero4();
+    }
+
+    const unsigned char *rec0 = ws + static_cast<size_t>(chain) * nchunks * F::REC;
+    static_assert(NFRAG + NUFR <= 63, "one chunk's copies must fit the vector-memory counter");
+    auto copy_chunk = [&](int cc) {
+        const unsigned char *src = rec0 + static_cast<size_t>(cc) * F::REC + lane * 16;
+        unsigned char *dst = lds + (cc & 1) * BUF;
+#pragma unroll
+        for (int f = 0; f < NFRAG; ++f) lds_copy16(src + f * F::FRAG, dst + f * F::FRAG);
+#pragma unroll
+        for (int f = 0; f < NUFR; ++f)  // U of tile jt: NR fragments of 512 B, contiguous
+            lds_copy16(src + F::OFF_U + static_cast<size_t>(jt) * NR * 512 + f * 1024,
+                       dst + F::OFF_U + f * 1024);
+    };
+    auto frag = [&](const unsigned char *buf, size_t off, int idx) {
+        return *reinterpret_cast<const f16x8 *>(buf + off + (static_cast<size_t>(idx) * 64 + lane) * 16);
+    };
+
+    f32x4 Oprev[NR];
+    int tprev = 0;
+    if (nchunks > 0) copy_chunk(0);
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = c * C, L = min(C, T - t0);
+        const float GC = gchunk[static_cast<size_t>(chain) * nchunks + c];  // scalar load
+        wait_vmem_all();  // chunk c's operands are in LDS; the previous stores have drained
+        if (c + 1 < nchunks) copy_chunk(c + 1);
+        if (c > 0) {  // the previous chunk's output (always a full chunk)
+#pragma unroll
+            for (int a = 0; a < NR; ++a)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    store_f32(o + ((static_cast<size_t>(b) * T + tprev + 16 * a + 4 * lg + rr) * Hv + hv) * D + col,
+                              scale * Oprev[a][rr]);
+        }
+        const unsigned char *buf = lds + (c & 1) * BUF;
+        f16x4 uf[NR];
+#pragma unroll
+        for (int a = 0; a < NR; ++a)
+            uf[a] = *reinterpret_cast<const f16x4 *>(buf + F::OFF_U + (a * 64 + lane) * 8);
+
+        // S as fp16 B operands over the key index (slots: tile 2kk rows, then tile 2kk+1 rows)
+        f16x8 bS[KD];
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) bS[kk] = cat(h4(S[2 * kk]), h4(S[2 * kk + 1]));
+        // operands of the first products, read from LDS up front so the reads overlap
+        f16x8 wf[NR][KD], qf[NR][KD];
+#pragma unroll
+        for (int a = 0; a < NR; ++a)
+#pragma unroll
+            for (int kk = 0; kk < KD; ++kk) {
+                wf[a][kk] = frag(buf, F::OFF_W, a * KD + kk);
+                qf[a][kk] = frag(buf, F::OFF_Q, a * KD + kk);
+            }
+        // Delta = U + (-W) S ;  O = (e^gamma Q) S
+        f32x4 Dl[NR], O[NR];
+#pragma unroll
+        for (int a = 0; a < NR; ++a) {
+            Dl[a] = f32x4{float(uf[a][0]), float(uf[a][1]), float(uf[a][2]), float(uf[a][3])};
+            O[a] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < KD; ++kk) {
+                Dl[a] = mma_f16_k32(wf[a][kk], bS[kk], Dl[a]);
+                O[a] = mma_f16_k32(qf[a][kk], bS[kk], O[a]);
+            }
+        }
+        f16x8 kf[NI][KC], pf[NR][KC];
+#pragma unroll
+        for (int it = 0; it < NI; ++it)
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) kf[it][kc] = frag(buf, F::OFF_K, it * KC + kc);
+#pragma unroll
+        for (int a = 0; a < NR; ++a)
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) pf[a][kc] = frag(buf, F::OFF_P, a * KC + kc);
+        f16x8 bD[KC];
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) bD[kc] = cat(h4(Dl[2 * kc]), h4(Dl[2 * kc + 1]));
+        // S = e^gamma_last S + (K^T dec) Delta
+#pragma unroll
+        for (int it = 0; it < NI; ++it) {
+            S[it] *= GC;
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) S[it] = mma_f16_k32(kf[it][kc], bD[kc], S[it]);
+        }
+        // O += P Delta
+#pragma unroll
+        for (int a = 0; a < NR; ++a)
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc)
+                if (32 * kc <= 16 * a + 15) O[a] = mma_f16_k32(pf[a][kc], bD[kc], O[a]);
+        if (L == C) {
+#pragma unroll
+            for (int a = 0; a < NR; ++a) Oprev[a] = O[a];
+            tprev = t0;
+        } else {  // the last, partial chunk: store now, rows past T are not stored
+#pragma unroll
+            for (int a = 0; a < NR; ++a)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int r = 16 * a + 4 * lg + rr;
+                    if (r < L)
+                        store_f32(o + ((static_cast<size_t>(b) * T + t0 + r) * Hv + hv) * D + col,
+                                  scale * O[a][rr]);
+                }
+        }
+    }
+    if (nchunks > 0 && T % C == 0) {  // the last chunk was full: its output is still pending
+#pragma unroll
+        for (int a = 0; a < NR; ++a)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                store_f32(o + ((static_cast<size_t>(b) * T + tprev + 16 * a + 4 * lg + rr) * Hv + hv) * D + col,
+                          scale * Oprev[a][rr]);
+    }
+    if (sT) {
+#pragma unroll
+        for (int it = 0; it < NI; ++it)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                sT[sbase + static_cast<size_t>(16 * it + 4 * lg + rr) * D + col] = S[it][rr];
+    }
+}
+
+template <int D, int C> size_t split_ws_bytes(int B, int T, int Hv) {
+    const size_t nch = static_cast<size_t>((T + C - 1) / C);
+    const size_t chains = static_cast<size_t>(B) * Hv;
+    return chains * nch * SplitCfg<D, C>::REC + chains * nch * sizeof(float) + 256;
+}
+
+template <int D, int C, typename TO> hipError_t launch_split_typed(const PrefillArgs &a) {
+    const int nch = (a.T + C - 1) / C;
+    const size_t chains = static_cast<size_t>(a.B) * a.Hv;
+    unsigned char *ws = static_cast<unsigned char *>(a.ws);
+    float *gch = reinterpret_cast<float *>(ws + chains * nch * SplitCfg<D, C>::REC);
+    hipLaunchKernelGGL((prep_kernel<D, C>), dim3(static_cast<unsigned>(chains * nch)), dim3(64), 0,
+                       a.stream, static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
+                       static_cast<const bf16_t *>(a.v), static_cast<const bf16_t *>(a.beta),
+                       static_cast<const bf16_t *>(a.g), ws, gch, a.T, a.Hk, a.Hv, nch);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    auto scan = scan_kernel<D, C, TO>;
+    const int lds = static_cast<int>(2 * (SplitCfg<D, C>::OFF_U + (C / 16) * 512));
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(scan),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(scan, dim3(static_cast<unsigned>(chains * (D / 16))), dim3(64),
+                       static_cast<size_t>(lds), a.stream, ws, gch, a.s0, static_cast<TO *>(a.o),
+                       a.sT, a.T, a.Hv, nch, a.scale);
+    return hipGetLastError();
+}
+
+template <int D, int C> hipError_t launch_split_out(const PrefillArgs &a) {
+    return a.out_dt == GDN_F32 ? launch_split_typed<D, C, float>(a)
+                               : launch_split_typed<D, C, bf16_t>(a);
+}
+
+}  // namespace
+
+bool chunk_split_supports(const PrefillArgs &a) {
+    return a.in_dt == GDN_BF16 && a.dk == a.dv && (a.dk == 64 || a.dk == 128) &&
+           (a.chunk == 32 || a.chunk == 64);
+}
+
+size_t chunk_split_workspace(const PrefillArgs &a) {
+    if (!chunk_split_supports(a)) return 0;
+    if (a.dk == 128)
+        return a.chunk == 64 ? split_ws_bytes<128, 64>(a.B, a.T, a.Hv)
+                             : split_ws_bytes<128, 32>(a.B, a.T, a.Hv);
+    return a.chunk == 64 ? split_ws_bytes<64, 64>(a.B, a.T, a.Hv)
+                         : split_ws_bytes<64, 32>(a.B, a.T, a.Hv);
+}
+
+hipError_t launch_chunk_split(const PrefillArgs &a) {
+    if (!chunk_split_supports(a)) return hipErrorNotSupported;
+    if (a.dk == 128)
+        return a.chunk == 64 ? launch_split_out<128, 64>(a) : launch_split_out<128, 32>(a);
+    return a.chunk == 64 ? launch_split_out<64, 64>(a) : launch_split_out<64, 32>(a);
+}
+
+}  // namespace gdn

@@ -22,11 +22,25 @@ bool overlap(const void *p, size_t n, const void *r, size_t m) {
     return a < b + m && b < a + n;
 }
 
-// "variant" override for A/B measurements: GDN_FORCE_VARIANT=recurrent routes bf16 prefill
-// to the token-by-token kernel.
-bool force_recurrent() {
-    const char *s = getenv("GDN_FORCE_VARIANT");
-    return s != nullptr && strcmp(s, "recurrent") == 0;
+// Prefill variants.  GDN_FORCE_VARIANT=recurrent|fused|split pins one for A/B measurements
+// (a variant that does not support the sizes falls back to the default choice).
+enum class Variant { Recurrent, Fused, Split };
+
+// Below this many (b, hv) chains the single-pass kernel leaves most compute units idle and
+// the two-kernel form (parallel over chunks) is used.
+constexpr long kSplitBelowChains = 128;
+
+Variant choose_variant(const gdn::PrefillArgs &a) {
+    const char *env = getenv("GDN_FORCE_VARIANT");
+    if (env != nullptr) {
+        if (strcmp(env, "recurrent") == 0) return Variant::Recurrent;
+        if (strcmp(env, "fused") == 0 && gdn::chunk_mfma_supports(a)) return Variant::Fused;
+        if (strcmp(env, "split") == 0 && gdn::chunk_split_supports(a)) return Variant::Split;
+    }
+    const long chains = static_cast<long>(a.B) * a.Hv;
+    if (gdn::chunk_split_supports(a) && chains < kSplitBelowChains) return Variant::Split;
+    if (gdn::chunk_mfma_supports(a)) return Variant::Fused;
+    return Variant::Recurrent;
 }
 
 }  // namespace
@@ -74,9 +88,6 @@ static gdn_status_t check_prefill(const gdn::PrefillArgs &a) {
     return GDN_OK;
 }
 
-static bool use_chunk_kernel(const gdn::PrefillArgs &a) {
-    return a.in_dt == GDN_BF16 && !force_recurrent() && gdn::chunk_mfma_supports(a);
-}
 
 size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
                                     gdn_dtype_t in_dtype) {
@@ -86,8 +97,12 @@ size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv
     if (B < 0 || T < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk != 0 || !dim_supported(dk) ||
         !dim_supported(dv) || (chunk != 16 && chunk != 32 && chunk != 64) || !dtype_known(in_dtype))
         return 0;
-    if (B == 0 || T == 0 || !use_chunk_kernel(a)) return 0;
-    return gdn::chunk_mfma_workspace(a);
+    if (B == 0 || T == 0) return 0;
+    switch (choose_variant(a)) {
+    case Variant::Split: return gdn::chunk_split_workspace(a);
+    case Variant::Fused: return gdn::chunk_mfma_workspace(a);
+    default: return 0;
+    }
 }
 
 gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v, const void *beta,
@@ -112,15 +127,15 @@ gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v, const vo
                    ? GDN_OK
                    : GDN_ERR_HIP;
     }
-    hipError_t e;
-    if (use_chunk_kernel(a)) {
-        const size_t need = gdn::chunk_mfma_workspace(a);
-        if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-            return GDN_ERR_INVALID_ARG;
-        e = gdn::launch_chunk_mfma(a);
-    } else {
-        e = gdn::launch_recurrent(a);
-    }
+    const Variant var = choose_variant(a);
+    const size_t need = var == Variant::Split   ? gdn::chunk_split_workspace(a)
+                        : var == Variant::Fused ? gdn::chunk_mfma_workspace(a)
+                                                : 0;
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GDN_ERR_INVALID_ARG;
+    if (need > 0 && !aligned(workspace, 256)) return GDN_ERR_INVALID_ARG;
+    hipError_t e = var == Variant::Split   ? gdn::launch_chunk_split(a)
+                   : var == Variant::Fused ? gdn::launch_chunk_mfma(a)
+                                           : gdn::launch_recurrent(a);
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 

@@ -42,6 +42,12 @@ bool chunk_mfma_supports(const PrefillArgs &a);
 size_t chunk_mfma_workspace(const PrefillArgs &a);
 hipError_t launch_chunk_mfma(const PrefillArgs &a);
 
+// Two-kernel chunk-parallel form (a fully parallel prep kernel and a per-chain scan kernel
+// through a workspace) for shapes with fewer chains than compute units.
+bool chunk_split_supports(const PrefillArgs &a);
+size_t chunk_split_workspace(const PrefillArgs &a);
+hipError_t launch_chunk_split(const PrefillArgs &a);
+
 // One streaming pass over the decode state.
 hipError_t launch_decode(const DecodeArgs &a);
 

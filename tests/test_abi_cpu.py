@@ -45,6 +45,13 @@ def test_version_and_status_strings(lib):
     assert gdn.gdn_status_string(99) == "GDN_ERR_UNKNOWN"
 
 
+def test_workspace_size_of_the_chunk_kernels(lib):
+    # few chains: the prep + scan form needs a workspace; one float32 path needs none
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16) > 16 * 64 * 65536
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 64, 2, 2, 16, 16, 16, gdn.GDN_F32) == 0
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 0, 2, 2, 128, 128, 64, gdn.GDN_BF16) == 0
+
+
 def test_workspace_size_rejects_bad_sizes(lib):
     assert gdn.gdn_chunk_fwd_workspace_size(1, 64, 2, 3, 16, 16, 16, gdn.GDN_BF16) == 0
     assert gdn.gdn_chunk_fwd_workspace_size(1, 64, 2, 2, 48, 16, 16, gdn.GDN_BF16) == 0

@@ -181,3 +181,58 @@ def test_decode_matches_prefill_path():
     M = np.abs(op).max()
     assert np.abs(od - op).max() <= 2e-3 * M
     assert np.abs(Sd - Sp).max() <= 2e-3 * np.abs(Sp).max()
+
+
+# ------------------------------------------------------------------ chunk-parallel variants
+@pytest.mark.parametrize("variant", ["fused", "split"])
+@pytest.mark.parametrize("d,chunk", [(128, 64), (128, 32), (64, 64), (64, 32)])
+def test_chunk_variants(variant, d, chunk, monkeypatch):
+    """Both chunk-parallel kernels (single pass; prep + scan through a workspace) against the
+    oracle, with grouped heads, an initial state, a scale and a ragged last chunk."""
+    monkeypatch.setenv("GDN_FORCE_VARIANT", variant)
+    inp = make_inputs(2, 157, 2, 4, d, d, dtype="bf16", s0_std=0.02, seed=500 + d + chunk)
+    check_prefill(inp, chunk, scale=0.8, tag="%s d%d c%d" % (variant, d, chunk))
+
+
+def test_variants_agree_and_are_deterministic(monkeypatch):
+    inp = make_inputs(1, 300, 1, 2, 128, 128, dtype="bf16", s0_std=0.02, seed=510)
+    res = {}
+    for variant in ("fused", "split"):
+        monkeypatch.setenv("GDN_FORCE_VARIANT", variant)
+        a = run_prefill(inp, 64)
+        b = run_prefill(inp, 64)
+        np.testing.assert_array_equal(a[0], b[0])
+        np.testing.assert_array_equal(a[1], b[1])
+        res[variant] = a
+    M = np.abs(res["fused"][0]).max()
+    assert np.abs(res["fused"][0] - res["split"][0]).max() <= 2e-3 * M
+
+
+# ------------------------------------------------------------------ the workloads, full size
+def _sampled_config_check(idx, nsample):
+    """Run a prefill workload at its full size through the default dispatch; compare every
+    output and the final state of `nsample` sampled (b, hv) chains with the oracle."""
+    c = CONFIGS[idx]
+    inp = config_inputs(idx)
+    o, sT = run_prefill(inp, c["chunk"])
+    nch = c["B"] * c["Hv"]
+    rng = np.random.Generator(np.random.PCG64(1000 + idx))
+    chains = np.arange(nch) if nsample >= nch else np.sort(rng.choice(nch, nsample, replace=False))
+    ro, rS = oracle_prefill(inp, chains=chains, use_init=inp.s0 is not None)
+    b, h = chains // c["Hv"], chains % c["Hv"]
+    e1 = check(o[b, :, h], ro, "bf16", c["name"] + " o")
+    e2 = check(sT[b, h], rS, "bf16", c["name"] + " final state")
+    print("%s: %d chains checked, o err %.2e (max %.2e), S err %.2e (max %.2e)"
+          % (c["name"], len(chains), e1[0], e1[1], e2[0], e2[1]))
+
+
+def test_config1_full():
+    _sampled_config_check(1, 16)
+
+
+def test_config2_sampled():
+    _sampled_config_check(2, 12)
+
+
+def test_config3_sampled():
+    _sampled_config_check(3, 2)

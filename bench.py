@@ -2,10 +2,10 @@
 """Benchmark of the Gated DeltaNet hot path on one MI355X.
 
 One step = one gdn_chunk_fwd over the prefill workload (default: B=1, T=4096, 16 heads,
-dk=dv=128, chunk 64, bf16 inputs, fp32 output and state) followed by one gdn_decode_step over
-the decode workload (B=256 sequences, 32 heads, dk=dv=128, fp32 state [256,32,128,128]
-updated in place; the 64 pre-drawn decode tokens are used in turn).  Inputs are seeded
-synthetic tensors (gdn_inputs.py), resident in HBM before the timed region.
+dk=dv=128, chunk 64, bf16 inputs, fp32 output and state) followed by the decode workload: 64
+consecutive gdn_decode_step calls (B=256 sequences, 32 heads, dk=dv=128, fp32 state
+[256,32,128,128] updated in place, one pre-drawn token per call).  Inputs are seeded synthetic
+tensors (gdn_inputs.py), resident in HBM before the timed region.
 
 Prints ONE JSON line:  value = prefill tokens/s (B*T / mean prefill launch time), with the
 decode state GB/s, both kernels' rooflines (algorithmic bytes / measured launch time,
@@ -28,8 +28,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, vendor figure
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
-    "prefill": os.path.join(ROOT, "linear_attention_token_gdn_amd", "csrc", "chunk_mfma.hip"),
-    "decode": os.path.join(ROOT, "linear_attention_token_gdn_amd", "csrc", "decode.hip"),
+    "prefill": [os.path.join(ROOT, "linear_attention_token_gdn_amd", "csrc", n)
+                for n in ("chunk_split.hip", "chunk_mfma.hip")],
+    "decode": [os.path.join(ROOT, "linear_attention_token_gdn_amd", "csrc", "decode.hip")],
 }
 
 
@@ -61,9 +62,12 @@ def decode_bytes(B, Hk, Hv, dk, dv, in_bytes=2, out_bytes=4):
     return state, state + other
 
 
-def source_hash(path):
-    with open(path, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel):
@@ -127,12 +131,15 @@ def _cpu_model():
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--prefill-config", type=int, default=1, choices=[1, 2, 3],
                     help="prefill workload: 1 = B1 T4096 H16 (default), 2 = B8 T8192 Hk16/Hv32, "
                          "3 = B1 T262144 H16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (known bytes, "
+                         "to scale the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--no-decode", action="store_true")
     args = ap.parse_args()
 
@@ -146,6 +153,16 @@ def main():
     from gdn_inputs import CONFIGS, config_inputs
 
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        nbytes = 1 << 30
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": nbytes, "calibrate_copy_bytes_written": nbytes,
+                          "launches": 5}))
+        return 0
     gdn.load_library()
 
     pc = CONFIGS[args.prefill_config]
@@ -173,14 +190,14 @@ def main():
         gdn.chunk_fwd(pt["q"], pt["k"], pt["v"], pt["beta"], pt["g"], initial_state=pt["s0"],
                       chunk=C, o=o, final_state=fs)
 
-    def decode(s):
-        i = s % nsteps_dec
-        gdn.decode_step(dq[i], dk_[i], dv_[i], db[i], dg[i], state, o=do)
+    def decode_all():
+        for i in range(nsteps_dec):
+            gdn.decode_step(dq[i], dk_[i], dv_[i], db[i], dg[i], state, o=do)
 
     for s in range(args.warmup):
         prefill()
         if not args.no_decode:
-            decode(s)
+            decode_all()
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -194,7 +211,7 @@ def main():
         e[1].record(stream)
         if not args.no_decode:
             e[2].record(stream)
-            decode(args.warmup + s)
+            decode_all()
             e[3].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
@@ -205,9 +222,12 @@ def main():
     pbytes = prefill_bytes(B, T, Hk, Hv, dk, dv, has_s0=pre_inp.s0 is not None)
     pre_tflops = flops / (pre_mean * 1e-3) / 1e12
     pre_gbs = pbytes / (pre_mean * 1e-3) / 1e9
+    plan = gdn.gdn_chunk_fwd_plan(B, T, Hk, Hv, dk, dv, C, gdn.GDN_BF16)
+    pre_kernels = {"split": "prep_kernel<%d,%d> + scan_kernel<%d,%d,float>" % (dk, C, dk, C),
+                   "fused": "chunk_kernel<%d,%d,float>" % (dk, C)}.get(plan, plan)
     rooflines = {
         "prefill": {
-            "kernel": "chunk_kernel<128,128,64,float>", "bound": "hbm",
+            "kernel": pre_kernels, "plan": plan, "bound": "hbm",
             "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(pre_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("prefill"),
             "algorithmic_bytes": pbytes, "algorithmic_flops": flops,
@@ -219,13 +239,13 @@ def main():
     dom = "prefill"
     result_decode = None
     if not args.no_decode:
-        dec_ms = [e[2].elapsed_time(e[3]) for e in ev]
+        dec_ms = [e[2].elapsed_time(e[3]) / nsteps_dec for e in ev]  # per decode launch
         dec_mean = sum(dec_ms) / len(dec_ms)
         sbytes, tbytes = decode_bytes(dc["B"], dc["Hk"], dc["Hv"], dc["dk"], dc["dv"])
         st_gbs = sbytes / (dec_mean * 1e-3) / 1e9
         tot_gbs = tbytes / (dec_mean * 1e-3) / 1e9
         rooflines["decode"] = {
-            "kernel": "decode_kernel<128,128,bf16,float>", "bound": "hbm",
+            "kernel": "decode_kernel<%d,%d,bf16,float>" % (dc["dk"], dc["dv"]), "bound": "hbm",
             "achieved": round(tot_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(tot_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode"),
             "algorithmic_bytes": tbytes, "mean_launch_ms": round(dec_mean, 4),
@@ -233,9 +253,9 @@ def main():
         result_decode = {
             "state_GBps": round(st_gbs, 1), "frac_hbm_peak": round(st_gbs / HBM_PEAK_GBS, 4),
             "us_per_step": round(dec_mean * 1e3, 2), "tokens_per_s": round(dc["B"] / (dec_mean * 1e-3), 1),
-            "state_bytes_per_step": sbytes,
+            "state_bytes_per_step": sbytes, "steps_per_bench_step": nsteps_dec,
         }
-        if dec_mean > pre_mean:
+        if dec_mean * nsteps_dec > pre_mean:
             dom = "decode"
 
     line = {

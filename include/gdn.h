@@ -13,9 +13,10 @@
  * expected to be L2-normalised by the caller (the library does not renormalise).
  *
  * Conventions shared by every entry point
- *   - All tensors are dense, row-major (innermost index last), in device memory, and
- *     16-byte aligned.  B = batch, T = tokens, Hk = q/k heads, Hv = value heads,
- *     dk = key/query head size, dv = value head size.
+ *   - All tensors are dense, row-major (innermost index last), in device memory.
+ *     Alignment: states 16 bytes; prefill q, k, v, o 16 bytes; beta, g and all decode
+ *     inputs/outputs one element; the workspace 256 bytes.  B = batch, T = tokens,
+ *     Hk = q/k heads, Hv = value heads, dk = key/query head size, dv = value head size.
  *   - Grouped heads: Hv must be a multiple of Hk; value head hv reads q/k head
  *     hv / (Hv/Hk) (groups of consecutive value heads share one q/k head).  beta and
  *     g are per value head.
@@ -67,6 +68,14 @@ const char *gdn_status_string(gdn_status_t status);
  */
 size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
                                     gdn_dtype_t in_dtype);
+
+/*
+ * Which kernels gdn_chunk_fwd runs for these sizes: "split" (a prep kernel parallel over
+ * chunks, then a scan kernel per chain, through the workspace), "fused" (one kernel per
+ * chain), "recurrent" (token by token; the fp32 path) or "invalid".  Static string.
+ */
+const char *gdn_chunk_fwd_plan(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
+                               gdn_dtype_t in_dtype);
 
 /*
  * Prefill: run Eq. (1) over T tokens for every (b, hv) chain, chunk by chunk.

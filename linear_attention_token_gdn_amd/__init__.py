@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libgdn.so")
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
 GDN_F32, GDN_BF16 = 0, 1
 EXPORTED_SYMBOLS = ("gdn_abi_version", "gdn_status_string", "gdn_chunk_fwd_workspace_size",
-                    "gdn_chunk_fwd", "gdn_decode_step")
+                    "gdn_chunk_fwd_plan", "gdn_chunk_fwd", "gdn_decode_step")
 
 _lib = None
 
@@ -51,6 +51,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_chunk_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i, i]
     lib.gdn_chunk_fwd_workspace_size.restype = sz
+    lib.gdn_chunk_fwd_plan.argtypes = [i, i, i, i, i, i, i, i]
+    lib.gdn_chunk_fwd_plan.restype = ctypes.c_char_p
     lib.gdn_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i,
                                   vp, sz, vp]
     lib.gdn_chunk_fwd.restype = i
@@ -74,6 +76,10 @@ status_string = gdn_status_string
 
 def gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, chunk, in_dtype) -> int:
     return int(load_library().gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, chunk, in_dtype))
+
+
+def gdn_chunk_fwd_plan(B, T, Hk, Hv, dk, dv, chunk, in_dtype) -> str:
+    return load_library().gdn_chunk_fwd_plan(B, T, Hk, Hv, dk, dv, chunk, in_dtype).decode()
 
 
 def gdn_chunk_fwd(q, k, v, beta, g, initial_state, o, final_state, B, T, Hk, Hv, dk, dv, chunk,

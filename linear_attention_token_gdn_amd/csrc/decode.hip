@@ -11,8 +11,10 @@
 //
 // One workgroup per (b, hv) state.  Thread (rg, cg) holds float4 column group cg of the rows
 // rg, rg + R, rg + 2R, ... (R row groups): every load and store instruction of a wavefront
-// covers whole 512-byte rows, and the state goes through the non-temporal path because it is
-// touched exactly once per step.
+// covers whole 512-byte rows.  The state is read with ordinary loads and written with
+// non-temporal stores (it is not read again in this step); on MI355X this pairing streams
+// ~6.2 TB/s for the 1 GiB read+write of a 256 x 32 x 128 x 128 state, as fast as a plain
+// read-modify-write kernel, while non-temporal loads cost ~15%.
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -53,7 +55,7 @@ decode_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__re
     f32x4 s[Sh::RPT];
 #pragma unroll
     for (int m = 0; m < Sh::RPT; ++m)
-        s[m] = __builtin_nontemporal_load(&S[(rg + Sh::R * m) * Sh::CG + cg]);
+        s[m] = S[(rg + Sh::R * m) * Sh::CG + cg];
     float kr[Sh::RPT], qr[Sh::RPT];
 #pragma unroll
     for (int m = 0; m < Sh::RPT; ++m) {

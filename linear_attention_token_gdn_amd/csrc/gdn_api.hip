@@ -89,6 +89,21 @@ static gdn_status_t check_prefill(const gdn::PrefillArgs &a) {
 }
 
 
+const char *gdn_chunk_fwd_plan(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
+                               gdn_dtype_t in_dtype) {
+    gdn::PrefillArgs a = {};
+    a.B = B; a.T = T; a.Hk = Hk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.chunk = chunk;
+    a.in_dt = in_dtype; a.out_dt = GDN_F32;
+    if (B < 0 || T < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk != 0 || !dim_supported(dk) ||
+        !dim_supported(dv) || (chunk != 16 && chunk != 32 && chunk != 64) || !dtype_known(in_dtype))
+        return "invalid";
+    switch (choose_variant(a)) {
+    case Variant::Split: return "split";
+    case Variant::Fused: return "fused";
+    default: return "recurrent";
+    }
+}
+
 size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
                                     gdn_dtype_t in_dtype) {
     gdn::PrefillArgs a = {};

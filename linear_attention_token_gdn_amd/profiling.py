@@ -1,0 +1,143 @@
+"""Summaries of rocprofv3 output for the profiles/ directory.
+
+    python -m linear_attention_token_gdn_amd.profiling trace  <kernel_trace.csv> "<command>"
+    python -m linear_attention_token_gdn_amd.profiling traffic <fetch_dir> <write_dir> \
+           <copy_fetch_dir> <copy_write_dir> "<command>"
+
+`trace` prints a markdown table of per-kernel launch counts and durations (from a
+`rocprofv3 --kernel-trace` CSV).  `traffic` turns two counter passes over the benchmark
+(`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`) and the same two passes over a plain 1 GiB copy
+into HBM bytes per launch: each counter is scaled by (known copy bytes / what the counter read
+for the copy).  It prints markdown and writes profiles/traffic.json, which bench.py reports
+while the kernel sources are unchanged.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SOURCES = {
+    "prefill": [os.path.join(ROOT, "linear_attention_token_gdn_amd", "csrc", n)
+                for n in ("chunk_split.hip", "chunk_mfma.hip")],
+    "decode": [os.path.join(ROOT, "linear_attention_token_gdn_amd", "csrc", "decode.hip")],
+}
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    """Kernel name without namespaces, return type and parameter list."""
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "", 1)
+    depth, cut = 0, len(name)
+    for i, ch in enumerate(name):  # first '(' outside template brackets
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            cut = i
+            break
+    return name[:cut].replace("gdn::", "").replace("unsigned short", "bf16").strip()
+
+
+def read_trace(path):
+    rows = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            rows.append((short_name(r["Kernel_Name"]), int(r["Grid_Size_X"]),
+                         (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    return rows
+
+
+def trace_table(path, command):
+    groups = {}
+    for name, grid, us in read_trace(path):
+        groups.setdefault((name, grid), []).append(us)
+    out = ["Command: `%s`" % command, "",
+           "| kernel | grid (threads) | launches | mean us | median us | min us |",
+           "|---|---|---|---|---|---|"]
+    for (name, grid), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        out.append("| `%s` | %d | %d | %.1f | %.1f | %.1f |" % (
+            name, grid, len(v), statistics.mean(v), statistics.median(v), min(v)))
+    return "\n".join(out)
+
+
+def read_counter(dirpath, counter):
+    """Per-dispatch counter values (KiB as rocprofv3 reports them) keyed by kernel name."""
+    files = glob.glob(os.path.join(dirpath, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError("no counter_collection.csv under %s" % dirpath)
+    per = {}
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            if r.get("Counter_Name") != counter:
+                continue
+            key = (short_name(r["Kernel_Name"]), r["Dispatch_Id"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    by_kernel = {}
+    for (name, _), val in per.items():
+        by_kernel.setdefault(name, []).append(val)
+    return by_kernel
+
+
+def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, command):
+    fetch, write = read_counter(fetch_dir, "FETCH_SIZE"), read_counter(write_dir, "WRITE_SIZE")
+    cf, cw = read_counter(cfetch_dir, "FETCH_SIZE"), read_counter(cwrite_dir, "WRITE_SIZE")
+    copy_f = max(statistics.median(v) for v in cf.values())
+    copy_w = max(statistics.median(v) for v in cw.values())
+    ref = (1 << 30)
+    sf, sw = ref / (copy_f * 1024.0), ref / (copy_w * 1024.0)
+    out = ["Command: `%s`" % command, "",
+           "Copy calibration (1 GiB read + 1 GiB written): FETCH_SIZE %.0f KiB, WRITE_SIZE %.0f KiB "
+           "per launch -> scale %.4f / %.4f" % (copy_f, copy_w, sf, sw), "",
+           "| kernel | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB |",
+           "|---|---|---|---|---|---|"]
+    res = {}
+    for name in sorted(set(fetch) | set(write)):
+        if "gdn" not in name and "kernel" not in name:
+            continue
+        f = statistics.median(fetch.get(name, [0.0]))
+        w = statistics.median(write.get(name, [0.0]))
+        rd, wr = f * 1024 * sf, w * 1024 * sw
+        res[name] = (rd, wr)
+        out.append("| `%s` | %d | %.0f | %.0f | %.1f | %.1f |" % (
+            name, len(fetch.get(name, [])), f, w, rd / 1e6, wr / 1e6))
+    rec = {"copy_scale_fetch": sf, "copy_scale_write": sw, "command": command}
+    pre = [n for n in res if n.startswith(("prep_kernel", "scan_kernel", "chunk_kernel"))]
+    if pre:
+        rec["prefill"] = {"kernels": pre, "bytes_per_launch": sum(sum(res[n]) for n in pre),
+                          "source_sha256_16": source_hash(SOURCES["prefill"])}
+    dec = [n for n in res if n.startswith("decode_kernel")]
+    if dec:
+        rec["decode"] = {"kernels": dec, "bytes_per_launch": sum(sum(res[n]) for n in dec),
+                         "source_sha256_16": source_hash(SOURCES["decode"])}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    return "\n".join(out)
+
+
+def main(argv):
+    if argv and argv[0] == "trace":
+        print(trace_table(argv[1], argv[2]))
+    elif argv and argv[0] == "traffic":
+        print(traffic(*argv[1:6]))
+    else:
+        print(__doc__)
+        return 2
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))

@@ -52,6 +52,14 @@ def test_workspace_size_of_the_chunk_kernels(lib):
     assert gdn.gdn_chunk_fwd_workspace_size(1, 0, 2, 2, 128, 128, 64, gdn.GDN_BF16) == 0
 
 
+def test_plan(lib):
+    assert gdn.gdn_chunk_fwd_plan(1, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16) == "split"
+    assert gdn.gdn_chunk_fwd_plan(8, 8192, 16, 32, 128, 128, 64, gdn.GDN_BF16) == "fused"
+    assert gdn.gdn_chunk_fwd_plan(1, 64, 2, 2, 16, 16, 16, gdn.GDN_F32) == "recurrent"
+    assert gdn.gdn_chunk_fwd_plan(1, 64, 2, 2, 16, 32, 16, gdn.GDN_BF16) == "recurrent"
+    assert gdn.gdn_chunk_fwd_plan(1, 64, 2, 3, 16, 16, 16, gdn.GDN_BF16) == "invalid"
+
+
 def test_workspace_size_rejects_bad_sizes(lib):
     assert gdn.gdn_chunk_fwd_workspace_size(1, 64, 2, 3, 16, 16, 16, gdn.GDN_BF16) == 0
     assert gdn.gdn_chunk_fwd_workspace_size(1, 64, 2, 2, 48, 16, 16, gdn.GDN_BF16) == 0

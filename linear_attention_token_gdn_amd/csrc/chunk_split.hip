@@ -275,12 +275,15 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 
 // ---------------------------------------------------------------------------------------
 // scan_kernel: one wavefront per (chain, 16-column tile of the state), chunks in order.
+// Only the state's own dependency chain runs here:
+//     Delta = U - W S ,    S <- e^gamma_last S + (K^T dec) Delta
+// and each chunk's starting state is written out (as the fp16 B-operand fragments the MFMAs
+// use) for out_kernel, which forms the outputs in parallel over all chunks.
 //
-// The operands of chunk c + 1 are copied global -> LDS by the asynchronous LDS-DMA path
-// (global_load_lds_dwordx4: 1 KiB per instruction, no registers) while chunk c is computed
-// from the other LDS buffer.  The compiler does not track these copies, so the kernel waits
-// for them itself (s_waitcnt vmcnt(0) at the top of every chunk: by then the copy and the
-// previous chunk's output stores have had a whole chunk of compute to complete).
+// Chunk c + 2's operands (-W, K^T dec, this tile's U: 36 KiB) are copied global -> LDS by the
+// asynchronous LDS-DMA path (global_load_lds_dwordx4, 1 KiB per instruction, no registers)
+// into one of three LDS buffers while chunk c is computed.  The compiler does not track these
+// copies, so the kernel waits for them itself with an explicit vector-memory count.
 
 // One 16-byte-per-lane asynchronous copy global -> LDS: lane i's 16 bytes land at
 // lds_dst + 16 i (lds_dst must be the same for the whole wave).  The address-space cast the
@@ -292,13 +295,20 @@ __device__ __forceinline__ void lds_copy16(const void *src, void *lds_dst) {
 #endif
 }
 
-// Wait for every outstanding vector-memory operation of this wave; also a compiler barrier
-// for memory accesses, so no LDS read of the freshly copied buffer moves above it.
-__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Workgroup barrier that waits only for this wave's LDS traffic (not for global memory).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding; also a compiler
+// barrier for memory accesses, so no LDS read of a freshly copied buffer moves above it.
+template <int N> __device__ __forceinline__ void wait_vmem() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Tiles of one chain on one XCD (blocks i and i + 8 share an XCD), so that the chain's
-// workspace records are fetched from HBM once and then served from that XCD's L2.
-__device__ __forceinline__ void scan_block_map(int blk, int nblk, int ntile, int &chain, int &tile) {
+// workspace records are fetched once and then served from that XCD's L2.
+__device__ __forceinline__ void chain_tile_map(int blk, int nblk, int ntile, int &chain, int &tile) {
     if ((nblk / ntile) % 8 == 0) {
         chain = (blk & 7) + 8 * (blk / (8 * ntile));
         tile = (blk >> 3) % ntile;
@@ -308,21 +318,35 @@ __device__ __forceinline__ void scan_block_map(int blk, int nblk, int ntile, int
     }
 }
 
-template <int D, int C, typename TO>
+template <int D, int C> struct ScanCfg {
+    using F = SplitCfg<D, C>;
+    static constexpr int NW_ = F::NR * F::KD;  // 1 KiB blocks of -W
+    static constexpr int NK_ = F::NI * F::KC;  // 1 KiB blocks of K^T dec
+    static constexpr int NU_ = F::NR / 2;      // 1 KiB blocks of one tile's U
+    static constexpr int OPS = NW_ + NK_ + NU_;  // copy instructions per chunk
+    static constexpr size_t BUF = static_cast<size_t>(OPS) * 1024;
+    static constexpr int NBUF = 3;
+    static constexpr int SFR = F::KD;          // 1 KiB blocks of one tile's start state
+    static constexpr size_t SREC = static_cast<size_t>(SFR) * 1024;
+    static_assert(OPS + 2 * SFR <= 63, "copies in flight must fit the vector-memory counter");
+};
+
+// One wavefront per (chain, 16-column tile), each streaming its own copy of the chunk
+// operands.  (One workgroup per chain sharing a single LDS copy was measured slower on
+// MI355X: the copies of a chunk then come through one compute unit and take about twice as
+// long.)
+template <int D, int C>
 __global__ void __launch_bounds__(64)
 scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchunk,
-            const float *__restrict__ s0, TO *__restrict__ o, float *__restrict__ sT, int T,
-            int Hv, int nchunks, float scale) {
+            unsigned char *__restrict__ sws, const float *__restrict__ s0,
+            float *__restrict__ sT, int nchunks) {
     using F = SplitCfg<D, C>;
+    using SC = ScanCfg<D, C>;
     constexpr int NR = F::NR, NI = F::NI, KD = F::KD, KC = F::KC;
-    constexpr int NFRAG = static_cast<int>(F::OFF_U / F::FRAG);  // 1 KiB operand blocks
-    constexpr int NUFR = NR * 64 * 8 / 1024;                       // this tile's U, 1 KiB blocks
-    constexpr size_t BUF = F::OFF_U + NUFR * 1024;                 // per-chunk LDS buffer
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];  // 2 x BUF
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];  // NBUF x BUF
     const int lane = threadIdx.x, li = lane & 15, lg = lane >> 4;
     int chain, jt;
-    scan_block_map(blockIdx.x, gridDim.x, NI, chain, jt);
-    const int b = chain / Hv, hv = chain - b * Hv;
+    chain_tile_map(blockIdx.x, gridDim.x, NI, chain, jt);
     const int col = 16 * jt + li;
 
     f32x4 S[NI];  // rows 16it + 4lg + rr of column col
@@ -339,77 +363,65 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
     }
 
     const unsigned char *rec0 = ws + static_cast<size_t>(chain) * nchunks * F::REC;
-    static_assert(NFRAG + NUFR <= 63, "one chunk's copies must fit the vector-memory counter");
+    unsigned char *srec0 = sws + (static_cast<size_t>(chain) * nchunks * NI + jt) * SC::SREC;
     auto copy_chunk = [&](int cc) {
         const unsigned char *src = rec0 + static_cast<size_t>(cc) * F::REC + lane * 16;
-        unsigned char *dst = lds + (cc & 1) * BUF;
+        unsigned char *dst = lds + (cc % SC::NBUF) * SC::BUF;
 #pragma unroll
-        for (int f = 0; f < NFRAG; ++f) lds_copy16(src + f * F::FRAG, dst + f * F::FRAG);
+        for (int f = 0; f < SC::NW_; ++f) lds_copy16(src + F::OFF_W + f * 1024, dst + f * 1024);
 #pragma unroll
-        for (int f = 0; f < NUFR; ++f)  // U of tile jt: NR fragments of 512 B, contiguous
+        for (int f = 0; f < SC::NK_; ++f)
+            lds_copy16(src + F::OFF_K + f * 1024, dst + (SC::NW_ + f) * 1024);
+#pragma unroll
+        for (int f = 0; f < SC::NU_; ++f)  // U of tile jt: NR fragments of 512 B, contiguous
             lds_copy16(src + F::OFF_U + static_cast<size_t>(jt) * NR * 512 + f * 1024,
-                       dst + F::OFF_U + f * 1024);
-    };
-    auto frag = [&](const unsigned char *buf, size_t off, int idx) {
-        return *reinterpret_cast<const f16x8 *>(buf + off + (static_cast<size_t>(idx) * 64 + lane) * 16);
+                       dst + (SC::NW_ + SC::NK_ + f) * 1024);
     };
 
-    f32x4 Oprev[NR];
-    int tprev = 0;
     if (nchunks > 0) copy_chunk(0);
+    if (nchunks > 1) copy_chunk(1);
     for (int c = 0; c < nchunks; ++c) {
-        const int t0 = c * C, L = min(C, T - t0);
         const float GC = gchunk[static_cast<size_t>(chain) * nchunks + c];  // scalar load
-        wait_vmem_all();  // chunk c's operands are in LDS; the previous stores have drained
-        if (c + 1 < nchunks) copy_chunk(c + 1);
-        if (c > 0) {  // the previous chunk's output (always a full chunk)
-#pragma unroll
-            for (int a = 0; a < NR; ++a)
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                    store_f32(o + ((static_cast<size_t>(b) * T + tprev + 16 * a + 4 * lg + rr) * Hv + hv) * D + col,
-                              scale * Oprev[a][rr]);
-        }
-        const unsigned char *buf = lds + (c & 1) * BUF;
-        f16x4 uf[NR];
-#pragma unroll
-        for (int a = 0; a < NR; ++a)
-            uf[a] = *reinterpret_cast<const f16x4 *>(buf + F::OFF_U + (a * 64 + lane) * 8);
+        // wait for the copy of chunk c.  From chunk 2 on, exactly chunk c+1's copy and the
+        // start-state stores of chunks c-2 and c-1 were issued after it (while c+1 exists);
+        // otherwise wait for everything.
+        if (c >= 2 && c + 1 < nchunks)
+            wait_vmem<SC::OPS + 2 * SC::SFR>();
+        else
+            wait_vmem<0>();
+        if (c + 2 < nchunks) copy_chunk(c + 2);
+        const unsigned char *buf = lds + (c % SC::NBUF) * SC::BUF;
 
-        // S as fp16 B operands over the key index (slots: tile 2kk rows, then tile 2kk+1 rows)
+        // the chunk's starting state as fp16 B operands: kept here and stored for out_kernel
         f16x8 bS[KD];
 #pragma unroll
-        for (int kk = 0; kk < KD; ++kk) bS[kk] = cat(h4(S[2 * kk]), h4(S[2 * kk + 1]));
-        // operands of the first products, read from LDS up front so the reads overlap
-        f16x8 wf[NR][KD], qf[NR][KD];
+        for (int kk = 0; kk < KD; ++kk) {
+            bS[kk] = cat(h4(S[2 * kk]), h4(S[2 * kk + 1]));
+            *reinterpret_cast<f16x8 *>(srec0 + static_cast<size_t>(c) * NI * SC::SREC + kk * 1024 + lane * 16) =
+                bS[kk];
+        }
+        f16x8 wf[NR][KD];
 #pragma unroll
         for (int a = 0; a < NR; ++a)
 #pragma unroll
-            for (int kk = 0; kk < KD; ++kk) {
-                wf[a][kk] = frag(buf, F::OFF_W, a * KD + kk);
-                qf[a][kk] = frag(buf, F::OFF_Q, a * KD + kk);
-            }
-        // Delta = U + (-W) S ;  O = (e^gamma Q) S
-        f32x4 Dl[NR], O[NR];
+            for (int kk = 0; kk < KD; ++kk)
+                wf[a][kk] = *reinterpret_cast<const f16x8 *>(buf + ((a * KD + kk) * 64 + lane) * 16);
+        // Delta = U + (-W) S
+        f32x4 Dl[NR];
 #pragma unroll
         for (int a = 0; a < NR; ++a) {
-            Dl[a] = f32x4{float(uf[a][0]), float(uf[a][1]), float(uf[a][2]), float(uf[a][3])};
-            O[a] = zero4();
+            const f16x4 u = *reinterpret_cast<const f16x4 *>(
+                buf + (SC::NW_ + SC::NK_) * 1024 + (a * 64 + lane) * 8);
+            Dl[a] = f32x4{float(u[0]), float(u[1]), float(u[2]), float(u[3])};
 #pragma unroll
-            for (int kk = 0; kk < KD; ++kk) {
-                Dl[a] = mma_f16_k32(wf[a][kk], bS[kk], Dl[a]);
-                O[a] = mma_f16_k32(qf[a][kk], bS[kk], O[a]);
-            }
+            for (int kk = 0; kk < KD; ++kk) Dl[a] = mma_f16_k32(wf[a][kk], bS[kk], Dl[a]);
         }
-        f16x8 kf[NI][KC], pf[NR][KC];
+        f16x8 kf[NI][KC];
 #pragma unroll
         for (int it = 0; it < NI; ++it)
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) kf[it][kc] = frag(buf, F::OFF_K, it * KC + kc);
-#pragma unroll
-        for (int a = 0; a < NR; ++a)
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc) pf[a][kc] = frag(buf, F::OFF_P, a * KC + kc);
+            for (int kc = 0; kc < KC; ++kc)
+                kf[it][kc] = *reinterpret_cast<const f16x8 *>(buf + ((SC::NW_ + it * KC + kc) * 64 + lane) * 16);
         f16x8 bD[KC];
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) bD[kc] = cat(h4(Dl[2 * kc]), h4(Dl[2 * kc + 1]));
@@ -420,35 +432,6 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) S[it] = mma_f16_k32(kf[it][kc], bD[kc], S[it]);
         }
-        // O += P Delta
-#pragma unroll
-        for (int a = 0; a < NR; ++a)
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc)
-                if (32 * kc <= 16 * a + 15) O[a] = mma_f16_k32(pf[a][kc], bD[kc], O[a]);
-        if (L == C) {
-#pragma unroll
-            for (int a = 0; a < NR; ++a) Oprev[a] = O[a];
-            tprev = t0;
-        } else {  // the last, partial chunk: store now, rows past T are not stored
-#pragma unroll
-            for (int a = 0; a < NR; ++a)
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int r = 16 * a + 4 * lg + rr;
-                    if (r < L)
-                        store_f32(o + ((static_cast<size_t>(b) * T + t0 + r) * Hv + hv) * D + col,
-                                  scale * O[a][rr]);
-                }
-        }
-    }
-    if (nchunks > 0 && T % C == 0) {  // the last chunk was full: its output is still pending
-#pragma unroll
-        for (int a = 0; a < NR; ++a)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-                store_f32(o + ((static_cast<size_t>(b) * T + tprev + 16 * a + 4 * lg + rr) * Hv + hv) * D + col,
-                          scale * Oprev[a][rr]);
     }
     if (sT) {
 #pragma unroll
@@ -459,10 +442,82 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// out_kernel: one wavefront per (chain, chunk, 16-column tile), all independent:
+//     Delta = U - W S_c  (the same fp16 operands and order as the scan, so the same values)
+//     O     = scale ((e^gamma Q) S_c + P Delta)
+template <int D, int C, typename TO>
+__global__ void __launch_bounds__(64)
+out_kernel(const unsigned char *__restrict__ ws, const unsigned char *__restrict__ sws,
+           TO *__restrict__ o, int T, int Hv, int nchunks, float scale) {
+    using F = SplitCfg<D, C>;
+    using SC = ScanCfg<D, C>;
+    constexpr int NR = F::NR, NI = F::NI, KD = F::KD, KC = F::KC;
+    const int lane = threadIdx.x, li = lane & 15, lg = lane >> 4;
+    // blocks: consecutive blocks share (chain, chunk), so its record stays in one L2
+    int cc_idx, jt;
+    chain_tile_map(blockIdx.x, gridDim.x, NI, cc_idx, jt);
+    const int chain = cc_idx / nchunks, c = cc_idx - chain * nchunks;
+    const int b = chain / Hv, hv = chain - b * Hv;
+    const int col = 16 * jt + li;
+    const int t0 = c * C, L = min(C, T - t0);
+    const unsigned char *rec = ws + (static_cast<size_t>(chain) * nchunks + c) * F::REC;
+    const unsigned char *srec = sws + ((static_cast<size_t>(chain) * nchunks + c) * NI + jt) * SC::SREC;
+    auto frag = [&](size_t off, int idx) {
+        return *reinterpret_cast<const f16x8 *>(rec + off + (static_cast<size_t>(idx) * 64 + lane) * 16);
+    };
+    f16x8 bS[KD], wf[NR][KD], qf[NR][KD], pf[NR][KC];
+    f16x4 uf[NR];
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk)
+        bS[kk] = *reinterpret_cast<const f16x8 *>(srec + kk * 1024 + lane * 16);
+#pragma unroll
+    for (int a = 0; a < NR; ++a) {
+        uf[a] = *reinterpret_cast<const f16x4 *>(rec + F::OFF_U + ((jt * NR + a) * 64 + lane) * 8);
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) {
+            wf[a][kk] = frag(F::OFF_W, a * KD + kk);
+            qf[a][kk] = frag(F::OFF_Q, a * KD + kk);
+        }
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) pf[a][kc] = frag(F::OFF_P, a * KC + kc);
+    }
+    f32x4 Dl[NR], O[NR];
+#pragma unroll
+    for (int a = 0; a < NR; ++a) {
+        Dl[a] = f32x4{float(uf[a][0]), float(uf[a][1]), float(uf[a][2]), float(uf[a][3])};
+        O[a] = zero4();
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) {
+            Dl[a] = mma_f16_k32(wf[a][kk], bS[kk], Dl[a]);
+            O[a] = mma_f16_k32(qf[a][kk], bS[kk], O[a]);
+        }
+    }
+    f16x8 bD[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) bD[kc] = cat(h4(Dl[2 * kc]), h4(Dl[2 * kc + 1]));
+#pragma unroll
+    for (int a = 0; a < NR; ++a) {
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+            if (32 * kc <= 16 * a + 15) O[a] = mma_f16_k32(pf[a][kc], bD[kc], O[a]);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int r = 16 * a + 4 * lg + rr;
+            if (r < L)
+                store_f32(o + ((static_cast<size_t>(b) * T + t0 + r) * Hv + hv) * D + col,
+                          scale * O[a][rr]);
+        }
+    }
+}
+
 template <int D, int C> size_t split_ws_bytes(int B, int T, int Hv) {
     const size_t nch = static_cast<size_t>((T + C - 1) / C);
     const size_t chains = static_cast<size_t>(B) * Hv;
-    return chains * nch * SplitCfg<D, C>::REC + chains * nch * sizeof(float) + 256;
+    // operand records | per-chunk decays (padded to 256 B) | per-(chunk, tile) start states
+    const size_t gbytes = (chains * nch * sizeof(float) + 255) / 256 * 256;
+    return chains * nch * SplitCfg<D, C>::REC + gbytes +
+           chains * nch * (D / 16) * ScanCfg<D, C>::SREC;
 }
 
 template <int D, int C, typename TO> hipError_t launch_split_typed(const PrefillArgs &a) {
@@ -470,20 +525,26 @@ template <int D, int C, typename TO> hipError_t launch_split_typed(const Prefill
     const size_t chains = static_cast<size_t>(a.B) * a.Hv;
     unsigned char *ws = static_cast<unsigned char *>(a.ws);
     float *gch = reinterpret_cast<float *>(ws + chains * nch * SplitCfg<D, C>::REC);
+    unsigned char *sws = ws + chains * nch * SplitCfg<D, C>::REC +
+                         (chains * nch * sizeof(float) + 255) / 256 * 256;
     hipLaunchKernelGGL((prep_kernel<D, C>), dim3(static_cast<unsigned>(chains * nch)), dim3(64), 0,
                        a.stream, static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
                        static_cast<const bf16_t *>(a.v), static_cast<const bf16_t *>(a.beta),
                        static_cast<const bf16_t *>(a.g), ws, gch, a.T, a.Hk, a.Hv, nch);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    auto scan = scan_kernel<D, C, TO>;
-    const int lds = static_cast<int>(2 * (SplitCfg<D, C>::OFF_U + (C / 16) * 512));
+    auto scan = scan_kernel<D, C>;
+    const int lds = static_cast<int>(ScanCfg<D, C>::NBUF * ScanCfg<D, C>::BUF);
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(scan),
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(scan, dim3(static_cast<unsigned>(chains * (D / 16))), dim3(64),
-                       static_cast<size_t>(lds), a.stream, ws, gch, a.s0, static_cast<TO *>(a.o),
-                       a.sT, a.T, a.Hv, nch, a.scale);
+                       static_cast<size_t>(lds), a.stream, ws, gch, sws, a.s0, a.sT, nch);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((out_kernel<D, C, TO>), dim3(static_cast<unsigned>(chains * nch * (D / 16))),
+                       dim3(64), 0, a.stream, ws, sws, static_cast<TO *>(a.o), a.T, a.Hv, nch,
+                       a.scale);
     return hipGetLastError();
 }
 

@@ -223,7 +223,8 @@ def main():
     pre_tflops = flops / (pre_mean * 1e-3) / 1e12
     pre_gbs = pbytes / (pre_mean * 1e-3) / 1e9
     plan = gdn.gdn_chunk_fwd_plan(B, T, Hk, Hv, dk, dv, C, gdn.GDN_BF16)
-    pre_kernels = {"split": "prep_kernel<%d,%d> + scan_kernel<%d,%d,float>" % (dk, C, dk, C),
+    pre_kernels = {"split": "prep_kernel<%d,%d> + scan_kernel<%d,%d> + out_kernel<%d,%d,float>"
+                            % (dk, C, dk, C, dk, C),
                    "fused": "chunk_kernel<%d,%d,float>" % (dk, C)}.get(plan, plan)
     rooflines = {
         "prefill": {

@@ -61,16 +61,39 @@ def read_trace(path):
     return rows
 
 
+def _label(name, width=70):
+    return name if len(name) <= width else name[:width] + "..."
+
+
+def read_stats(path):
+    """rocprofv3 --stats kernel summary: (name, calls, average us, min us, max us, share %)."""
+    rows = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            rows.append((short_name(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    return rows
+
+
 def trace_table(path, command):
     groups = {}
     for name, grid, us in read_trace(path):
         groups.setdefault((name, grid), []).append(us)
     out = ["Command: `%s`" % command, "",
+           "Per-launch durations from the kernel trace:", "",
            "| kernel | grid (threads) | launches | mean us | median us | min us |",
            "|---|---|---|---|---|---|"]
     for (name, grid), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         out.append("| `%s` | %d | %d | %.1f | %.1f | %.1f |" % (
-            name, grid, len(v), statistics.mean(v), statistics.median(v), min(v)))
+            _label(name), grid, len(v), statistics.mean(v), statistics.median(v), min(v)))
+    stats = glob.glob(os.path.join(os.path.dirname(path), "*kernel_stats.csv"))
+    if stats:
+        out += ["", "`--stats` summary (%s):" % os.path.basename(stats[0]), "",
+                "| kernel | calls | average us | min us | max us | % of GPU time |",
+                "|---|---|---|---|---|---|"]
+        for name, calls, avg, mn, mx, pct in read_stats(stats[0]):
+            out.append("| `%s` | %d | %.1f | %.1f | %.1f | %.2f |" % (_label(name), calls, avg, mn,
+                                                                     mx, pct))
     return "\n".join(out)
 
 
@@ -113,9 +136,9 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, command):
         rd, wr = f * 1024 * sf, w * 1024 * sw
         res[name] = (rd, wr)
         out.append("| `%s` | %d | %.0f | %.0f | %.1f | %.1f |" % (
-            name, len(fetch.get(name, [])), f, w, rd / 1e6, wr / 1e6))
+            _label(name), len(fetch.get(name, [])), f, w, rd / 1e6, wr / 1e6))
     rec = {"copy_scale_fetch": sf, "copy_scale_write": sw, "command": command}
-    pre = [n for n in res if n.startswith(("prep_kernel", "scan_kernel", "chunk_kernel"))]
+    pre = [n for n in res if n.startswith(("prep_kernel", "scan_kernel", "out_kernel", "chunk_kernel"))]
     if pre:
         rec["prefill"] = {"kernels": pre, "bytes_per_launch": sum(sum(res[n]) for n in pre),
                           "source_sha256_16": source_hash(SOURCES["prefill"])}

@@ -274,36 +274,24 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 }
 
 // ---------------------------------------------------------------------------------------
-// scan_kernel: one wavefront per (chain, 16-column tile of the state), chunks in order.
+// scan_kernel: one workgroup per (chain, 16-column tile of the state), chunks in order.
 // Only the state's own dependency chain runs here:
 //     Delta = U - W S ,    S <- e^gamma_last S + (K^T dec) Delta
 // and each chunk's starting state is written out (as the fp16 B-operand fragments the MFMAs
 // use) for out_kernel, which forms the outputs in parallel over all chunks.
 //
-// Chunk c + 2's operands (-W, K^T dec, this tile's U: 36 KiB) are copied global -> LDS by the
-// asynchronous LDS-DMA path (global_load_lds_dwordx4, 1 KiB per instruction, no registers)
-// into one of three LDS buffers while chunk c is computed.  The compiler does not track these
-// copies, so the kernel waits for them itself with an explicit vector-memory count.
-
-// One 16-byte-per-lane asynchronous copy global -> LDS: lane i's 16 bytes land at
-// lds_dst + 16 i (lds_dst must be the same for the whole wave).  The address-space cast the
-// builtin needs only exists in the device pass.
-__device__ __forceinline__ void lds_copy16(const void *src, void *lds_dst) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_dst, 16, 0,
-                                     0);
-#endif
-}
+// The workgroup's NWV = D/32 wavefronts split the state's rows: wavefront w keeps rows
+// 32w .. 32w+31 of the tile and needs only the matching slices of the chunk operands
+// (columns 32w.. of -W, rows 32w.. of K^T dec: 8 KiB per chunk at D = 128, C = 64), which
+// it streams straight into registers, several chunks ahead.  One wavefront alone streams at
+// most about 48 GB/s on MI355X and one compute unit about 145 GB/s, so splitting the
+// operand stream four ways is what shortens a chunk on the sequential path.  The partial
+// products W[:, 32w..] S[32w.., :] are summed through LDS (each wavefront finishes some row
+// blocks of Delta), and every wavefront then reads the whole of Delta back.
 
 // Workgroup barrier that waits only for this wave's LDS traffic (not for global memory).
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Wait until at most N vector-memory operations of this wave are outstanding; also a compiler
-// barrier for memory accesses, so no LDS read of a freshly copied buffer moves above it.
-template <int N> __device__ __forceinline__ void wait_vmem() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Tiles of one chain on one XCD (blocks i and i + 8 share an XCD), so that the chain's
@@ -320,125 +308,142 @@ __device__ __forceinline__ void chain_tile_map(int blk, int nblk, int ntile, int
 
 template <int D, int C> struct ScanCfg {
     using F = SplitCfg<D, C>;
-    static constexpr int NW_ = F::NR * F::KD;  // 1 KiB blocks of -W
-    static constexpr int NK_ = F::NI * F::KC;  // 1 KiB blocks of K^T dec
-    static constexpr int NU_ = F::NR / 2;      // 1 KiB blocks of one tile's U
-    static constexpr int OPS = NW_ + NK_ + NU_;  // copy instructions per chunk
-    static constexpr size_t BUF = static_cast<size_t>(OPS) * 1024;
-    static constexpr int NBUF = 3;
-    static constexpr int SFR = F::KD;          // 1 KiB blocks of one tile's start state
+    static constexpr int NWV = F::KD;                      // wavefronts: 32 state rows each
+    static constexpr int NRW = (F::NR + NWV - 1) / NWV;    // Delta row blocks finished per wave
+    static constexpr int LOADS = F::NR + 2 * F::KC + NRW + 1;  // global loads per chunk and wave
+    static constexpr int DEPTH = 6; // chunks in flight
+    static constexpr int SFR = F::KD;                      // 1 KiB blocks of one tile's start state
     static constexpr size_t SREC = static_cast<size_t>(SFR) * 1024;
-    static_assert(OPS + 2 * SFR <= 63, "copies in flight must fit the vector-memory counter");
+    static_assert(DEPTH >= 2, "scan pipeline depth");
 };
 
-// One wavefront per (chain, 16-column tile), each streaming its own copy of the chunk
-// operands.  (One workgroup per chain sharing a single LDS copy was measured slower on
-// MI355X: the copies of a chunk then come through one compute unit and take about twice as
-// long.)
+template <int D, int C> struct ScanOps {  // one wave's operands of one chunk
+    f16x8 wf[SplitCfg<D, C>::NR];          // -W, rows 16a.., k-step w
+    f16x8 kf[2][SplitCfg<D, C>::KC];       // K^T dec, row blocks 2w, 2w+1
+    f16x4 uf[ScanCfg<D, C>::NRW];          // U of this tile, the row blocks this wave finishes
+    float gc;                              // e^gamma_last of the chunk
+};
+
 template <int D, int C>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__((64 * ScanCfg<D, C>::NWV)) __attribute__((amdgpu_waves_per_eu(1, 1)))
 scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchunk,
             unsigned char *__restrict__ sws, const float *__restrict__ s0,
             float *__restrict__ sT, int nchunks) {
     using F = SplitCfg<D, C>;
     using SC = ScanCfg<D, C>;
     constexpr int NR = F::NR, NI = F::NI, KD = F::KD, KC = F::KC;
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];  // NBUF x BUF
-    const int lane = threadIdx.x, li = lane & 15, lg = lane >> 4;
+    constexpr int NWV = SC::NWV, NRW = SC::NRW, DEPTH = SC::DEPTH;
+    __shared__ f32x4 s_part[NWV][NR][64];  // partial Delta blocks, accumulator layout
+    __shared__ f16x4 s_dlt[NR][64];         // Delta, fp16, accumulator layout
+    const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __builtin_assume(w >= 0 && w < NWV);
     int chain, jt;
     chain_tile_map(blockIdx.x, gridDim.x, NI, chain, jt);
     const int col = 16 * jt + li;
 
-    f32x4 S[NI];  // rows 16it + 4lg + rr of column col
+    f32x4 S[2];  // rows 32w + 16i + 4lg + rr of column col
     const size_t sbase = static_cast<size_t>(chain) * D * D;
     if (s0 != nullptr) {  // one branch, so that all loads are in flight together
 #pragma unroll
-        for (int it = 0; it < NI; ++it)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr)
-                S[it][rr] = s0[sbase + static_cast<size_t>(16 * it + 4 * lg + rr) * D + col];
+                S[i][rr] = s0[sbase + static_cast<size_t>(32 * w + 16 * i + 4 * lg + rr) * D + col];
     } else {
-#pragma unroll
-        for (int it = 0; it < NI; ++it) S[it] = zero4();
+        S[0] = S[1] = zero4();
     }
 
     const unsigned char *rec0 = ws + static_cast<size_t>(chain) * nchunks * F::REC;
-    unsigned char *srec0 = sws + (static_cast<size_t>(chain) * nchunks * NI + jt) * SC::SREC;
-    auto copy_chunk = [&](int cc) {
-        const unsigned char *src = rec0 + static_cast<size_t>(cc) * F::REC + lane * 16;
-        unsigned char *dst = lds + (cc % SC::NBUF) * SC::BUF;
-#pragma unroll
-        for (int f = 0; f < SC::NW_; ++f) lds_copy16(src + F::OFF_W + f * 1024, dst + f * 1024);
-#pragma unroll
-        for (int f = 0; f < SC::NK_; ++f)
-            lds_copy16(src + F::OFF_K + f * 1024, dst + (SC::NW_ + f) * 1024);
-#pragma unroll
-        for (int f = 0; f < SC::NU_; ++f)  // U of tile jt: NR fragments of 512 B, contiguous
-            lds_copy16(src + F::OFF_U + static_cast<size_t>(jt) * NR * 512 + f * 1024,
-                       dst + (SC::NW_ + SC::NK_ + f) * 1024);
-    };
-
-    if (nchunks > 0) copy_chunk(0);
-    if (nchunks > 1) copy_chunk(1);
-    for (int c = 0; c < nchunks; ++c) {
-        const float GC = gchunk[static_cast<size_t>(chain) * nchunks + c];  // scalar load
-        // wait for the copy of chunk c.  From chunk 2 on, exactly chunk c+1's copy and the
-        // start-state stores of chunks c-2 and c-1 were issued after it (while c+1 exists);
-        // otherwise wait for everything.
-        if (c >= 2 && c + 1 < nchunks)
-            wait_vmem<SC::OPS + 2 * SC::SFR>();
-        else
-            wait_vmem<0>();
-        if (c + 2 < nchunks) copy_chunk(c + 2);
-        const unsigned char *buf = lds + (c % SC::NBUF) * SC::BUF;
-
-        // the chunk's starting state as fp16 B operands: kept here and stored for out_kernel
-        f16x8 bS[KD];
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk) {
-            bS[kk] = cat(h4(S[2 * kk]), h4(S[2 * kk + 1]));
-            *reinterpret_cast<f16x8 *>(srec0 + static_cast<size_t>(c) * NI * SC::SREC + kk * 1024 + lane * 16) =
-                bS[kk];
-        }
-        f16x8 wf[NR][KD];
+    unsigned char *srec0 = sws + (static_cast<size_t>(chain) * nchunks * NI + jt) * SC::SREC +
+                           w * 1024 + lane * 16;
+    // this chain's per-chunk decays (raw buffer, 32-bit data format; reads past the end give 0)
+    const __amdgpu_buffer_rsrc_t gsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(gchunk + static_cast<size_t>(chain) * nchunks), 0, 4 * nchunks,
+        0x00020000);
+    auto load = [&](ScanOps<D, C> &o, int cc) {
+        const unsigned char *r = rec0 + static_cast<size_t>(cc) * F::REC;
 #pragma unroll
         for (int a = 0; a < NR; ++a)
+            o.wf[a] = *reinterpret_cast<const f16x8 *>(r + F::OFF_W + ((a * KD + w) * 64 + lane) * 16);
 #pragma unroll
-            for (int kk = 0; kk < KD; ++kk)
-                wf[a][kk] = *reinterpret_cast<const f16x8 *>(buf + ((a * KD + kk) * 64 + lane) * 16);
-        // Delta = U + (-W) S
-        f32x4 Dl[NR];
-#pragma unroll
-        for (int a = 0; a < NR; ++a) {
-            const f16x4 u = *reinterpret_cast<const f16x4 *>(
-                buf + (SC::NW_ + SC::NK_) * 1024 + (a * 64 + lane) * 8);
-            Dl[a] = f32x4{float(u[0]), float(u[1]), float(u[2]), float(u[3])};
-#pragma unroll
-            for (int kk = 0; kk < KD; ++kk) Dl[a] = mma_f16_k32(wf[a][kk], bS[kk], Dl[a]);
-        }
-        f16x8 kf[NI][KC];
-#pragma unroll
-        for (int it = 0; it < NI; ++it)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc)
-                kf[it][kc] = *reinterpret_cast<const f16x8 *>(buf + ((SC::NW_ + it * KC + kc) * 64 + lane) * 16);
+                o.kf[i][kc] = *reinterpret_cast<const f16x8 *>(
+                    r + F::OFF_K + (((2 * w + i) * KC + kc) * 64 + lane) * 16);
+#pragma unroll
+        for (int j = 0; j < NRW; ++j) {
+            const int a = min(w + j * NWV, NR - 1);  // clamped: loaded but unused past NR
+            o.uf[j] = *reinterpret_cast<const f16x4 *>(r + F::OFF_U + ((jt * NR + a) * 64 + lane) * 8);
+        }
+        // through a buffer descriptor, so that it stays a vector-memory load: a scalar load
+        // still in flight would hold up every LDS wait, which counts scalar loads too
+        o.gc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gsrc, 0, 4 * cc, 0));
+    };
+    auto step = [&](const ScanOps<D, C> &o, int c) {
+        const f16x8 bS = cat(h4(S[0]), h4(S[1]));  // k-step w of the B operand S
+        *reinterpret_cast<f16x8 *>(srec0 + static_cast<size_t>(c) * NI * SC::SREC) = bS;
+        f32x4 pa[NR];
+#pragma unroll
+        for (int a = 0; a < NR; ++a) pa[a] = mma_f16_k32(o.wf[a], bS, zero4());
+#pragma unroll
+        for (int a = 0; a < NR; ++a) s_part[w][a][lane] = pa[a];
+        // the independent products back to back, then their LDS writes
+        __builtin_amdgcn_sched_group_barrier(0x008, NR, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, NR, 0);
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j < NRW; ++j) {
+            const int a = w + j * NWV;
+            if (a < NR) {
+                f32x4 p[NWV];
+#pragma unroll
+                for (int v = 0; v < NWV; ++v) p[v] = s_part[v][a][lane];
+                // issue all the partial reads before any of the adds that use them
+                __builtin_amdgcn_sched_group_barrier(0x100, NWV, 0);
+                f32x4 d = f32x4{float(o.uf[j][0]), float(o.uf[j][1]), float(o.uf[j][2]),
+                                float(o.uf[j][3])};
+#pragma unroll
+                for (int v = 0; v < NWV; ++v) d += p[v];
+                s_dlt[a][lane] = h4(d);
+            }
+        }
+        lds_barrier();
         f16x8 bD[KC];
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) bD[kc] = cat(h4(Dl[2 * kc]), h4(Dl[2 * kc + 1]));
-        // S = e^gamma_last S + (K^T dec) Delta
+        for (int kc = 0; kc < KC; ++kc) bD[kc] = cat(s_dlt[2 * kc][lane], s_dlt[2 * kc + 1][lane]);
 #pragma unroll
-        for (int it = 0; it < NI; ++it) {
-            S[it] *= GC;
+        for (int i = 0; i < 2; ++i) {
+            S[i] *= o.gc;
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) S[it] = mma_f16_k32(kf[it][kc], bD[kc], S[it]);
+            for (int kc = 0; kc < KC; ++kc) S[i] = mma_f16_k32(o.kf[i][kc], bD[kc], S[i]);
+        }
+    };
+
+    // Ring of DEPTH chunks of operands in registers.  The main loop is branch-free, so the
+    // compiler's vector-memory waits stay exact (each step waits only for its own chunk's
+    // loads, issued DEPTH steps earlier); loads past the last chunk re-read the last chunk.
+    ScanOps<D, C> ring[DEPTH];
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s) load(ring[s], min(s, nchunks - 1));
+    int c0 = 0;
+    for (; c0 + DEPTH <= nchunks; c0 += DEPTH) {
+#pragma unroll
+        for (int s = 0; s < DEPTH; ++s) {
+            step(ring[s], c0 + s);
+            load(ring[s], min(c0 + s + DEPTH, nchunks - 1));
         }
     }
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s)
+        if (c0 + s < nchunks) step(ring[s], c0 + s);
     if (sT) {
 #pragma unroll
-        for (int it = 0; it < NI; ++it)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr)
-                sT[sbase + static_cast<size_t>(16 * it + 4 * lg + rr) * D + col] = S[it][rr];
+                sT[sbase + static_cast<size_t>(32 * w + 16 * i + 4 * lg + rr) * D + col] = S[i][rr];
     }
 }
 
@@ -533,13 +538,8 @@ template <int D, int C, typename TO> hipError_t launch_split_typed(const Prefill
                        static_cast<const bf16_t *>(a.g), ws, gch, a.T, a.Hk, a.Hv, nch);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    auto scan = scan_kernel<D, C>;
-    const int lds = static_cast<int>(ScanCfg<D, C>::NBUF * ScanCfg<D, C>::BUF);
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(scan),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(scan, dim3(static_cast<unsigned>(chains * (D / 16))), dim3(64),
-                       static_cast<size_t>(lds), a.stream, ws, gch, sws, a.s0, a.sT, nch);
+    hipLaunchKernelGGL((scan_kernel<D, C>), dim3(static_cast<unsigned>(chains * (D / 16))),
+                       dim3(64 * ScanCfg<D, C>::NWV), 0, a.stream, ws, gch, sws, a.s0, a.sT, nch);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((out_kernel<D, C, TO>), dim3(static_cast<unsigned>(chains * nch * (D / 16))),

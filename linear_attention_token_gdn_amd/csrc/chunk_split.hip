@@ -80,9 +80,11 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             float *__restrict__ gchunk, int T, int Hk, int Hv, int nchunks) {
     using F = SplitCfg<D, C>;
     constexpr int NR = F::NR, KD = F::KD;
-    __shared__ float s_gam[C], s_Gam[C], s_dec[C], s_bet[C];
-    __shared__ float s_ad[NR][16][20];          // diagonal blocks of A (fp32)
-    __shared__ __attribute__((aligned(16))) f16 s_td[NR][16][20];  // their inverses (fp16)
+    // per-row gate values: gamma (chunk-local cumulative log gate), e^gamma,
+    // e^(gamma_last - gamma), beta; rows past T have g = beta = 0
+    __shared__ __attribute__((aligned(16))) float s_gam[64], s_Gam[64], s_dec[64], s_bet[64];
+    __shared__ __attribute__((aligned(16))) float s_adT[NR][16][16];  // diagonal blocks of A, transposed
+    __shared__ __attribute__((aligned(16))) f16 s_td[NR][16][20];     // their inverses (fp16)
 
     const int lane = threadIdx.x, li = lane & 15, lg = lane >> 4;
     const int chain = blockIdx.x / nchunks, c = blockIdx.x - chain * nchunks;
@@ -91,46 +93,72 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const int t0 = c * C, L = min(C, T - t0);
     unsigned char *rec = ws + (static_cast<size_t>(chain) * nchunks + c) * F::REC;
 
+    // ---- gate loads first: the vector-memory counter is in order, so their wait below
+    //      does not include the K, Q, V loads issued after them
+    // (index clamped into the chunk so that the loads need no branch; rows past L are zeroed
+    // where the values are first used)
+    const size_t gi = (static_cast<size_t>(b) * T + t0 + min(lane, L - 1)) * Hv + hv;
+    const bf16_t g_raw = g[gi], b_raw = beta[gi];
+    __builtin_amdgcn_sched_barrier(0);  // keep these two loads ahead of the ones below
     // ---- row fragments of K, Q, V (lane: row 16a + li, columns 32kk + 8lg .. +7), bf16
+    //      Rows past the chunk's end load its last row (no branch, so the waits stay exact)
+    //      and are zeroed by a mask.
     u16x8 Kf[NR][KD], Qf[NR][KD], Vf[NR][KD];
 #pragma unroll
     for (int a = 0; a < NR; ++a) {
         const int r = 16 * a + li;
-        const size_t row = static_cast<size_t>(b) * T + t0 + r;
+        const size_t row = static_cast<size_t>(b) * T + t0 + min(r, L - 1);
 #pragma unroll
         for (int kk = 0; kk < KD; ++kk) {
-            Kf[a][kk] = Qf[a][kk] = Vf[a][kk] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            if (r < L) {
-                const size_t oq = (row * Hk + hq) * D + 32 * kk + 8 * lg;
-                Kf[a][kk] = *reinterpret_cast<const u16x8 *>(k + oq);
-                Qf[a][kk] = *reinterpret_cast<const u16x8 *>(q + oq);
-                Vf[a][kk] = *reinterpret_cast<const u16x8 *>(v + (row * Hv + hv) * D + 32 * kk + 8 * lg);
-            }
+            const size_t oq = (row * Hk + hq) * D + 32 * kk + 8 * lg;
+            Kf[a][kk] = *reinterpret_cast<const u16x8 *>(k + oq);
+            Qf[a][kk] = *reinterpret_cast<const u16x8 *>(q + oq);
+            Vf[a][kk] = *reinterpret_cast<const u16x8 *>(v + (row * Hv + hv) * D + 32 * kk + 8 * lg);
         }
     }
-    // ---- gates: chunk-local inclusive cumulative sum of g (rows past T: g = beta = 0)
-    {
-        float gv = 0.f, bv = 0.f;
-        if (lane < L) {
-            const size_t gi = (static_cast<size_t>(b) * T + t0 + lane) * Hv + hv;
-            gv = bf16_to_f32(g[gi]);
-            bv = bf16_to_f32(beta[gi]);
+    __builtin_amdgcn_sched_barrier(0);  // all loads are issued before anything waits
+#pragma unroll
+    for (int a = 0; a < NR; ++a) {
+        const uint16_t m = (16 * a + li < L) ? 0xffff : 0;
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) {
+            Kf[a][kk] &= m;
+            Qf[a][kk] &= m;
+            Vf[a][kk] &= m;
         }
+    }
+    // ---- gates: chunk-local inclusive cumulative sum of g
+    {
+        float gv = lane < L ? bf16_to_f32(g_raw) : 0.f;
+        const float bv = lane < L ? bf16_to_f32(b_raw) : 0.f;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const float y = __shfl_up(gv, off);
             if (lane >= off) gv += y;
         }
         const float glast = __shfl(gv, C - 1);
-        if (lane < C) {
-            s_gam[lane] = gv;
-            s_Gam[lane] = __expf(gv);
-            s_dec[lane] = __expf(glast - gv);
-            s_bet[lane] = bv;
-        }
+        // every lane writes (no branch); entries past C are not read
+        s_gam[lane] = gv;
+        s_Gam[lane] = __expf(gv);
+        s_dec[lane] = __expf(glast - gv);
+        s_bet[lane] = bv;
         if (lane == 0) gchunk[static_cast<size_t>(chain) * nchunks + c] = __expf(glast);
     }
     __syncthreads();
+    // gate values in registers: accumulator-layout rows 16a + 4lg + rr (one 16-byte read
+    // each) and row-layout rows 16a + li
+    f32x4 gamA[NR], GamA[NR], decA[NR], betA[NR];
+    float gamR[NR], GamR[NR], betR[NR];
+#pragma unroll
+    for (int a = 0; a < NR; ++a) {
+        gamA[a] = *reinterpret_cast<const f32x4 *>(&s_gam[16 * a + 4 * lg]);
+        GamA[a] = *reinterpret_cast<const f32x4 *>(&s_Gam[16 * a + 4 * lg]);
+        decA[a] = *reinterpret_cast<const f32x4 *>(&s_dec[16 * a + 4 * lg]);
+        betA[a] = *reinterpret_cast<const f32x4 *>(&s_bet[16 * a + 4 * lg]);
+        gamR[a] = s_gam[16 * a + li];
+        GamR[a] = s_Gam[16 * a + li];
+        betR[a] = s_bet[16 * a + li];
+    }
 
     // ---- KK^T: tile (m-block cb, n-block a) in accumulator layout holds
     //      KK^T[16a + li][16cb + 4lg + rr] (the product is symmetric), i.e. exactly the
@@ -139,7 +167,6 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
     for (int a = 0; a < NR; ++a) {
         const int r = 16 * a + li;
-        const float gr = s_gam[r], br = s_bet[r];
 #pragma unroll
         for (int cb = 0; cb <= a; ++cb) {
             f32x4 acc = zero4();
@@ -148,9 +175,9 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int s = 16 * cb + 4 * lg + rr;
-                const float av = (s < r) ? br * __expf(gr - s_gam[s]) * acc[rr] : 0.f;
+                const float av = (s < r) ? betR[a] * __expf(gamR[a] - gamA[cb][rr]) * acc[rr] : 0.f;
                 if (cb == a)
-                    s_ad[a][li][4 * lg + rr] = av;  // A[r][s] of the diagonal block
+                    s_adT[a][4 * lg + rr][li] = av;  // A[r][s] of the diagonal block, stored [s][r]
                 else
                     anf[a][cb][rr] = f16(-av);
             }
@@ -161,7 +188,6 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
     for (int rt = 0; rt < NR; ++rt) {
         const int r = 16 * rt + li;
-        const float gr = s_gam[r];
 #pragma unroll
         for (int kc = 0; kc < F::KC; ++kc) {
             f16x4 half[2];
@@ -176,7 +202,7 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
                         const int s = 16 * st + 4 * lg + rr;
-                        half[h][rr] = f16((s <= r) ? __expf(gr - s_gam[s]) * acc[rr] : 0.f);
+                        half[h][rr] = f16((s <= r) ? __expf(gamR[rt] - gamA[st][rr]) * acc[rr] : 0.f);
                     }
                 }
             }
@@ -187,16 +213,23 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     __syncthreads();
 
     // ---- inverses of the 16x16 diagonal blocks of I + A: lane (li, lg) solves column li of
-    //      block lg by forward substitution in fp32
+    //      block lg by forward substitution in fp32; column s of the block is contiguous
     {
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = (r == li) ? 1.f : 0.f;
         if (lg < NR) {
 #pragma unroll
-            for (int s = 0; s < 16; ++s)
+            for (int s = 0; s < 15; ++s) {
+                float col[16];
 #pragma unroll
-                for (int r = s + 1; r < 16; ++r) x[r] -= s_ad[lg][r][s] * x[s];
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const f32x4 t = *reinterpret_cast<const f32x4 *>(&s_adT[lg][s][4 * r4]);
+                    col[4 * r4] = t[0], col[4 * r4 + 1] = t[1], col[4 * r4 + 2] = t[2], col[4 * r4 + 3] = t[3];
+                }
+#pragma unroll
+                for (int r = s + 1; r < 16; ++r) x[r] -= col[r] * x[s];
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) s_td[lg][r][li] = f16(x[r]);
         }
@@ -235,13 +268,11 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                 f32x4 yu, yw;
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
-                    const int s = 16 * a + 4 * lg + rr;
-                    const float bs = s_bet[s];
-                    yu[rr] = bs * Vt[rr];
-                    yw[rr] = bs * s_Gam[s] * Kt[rr];
-                    kt[a][rr] = f16(s_dec[s] * Kt[rr]);
+                    yu[rr] = betA[a][rr] * Vt[rr];
+                    yw[rr] = betA[a][rr] * GamA[a][rr] * Kt[rr];
+                    kt[a][rr] = f16(decA[a][rr] * Kt[rr]);
                 }
-                const float gq = s_Gam[16 * a + li];
+                const float gq = GamR[a];
                 qq[a][h] = f16x4{f16(gq * Qt[0]), f16(gq * Qt[1]), f16(gq * Qt[2]), f16(gq * Qt[3])};
 #pragma unroll
                 for (int cb = 0; cb < a; ++cb) {

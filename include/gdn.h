@@ -71,8 +71,9 @@ size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv
 
 /*
  * Which kernels gdn_chunk_fwd runs for these sizes: "split" (a prep kernel parallel over
- * chunks, then a scan kernel per chain, through the workspace), "fused" (one kernel per
- * chain), "recurrent" (token by token; the fp32 path) or "invalid".  Static string.
+ * chunks, a state-scan kernel per chain, then an output kernel parallel over chunks, all
+ * through the workspace), "fused" (one kernel per chain), "recurrent" (token by token; the
+ * fp32 path) or "invalid".  Static string.
  */
 const char *gdn_chunk_fwd_plan(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
                                gdn_dtype_t in_dtype);

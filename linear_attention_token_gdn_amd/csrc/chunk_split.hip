@@ -1,4 +1,4 @@
-// chunk_split.hip -- two-kernel chunk-parallel prefill for shapes with few (b, hv) chains.
+// chunk_split.hip -- three-kernel chunk-parallel prefill for shapes with few (b, hv) chains.
 //
 // Same exact rewriting of Eq. (1) of the explainer page "論文解説: Qwen3.8-Next の設計"
 // (ta-paperlens.web.app, section "GDNの中身") as chunk_mfma.hip:

@@ -10,7 +10,10 @@ tensors (gdn_inputs.py), resident in HBM before the timed region.
 Prints ONE JSON line:  value = prefill tokens/s (B*T / mean prefill launch time), with the
 decode state GB/s, both kernels' rooflines (algorithmic bytes / measured launch time,
 against 8 TB/s HBM and 2.5 PFLOP/s dense fp16/bf16 MFMA), and the fp64 oracle's throughput
-on the host cores as a reported CPU baseline.
+on the host cores as a reported CPU baseline.  Outside the step, "decode_tokens" reports
+gdn_decode_tokens over T = 2, 4, 8 tokens of the decode workload per call (one read and one
+write of every state per call; in place, and for T = 8 also into a separate output state, as a
+verifier keeping the old state would call it).
 """
 from __future__ import annotations
 
@@ -56,9 +59,11 @@ def prefill_bytes(B, T, Hk, Hv, dk, dv, in_bytes=2, out_bytes=4, has_s0=False):
     return rd + wr
 
 
-def decode_bytes(B, Hk, Hv, dk, dv, in_bytes=2, out_bytes=4):
+def decode_bytes(B, Hk, Hv, dk, dv, T=1, in_bytes=2, out_bytes=4):
+    """Algorithmic bytes of one decode call over T tokens: the state read and written once,
+    plus every token's inputs and outputs."""
     state = 2 * B * Hv * dk * dv * 4
-    other = B * (2 * Hk * dk + Hv * dv + 2 * Hv) * in_bytes + B * Hv * dv * out_bytes
+    other = B * T * ((2 * Hk * dk + Hv * dv + 2 * Hv) * in_bytes + Hv * dv * out_bytes)
     return state, state + other
 
 
@@ -259,6 +264,36 @@ def main():
         if dec_mean * nsteps_dec > pre_mean:
             dom = "decode"
 
+    # ---- several tokens per decode call (not part of the step): T tokens of the decode
+    #      workload applied with one read and one write of every state
+    multi = None
+    if not args.no_decode:
+        multi = {}
+        st_out = torch.empty_like(state)
+        for Tn, in_place in ((2, True), (4, True), (8, True), (8, False)):
+            mq, mk, mv = (dt[n][:, :Tn].contiguous() for n in ("q", "k", "v"))
+            mb, mg = (dt[n][:, :Tn].contiguous() for n in ("beta", "g"))
+            mo = torch.empty((dc["B"], Tn, dc["Hv"], dc["dv"]), dtype=torch.float32, device=dev)
+            dst = state if in_place else st_out
+            call = lambda: gdn.decode_tokens(mq, mk, mv, mb, mg, state, state_out=dst, o=mo)
+            call()
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(5)]
+            for e0, e1 in evs:
+                e0.record(stream)
+                call()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
+            sb, tb = decode_bytes(dc["B"], dc["Hk"], dc["Hv"], dc["dk"], dc["dv"], Tn)
+            multi["T%d%s" % (Tn, "" if in_place else "_to_separate_state")] = {
+                                 "us_per_call": round(ms * 1e3, 2),
+                                 "tokens_per_s": round(dc["B"] * Tn / (ms * 1e-3), 1),
+                                 "state_GBps": round(sb / (ms * 1e-3) / 1e9, 1),
+                                 "total_GBps": round(tb / (ms * 1e-3) / 1e9, 1),
+                                 "frac_hbm_peak": round(tb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
     line = {
         "metric": "GDN prefill tokens/s + % bf16 MFMA peak; decode state GB/s % HBM peak",
         "value": round(B * T / (pre_mean * 1e-3), 1),
@@ -279,6 +314,7 @@ def main():
                     "frac_bf16_mfma_peak": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                     "GBps": round(pre_gbs, 1), "frac_hbm_peak": round(pre_gbs / HBM_PEAK_GBS, 4)},
         "decode": result_decode,
+        "decode_tokens": multi,
         "roofline": dict(rooflines[dom], kernel_role=dom),
         "rooflines": rooflines,
     }

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -119,6 +119,32 @@ gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v, const 
                              const void *g, float *state, void *o, int B, int Hk, int Hv,
                              int dk, int dv, float scale, gdn_dtype_t in_dtype,
                              gdn_dtype_t out_dtype, void *stream);
+
+/*
+ * Decode several tokens per sequence in one pass over the state: apply T consecutive tokens
+ * of Eq. (1) to every state and read out every one of them, e.g. T drafted tokens being
+ * verified (multi-token prediction) or a short continuation.  Each state is read once and
+ * written once for all T tokens; T = 1 is gdn_decode_step.
+ *
+ *   q, k       [B, T, Hk, dk]   in_dtype     token t of sequence b at row b*T + t
+ *   v          [B, T, Hv, dv]   in_dtype
+ *   beta, g    [B, T, Hv]       in_dtype
+ *   state_in   [B, Hv, dk, dv]  fp32, the state before the T tokens, or NULL for zeros
+ *   state_out  [B, Hv, dk, dv]  fp32, written with the state after the T tokens; either the
+ *                               same pointer as state_in (update in place) or not
+ *                               overlapping it.  Keeping state_in intact lets a verifier that
+ *                               accepts only the first m < T tokens re-apply those m.
+ *   o          [B, T, Hv, dv]   out_dtype, o_t = scale * S_t^T q_t; must not overlap any
+ *                               input or either state
+ *
+ * T = 0 copies state_in (or zeros) to state_out and touches nothing else.  Any T >= 0 is
+ * accepted; the kernel walks the T tokens in order, so long runs belong to gdn_chunk_fwd.
+ * Supported: dk, dv in {16, 32, 64, 128}.  B = 0 is a no-op.
+ */
+gdn_status_t gdn_decode_tokens(const void *q, const void *k, const void *v, const void *beta,
+                               const void *g, const float *state_in, float *state_out, void *o,
+                               int B, int T, int Hk, int Hv, int dk, int dv, float scale,
+                               gdn_dtype_t in_dtype, gdn_dtype_t out_dtype, void *stream);
 
 #ifdef __cplusplus
 }

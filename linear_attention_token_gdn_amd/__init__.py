@@ -11,7 +11,8 @@ properties, allocates outputs with torch and passes raw pointers and the current
 stream through ctypes.  There is no CPU fallback: without the built library every call raises.
 
 The C entry points are exposed unchanged as ``gdn_chunk_fwd``, ``gdn_decode_step``,
-``gdn_chunk_fwd_workspace_size``, ``gdn_status_string`` and ``gdn_abi_version``.
+``gdn_decode_tokens``, ``gdn_chunk_fwd_workspace_size``, ``gdn_chunk_fwd_plan``,
+``gdn_status_string`` and ``gdn_abi_version``.
 """
 from __future__ import annotations
 
@@ -24,7 +25,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libgdn.so")
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
 GDN_F32, GDN_BF16 = 0, 1
 EXPORTED_SYMBOLS = ("gdn_abi_version", "gdn_status_string", "gdn_chunk_fwd_workspace_size",
-                    "gdn_chunk_fwd_plan", "gdn_chunk_fwd", "gdn_decode_step")
+                    "gdn_chunk_fwd_plan", "gdn_chunk_fwd", "gdn_decode_step", "gdn_decode_tokens")
 
 _lib = None
 
@@ -58,6 +59,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_chunk_fwd.restype = i
     lib.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
     lib.gdn_decode_step.restype = i
+    lib.gdn_decode_tokens.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i,
+                                      vp]
+    lib.gdn_decode_tokens.restype = i
     _lib = lib
     return lib
 
@@ -95,6 +99,14 @@ def gdn_decode_step(q, k, v, beta, g, state, o, B, Hk, Hv, dk, dv, scale, in_dty
     """Raw call: pointer arguments are ints (device addresses) or None."""
     return int(load_library().gdn_decode_step(q, k, v, beta, g, state, o, B, Hk, Hv, dk, dv, scale,
                                               in_dtype, out_dtype, stream))
+
+
+def gdn_decode_tokens(q, k, v, beta, g, state_in, state_out, o, B, T, Hk, Hv, dk, dv, scale,
+                      in_dtype, out_dtype, stream) -> int:
+    """Raw call: pointer arguments are ints (device addresses) or None."""
+    return int(load_library().gdn_decode_tokens(q, k, v, beta, g, state_in, state_out, o, B, T,
+                                                Hk, Hv, dk, dv, scale, in_dtype, out_dtype,
+                                                stream))
 
 
 # ------------------------------------------------------------------ torch-facing wrappers
@@ -188,3 +200,36 @@ def decode_step(q, k, v, beta, g, state, scale=1.0, out_dtype=None, o=None):
     if st != GDN_OK:
         raise GdnError(st, "gdn_decode_step")
     return o
+
+
+def decode_tokens(q, k, v, beta, g, state, state_out=None, scale=1.0, out_dtype=None, o=None):
+    """T tokens per sequence in one pass over the state.  q, k: [B,T,Hk,dk]; v: [B,T,Hv,dv];
+    beta, g: [B,T,Hv]; state: [B,Hv,dk,dv] float32 (or None for zeros).  The state after the
+    T tokens goes to ``state_out`` (default: ``state`` itself, updated in place).  Returns
+    (o [B,T,Hv,dv], state_out)."""
+    import torch
+    lib = load_library()
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dev, dt = q.device, q.dtype
+    for t, n, s in ((q, "q", (B, T, Hk, dk)), (k, "k", (B, T, Hk, dk)), (v, "v", (B, T, Hv, dv)),
+                    (beta, "beta", (B, T, Hv)), (g, "g", (B, T, Hv))):
+        _check(t, n, s, dt, dev)
+    if state is not None:
+        _check(state, "state", (B, Hv, dk, dv), torch.float32, dev)
+    if state_out is None:
+        state_out = state if state is not None else torch.empty((B, Hv, dk, dv),
+                                                                 dtype=torch.float32, device=dev)
+    _check(state_out, "state_out", (B, Hv, dk, dv), torch.float32, dev)
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((B, T, Hv, dv), dtype=out_dtype, device=dev)
+    else:
+        _check(o, "o", (B, T, Hv, dv), out_dtype, dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.gdn_decode_tokens(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(state),
+                               _ptr(state_out), _ptr(o), B, T, Hk, Hv, dk, dv, float(scale),
+                               _dtype_code(dt), _dtype_code(out_dtype), stream)
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_decode_tokens")
+    return o, state_out

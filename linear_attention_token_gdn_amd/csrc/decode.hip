@@ -1,13 +1,15 @@
-// decode.hip -- one decode step of the gated delta rule as a single streaming pass over the
+// decode.hip -- decode steps of the gated delta rule as a single streaming pass over the
 // fp32 state (explainer page "論文解説: Qwen3.8-Next の設計", ta-paperlens.web.app, section
-// "GDNの中身", Eq. (1), applied to one new token per sequence).
+// "GDNの中身", Eq. (1), applied to T = 1 .. 16 new tokens per sequence: T = 1 is the plain
+// decode step; T > 1 applies several tokens, e.g. drafted ones being verified, with one read
+// and one write of the state for all of them).
 //
 // With e = S^T k and f = S^T q taken from the OLD state, one token of Eq. (1) is
 //     w  = beta (v - alpha e)
 //     S' = alpha S + k w^T
 //     o  = scale S'^T q = scale (alpha f + (k^T q) w)
 // so both dk-reductions come from one read of S, and S' is written while the slice is still
-// in registers: exactly one read and one write of every state byte.
+// in registers: exactly one read and one write of every state byte per call, whatever T.
 //
 // One workgroup per (b, hv) state.  Thread (rg, cg) holds float4 column group cg of the rows
 // rg, rg + R, rg + 2R, ... (R row groups): every load and store instruction of a wavefront
@@ -22,6 +24,12 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Workgroup barrier that orders LDS only: it does not wait for this thread's global loads
+// or stores (a __syncthreads would wait for every token's output stores).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int DK, int DV> struct DecodeShape {
     static constexpr int CG = DV / 4;                                  // float4 groups per row
     static constexpr int RPT = (DK * DV / 1024) > 0 ? DK * DV / 1024 : 1;  // rows per thread
@@ -31,16 +39,22 @@ template <int DK, int DV> struct DecodeShape {
     static_assert(NT % 64 == 0 && NT <= 256, "decode block shape");
 };
 
-template <int DK, int DV, typename TI, typename TO>
+// Tokens whose inputs are staged in LDS together (one burst of loads per block of tokens).
+constexpr int kTokBlock = 8;
+
+template <int DK, int DV, typename TI, typename TO, bool MULTI>
 __global__ void __launch_bounds__((DecodeShape<DK, DV>::NT))
 decode_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__restrict__ v,
-              const TI *__restrict__ beta, const TI *__restrict__ g, float *__restrict__ state,
-              TO *__restrict__ o, int Hk, int Hv, float scale) {
+              const TI *__restrict__ beta, const TI *__restrict__ g, const float *state_in,
+              float *state_out, TO *__restrict__ o, int T, int Hk, int Hv, float scale) {
     using Sh = DecodeShape<DK, DV>;
     __shared__ float red_e[Sh::NW][DV];
     __shared__ float red_f[Sh::NW][DV];
     __shared__ float red_kq[Sh::NW];
     __shared__ __attribute__((aligned(16))) float w_sh[DV];
+    // the current block of tokens' inputs, fp32
+    __shared__ float t_k[kTokBlock][DK], t_q[kTokBlock][DK], t_v[kTokBlock][DV];
+    __shared__ float t_alpha[kTokBlock], t_beta[kTokBlock];
 
     const int head = blockIdx.x;  // b * Hv + hv
     const int b = head / Hv, hv = head - b * Hv;
@@ -48,88 +62,136 @@ decode_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__re
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cg = tid % Sh::CG, rg = tid / Sh::CG;
 
-    f32x4 *S = reinterpret_cast<f32x4 *>(state + static_cast<size_t>(head) * DK * DV);
-    const TI *kp = k + (static_cast<size_t>(b) * Hk + hq) * DK;
-    const TI *qp = q + (static_cast<size_t>(b) * Hk + hq) * DK;
+    // token t of sequence b: q/k row (b*T + t)*Hk + hq, v/o row (b*T + t)*Hv + hv
+    const size_t tok0 = static_cast<size_t>(b) * T;
 
+    // the state tile of this thread; every element is read before any is written, so the
+    // update may be in place (state_out == state_in)
     f32x4 s[Sh::RPT];
+    const size_t sbase = static_cast<size_t>(head) * DK * DV;
+    if (state_in != nullptr) {
+        const f32x4 *Si = reinterpret_cast<const f32x4 *>(state_in + sbase);
+#pragma unroll
+        for (int m = 0; m < Sh::RPT; ++m) s[m] = Si[(rg + Sh::R * m) * Sh::CG + cg];
+    } else {
+#pragma unroll
+        for (int m = 0; m < Sh::RPT; ++m) s[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    for (int t0 = 0; t0 < T; t0 += kTokBlock) {
+        const int nt = MULTI ? min(kTokBlock, T - t0) : 1;
+        // a single token reads its inputs straight into registers (no staging barrier)
+        float kr1[Sh::RPT], qr1[Sh::RPT], v1 = 0.f, a1 = 0.f, b1 = 0.f;
+        if constexpr (!MULTI) {
+#pragma unroll
+            for (int m = 0; m < Sh::RPT; ++m) {
+                const size_t off = (tok0 * Hk + hq) * DK + rg + Sh::R * m;
+                kr1[m] = load_f32(k + off);
+                qr1[m] = load_f32(q + off);
+            }
+            const size_t gi = tok0 * Hv + hv;
+            a1 = expf(load_f32(g + gi));
+            b1 = load_f32(beta + gi);
+            if (tid < DV) v1 = load_f32(v + gi * DV + tid);
+        }
+        // ---- stage the block's inputs (all loads of the block in flight together)
+        if constexpr (MULTI) {
+        for (int i = tid; i < nt * DK; i += Sh::NT) {
+            const int tt = i / DK, c = i - tt * DK;
+            const size_t off = ((tok0 + t0 + tt) * Hk + hq) * DK + c;
+            t_k[tt][c] = load_f32(k + off);
+            t_q[tt][c] = load_f32(q + off);
+        }
+        for (int i = tid; i < nt * DV; i += Sh::NT) {
+            const int tt = i / DV, c = i - tt * DV;
+            t_v[tt][c] = load_f32(v + ((tok0 + t0 + tt) * Hv + hv) * DV + c);
+        }
+        if (tid < nt) {
+            const size_t gi = (tok0 + t0 + tid) * Hv + hv;
+            t_alpha[tid] = expf(load_f32(g + gi));
+            t_beta[tid] = load_f32(beta + gi);
+        }
+        lds_barrier();
+        }
+
+        for (int tt = 0; tt < nt; ++tt) {
+            float kr[Sh::RPT], qr[Sh::RPT];
+#pragma unroll
+            for (int m = 0; m < Sh::RPT; ++m) {
+                kr[m] = MULTI ? t_k[tt][rg + Sh::R * m] : kr1[m];
+                qr[m] = MULTI ? t_q[tt][rg + Sh::R * m] : qr1[m];
+            }
+            f32x4 e = {0.f, 0.f, 0.f, 0.f}, f = e;
+            float kq = 0.f;
+#pragma unroll
+            for (int m = 0; m < Sh::RPT; ++m) {
+                e.x += kr[m] * s[m].x; e.y += kr[m] * s[m].y; e.z += kr[m] * s[m].z; e.w += kr[m] * s[m].w;
+                f.x += qr[m] * s[m].x; f.y += qr[m] * s[m].y; f.z += qr[m] * s[m].z; f.w += qr[m] * s[m].w;
+                kq += kr[m] * qr[m];
+            }
+            if (cg != 0) kq = 0.f;  // every row counted once
+            // reduce over the row groups held by this wavefront (lanes CG apart share columns)
+#pragma unroll
+            for (int off = Sh::CG; off < 64; off <<= 1) {
+                e.x += __shfl_xor(e.x, off); e.y += __shfl_xor(e.y, off);
+                e.z += __shfl_xor(e.z, off); e.w += __shfl_xor(e.w, off);
+                f.x += __shfl_xor(f.x, off); f.y += __shfl_xor(f.y, off);
+                f.z += __shfl_xor(f.z, off); f.w += __shfl_xor(f.w, off);
+            }
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) kq += __shfl_xor(kq, off);
+            if (lane < Sh::CG) {
+                red_e[wave][4 * cg + 0] = e.x; red_e[wave][4 * cg + 1] = e.y;
+                red_e[wave][4 * cg + 2] = e.z; red_e[wave][4 * cg + 3] = e.w;
+                red_f[wave][4 * cg + 0] = f.x; red_f[wave][4 * cg + 1] = f.y;
+                red_f[wave][4 * cg + 2] = f.z; red_f[wave][4 * cg + 3] = f.w;
+            }
+            if (lane == 0) red_kq[wave] = kq;
+            lds_barrier();
+
+            const float alpha = MULTI ? t_alpha[tt] : a1;
+            if (tid < DV) {
+                float ej = 0.f, fj = 0.f, kqs = 0.f;
+#pragma unroll
+                for (int w = 0; w < Sh::NW; ++w) {
+                    ej += red_e[w][tid];
+                    fj += red_f[w][tid];
+                    kqs += red_kq[w];
+                }
+                const float wj = MULTI ? t_beta[tt] * (t_v[tt][tid] - alpha * ej) : b1 * (v1 - alpha * ej);
+                w_sh[tid] = wj;
+                store_f32(o + ((tok0 + t0 + tt) * Hv + hv) * DV + tid, scale * (alpha * fj + kqs * wj));
+            }
+            lds_barrier();  // also: every read of red_* above is done before the next token
+
+            const f32x4 w4 = reinterpret_cast<const f32x4 *>(w_sh)[cg];
+#pragma unroll
+            for (int m = 0; m < Sh::RPT; ++m) {
+                s[m].x = alpha * s[m].x + kr[m] * w4.x;
+                s[m].y = alpha * s[m].y + kr[m] * w4.y;
+                s[m].z = alpha * s[m].z + kr[m] * w4.z;
+                s[m].w = alpha * s[m].w + kr[m] * w4.w;
+            }
+        }
+        // the next block overwrites the staged inputs: the last token's barrier above already
+        // ordered every read of t_* before this point
+    }
+    f32x4 *So = reinterpret_cast<f32x4 *>(state_out + sbase);
 #pragma unroll
     for (int m = 0; m < Sh::RPT; ++m)
-        s[m] = S[(rg + Sh::R * m) * Sh::CG + cg];
-    float kr[Sh::RPT], qr[Sh::RPT];
-#pragma unroll
-    for (int m = 0; m < Sh::RPT; ++m) {
-        kr[m] = load_f32(kp + rg + Sh::R * m);
-        qr[m] = load_f32(qp + rg + Sh::R * m);
-    }
-
-    f32x4 e = {0.f, 0.f, 0.f, 0.f}, f = e;
-    float kq = 0.f;
-#pragma unroll
-    for (int m = 0; m < Sh::RPT; ++m) {
-        e.x += kr[m] * s[m].x; e.y += kr[m] * s[m].y; e.z += kr[m] * s[m].z; e.w += kr[m] * s[m].w;
-        f.x += qr[m] * s[m].x; f.y += qr[m] * s[m].y; f.z += qr[m] * s[m].z; f.w += qr[m] * s[m].w;
-        kq += kr[m] * qr[m];
-    }
-    if (cg != 0) kq = 0.f;  // every row counted once
-    // reduce over the row groups held by this wavefront (lanes CG apart share columns)
-#pragma unroll
-    for (int off = Sh::CG; off < 64; off <<= 1) {
-        e.x += __shfl_xor(e.x, off); e.y += __shfl_xor(e.y, off);
-        e.z += __shfl_xor(e.z, off); e.w += __shfl_xor(e.w, off);
-        f.x += __shfl_xor(f.x, off); f.y += __shfl_xor(f.y, off);
-        f.z += __shfl_xor(f.z, off); f.w += __shfl_xor(f.w, off);
-    }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) kq += __shfl_xor(kq, off);
-    if (lane < Sh::CG) {
-        red_e[wave][4 * cg + 0] = e.x; red_e[wave][4 * cg + 1] = e.y;
-        red_e[wave][4 * cg + 2] = e.z; red_e[wave][4 * cg + 3] = e.w;
-        red_f[wave][4 * cg + 0] = f.x; red_f[wave][4 * cg + 1] = f.y;
-        red_f[wave][4 * cg + 2] = f.z; red_f[wave][4 * cg + 3] = f.w;
-    }
-    if (lane == 0) red_kq[wave] = kq;
-    __syncthreads();
-
-    const size_t gi = static_cast<size_t>(head);
-    const float alpha = expf(load_f32(g + gi));
-    const float bt = load_f32(beta + gi);
-    if (tid < DV) {
-        float ej = 0.f, fj = 0.f, kqs = 0.f;
-#pragma unroll
-        for (int w = 0; w < Sh::NW; ++w) {
-            ej += red_e[w][tid];
-            fj += red_f[w][tid];
-            kqs += red_kq[w];
-        }
-        const float vj = load_f32(v + gi * DV + tid);
-        const float wj = bt * (vj - alpha * ej);
-        w_sh[tid] = wj;
-        store_f32(o + gi * DV + tid, scale * (alpha * fj + kqs * wj));
-    }
-    __syncthreads();
-
-    const f32x4 w4 = reinterpret_cast<const f32x4 *>(w_sh)[cg];
-#pragma unroll
-    for (int m = 0; m < Sh::RPT; ++m) {
-        f32x4 x = s[m];
-        x.x = alpha * x.x + kr[m] * w4.x;
-        x.y = alpha * x.y + kr[m] * w4.y;
-        x.z = alpha * x.z + kr[m] * w4.z;
-        x.w = alpha * x.w + kr[m] * w4.w;
-        __builtin_nontemporal_store(x, &S[(rg + Sh::R * m) * Sh::CG + cg]);
-    }
+        __builtin_nontemporal_store(s[m], &So[(rg + Sh::R * m) * Sh::CG + cg]);
 }
 
 template <int DK, int DV, typename TI, typename TO>
 hipError_t launch_typed(const DecodeArgs &a) {
     using Sh = DecodeShape<DK, DV>;
     const unsigned nblk = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.Hv);
-    hipLaunchKernelGGL((decode_kernel<DK, DV, TI, TO>), dim3(nblk), dim3(Sh::NT), 0, a.stream,
+    auto kern = a.T == 1 ? decode_kernel<DK, DV, TI, TO, false> : decode_kernel<DK, DV, TI, TO, true>;
+    hipLaunchKernelGGL(kern, dim3(nblk), dim3(Sh::NT), 0, a.stream,
                        static_cast<const TI *>(a.q), static_cast<const TI *>(a.k),
                        static_cast<const TI *>(a.v), static_cast<const TI *>(a.beta),
-                       static_cast<const TI *>(a.g), a.state, static_cast<TO *>(a.o), a.Hk, a.Hv,
-                       a.scale);
+                       static_cast<const TI *>(a.g), a.state_in, a.state, static_cast<TO *>(a.o),
+                       a.T, a.Hk, a.Hv, a.scale);
     return hipGetLastError();
 }
 
@@ -154,7 +216,7 @@ template <int DK> hipError_t launch_dk(const DecodeArgs &a) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &a) {
-    if (a.B == 0) return hipSuccess;
+    if (a.B == 0 || a.Hv == 0) return hipSuccess;
     switch (a.dk) {
     case 16: return launch_dk<16>(a);
     case 32: return launch_dk<32>(a);

@@ -154,34 +154,54 @@ gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v, const vo
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
-gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v, const void *beta,
-                             const void *g, float *state, void *o, int B, int Hk, int Hv,
-                             int dk, int dv, float scale, gdn_dtype_t in_dtype,
-                             gdn_dtype_t out_dtype, void *stream) {
-    if (B < 0 || Hk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || Hv % Hk != 0)
+gdn_status_t gdn_decode_tokens(const void *q, const void *k, const void *v, const void *beta,
+                               const void *g, const float *state_in, float *state_out, void *o,
+                               int B, int T, int Hk, int Hv, int dk, int dv, float scale,
+                               gdn_dtype_t in_dtype, gdn_dtype_t out_dtype, void *stream) {
+    if (B < 0 || T < 0 || Hk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || Hv % Hk != 0)
         return GDN_ERR_INVALID_ARG;
     if (!dtype_known(in_dtype) || !dtype_known(out_dtype)) return GDN_ERR_UNSUPPORTED;
     if (!dim_supported(dk) || !dim_supported(dv)) return GDN_ERR_UNSUPPORTED;
     if (B == 0) return GDN_OK;
-    if (!q || !k || !v || !beta || !g || !state || !o) return GDN_ERR_INVALID_ARG;
+    if (!state_out) return GDN_ERR_INVALID_ARG;
+    if (T > 0 && (!q || !k || !v || !beta || !g || !o)) return GDN_ERR_INVALID_ARG;
     const size_t ib = dtype_bytes(in_dtype), ob = dtype_bytes(out_dtype);
-    if (!aligned(q, ib) || !aligned(k, ib) || !aligned(v, ib) || !aligned(beta, ib) ||
-        !aligned(g, ib) || !aligned(o, ob) || !aligned(state, 16))
-        return GDN_ERR_INVALID_ARG;
-    const size_t nq = size_t(B) * Hk * dk * ib, nv = size_t(B) * Hv * dv * ib;
-    const size_t ng = size_t(B) * Hv * ib, no = size_t(B) * Hv * dv * ob;
+    if (!aligned(state_out, 16) || (state_in && !aligned(state_in, 16))) return GDN_ERR_INVALID_ARG;
     const size_t ns = size_t(B) * Hv * dk * dv * sizeof(float);
+    // the input state is either the output state itself (in place) or disjoint from it
+    if (state_in != state_out && overlap(state_in, ns, state_out, ns)) return GDN_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (T == 0)
+        return gdn::launch_state_init(state_in, state_out, size_t(B) * Hv * dk * dv, st) == hipSuccess
+                   ? GDN_OK
+                   : GDN_ERR_HIP;
+    if (!aligned(q, ib) || !aligned(k, ib) || !aligned(v, ib) || !aligned(beta, ib) ||
+        !aligned(g, ib) || !aligned(o, ob))
+        return GDN_ERR_INVALID_ARG;
+    const size_t nq = size_t(B) * T * Hk * dk * ib, nv = size_t(B) * T * Hv * dv * ib;
+    const size_t ng = size_t(B) * T * Hv * ib, no = size_t(B) * T * Hv * dv * ob;
     if (overlap(o, no, q, nq) || overlap(o, no, k, nq) || overlap(o, no, v, nv) ||
-        overlap(o, no, beta, ng) || overlap(o, no, g, ng) || overlap(o, no, state, ns) ||
-        overlap(state, ns, q, nq) || overlap(state, ns, k, nq) || overlap(state, ns, v, nv) ||
-        overlap(state, ns, beta, ng) || overlap(state, ns, g, ng))
+        overlap(o, no, beta, ng) || overlap(o, no, g, ng) || overlap(o, no, state_out, ns) ||
+        overlap(o, no, state_in, ns) || overlap(state_out, ns, q, nq) ||
+        overlap(state_out, ns, k, nq) || overlap(state_out, ns, v, nv) ||
+        overlap(state_out, ns, beta, ng) || overlap(state_out, ns, g, ng))
         return GDN_ERR_INVALID_ARG;
     gdn::DecodeArgs a;
-    a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g; a.state = state; a.o = o;
-    a.B = B; a.Hk = Hk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.scale = scale;
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g;
+    a.state_in = state_in; a.state = state_out; a.o = o;
+    a.B = B; a.T = T; a.Hk = Hk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.scale = scale;
     a.in_dt = in_dtype; a.out_dt = out_dtype;
-    a.stream = static_cast<hipStream_t>(stream);
+    a.stream = st;
     return gdn::launch_decode(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v, const void *beta,
+                             const void *g, float *state, void *o, int B, int Hk, int Hv,
+                             int dk, int dv, float scale, gdn_dtype_t in_dtype,
+                             gdn_dtype_t out_dtype, void *stream) {
+    if (B > 0 && !state) return GDN_ERR_INVALID_ARG;  // the state is required here
+    return gdn_decode_tokens(q, k, v, beta, g, state, state, o, B, 1, Hk, Hv, dk, dv, scale,
+                             in_dtype, out_dtype, stream);
 }
 
 }  // extern "C"

@@ -25,9 +25,10 @@ struct PrefillArgs {
 
 struct DecodeArgs {
     const void *q, *k, *v, *beta, *g;
-    float *state;
+    const float *state_in;  // may equal state, or be null for a zero state
+    float *state;           // written with the state after the T tokens
     void *o;
-    int B, Hk, Hv, dk, dv;
+    int B, T, Hk, Hv, dk, dv;
     float scale;
     gdn_dtype_t in_dt, out_dt;
     hipStream_t stream;

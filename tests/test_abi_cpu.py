@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gdn.gdn_abi_version() == 1
+    assert gdn.gdn_abi_version() == 2
     assert gdn.gdn_status_string(0) == "GDN_OK"
     assert gdn.gdn_status_string(1) == "GDN_ERR_INVALID_ARG"
     assert gdn.gdn_status_string(2) == "GDN_ERR_UNSUPPORTED"
@@ -133,6 +133,34 @@ def test_decode_validation(lib, kw, status):
 
 def test_decode_empty_batch_is_noop(lib):
     assert decode(B=0) == gdn.GDN_OK
+
+
+def decode_tokens(**kw):
+    a = dict(q=P["q"], k=P["k"], v=P["v"], beta=P["beta"], g=P["g"], state_in=P["s0"],
+             state_out=P["s0"], o=P["o"], B=2, T=2, Hk=2, Hv=4, dk=16, dv=32, scale=1.0,
+             in_dtype=gdn.GDN_BF16, out_dtype=gdn.GDN_F32, stream=None)
+    a.update(kw)
+    return gdn.gdn_decode_tokens(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), gdn.GDN_ERR_INVALID_ARG),
+    (dict(Hv=3), gdn.GDN_ERR_INVALID_ARG),
+    (dict(dv=48), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(out_dtype=7), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(state_out=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(state_in=P["s0"] + 16), gdn.GDN_ERR_INVALID_ARG),  # partial state overlap
+    (dict(state_out=P["s0"] + 4), gdn.GDN_ERR_INVALID_ARG),  # misaligned
+    (dict(q=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(o=P["k"]), gdn.GDN_ERR_INVALID_ARG),               # o overlaps k
+    (dict(state_in=P["s0"], state_out=P["sT"], o=P["s0"]), gdn.GDN_ERR_INVALID_ARG),
+])
+def test_decode_tokens_validation(lib, kw, status):
+    assert decode_tokens(**kw) == status
+
+
+def test_decode_tokens_empty_batch_is_noop(lib):
+    assert decode_tokens(B=0) == gdn.GDN_OK
 
 
 def test_missing_library_fails_loudly(tmp_path):

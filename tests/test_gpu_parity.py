@@ -236,3 +236,70 @@ def test_config2_sampled():
 
 def test_config3_sampled():
     _sampled_config_check(3, 2)
+
+
+# ------------------------------------------------------------------ several tokens per decode call
+def run_decode_tokens(inp, scale=1.0, in_place=True, use_init=True):
+    gdn = gdn_mod()
+    t = inp.to_torch(DEV)
+    s_in = t["s0"].clone() if use_init else None
+    shape = (inp.q.shape[0], inp.v.shape[2], inp.q.shape[3], inp.v.shape[3])
+    s_out = None if in_place else torch.full(shape, float("nan"), device=DEV)
+    o, s_out = gdn.decode_tokens(t["q"], t["k"], t["v"], t["beta"], t["g"], s_in,
+                                 state_out=s_out, scale=scale)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), s_out.cpu().numpy(), (None if s_in is None else s_in.cpu().numpy())
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 8])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (64, 32), (128, 128)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_tokens_matches_oracle(T, dk, dv, dtype):
+    inp = make_inputs(3, T, 2, 4, dk, dv, dtype=dtype, s0_std=0.02, seed=600 + 7 * T + dk + dv)
+    o, S, s_in = run_decode_tokens(inp, scale=0.9, in_place=False)
+    ro, rS = oracle_prefill(inp, scale=0.9)
+    check(o, ro, dtype, "decode_tokens o T=%d" % T)
+    check(S, rS, dtype, "decode_tokens state T=%d" % T)
+    np.testing.assert_array_equal(s_in, inp.s0)  # the input state is left as it was
+
+
+def test_decode_tokens_equals_repeated_decode_steps():
+    """One call over T tokens performs exactly the arithmetic of T single-token calls."""
+    inp = make_inputs(4, 6, 2, 4, 128, 128, dtype="bf16", s0_std=0.02, seed=610)
+    o1, S1 = run_decode_steps(inp, 6, scale=0.7)
+    o2, S2, _ = run_decode_tokens(inp, scale=0.7, in_place=True)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(S1, S2)
+
+
+def test_decode_tokens_zero_state_and_zero_tokens():
+    gdn = gdn_mod()
+    inp = make_inputs(2, 3, 1, 2, 64, 64, dtype="bf16", seed=611)
+    o, S, _ = run_decode_tokens(inp, use_init=False, in_place=False)
+    ro, rS = oracle_prefill(inp, use_init=False)
+    check(o, ro, "bf16", "decode_tokens o, zero state")
+    check(S, rS, "bf16", "decode_tokens state, zero state")
+    t = inp.to_torch(DEV)
+    e = {n: t[n][:, :0].contiguous() for n in ("q", "k", "v", "beta", "g")}
+    s_in = torch.randn((2, 2, 64, 64), device=DEV)
+    s_out = torch.full_like(s_in, 7.0)
+    o, s_out = gdn.decode_tokens(e["q"], e["k"], e["v"], e["beta"], e["g"], s_in,
+                                 state_out=s_out)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 0, 2, 64)
+    assert torch.equal(s_out, s_in)
+
+
+def test_decode_tokens_workload_sampled():
+    """The decode workload's sizes (B=256, 32 heads, d=128) with T=8 tokens per call;
+    every output and final state of 32 sampled chains against the oracle."""
+    c = CONFIGS[4]
+    inp = make_inputs(c["B"], 8, c["Hk"], c["Hv"], c["dk"], c["dv"], dtype="bf16",
+                      s0_std=0.02, seed=612)
+    o, S, _ = run_decode_tokens(inp, in_place=True)
+    rng = np.random.Generator(np.random.PCG64(612))
+    chains = np.sort(rng.choice(c["B"] * c["Hv"], 32, replace=False))
+    ro, rS = oracle_prefill(inp, chains=chains)
+    b, h = chains // c["Hv"], chains % c["Hv"]
+    check(o[b, :, h], ro, "bf16", "decode_tokens workload o")
+    check(S[b, h], rS, "bf16", "decode_tokens workload state")

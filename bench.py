@@ -13,7 +13,8 @@ against 8 TB/s HBM and 2.5 PFLOP/s dense fp16/bf16 MFMA), and the fp64 oracle's 
 on the host cores as a reported CPU baseline.  Outside the step, "decode_tokens" reports
 gdn_decode_tokens over T = 2, 4, 8 tokens of the decode workload per call (one read and one
 write of every state per call; in place, and for T = 8 also into a separate output state, as a
-verifier keeping the old state would call it).
+verifier keeping the old state would call it); "prologue_and_packed" reports the prefill with
+the fused input prologue and a packed batch of 32 variable-length sequences.
 """
 from __future__ import annotations
 
@@ -132,6 +133,75 @@ def _cpu_model():
     return "unknown"
 
 
+# ------------------------------------------------------------------ prologue / packed sequences
+def _time(torch, stream, fn, reps=10):
+    fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return sum(e0.elapsed_time(e1) for e0, e1 in evs) / reps
+
+
+def prologue_and_packed(gdn, torch, dev, stream, pt, pc, o, fs):
+    """(1) The prefill workload with the fused input prologue (q, k normalised and both gates
+    taken as logits inside the kernels), against the same call on prepared inputs and against
+    preparing them first with separate torch kernels.  (2) A packed batch: 32 sequences of
+    seeded log-uniform lengths (64 .. 8192 tokens), 16 heads, d = 128, bf16, in one call."""
+    import numpy as np
+    allf = gdn.GDN_QK_L2NORM | gdn.GDN_BETA_LOGIT | gdn.GDN_G_LOGIT
+    C = pc["chunk"]
+    fused = lambda: gdn.chunk_fwd_varlen(pt["q"], pt["k"], pt["v"], pt["beta"], pt["g"],
+                                         initial_state=pt["s0"], chunk=C, flags=allf, o=o,
+                                         final_state=fs)
+    F = torch.nn.functional
+
+    def unfused():
+        qn = F.normalize(pt["q"].float(), dim=-1).to(pt["q"].dtype)
+        kn = F.normalize(pt["k"].float(), dim=-1).to(pt["k"].dtype)
+        bt = torch.sigmoid(pt["beta"].float()).to(pt["beta"].dtype)
+        gt = F.logsigmoid(pt["g"].float()).to(pt["g"].dtype)
+        gdn.chunk_fwd(qn, kn, pt["v"], bt, gt, initial_state=pt["s0"], chunk=C, o=o,
+                      final_state=fs)
+
+    plain = lambda: gdn.chunk_fwd(pt["q"], pt["k"], pt["v"], pt["beta"], pt["g"],
+                                  initial_state=pt["s0"], chunk=C, o=o, final_state=fs)
+    plain_ms = _time(torch, stream, plain)  # standalone, like the two below
+    fused_ms = _time(torch, stream, fused)
+    unfused_ms = _time(torch, stream, unfused)
+    B, T = pc["B"], pc["T"]
+    res = {"prologue": {
+        "workload": pc["name"], "flags": "qk_l2norm+beta_logit+g_logit",
+        "fused_ms": round(fused_ms, 4), "plain_inputs_ms": round(plain_ms, 4),
+        "separate_torch_prologue_ms": round(unfused_ms, 4),
+        "fused_tokens_per_s": round(B * T / (fused_ms * 1e-3), 1)}}
+
+    rng = np.random.Generator(np.random.PCG64(11))
+    lengths = np.exp(rng.uniform(np.log(64), np.log(8192), 32)).astype(np.int64)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    Tp, H, d = int(cu[-1]), 16, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(12)
+    mk = lambda *shape: torch.randn(*shape, device=dev, generator=g).to(torch.bfloat16)
+    q, k, v = mk(Tp, H, d), mk(Tp, H, d), mk(Tp, H, d)
+    beta, ga = mk(Tp, H), mk(Tp, H) + 4.0
+    cu_t = torch.from_numpy(cu).to(dev)
+    ob = torch.empty((Tp, H, d), dtype=torch.float32, device=dev)
+    sb = torch.empty((32, H, d, d), dtype=torch.float32, device=dev)
+    packed = lambda: gdn.chunk_fwd_varlen(q, k, v, beta, ga, cu_seqlens=cu_t, chunk=64,
+                                          flags=allf, o=ob, final_state=sb)
+    packed_ms = _time(torch, stream, packed, reps=5)
+    res["packed"] = {"sequences": 32, "tokens": Tp, "min_len": int(lengths.min()),
+                     "max_len": int(lengths.max()), "heads": H, "d": d, "dtype": "bf16",
+                     "flags": "qk_l2norm+beta_logit+g_logit",
+                     "ms": round(packed_ms, 4), "tokens_per_s": round(Tp / (packed_ms * 1e-3), 1)}
+    return res
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -146,6 +216,8 @@ def main():
                     help="only run a plain 1 GiB device-to-device copy 5 times (known bytes, "
                          "to scale the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the input-prologue and packed-sequence measurements")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -294,6 +366,9 @@ def main():
                                  "total_GBps": round(tb / (ms * 1e-3) / 1e9, 1),
                                  "frac_hbm_peak": round(tb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
+    # ---- the input prologue and packed sequences (not part of the step)
+    extras = None if args.no_extras else prologue_and_packed(gdn, torch, dev, stream, pt, pc, o, fs)
+
     line = {
         "metric": "GDN prefill tokens/s + % bf16 MFMA peak; decode state GB/s % HBM peak",
         "value": round(B * T / (pre_mean * 1e-3), 1),
@@ -315,6 +390,7 @@ def main():
                     "GBps": round(pre_gbs, 1), "frac_hbm_peak": round(pre_gbs / HBM_PEAK_GBS, 4)},
         "decode": result_decode,
         "decode_tokens": multi,
+        "prologue_and_packed": extras,
         "roofline": dict(rooflines[dom], kernel_role=dom),
         "rooflines": rooflines,
     }

@@ -36,6 +36,7 @@
 #define GDN_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -55,6 +56,18 @@ typedef enum gdn_dtype {
     GDN_F32 = 0,
     GDN_BF16 = 1
 } gdn_dtype_t;
+
+/*
+ * Input prologue flags (gdn_chunk_fwd_varlen, gdn_decode_tokens): the library applies these
+ * to the inputs as it reads them, so no separate pass over q, k, beta, g is needed.
+ *   GDN_QK_L2NORM   q and k are L2-normalised per token and head: x / max(||x||_2, 1e-6),
+ *                   computed in fp32 from the stored values
+ *   GDN_BETA_LOGIT  beta holds logits: beta = sigmoid(x)
+ *   GDN_G_LOGIT     g holds logits of alpha: log alpha = log sigmoid(x) (instead of log alpha)
+ */
+#define GDN_QK_L2NORM 1u
+#define GDN_BETA_LOGIT 2u
+#define GDN_G_LOGIT 4u
 
 /* Returns GDN_ABI_VERSION of the built library. */
 int gdn_abi_version(void);
@@ -139,12 +152,48 @@ gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v, const 
  *
  * T = 0 copies state_in (or zeros) to state_out and touches nothing else.  Any T >= 0 is
  * accepted; the kernel walks the T tokens in order, so long runs belong to gdn_chunk_fwd.
+ * flags: the input prologue (GDN_QK_L2NORM | GDN_BETA_LOGIT | GDN_G_LOGIT, or 0).
  * Supported: dk, dv in {16, 32, 64, 128}.  B = 0 is a no-op.
  */
 gdn_status_t gdn_decode_tokens(const void *q, const void *k, const void *v, const void *beta,
                                const void *g, const float *state_in, float *state_out, void *o,
                                int B, int T, int Hk, int Hv, int dk, int dv, float scale,
-                               gdn_dtype_t in_dtype, gdn_dtype_t out_dtype, void *stream);
+                               unsigned flags, gdn_dtype_t in_dtype, gdn_dtype_t out_dtype,
+                               void *stream);
+
+/*
+ * Prefill with the input prologue and, optionally, packed sequences of different lengths
+ * (the serving layout: one tensor of all the batch's tokens, no padding).
+ *
+ *   cu_seqlens   NULL: dense batches, exactly as gdn_chunk_fwd with B = num_seqs and T
+ *                tokens per sequence.
+ *                Otherwise DEVICE memory, num_seqs + 1 int32 offsets, nondecreasing, from 0
+ *                to T: sequence i is rows cu_seqlens[i] .. cu_seqlens[i+1]-1 of
+ *                  q, k       [T, Hk, dk]  in_dtype
+ *                  v          [T, Hv, dv]  in_dtype
+ *                  beta, g    [T, Hv]      in_dtype
+ *                  o          [T, Hv, dv]  out_dtype
+ *                and has its own state: initial_state / final_state [num_seqs, Hv, dk, dv]
+ *                fp32.  Chunks never cross a sequence boundary; a sequence of length 0 gets
+ *                final = initial.  The offsets are not read on the host: offsets outside
+ *                [0, T] or decreasing are clamped on the device (wrong lengths, but no access
+ *                outside the tensors).
+ *   flags        GDN_QK_L2NORM | GDN_BETA_LOGIT | GDN_G_LOGIT (or 0); other bits are invalid
+ *
+ * Every other argument, alignment rule and error is as for gdn_chunk_fwd.  Packed sequences
+ * run the single-pass kernels ("fused", or "recurrent" for fp32 and odd head sizes), which
+ * need no workspace.
+ */
+gdn_status_t gdn_chunk_fwd_varlen(const void *q, const void *k, const void *v, const void *beta,
+                                  const void *g, const float *initial_state, void *o,
+                                  float *final_state, const int32_t *cu_seqlens, int num_seqs,
+                                  int T, int Hk, int Hv, int dk, int dv, int chunk, float scale,
+                                  unsigned flags, gdn_dtype_t in_dtype, gdn_dtype_t out_dtype,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of gdn_chunk_fwd_varlen: packed != 0 for cu_seqlens != NULL (then 0). */
+size_t gdn_chunk_fwd_varlen_workspace_size(int num_seqs, int T, int Hk, int Hv, int dk, int dv,
+                                           int chunk, gdn_dtype_t in_dtype, int packed);
 
 #ifdef __cplusplus
 }

@@ -11,7 +11,8 @@ properties, allocates outputs with torch and passes raw pointers and the current
 stream through ctypes.  There is no CPU fallback: without the built library every call raises.
 
 The C entry points are exposed unchanged as ``gdn_chunk_fwd``, ``gdn_decode_step``,
-``gdn_decode_tokens``, ``gdn_chunk_fwd_workspace_size``, ``gdn_chunk_fwd_plan``,
+``gdn_decode_tokens``, ``gdn_chunk_fwd_varlen``, ``gdn_chunk_fwd_varlen_workspace_size``,
+``gdn_chunk_fwd_workspace_size``, ``gdn_chunk_fwd_plan``,
 ``gdn_status_string`` and ``gdn_abi_version``.
 """
 from __future__ import annotations
@@ -24,8 +25,10 @@ LIB_PATH = os.path.join(PKG_DIR, "libgdn.so")
 
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
 GDN_F32, GDN_BF16 = 0, 1
+GDN_QK_L2NORM, GDN_BETA_LOGIT, GDN_G_LOGIT = 1, 2, 4  # input prologue flags
 EXPORTED_SYMBOLS = ("gdn_abi_version", "gdn_status_string", "gdn_chunk_fwd_workspace_size",
-                    "gdn_chunk_fwd_plan", "gdn_chunk_fwd", "gdn_decode_step", "gdn_decode_tokens")
+                    "gdn_chunk_fwd_plan", "gdn_chunk_fwd", "gdn_decode_step", "gdn_decode_tokens",
+                    "gdn_chunk_fwd_varlen", "gdn_chunk_fwd_varlen_workspace_size")
 
 _lib = None
 
@@ -59,9 +62,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_chunk_fwd.restype = i
     lib.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
     lib.gdn_decode_step.restype = i
-    lib.gdn_decode_tokens.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i,
+    u = ctypes.c_uint
+    lib.gdn_decode_tokens.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, u, i, i,
                                       vp]
     lib.gdn_decode_tokens.restype = i
+    lib.gdn_chunk_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f,
+                                         u, i, i, vp, sz, vp]
+    lib.gdn_chunk_fwd_varlen.restype = i
+    lib.gdn_chunk_fwd_varlen_workspace_size.argtypes = [i, i, i, i, i, i, i, i, i]
+    lib.gdn_chunk_fwd_varlen_workspace_size.restype = sz
     _lib = lib
     return lib
 
@@ -102,11 +111,26 @@ def gdn_decode_step(q, k, v, beta, g, state, o, B, Hk, Hv, dk, dv, scale, in_dty
 
 
 def gdn_decode_tokens(q, k, v, beta, g, state_in, state_out, o, B, T, Hk, Hv, dk, dv, scale,
-                      in_dtype, out_dtype, stream) -> int:
+                      flags, in_dtype, out_dtype, stream) -> int:
     """Raw call: pointer arguments are ints (device addresses) or None."""
     return int(load_library().gdn_decode_tokens(q, k, v, beta, g, state_in, state_out, o, B, T,
-                                                Hk, Hv, dk, dv, scale, in_dtype, out_dtype,
-                                                stream))
+                                                Hk, Hv, dk, dv, scale, flags, in_dtype,
+                                                out_dtype, stream))
+
+
+def gdn_chunk_fwd_varlen(q, k, v, beta, g, initial_state, o, final_state, cu_seqlens, num_seqs,
+                         T, Hk, Hv, dk, dv, chunk, scale, flags, in_dtype, out_dtype, workspace,
+                         workspace_bytes, stream) -> int:
+    """Raw call: pointer arguments are ints (device addresses) or None."""
+    return int(load_library().gdn_chunk_fwd_varlen(
+        q, k, v, beta, g, initial_state, o, final_state, cu_seqlens, num_seqs, T, Hk, Hv, dk, dv,
+        chunk, scale, flags, in_dtype, out_dtype, workspace, workspace_bytes, stream))
+
+
+def gdn_chunk_fwd_varlen_workspace_size(num_seqs, T, Hk, Hv, dk, dv, chunk, in_dtype,
+                                        packed) -> int:
+    return int(load_library().gdn_chunk_fwd_varlen_workspace_size(num_seqs, T, Hk, Hv, dk, dv,
+                                                                  chunk, in_dtype, packed))
 
 
 # ------------------------------------------------------------------ torch-facing wrappers
@@ -202,10 +226,12 @@ def decode_step(q, k, v, beta, g, state, scale=1.0, out_dtype=None, o=None):
     return o
 
 
-def decode_tokens(q, k, v, beta, g, state, state_out=None, scale=1.0, out_dtype=None, o=None):
+def decode_tokens(q, k, v, beta, g, state, state_out=None, scale=1.0, out_dtype=None, o=None,
+                  flags=0):
     """T tokens per sequence in one pass over the state.  q, k: [B,T,Hk,dk]; v: [B,T,Hv,dv];
     beta, g: [B,T,Hv]; state: [B,Hv,dk,dv] float32 (or None for zeros).  The state after the
-    T tokens goes to ``state_out`` (default: ``state`` itself, updated in place).  Returns
+    T tokens goes to ``state_out`` (default: ``state`` itself, updated in place).  ``flags``:
+    the input prologue (GDN_QK_L2NORM | GDN_BETA_LOGIT | GDN_G_LOGIT).  Returns
     (o [B,T,Hv,dv], state_out)."""
     import torch
     lib = load_library()
@@ -229,7 +255,61 @@ def decode_tokens(q, k, v, beta, g, state, state_out=None, scale=1.0, out_dtype=
     stream = torch.cuda.current_stream(dev).cuda_stream
     st = lib.gdn_decode_tokens(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(state),
                                _ptr(state_out), _ptr(o), B, T, Hk, Hv, dk, dv, float(scale),
-                               _dtype_code(dt), _dtype_code(out_dtype), stream)
+                               int(flags), _dtype_code(dt), _dtype_code(out_dtype), stream)
     if st != GDN_OK:
         raise GdnError(st, "gdn_decode_tokens")
     return o, state_out
+
+
+def chunk_fwd_varlen(q, k, v, beta, g, cu_seqlens=None, initial_state=None,
+                     output_final_state=True, chunk=64, scale=1.0, flags=0, out_dtype=None,
+                     final_state=None, o=None, workspace=None):
+    """Prefill with the input prologue and, optionally, packed sequences.
+
+    Packed (``cu_seqlens`` an int32 device tensor of N+1 offsets): q, k: [T,Hk,dk]; v: [T,Hv,dv];
+    beta, g: [T,Hv]; states [N,Hv,dk,dv].  Dense (``cu_seqlens`` None): the shapes of
+    ``chunk_fwd``.  ``flags``: GDN_QK_L2NORM | GDN_BETA_LOGIT | GDN_G_LOGIT.  Returns
+    (o, final_state or None)."""
+    import torch
+    lib = load_library()
+    dev, dt = q.device, q.dtype
+    if cu_seqlens is None:
+        B, T, Hk, dk = q.shape
+        Hv, dv = v.shape[2], v.shape[3]
+        lead = (B, T)
+        nseq = B
+    else:
+        T, Hk, dk = q.shape
+        Hv, dv = v.shape[1], v.shape[2]
+        lead = (T,)
+        nseq = cu_seqlens.numel() - 1
+        _check(cu_seqlens, "cu_seqlens", (nseq + 1,), torch.int32, dev)
+    for t, n, s_ in ((q, "q", lead + (Hk, dk)), (k, "k", lead + (Hk, dk)),
+                     (v, "v", lead + (Hv, dv)), (beta, "beta", lead + (Hv,)),
+                     (g, "g", lead + (Hv,))):
+        _check(t, n, s_, dt, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (nseq, Hv, dk, dv), torch.float32, dev)
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty(lead + (Hv, dv), dtype=out_dtype, device=dev)
+    else:
+        _check(o, "o", lead + (Hv, dv), out_dtype, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((nseq, Hv, dk, dv), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check(final_state, "final_state", (nseq, Hv, dk, dv), torch.float32, dev)
+    in_code, out_code = _dtype_code(dt), _dtype_code(out_dtype)
+    need = int(lib.gdn_chunk_fwd_varlen_workspace_size(nseq, T, Hk, Hv, dk, dv, chunk, in_code,
+                                                       int(cu_seqlens is not None)))
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.gdn_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                                  _ptr(initial_state), _ptr(o), _ptr(final_state),
+                                  _ptr(cu_seqlens), nseq, T, Hk, Hv, dk, dv, chunk, float(scale),
+                                  int(flags), in_code, out_code, _ptr(workspace), ws_bytes, stream)
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_chunk_fwd_varlen")
+    return o, final_state

@@ -124,7 +124,8 @@ __global__ void __launch_bounds__((Cfg<D, C>::NT))
 chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
              const bf16_t *__restrict__ v, const bf16_t *__restrict__ beta,
              const bf16_t *__restrict__ g, const float *__restrict__ s0, TO *__restrict__ o,
-             float *__restrict__ sT, int T, int Hk, int Hv, float scale) {
+             float *__restrict__ sT, int T, const int32_t *__restrict__ cu, unsigned flags,
+             int Hk, int Hv, float scale) {
     using F = Cfg<D, C>;
     constexpr int NT = F::NT, NR = F::NR;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -137,6 +138,9 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const int chain = chain_of_block(blockIdx.x, gridDim.x, G);
     const int b = chain / Hv, hv = chain - b * Hv, hq = hv / G;
     const int col = 16 * wave + li;  // the state column this lane holds
+    size_t base;  // this sequence's first row and length
+    int len;
+    seq_range(cu, T, b, base, len);
 
     // ---- the state: tile it holds rows 16it + 4lg + r of column `col`
     f32x4 S[F::NI];
@@ -152,11 +156,11 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         for (int it = 0; it < F::NI; ++it) S[it] = zero4();
     }
 
-    // ---- raw inputs of the next chunk, prefetched into registers (rows past T read as 0)
+    // ---- raw inputs of the next chunk, prefetched into registers (rows past the end read as 0)
     u16x8 pq[F::NQ], pk[F::NQ], pv[F::NQ];
     bf16_t pg = 0, pb = 0;
     auto prefetch = [&](int cidx) {
-        const int tt = cidx * C, L = min(C, T - tt);
+        const int tt = cidx * C, L = min(C, len - tt);
 #pragma unroll
         for (int n = 0; n < F::NQ; ++n) {
             const int idx = tid + n * NT, r = idx / (D / 8), cc = idx - r * (D / 8);
@@ -164,7 +168,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             pk[n] = pq[n];
             pv[n] = pq[n];
             if (r < L) {
-                const size_t row = static_cast<size_t>(b) * T + tt + r;
+                const size_t row = base + tt + r;
                 const size_t oq = (row * Hk + hq) * D + cc * 8, ov = (row * Hv + hv) * D + cc * 8;
                 pq[n] = *reinterpret_cast<const u16x8 *>(q + oq);
                 pk[n] = *reinterpret_cast<const u16x8 *>(k + oq);
@@ -174,13 +178,13 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         pg = 0;
         pb = 0;
         if (tid < L) {
-            const size_t gi = (static_cast<size_t>(b) * T + tt + tid) * Hv + hv;
+            const size_t gi = (base + tt + tid) * Hv + hv;
             pg = g[gi];
             pb = beta[gi];
         }
     };
 
-    const int nchunks = (T + C - 1) / C;
+    const int nchunks = (len + C - 1) / C;
     if (nchunks > 0) prefetch(0);
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = c * C;
@@ -190,11 +194,28 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
         for (int n = 0; n < F::NQ; ++n) {
             const int idx = tid + n * NT, r = idx / (D / 8), cc = idx - r * (D / 8);
+            float qs = 1.f, ks = 1.f;  // L2 normalisation: the D/8 consecutive lanes of a row
+            if (flags & GDN_QK_L2NORM) {
+                float qq = 0.f, kq = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float a = bf16_to_f32(pq[n][e]), c2 = bf16_to_f32(pk[n][e]);
+                    qq += a * a;
+                    kq += c2 * c2;
+                }
+#pragma unroll
+                for (int off = 1; off < D / 8; off <<= 1) {
+                    qq += __shfl_xor(qq, off);
+                    kq += __shfl_xor(kq, off);
+                }
+                qs = inv_norm_from_sumsq(qq);
+                ks = inv_norm_from_sumsq(kq);
+            }
             f16x8 qh, kh, vh;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                qh[e] = f16(bf16_to_f32(pq[n][e]));
-                kh[e] = f16(bf16_to_f32(pk[n][e]));
+                qh[e] = f16(qs * bf16_to_f32(pq[n][e]));
+                kh[e] = f16(ks * bf16_to_f32(pk[n][e]));
                 vh[e] = f16(bf16_to_f32(pv[n][e]));
             }
             *reinterpret_cast<f16x8 *>(&sm.q[r][cc * 8]) = qh;
@@ -202,7 +223,8 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             *reinterpret_cast<f16x8 *>(&sm.v[r][cc * 8]) = vh;
         }
         if (wave == 0) {
-            float gv = bf16_to_f32(pg);
+            const int L = min(C, len - t0);  // rows past the end: g = beta = 0
+            float gv = lane < L ? log_alpha_from_input(bf16_to_f32(pg), flags) : 0.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {  // inclusive prefix sum over the chunk
                 const float y = __shfl_up(gv, off);
@@ -213,7 +235,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                 sm.gam[lane] = gv;
                 sm.Gam[lane] = __expf(gv);
                 sm.dec[lane] = __expf(glast - gv);
-                sm.bet[lane] = bf16_to_f32(pb);
+                sm.bet[lane] = lane < L ? beta_from_input(bf16_to_f32(pb), flags) : 0.f;
             }
         }
         if (c > 0) {
@@ -222,7 +244,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             for (int n = 0; n < F::NO; ++n) {
                 const int idx = tid + n * NT, r = idx / (D / 4), cc = idx - r * (D / 4);
                 const f32x4 x = *reinterpret_cast<const f32x4 *>(&sm.ost[r][cc * 4]);
-                store4<TO>(o + ((static_cast<size_t>(b) * T + tp + r) * Hv + hv) * D + cc * 4, x);
+                store4<TO>(o + ((base + tp + r) * Hv + hv) * D + cc * 4, x);
             }
         }
         if (c + 1 < nchunks) prefetch(c + 1);
@@ -404,13 +426,13 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     // ---- the last chunk's output (rows past T are not stored) and the final state
     lds_barrier();
     if (nchunks > 0) {
-        const int tp = (nchunks - 1) * C, L = T - tp;
+        const int tp = (nchunks - 1) * C, L = len - tp;
 #pragma unroll
         for (int n = 0; n < F::NO; ++n) {
             const int idx = tid + n * NT, r = idx / (D / 4), cc = idx - r * (D / 4);
             if (r < L) {
                 const f32x4 x = *reinterpret_cast<const f32x4 *>(&sm.ost[r][cc * 4]);
-                store4<TO>(o + ((static_cast<size_t>(b) * T + tp + r) * Hv + hv) * D + cc * 4, x);
+                store4<TO>(o + ((base + tp + r) * Hv + hv) * D + cc * 4, x);
             }
         }
     }
@@ -435,7 +457,7 @@ template <int D, int C, typename TO> hipError_t launch_typed(const PrefillArgs &
                        static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
                        static_cast<const bf16_t *>(a.v), static_cast<const bf16_t *>(a.beta),
                        static_cast<const bf16_t *>(a.g), a.s0, static_cast<TO *>(a.o), a.sT, a.T,
-                       a.Hk, a.Hv, a.scale);
+                       a.cu, a.flags, a.Hk, a.Hv, a.scale);
     return hipGetLastError();
 }
 

@@ -71,15 +71,24 @@ template <int D, int C> struct SplitCfg {
 };
 
 // ---------------------------------------------------------------------------------------
-// prep_kernel: one wavefront per (chain, chunk)
-template <int D, int C>
+// prep_kernel: one wavefront per (chain, chunk).  NORM: q and k are L2-normalised per row
+// here (then held as fp16 for the matrix cores, since the normalised values are not bf16);
+// flags: the gate transforms of the input prologue.
+template <int D, int C, bool NORM>
 __global__ void __launch_bounds__(64)
 prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             const bf16_t *__restrict__ v, const bf16_t *__restrict__ beta,
             const bf16_t *__restrict__ g, unsigned char *__restrict__ ws,
-            float *__restrict__ gchunk, int T, int Hk, int Hv, int nchunks) {
+            float *__restrict__ gchunk, int T, int Hk, int Hv, int nchunks, unsigned flags) {
     using F = SplitCfg<D, C>;
     constexpr int NR = F::NR, KD = F::KD;
+    // products with a K or Q operand: bf16 inputs as stored, or fp16 once normalised
+    auto mma_kq = [](u16x8 a, u16x8 b, f32x4 acc) {
+        if constexpr (NORM)
+            return mma_f16_k32(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc);
+        else
+            return mma_bf16_k32(a, b, acc);
+    };
     // per-row gate values: gamma (chunk-local cumulative log gate), e^gamma,
     // e^(gamma_last - gamma), beta; rows past T have g = beta = 0
     __shared__ __attribute__((aligned(16))) float s_gam[64], s_Gam[64], s_dec[64], s_bet[64];
@@ -127,10 +136,37 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             Vf[a][kk] &= m;
         }
     }
-    // ---- gates: chunk-local inclusive cumulative sum of g
+    if constexpr (NORM) {
+        // row 16a + li is spread over the lanes li + 16 lg and the KD fragments of each
+#pragma unroll
+        for (int a = 0; a < NR; ++a) {
+            float kss = 0.f, qss = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < KD; ++kk)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = bf16_to_f32(Kf[a][kk][e]), y = bf16_to_f32(Qf[a][kk][e]);
+                    kss += x * x;
+                    qss += y * y;
+                }
+            kss += __shfl_xor(kss, 16);
+            kss += __shfl_xor(kss, 32);
+            qss += __shfl_xor(qss, 16);
+            qss += __shfl_xor(qss, 32);
+            const float kr = inv_norm_from_sumsq(kss), qr = inv_norm_from_sumsq(qss);
+#pragma unroll
+            for (int kk = 0; kk < KD; ++kk)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    Kf[a][kk][e] = __builtin_bit_cast(uint16_t, f16(kr * bf16_to_f32(Kf[a][kk][e])));
+                    Qf[a][kk][e] = __builtin_bit_cast(uint16_t, f16(qr * bf16_to_f32(Qf[a][kk][e])));
+                }
+        }
+    }
+    // ---- gates: chunk-local inclusive cumulative sum of g (rows past L: g = beta = 0)
     {
-        float gv = lane < L ? bf16_to_f32(g_raw) : 0.f;
-        const float bv = lane < L ? bf16_to_f32(b_raw) : 0.f;
+        float gv = lane < L ? log_alpha_from_input(bf16_to_f32(g_raw), flags) : 0.f;
+        const float bv = lane < L ? beta_from_input(bf16_to_f32(b_raw), flags) : 0.f;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const float y = __shfl_up(gv, off);
@@ -171,7 +207,7 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         for (int cb = 0; cb <= a; ++cb) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < KD; ++kk) acc = mma_bf16_k32(Kf[cb][kk], Kf[a][kk], acc);
+            for (int kk = 0; kk < KD; ++kk) acc = mma_kq(Kf[cb][kk], Kf[a][kk], acc);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int s = 16 * cb + 4 * lg + rr;
@@ -198,7 +234,7 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                 if (st <= rt) {
                     f32x4 acc = zero4();
 #pragma unroll
-                    for (int kk = 0; kk < KD; ++kk) acc = mma_bf16_k32(Kf[st][kk], Qf[rt][kk], acc);
+                    for (int kk = 0; kk < KD; ++kk) acc = mma_kq(Kf[st][kk], Qf[rt][kk], acc);
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
                         const int s = 16 * st + 4 * lg + rr;
@@ -241,11 +277,17 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 
     // ---- 0/1 selection fragment: B[k][n] = (k == 16h + n), and as an A operand
     //      A[m][k] = (k == 16h + m); both have the same register content
-    u16x8 sel[2];
+    //      (one = 1.0 in bf16 for V; in the K/Q operand type for K and Q)
+    constexpr uint16_t kOneKQ = NORM ? 0x3c00 : 0x3f80;
+    u16x8 sel[2], selkq[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sel[h][e] = (8 * lg + e == 16 * h + li) ? 0x3f80 : 0;
+        for (int e = 0; e < 8; ++e) {
+            const bool on = (8 * lg + e == 16 * h + li);
+            sel[h][e] = on ? 0x3f80 : 0;
+            selkq[h][e] = on ? kOneKQ : 0;
+        }
 
     // per-lane row scalings (rows 16a + 4lg + rr of the accumulator layout)
     // ---- panels: for every 16-column panel p = 2kk + h of the head dimension, the blocked
@@ -262,9 +304,9 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             f16x4 kt[NR];
 #pragma unroll
             for (int a = 0; a < NR; ++a) {
-                const f32x4 Kt = mma_bf16_k32(Kf[a][kk], sel[h], zero4());  // K[16a+4lg+rr][16p+li]
+                const f32x4 Kt = mma_kq(Kf[a][kk], selkq[h], zero4());      // K[16a+4lg+rr][16p+li]
                 const f32x4 Vt = mma_bf16_k32(Vf[a][kk], sel[h], zero4());  // V[16a+4lg+rr][16p+li]
-                const f32x4 Qt = mma_bf16_k32(sel[h], Qf[a][kk], zero4());  // Q[16a+li][16p+4lg+rr]
+                const f32x4 Qt = mma_kq(selkq[h], Qf[a][kk], zero4());      // Q[16a+li][16p+4lg+rr]
                 f32x4 yu, yw;
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
@@ -563,10 +605,11 @@ template <int D, int C, typename TO> hipError_t launch_split_typed(const Prefill
     float *gch = reinterpret_cast<float *>(ws + chains * nch * SplitCfg<D, C>::REC);
     unsigned char *sws = ws + chains * nch * SplitCfg<D, C>::REC +
                          (chains * nch * sizeof(float) + 255) / 256 * 256;
-    hipLaunchKernelGGL((prep_kernel<D, C>), dim3(static_cast<unsigned>(chains * nch)), dim3(64), 0,
-                       a.stream, static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
+    auto prep = (a.flags & GDN_QK_L2NORM) ? prep_kernel<D, C, true> : prep_kernel<D, C, false>;
+    hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(chains * nch)), dim3(64), 0, a.stream,
+                       static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
                        static_cast<const bf16_t *>(a.v), static_cast<const bf16_t *>(a.beta),
-                       static_cast<const bf16_t *>(a.g), ws, gch, a.T, a.Hk, a.Hv, nch);
+                       static_cast<const bf16_t *>(a.g), ws, gch, a.T, a.Hk, a.Hv, nch, a.flags);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((scan_kernel<D, C>), dim3(static_cast<unsigned>(chains * (D / 16))),
@@ -587,7 +630,7 @@ template <int D, int C> hipError_t launch_split_out(const PrefillArgs &a) {
 }  // namespace
 
 bool chunk_split_supports(const PrefillArgs &a) {
-    return a.in_dt == GDN_BF16 && a.dk == a.dv && (a.dk == 64 || a.dk == 128) &&
+    return a.cu == nullptr && a.in_dt == GDN_BF16 && a.dk == a.dv && (a.dk == 64 || a.dk == 128) &&
            (a.chunk == 32 || a.chunk == 64);
 }
 

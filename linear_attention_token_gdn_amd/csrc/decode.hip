@@ -46,7 +46,8 @@ template <int DK, int DV, typename TI, typename TO, bool MULTI>
 __global__ void __launch_bounds__((DecodeShape<DK, DV>::NT))
 decode_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__restrict__ v,
               const TI *__restrict__ beta, const TI *__restrict__ g, const float *state_in,
-              float *state_out, TO *__restrict__ o, int T, int Hk, int Hv, float scale) {
+              float *state_out, TO *__restrict__ o, int T, int Hk, int Hv, float scale,
+              unsigned flags) {
     using Sh = DecodeShape<DK, DV>;
     __shared__ float red_e[Sh::NW][DV];
     __shared__ float red_f[Sh::NW][DV];
@@ -90,8 +91,8 @@ decode_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__re
                 qr1[m] = load_f32(q + off);
             }
             const size_t gi = tok0 * Hv + hv;
-            a1 = expf(load_f32(g + gi));
-            b1 = load_f32(beta + gi);
+            a1 = expf(log_alpha_from_input(load_f32(g + gi), flags));
+            b1 = beta_from_input(load_f32(beta + gi), flags);
             if (tid < DV) v1 = load_f32(v + gi * DV + tid);
         }
         // ---- stage the block's inputs (all loads of the block in flight together)
@@ -108,10 +109,24 @@ decode_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__re
         }
         if (tid < nt) {
             const size_t gi = (tok0 + t0 + tid) * Hv + hv;
-            t_alpha[tid] = expf(load_f32(g + gi));
-            t_beta[tid] = load_f32(beta + gi);
+            t_alpha[tid] = expf(log_alpha_from_input(load_f32(g + gi), flags));
+            t_beta[tid] = beta_from_input(load_f32(beta + gi), flags);
         }
         lds_barrier();
+        if (flags & GDN_QK_L2NORM) {
+            // normalise the staged k and q rows: 16 threads per row
+            const int grp = tid >> 4, l16 = tid & 15;
+            for (int pr = grp; pr < 2 * nt; pr += Sh::NT / 16) {
+                float *row = (pr & 1) ? t_q[pr >> 1] : t_k[pr >> 1];
+                float ss = 0.f;
+                for (int i = l16; i < DK; i += 16) ss += row[i] * row[i];
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) ss += __shfl_xor(ss, off);
+                const float r = inv_norm_from_sumsq(ss);
+                for (int i = l16; i < DK; i += 16) row[i] *= r;
+            }
+            lds_barrier();
+        }
         }
 
         for (int tt = 0; tt < nt; ++tt) {
@@ -186,12 +201,14 @@ template <int DK, int DV, typename TI, typename TO>
 hipError_t launch_typed(const DecodeArgs &a) {
     using Sh = DecodeShape<DK, DV>;
     const unsigned nblk = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.Hv);
-    auto kern = a.T == 1 ? decode_kernel<DK, DV, TI, TO, false> : decode_kernel<DK, DV, TI, TO, true>;
+    // one token without normalisation reads its inputs into registers; otherwise through LDS
+    const bool staged = a.T > 1 || (a.flags & GDN_QK_L2NORM);
+    auto kern = staged ? decode_kernel<DK, DV, TI, TO, true> : decode_kernel<DK, DV, TI, TO, false>;
     hipLaunchKernelGGL(kern, dim3(nblk), dim3(Sh::NT), 0, a.stream,
                        static_cast<const TI *>(a.q), static_cast<const TI *>(a.k),
                        static_cast<const TI *>(a.v), static_cast<const TI *>(a.beta),
                        static_cast<const TI *>(a.g), a.state_in, a.state, static_cast<TO *>(a.o),
-                       a.T, a.Hk, a.Hv, a.scale);
+                       a.T, a.Hk, a.Hv, a.scale, a.flags);
     return hipGetLastError();
 }
 

@@ -66,11 +66,14 @@ static gdn_status_t check_prefill(const gdn::PrefillArgs &a) {
     if (!dtype_known(a.in_dt) || !dtype_known(a.out_dt)) return GDN_ERR_UNSUPPORTED;
     if (!dim_supported(a.dk) || !dim_supported(a.dv)) return GDN_ERR_UNSUPPORTED;
     if (a.chunk != 16 && a.chunk != 32 && a.chunk != 64) return GDN_ERR_UNSUPPORTED;
+    if (a.flags & ~(GDN_QK_L2NORM | GDN_BETA_LOGIT | GDN_G_LOGIT)) return GDN_ERR_INVALID_ARG;
     const size_t B = a.B, T = a.T, Hk = a.Hk, Hv = a.Hv, dk = a.dk, dv = a.dv;
+    const size_t rows = a.cu ? T : B * T;  // token rows of the q, k, v, beta, g, o tensors
     const size_t ib = dtype_bytes(a.in_dt), ob = dtype_bytes(a.out_dt);
-    const size_t nq = B * T * Hk * dk * ib, nv = B * T * Hv * dv * ib, ng = B * T * Hv * ib;
-    const size_t no = B * T * Hv * dv * ob, ns = B * Hv * dk * dv * sizeof(float);
-    if (B * T > 0) {
+    const size_t nq = rows * Hk * dk * ib, nv = rows * Hv * dv * ib, ng = rows * Hv * ib;
+    const size_t no = rows * Hv * dv * ob, ns = B * Hv * dk * dv * sizeof(float);
+    if (a.cu && (B == 0 || !aligned(a.cu, 4))) return GDN_ERR_INVALID_ARG;
+    if (rows > 0) {
         if (!a.q || !a.k || !a.v || !a.beta || !a.g || !a.o) return GDN_ERR_INVALID_ARG;
         if (!aligned(a.q, 16) || !aligned(a.k, 16) || !aligned(a.v, 16) || !aligned(a.o, 16))
             return GDN_ERR_INVALID_ARG;
@@ -82,10 +85,33 @@ static gdn_status_t check_prefill(const gdn::PrefillArgs &a) {
     }
     if ((a.s0 && !aligned(a.s0, 16)) || (a.sT && !aligned(a.sT, 16))) return GDN_ERR_INVALID_ARG;
     if (a.sT && a.sT != a.s0 && overlap(a.sT, ns, a.s0, ns)) return GDN_ERR_INVALID_ARG;
-    if (a.sT && B * T > 0 &&
+    if (a.sT && rows > 0 &&
         (overlap(a.sT, ns, a.q, nq) || overlap(a.sT, ns, a.k, nq) || overlap(a.sT, ns, a.v, nv)))
         return GDN_ERR_INVALID_ARG;
     return GDN_OK;
+}
+
+// The whole prefill: validation, the T = 0 case, workspace check and dispatch.
+static gdn_status_t run_prefill(gdn::PrefillArgs &a) {
+    gdn_status_t st = check_prefill(a);
+    if (st != GDN_OK) return st;
+    if (a.B == 0) return GDN_OK;
+    if (a.T == 0) {  // no tokens at all: final = initial
+        if (!a.sT) return GDN_OK;
+        const size_t n = static_cast<size_t>(a.B) * a.Hv * a.dk * a.dv;
+        return gdn::launch_state_init(a.s0, a.sT, n, a.stream) == hipSuccess ? GDN_OK
+                                                                              : GDN_ERR_HIP;
+    }
+    const Variant var = choose_variant(a);
+    const size_t need = var == Variant::Split   ? gdn::chunk_split_workspace(a)
+                        : var == Variant::Fused ? gdn::chunk_mfma_workspace(a)
+                                                : 0;
+    if (need > 0 && (a.ws == nullptr || a.ws_bytes < need)) return GDN_ERR_INVALID_ARG;
+    if (need > 0 && !aligned(a.ws, 256)) return GDN_ERR_INVALID_ARG;
+    hipError_t e = var == Variant::Split   ? gdn::launch_chunk_split(a)
+                   : var == Variant::Fused ? gdn::launch_chunk_mfma(a)
+                                           : gdn::launch_recurrent(a);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
 
@@ -125,41 +151,42 @@ gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v, const vo
                            float *final_state, int B, int T, int Hk, int Hv, int dk, int dv,
                            int chunk, float scale, gdn_dtype_t in_dtype, gdn_dtype_t out_dtype,
                            void *workspace, size_t workspace_bytes, void *stream) {
+    return gdn_chunk_fwd_varlen(q, k, v, beta, g, initial_state, o, final_state, nullptr, B, T,
+                                Hk, Hv, dk, dv, chunk, scale, 0u, in_dtype, out_dtype, workspace,
+                                workspace_bytes, stream);
+}
+
+gdn_status_t gdn_chunk_fwd_varlen(const void *q, const void *k, const void *v, const void *beta,
+                                  const void *g, const float *initial_state, void *o,
+                                  float *final_state, const int32_t *cu_seqlens, int num_seqs,
+                                  int T, int Hk, int Hv, int dk, int dv, int chunk, float scale,
+                                  unsigned flags, gdn_dtype_t in_dtype, gdn_dtype_t out_dtype,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
     gdn::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g;
     a.s0 = initial_state; a.o = o; a.sT = final_state;
-    a.B = B; a.T = T; a.Hk = Hk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.chunk = chunk;
+    a.B = num_seqs; a.T = T; a.Hk = Hk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.chunk = chunk;
+    a.cu = cu_seqlens; a.flags = flags;
     a.scale = scale; a.in_dt = in_dtype; a.out_dt = out_dtype;
     a.ws = workspace; a.ws_bytes = workspace_bytes;
     a.stream = static_cast<hipStream_t>(stream);
-    gdn_status_t st = check_prefill(a);
-    if (st != GDN_OK) return st;
-    if (B == 0) return GDN_OK;
-    if (T == 0) {
-        if (!final_state) return GDN_OK;
-        const size_t n = static_cast<size_t>(B) * Hv * dk * dv;
-        return gdn::launch_state_init(initial_state, final_state, n, a.stream) == hipSuccess
-                   ? GDN_OK
-                   : GDN_ERR_HIP;
-    }
-    const Variant var = choose_variant(a);
-    const size_t need = var == Variant::Split   ? gdn::chunk_split_workspace(a)
-                        : var == Variant::Fused ? gdn::chunk_mfma_workspace(a)
-                                                : 0;
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GDN_ERR_INVALID_ARG;
-    if (need > 0 && !aligned(workspace, 256)) return GDN_ERR_INVALID_ARG;
-    hipError_t e = var == Variant::Split   ? gdn::launch_chunk_split(a)
-                   : var == Variant::Fused ? gdn::launch_chunk_mfma(a)
-                                           : gdn::launch_recurrent(a);
-    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    return run_prefill(a);
+}
+
+size_t gdn_chunk_fwd_varlen_workspace_size(int num_seqs, int T, int Hk, int Hv, int dk, int dv,
+                                           int chunk, gdn_dtype_t in_dtype, int packed) {
+    if (packed) return 0;  // packed sequences run the single-pass kernels, which need none
+    return gdn_chunk_fwd_workspace_size(num_seqs, T, Hk, Hv, dk, dv, chunk, in_dtype);
 }
 
 gdn_status_t gdn_decode_tokens(const void *q, const void *k, const void *v, const void *beta,
                                const void *g, const float *state_in, float *state_out, void *o,
                                int B, int T, int Hk, int Hv, int dk, int dv, float scale,
-                               gdn_dtype_t in_dtype, gdn_dtype_t out_dtype, void *stream) {
+                               unsigned flags, gdn_dtype_t in_dtype, gdn_dtype_t out_dtype,
+                               void *stream) {
     if (B < 0 || T < 0 || Hk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || Hv % Hk != 0)
         return GDN_ERR_INVALID_ARG;
+    if (flags & ~(GDN_QK_L2NORM | GDN_BETA_LOGIT | GDN_G_LOGIT)) return GDN_ERR_INVALID_ARG;
     if (!dtype_known(in_dtype) || !dtype_known(out_dtype)) return GDN_ERR_UNSUPPORTED;
     if (!dim_supported(dk) || !dim_supported(dv)) return GDN_ERR_UNSUPPORTED;
     if (B == 0) return GDN_OK;
@@ -190,7 +217,7 @@ gdn_status_t gdn_decode_tokens(const void *q, const void *k, const void *v, cons
     a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g;
     a.state_in = state_in; a.state = state_out; a.o = o;
     a.B = B; a.T = T; a.Hk = Hk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.scale = scale;
-    a.in_dt = in_dtype; a.out_dt = out_dtype;
+    a.flags = flags; a.in_dt = in_dtype; a.out_dt = out_dtype;
     a.stream = st;
     return gdn::launch_decode(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
@@ -200,7 +227,7 @@ gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v, const 
                              int dk, int dv, float scale, gdn_dtype_t in_dtype,
                              gdn_dtype_t out_dtype, void *stream) {
     if (B > 0 && !state) return GDN_ERR_INVALID_ARG;  // the state is required here
-    return gdn_decode_tokens(q, k, v, beta, g, state, state, o, B, 1, Hk, Hv, dk, dv, scale,
+    return gdn_decode_tokens(q, k, v, beta, g, state, state, o, B, 1, Hk, Hv, dk, dv, scale, 0u,
                              in_dtype, out_dtype, stream);
 }
 

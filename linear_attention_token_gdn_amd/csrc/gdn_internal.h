@@ -15,7 +15,11 @@ struct PrefillArgs {
     const float *s0;  // may be null (zero state)
     void *o;
     float *sT;        // may be null (not written); may equal s0
+    // B sequences.  Dense: sequence b is rows b*T .. b*T+T-1.  Packed (cu != null, device
+    // memory): sequence b is rows cu[b] .. cu[b+1]-1 of T rows in all.
     int B, T, Hk, Hv, dk, dv, chunk;
+    const int32_t *cu;
+    unsigned flags;   // GDN_QK_L2NORM | GDN_BETA_LOGIT | GDN_G_LOGIT
     float scale;
     gdn_dtype_t in_dt, out_dt;
     void *ws;
@@ -29,6 +33,7 @@ struct DecodeArgs {
     float *state;           // written with the state after the T tokens
     void *o;
     int B, T, Hk, Hv, dk, dv;
+    unsigned flags;
     float scale;
     gdn_dtype_t in_dt, out_dt;
     hipStream_t stream;
@@ -76,6 +81,37 @@ template <typename T> __device__ __forceinline__ float load_f32(const T *p);
 template <> __device__ __forceinline__ float load_f32<float>(const float *p) { return *p; }
 template <> __device__ __forceinline__ float load_f32<bf16_t>(const bf16_t *p) {
     return bf16_to_f32(*p);
+}
+
+// ---- where a sequence's tokens are (see PrefillArgs): first row and length.  Packed
+//      offsets are clamped into [0, T] and made nondecreasing, so malformed offsets can only
+//      give wrong lengths, never accesses outside the tensors.
+__device__ __forceinline__ void seq_range(const int32_t *cu, int T, int seq, size_t &base,
+                                          int &len) {
+    if (cu == nullptr) {
+        base = static_cast<size_t>(seq) * T;
+        len = T;
+    } else {
+        const int a = min(max(cu[seq], 0), T);
+        const int b = min(max(cu[seq + 1], a), T);
+        base = static_cast<size_t>(a);
+        len = b - a;
+    }
+}
+
+// ---- the input prologue (flags of gdn_chunk_fwd_varlen / gdn_decode_tokens)
+__device__ __forceinline__ float beta_from_input(float x, unsigned flags) {
+    return (flags & GDN_BETA_LOGIT) ? 1.f / (1.f + expf(-x)) : x;
+}
+// log alpha; from a logit x: log sigmoid(x) = -log(1 + e^-x), evaluated without overflow
+__device__ __forceinline__ float log_alpha_from_input(float x, unsigned flags) {
+    if (!(flags & GDN_G_LOGIT)) return x;
+    return x >= 0.f ? -log1pf(expf(-x)) : x - log1pf(expf(x));
+}
+// 1 / max(||x||_2, eps) for the L2 normalisation of q and k
+constexpr float kNormEps = 1e-6f;
+__device__ __forceinline__ float inv_norm_from_sumsq(float ss) {
+    return 1.f / fmaxf(sqrtf(ss), kNormEps);
 }
 
 template <typename T> __device__ __forceinline__ void store_f32(T *p, float x);

@@ -18,38 +18,55 @@ __global__ void __launch_bounds__((DV < 64 ? 64 : DV))
 recurrent_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__restrict__ v,
                  const TI *__restrict__ beta, const TI *__restrict__ g,
                  const float *__restrict__ s0, TO *__restrict__ o, float *__restrict__ sT,
-                 int T, int Hk, int Hv, float scale) {
+                 int T, const int32_t *__restrict__ cu, unsigned flags, int Hk, int Hv,
+                 float scale) {
     const int head = blockIdx.x;  // b * Hv + hv
     const int b = head / Hv, hv = head - b * Hv;
     const int hq = hv / (Hv / Hk);
     const int j = threadIdx.x;
     if (j >= DV) return;
     const size_t sbase = static_cast<size_t>(head) * DK * DV;
+    size_t base;
+    int len;
+    seq_range(cu, T, b, base, len);
+    const bool norm = (flags & GDN_QK_L2NORM) != 0;
 
     float S[DK];
 #pragma unroll
     for (int i = 0; i < DK; ++i) S[i] = s0 ? s0[sbase + static_cast<size_t>(i) * DV + j] : 0.f;
 
-    for (int t = 0; t < T; ++t) {
-        const size_t bt = static_cast<size_t>(b) * T + t;
+    for (int t = 0; t < len; ++t) {
+        const size_t bt = base + t;
         const TI *kt = k + (bt * Hk + hq) * DK;
         const TI *qt = q + (bt * Hk + hq) * DK;
-        const float alpha = expf(load_f32(g + bt * Hv + hv));
-        const float bet = load_f32(beta + bt * Hv + hv);
+        const float alpha = expf(log_alpha_from_input(load_f32(g + bt * Hv + hv), flags));
+        const float bet = beta_from_input(load_f32(beta + bt * Hv + hv), flags);
         const float vj = load_f32(v + (bt * Hv + hv) * DV + j);
         float kv[DK];
+        float kss = 0.f;
 #pragma unroll
-        for (int i = 0; i < DK; ++i) kv[i] = load_f32(kt + i);
+        for (int i = 0; i < DK; ++i) {
+            kv[i] = load_f32(kt + i);
+            kss += kv[i] * kv[i];
+        }
+        if (norm) {  // (every thread forms the same norms: no exchange needed)
+            const float r = inv_norm_from_sumsq(kss);
+#pragma unroll
+            for (int i = 0; i < DK; ++i) kv[i] *= r;
+        }
         float e = 0.f;
 #pragma unroll
         for (int i = 0; i < DK; ++i) e += kv[i] * S[i];
         const float w = bet * (vj - alpha * e);
-        float f = 0.f;
+        float f = 0.f, qss = 0.f;
 #pragma unroll
         for (int i = 0; i < DK; ++i) {
             S[i] = alpha * S[i] + kv[i] * w;
-            f += load_f32(qt + i) * S[i];
+            const float qi = load_f32(qt + i);
+            f += qi * S[i];
+            qss += qi * qi;
         }
+        if (norm) f *= inv_norm_from_sumsq(qss);  // the read-out is linear in q
         store_f32(o + (bt * Hv + hv) * DV + j, scale * f);
     }
     if (sT) {
@@ -64,8 +81,8 @@ hipError_t launch_typed(const PrefillArgs &a) {
     hipLaunchKernelGGL((recurrent_kernel<DK, DV, TI, TO>), dim3(nblk), dim3(DV < 64 ? 64 : DV), 0,
                        a.stream, static_cast<const TI *>(a.q), static_cast<const TI *>(a.k),
                        static_cast<const TI *>(a.v), static_cast<const TI *>(a.beta),
-                       static_cast<const TI *>(a.g), a.s0, static_cast<TO *>(a.o), a.sT, a.T,
-                       a.Hk, a.Hv, a.scale);
+                       static_cast<const TI *>(a.g), a.s0, static_cast<TO *>(a.o), a.sT, a.T, a.cu,
+                       a.flags, a.Hk, a.Hv, a.scale);
     return hipGetLastError();
 }
 

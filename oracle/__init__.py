@@ -61,6 +61,12 @@ def _load():
                                                    ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                    ctypes.c_double, ctypes.c_int]
             lib.gdn_oracle_decode_step.restype = ctypes.c_int
+            lib.gdn_oracle_run_packed.argtypes = [f32p, f32p, f32p, f32p, f32p, f64p, i64p,
+                                                  ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                  ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                  ctypes.c_double, ctypes.c_uint, f64p, f64p,
+                                                  ctypes.c_int]
+            lib.gdn_oracle_run_packed.restype = ctypes.c_int
             lib.gdn_oracle_max_threads.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -125,6 +131,42 @@ def run(q, k, v, beta, g, s0=None, scale=1.0, chains=None, nthreads=0,
         o = o.reshape(B, Hv, T, dv).transpose(0, 2, 1, 3)
         if sT is not None:
             sT = sT.reshape(B, Hv, dk, dv)
+    return o, sT
+
+
+QK_L2NORM, BETA_LOGIT, G_LOGIT = 1, 2, 4  # input prologue flags
+
+
+def run_packed(q, k, v, beta, g, cu_seqlens, s0=None, scale=1.0, flags=0, nthreads=0,
+               want_state=True):
+    """Packed sequences with the input prologue.  q, k: [T,Hk,dk]; v: [T,Hv,dv]; beta, g:
+    [T,Hv]; cu_seqlens: N+1 offsets (sequence i = rows cu[i]..cu[i+1]-1); s0: [N,Hv,dk,dv] or
+    None.  ``flags``: QK_L2NORM | BETA_LOGIT | G_LOGIT.  Returns (o [T,Hv,dv] fp64,
+    sT [N,Hv,dk,dv] fp64 or None)."""
+    lib = _load()
+    T, Hk, dk = np.shape(q)
+    Hv, dv = np.shape(v)[1], np.shape(v)[2]
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64).ravel())
+    N = cu.size - 1
+    q = _f32(q, (T, Hk, dk))
+    k = _f32(k, (T, Hk, dk))
+    v = _f32(v, (T, Hv, dv))
+    beta = _f32(beta, (T, Hv))
+    g = _f32(g, (T, Hv))
+    if s0 is not None:
+        s0 = np.ascontiguousarray(s0, dtype=np.float64)
+        if s0.shape != (N, Hv, dk, dv):
+            raise ValueError("s0 must have shape %s" % ((N, Hv, dk, dv),))
+    o = np.empty((T, Hv, dv), dtype=np.float64)
+    sT = np.empty((N, Hv, dk, dv), dtype=np.float64) if want_state else None
+    rc = lib.gdn_oracle_run_packed(_ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float),
+                                   _ptr(v, ctypes.c_float), _ptr(beta, ctypes.c_float),
+                                   _ptr(g, ctypes.c_float), _ptr(s0, ctypes.c_double),
+                                   _ptr(cu, ctypes.c_int64), N, T, Hk, Hv, dk, dv,
+                                   float(scale), int(flags), _ptr(o, ctypes.c_double),
+                                   _ptr(sT, ctypes.c_double), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("gdn_oracle_run_packed failed with code %d" % rc)
     return o, sT
 
 

@@ -34,7 +34,10 @@
  * Parity status: pinned by the CPU tests (closed forms for beta = 0 and
  * beta = 1, orthonormal-key retrieval, exact rational brute force on tiny
  * sizes, dense transition-matrix products, an independently derived chunked
- * form, linearity, split/resume and GQA equivalence).
+ * form, linearity, split/resume and GQA equivalence).  The packed-sequence
+ * entry point with its input prologue is pinned by reduction to per-sequence
+ * runs, by scale invariance of the normalisation and by the closed forms
+ * sigmoid(0) = 1/2 and pure decay products.
  */
 #include <math.h>
 #include <stdint.h>
@@ -46,8 +49,8 @@
 
 /* Apply one token of Eq. (1) to the state S (dk x dv, row-major) and write
  * o = scale * S^T q for the updated state.  e and f are dv-long scratch. */
-static void gdn_oracle_token(double *S, const float *q, const float *k,
-                             const float *v, double alpha, double beta,
+static void gdn_oracle_token(double *S, const double *q, const double *k,
+                             const double *v, double alpha, double beta,
                              double scale, int dk, int dv, double *e,
                              double *f, double *o)
 {
@@ -55,29 +58,65 @@ static void gdn_oracle_token(double *S, const float *q, const float *k,
     for (int j = 0; j < dv; ++j)
         e[j] = 0.0;
     for (int i = 0; i < dk; ++i) {
-        const double ki = (double)k[i];
+        const double ki = k[i];
         const double *row = S + (size_t)i * dv;
         for (int j = 0; j < dv; ++j)
             e[j] += ki * row[j];
     }
     /* S = alpha * (S - beta k e^T) + beta k v^T  ==  alpha (I - beta k k^T) S + beta k v^T */
     for (int i = 0; i < dk; ++i) {
-        const double ki = (double)k[i];
+        const double ki = k[i];
         double *row = S + (size_t)i * dv;
         for (int j = 0; j < dv; ++j)
-            row[j] = alpha * (row[j] - beta * ki * e[j]) + beta * ki * (double)v[j];
+            row[j] = alpha * (row[j] - beta * ki * e[j]) + beta * ki * v[j];
     }
     /* o = scale * S^T q, read from the updated state. */
     for (int j = 0; j < dv; ++j)
         f[j] = 0.0;
     for (int i = 0; i < dk; ++i) {
-        const double qi = (double)q[i];
+        const double qi = q[i];
         const double *row = S + (size_t)i * dv;
         for (int j = 0; j < dv; ++j)
             f[j] += qi * row[j];
     }
     for (int j = 0; j < dv; ++j)
         o[j] = scale * f[j];
+}
+
+/* Widen n stored values to double. */
+static void gdn_oracle_widen(const float *x, int n, double *y)
+{
+    for (int i = 0; i < n; ++i)
+        y[i] = (double)x[i];
+}
+
+/* The input prologue (plain definitions, fp64; flag values as in the library's header):
+ *   1: q, k -> x / max(||x||_2, 1e-6)     2: beta = sigmoid(x)     4: log alpha = log sigmoid(x) */
+#define GDN_ORACLE_QK_L2NORM 1u
+#define GDN_ORACLE_BETA_LOGIT 2u
+#define GDN_ORACLE_G_LOGIT 4u
+
+static void gdn_oracle_l2normalise(double *x, int n)
+{
+    double ss = 0.0;
+    for (int i = 0; i < n; ++i)
+        ss += x[i] * x[i];
+    double nrm = sqrt(ss);
+    if (nrm < 1e-6)
+        nrm = 1e-6;
+    for (int i = 0; i < n; ++i)
+        x[i] = x[i] / nrm;
+}
+
+static double gdn_oracle_sigmoid(double x)
+{
+    return 1.0 / (1.0 + exp(-x));
+}
+
+static double gdn_oracle_log_sigmoid(double x)
+{
+    /* log(1 / (1 + e^-x)), written so that neither branch overflows */
+    return x >= 0.0 ? -log1p(exp(-x)) : x - log1p(exp(x));
 }
 
 static int gdn_oracle_dims_ok(int B, int T, int Hk, int Hv, int dk, int dv)
@@ -141,19 +180,98 @@ int gdn_oracle_run(const float *q, const float *k, const float *v,
         } else {
             memset(S, 0, sizeof(double) * ssz);
         }
+        double *qd = (double *)malloc(sizeof(double) * (size_t)(2 * dk + dv));
+        if (!qd) {
+            free(S); free(e); free(f);
+            failed = 1;
+            continue;
+        }
+        double *kd = qd + dk, *vd = kd + dk;
         for (int t = 0; t < T; ++t) {
             const size_t bt = (size_t)b * T + t;
-            const float *qt = q + (bt * Hk + hq) * dk;
-            const float *kt = k + (bt * Hk + hq) * dk;
-            const float *vt = v + (bt * Hv + hv) * dv;
+            gdn_oracle_widen(q + (bt * Hk + hq) * dk, dk, qd);
+            gdn_oracle_widen(k + (bt * Hk + hq) * dk, dk, kd);
+            gdn_oracle_widen(v + (bt * Hv + hv) * dv, dv, vd);
             const double alpha = exp((double)g[bt * Hv + hv]);
             const double bet = (double)beta[bt * Hv + hv];
             double *ot = o + ((size_t)c * T + t) * dv;
-            gdn_oracle_token(S, qt, kt, vt, alpha, bet, scale, dk, dv, e, f, ot);
+            gdn_oracle_token(S, qd, kd, vd, alpha, bet, scale, dk, dv, e, f, ot);
         }
         if (sT)
             memcpy(sT + (size_t)c * ssz, S, sizeof(double) * ssz);
-        free(S); free(e); free(f);
+        free(S); free(e); free(f); free(qd);
+    }
+    return failed ? -2 : 0;
+}
+
+/*
+ * Packed sequences with the input prologue.  Sequence i is token rows
+ * cu[i] .. cu[i+1]-1 (cu: N+1 nondecreasing offsets from 0 to T) of
+ *   q, k [T, Hk, dk]   v [T, Hv, dv]   beta, g [T, Hv]   o [T, Hv, dv]
+ * and has its own state: s0, sT [N, Hv, dk, dv] (s0 NULL = zeros, sT NULL = not written).
+ * `flags` selects the prologue applied to every token's stored inputs before Eq. (1):
+ * 1 = L2-normalise q and k, 2 = beta from a logit, 4 = log alpha from a logit.
+ * Returns 0, -1 on bad arguments, -2 on allocation failure.
+ */
+int gdn_oracle_run_packed(const float *q, const float *k, const float *v,
+                          const float *beta, const float *g, const double *s0,
+                          const int64_t *cu, int N, int T, int Hk, int Hv, int dk,
+                          int dv, double scale, unsigned flags, double *o, double *sT,
+                          int nthreads)
+{
+    if (!gdn_oracle_dims_ok(N, T, Hk, Hv, dk, dv) || cu == NULL)
+        return -1;
+    if (cu[0] != 0 || cu[N] != T)
+        return -1;
+    for (int i = 0; i < N; ++i)
+        if (cu[i + 1] < cu[i])
+            return -1;
+    if (T > 0 && (q == NULL || k == NULL || v == NULL || beta == NULL ||
+                  g == NULL || o == NULL))
+        return -1;
+    const int G = Hv / Hk;
+    const int64_t n = (int64_t)N * Hv;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : failed)
+#endif
+    for (int64_t c = 0; c < n; ++c) {
+        const int i = (int)(c / Hv), hv = (int)(c % Hv), hq = hv / G;
+        const size_t ssz = (size_t)dk * dv;
+        double *S = (double *)malloc(sizeof(double) * ssz);
+        double *buf = (double *)malloc(sizeof(double) * (size_t)(2 * dk + 3 * dv));
+        if (!S || !buf) {
+            free(S); free(buf);
+            failed = 1;
+            continue;
+        }
+        double *qd = buf, *kd = qd + dk, *vd = kd + dk, *e = vd + dv, *f = e + dv;
+        if (s0)
+            memcpy(S, s0 + (size_t)c * ssz, sizeof(double) * ssz);
+        else
+            memset(S, 0, sizeof(double) * ssz);
+        for (int64_t r = cu[i]; r < cu[i + 1]; ++r) {
+            gdn_oracle_widen(q + ((size_t)r * Hk + hq) * dk, dk, qd);
+            gdn_oracle_widen(k + ((size_t)r * Hk + hq) * dk, dk, kd);
+            gdn_oracle_widen(v + ((size_t)r * Hv + hv) * dv, dv, vd);
+            double gx = (double)g[(size_t)r * Hv + hv];
+            double bx = (double)beta[(size_t)r * Hv + hv];
+            if (flags & GDN_ORACLE_QK_L2NORM) {
+                gdn_oracle_l2normalise(qd, dk);
+                gdn_oracle_l2normalise(kd, dk);
+            }
+            if (flags & GDN_ORACLE_BETA_LOGIT)
+                bx = gdn_oracle_sigmoid(bx);
+            if (flags & GDN_ORACLE_G_LOGIT)
+                gx = gdn_oracle_log_sigmoid(gx);
+            gdn_oracle_token(S, qd, kd, vd, exp(gx), bx, scale, dk, dv, e, f,
+                             o + ((size_t)r * Hv + hv) * dv);
+        }
+        if (sT)
+            memcpy(sT + (size_t)c * ssz, S, sizeof(double) * ssz);
+        free(S); free(buf);
     }
     return failed ? -2 : 0;
 }
@@ -189,13 +307,20 @@ int gdn_oracle_decode_step(const float *q, const float *k, const float *v,
             failed = 1;
             continue;
         }
-        gdn_oracle_token(state + (size_t)id * dk * dv,
-                         q + ((size_t)b * Hk + hq) * dk,
-                         k + ((size_t)b * Hk + hq) * dk,
-                         v + (size_t)id * dv, exp((double)g[id]),
-                         (double)beta[id], scale, dk, dv, e, f,
-                         o + (size_t)id * dv);
-        free(e); free(f);
+        double *qd = (double *)malloc(sizeof(double) * (size_t)(2 * dk + dv));
+        if (!qd) {
+            free(e); free(f);
+            failed = 1;
+            continue;
+        }
+        double *kd = qd + dk, *vd = kd + dk;
+        gdn_oracle_widen(q + ((size_t)b * Hk + hq) * dk, dk, qd);
+        gdn_oracle_widen(k + ((size_t)b * Hk + hq) * dk, dk, kd);
+        gdn_oracle_widen(v + (size_t)id * dv, dv, vd);
+        gdn_oracle_token(state + (size_t)id * dk * dv, qd, kd, vd,
+                         exp((double)g[id]), (double)beta[id], scale, dk, dv,
+                         e, f, o + (size_t)id * dv);
+        free(e); free(f); free(qd);
     }
     return failed ? -2 : 0;
 }

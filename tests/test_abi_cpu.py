@@ -70,7 +70,8 @@ def test_workspace_size_rejects_bad_sizes(lib):
 # fake, well-aligned, non-overlapping device addresses: validation must reject the call
 # before anything dereferences them
 BASE = 1 << 40
-P = {n: BASE + i * (1 << 32) for i, n in enumerate(["q", "k", "v", "beta", "g", "s0", "o", "sT"])}
+P = {n: BASE + i * (1 << 32)
+     for i, n in enumerate(["q", "k", "v", "beta", "g", "s0", "o", "sT", "cu"])}
 
 
 def prefill(**kw):
@@ -138,7 +139,7 @@ def test_decode_empty_batch_is_noop(lib):
 def decode_tokens(**kw):
     a = dict(q=P["q"], k=P["k"], v=P["v"], beta=P["beta"], g=P["g"], state_in=P["s0"],
              state_out=P["s0"], o=P["o"], B=2, T=2, Hk=2, Hv=4, dk=16, dv=32, scale=1.0,
-             in_dtype=gdn.GDN_BF16, out_dtype=gdn.GDN_F32, stream=None)
+             flags=0, in_dtype=gdn.GDN_BF16, out_dtype=gdn.GDN_F32, stream=None)
     a.update(kw)
     return gdn.gdn_decode_tokens(**a)
 
@@ -154,6 +155,7 @@ def decode_tokens(**kw):
     (dict(q=None), gdn.GDN_ERR_INVALID_ARG),
     (dict(o=P["k"]), gdn.GDN_ERR_INVALID_ARG),               # o overlaps k
     (dict(state_in=P["s0"], state_out=P["sT"], o=P["s0"]), gdn.GDN_ERR_INVALID_ARG),
+    (dict(flags=8), gdn.GDN_ERR_INVALID_ARG),                # unknown prologue flag
 ])
 def test_decode_tokens_validation(lib, kw, status):
     assert decode_tokens(**kw) == status
@@ -171,3 +173,33 @@ def test_missing_library_fails_loudly(tmp_path):
             gdn.load_library(str(tmp_path / "missing.so"))
     finally:
         gdn._lib = saved
+
+
+def prefill_varlen(**kw):
+    a = dict(q=P["q"], k=P["k"], v=P["v"], beta=P["beta"], g=P["g"], initial_state=P["s0"],
+             o=P["o"], final_state=P["sT"], cu_seqlens=P["cu"], num_seqs=3, T=100, Hk=2, Hv=4,
+             dk=64, dv=64, chunk=64, scale=1.0, flags=gdn.GDN_QK_L2NORM | gdn.GDN_BETA_LOGIT,
+             in_dtype=gdn.GDN_BF16, out_dtype=gdn.GDN_F32, workspace=None, workspace_bytes=0,
+             stream=None)
+    a.update(kw)
+    return gdn.gdn_chunk_fwd_varlen(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=16), gdn.GDN_ERR_INVALID_ARG),
+    (dict(num_seqs=0), gdn.GDN_ERR_INVALID_ARG),           # packed needs >= 1 sequence
+    (dict(cu_seqlens=P["cu"] + 2), gdn.GDN_ERR_INVALID_ARG),  # misaligned offsets
+    (dict(dk=48), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(chunk=128), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(q=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(o=P["q"] + 128), gdn.GDN_ERR_INVALID_ARG),       # o overlaps q
+])
+def test_prefill_varlen_validation(lib, kw, status):
+    assert prefill_varlen(**kw) == status
+
+
+def test_varlen_workspace(lib):
+    # packed sequences use the single-pass kernels: no workspace; dense = gdn_chunk_fwd's
+    assert gdn.gdn_chunk_fwd_varlen_workspace_size(4, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1) == 0
+    assert (gdn.gdn_chunk_fwd_varlen_workspace_size(1, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 0)
+            == gdn.gdn_chunk_fwd_workspace_size(1, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16))

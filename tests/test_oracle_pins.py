@@ -398,3 +398,103 @@ def test_bf16_rounding_helper():
     # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: rounds to even (1.0)
     assert r[1] == 1.0
     np.testing.assert_allclose(r, x, rtol=2 ** -8)
+
+
+# ------------------------------------------------------------------ packed sequences and prologue
+def _packed(lengths, Hk=2, Hv=4, dk=16, dv=8, seed=900, s0_std=0.3):
+    """Random packed inputs: the rows of len(lengths) sequences back to back."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    T, N = int(sum(lengths)), len(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    q = rng.standard_normal((T, Hk, dk)).astype(np.float32)
+    k = rng.standard_normal((T, Hk, dk)).astype(np.float32)
+    v = rng.standard_normal((T, Hv, dv)).astype(np.float32)
+    beta = rng.uniform(0.05, 0.95, (T, Hv)).astype(np.float32)
+    g = -rng.uniform(0.01, 0.3, (T, Hv)).astype(np.float32)
+    s0 = rng.standard_normal((N, Hv, dk, dv)) * s0_std
+    return dict(q=q, k=k, v=v, beta=beta, g=g, cu=cu, s0=s0)
+
+
+def test_packed_reduces_to_separate_sequences():
+    """Without a prologue, each packed sequence is exactly a run of the plain recurrence
+    over its own rows from its own state (including an empty one and a single token)."""
+    p = _packed([5, 0, 17, 1, 33])
+    o, sT = oracle.run_packed(p["q"], p["k"], p["v"], p["beta"], p["g"], p["cu"], s0=p["s0"],
+                              scale=0.7)
+    cu = p["cu"]
+    for i in range(len(cu) - 1):
+        a, b = cu[i], cu[i + 1]
+        oi, si = oracle.run(p["q"][None, a:b], p["k"][None, a:b], p["v"][None, a:b],
+                            p["beta"][None, a:b], p["g"][None, a:b], s0=p["s0"][i:i + 1],
+                            scale=0.7)
+        np.testing.assert_array_equal(o[a:b], oi[0])
+        np.testing.assert_array_equal(sT[i], si[0])
+
+
+def test_l2norm_prologue_is_scale_invariant_and_normalises():
+    """GDN_QK_L2NORM: (i) scaling a token's q or k by a power of two changes nothing (bitwise);
+    (ii) it equals the plain recurrence on q/||q||, k/||k|| formed independently in numpy."""
+    p = _packed([9, 14], seed=901)
+    o1, s1 = oracle.run_packed(p["q"], p["k"], p["v"], p["beta"], p["g"], p["cu"], s0=p["s0"],
+                               flags=oracle.QK_L2NORM)
+    rng = np.random.Generator(np.random.PCG64(902))
+    fq = (2.0 ** rng.integers(-6, 7, (p["q"].shape[0], p["q"].shape[1], 1))).astype(np.float32)
+    fk = (2.0 ** rng.integers(-6, 7, (p["k"].shape[0], p["k"].shape[1], 1))).astype(np.float32)
+    o2, s2 = oracle.run_packed(p["q"] * fq, p["k"] * fk, p["v"], p["beta"], p["g"], p["cu"],
+                               s0=p["s0"], flags=oracle.QK_L2NORM)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(s1, s2)
+    qn = p["q"].astype(np.float64)
+    qn /= np.linalg.norm(qn, axis=-1, keepdims=True)
+    kn = p["k"].astype(np.float64)
+    kn /= np.linalg.norm(kn, axis=-1, keepdims=True)
+    o3, s3 = oracle.run_packed(qn.astype(np.float32), kn.astype(np.float32), p["v"], p["beta"],
+                               p["g"], p["cu"], s0=p["s0"])
+    # the only difference: numpy's normalised values rounded to fp32 (u = 6e-8)
+    assert np.abs(o1 - o3).max() <= 1e-6 * np.abs(o1).max()
+    assert np.abs(s1 - s3).max() <= 1e-6 * np.abs(s1).max()
+
+
+def test_beta_logit_zero_is_one_half():
+    """GDN_BETA_LOGIT with logits 0 is exactly beta = 1/2 (sigmoid(0) = 1/2 in any precision)."""
+    p = _packed([11, 6], seed=903)
+    z = np.zeros_like(p["beta"])
+    o1, s1 = oracle.run_packed(p["q"], p["k"], p["v"], z, p["g"], p["cu"], s0=p["s0"],
+                               flags=oracle.BETA_LOGIT)
+    o2, s2 = oracle.run_packed(p["q"], p["k"], p["v"], z + 0.5, p["g"], p["cu"], s0=p["s0"])
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(s1, s2)
+
+
+def test_g_logit_pure_decay_closed_form():
+    """GDN_G_LOGIT with beta = 0: every state decays by the product of sigmoid(x_t), and
+    o_t = (prod_{s<=t} sigmoid(x_s)) S0^T q_t (the closed form of Eq. (1) at beta = 0)."""
+    p = _packed([7, 12], Hk=1, Hv=2, dk=8, dv=4, seed=904)
+    rng = np.random.Generator(np.random.PCG64(905))
+    x = rng.uniform(-4, 6, p["g"].shape).astype(np.float32)
+    zero = np.zeros_like(p["beta"])
+    o, sT = oracle.run_packed(p["q"], p["k"], p["v"], zero, x, p["cu"], s0=p["s0"],
+                              flags=oracle.G_LOGIT)
+    sig = 1.0 / (1.0 + np.exp(-x.astype(np.float64)))
+    cu = p["cu"]
+    for i in range(len(cu) - 1):
+        a, b = cu[i], cu[i + 1]
+        for h in range(2):
+            decay = np.cumprod(sig[a:b, h])
+            np.testing.assert_allclose(sT[i, h], decay[-1] * p["s0"][i, h], rtol=1e-12, atol=0)
+            ref = decay[:, None] * (p["q"][a:b, 0].astype(np.float64) @ p["s0"][i, h])
+            np.testing.assert_allclose(o[a:b, h], ref, rtol=1e-12, atol=1e-300)
+    # a very large logit means alpha = 1 to within rounding: no decay at all
+    o1, s1 = oracle.run_packed(p["q"], p["k"], p["v"], p["beta"], np.full_like(x, 60.0),
+                               p["cu"], s0=p["s0"], flags=oracle.G_LOGIT)
+    o2, s2 = oracle.run_packed(p["q"], p["k"], p["v"], p["beta"], np.zeros_like(x), p["cu"],
+                               s0=p["s0"])
+    np.testing.assert_allclose(o1, o2, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(s1, s2, rtol=1e-13, atol=1e-15)
+
+
+def test_packed_rejects_bad_offsets():
+    p = _packed([3, 4], seed=906)
+    for cu in ([0, 5, 6], [1, 3, 7], [0, 4, 3, 7][:3]):
+        with pytest.raises(RuntimeError):
+            oracle.run_packed(p["q"], p["k"], p["v"], p["beta"], p["g"], cu)

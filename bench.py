@@ -195,6 +195,17 @@ def prologue_and_packed(gdn, torch, dev, stream, pt, pc, o, fs):
     packed = lambda: gdn.chunk_fwd_varlen(q, k, v, beta, ga, cu_seqlens=cu_t, chunk=64,
                                           flags=allf, o=ob, final_state=sb)
     packed_ms = _time(torch, stream, packed, reps=5)
+    # backward of the prefill workload: all gradients, from a random gradient of o
+    d_o = torch.randn(pt["v"].shape, device=dev, generator=g)
+    bws = torch.empty(gdn.gdn_backward_workspace_size(B, T, pt["q"].shape[2], pt["v"].shape[2],
+                                                      pt["q"].shape[3], pt["v"].shape[3]),
+                      dtype=torch.uint8, device=dev)
+    bwd = lambda: gdn.backward(pt["q"], pt["k"], pt["v"], pt["beta"], pt["g"], d_o,
+                               initial_state=pt["s0"], workspace=bws)
+    bwd_ms = _time(torch, stream, bwd, reps=3)
+    res["backward"] = {"workload": pc["name"], "ms": round(bwd_ms, 3),
+                       "tokens_per_s": round(B * T / (bwd_ms * 1e-3), 1),
+                       "kernel": "backward_kernel (token-recurrent, checkpoint every 64 tokens)"}
     res["packed"] = {"sequences": 32, "tokens": Tp, "min_len": int(lengths.min()),
                      "max_len": int(lengths.max()), "heads": H, "d": d, "dtype": "bf16",
                      "flags": "qk_l2norm+beta_logit+g_logit",

@@ -195,6 +195,32 @@ gdn_status_t gdn_chunk_fwd_varlen(const void *q, const void *k, const void *v, c
 size_t gdn_chunk_fwd_varlen_workspace_size(int num_seqs, int T, int Hk, int Hv, int dk, int dv,
                                            int chunk, gdn_dtype_t in_dtype, int packed);
 
+/*
+ * Backward: the gradients of Eq. (1) over T tokens for every (b, hv) chain (training).
+ * Inputs are the forward inputs of gdn_chunk_fwd (already in the form the recurrence takes:
+ * unit q/k, beta, g = log alpha; the input prologue is not differentiated here) plus
+ *   d_o            [B, T, Hv, dv]   dout_dtype   gradient of the outputs o
+ *   d_final_state  [B, Hv, dk, dv]  fp32, gradient of the final state, or NULL for zero
+ * and it writes, all fp32, fully overwritten:
+ *   dq, dk         [B, T, Hk, dk]   (a q/k head's gradient sums over its Hv/Hk value heads)
+ *   dv             [B, T, Hv, dv]
+ *   dbeta, dg      [B, T, Hv]       (dg: gradient w.r.t. g = log alpha)
+ *   d_initial_state [B, Hv, dk, dv] or NULL to skip
+ * Outputs must not overlap each other or any input.  The workspace (at least
+ * gdn_backward_workspace_size(...) bytes, 256-byte aligned) holds a state checkpoint every
+ * 64 tokens per chain, one block of recomputed states per chain and, with grouped heads, the
+ * per-value-head parts of dq and dk.  Supported: dk, dv in {16, 32, 64, 128}; in_dtype and
+ * dout_dtype GDN_F32 or GDN_BF16.  Deterministic (no atomics).  B = 0 is a no-op.
+ */
+size_t gdn_backward_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv);
+gdn_status_t gdn_backward(const void *q, const void *k, const void *v, const void *beta,
+                          const void *g, const float *initial_state, const void *d_o,
+                          const float *d_final_state, float *dq, float *dk, float *dv,
+                          float *dbeta, float *dg, float *d_initial_state, int B, int T, int Hk,
+                          int Hv, int dk_dim, int dv_dim, float scale, gdn_dtype_t in_dtype,
+                          gdn_dtype_t dout_dtype, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
 #ifdef __cplusplus
 }
 #endif

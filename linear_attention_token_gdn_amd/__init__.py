@@ -12,7 +12,8 @@ stream through ctypes.  There is no CPU fallback: without the built library ever
 
 The C entry points are exposed unchanged as ``gdn_chunk_fwd``, ``gdn_decode_step``,
 ``gdn_decode_tokens``, ``gdn_chunk_fwd_varlen``, ``gdn_chunk_fwd_varlen_workspace_size``,
-``gdn_chunk_fwd_workspace_size``, ``gdn_chunk_fwd_plan``,
+``gdn_backward``, ``gdn_backward_workspace_size``, ``gdn_chunk_fwd_workspace_size``,
+``gdn_chunk_fwd_plan``,
 ``gdn_status_string`` and ``gdn_abi_version``.
 """
 from __future__ import annotations
@@ -28,7 +29,8 @@ GDN_F32, GDN_BF16 = 0, 1
 GDN_QK_L2NORM, GDN_BETA_LOGIT, GDN_G_LOGIT = 1, 2, 4  # input prologue flags
 EXPORTED_SYMBOLS = ("gdn_abi_version", "gdn_status_string", "gdn_chunk_fwd_workspace_size",
                     "gdn_chunk_fwd_plan", "gdn_chunk_fwd", "gdn_decode_step", "gdn_decode_tokens",
-                    "gdn_chunk_fwd_varlen", "gdn_chunk_fwd_varlen_workspace_size")
+                    "gdn_chunk_fwd_varlen", "gdn_chunk_fwd_varlen_workspace_size",
+                    "gdn_backward", "gdn_backward_workspace_size")
 
 _lib = None
 
@@ -71,6 +73,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_chunk_fwd_varlen.restype = i
     lib.gdn_chunk_fwd_varlen_workspace_size.argtypes = [i, i, i, i, i, i, i, i, i]
     lib.gdn_chunk_fwd_varlen_workspace_size.restype = sz
+    lib.gdn_backward_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.gdn_backward_workspace_size.restype = sz
+    lib.gdn_backward.argtypes = [vp] * 14 + [i] * 6 + [f, i, i, vp, sz, vp]
+    lib.gdn_backward.restype = i
     _lib = lib
     return lib
 
@@ -131,6 +137,20 @@ def gdn_chunk_fwd_varlen_workspace_size(num_seqs, T, Hk, Hv, dk, dv, chunk, in_d
                                         packed) -> int:
     return int(load_library().gdn_chunk_fwd_varlen_workspace_size(num_seqs, T, Hk, Hv, dk, dv,
                                                                   chunk, in_dtype, packed))
+
+
+def gdn_backward_workspace_size(B, T, Hk, Hv, dk, dv) -> int:
+    return int(load_library().gdn_backward_workspace_size(B, T, Hk, Hv, dk, dv))
+
+
+def gdn_backward(q, k, v, beta, g, initial_state, d_o, d_final_state, dq, dk, dv, dbeta, dg,
+                 d_initial_state, B, T, Hk, Hv, dk_dim, dv_dim, scale, in_dtype, dout_dtype,
+                 workspace, workspace_bytes, stream) -> int:
+    """Raw call: pointer arguments are ints (device addresses) or None."""
+    return int(load_library().gdn_backward(
+        q, k, v, beta, g, initial_state, d_o, d_final_state, dq, dk, dv, dbeta, dg,
+        d_initial_state, B, T, Hk, Hv, dk_dim, dv_dim, scale, in_dtype, dout_dtype, workspace,
+        workspace_bytes, stream))
 
 
 # ------------------------------------------------------------------ torch-facing wrappers
@@ -313,3 +333,42 @@ def chunk_fwd_varlen(q, k, v, beta, g, cu_seqlens=None, initial_state=None,
     if st != GDN_OK:
         raise GdnError(st, "gdn_chunk_fwd_varlen")
     return o, final_state
+
+
+def backward(q, k, v, beta, g, d_o, initial_state=None, d_final_state=None, scale=1.0,
+             want_d_initial_state=True, workspace=None):
+    """Gradients of ``chunk_fwd``'s outputs.  Shapes as ``chunk_fwd``; d_o: [B,T,Hv,dv]
+    (float32 or bfloat16); d_final_state: [B,Hv,dk,dv] float32 or None.  Returns a dict of
+    float32 tensors dq, dk [B,T,Hk,dk], dv [B,T,Hv,dv], dbeta, dg [B,T,Hv] and
+    d_initial_state [B,Hv,dk,dv] (or None)."""
+    import torch
+    lib = load_library()
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dev, dt = q.device, q.dtype
+    for t, n, s_ in ((q, "q", (B, T, Hk, dk)), (k, "k", (B, T, Hk, dk)),
+                     (v, "v", (B, T, Hv, dv)), (beta, "beta", (B, T, Hv)), (g, "g", (B, T, Hv))):
+        _check(t, n, s_, dt, dev)
+    _check(d_o, "d_o", (B, T, Hv, dv), d_o.dtype, dev)
+    for st, n in ((initial_state, "initial_state"), (d_final_state, "d_final_state")):
+        if st is not None:
+            _check(st, n, (B, Hv, dk, dv), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dq": torch.empty((B, T, Hk, dk), **f32), "dk": torch.empty((B, T, Hk, dk), **f32),
+           "dv": torch.empty((B, T, Hv, dv), **f32), "dbeta": torch.empty((B, T, Hv), **f32),
+           "dg": torch.empty((B, T, Hv), **f32),
+           "d_initial_state": torch.empty((B, Hv, dk, dv), **f32) if want_d_initial_state else None}
+    need = int(lib.gdn_backward_workspace_size(B, T, Hk, Hv, dk, dv))
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.gdn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(initial_state),
+                          _ptr(d_o), _ptr(d_final_state), _ptr(out["dq"]), _ptr(out["dk"]),
+                          _ptr(out["dv"]), _ptr(out["dbeta"]), _ptr(out["dg"]),
+                          _ptr(out["d_initial_state"]), B, T, Hk, Hv, dk, dv, float(scale),
+                          _dtype_code(dt), _dtype_code(d_o.dtype), _ptr(workspace), ws_bytes,
+                          stream)
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_backward")
+    return out

@@ -231,4 +231,63 @@ gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v, const 
                              in_dtype, out_dtype, stream);
 }
 
+size_t gdn_backward_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv) {
+    if (B <= 0 || T < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk != 0 || !dim_supported(dk) ||
+        !dim_supported(dv))
+        return 0;
+    return gdn::backward_workspace(B, T, Hk, Hv, dk, dv);
+}
+
+gdn_status_t gdn_backward(const void *q, const void *k, const void *v, const void *beta,
+                          const void *g, const float *initial_state, const void *d_o,
+                          const float *d_final_state, float *dq, float *dk, float *dv,
+                          float *dbeta, float *dg, float *d_initial_state, int B, int T, int Hk,
+                          int Hv, int dk_dim, int dv_dim, float scale, gdn_dtype_t in_dtype,
+                          gdn_dtype_t dout_dtype, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+    if (B < 0 || T < 0 || Hk <= 0 || Hv <= 0 || dk_dim <= 0 || dv_dim <= 0 || Hv % Hk != 0)
+        return GDN_ERR_INVALID_ARG;
+    if (!dtype_known(in_dtype) || !dtype_known(dout_dtype)) return GDN_ERR_UNSUPPORTED;
+    if (!dim_supported(dk_dim) || !dim_supported(dv_dim)) return GDN_ERR_UNSUPPORTED;
+    if (B == 0) return GDN_OK;
+    const size_t BT = size_t(B) * T;
+    const size_t ib = dtype_bytes(in_dtype), db = dtype_bytes(dout_dtype);
+    const size_t nq = BT * Hk * dk_dim, nv = BT * Hv * dv_dim, ng = BT * Hv;
+    const size_t ns = size_t(B) * Hv * dk_dim * dv_dim;
+    if (T > 0) {
+        if (!q || !k || !v || !beta || !g || !d_o || !dq || !dk || !dv || !dbeta || !dg)
+            return GDN_ERR_INVALID_ARG;
+        if (!aligned(q, ib) || !aligned(k, ib) || !aligned(v, ib) || !aligned(beta, ib) ||
+            !aligned(g, ib) || !aligned(d_o, db) || !aligned(dv, 16))
+            return GDN_ERR_INVALID_ARG;
+        // every output is disjoint from every input and from the other outputs
+        const void *in[] = {q, k, v, beta, g, d_o, initial_state, d_final_state};
+        const size_t inb[] = {nq * ib, nq * ib, nv * ib, ng * ib, ng * ib, nv * db, ns * 4, ns * 4};
+        float *out[] = {dq, dk, dv, dbeta, dg, d_initial_state};
+        const size_t outb[] = {nq * 4, nq * 4, nv * 4, ng * 4, ng * 4, ns * 4};
+        for (int i = 0; i < 6; ++i) {
+            for (int j = 0; j < 8; ++j)
+                if (overlap(out[i], outb[i], in[j], inb[j])) return GDN_ERR_INVALID_ARG;
+            for (int j = i + 1; j < 6; ++j)
+                if (overlap(out[i], outb[i], out[j], outb[j])) return GDN_ERR_INVALID_ARG;
+        }
+    }
+    if ((initial_state && !aligned(initial_state, 16)) ||
+        (d_final_state && !aligned(d_final_state, 16)) ||
+        (d_initial_state && !aligned(d_initial_state, 16)))
+        return GDN_ERR_INVALID_ARG;
+    const size_t need = gdn::backward_workspace(B, T, Hk, Hv, dk_dim, dv_dim);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+        return GDN_ERR_INVALID_ARG;
+    gdn::BackwardArgs a;
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g; a.s0 = initial_state;
+    a.dO = d_o; a.dST = d_final_state;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dbeta = dbeta; a.dg = dg; a.dS0 = d_initial_state;
+    a.B = B; a.T = T; a.Hk = Hk; a.Hv = Hv; a.dk_ = dk_dim; a.dv_ = dv_dim; a.scale = scale;
+    a.in_dt = in_dtype; a.dout_dt = dout_dtype;
+    a.ws = workspace;
+    a.stream = static_cast<hipStream_t>(stream);
+    return gdn::launch_backward(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 }  // extern "C"

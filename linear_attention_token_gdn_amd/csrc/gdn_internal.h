@@ -39,6 +39,22 @@ struct DecodeArgs {
     hipStream_t stream;
 };
 
+struct BackwardArgs {
+    const void *q, *k, *v, *beta, *g;  // the forward inputs (in_dt)
+    const float *s0;                    // may be null (zero initial state)
+    const void *dO;                     // [B,T,Hv,dv] (dout_dt)
+    const float *dST;                   // may be null (zero)
+    float *dq, *dk, *dv, *dbeta, *dg, *dS0;  // dS0 may be null
+    int B, T, Hk, Hv, dk_, dv_;               // dk_, dv_: head sizes
+    float scale;
+    gdn_dtype_t in_dt, dout_dt;
+    void *ws;
+    hipStream_t stream;
+};
+// The reverse recurrence (csrc/backward.hip) and the workspace it needs.
+size_t backward_workspace(int B, int T, int Hk, int Hv, int dk, int dv);
+hipError_t launch_backward(const BackwardArgs &a);
+
 // Token-by-token kernel: every (dk, dv) in {16,32,64,128}^2, both dtypes.  It is the fp32
 // path and the fallback of the chunked kernel.
 hipError_t launch_recurrent(const PrefillArgs &a);

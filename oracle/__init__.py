@@ -67,6 +67,12 @@ def _load():
                                                   ctypes.c_double, ctypes.c_uint, f64p, f64p,
                                                   ctypes.c_int]
             lib.gdn_oracle_run_packed.restype = ctypes.c_int
+            lib.gdn_oracle_backward.argtypes = [f32p, f32p, f32p, f32p, f32p, f64p, f64p, f64p,
+                                                ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_double, f64p, f64p, f64p, f64p, f64p,
+                                                f64p]
+            lib.gdn_oracle_backward.restype = ctypes.c_int
             lib.gdn_oracle_max_threads.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -135,6 +141,34 @@ def run(q, k, v, beta, g, s0=None, scale=1.0, chains=None, nthreads=0,
 
 
 QK_L2NORM, BETA_LOGIT, G_LOGIT = 1, 2, 4  # input prologue flags
+
+
+def backward(q, k, v, beta, g, dO, s0=None, dST=None, scale=1.0):
+    """Gradients of the recurrence.  Shapes as ``run``; dO: [B,T,Hv,dv]; dST: [B,Hv,dk,dv]
+    or None.  Returns dict dq, dk [B,T,Hk,dk], dv [B,T,Hv,dv], dbeta, dg [B,T,Hv],
+    dS0 [B,Hv,dk,dv] (fp64; dg is the gradient w.r.t. g = log alpha)."""
+    lib = _load()
+    B, T, Hk, dk = np.shape(q)
+    Hv, dv = np.shape(v)[2], np.shape(v)[3]
+    q, k = _f32(q, (B, T, Hk, dk)), _f32(k, (B, T, Hk, dk))
+    v = _f32(v, (B, T, Hv, dv))
+    beta, g = _f32(beta, (B, T, Hv)), _f32(g, (B, T, Hv))
+    f64 = lambda a, shape: None if a is None else np.ascontiguousarray(a, dtype=np.float64).reshape(shape)
+    s0 = f64(s0, (B, Hv, dk, dv))
+    dST = f64(dST, (B, Hv, dk, dv))
+    dO = f64(dO, (B, T, Hv, dv))
+    out = {"dq": np.empty((B, T, Hk, dk)), "dk": np.empty((B, T, Hk, dk)),
+           "dv": np.empty((B, T, Hv, dv)), "dbeta": np.empty((B, T, Hv)),
+           "dg": np.empty((B, T, Hv)), "dS0": np.empty((B, Hv, dk, dv))}
+    p = lambda a: _ptr(a, ctypes.c_double)
+    rc = lib.gdn_oracle_backward(_ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float),
+                                 _ptr(v, ctypes.c_float), _ptr(beta, ctypes.c_float),
+                                 _ptr(g, ctypes.c_float), p(s0), p(dO), p(dST), B, T, Hk, Hv,
+                                 dk, dv, float(scale), p(out["dq"]), p(out["dk"]), p(out["dv"]),
+                                 p(out["dbeta"]), p(out["dg"]), p(out["dS0"]))
+    if rc != 0:
+        raise RuntimeError("gdn_oracle_backward failed with code %d" % rc)
+    return out
 
 
 def run_packed(q, k, v, beta, g, cu_seqlens, s0=None, scale=1.0, flags=0, nthreads=0,

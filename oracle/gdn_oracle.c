@@ -333,3 +333,136 @@ int gdn_oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/*
+ * Backward of the recurrence (reverse-mode differentiation of Eq. (1), token by token).
+ * Given the forward inputs and the gradients dO of the outputs o (and dST of the final
+ * state, or NULL for zero), returns the gradients of every input:
+ *   dq, dk [B, T, Hk, dk] (summed over the G value heads that share a q/k head)
+ *   dv [B, T, Hv, dv]   dbeta, dg [B, T, Hv] (dg: gradient w.r.t. g = log alpha)
+ *   dS0 [B, Hv, dk, dv]
+ * All fp64.  With X = S_{t-1}, e = X^T k, u = dS_t^T k (dS_t: gradient w.r.t. S_t once the
+ * read-out o_t = scale S_t^T q_t has added scale q dO_t^T):
+ *   S_t = alpha (X - beta k e^T) + beta k v^T
+ *   dq_t  = scale S_t dO_t
+ *   dv_t  = beta u
+ *   dbeta = u . (v - alpha e)
+ *   dalpha = <dS_t, X> - beta u . e,   dg = alpha dalpha
+ *   dk_t  = beta dS_t (v - alpha e) - alpha beta X u
+ *   dS_{t-1} = alpha (dS_t - beta k u^T)
+ * Returns 0, -1 on bad arguments, -2 on allocation failure.
+ */
+int gdn_oracle_backward(const float *q, const float *k, const float *v,
+                        const float *beta, const float *g, const double *s0,
+                        const double *dO, const double *dST, int B, int T, int Hk,
+                        int Hv, int dk, int dv, double scale, double *dq, double *dk_out,
+                        double *dv_out, double *dbeta, double *dg, double *dS0)
+{
+    if (!gdn_oracle_dims_ok(B, T, Hk, Hv, dk, dv))
+        return -1;
+    if (T > 0 && (!q || !k || !v || !beta || !g || !dO || !dq || !dk_out || !dv_out ||
+                  !dbeta || !dg))
+        return -1;
+    if (!dS0)
+        return -1;
+    const int G = Hv / Hk;
+    const size_t ssz = (size_t)dk * dv;
+    /* dq and dk accumulate over the value heads of a group */
+    if (T > 0) {
+        memset(dq, 0, sizeof(double) * (size_t)B * T * Hk * dk);
+        memset(dk_out, 0, sizeof(double) * (size_t)B * T * Hk * dk);
+    }
+    double *hist = (double *)malloc(sizeof(double) * ssz * (size_t)(T + 1));
+    double *dS = (double *)malloc(sizeof(double) * ssz);
+    double *buf = (double *)malloc(sizeof(double) * (size_t)(3 * dk + 6 * dv));
+    if (!hist || !dS || !buf) {
+        free(hist); free(dS); free(buf);
+        return -2;
+    }
+    double *qd = buf, *kd = qd + dk, *vd = kd + dk, *e = vd + dv, *f = e + dv, *o = f + dv;
+    double *u = o + dv, *w = u + dv, *ro = w + dv, *tmp = ro + dv;
+    (void)tmp;
+    for (int b = 0; b < B; ++b)
+        for (int hv = 0; hv < Hv; ++hv) {
+            const int hq = hv / G;
+            const size_t chain = (size_t)b * Hv + hv;
+            /* forward, keeping every state S_0 .. S_T */
+            if (s0)
+                memcpy(hist, s0 + chain * ssz, sizeof(double) * ssz);
+            else
+                memset(hist, 0, sizeof(double) * ssz);
+            for (int t = 0; t < T; ++t) {
+                const size_t bt = (size_t)b * T + t;
+                memcpy(hist + (size_t)(t + 1) * ssz, hist + (size_t)t * ssz, sizeof(double) * ssz);
+                gdn_oracle_widen(q + (bt * Hk + hq) * dk, dk, qd);
+                gdn_oracle_widen(k + (bt * Hk + hq) * dk, dk, kd);
+                gdn_oracle_widen(v + (bt * Hv + hv) * dv, dv, vd);
+                gdn_oracle_token(hist + (size_t)(t + 1) * ssz, qd, kd, vd,
+                                 exp((double)g[bt * Hv + hv]), (double)beta[bt * Hv + hv],
+                                 scale, dk, dv, e, f, o);
+            }
+            /* reverse */
+            if (dST)
+                memcpy(dS, dST + chain * ssz, sizeof(double) * ssz);
+            else
+                memset(dS, 0, sizeof(double) * ssz);
+            for (int t = T - 1; t >= 0; --t) {
+                const size_t bt = (size_t)b * T + t;
+                const double *X = hist + (size_t)t * ssz, *St = hist + (size_t)(t + 1) * ssz;
+                const double alpha = exp((double)g[bt * Hv + hv]);
+                const double bet = (double)beta[bt * Hv + hv];
+                gdn_oracle_widen(q + (bt * Hk + hq) * dk, dk, qd);
+                gdn_oracle_widen(k + (bt * Hk + hq) * dk, dk, kd);
+                gdn_oracle_widen(v + (bt * Hv + hv) * dv, dv, vd);
+                const double *dOt = dO + (bt * Hv + hv) * dv;
+                /* read-out: o_t = scale S_t^T q  ->  dq_t and dS_t += scale q dO^T */
+                double *dqt = dq + (bt * Hk + hq) * dk;
+                for (int i = 0; i < dk; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < dv; ++j)
+                        acc += St[(size_t)i * dv + j] * dOt[j];
+                    dqt[i] += scale * acc;
+                    for (int j = 0; j < dv; ++j)
+                        dS[(size_t)i * dv + j] += scale * qd[i] * dOt[j];
+                }
+                /* e = X^T k, u = dS^T k */
+                for (int j = 0; j < dv; ++j) {
+                    double ae = 0.0, au = 0.0;
+                    for (int i = 0; i < dk; ++i) {
+                        ae += X[(size_t)i * dv + j] * kd[i];
+                        au += dS[(size_t)i * dv + j] * kd[i];
+                    }
+                    e[j] = ae;
+                    u[j] = au;
+                }
+                double db = 0.0, ue = 0.0, dsx = 0.0;
+                for (int j = 0; j < dv; ++j) {
+                    w[j] = vd[j] - alpha * e[j];
+                    db += u[j] * w[j];
+                    ue += u[j] * e[j];
+                    dv_out[(bt * Hv + hv) * dv + j] = bet * u[j];
+                }
+                for (size_t n = 0; n < ssz; ++n)
+                    dsx += dS[n] * X[n];
+                dbeta[bt * Hv + hv] = db;
+                dg[bt * Hv + hv] = alpha * (dsx - bet * ue);
+                /* dk_t = beta dS w - alpha beta X u */
+                double *dkt = dk_out + (bt * Hk + hq) * dk;
+                for (int i = 0; i < dk; ++i) {
+                    double a1 = 0.0, a2 = 0.0;
+                    for (int j = 0; j < dv; ++j) {
+                        a1 += dS[(size_t)i * dv + j] * w[j];
+                        a2 += X[(size_t)i * dv + j] * u[j];
+                    }
+                    dkt[i] += bet * a1 - alpha * bet * a2;
+                }
+                /* dS_{t-1} = alpha (dS - beta k u^T) */
+                for (int i = 0; i < dk; ++i)
+                    for (int j = 0; j < dv; ++j)
+                        dS[(size_t)i * dv + j] = alpha * (dS[(size_t)i * dv + j] - bet * kd[i] * u[j]);
+            }
+            memcpy(dS0 + chain * ssz, dS, sizeof(double) * ssz);
+        }
+    free(hist); free(dS); free(buf);
+    return 0;
+}

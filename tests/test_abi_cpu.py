@@ -203,3 +203,35 @@ def test_varlen_workspace(lib):
     assert gdn.gdn_chunk_fwd_varlen_workspace_size(4, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1) == 0
     assert (gdn.gdn_chunk_fwd_varlen_workspace_size(1, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 0)
             == gdn.gdn_chunk_fwd_workspace_size(1, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16))
+
+
+def backward_call(**kw):
+    a = dict(q=P["q"], k=P["k"], v=P["v"], beta=P["beta"], g=P["g"], initial_state=P["s0"],
+             d_o=P["o"], d_final_state=None, dq=P["sT"], dk=P["sT"] + (1 << 28),
+             dv=P["sT"] + (2 << 28), dbeta=P["sT"] + (3 << 28), dg=P["cu"],
+             d_initial_state=P["cu"] + (1 << 28), B=2, T=8, Hk=1, Hv=2, dk_dim=16, dv_dim=16,
+             scale=1.0, in_dtype=gdn.GDN_BF16, dout_dtype=gdn.GDN_F32, workspace=None,
+             workspace_bytes=0, stream=None)
+    a.update(kw)
+    return gdn.gdn_backward(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hv=3), gdn.GDN_ERR_INVALID_ARG),
+    (dict(dk_dim=24), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(dout_dtype=9), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(dq=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(dq=P["q"]), gdn.GDN_ERR_INVALID_ARG),              # output overlaps an input
+    (dict(dk=P["sT"] + 64), gdn.GDN_ERR_INVALID_ARG),        # outputs overlap each other
+    (dict(), gdn.GDN_ERR_INVALID_ARG),                        # no workspace given
+])
+def test_backward_validation(lib, kw, status):
+    assert backward_call(**kw) == status
+
+
+def test_backward_workspace_size(lib):
+    n = gdn.gdn_backward_workspace_size(1, 4096, 16, 16, 128, 128)
+    assert n == (16 * 64 + 16 * 65) * 128 * 128 * 4      # checkpoints + one block per chain
+    assert gdn.gdn_backward_workspace_size(1, 100, 1, 2, 64, 64) > 0
+    assert gdn.gdn_backward_workspace_size(0, 100, 1, 2, 64, 64) == 0
+    assert backward_call(B=0) == gdn.GDN_OK

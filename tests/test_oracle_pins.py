@@ -498,3 +498,76 @@ def test_packed_rejects_bad_offsets():
     for cu in ([0, 5, 6], [1, 3, 7], [0, 4, 3, 7][:3]):
         with pytest.raises(RuntimeError):
             oracle.run_packed(p["q"], p["k"], p["v"], p["beta"], p["g"], cu)
+
+
+# ------------------------------------------------------------------ backward
+def _torch_forward(q, k, v, beta, g, s0, scale):
+    """Plain float64 torch loop of Eq. (1), used only to get reference gradients from autograd
+    (an independent derivation of the backward)."""
+    import torch
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    G = Hv // Hk
+    outs, finals = [], []
+    for b in range(B):
+        ob, fb = [], []
+        for hv in range(Hv):
+            S = s0[b, hv]
+            ot = []
+            for t in range(T):
+                kt, qt, vt = k[b, t, hv // G], q[b, t, hv // G], v[b, t, hv]
+                a, bt = torch.exp(g[b, t, hv]), beta[b, t, hv]
+                S = a * (S - bt * torch.outer(kt, kt @ S)) + bt * torch.outer(kt, vt)
+                ot.append(scale * (S.T @ qt))
+            ob.append(torch.stack(ot))
+            fb.append(S)
+        outs.append(torch.stack(ob, dim=1))
+        finals.append(torch.stack(fb))
+    return torch.stack(outs), torch.stack(finals)
+
+
+@pytest.mark.parametrize("B,T,Hk,Hv,dk,dv", [(1, 5, 1, 1, 4, 3), (2, 7, 1, 2, 3, 5)])
+def test_backward_matches_autograd(B, T, Hk, Hv, dk, dv):
+    """Every gradient of the oracle's backward against torch autograd (float64) through a
+    plain forward loop, with random upstream gradients of the outputs and the final state."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.Generator(np.random.PCG64(950 + T))
+    q = rng.standard_normal((B, T, Hk, dk)).astype(np.float32)
+    k = rng.standard_normal((B, T, Hk, dk)).astype(np.float32) * 0.5
+    v = rng.standard_normal((B, T, Hv, dv)).astype(np.float32)
+    beta = rng.uniform(0.1, 0.9, (B, T, Hv)).astype(np.float32)
+    g = -rng.uniform(0.01, 0.5, (B, T, Hv)).astype(np.float32)
+    s0 = rng.standard_normal((B, Hv, dk, dv))
+    dO = rng.standard_normal((B, T, Hv, dv))
+    dST = rng.standard_normal((B, Hv, dk, dv))
+    scale = 0.75
+    ref = oracle.backward(q, k, v, beta, g, dO, s0=s0, dST=dST, scale=scale)
+    tt = {n: torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=True)
+          for n, a in (("q", q), ("k", k), ("v", v), ("beta", beta), ("g", g), ("s0", s0))}
+    o, sT = _torch_forward(tt["q"], tt["k"], tt["v"], tt["beta"], tt["g"], tt["s0"], scale)
+    loss = (o * torch.tensor(dO)).sum() + (sT * torch.tensor(dST)).sum()
+    loss.backward()
+    for name, key in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("beta", "dbeta"), ("g", "dg"),
+                      ("s0", "dS0")):
+        np.testing.assert_allclose(ref[key], tt[name].grad.numpy(), rtol=1e-10, atol=1e-12,
+                                   err_msg=key)
+
+
+def test_backward_pure_readout_closed_form():
+    """beta = 0 and g = 0 keep the state fixed: o_t = scale S0^T q_t, so dS0 = dST +
+    scale sum_t q_t dO_t^T, dq_t = scale S0 dO_t, and dk = dv = dbeta-free terms vanish."""
+    rng = np.random.Generator(np.random.PCG64(960))
+    B, T, H, dk, dv = 1, 6, 1, 4, 3
+    q = rng.standard_normal((B, T, H, dk)).astype(np.float32)
+    k = rng.standard_normal((B, T, H, dk)).astype(np.float32)
+    v = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    zero = np.zeros((B, T, H), dtype=np.float32)
+    s0 = rng.standard_normal((B, H, dk, dv))
+    dO = rng.standard_normal((B, T, H, dv))
+    dST = rng.standard_normal((B, H, dk, dv))
+    r = oracle.backward(q, k, v, zero, zero, dO, s0=s0, dST=dST, scale=2.0)
+    qd = q.astype(np.float64)[0, :, 0]
+    np.testing.assert_allclose(r["dS0"][0, 0], dST[0, 0] + 2.0 * qd.T @ dO[0, :, 0], rtol=1e-13)
+    np.testing.assert_allclose(r["dq"][0, :, 0], 2.0 * dO[0, :, 0] @ s0[0, 0].T, rtol=1e-13)
+    np.testing.assert_array_equal(r["dk"], 0.0)
+    np.testing.assert_array_equal(r["dv"], 0.0)

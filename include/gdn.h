@@ -30,7 +30,7 @@
  *     surface at the caller's next synchronisation of the stream.  NaN and Inf in the
  *     inputs propagate; they are not checked.
  *   - Results are deterministic: the same inputs, sizes and stream give bit-identical
- *     outputs (no atomics are used).
+ *     outputs (no floating-point atomics; the only atomics are integer counts in LDS).
  */
 #ifndef GDN_H
 #define GDN_H
@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -220,6 +220,46 @@ gdn_status_t gdn_backward(const void *q, const void *k, const void *v, const voi
                           int Hv, int dk_dim, int dv_dim, float scale, gdn_dtype_t in_dtype,
                           gdn_dtype_t dout_dtype, void *workspace, size_t workspace_bytes,
                           void *stream);
+
+/*
+ * QSA compressed indexer (explainer page "論文解説: Qwen3.8-Next の設計", section "部品②: QSA"):
+ * for every query token, the key blocks its sparse attention keeps.  The indexer is
+ * multi-query attention with Hq = 4 query heads over one shared key head.  Keys are averaged
+ * over blocks of r tokens before the position encoding, and each block is rotated at the
+ * position of its first token; scoring then costs one product per (query, block) instead of
+ * per (query, key).
+ *
+ *   q            [B, T, 4, d]   in_dtype   indexer queries (query at position t = row t)
+ *   k            [B, T, d]      in_dtype   indexer keys
+ *   sel          [B, T, nsel]   int32 out  kept block indices of each query, ascending, padded
+ *                                          with -1 when fewer than nsel blocks are eligible;
+ *                                          block j stands for tokens j*r .. min((j+1)r, T)-1
+ *   importance   [B, T, nb]     fp32 out   (nb = ceil(T/r)) the importance of every block for
+ *                                          every query, 0 where not eligible; NULL to skip
+ *   r            tokens per block (the compression rate; 4 on the page)
+ *   nsel         blocks kept per query (the token budget / r; 2048 / 4 = 512 on the page)
+ *   rope_dims    leading dimensions rotated (rotate-half pairs (i, i + rope_dims/2), angle
+ *                pos * rope_base^(-2i/rope_dims)); 0..d, even (64 of 128 on the page)
+ *   scale        score scale (1/sqrt(d) for the usual attention temperature)
+ *
+ * Block j is eligible for the query at t when all its tokens are at or before t (the block
+ * still being filled is not scored).  Its importance is the sum over the 4 heads of the
+ * softmax over the eligible blocks of scale * rope(q_{t,h}, t) . rope(mean(k in j), j*r).
+ * The kept blocks are the nsel most important eligible ones, ties to the lower index.  The
+ * scores are computed from fp16 copies of the rotated queries and pooled keys (power-of-two
+ * scaled per row and per batch, so no range is lost) with fp32 accumulation; the selection is
+ * exact for the fp32 importance values this produces.
+ *
+ * Supported: Hq = 4; d in {64, 128}; in_dtype GDN_F32 or GDN_BF16.  The workspace (at least
+ * gdn_qsa_workspace_size(...) bytes, 256-byte aligned) holds the fp16 queries and pooled keys.
+ * Outputs must not overlap the inputs, each other or the workspace.  B = 0 or T = 0 is a
+ * no-op.  Deterministic.
+ */
+size_t gdn_qsa_workspace_size(int B, int T, int Hq, int d, int r);
+gdn_status_t gdn_qsa_index(const void *q, const void *k, int32_t *sel, float *importance, int B,
+                           int T, int Hq, int d, int r, int nsel, int rope_dims, float rope_base,
+                           float scale, gdn_dtype_t in_dtype, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

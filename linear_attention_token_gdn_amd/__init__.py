@@ -13,6 +13,7 @@ stream through ctypes.  There is no CPU fallback: without the built library ever
 The C entry points are exposed unchanged as ``gdn_chunk_fwd``, ``gdn_decode_step``,
 ``gdn_decode_tokens``, ``gdn_chunk_fwd_varlen``, ``gdn_chunk_fwd_varlen_workspace_size``,
 ``gdn_backward``, ``gdn_backward_workspace_size``, ``gdn_chunk_fwd_workspace_size``,
+``gdn_qsa_index``, ``gdn_qsa_workspace_size``,
 ``gdn_chunk_fwd_plan``,
 ``gdn_status_string`` and ``gdn_abi_version``.
 """
@@ -30,7 +31,8 @@ GDN_QK_L2NORM, GDN_BETA_LOGIT, GDN_G_LOGIT = 1, 2, 4  # input prologue flags
 EXPORTED_SYMBOLS = ("gdn_abi_version", "gdn_status_string", "gdn_chunk_fwd_workspace_size",
                     "gdn_chunk_fwd_plan", "gdn_chunk_fwd", "gdn_decode_step", "gdn_decode_tokens",
                     "gdn_chunk_fwd_varlen", "gdn_chunk_fwd_varlen_workspace_size",
-                    "gdn_backward", "gdn_backward_workspace_size")
+                    "gdn_backward", "gdn_backward_workspace_size", "gdn_qsa_workspace_size",
+                    "gdn_qsa_index")
 
 _lib = None
 
@@ -77,6 +79,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_backward_workspace_size.restype = sz
     lib.gdn_backward.argtypes = [vp] * 14 + [i] * 6 + [f, i, i, vp, sz, vp]
     lib.gdn_backward.restype = i
+    lib.gdn_qsa_workspace_size.argtypes = [i, i, i, i, i]
+    lib.gdn_qsa_workspace_size.restype = sz
+    lib.gdn_qsa_index.argtypes = [vp, vp, vp, vp] + [i] * 7 + [f, f, i, vp, sz, vp]
+    lib.gdn_qsa_index.restype = i
     _lib = lib
     return lib
 
@@ -131,6 +137,18 @@ def gdn_chunk_fwd_varlen(q, k, v, beta, g, initial_state, o, final_state, cu_seq
     return int(load_library().gdn_chunk_fwd_varlen(
         q, k, v, beta, g, initial_state, o, final_state, cu_seqlens, num_seqs, T, Hk, Hv, dk, dv,
         chunk, scale, flags, in_dtype, out_dtype, workspace, workspace_bytes, stream))
+
+
+def gdn_qsa_workspace_size(B, T, Hq, d, r) -> int:
+    return int(load_library().gdn_qsa_workspace_size(B, T, Hq, d, r))
+
+
+def gdn_qsa_index(q, k, sel, importance, B, T, Hq, d, r, nsel, rope_dims, rope_base, scale,
+                  in_dtype, workspace, workspace_bytes, stream) -> int:
+    """Raw call: pointer arguments are ints (device addresses) or None."""
+    return int(load_library().gdn_qsa_index(q, k, sel, importance, B, T, Hq, d, r, nsel,
+                                            rope_dims, rope_base, scale, in_dtype, workspace,
+                                            workspace_bytes, stream))
 
 
 def gdn_chunk_fwd_varlen_workspace_size(num_seqs, T, Hk, Hv, dk, dv, chunk, in_dtype,
@@ -372,3 +390,34 @@ def backward(q, k, v, beta, g, d_o, initial_state=None, d_final_state=None, scal
     if st != GDN_OK:
         raise GdnError(st, "gdn_backward")
     return out
+
+
+def qsa_index(q, k, r=4, nsel=512, rope_dims=64, rope_base=10000.0, scale=None,
+              want_importance=False, sel=None, workspace=None):
+    """QSA compressed indexer.  q: [B,T,4,d], k: [B,T,d] (bfloat16 or float32, d in {64,128}).
+    Returns (sel [B,T,nsel] int32: the kept block indices of each query, ascending, -1 padded;
+    importance [B,T,ceil(T/r)] float32 or None).  ``scale`` defaults to 1/sqrt(d)."""
+    import torch
+    lib = load_library()
+    B, T, Hq, d = q.shape
+    dev, dt = q.device, q.dtype
+    _check(q, "q", (B, T, Hq, d), dt, dev)
+    _check(k, "k", (B, T, d), dt, dev)
+    scale = 1.0 / float(d) ** 0.5 if scale is None else float(scale)
+    nb = (T + r - 1) // r
+    if sel is None:
+        sel = torch.empty((B, T, nsel), dtype=torch.int32, device=dev)
+    else:
+        _check(sel, "sel", (B, T, nsel), torch.int32, dev)
+    imp = torch.empty((B, T, nb), dtype=torch.float32, device=dev) if want_importance else None
+    need = int(lib.gdn_qsa_workspace_size(B, T, Hq, d, r))
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.gdn_qsa_index(_ptr(q), _ptr(k), _ptr(sel), _ptr(imp), B, T, Hq, d, r, nsel,
+                           rope_dims, float(rope_base), scale, _dtype_code(dt), _ptr(workspace),
+                           ws_bytes, stream)
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_qsa_index")
+    return sel, imp

@@ -290,4 +290,46 @@ gdn_status_t gdn_backward(const void *q, const void *k, const void *v, const voi
     return gdn::launch_backward(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+size_t gdn_qsa_workspace_size(int B, int T, int Hq, int d, int r) {
+    if (B <= 0 || T <= 0 || Hq != 4 || (d != 64 && d != 128) || r < 1) return 0;
+    return gdn::qsa_workspace(B, T, d, r);
+}
+
+gdn_status_t gdn_qsa_index(const void *q, const void *k, int32_t *sel, float *importance, int B,
+                           int T, int Hq, int d, int r, int nsel, int rope_dims, float rope_base,
+                           float scale, gdn_dtype_t in_dtype, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    if (B < 0 || T < 0 || Hq <= 0 || d <= 0 || r < 1 || nsel < 1) return GDN_ERR_INVALID_ARG;
+    if (rope_dims < 0 || rope_dims > d || rope_dims % 2 != 0) return GDN_ERR_INVALID_ARG;
+    if (!(scale == scale) || scale - scale != 0.f) return GDN_ERR_INVALID_ARG;  // NaN or Inf
+    if (rope_dims > 0 && !(rope_base > 0.f && rope_base - rope_base == 0.f))
+        return GDN_ERR_INVALID_ARG;
+    if (!dtype_known(in_dtype)) return GDN_ERR_UNSUPPORTED;
+    if (Hq != 4 || (d != 64 && d != 128)) return GDN_ERR_UNSUPPORTED;
+    if (B == 0 || T == 0) return GDN_OK;
+    const size_t ib = dtype_bytes(in_dtype);
+    const size_t BT = size_t(B) * T, nb = (size_t(T) + r - 1) / r;
+    const size_t qb = BT * Hq * d * ib, kb = BT * d * ib, sb = BT * nsel * 4, mb = BT * nb * 4;
+    if (!q || !k || !sel) return GDN_ERR_INVALID_ARG;
+    if (!aligned(q, ib) || !aligned(k, ib) || !aligned(sel, 4) ||
+        (importance && !aligned(importance, 4)))
+        return GDN_ERR_INVALID_ARG;
+    const size_t need = gdn::qsa_workspace(B, T, d, r);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return GDN_ERR_INVALID_ARG;
+    // outputs are disjoint from the inputs, from each other and from the workspace
+    const void *ro[] = {q, k, workspace};
+    const size_t rob[] = {qb, kb, need};
+    for (int j = 0; j < 3; ++j)
+        if (overlap(sel, sb, ro[j], rob[j]) || overlap(importance, mb, ro[j], rob[j]))
+            return GDN_ERR_INVALID_ARG;
+    if (overlap(sel, sb, importance, mb)) return GDN_ERR_INVALID_ARG;
+    gdn::QsaArgs a;
+    a.q = q; a.k = k; a.sel = sel; a.imp = importance;
+    a.B = B; a.T = T; a.d = d; a.r = r; a.nsel = nsel; a.rope_dims = rope_dims;
+    a.rope_base = rope_base; a.scale = scale; a.in_dt = in_dtype;
+    a.ws = workspace;
+    a.stream = static_cast<hipStream_t>(stream);
+    return gdn::launch_qsa(a) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 }  // extern "C"

@@ -55,6 +55,20 @@ struct BackwardArgs {
 size_t backward_workspace(int B, int T, int Hk, int Hv, int dk, int dv);
 hipError_t launch_backward(const BackwardArgs &a);
 
+struct QsaArgs {
+    const void *q, *k;   // [B, T, 4, d] and [B, T, d] (in_dt)
+    int32_t *sel;        // [B, T, nsel]
+    float *imp;          // [B, T, ceil(T/r)] or null
+    int B, T, d, r, nsel, rope_dims;
+    float rope_base, scale;
+    gdn_dtype_t in_dt;
+    void *ws;
+    hipStream_t stream;
+};
+// The QSA compressed indexer (csrc/qsa.hip) and its workspace.
+size_t qsa_workspace(int B, int T, int d, int r);
+hipError_t launch_qsa(const QsaArgs &a);
+
 // Token-by-token kernel: every (dk, dv) in {16,32,64,128}^2, both dtypes.  It is the fp32
 // path and the fallback of the chunked kernel.
 hipError_t launch_recurrent(const PrefillArgs &a);

@@ -1,0 +1,506 @@
+// qsa.hip -- the QSA compressed indexer: which key blocks each query attends to.
+//
+// Explainer page "論文解説: Qwen3.8-Next の設計" (ta-paperlens.web.app), section "部品②: QSA":
+// the keys (one shared key head, the indexer being multi-query attention with four query
+// heads) are cut into blocks of r tokens and mean-pooled before the position encoding, each
+// block gets one position (its first token), rotary encoding covers part of the head
+// dimension, and a token budget of K tokens (K / r blocks) keeps the most important blocks.
+//
+// Readings of what the page leaves open (the oracle and include/gdn.h state the same):
+//   - block j holds tokens j*r .. min((j+1)r, T) - 1 and is eligible for the query at t when
+//     its last token is at or before t;
+//   - rotate-half pairing (i, i + R/2) for i < R/2, angle pos * base^(-2i/R);
+//   - the importance of block j for query t is the sum over the four heads of the softmax
+//     over eligible blocks of scale * q_{t,h} . kbar_j;
+//   - the nsel most important eligible blocks are kept (ties: lower index), ascending.
+//
+// Four kernels:
+//   rope_q_kernel   rotated queries -> fp16 with a power-of-two scale per (token, head) row
+//   pool_k_kernel   block means, rotated at the block's first position -> fp32, plus one
+//                   partial max |kbar| per 64 blocks
+//   pack_k_kernel   fp32 -> fp16 with one power-of-two scale per batch (from the partial maxima)
+//   select_kernel   one wavefront per 16 queries: the scores on the matrix cores (fp16 in,
+//                   fp32 accumulate) in sweeps over the eligible blocks -- one for the softmax
+//                   statistics, up to four for an exact 8-bit radix select of the nsel-th
+//                   largest importance, one that writes the kept block indices in order.
+// Recomputing the scores in every sweep costs less than storing them: a score row costs 4 B
+// of HBM traffic per block against 1024 multiply-adds on the matrix cores, and the sweeps are
+// bound by the exponentials on the vector units either way.
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kHq = 4;             // query heads per token: the four rows of an MFMA group
+constexpr int kTok = 16;           // queries per wavefront
+constexpr int kPoolBlocks = 64;    // blocks per workgroup of the key kernels (one partial max)
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x4 mma(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// sin and cos of pos * base^(-2m/R): the angle is formed and reduced to [-pi, pi] in fp64
+// (positions reach 2^20 and more, where an fp32 angle would be off by a large fraction of a
+// radian), then evaluated in fp32.
+__device__ __forceinline__ void rope_angle(double pos, int m, int R, double log2base, float &c,
+                                           float &s) {
+    const double inv_freq = exp2(-(2.0 * m / R) * log2base);
+    const double th = pos * inv_freq;
+    const double n = rint(th * 0.15915494309189535);       // 1 / (2 pi)
+    double red = fma(-n, 6.283185307179586, th);           // 2 pi, high part
+    red = fma(-n, 2.4492935982947064e-16, red);            // 2 pi, low part
+    sincosf(static_cast<float>(red), &s, &c);
+}
+
+// Rotated value of element i of a row whose elements are x(i): rotate-half over the first R.
+template <typename F>
+__device__ __forceinline__ float rope_elem(F x, int i, int R, double pos, double log2base) {
+    const int h = R / 2;
+    if (i >= R) return x(i);
+    float c, s;
+    if (i < h) {
+        rope_angle(pos, i, R, log2base, c, s);
+        return x(i) * c - x(i + h) * s;
+    }
+    rope_angle(pos, i - h, R, log2base, c, s);
+    return x(i - h) * s + x(i) * c;
+}
+
+// 2^(14 - e) where max = f 2^e, f in [0.5, 1): scales the largest magnitude into [2^13, 2^14),
+// well inside fp16 (and exact: a power of two).
+__device__ __forceinline__ int scale_exp(float maxabs) {
+    int e;
+    frexpf(maxabs, &e);
+    return 14 - e;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+    for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+// ---------------------------------------------------------------------------------------
+// rope_q_kernel: one wavefront per (token, head) row; block = the four heads of one token.
+template <int D, typename TI>
+__global__ void __launch_bounds__(256)
+rope_q_kernel(const TI *__restrict__ q, f16 *__restrict__ q16, float *__restrict__ qinv, int T,
+              int R, double log2base) {
+    const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
+    const size_t tok = blockIdx.x;  // b * T + t
+    const double pos = static_cast<double>(tok % static_cast<size_t>(T));
+    const TI *row = q + (tok * kHq + h) * D;
+    auto x = [&](int i) { return load_f32(row + i); };
+    float out[D / 64];
+    float mx = 0.f;
+#pragma unroll
+    for (int u = 0; u < D / 64; ++u) {
+        out[u] = rope_elem(x, lane + 64 * u, R, pos, log2base);
+        mx = fmaxf(mx, fabsf(out[u]));
+    }
+    const int e = scale_exp(wave_max(mx));
+    f16 *dst = q16 + (tok * kHq + h) * D;
+#pragma unroll
+    for (int u = 0; u < D / 64; ++u) dst[lane + 64 * u] = static_cast<f16>(ldexpf(out[u], e));
+    if (lane == 0) qinv[tok * kHq + h] = ldexpf(1.f, -e);
+}
+
+// ---------------------------------------------------------------------------------------
+// pool_k_kernel: workgroup p of batch b pools blocks 64p .. 64p+63 (16 per wavefront) and
+// writes the largest magnitude it produced to part[b][p].
+template <int D, typename TI>
+__global__ void __launch_bounds__(256)
+pool_k_kernel(const TI *__restrict__ k, float *__restrict__ kf, float *__restrict__ part, int T,
+              int r, int nb, int nparts, int R, double log2base) {
+    __shared__ float s_max[4];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int b = blockIdx.x / nparts, p = blockIdx.x % nparts;
+    const TI *kb = k + static_cast<size_t>(b) * T * D;
+    float mx = 0.f;
+    for (int jj = 0; jj < kPoolBlocks / 4; ++jj) {
+        const int j = p * kPoolBlocks + w * (kPoolBlocks / 4) + jj;
+        if (j >= nb) break;
+        const int t0 = j * r, t1 = min(t0 + r, T);
+        const float inv = 1.f / static_cast<float>(t1 - t0);
+        auto mean = [&](int i) {
+            float s = 0.f;
+            for (int t = t0; t < t1; ++t) s += load_f32(kb + static_cast<size_t>(t) * D + i);
+            return s * inv;
+        };
+        float *dst = kf + (static_cast<size_t>(b) * nb + j) * D;
+#pragma unroll
+        for (int u = 0; u < D / 64; ++u) {
+            const float y = rope_elem(mean, lane + 64 * u, R, static_cast<double>(t0), log2base);
+            dst[lane + 64 * u] = y;
+            mx = fmaxf(mx, fabsf(y));
+        }
+    }
+    mx = wave_max(mx);
+    if (lane == 0) s_max[w] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        part[static_cast<size_t>(b) * nparts + p] =
+            fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+}
+
+// ---------------------------------------------------------------------------------------
+// pack_k_kernel: every workgroup of batch b reduces the batch's partial maxima (the same value
+// in each), converts its 64 blocks to fp16 with the batch's power-of-two scale; the first one
+// also stores the inverse scale.
+template <int D>
+__global__ void __launch_bounds__(256)
+pack_k_kernel(const float *__restrict__ kf, const float *__restrict__ part, f16 *__restrict__ k16,
+              float *__restrict__ kinv, int nb, int nparts) {
+    __shared__ float s_max[4];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int b = blockIdx.x / nparts, p = blockIdx.x % nparts;
+    float mx = 0.f;
+    for (int i = threadIdx.x; i < nparts; i += 256)
+        mx = fmaxf(mx, part[static_cast<size_t>(b) * nparts + i]);
+    mx = wave_max(mx);
+    if (lane == 0) s_max[w] = mx;
+    __syncthreads();
+    const int e = scale_exp(fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3])));
+    if (p == 0 && threadIdx.x == 0) kinv[b] = ldexpf(1.f, -e);
+    const int j0 = p * kPoolBlocks, nblk = min(kPoolBlocks, nb - j0);
+    const size_t base = (static_cast<size_t>(b) * nb + j0) * D;
+    for (int i = threadIdx.x * 8; i < nblk * D; i += 256 * 8) {
+        const float4 lo = *reinterpret_cast<const float4 *>(kf + base + i);
+        const float4 hi = *reinterpret_cast<const float4 *>(kf + base + i + 4);
+        f16x8 h;
+        h[0] = static_cast<f16>(ldexpf(lo.x, e)); h[1] = static_cast<f16>(ldexpf(lo.y, e));
+        h[2] = static_cast<f16>(ldexpf(lo.z, e)); h[3] = static_cast<f16>(ldexpf(lo.w, e));
+        h[4] = static_cast<f16>(ldexpf(hi.x, e)); h[5] = static_cast<f16>(ldexpf(hi.y, e));
+        h[6] = static_cast<f16>(ldexpf(hi.z, e)); h[7] = static_cast<f16>(ldexpf(hi.w, e));
+        *reinterpret_cast<f16x8 *>(k16 + base + i) = h;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// select_kernel: one wavefront per 16 consecutive queries of one batch.
+//
+// MFMA layout (16x16x32): the A operand row m = lane & 15 is query 4a + m/4, head m % 4 of row
+// tile a (a = 0..3); the B operand column n = lane & 15 is block 16 jt + n.  The accumulator
+// of lane l then holds, for row tile a, the four head scores of query 4a + l/16 against block
+// 16 jt + l%16 -- a query's four heads sit in one lane, so the head sum needs no exchange.
+//
+// The importance of an element is formed by one function in every sweep, so its fp32 bits are
+// identical wherever it is compared.
+__device__ __forceinline__ float head_sum(f32x4 acc, const float *cf, const float *ls) {
+    float i = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[0], cf[0], -ls[0]));
+    i += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[1], cf[1], -ls[1]));
+    i += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[2], cf[2], -ls[2]));
+    i += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[3], cf[3], -ls[3]));
+    return i;
+}
+
+__device__ __forceinline__ int group_popc(unsigned long long m, int g) {
+    return __builtin_popcount(static_cast<unsigned>(m >> (16 * g)) & 0xffffu);
+}
+__device__ __forceinline__ int group_below(unsigned long long m, int g, int c) {
+    return __builtin_popcount(static_cast<unsigned>(m >> (16 * g)) & ((1u << c) - 1u));
+}
+
+template <int D>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
+              const f16 *__restrict__ k16, const float *__restrict__ kinv,
+              int32_t *__restrict__ sel, float *__restrict__ imp, int B, int T, int r, int nb,
+              int nsel, float scale_log2e) {
+    constexpr int KD = D / 32;
+    __shared__ unsigned s_hist[kTok][256];
+    __shared__ unsigned s_pref[kTok], s_mask[kTok];
+    __shared__ int s_krem[kTok], s_kt[kTok], s_act[kTok];
+
+    const int lane = threadIdx.x, g = lane >> 4, c = lane & 15;
+    const int ntt = (T + kTok - 1) / kTok;
+    const int b = blockIdx.x % B;
+    const int tile = ntt - 1 - blockIdx.x / B;  // the longest rows first
+    const int t0 = tile * kTok;
+    auto nelig = [&](int t) { return t >= T ? 0 : (t == T - 1 ? nb : (t + 1) / r); };
+    const int ntj = (nelig(min(t0 + kTok - 1, T - 1)) + 15) / 16;
+
+    // operands and per-element constants
+    f16x8 qa[4][KD];
+    float cf[4][4], ls[4][4];
+    int ne[4];
+    const float ks = kinv[b] * scale_log2e;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int tq = min(t0 + 4 * a + (c >> 2), T - 1);
+        const f16 *row = q16 + ((static_cast<size_t>(b) * T + tq) * kHq + (c & 3)) * D + 8 * g;
+#pragma unroll
+        for (int s = 0; s < KD; ++s) qa[a][s] = *reinterpret_cast<const f16x8 *>(row + 32 * s);
+        const int t = t0 + 4 * a + g;
+        ne[a] = nelig(t);
+        const float *qi = qinv + (static_cast<size_t>(b) * T + min(t, T - 1)) * kHq;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) cf[a][h] = qi[h] * ks;
+    }
+    const f16 *kbase = k16 + static_cast<size_t>(b) * nb * D + 8 * g;
+    auto load_b = [&](int jt, f16x8 (&kb)[KD]) {
+        const int j = min(16 * jt + c, nb - 1);
+#pragma unroll
+        for (int s = 0; s < KD; ++s)
+            kb[s] = *reinterpret_cast<const f16x8 *>(kbase + static_cast<size_t>(j) * D + 32 * s);
+    };
+    auto scores = [&](const f16x8 (&kb)[KD], f32x4 (&acc)[4]) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KD; ++s) acc[a] = mma(qa[a][s], kb[s], acc[a]);
+        }
+    };
+
+    // ---- sweep 1: per (query, head) running max and sum of 2^x over the eligible blocks
+    {
+        float mx[4][4], sm[4][4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int h = 0; h < 4; ++h) { mx[a][h] = -3.402823466e38f; sm[a][h] = 0.f; }
+        f16x8 kb[KD], kn[KD];
+        if (ntj > 0) load_b(0, kb);
+        for (int jt = 0; jt < ntj; ++jt) {
+            load_b(min(jt + 1, ntj - 1), kn);
+            f32x4 acc[4];
+            scores(kb, acc);
+            const int j = 16 * jt + c;
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const float x = j < ne[a] ? acc[a][h] * cf[a][h] : -INFINITY;
+                    const float d = x - mx[a][h];
+                    const float e = __builtin_amdgcn_exp2f(-fabsf(d));
+                    const bool gt = x > mx[a][h];
+                    sm[a][h] = gt ? __builtin_fmaf(sm[a][h], e, 1.f) : sm[a][h] + e;
+                    mx[a][h] = gt ? x : mx[a][h];
+                }
+#pragma unroll
+            for (int s = 0; s < KD; ++s) kb[s] = kn[s];
+        }
+        // combine the 16 lanes of a group, then take lane 16g's result so that every lane of
+        // the group holds the same bits
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                float m = mx[a][h], l = sm[a][h];
+                for (int off = 1; off < 16; off <<= 1) {
+                    const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
+                    const float mn = fmaxf(m, m2);
+                    l = l * __builtin_amdgcn_exp2f(m - mn) + l2 * __builtin_amdgcn_exp2f(m2 - mn);
+                    m = mn;
+                }
+                const float lse = l > 0.f ? m + __log2f(l) : INFINITY;
+                ls[a][h] = __shfl(lse, lane & 48);
+            }
+    }
+
+    // ---- per-query selection state: keep blocks with (key & mask) > pref, and the first
+    //      kt (in index order) of those with (key & mask) == pref.  key = bits of the
+    //      importance (positive floats order as their bits).
+    if (lane < kTok) {
+        const int n = nelig(t0 + lane);
+        s_pref[lane] = 0u;
+        s_mask[lane] = 0u;
+        s_kt[lane] = 0x7fffffff;
+        s_krem[lane] = nsel;
+        s_act[lane] = n > nsel;  // otherwise every eligible block is kept
+    }
+    for (int pass = 0; pass < 4; ++pass) {
+        __syncthreads();
+        int any = 0;
+#pragma unroll
+        for (int tk = 0; tk < kTok; ++tk) any |= s_act[tk];
+        if (!any) break;
+        const int shift = 24 - 8 * pass;
+        const unsigned hi = pass == 0 ? 0u : ~((1u << (shift + 8)) - 1u);
+        for (int i = lane; i < kTok * 256; i += 64) (&s_hist[0][0])[i] = 0u;
+        unsigned pref[4];
+        bool act[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) { pref[a] = s_pref[4 * a + g]; act[a] = s_act[4 * a + g]; }
+        __syncthreads();
+        f16x8 kb[KD], kn[KD];
+        if (ntj > 0) load_b(0, kb);
+        for (int jt = 0; jt < ntj; ++jt) {
+            load_b(min(jt + 1, ntj - 1), kn);
+            f32x4 acc[4];
+            scores(kb, acc);
+            const int j = 16 * jt + c;
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const unsigned key = __float_as_uint(head_sum(acc[a], cf[a], ls[a]));
+                if (act[a] && j < ne[a] && ((key ^ pref[a]) & hi) == 0u)
+                    atomicAdd(&s_hist[4 * a + g][(key >> shift) & 255u], 1u);
+            }
+#pragma unroll
+            for (int s = 0; s < KD; ++s) kb[s] = kn[s];
+        }
+        __syncthreads();
+        // find, per active query, the bin that holds the krem-th largest remaining key
+        for (int tk = 0; tk < kTok; ++tk) {
+            if (!s_act[tk]) continue;
+            const int krem = s_krem[tk];
+            const uint4 h4 = *reinterpret_cast<const uint4 *>(&s_hist[tk][4 * lane]);
+            const int own = static_cast<int>(h4.x + h4.y + h4.z + h4.w);
+            int suf = own;  // sum over lanes >= lane
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_down(suf, off);
+                if (lane + off < 64) suf += y;
+            }
+            const int above = suf - own;
+            const bool here = above < krem && krem <= suf;
+            int digit = 0, abv = above, cnt = 0;
+            if (here) {
+                const unsigned hb[4] = {h4.x, h4.y, h4.z, h4.w};
+                int run = above;
+#pragma unroll
+                for (int q = 3; q >= 0; --q) {
+                    if (run + static_cast<int>(hb[q]) >= krem) {
+                        digit = 4 * lane + q;
+                        abv = run;
+                        cnt = static_cast<int>(hb[q]);
+                        break;
+                    }
+                    run += static_cast<int>(hb[q]);
+                }
+            }
+            const int src = __ffsll(static_cast<long long>(__ballot(here))) - 1;
+            digit = __shfl(digit, src);
+            abv = __shfl(abv, src);
+            cnt = __shfl(cnt, src);
+            if (lane == 0) {
+                const int left = krem - abv;  // to take from this bin
+                s_pref[tk] |= static_cast<unsigned>(digit) << shift;
+                s_mask[tk] = ~((1u << shift) - 1u);
+                s_krem[tk] = left;
+                if (cnt == left) {          // the whole bin is kept: done
+                    s_act[tk] = 0;
+                } else if (shift == 0) {    // one key value: keep its first `left` copies
+                    s_kt[tk] = left;
+                    s_act[tk] = 0;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- last sweep: write the kept blocks in ascending order (and the importance)
+    unsigned pref[4], mask[4];
+    int kt[4], cnt[4], ties[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        pref[a] = s_pref[4 * a + g];
+        mask[a] = s_mask[4 * a + g];
+        kt[a] = s_kt[4 * a + g];
+        cnt[a] = 0;
+        ties[a] = 0;
+    }
+    {
+        f16x8 kb[KD], kn[KD];
+        if (ntj > 0) load_b(0, kb);
+        for (int jt = 0; jt < ntj; ++jt) {
+            load_b(min(jt + 1, ntj - 1), kn);
+            f32x4 acc[4];
+            scores(kb, acc);
+            const int j = 16 * jt + c;
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const float iv = head_sum(acc[a], cf[a], ls[a]);
+                const unsigned km = __float_as_uint(iv) & mask[a];
+                const bool el = j < ne[a];
+                const bool eq = el && km == pref[a];
+                const unsigned long long meq = __ballot(eq);
+                const bool take = el && (km > pref[a] || (eq && ties[a] + group_below(meq, g, c) < kt[a]));
+                const unsigned long long mt = __ballot(take);
+                const int pos = cnt[a] + group_below(mt, g, c);
+                const int t = t0 + 4 * a + g;
+                const size_t rowo = static_cast<size_t>(b) * T + t;
+                if (take && pos < nsel) sel[rowo * nsel + pos] = j;
+                if (imp != nullptr && t < T && j < nb) imp[rowo * nb + j] = el ? iv : 0.f;
+                cnt[a] += group_popc(mt, g);
+                ties[a] += group_popc(meq, g);
+            }
+#pragma unroll
+            for (int s = 0; s < KD; ++s) kb[s] = kn[s];
+        }
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int t = t0 + 4 * a + g;
+        if (t >= T) continue;
+        const size_t rowo = static_cast<size_t>(b) * T + t;
+        for (int p = cnt[a] + c; p < nsel; p += 16) sel[rowo * nsel + p] = -1;
+        if (imp != nullptr)
+            for (int j = 16 * ntj + c; j < nb; j += 16) imp[rowo * nb + j] = 0.f;
+    }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct QsaLayout {
+    size_t q16, qinv, kf, k16, part, kinv, total;
+    int nb, nparts;
+};
+
+QsaLayout qsa_layout(int B, int T, int d, int r) {
+    QsaLayout L;
+    L.nb = (T + r - 1) / r;
+    L.nparts = (L.nb + kPoolBlocks - 1) / kPoolBlocks;
+    const size_t BT = static_cast<size_t>(B) * T, Bn = static_cast<size_t>(B) * L.nb;
+    size_t o = 0;
+    L.q16 = o;  o = align256(o + BT * kHq * d * 2);
+    L.qinv = o; o = align256(o + BT * kHq * 4);
+    L.kf = o;   o = align256(o + Bn * d * 4);
+    L.k16 = o;  o = align256(o + Bn * d * 2);
+    L.part = o; o = align256(o + static_cast<size_t>(B) * L.nparts * 4);
+    L.kinv = o; o = align256(o + static_cast<size_t>(B) * 4);
+    L.total = o;
+    return L;
+}
+
+template <int D, typename TI>
+hipError_t launch_qsa_t(const QsaArgs &a) {
+    const QsaLayout L = qsa_layout(a.B, a.T, D, a.r);
+    char *ws = static_cast<char *>(a.ws);
+    f16 *q16 = reinterpret_cast<f16 *>(ws + L.q16);
+    float *qinv = reinterpret_cast<float *>(ws + L.qinv);
+    float *kf = reinterpret_cast<float *>(ws + L.kf);
+    f16 *k16 = reinterpret_cast<f16 *>(ws + L.k16);
+    float *part = reinterpret_cast<float *>(ws + L.part);
+    float *kinv = reinterpret_cast<float *>(ws + L.kinv);
+    const double log2base = a.rope_dims > 0 ? log2(static_cast<double>(a.rope_base)) : 0.0;
+    const size_t BT = static_cast<size_t>(a.B) * a.T;
+    hipLaunchKernelGGL((rope_q_kernel<D, TI>), dim3(static_cast<unsigned>(BT)), dim3(256), 0,
+                       a.stream, static_cast<const TI *>(a.q), q16, qinv, a.T, a.rope_dims,
+                       log2base);
+    hipLaunchKernelGGL((pool_k_kernel<D, TI>), dim3(a.B * L.nparts), dim3(256), 0, a.stream,
+                       static_cast<const TI *>(a.k), kf, part, a.T, a.r, L.nb, L.nparts,
+                       a.rope_dims, log2base);
+    hipLaunchKernelGGL((pack_k_kernel<D>), dim3(a.B * L.nparts), dim3(256), 0, a.stream, kf, part,
+                       k16, kinv, L.nb, L.nparts);
+    const int ntt = (a.T + kTok - 1) / kTok;
+    hipLaunchKernelGGL((select_kernel<D>), dim3(a.B * ntt), dim3(64), 0, a.stream, q16, qinv, k16,
+                       kinv, a.sel, a.imp, a.B, a.T, a.r, L.nb, a.nsel, a.scale * kLog2e);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t qsa_workspace(int B, int T, int d, int r) { return qsa_layout(B, T, d, r).total; }
+
+hipError_t launch_qsa(const QsaArgs &a) {
+    const bool bf = a.in_dt == GDN_BF16;
+    if (a.d == 128) return bf ? launch_qsa_t<128, bf16_t>(a) : launch_qsa_t<128, float>(a);
+    return bf ? launch_qsa_t<64, bf16_t>(a) : launch_qsa_t<64, float>(a);
+}
+
+}  // namespace gdn

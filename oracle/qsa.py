@@ -52,20 +52,22 @@ def rope(x, pos, rope_dims, base=10000.0):
     return x
 
 
-def importance(q, k, r, rope_dims=64, base=10000.0, scale=None):
-    """q: [B, T, Hq, d]; k: [B, T, d] (the shared key head).  Returns (imp [B, T, nb] fp64,
-    eligible mask [T, nb]): imp[b, t, j] = sum_h softmax_j(scale * q_{t,h} . kbar_j) over the
-    eligible blocks, 0 elsewhere; scale defaults to 1/sqrt(d)."""
+def importance(q, k, r, rope_dims=64, base=10000.0, scale=None, rows=None):
+    """q: [B, T, Hq, d]; k: [B, T, d] (the shared key head).  Returns (imp [B, n, nb] fp64,
+    eligible mask [n, nb]) for the query positions `rows` (all T by default; n of them):
+    imp[b, i, j] = sum_h softmax_j(scale * q_{t,h} . kbar_j) over the blocks eligible for
+    t = rows[i], 0 elsewhere; scale defaults to 1/sqrt(d)."""
     q = np.asarray(q, dtype=np.float64)
     B, T, Hq, d = q.shape
     if scale is None:
         scale = 1.0 / np.sqrt(d)
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
     kb = pool_keys(k, r)
     nb = kb.shape[1]
-    kb = rope(kb, np.arange(nb) * r, rope_dims, base)          # position: the block's first
-    qr = rope(q, np.arange(T)[None, :, None], rope_dims, base)  # token; queries at their own
+    kb = rope(kb, np.arange(nb) * r, rope_dims, base)                # a block sits at its first
+    qr = rope(q[:, rows], rows[None, :, None], rope_dims, base)      # token; a query at its own
     last = np.minimum((np.arange(nb) + 1) * r, T) - 1
-    elig = last[None, :] <= np.arange(T)[:, None]               # [T, nb]
+    elig = last[None, :] <= rows[:, None]                            # [n, nb]
     s = np.einsum("bthd,bjd->bthj", qr, kb) * scale
     s = np.where(elig[None, :, None, :], s, -np.inf)
     m = s.max(axis=-1, keepdims=True)

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gdn.gdn_abi_version() == 2
+    assert gdn.gdn_abi_version() == 3
     assert gdn.gdn_status_string(0) == "GDN_OK"
     assert gdn.gdn_status_string(1) == "GDN_ERR_INVALID_ARG"
     assert gdn.gdn_status_string(2) == "GDN_ERR_UNSUPPORTED"
@@ -71,7 +71,7 @@ def test_workspace_size_rejects_bad_sizes(lib):
 # before anything dereferences them
 BASE = 1 << 40
 P = {n: BASE + i * (1 << 32)
-     for i, n in enumerate(["q", "k", "v", "beta", "g", "s0", "o", "sT", "cu"])}
+     for i, n in enumerate(["q", "k", "v", "beta", "g", "s0", "o", "sT", "cu", "ws"])}
 
 
 def prefill(**kw):
@@ -235,3 +235,43 @@ def test_backward_workspace_size(lib):
     assert gdn.gdn_backward_workspace_size(1, 100, 1, 2, 64, 64) > 0
     assert gdn.gdn_backward_workspace_size(0, 100, 1, 2, 64, 64) == 0
     assert backward_call(B=0) == gdn.GDN_OK
+
+
+def qsa_call(**kw):
+    a = dict(q=P["q"], k=P["k"], sel=P["sT"], importance=None, B=2, T=64, Hq=4, d=128, r=4,
+             nsel=8, rope_dims=64, rope_base=10000.0, scale=0.088, in_dtype=gdn.GDN_BF16,
+             workspace=P["ws"], workspace_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return gdn.gdn_qsa_index(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=2), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(d=96), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(in_dtype=7), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(r=0), gdn.GDN_ERR_INVALID_ARG),
+    (dict(nsel=0), gdn.GDN_ERR_INVALID_ARG),
+    (dict(rope_dims=63), gdn.GDN_ERR_INVALID_ARG),
+    (dict(rope_dims=130), gdn.GDN_ERR_INVALID_ARG),
+    (dict(rope_base=0.0), gdn.GDN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), gdn.GDN_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), gdn.GDN_ERR_INVALID_ARG),
+    (dict(sel=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(sel=P["q"]), gdn.GDN_ERR_INVALID_ARG),               # output overlaps an input
+    (dict(importance=P["sT"] + 64), gdn.GDN_ERR_INVALID_ARG),  # outputs overlap each other
+    (dict(workspace=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(workspace_bytes=1024), gdn.GDN_ERR_INVALID_ARG),
+    (dict(workspace=P["ws"] + 64), gdn.GDN_ERR_INVALID_ARG),   # misaligned workspace
+])
+def test_qsa_validation(lib, kw, status):
+    assert qsa_call(**kw) == status
+
+
+def test_qsa_workspace_and_empty_calls(lib):
+    # q16 + qinv + kbar fp32 + kbar fp16 + partial maxima + scale, each 256-aligned
+    n = gdn.gdn_qsa_workspace_size(1, 65536, 4, 128, 4)
+    assert n == 65536 * 4 * 128 * 2 + 65536 * 4 * 4 + 16384 * 128 * (4 + 2) + 1024 + 256
+    assert gdn.gdn_qsa_workspace_size(1, 64, 2, 128, 4) == 0
+    assert gdn.gdn_qsa_workspace_size(0, 64, 4, 128, 4) == 0
+    assert qsa_call(B=0) == gdn.GDN_OK
+    assert qsa_call(T=0) == gdn.GDN_OK

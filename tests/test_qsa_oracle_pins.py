@@ -203,3 +203,11 @@ def test_full_indexer_shapes():
     q, k = small_case(13, B=1, T=40, d=16)
     sel, imp = qsa.qsa_index(q, k, r=4, budget_tokens=12, rope_dims=8)
     assert sel.shape == (1, 40, 3) and imp.shape == (1, 40, 10)
+
+
+def test_importance_of_selected_rows():
+    q, k = small_case(14, T=41)
+    full, elig = qsa.importance(q, k, r=4, rope_dims=8)
+    rows = [40, 3, 17, 0]
+    part, pe = qsa.importance(q, k, r=4, rope_dims=8, rows=rows)
+    assert np.allclose(part, full[:, rows], atol=1e-15) and np.array_equal(pe, elig[rows])

@@ -86,10 +86,11 @@ __device__ __forceinline__ float wave_max(float x) {
 
 // ---------------------------------------------------------------------------------------
 // rope_q_kernel: one wavefront per (token, head) row; block = the four heads of one token.
+// Writes the fp16 row, 1/scale, and an upper bound of the fp16 row's L2 norm.
 template <int D, typename TI>
 __global__ void __launch_bounds__(256)
-rope_q_kernel(const TI *__restrict__ q, f16 *__restrict__ q16, float *__restrict__ qinv, int T,
-              int R, double log2base) {
+rope_q_kernel(const TI *__restrict__ q, f16 *__restrict__ q16, float *__restrict__ qinv,
+              float *__restrict__ qnorm, int T, int R, double log2base) {
     const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
     const size_t tok = blockIdx.x;  // b * T + t
     const double pos = static_cast<double>(tok % static_cast<size_t>(T));
@@ -104,23 +105,32 @@ rope_q_kernel(const TI *__restrict__ q, f16 *__restrict__ q16, float *__restrict
     }
     const int e = scale_exp(wave_max(mx));
     f16 *dst = q16 + (tok * kHq + h) * D;
+    float ss = 0.f;
 #pragma unroll
-    for (int u = 0; u < D / 64; ++u) dst[lane + 64 * u] = static_cast<f16>(ldexpf(out[u], e));
-    if (lane == 0) qinv[tok * kHq + h] = ldexpf(1.f, -e);
+    for (int u = 0; u < D / 64; ++u) {
+        const f16 v = static_cast<f16>(ldexpf(out[u], e));
+        dst[lane + 64 * u] = v;
+        ss += static_cast<float>(v) * static_cast<float>(v);
+    }
+    for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off);
+    if (lane == 0) {
+        qinv[tok * kHq + h] = ldexpf(1.f, -e);
+        qnorm[tok * kHq + h] = sqrtf(ss) * (1.f + 0x1p-20f);
+    }
 }
 
 // ---------------------------------------------------------------------------------------
 // pool_k_kernel: workgroup p of batch b pools blocks 64p .. 64p+63 (16 per wavefront) and
-// writes the largest magnitude it produced to part[b][p].
+// writes the largest element magnitude and the largest row norm it produced to part[b][p].
 template <int D, typename TI>
 __global__ void __launch_bounds__(256)
-pool_k_kernel(const TI *__restrict__ k, float *__restrict__ kf, float *__restrict__ part, int T,
+pool_k_kernel(const TI *__restrict__ k, float *__restrict__ kf, float2 *__restrict__ part, int T,
               int r, int nb, int nparts, int R, double log2base) {
-    __shared__ float s_max[4];
+    __shared__ float s_max[4], s_nrm[4];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int b = blockIdx.x / nparts, p = blockIdx.x % nparts;
     const TI *kb = k + static_cast<size_t>(b) * T * D;
-    float mx = 0.f;
+    float mx = 0.f, nx = 0.f;
     for (int jj = 0; jj < kPoolBlocks / 4; ++jj) {
         const int j = p * kPoolBlocks + w * (kPoolBlocks / 4) + jj;
         if (j >= nb) break;
@@ -132,40 +142,54 @@ pool_k_kernel(const TI *__restrict__ k, float *__restrict__ kf, float *__restric
             return s * inv;
         };
         float *dst = kf + (static_cast<size_t>(b) * nb + j) * D;
+        float ss = 0.f;
 #pragma unroll
         for (int u = 0; u < D / 64; ++u) {
             const float y = rope_elem(mean, lane + 64 * u, R, static_cast<double>(t0), log2base);
             dst[lane + 64 * u] = y;
             mx = fmaxf(mx, fabsf(y));
+            ss += y * y;
         }
+        for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off);
+        nx = fmaxf(nx, ss);
     }
     mx = wave_max(mx);
-    if (lane == 0) s_max[w] = mx;
+    if (lane == 0) { s_max[w] = mx; s_nrm[w] = nx; }
     __syncthreads();
     if (threadIdx.x == 0)
         part[static_cast<size_t>(b) * nparts + p] =
-            fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+            make_float2(fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3])),
+                        sqrtf(fmaxf(fmaxf(s_nrm[0], s_nrm[1]), fmaxf(s_nrm[2], s_nrm[3]))));
 }
 
 // ---------------------------------------------------------------------------------------
 // pack_k_kernel: every workgroup of batch b reduces the batch's partial maxima (the same value
 // in each), converts its 64 blocks to fp16 with the batch's power-of-two scale; the first one
-// also stores the inverse scale.
+// also stores {inverse scale, upper bound of the fp16 rows' L2 norms}.
 template <int D>
 __global__ void __launch_bounds__(256)
-pack_k_kernel(const float *__restrict__ kf, const float *__restrict__ part, f16 *__restrict__ k16,
-              float *__restrict__ kinv, int nb, int nparts) {
-    __shared__ float s_max[4];
+pack_k_kernel(const float *__restrict__ kf, const float2 *__restrict__ part,
+              f16 *__restrict__ k16, float2 *__restrict__ kstat, int nb, int nparts) {
+    __shared__ float s_max[4], s_nrm[4];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int b = blockIdx.x / nparts, p = blockIdx.x % nparts;
-    float mx = 0.f;
-    for (int i = threadIdx.x; i < nparts; i += 256)
-        mx = fmaxf(mx, part[static_cast<size_t>(b) * nparts + i]);
+    float mx = 0.f, nx = 0.f;
+    for (int i = threadIdx.x; i < nparts; i += 256) {
+        const float2 v = part[static_cast<size_t>(b) * nparts + i];
+        mx = fmaxf(mx, v.x);
+        nx = fmaxf(nx, v.y);
+    }
     mx = wave_max(mx);
-    if (lane == 0) s_max[w] = mx;
+    nx = wave_max(nx);
+    if (lane == 0) { s_max[w] = mx; s_nrm[w] = nx; }
     __syncthreads();
     const int e = scale_exp(fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3])));
-    if (p == 0 && threadIdx.x == 0) kinv[b] = ldexpf(1.f, -e);
+    if (p == 0 && threadIdx.x == 0) {
+        // fp16 rounding grows a row by at most a factor (1 + 2^-11), plus the absolute
+        // rounding of subnormal elements
+        const float n = fmaxf(fmaxf(s_nrm[0], s_nrm[1]), fmaxf(s_nrm[2], s_nrm[3]));
+        kstat[b] = make_float2(ldexpf(1.f, -e), ldexpf(n, e) * (1.f + 0x1p-9f) + 0x1p-14f);
+    }
     const int j0 = p * kPoolBlocks, nblk = min(kPoolBlocks, nb - j0);
     const size_t base = (static_cast<size_t>(b) * nb + j0) * D;
     for (int i = threadIdx.x * 8; i < nblk * D; i += 256 * 8) {
@@ -188,6 +212,12 @@ pack_k_kernel(const float *__restrict__ kf, const float *__restrict__ part, f16 
 // of lane l then holds, for row tile a, the four head scores of query 4a + l/16 against block
 // 16 jt + l%16 -- a query's four heads sit in one lane, so the head sum needs no exchange.
 //
+// Every sweep over the blocks is software-pipelined: the matrix-core products of tile jt + 1
+// are issued between the vector instructions that consume tile jt, and the key fragments of a
+// tile are loaded a whole tile ahead.  The loop bodies have no branches (masked histogram
+// updates go to a per-lane dummy counter, masked stores through a buffer resource whose range
+// check drops them), so the loads stay in flight across iterations.
+//
 // The importance of an element is formed by one function in every sweep, so its fp32 bits are
 // identical wherever it is compared.
 __device__ __forceinline__ float head_sum(f32x4 acc, const float *cf, const float *ls) {
@@ -205,14 +235,29 @@ __device__ __forceinline__ int group_below(unsigned long long m, int g, int c) {
     return __builtin_popcount(static_cast<unsigned>(m >> (16 * g)) & ((1u << c) - 1u));
 }
 
-template <int D>
+// One MFMA, then nv vector instructions, n times: keeps the matrix core busy while the
+// wavefront works through the previous tile.
+#define QSA_INTERLEAVE(n, nv)                                                                  \
+    _Pragma("unroll") for (int _i = 0; _i < (n); ++_i) {                                       \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
+        __builtin_amdgcn_sched_group_barrier(0x002, (nv), 0);                                  \
+    }
+
+template <int N> struct Nv { static constexpr int value = N; };
+typedef Nv<3> NV3;
+typedef Nv<4> NV4;
+
+constexpr int kHistWords = kTok * 256 + 64;  // 16 histograms of 256 bins, 64 dummy counters
+constexpr unsigned kOob = 0x7ffffff0u;       // a buffer offset past any range: store dropped
+
+template <int D, bool IMP>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
-              const f16 *__restrict__ k16, const float *__restrict__ kinv,
-              int32_t *__restrict__ sel, float *__restrict__ imp, int B, int T, int r, int nb,
-              int nsel, float scale_log2e) {
+              const float *__restrict__ qnorm, const f16 *__restrict__ k16,
+              const float2 *__restrict__ kstat, int32_t *__restrict__ sel,
+              float *__restrict__ imp, int B, int T, int r, int nb, int nsel, float scale_log2e) {
     constexpr int KD = D / 32;
-    __shared__ unsigned s_hist[kTok][256];
+    __shared__ unsigned s_hist[kHistWords];
     __shared__ unsigned s_pref[kTok], s_mask[kTok];
     __shared__ int s_krem[kTok], s_kt[kTok], s_act[kTok];
 
@@ -228,7 +273,8 @@ select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
     f16x8 qa[4][KD];
     float cf[4][4], ls[4][4];
     int ne[4];
-    const float ks = kinv[b] * scale_log2e;
+    const float2 ks = kstat[b];
+    const float ksc = ks.x * scale_log2e;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
         const int tq = min(t0 + 4 * a + (c >> 2), T - 1);
@@ -237,9 +283,13 @@ select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
         for (int s = 0; s < KD; ++s) qa[a][s] = *reinterpret_cast<const f16x8 *>(row + 32 * s);
         const int t = t0 + 4 * a + g;
         ne[a] = nelig(t);
-        const float *qi = qinv + (static_cast<size_t>(b) * T + min(t, T - 1)) * kHq;
+        const size_t qr = (static_cast<size_t>(b) * T + min(t, T - 1)) * kHq;
 #pragma unroll
-        for (int h = 0; h < 4; ++h) cf[a][h] = qi[h] * ks;
+        for (int h = 0; h < 4; ++h) {
+            cf[a][h] = qinv[qr + h] * ksc;
+            // |score * cf| <= |cf| ||q16|| ||k16||: an upper bound of every exponent of the row
+            ls[a][h] = fabsf(cf[a][h]) * qnorm[qr + h] * ks.y * (1.f + 0x1p-10f);
+        }
     }
     const f16 *kbase = k16 + static_cast<size_t>(b) * nb * D + 8 * g;
     auto load_b = [&](int jt, f16x8 (&kb)[KD]) {
@@ -250,57 +300,107 @@ select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
     };
     auto scores = [&](const f16x8 (&kb)[KD], f32x4 (&acc)[4]) {
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < KD; ++s)
 #pragma unroll
-            for (int s = 0; s < KD; ++s) acc[a] = mma(qa[a][s], kb[s], acc[a]);
+            for (int a = 0; a < 4; ++a)
+                acc[a] = mma(qa[a][s], kb[s], s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[a]);
+    };
+    // the pipelined sweep: body(jt, acc) consumes tile jt; NV = its vector instructions per
+    // matrix-core product, for the interleave
+    auto sweep = [&](auto &&body, auto nv_tag) {
+        constexpr int NV = decltype(nv_tag)::value;
+        if (ntj == 0) return;
+        f16x8 K0[KD], K1[KD];
+        f32x4 A0[4], A1[4];
+        load_b(0, K0);
+        load_b(min(1, ntj - 1), K1);
+        scores(K0, A0);
+        int jt = 0;
+        for (; jt + 2 <= ntj; jt += 2) {
+            load_b(min(jt + 2, ntj - 1), K0);
+            __builtin_amdgcn_sched_barrier(0);
+            scores(K1, A1);
+            body(jt, A0);
+            QSA_INTERLEAVE(4 * KD, NV)
+            __builtin_amdgcn_sched_barrier(0);
+            load_b(min(jt + 3, ntj - 1), K1);
+            __builtin_amdgcn_sched_barrier(0);
+            scores(K0, A0);
+            body(jt + 1, A1);
+            QSA_INTERLEAVE(4 * KD, NV)
+            __builtin_amdgcn_sched_barrier(0);
         }
+        if (jt < ntj) body(jt, A0);
     };
 
-    // ---- sweep 1: per (query, head) running max and sum of 2^x over the eligible blocks
+    // ---- sweep 1: per (query, head) sum of 2^(x - bound) over the eligible blocks, x the
+    //      score in log2 units; lse = bound + log2(sum).  If a sum comes out below 2^-100 (the
+    //      bound far above every score: huge norms), the wavefront redoes the sweep with a
+    //      running maximum instead.
     {
-        float mx[4][4], sm[4][4];
+        float sm[4][4];
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int h = 0; h < 4; ++h) { mx[a][h] = -3.402823466e38f; sm[a][h] = 0.f; }
-        f16x8 kb[KD], kn[KD];
-        if (ntj > 0) load_b(0, kb);
-        for (int jt = 0; jt < ntj; ++jt) {
-            load_b(min(jt + 1, ntj - 1), kn);
-            f32x4 acc[4];
-            scores(kb, acc);
+            for (int h = 0; h < 4; ++h) sm[a][h] = 0.f;
+        sweep([&](int jt, f32x4 (&acc)[4]) {
             const int j = 16 * jt + c;
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
                 for (int h = 0; h < 4; ++h) {
-                    const float x = j < ne[a] ? acc[a][h] * cf[a][h] : -INFINITY;
-                    const float d = x - mx[a][h];
-                    const float e = __builtin_amdgcn_exp2f(-fabsf(d));
-                    const bool gt = x > mx[a][h];
-                    sm[a][h] = gt ? __builtin_fmaf(sm[a][h], e, 1.f) : sm[a][h] + e;
-                    mx[a][h] = gt ? x : mx[a][h];
+                    const float e = __builtin_amdgcn_exp2f(
+                        __builtin_fmaf(acc[a][h], cf[a][h], -ls[a][h]));
+                    sm[a][h] += j < ne[a] ? e : 0.f;
                 }
-#pragma unroll
-            for (int s = 0; s < KD; ++s) kb[s] = kn[s];
-        }
-        // combine the 16 lanes of a group, then take lane 16g's result so that every lane of
-        // the group holds the same bits
+        }, NV3{});
+        bool low = false;
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
-                float m = mx[a][h], l = sm[a][h];
-                for (int off = 1; off < 16; off <<= 1) {
-                    const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
-                    const float mn = fmaxf(m, m2);
-                    l = l * __builtin_amdgcn_exp2f(m - mn) + l2 * __builtin_amdgcn_exp2f(m2 - mn);
-                    m = mn;
-                }
-                const float lse = l > 0.f ? m + __log2f(l) : INFINITY;
-                ls[a][h] = __shfl(lse, lane & 48);
+                float l = sm[a][h];
+                for (int off = 1; off < 16; off <<= 1) l += __shfl_xor(l, off);
+                l = __shfl(l, lane & 48);  // every lane of the group: lane 16g's bits
+                low |= ne[a] > 0 && !(l >= 0x1p-100f);
+                ls[a][h] = l > 0.f ? ls[a][h] + __log2f(l) : INFINITY;
             }
+        if (__ballot(low) != 0ull) {
+            float mx[4][4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int h = 0; h < 4; ++h) { mx[a][h] = -3.402823466e38f; sm[a][h] = 0.f; }
+            sweep([&](int jt, f32x4 (&acc)[4]) {
+                const int j = 16 * jt + c;
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        const float x = j < ne[a] ? acc[a][h] * cf[a][h] : -INFINITY;
+                        const float d = x - mx[a][h];
+                        const float e = __builtin_amdgcn_exp2f(-fabsf(d));
+                        const bool gt = x > mx[a][h];
+                        sm[a][h] = gt ? __builtin_fmaf(sm[a][h], e, 1.f) : sm[a][h] + e;
+                        mx[a][h] = gt ? x : mx[a][h];
+                    }
+            }, NV4{});
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    float m = mx[a][h], l = sm[a][h];
+                    for (int off = 1; off < 16; off <<= 1) {
+                        const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
+                        const float mn = fmaxf(m, m2);
+                        l = l * __builtin_amdgcn_exp2f(m - mn) +
+                            l2 * __builtin_amdgcn_exp2f(m2 - mn);
+                        m = mn;
+                    }
+                    const float lse = l > 0.f ? m + __log2f(l) : INFINITY;
+                    ls[a][h] = __shfl(lse, lane & 48);
+                }
+        }
     }
 
     // ---- per-query selection state: keep blocks with (key & mask) > pref, and the first
@@ -322,34 +422,30 @@ select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
         if (!any) break;
         const int shift = 24 - 8 * pass;
         const unsigned hi = pass == 0 ? 0u : ~((1u << (shift + 8)) - 1u);
-        for (int i = lane; i < kTok * 256; i += 64) (&s_hist[0][0])[i] = 0u;
+        for (int i = lane; i < kHistWords; i += 64) s_hist[i] = 0u;
         unsigned pref[4];
         bool act[4];
 #pragma unroll
         for (int a = 0; a < 4; ++a) { pref[a] = s_pref[4 * a + g]; act[a] = s_act[4 * a + g]; }
         __syncthreads();
-        f16x8 kb[KD], kn[KD];
-        if (ntj > 0) load_b(0, kb);
-        for (int jt = 0; jt < ntj; ++jt) {
-            load_b(min(jt + 1, ntj - 1), kn);
-            f32x4 acc[4];
-            scores(kb, acc);
+        sweep([&](int jt, f32x4 (&acc)[4]) {
             const int j = 16 * jt + c;
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                const unsigned key = __float_as_uint(head_sum(acc[a], cf[a], ls[a]));
-                if (act[a] && j < ne[a] && ((key ^ pref[a]) & hi) == 0u)
-                    atomicAdd(&s_hist[4 * a + g][(key >> shift) & 255u], 1u);
+                unsigned key = __float_as_uint(head_sum(acc[a], cf[a], ls[a]));
+                asm volatile("" : "+v"(key));  // computed by every lane: no branch around it
+                const bool m = act[a] & (j < ne[a]) & (((key ^ pref[a]) & hi) == 0u);
+                const unsigned idx = m ? (4 * a + g) * 256 + ((key >> shift) & 255u)
+                                       : kTok * 256 + lane;
+                atomicAdd(&s_hist[idx], 1u);
             }
-#pragma unroll
-            for (int s = 0; s < KD; ++s) kb[s] = kn[s];
-        }
+        }, NV4{});
         __syncthreads();
         // find, per active query, the bin that holds the krem-th largest remaining key
         for (int tk = 0; tk < kTok; ++tk) {
             if (!s_act[tk]) continue;
             const int krem = s_krem[tk];
-            const uint4 h4 = *reinterpret_cast<const uint4 *>(&s_hist[tk][4 * lane]);
+            const uint4 h4 = *reinterpret_cast<const uint4 *>(&s_hist[tk * 256 + 4 * lane]);
             const int own = static_cast<int>(h4.x + h4.y + h4.z + h4.w);
             int suf = own;  // sum over lanes >= lane
             for (int off = 1; off < 64; off <<= 1) {
@@ -404,42 +500,46 @@ select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
         cnt[a] = 0;
         ties[a] = 0;
     }
-    {
-        f16x8 kb[KD], kn[KD];
-        if (ntj > 0) load_b(0, kb);
-        for (int jt = 0; jt < ntj; ++jt) {
-            load_b(min(jt + 1, ntj - 1), kn);
-            f32x4 acc[4];
-            scores(kb, acc);
-            const int j = 16 * jt + c;
+    const int rows = min(kTok, T - t0);
+    const size_t row0 = static_cast<size_t>(b) * T + t0;
+    const __amdgpu_buffer_rsrc_t sel_rs = __builtin_amdgcn_make_buffer_rsrc(
+        sel + row0 * nsel, 0, rows * nsel * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t imp_rs = __builtin_amdgcn_make_buffer_rsrc(
+        IMP ? static_cast<void *>(imp + row0 * nb) : static_cast<void *>(sel), 0, IMP ? rows * nb * 4 : 0, 0x00020000);
+    sweep([&](int jt, f32x4 (&acc)[4]) {
+        const int j = 16 * jt + c;
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const float iv = head_sum(acc[a], cf[a], ls[a]);
-                const unsigned km = __float_as_uint(iv) & mask[a];
-                const bool el = j < ne[a];
-                const bool eq = el && km == pref[a];
-                const unsigned long long meq = __ballot(eq);
-                const bool take = el && (km > pref[a] || (eq && ties[a] + group_below(meq, g, c) < kt[a]));
-                const unsigned long long mt = __ballot(take);
-                const int pos = cnt[a] + group_below(mt, g, c);
-                const int t = t0 + 4 * a + g;
-                const size_t rowo = static_cast<size_t>(b) * T + t;
-                if (take && pos < nsel) sel[rowo * nsel + pos] = j;
-                if (imp != nullptr && t < T && j < nb) imp[rowo * nb + j] = el ? iv : 0.f;
-                cnt[a] += group_popc(mt, g);
-                ties[a] += group_popc(meq, g);
+        for (int a = 0; a < 4; ++a) {
+            float iv = head_sum(acc[a], cf[a], ls[a]);
+            asm volatile("" : "+v"(iv));  // computed by every lane: no branch around it
+            const unsigned km = __float_as_uint(iv) & mask[a];
+            const bool el = j < ne[a];
+            const bool eq = el && km == pref[a];
+            const unsigned long long meq = __ballot(eq);
+            const bool take =
+                el && (km > pref[a] || (eq && ties[a] + group_below(meq, g, c) < kt[a]));
+            const unsigned long long mt = __ballot(take);
+            const int pos = cnt[a] + group_below(mt, g, c);
+            const int tl = 4 * a + g;  // query within the tile
+            const unsigned so = take && pos < nsel ? static_cast<unsigned>(tl * nsel + pos) * 4u
+                                                   : kOob;
+            __builtin_amdgcn_raw_buffer_store_b32(j, sel_rs, static_cast<int>(so), 0, 0);
+            if (IMP) {
+                const unsigned io = j < nb ? static_cast<unsigned>(tl * nb + j) * 4u : kOob;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(el ? iv : 0.f), imp_rs,
+                                                      static_cast<int>(io), 0, 0);
             }
-#pragma unroll
-            for (int s = 0; s < KD; ++s) kb[s] = kn[s];
+            cnt[a] += group_popc(mt, g);
+            ties[a] += group_popc(meq, g);
         }
-    }
+    }, NV4{});
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
         const int t = t0 + 4 * a + g;
         if (t >= T) continue;
         const size_t rowo = static_cast<size_t>(b) * T + t;
         for (int p = cnt[a] + c; p < nsel; p += 16) sel[rowo * nsel + p] = -1;
-        if (imp != nullptr)
+        if (IMP)
             for (int j = 16 * ntj + c; j < nb; j += 16) imp[rowo * nb + j] = 0.f;
     }
 }
@@ -447,7 +547,7 @@ select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct QsaLayout {
-    size_t q16, qinv, kf, k16, part, kinv, total;
+    size_t q16, qinv, qnorm, kf, k16, part, kstat, total;
     int nb, nparts;
 };
 
@@ -457,12 +557,13 @@ QsaLayout qsa_layout(int B, int T, int d, int r) {
     L.nparts = (L.nb + kPoolBlocks - 1) / kPoolBlocks;
     const size_t BT = static_cast<size_t>(B) * T, Bn = static_cast<size_t>(B) * L.nb;
     size_t o = 0;
-    L.q16 = o;  o = align256(o + BT * kHq * d * 2);
-    L.qinv = o; o = align256(o + BT * kHq * 4);
-    L.kf = o;   o = align256(o + Bn * d * 4);
-    L.k16 = o;  o = align256(o + Bn * d * 2);
-    L.part = o; o = align256(o + static_cast<size_t>(B) * L.nparts * 4);
-    L.kinv = o; o = align256(o + static_cast<size_t>(B) * 4);
+    L.q16 = o;   o = align256(o + BT * kHq * d * 2);
+    L.qinv = o;  o = align256(o + BT * kHq * 4);
+    L.qnorm = o; o = align256(o + BT * kHq * 4);
+    L.kf = o;    o = align256(o + Bn * d * 4);
+    L.k16 = o;   o = align256(o + Bn * d * 2);
+    L.part = o;  o = align256(o + static_cast<size_t>(B) * L.nparts * 8);
+    L.kstat = o; o = align256(o + static_cast<size_t>(B) * 8);
     L.total = o;
     return L;
 }
@@ -473,23 +574,30 @@ hipError_t launch_qsa_t(const QsaArgs &a) {
     char *ws = static_cast<char *>(a.ws);
     f16 *q16 = reinterpret_cast<f16 *>(ws + L.q16);
     float *qinv = reinterpret_cast<float *>(ws + L.qinv);
+    float *qnorm = reinterpret_cast<float *>(ws + L.qnorm);
     float *kf = reinterpret_cast<float *>(ws + L.kf);
     f16 *k16 = reinterpret_cast<f16 *>(ws + L.k16);
-    float *part = reinterpret_cast<float *>(ws + L.part);
-    float *kinv = reinterpret_cast<float *>(ws + L.kinv);
+    float2 *part = reinterpret_cast<float2 *>(ws + L.part);
+    float2 *kstat = reinterpret_cast<float2 *>(ws + L.kstat);
     const double log2base = a.rope_dims > 0 ? log2(static_cast<double>(a.rope_base)) : 0.0;
     const size_t BT = static_cast<size_t>(a.B) * a.T;
     hipLaunchKernelGGL((rope_q_kernel<D, TI>), dim3(static_cast<unsigned>(BT)), dim3(256), 0,
-                       a.stream, static_cast<const TI *>(a.q), q16, qinv, a.T, a.rope_dims,
-                       log2base);
+                       a.stream, static_cast<const TI *>(a.q), q16, qinv, qnorm, a.T,
+                       a.rope_dims, log2base);
     hipLaunchKernelGGL((pool_k_kernel<D, TI>), dim3(a.B * L.nparts), dim3(256), 0, a.stream,
                        static_cast<const TI *>(a.k), kf, part, a.T, a.r, L.nb, L.nparts,
                        a.rope_dims, log2base);
     hipLaunchKernelGGL((pack_k_kernel<D>), dim3(a.B * L.nparts), dim3(256), 0, a.stream, kf, part,
-                       k16, kinv, L.nb, L.nparts);
+                       k16, kstat, L.nb, L.nparts);
     const int ntt = (a.T + kTok - 1) / kTok;
-    hipLaunchKernelGGL((select_kernel<D>), dim3(a.B * ntt), dim3(64), 0, a.stream, q16, qinv, k16,
-                       kinv, a.sel, a.imp, a.B, a.T, a.r, L.nb, a.nsel, a.scale * kLog2e);
+    if (a.imp != nullptr)
+        hipLaunchKernelGGL((select_kernel<D, true>), dim3(a.B * ntt), dim3(64), 0, a.stream, q16,
+                           qinv, qnorm, k16, kstat, a.sel, a.imp, a.B, a.T, a.r, L.nb, a.nsel,
+                           a.scale * kLog2e);
+    else
+        hipLaunchKernelGGL((select_kernel<D, false>), dim3(a.B * ntt), dim3(64), 0, a.stream,
+                           q16, qinv, qnorm, k16, kstat, a.sel, a.imp, a.B, a.T, a.r, L.nb,
+                           a.nsel, a.scale * kLog2e);
     return hipGetLastError();
 }
 

@@ -268,9 +268,9 @@ def test_qsa_validation(lib, kw, status):
 
 
 def test_qsa_workspace_and_empty_calls(lib):
-    # q16 + qinv + kbar fp32 + kbar fp16 + partial maxima + scale, each 256-aligned
     n = gdn.gdn_qsa_workspace_size(1, 65536, 4, 128, 4)
-    assert n == 65536 * 4 * 128 * 2 + 65536 * 4 * 4 + 16384 * 128 * (4 + 2) + 1024 + 256
+    # q16 + qinv + qnorm + kbar fp32 + kbar fp16 + partial maxima (2 floats) + batch stats
+    assert n == 65536 * 4 * 128 * 2 + 2 * 65536 * 4 * 4 + 16384 * 128 * (4 + 2) + 2048 + 256
     assert gdn.gdn_qsa_workspace_size(1, 64, 2, 128, 4) == 0
     assert gdn.gdn_qsa_workspace_size(0, 64, 4, 128, 4) == 0
     assert qsa_call(B=0) == gdn.GDN_OK

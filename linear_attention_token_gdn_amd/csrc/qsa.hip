@@ -18,7 +18,8 @@
 //   rope_q_kernel   rotated queries -> fp16 with a power-of-two scale per (token, head) row
 //   pool_k_kernel   block means, rotated at the block's first position -> fp32, plus one
 //                   partial max |kbar| per 64 blocks
-//   pack_k_kernel   fp32 -> fp16 with one power-of-two scale per batch (from the partial maxima)
+//   pack_k_kernel   fp32 -> fp16 with one power-of-two scale per batch (from the partial
+//                   maxima), stored in MFMA-fragment order
 //   select_kernel   one wavefront per 16 queries: the scores on the matrix cores (fp16 in,
 //                   fp32 accumulate) in sweeps over the eligible blocks -- one for the softmax
 //                   statistics, up to four for an exact 8-bit radix select of the nsel-th
@@ -164,12 +165,18 @@ pool_k_kernel(const TI *__restrict__ k, float *__restrict__ kf, float2 *__restri
 
 // ---------------------------------------------------------------------------------------
 // pack_k_kernel: every workgroup of batch b reduces the batch's partial maxima (the same value
-// in each), converts its 64 blocks to fp16 with the batch's power-of-two scale; the first one
+// in each) and converts its 64 blocks to fp16 with the batch's power-of-two scale; the first one
 // also stores {inverse scale, upper bound of the fp16 rows' L2 norms}.
+//
+// The fp16 keys are stored in MFMA-fragment order: for every tile of 16 blocks and every 32-wide
+// k-step, the 64 lanes' 16-byte B-operand pieces (lane l: block 16 tile + l%16, dimensions
+// 32 s + 8 (l/16) .. +7) lie contiguously in 1 KiB, so the select kernel reads each operand
+// with one fully coalesced load.  Blocks past the end of the last tile are zero.
 template <int D>
 __global__ void __launch_bounds__(256)
 pack_k_kernel(const float *__restrict__ kf, const float2 *__restrict__ part,
               f16 *__restrict__ k16, float2 *__restrict__ kstat, int nb, int nparts) {
+    constexpr int KD = D / 32;
     __shared__ float s_max[4], s_nrm[4];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int b = blockIdx.x / nparts, p = blockIdx.x % nparts;
@@ -190,17 +197,25 @@ pack_k_kernel(const float *__restrict__ kf, const float2 *__restrict__ part,
         const float n = fmaxf(fmaxf(s_nrm[0], s_nrm[1]), fmaxf(s_nrm[2], s_nrm[3]));
         kstat[b] = make_float2(ldexpf(1.f, -e), ldexpf(n, e) * (1.f + 0x1p-9f) + 0x1p-14f);
     }
-    const int j0 = p * kPoolBlocks, nblk = min(kPoolBlocks, nb - j0);
-    const size_t base = (static_cast<size_t>(b) * nb + j0) * D;
-    for (int i = threadIdx.x * 8; i < nblk * D; i += 256 * 8) {
-        const float4 lo = *reinterpret_cast<const float4 *>(kf + base + i);
-        const float4 hi = *reinterpret_cast<const float4 *>(kf + base + i + 4);
+    const int ntk = (nb + 15) / 16;
+    const int tile0 = p * (kPoolBlocks / 16), ntl = min(kPoolBlocks / 16, ntk - tile0);
+    const size_t obase = (static_cast<size_t>(b) * ntk + tile0) * KD * 512;  // in fp16 elements
+    for (int i = threadIdx.x; i < ntl * KD * 64; i += 256) {
+        const int ln = i & 63, s = (i >> 6) % KD, tl = (i >> 6) / KD;
+        const int j = (tile0 + tl) * 16 + (ln & 15), d0 = 32 * s + 8 * (ln >> 4);
+        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (j < nb) {
+            const float *src = kf + (static_cast<size_t>(b) * nb + j) * D + d0;
+            const float4 lo = *reinterpret_cast<const float4 *>(src);
+            const float4 hi = *reinterpret_cast<const float4 *>(src + 4);
+            v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+            v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+        }
         f16x8 h;
-        h[0] = static_cast<f16>(ldexpf(lo.x, e)); h[1] = static_cast<f16>(ldexpf(lo.y, e));
-        h[2] = static_cast<f16>(ldexpf(lo.z, e)); h[3] = static_cast<f16>(ldexpf(lo.w, e));
-        h[4] = static_cast<f16>(ldexpf(hi.x, e)); h[5] = static_cast<f16>(ldexpf(hi.y, e));
-        h[6] = static_cast<f16>(ldexpf(hi.z, e)); h[7] = static_cast<f16>(ldexpf(hi.w, e));
-        *reinterpret_cast<f16x8 *>(k16 + base + i) = h;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) h[u] = static_cast<f16>(ldexpf(v[u], e));
+        *reinterpret_cast<f16x8 *>(k16 + obase + (static_cast<size_t>(tl) * KD + s) * 512 +
+                                   8 * ln) = h;
     }
 }
 
@@ -258,8 +273,8 @@ select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
               float *__restrict__ imp, int B, int T, int r, int nb, int nsel, float scale_log2e) {
     constexpr int KD = D / 32;
     __shared__ unsigned s_hist[kHistWords];
-    __shared__ unsigned s_pref[kTok], s_mask[kTok];
-    __shared__ int s_krem[kTok], s_kt[kTok], s_act[kTok];
+    __shared__ unsigned s_lo[kTok], s_hi[kTok];
+    __shared__ int s_shift[kTok], s_krem[kTok], s_kt[kTok], s_act[kTok];
 
     const int lane = threadIdx.x, g = lane >> 4, c = lane & 15;
     const int ntt = (T + kTok - 1) / kTok;
@@ -291,12 +306,14 @@ select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
             ls[a][h] = fabsf(cf[a][h]) * qnorm[qr + h] * ks.y * (1.f + 0x1p-10f);
         }
     }
-    const f16 *kbase = k16 + static_cast<size_t>(b) * nb * D + 8 * g;
+    // fragment-ordered keys (pack_k_kernel): one coalesced 1 KiB load per operand
+    const int ntk = (nb + 15) / 16;
+    const f16 *kbase = k16 + static_cast<size_t>(b) * ntk * KD * 512 + 8 * lane;
     auto load_b = [&](int jt, f16x8 (&kb)[KD]) {
-        const int j = min(16 * jt + c, nb - 1);
+        const size_t o = static_cast<size_t>(min(jt, ntk - 1)) * KD * 512;
 #pragma unroll
         for (int s = 0; s < KD; ++s)
-            kb[s] = *reinterpret_cast<const f16x8 *>(kbase + static_cast<size_t>(j) * D + 32 * s);
+            kb[s] = *reinterpret_cast<const f16x8 *>(kbase + o + s * 512);
     };
     auto scores = [&](const f16x8 (&kb)[KD], f32x4 (&acc)[4]) {
 #pragma unroll
@@ -403,45 +420,77 @@ select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
         }
     }
 
-    // ---- per-query selection state: keep blocks with (key & mask) > pref, and the first
-    //      kt (in index order) of those with (key & mask) == pref.  key = bits of the
-    //      importance (positive floats order as their bits).
+    // ---- exact selection of the nsel largest keys per query (key = the fp32 bits of the
+    //      importance: positive floats order as their bits).  Each pass histograms the keys of
+    //      a query that lie in its current range [lo, hi) into 256 bins and narrows the range
+    //      to the bin holding the krem-th largest of them.  A query is done when a whole bin is
+    //      kept (count == krem) or the range is one value (keep its first krem copies in index
+    //      order).  In the end a block is kept if key >= hi, or lo <= key < hi among the first
+    //      kt such blocks; a query with at most nsel eligible blocks keeps all (lo = hi = 0).
+    //
+    //      The first pass bins by 1/16 of a binade over the 16 binades below 4.004 / nsel: the
+    //      importances of a query sum to 4 (four distributions), so the nsel-th largest cannot
+    //      exceed 4 / nsel, and the bins fall where the keys spread instead of on the few
+    //      exponent values they share.  The two end bins hold everything below and above.
+    const unsigned wtop = __float_as_uint(4.f * (1.f + 0x1p-10f) / static_cast<float>(nsel)) >> 19;
+    const unsigned wbase = wtop - 254u;
     if (lane < kTok) {
-        const int n = nelig(t0 + lane);
-        s_pref[lane] = 0u;
-        s_mask[lane] = 0u;
+        s_lo[lane] = 0u;
+        s_hi[lane] = 0u;
+        s_shift[lane] = 0;
         s_kt[lane] = 0x7fffffff;
         s_krem[lane] = nsel;
-        s_act[lane] = n > nsel;  // otherwise every eligible block is kept
+        s_act[lane] = nelig(t0 + lane) > nsel;
     }
-    for (int pass = 0; pass < 4; ++pass) {
+    for (int pass = 0; pass < 5; ++pass) {
         __syncthreads();
         int any = 0;
 #pragma unroll
         for (int tk = 0; tk < kTok; ++tk) any |= s_act[tk];
         if (!any) break;
-        const int shift = 24 - 8 * pass;
-        const unsigned hi = pass == 0 ? 0u : ~((1u << (shift + 8)) - 1u);
         for (int i = lane; i < kHistWords; i += 64) s_hist[i] = 0u;
-        unsigned pref[4];
+        unsigned lo[4], wd[4];
+        int sh[4];
         bool act[4];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) { pref[a] = s_pref[4 * a + g]; act[a] = s_act[4 * a + g]; }
+        for (int a = 0; a < 4; ++a) {
+            const int tk = 4 * a + g;
+            lo[a] = s_lo[tk];
+            wd[a] = s_hi[tk] - s_lo[tk];
+            sh[a] = s_shift[tk];
+            act[a] = s_act[tk];
+        }
         __syncthreads();
-        sweep([&](int jt, f32x4 (&acc)[4]) {
-            const int j = 16 * jt + c;
+        if (pass == 0) {
+            sweep([&](int jt, f32x4 (&acc)[4]) {
+                const int j = 16 * jt + c;
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                unsigned key = __float_as_uint(head_sum(acc[a], cf[a], ls[a]));
-                asm volatile("" : "+v"(key));  // computed by every lane: no branch around it
-                const bool m = act[a] & (j < ne[a]) & (((key ^ pref[a]) & hi) == 0u);
-                const unsigned idx = m ? (4 * a + g) * 256 + ((key >> shift) & 255u)
-                                       : kTok * 256 + lane;
-                atomicAdd(&s_hist[idx], 1u);
-            }
-        }, NV4{});
+                for (int a = 0; a < 4; ++a) {
+                    unsigned key = __float_as_uint(head_sum(acc[a], cf[a], ls[a]));
+                    asm volatile("" : "+v"(key));  // computed by every lane: no branch around it
+                    const int d = min(max(static_cast<int>((key >> 19) - wbase), 0), 255);
+                    const unsigned idx = (act[a] & (j < ne[a])) ? (4 * a + g) * 256 + d
+                                                               : kTok * 256 + lane;
+                    atomicAdd(&s_hist[idx], 1u);
+                }
+            }, NV4{});
+        } else {
+            sweep([&](int jt, f32x4 (&acc)[4]) {
+                const int j = 16 * jt + c;
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    unsigned key = __float_as_uint(head_sum(acc[a], cf[a], ls[a]));
+                    asm volatile("" : "+v"(key));
+                    const unsigned off = key - lo[a];
+                    const unsigned idx = (act[a] & (j < ne[a]) & (off < wd[a]))
+                                             ? (4 * a + g) * 256 + (off >> sh[a])
+                                             : kTok * 256 + lane;
+                    atomicAdd(&s_hist[idx], 1u);
+                }
+            }, NV4{});
+        }
         __syncthreads();
-        // find, per active query, the bin that holds the krem-th largest remaining key
+        // per active query: the bin holding the krem-th largest key of the range
         for (int tk = 0; tk < kTok; ++tk) {
             if (!s_act[tk]) continue;
             const int krem = s_krem[tk];
@@ -474,14 +523,27 @@ select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
             abv = __shfl(abv, src);
             cnt = __shfl(cnt, src);
             if (lane == 0) {
-                const int left = krem - abv;  // to take from this bin
-                s_pref[tk] |= static_cast<unsigned>(digit) << shift;
-                s_mask[tk] = ~((1u << shift) - 1u);
+                const unsigned d = static_cast<unsigned>(digit);
+                unsigned nlo, nhi;
+                if (pass == 0) {
+                    nlo = d == 0 ? 0u : (wbase + d) << 19;
+                    nhi = d == 255 ? 0x80000000u : (wbase + d + 1) << 19;
+                } else {
+                    const unsigned l0 = s_lo[tk];
+                    const int shf = s_shift[tk];
+                    nlo = l0 + (d << shf);
+                    nhi = min(s_hi[tk], nlo + (1u << shf));
+                }
+                const int left = krem - abv;  // to keep from the new range
+                s_lo[tk] = nlo;
+                s_hi[tk] = nhi;
                 s_krem[tk] = left;
-                if (cnt == left) {          // the whole bin is kept: done
-                    s_act[tk] = 0;
-                } else if (shift == 0) {    // one key value: keep its first `left` copies
-                    s_kt[tk] = left;
+                const unsigned w = nhi - nlo;
+                s_shift[tk] = w <= 256u ? 0 : 32 - __clz(w - 1u) - 8;
+                if (cnt == left) {
+                    s_act[tk] = 0;          // the whole range is kept
+                } else if (w == 1u || pass == 4) {
+                    s_kt[tk] = left;        // one key value: its first `left` copies
                     s_act[tk] = 0;
                 }
             }
@@ -490,34 +552,46 @@ select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
     __syncthreads();
 
     // ---- last sweep: write the kept blocks in ascending order (and the importance)
-    unsigned pref[4], mask[4];
+    unsigned lo[4], wd[4], hi[4];
     int kt[4], cnt[4], ties[4];
+    int anytie = 0;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-        pref[a] = s_pref[4 * a + g];
-        mask[a] = s_mask[4 * a + g];
-        kt[a] = s_kt[4 * a + g];
+        const int tk = 4 * a + g;
+        lo[a] = s_lo[tk];
+        hi[a] = s_hi[tk];
+        wd[a] = hi[a] - lo[a];
+        kt[a] = s_kt[tk];
         cnt[a] = 0;
         ties[a] = 0;
     }
+#pragma unroll
+    for (int tk = 0; tk < kTok; ++tk) anytie |= s_kt[tk] != 0x7fffffff;
     const int rows = min(kTok, T - t0);
     const size_t row0 = static_cast<size_t>(b) * T + t0;
     const __amdgpu_buffer_rsrc_t sel_rs = __builtin_amdgcn_make_buffer_rsrc(
         sel + row0 * nsel, 0, rows * nsel * 4, 0x00020000);
     const __amdgpu_buffer_rsrc_t imp_rs = __builtin_amdgcn_make_buffer_rsrc(
-        IMP ? static_cast<void *>(imp + row0 * nb) : static_cast<void *>(sel), 0, IMP ? rows * nb * 4 : 0, 0x00020000);
-    sweep([&](int jt, f32x4 (&acc)[4]) {
+        IMP ? static_cast<void *>(imp + row0 * nb) : static_cast<void *>(sel), 0,
+        IMP ? rows * nb * 4 : 0, 0x00020000);
+    auto out_body = [&](int jt, f32x4 (&acc)[4], auto tie_tag) {
+        constexpr bool TIES = decltype(tie_tag)::value != 0;
         const int j = 16 * jt + c;
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             float iv = head_sum(acc[a], cf[a], ls[a]);
             asm volatile("" : "+v"(iv));  // computed by every lane: no branch around it
-            const unsigned km = __float_as_uint(iv) & mask[a];
+            const unsigned key = __float_as_uint(iv);
             const bool el = j < ne[a];
-            const bool eq = el && km == pref[a];
-            const unsigned long long meq = __ballot(eq);
-            const bool take =
-                el && (km > pref[a] || (eq && ties[a] + group_below(meq, g, c) < kt[a]));
+            bool take = el && key >= hi[a];
+            unsigned long long meq = 0ull;
+            if (TIES) {
+                const bool inr = el && key - lo[a] < wd[a];
+                meq = __ballot(inr);
+                take = take || (inr && ties[a] + group_below(meq, g, c) < kt[a]);
+            } else {
+                take = take || (el && key - lo[a] < wd[a]);
+            }
             const unsigned long long mt = __ballot(take);
             const int pos = cnt[a] + group_below(mt, g, c);
             const int tl = 4 * a + g;  // query within the tile
@@ -530,9 +604,13 @@ select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
                                                       static_cast<int>(io), 0, 0);
             }
             cnt[a] += group_popc(mt, g);
-            ties[a] += group_popc(meq, g);
+            if (TIES) ties[a] += group_popc(meq, g);
         }
-    }, NV4{});
+    };
+    if (anytie)
+        sweep([&](int jt, f32x4 (&acc)[4]) { out_body(jt, acc, Nv<1>{}); }, NV4{});
+    else
+        sweep([&](int jt, f32x4 (&acc)[4]) { out_body(jt, acc, Nv<0>{}); }, NV4{});
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
         const int t = t0 + 4 * a + g;
@@ -561,7 +639,7 @@ QsaLayout qsa_layout(int B, int T, int d, int r) {
     L.qinv = o;  o = align256(o + BT * kHq * 4);
     L.qnorm = o; o = align256(o + BT * kHq * 4);
     L.kf = o;    o = align256(o + Bn * d * 4);
-    L.k16 = o;   o = align256(o + Bn * d * 2);
+    L.k16 = o;   o = align256(o + static_cast<size_t>(B) * ((L.nb + 15) / 16) * 16 * d * 2);
     L.part = o;  o = align256(o + static_cast<size_t>(B) * L.nparts * 8);
     L.kstat = o; o = align256(o + static_cast<size_t>(B) * 8);
     L.total = o;

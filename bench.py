@@ -14,7 +14,8 @@ on the host cores as a reported CPU baseline.  Outside the step, "decode_tokens"
 gdn_decode_tokens over T = 2, 4, 8 tokens of the decode workload per call (one read and one
 write of every state per call; in place, and for T = 8 also into a separate output state, as a
 verifier keeping the old state would call it); "prologue_and_packed" reports the prefill with
-the fused input prologue and a packed batch of 32 variable-length sequences.
+the fused input prologue and a packed batch of 32 variable-length sequences; "qsa_indexer"
+reports the QSA compressed indexer (gdn_qsa_index) on a 65536-token sequence.
 """
 from __future__ import annotations
 
@@ -213,6 +214,53 @@ def prologue_and_packed(gdn, torch, dev, stream, pt, pc, o, fs):
     return res
 
 
+EXP_PEAK_PER_S = 256 * 4 * 2.4e9 * 64 / 16  # v_exp_f32: a wave64 every 16 cycles per SIMD
+
+
+def qsa_indexer(gdn, torch, dev, stream, with_cpu=True):
+    """The QSA compressed indexer (gdn_qsa_index) on B=1, T=65536, 4 query heads and one key
+    head of d=128 (bf16, seeded N(0,1)), r=4 (16384 blocks), 512 blocks (2048 tokens) kept,
+    64 rotated dimensions.  The scoring and selection kernel is bound by the exponentials of
+    the softmax (4 per query-block pair per evaluation of the importance), so its roofline is
+    the vector units' exp rate; the fp64 oracle is timed on a sample of query rows."""
+    B, T, d, r, nsel = 1, 65536, 128, 4, 512
+    g = torch.Generator(device=dev)
+    g.manual_seed(21)
+    q = torch.randn(B, T, 4, d, device=dev, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, T, d, device=dev, generator=g).to(torch.bfloat16)
+    ws = torch.empty(gdn.gdn_qsa_workspace_size(B, T, 4, d, r), dtype=torch.uint8, device=dev)
+    sel = torch.empty(B, T, nsel, dtype=torch.int32, device=dev)
+    call = lambda: gdn.qsa_index(q, k, r=r, nsel=nsel, rope_dims=64, sel=sel, workspace=ws)
+    ms = _time(torch, stream, call, reps=5)
+    nb = -(-T // r)
+    pairs = sum(min((t + 1) // r, nb) for t in range(T - 1)) + nb  # eligible (query, block)
+    res = {"workload": "B=1 T=65536 Hq=4 d=128 r=4 nsel=512 rope_dims=64 bf16",
+           "ms": round(ms, 3), "queries_per_s": round(B * T / (ms * 1e-3), 1),
+           "scored_pairs_per_s": round(pairs / (ms * 1e-3), 1),
+           # the definition needs two evaluations per pair (softmax normaliser, importance)
+           "roofline": {"bound": "alu", "unit": "exp/s", "peak": EXP_PEAK_PER_S,
+                        "achieved": round(8 * pairs / (ms * 1e-3), 1),
+                        "frac": round(8 * pairs / (ms * 1e-3) / EXP_PEAK_PER_S, 4),
+                        "algorithmic_exps_per_pair": 8},
+           "score_TFLOPs_one_pass": round(2 * 4 * d * pairs / (ms * 1e-3) / 1e12, 2)}
+    if with_cpu:
+        import numpy as np
+        from oracle import qsa as oq
+        qn = q.float().cpu().numpy().astype(np.float64)
+        kn = k.float().cpu().numpy().astype(np.float64)
+        rows = np.linspace(T // 2, T - 1, 8).astype(np.int64)
+        t0 = time.perf_counter()
+        imp, elig = oq.importance(qn, kn, r, 64, 10000.0, 1.0 / d ** 0.5, rows=rows)
+        oq.select(imp, elig, nsel)
+        cpu_s = time.perf_counter() - t0
+        pairs_s = sum(min((int(t) + 1) // r, nb) for t in rows)
+        res["cpu_baseline"] = {"value": round(pairs_s / cpu_s, 1), "unit": "scored pairs/s",
+                               "kind": "oracle", "cores": 1,  # numpy loops, one thread
+                               "sample": "8 query rows in the second half of the sequence "
+                                         "(keys pooled for the whole sequence)"}
+    return res
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -311,7 +359,7 @@ def main():
     pre_tflops = flops / (pre_mean * 1e-3) / 1e12
     pre_gbs = pbytes / (pre_mean * 1e-3) / 1e9
     plan = gdn.gdn_chunk_fwd_plan(B, T, Hk, Hv, dk, dv, C, gdn.GDN_BF16)
-    pre_kernels = {"split": "prep_kernel<%d,%d> + scan_kernel<%d,%d> + out_kernel<%d,%d,float>"
+    pre_kernels = {"split": "prep_kernel<%d,%d,false> + scan_kernel<%d,%d> + out_kernel<%d,%d,float>"
                             % (dk, C, dk, C, dk, C),
                    "fused": "chunk_kernel<%d,%d,float>" % (dk, C)}.get(plan, plan)
     rooflines = {
@@ -334,7 +382,8 @@ def main():
         st_gbs = sbytes / (dec_mean * 1e-3) / 1e9
         tot_gbs = tbytes / (dec_mean * 1e-3) / 1e9
         rooflines["decode"] = {
-            "kernel": "decode_kernel<%d,%d,bf16,float>" % (dc["dk"], dc["dv"]), "bound": "hbm",
+            "kernel": "decode_kernel<%d,%d,bf16,float,false>" % (dc["dk"], dc["dv"]),
+            "bound": "hbm",
             "achieved": round(tot_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(tot_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode"),
             "algorithmic_bytes": tbytes, "mean_launch_ms": round(dec_mean, 4),
@@ -379,6 +428,8 @@ def main():
 
     # ---- the input prologue and packed sequences (not part of the step)
     extras = None if args.no_extras else prologue_and_packed(gdn, torch, dev, stream, pt, pc, o, fs)
+    qsa = None if args.no_extras else qsa_indexer(gdn, torch, dev, stream,
+                                                   with_cpu=not args.no_cpu_baseline)
 
     line = {
         "metric": "GDN prefill tokens/s + % bf16 MFMA peak; decode state GB/s % HBM peak",
@@ -402,6 +453,7 @@ def main():
         "decode": result_decode,
         "decode_tokens": multi,
         "prologue_and_packed": extras,
+        "qsa_indexer": qsa,
         "roofline": dict(rooflines[dom], kernel_role=dom),
         "rooflines": rooflines,
     }

@@ -37,8 +37,29 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
+_TARG = {"t": "bf16", "f": "float", "Lb0E": "false", "Lb1E": "true"}
+
+
+def _unmangle(name: str) -> str:
+    """`_ZN3gdn12_GLOBAL__N_1<len><name>I<args>E...` -> `name<args>` for the template
+    arguments used here (integers, bools, bf16, float); other names unchanged."""
+    import re
+    m = re.match(r"_ZN3gdn12_GLOBAL__N_1(\d+)", name)
+    if not m:
+        return name
+    i = m.end()
+    n = int(m.group(1))
+    base, rest = name[i:i + n], name[i + n:]
+    if not rest.startswith("I"):
+        return base
+    args = re.findall(r"Li(\d+)E|(Lb[01]E)|([tf])(?=[^a-z]|$)", rest[1:rest.find("EE") + 1])
+    out = [a or _TARG[b or c] for a, b, c in args]
+    return "%s<%s>" % (base, ", ".join(out))
+
+
 def short_name(name: str) -> str:
     """Kernel name without namespaces, return type and parameter list."""
+    name = _unmangle(name)
     name = name.replace("(anonymous namespace)::", "").replace("void ", "", 1)
     depth, cut = 0, len(name)
     for i, ch in enumerate(name):  # first '(' outside template brackets
@@ -142,7 +163,8 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, command):
     if pre:
         rec["prefill"] = {"kernels": pre, "bytes_per_launch": sum(sum(res[n]) for n in pre),
                           "source_sha256_16": source_hash(SOURCES["prefill"])}
-    dec = [n for n in res if n.startswith("decode_kernel")]
+    # the single-token decode kernel (MULTI = false) of the benchmark step
+    dec = [n for n in res if n.startswith("decode_kernel") and n.endswith("false>")]
     if dec:
         rec["decode"] = {"kernels": dec, "bytes_per_launch": sum(sum(res[n]) for n in dec),
                          "source_sha256_16": source_hash(SOURCES["decode"])}

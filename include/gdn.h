@@ -209,7 +209,7 @@ size_t gdn_chunk_fwd_varlen_workspace_size(int num_seqs, int T, int Hk, int Hv, 
  * Outputs must not overlap each other or any input.  The workspace (at least
  * gdn_backward_workspace_size(...) bytes, 256-byte aligned) holds a state checkpoint every
  * 64 tokens per chain, one block of recomputed states per chain and, when a chain is split
- * into slices of 32 state columns (dv > 32) or with grouped heads, the per-slice and
+ * into slices of 16 state columns (dv > 16) or with grouped heads, the per-slice and
  * per-value-head parts of dq, dk, dbeta and dg.  Supported: dk, dv in {16, 32, 64, 128}; in_dtype and
  * dout_dtype GDN_F32 or GDN_BF16.  Deterministic (no atomics).  B = 0 is a no-op.
  */

@@ -10,7 +10,7 @@
 //
 // Both recurrences act on the state column by column (S_t's column j depends only on column j
 // of S_{t-1}; dS_{t-1}'s column j only on column j of dS), so every (b, hv) chain is split into
-// slices of SW <= 32 state columns, one workgroup each.  Only per-token scalars and row vectors
+// slices of SW <= 16 state columns, one workgroup each.  Only per-token scalars and row vectors
 // need sums over all columns: each slice writes its parts of dq, dk (rows of S dO, dS w and
 // X u), dbeta (u . w) and dg (<dS, X>, u . e), and a second kernel adds the slices (and the
 // value heads of a grouped q/k head) up -- no atomics, so the results are deterministic.
@@ -49,7 +49,7 @@ __device__ __forceinline__ void store1(float x, __amdgpu_buffer_rsrc_t r, unsign
 }
 
 template <int DK, int DV> struct BwdShape {
-    static constexpr int SW = DV < 32 ? DV : 32;                 // state columns per slice
+    static constexpr int SW = DV < 16 ? DV : 16;                 // state columns per slice
     static constexpr int NS = DV / SW;                           // slices per chain
     static constexpr int CG = SW / 4;                            // float4 groups per row
     static constexpr int R = DK < 256 / CG ? DK : 256 / CG;      // row groups
@@ -345,7 +345,7 @@ struct BwdLayout {
     size_t ckpt, hist, dq, dk, db, dg, total;
 };
 BwdLayout bwd_layout(int B, int T, int Hk, int Hv, int dk, int dv) {
-    const int NS = dv < 32 ? 1 : dv / 32;
+    const int NS = dv < 16 ? 1 : dv / 16;
     const size_t chains = static_cast<size_t>(B) * Hv;
     const size_t nblk = (static_cast<size_t>(T) + kBlk - 1) / kBlk;
     const size_t SS = static_cast<size_t>(dk) * dv;  // all slices of a chain

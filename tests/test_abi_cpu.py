@@ -231,10 +231,10 @@ def test_backward_validation(lib, kw, status):
 
 def test_backward_workspace_size(lib):
     n = gdn.gdn_backward_workspace_size(1, 4096, 16, 16, 128, 128)
-    # checkpoints + one block per chain, then the parts of dq, dk (4 slices of 32 columns)
+    # checkpoints + one block per chain, then the parts of dq, dk (8 slices of 16 columns)
     # and of dbeta, dg
-    assert n == ((16 * 64 + 16 * 65) * 128 * 128 + 2 * 4096 * 16 * 4 * 128
-                 + 2 * 4096 * 16 * 4) * 4
+    assert n == ((16 * 64 + 16 * 65) * 128 * 128 + 2 * 4096 * 16 * 8 * 128
+                 + 2 * 4096 * 16 * 8) * 4
     assert gdn.gdn_backward_workspace_size(1, 64, 2, 2, 32, 16) == (2 * 1 + 2 * 65) * 32 * 16 * 4
     assert gdn.gdn_backward_workspace_size(1, 100, 1, 2, 64, 64) > 0
     assert gdn.gdn_backward_workspace_size(0, 100, 1, 2, 64, 64) == 0

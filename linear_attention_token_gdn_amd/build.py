@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 SOURCES = ["gdn_api.hip", "decode.hip", "recurrent.hip", "chunk_mfma.hip", "chunk_split.hip",
-           "backward.hip", "qsa.hip"]
+           "backward.hip", "backward_chunk.hip", "qsa.hip"]
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

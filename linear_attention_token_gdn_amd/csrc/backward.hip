@@ -23,6 +23,9 @@
 // (double-buffered by token parity).  Every token's inputs are loaded one token ahead, and the
 // token loops have no branches (masked stores go through buffer resources whose range check
 // drops them), so those loads stay in flight while the previous token is processed.
+#include <stdlib.h>
+#include <string.h>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -330,6 +333,8 @@ __global__ void part_sum_kernel(const float *__restrict__ part, float *__restric
     }
 }
 
+}  // namespace
+
 hipError_t launch_part_sum(const float *part, float *out, size_t n, int M, int W,
                            hipStream_t st) {
     if (n == 0) return hipSuccess;  // T = 0: nothing to sum (and no empty grid)
@@ -338,6 +343,8 @@ hipError_t launch_part_sum(const float *part, float *out, size_t n, int M, int W
     hipLaunchKernelGGL(part_sum_kernel, dim3(nb), dim3(256), 0, st, part, out, n, M, W);
     return hipGetLastError();
 }
+
+namespace {
 
 // workspace: checkpoints, block history, then (when a sum is needed) the parts of dq, dk
 // (rows x Hv x NS x dk) and of dbeta, dg (rows x Hv x NS)
@@ -422,11 +429,21 @@ template <int DK> hipError_t launch_dk(const BackwardArgs &a) {
 }  // namespace
 
 size_t backward_workspace(int B, int T, int Hk, int Hv, int dk, int dv) {
-    return bwd_layout(B, T, Hk, Hv, dk, dv).total;
+    const size_t tok = bwd_layout(B, T, Hk, Hv, dk, dv).total;
+    if ((dk == 64 || dk == 128) && (dv == 64 || dv == 128)) {
+        const size_t ch = backward_chunk_workspace(B, T, Hk, Hv, dk, dv);
+        return ch > tok ? ch : tok;  // enough for either path
+    }
+    return tok;
 }
 
+// GDN_BWD=token pins the token-recurrent path (for comparisons); otherwise the chunk-parallel
+// path runs wherever it supports the sizes.
 hipError_t launch_backward(const BackwardArgs &a) {
     if (a.B == 0) return hipSuccess;
+    const char *env = getenv("GDN_BWD");
+    const bool token = env != nullptr && strcmp(env, "token") == 0;
+    if (!token && backward_chunk_supports(a)) return launch_backward_chunk(a);
     switch (a.dk_) {
     case 16: return launch_dk<16>(a);
     case 32: return launch_dk<32>(a);

@@ -54,6 +54,13 @@ struct BackwardArgs {
 // The reverse recurrence (csrc/backward.hip) and the workspace it needs.
 size_t backward_workspace(int B, int T, int Hk, int Hv, int dk, int dv);
 hipError_t launch_backward(const BackwardArgs &a);
+// The chunk-parallel form (csrc/backward_chunk.hip), for dk, dv in {64, 128}.
+bool backward_chunk_supports(const BackwardArgs &a);
+size_t backward_chunk_workspace(int B, int T, int Hk, int Hv, int dk, int dv);
+hipError_t launch_backward_chunk(const BackwardArgs &a);
+// out[r][h][i] = sum_j part[((r H + h) M + j) W + i] for i < W, n = rows * H * W outputs
+hipError_t launch_part_sum(const float *part, float *out, size_t n, int M, int W,
+                           hipStream_t st);
 
 struct QsaArgs {
     const void *q, *k;   // [B, T, 4, d] and [B, T, d] (in_dt)

@@ -1,5 +1,7 @@
 """GPU parity of the backward (gdn_backward, through its C ABI) against the fp64 oracle's
-reverse recurrence (itself pinned to torch autograd and a closed form on the CPU).
+reverse recurrence (itself pinned to torch autograd and a closed form on the CPU).  Head sizes
+in {64, 128} run the chunk-parallel kernels by default; GDN_BWD=token pins the token-recurrent
+path, and both are tested.
 
 Bars (tests/parity.py), per gradient tensor: fp32 inputs eps <= 1e-5 max(1, M); bf16 inputs
 eps <= 2e-3 M.  The kernel computes in fp32 from the stored inputs, so bf16 inputs add no
@@ -60,13 +62,30 @@ def test_backward_head_sizes(dk, dv, dtype):
         check(got[n], ref[r], dtype, "%s dk%d dv%d %s" % (n, dk, dv, dtype))
 
 
-def test_backward_long_ragged_grouped():
-    """T = 157 (three checkpoint blocks, the last one partial), grouped heads (Hv = 2 Hk),
-    no initial state, bf16 gradient of the output."""
+@pytest.mark.parametrize("variant", ["chunk", "token"])
+def test_backward_long_ragged_grouped(variant, monkeypatch):
+    """T = 157 (three checkpoint blocks / chunks, the last one partial), grouped heads
+    (Hv = 2 Hk), no initial state, bf16 gradient of the output."""
+    if variant == "token":
+        monkeypatch.setenv("GDN_BWD", "token")
     inp = make_inputs(1, 157, 2, 4, 128, 128, dtype="bf16", seed=810)
     got, ref = run_case(inp, 811, dout_bf16=True)
     for n, r in GRADS:
-        check(got[n], ref[r], "bf16", n + " T=157 gqa")
+        check(got[n], ref[r], "bf16", n + " T=157 gqa " + variant)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 64), (64, 128), (128, 128)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_chunked_against_token(dk, dv, dtype, monkeypatch):
+    """The two paths against the oracle on one longer ragged case (T = 300: five chunks), with
+    an initial state and a final-state gradient."""
+    inp = make_inputs(1, 300, 1, 2, dk, dv, dtype=dtype, s0_std=0.02, seed=840 + dk + dv)
+    got, ref = run_case(inp, 841, scale=0.8)
+    monkeypatch.setenv("GDN_BWD", "token")
+    tok, _ = run_case(inp, 841, scale=0.8)
+    for n, r in GRADS:
+        check(got[n], ref[r], dtype, "%s chunk dk%d dv%d %s" % (n, dk, dv, dtype))
+        check(tok[n], ref[r], dtype, "%s token dk%d dv%d %s" % (n, dk, dv, dtype))
 
 
 @pytest.mark.parametrize("T", [0, 1, 64, 65])

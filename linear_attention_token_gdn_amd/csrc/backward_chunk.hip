@@ -33,6 +33,18 @@ constexpr int kC = 64;    // tokens per chunk
 constexpr int kNT = 256;  // threads per workgroup
 
 __device__ __forceinline__ void bar() { __syncthreads(); }
+// Workgroup barrier that waits only for LDS traffic, not for global loads still in flight
+// (__syncthreads also waits for those, which would defeat a prefetch).
+__device__ __forceinline__ void lds_bar() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// A uniform fp32 load through a buffer resource: a vector-memory load, so a load in flight
+// does not hold up the LDS-only barrier (which also counts scalar loads).
+__device__ __forceinline__ float vload1(const float *p) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), 0, 4,
+                                                                       0x00020000);
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, 0));
+}
 
 // Register-tile product: acc[i][j] += sum_k A(row_i, k) B(k, col_j), row_i = ty + i NY,
 // col_j = tx + j NX with (ty, tx) = (tid / NX, tid % NX) and NY = 256 / NX.  A(r, k) = A[r ar
@@ -70,6 +82,22 @@ template <int NX> __device__ __forceinline__ float row_sum(float x) {
     return x;
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// One 16 x 16 output block on the matrix cores in fp32: acc += A(16 x K) B(K x 16), with A(m, k)
+// = A[m ar + k ak] and B(k, n) = B[k bk + n bc] (pointers already at the block's origin).
+// Lane l supplies A(l%16, k + l/16) and B(k + l/16, l%16) and holds D(4 (l/16) + i, l%16).
+__device__ __forceinline__ f32x4 mfma_blk(f32x4 acc, const float *A, int ar, int ak,
+                                          const float *B, int bk, int bc, int K) {
+    const int lane = threadIdx.x & 63, mi = lane & 15, kq = lane >> 4;
+    const float *a = A + mi * ar + kq * ak;
+    const float *b = B + kq * bk + mi * bc;
+#pragma unroll 8
+    for (int k = 0; k < K; k += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[k * ak], b[k * bk], acc, 0, 0, 0);
+    return acc;
+}
+
 template <int DK, int DV> struct CB {
     // records per (chain, chunk), fp32, row-major
     static constexpr size_t OFF_W = 0;                          // [C][DK]
@@ -96,15 +124,50 @@ __device__ __forceinline__ float wave_scan(float x, int lane) {
     return x;
 }
 
-// load rows t0 .. t0+L-1 of a [.., H, D] tensor at head h into an LDS [C][ld] block (zeros past L)
-template <int D, typename TI>
-__device__ __forceinline__ void load_rows(float *dst, int ld, const TI *src, size_t row0, int H,
-                                          int h, int L, float mul = 1.f) {
-    for (int i = threadIdx.x; i < kC * D; i += kNT) {
-        const int r = i / D, c = i - r * D;
-        dst[r * ld + c] = r < L ? mul * load_f32(src + ((row0 + r) * H + h) * D + c) : 0.f;
+// Bulk copies with every load in flight before the first LDS store: a ROWS x COLS tile (COLS a
+// multiple of 4) of a row-major fp32 matrix with row stride sld, as float4 per thread.
+template <int ROWS, int COLS> struct Tile4 {
+    static constexpr int N = ROWS * COLS / 4 / kNT;  // float4 per thread
+    static_assert(N * 4 * kNT == ROWS * COLS, "tile must split evenly over the threads");
+    float4 v[N];
+    __device__ __forceinline__ void load(const float *src, int sld, float mul = 1.f) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int idx = (i * kNT + threadIdx.x) * 4, r = idx / COLS, c = idx - r * COLS;
+            v[i] = *reinterpret_cast<const float4 *>(src + static_cast<size_t>(r) * sld + c);
+            v[i].x *= mul; v[i].y *= mul; v[i].z *= mul; v[i].w *= mul;
+        }
     }
-}
+    // rows of a [.., H, D] input tensor (any stored type) at head h; zero past L
+    template <typename TI>
+    __device__ __forceinline__ void load_in(const TI *src, size_t row0, int H, int h, int c0,
+                                            int D, int L, float mul = 1.f) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int idx = (i * kNT + threadIdx.x) * 4, r = idx / COLS, c = idx - r * COLS;
+            const TI *p = src + ((row0 + min(r, L - 1)) * H + h) * D + c0 + c;
+            float4 x = load4(p);
+            const float m = r < L ? mul : 0.f;
+            v[i] = make_float4(m * x.x, m * x.y, m * x.z, m * x.w);
+        }
+    }
+    __device__ __forceinline__ void store(float *dst, int ld) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int idx = (i * kNT + threadIdx.x) * 4, r = idx / COLS, c = idx - r * COLS;
+            float *d = dst + r * ld + c;
+            d[0] = v[i].x; d[1] = v[i].y; d[2] = v[i].z; d[3] = v[i].w;
+        }
+    }
+    __device__ static __forceinline__ float4 load4(const float *p) {
+        return *reinterpret_cast<const float4 *>(p);
+    }
+    __device__ static __forceinline__ float4 load4(const bf16_t *p) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(p);
+        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+    }
+};
 
 // ---------------------------------------------------------------------------------------
 template <int DK, int DV, typename TI>
@@ -123,13 +186,24 @@ bprep_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
     const int tid = threadIdx.x;
     float *R = rec + (static_cast<size_t>(chain) * nch + c) * F::REC;
 
-    load_rows<DK>(sK, LK, k, row0, Hk, hq, L);
-    load_rows<DK>(sQ, LK, q, row0, Hk, hq, L);
-    load_rows<DV>(sV, LV, v, row0, Hv, hv, L);
-    if (tid < 64) {
-        const float gg = tid < L ? load_f32(g + (row0 + tid) * Hv + hv) : 0.f;
-        sgam[tid] = wave_scan(gg, tid);
-        sbeta[tid] = tid < L ? load_f32(beta + (row0 + tid) * Hv + hv) : 0.f;
+    {
+        Tile4<kC, DK> tk, tq;
+        Tile4<kC, DV> tv;
+        tk.load_in(k, row0, Hk, hq, 0, DK, L);
+        tq.load_in(q, row0, Hk, hq, 0, DK, L);
+        tv.load_in(v, row0, Hv, hv, 0, DV, L);
+        float gg = 0.f, bb = 0.f;
+        if (tid < 64 && tid < L) {
+            gg = load_f32(g + (row0 + tid) * Hv + hv);
+            bb = load_f32(beta + (row0 + tid) * Hv + hv);
+        }
+        tk.store(sK, LK);
+        tq.store(sQ, LK);
+        tv.store(sV, LV);
+        if (tid < 64) {
+            sgam[tid] = wave_scan(gg, tid);
+            sbeta[tid] = bb;
+        }
     }
     bar();
     const float glast = sgam[kC - 1];
@@ -207,7 +281,10 @@ bprep_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
 
 // ---------------------------------------------------------------------------------------
 // bscan_kernel: blocks [0, chains * NSL) run the forward state chain, the rest the reverse
-// gradient chain; one block per (chain, 16-column slice).
+// gradient chain; one block per (chain, 16-column slice).  The per-chunk products run on the
+// matrix cores (fp32), each wavefront owning whole 16 x 16 output blocks; the LDS row strides
+// are chosen per operand orientation so that a product's 64 lanes read 64 different banks
+// (stride = 4 mod 64 floats where a lane group walks rows, 16 mod 64 where it walks columns).
 template <int DK, int DV, typename TD>
 __global__ void __launch_bounds__(kNT)
 bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
@@ -215,11 +292,12 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
              float *__restrict__ Sc, float *__restrict__ dSe, float *__restrict__ dS0, int T,
              int Hv, int nch, int chains, float scale) {
     using F = CB<DK, DV>;
-    constexpr int LK = F::LK, LC = F::LC, NSL = DV / 16, LS = 17;
-    constexpr int TMS = DK / 64;  // rows per thread of a DK x 16 tile (NX = 4, NY = 64)
-    __shared__ float sM1[kC * LK], sM2[kC * LK], sM3[kC * LK], sP[kC * LC];
-    __shared__ float sS[DK * LS], sD[kC * LS], sO[kC * LS];
-    const int tid = threadIdx.x;
+    constexpr int NSL = DV / 16;
+    constexpr int L4 = DK + 4, L16 = DK + 16, LP = kC + 16;  // strides (see above)
+    constexpr int NRB = DK / 16 / 4;                          // DK-row blocks per wavefront
+    __shared__ float sM1[kC * L16], sM2[kC * L16], sM3[kC * L16], sP[kC * LP];
+    __shared__ float sS[DK * 16], sD[kC * 16], sO[kC * 16];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, mi = lane & 15, kq = lane >> 4;
     const bool fwd = blockIdx.x < chains * NSL;
     const int idx = fwd ? blockIdx.x : blockIdx.x - chains * NSL;
     const int chain = idx / NSL, sl = idx - chain * NSL, col0 = 16 * sl;
@@ -228,100 +306,116 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
     const float *init = fwd ? s0 : dST;
     for (int i = tid; i < DK * 16; i += kNT) {
         const int r = i / 16, cc = i % 16;
-        sS[r * LS + cc] = init ? init[chain * SS + r * DV + col0 + cc] : 0.f;
+        sS[i] = init ? init[chain * SS + r * DV + col0 + cc] : 0.f;
     }
-    const int ty = tid / 4, tx = tid % 4;  // tiles with NX = 4, NY = 64
-    auto load_mat = [&](float *dst, int ld, const float *src, int rows, int cols) {
-        for (int i = tid; i < rows * cols; i += kNT) {
-            const int r = i / cols, cc = i - r * cols;
-            dst[r * ld + cc] = src[i];
-        }
-    };
     auto save_state = [&](float *dst) {
         for (int i = tid; i < DK * 16; i += kNT) {
             const int r = i / 16, cc = i % 16;
-            dst[r * DV + col0 + cc] = sS[r * LS + cc];
+            dst[r * DV + col0 + cc] = sS[i];
         }
     };
+    auto recp = [&](int c) { return rec + (static_cast<size_t>(chain) * nch + c) * F::REC; };
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    // The next chunk's operands are loaded into registers while this chunk is computed, then
+    // written to LDS: the sequential chain never waits for a record fetch.
     if (fwd) {
+        Tile4<kC, DK> nW, nK;
+        Tile4<kC, 16> nU;
+        auto fetch = [&](int c) {
+            const float *R = recp(c);
+            nW.load(R + F::OFF_W, DK);
+            nK.load(R + F::OFF_KT, DK);
+            nU.load(R + F::OFF_U + col0, DV);
+        };
+        auto put = [&]() {
+            nW.store(sM1, L4);   // A, rows walked by lanes
+            nK.store(sM2, L16);  // A transposed
+            nU.store(sO, 16);
+        };
+        fetch(0);
+        float el = vload1(recp(0) + F::OFF_EL);
+        put();
         for (int c = 0; c < nch; ++c) {
-            const float *R = rec + (static_cast<size_t>(chain) * nch + c) * F::REC;
-            bar();
+            lds_bar();
             save_state(Sc + (static_cast<size_t>(chain) * nch + c) * SS);
-            load_mat(sM1, LK, R + F::OFF_W, kC, DK);
-            load_mat(sM2, LK, R + F::OFF_KT, kC, DK);
-            for (int i = tid; i < kC * 16; i += kNT) {
-                const int r = i / 16, cc = i % 16;
-                sO[r * LS + cc] = R[F::OFF_U + r * DV + col0 + cc];
-            }
-            const float el = R[F::OFF_EL];
-            bar();
-            // Delta = U - W S  (64 x 16)
+            fetch(min(c + 1, nch - 1));
+            const float eln = vload1(recp(min(c + 1, nch - 1)) + F::OFF_EL);
+            // Delta = U - W S: wavefront w, rows 16w..16w+15
             {
-                float d[1][4];
-                zero(d);
-                mm<1, 4, 4>(d, sM1, LK, 1, sS, LS, 1, DK);
+                const f32x4 d = mfma_blk(z4, sM1 + 16 * w * L4, L4, 1, sS, 16, 1, DK);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) sD[ty * LS + tx + 4 * j] = sO[ty * LS + tx + 4 * j] - d[0][j];
+                for (int i = 0; i < 4; ++i) {
+                    const int o = (16 * w + 4 * kq + i) * 16 + mi;
+                    sD[o] = sO[o] - d[i];
+                }
             }
-            bar();
-            // S <- e^gamma_last S + Kt^T Delta  (DK x 16; each thread updates its own entries)
-            {
-                float s[TMS][4];
-                zero(s);
-                mm<TMS, 4, 4>(s, sM2, 1, LK, sD, LS, 1, kC);
+            lds_bar();
+            // S <- e^gamma_last S + Kt^T Delta: row blocks w, w + 4, ...
 #pragma unroll
-                for (int i = 0; i < TMS; ++i)
+            for (int j = 0; j < NRB; ++j) {
+                const int m0 = 16 * (w + 4 * j);
+                const f32x4 u = mfma_blk(z4, sM2 + m0, 1, L16, sD, 16, 1, kC);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        float &x = sS[(ty + 64 * i) * LS + tx + 4 * j];
-                        x = el * x + s[i][j];
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    float &x = sS[(m0 + 4 * kq + i) * 16 + mi];
+                    x = el * x + u[i];
+                }
             }
+            lds_bar();
+            put();
+            el = eln;
         }
     } else {
+        Tile4<kC, kC> nP;
+        Tile4<kC, DK> nK, nG, nW;
+        Tile4<kC, 16> nO;
+        auto fetch = [&](int c) {
+            const float *R = recp(c);
+            nP.load(R + F::OFF_P, kC);
+            nK.load(R + F::OFF_KT, DK);
+            nG.load(R + F::OFF_GQ, DK);
+            nW.load(R + F::OFF_W, DK);
+            nO.load_in(dO, static_cast<size_t>(b) * T + c * kC, Hv, hv, col0, DV,
+                       min(kC, T - c * kC), scale);
+        };
+        auto put = [&]() {
+            nP.store(sP, LP);    // A transposed
+            nK.store(sM1, L4);   // A
+            nG.store(sM2, L16);  // A transposed
+            nW.store(sM3, L16);  // A transposed
+            nO.store(sO, 16);
+        };
+        fetch(nch - 1);
+        float el = vload1(recp(nch - 1) + F::OFF_EL);
+        put();
         for (int c = nch - 1; c >= 0; --c) {
-            const float *R = rec + (static_cast<size_t>(chain) * nch + c) * F::REC;
-            bar();
+            lds_bar();
             save_state(dSe + (static_cast<size_t>(chain) * nch + c) * SS);
-            load_mat(sP, LC, R + F::OFF_P, kC, kC);
-            load_mat(sM1, LK, R + F::OFF_KT, kC, DK);
-            load_mat(sM2, LK, R + F::OFF_GQ, kC, DK);
-            load_mat(sM3, LK, R + F::OFF_W, kC, DK);
-            const int L = min(kC, T - c * kC);
-            const size_t row0 = static_cast<size_t>(b) * T + c * kC;
-            for (int i = tid; i < kC * 16; i += kNT) {
-                const int r = i / 16, cc = i % 16;
-                sO[r * LS + cc] =
-                    r < L ? scale * load_f32(dO + ((row0 + r) * Hv + hv) * DV + col0 + cc) : 0.f;
-            }
-            const float el = R[F::OFF_EL];
-            bar();
-            // dDelta = P^T dO' + Kt dS  (64 x 16)
+            fetch(max(c - 1, 0));
+            const float eln = vload1(recp(max(c - 1, 0)) + F::OFF_EL);
+            // dDelta = P^T dO' + Kt dS: wavefront w, rows 16w..
             {
-                float d[1][4];
-                zero(d);
-                mm<1, 4, 4>(d, sP, 1, LC, sO, LS, 1, kC);
-                mm<1, 4, 4>(d, sM1, LK, 1, sS, LS, 1, DK);
+                f32x4 d = mfma_blk(z4, sP + 16 * w, 1, LP, sO, 16, 1, kC);
+                d = mfma_blk(d, sM1 + 16 * w * L4, L4, 1, sS, 16, 1, DK);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) sD[ty * LS + tx + 4 * j] = d[0][j];
+                for (int i = 0; i < 4; ++i) sD[(16 * w + 4 * kq + i) * 16 + mi] = d[i];
             }
-            bar();
+            lds_bar();
             // dS <- e^gamma_last dS + (Gm Q)^T dO' - W^T dDelta
-            {
-                float s[TMS][4], w[TMS][4];
-                zero(s);
-                zero(w);
-                mm<TMS, 4, 4>(s, sM2, 1, LK, sO, LS, 1, kC);
-                mm<TMS, 4, 4>(w, sM3, 1, LK, sD, LS, 1, kC);
 #pragma unroll
-                for (int i = 0; i < TMS; ++i)
+            for (int j = 0; j < NRB; ++j) {
+                const int m0 = 16 * (w + 4 * j);
+                const f32x4 u = mfma_blk(z4, sM2 + m0, 1, L16, sO, 16, 1, kC);
+                const f32x4 x = mfma_blk(z4, sM3 + m0, 1, L16, sD, 16, 1, kC);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        float &x = sS[(ty + 64 * i) * LS + tx + 4 * j];
-                        x = el * x + s[i][j] - w[i][j];
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    float &y = sS[(m0 + 4 * kq + i) * 16 + mi];
+                    y = el * y + u[i] - x[i];
+                }
             }
+            lds_bar();
+            put();
+            el = eln;
         }
         bar();
         if (dS0 != nullptr) save_state(dS0 + chain * SS);
@@ -361,15 +455,24 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
     const float *S0 = Sc + (static_cast<size_t>(chain) * nch + c) * SS;
     const float *DSE = dSe + (static_cast<size_t>(chain) * nch + c) * SS;
 
-    for (int i = tid; i < kC * DK; i += kNT) sW[(i / DK) * LK + i % DK] = R[F::OFF_W + i];
-    for (int i = tid; i < kC * kC; i += kNT) {
-        sP[(i / kC) * LC + i % kC] = R[F::OFF_P + i];
-        sT[(i / kC) * LC + i % kC] = R[F::OFF_T + i];
-    }
-    if (tid < 64) {
-        const float gg = tid < L ? load_f32(g + (row0 + tid) * Hv + hv) : 0.f;
-        sgam[tid] = wave_scan(gg, tid);
-        sbeta[tid] = tid < L ? load_f32(beta + (row0 + tid) * Hv + hv) : 0.f;
+    {
+        Tile4<kC, DK> tw;
+        Tile4<kC, kC> tp, tt;
+        tw.load(R + F::OFF_W, DK);
+        tp.load(R + F::OFF_P, kC);
+        tt.load(R + F::OFF_T, kC);
+        float gg = 0.f, bb = 0.f;
+        if (tid < 64 && tid < L) {
+            gg = load_f32(g + (row0 + tid) * Hv + hv);
+            bb = load_f32(beta + (row0 + tid) * Hv + hv);
+        }
+        tw.store(sW, LK);
+        tp.store(sP, LC);
+        tt.store(sT, LC);
+        if (tid < 64) {
+            sgam[tid] = wave_scan(gg, tid);
+            sbeta[tid] = bb;
+        }
     }
 
     // accumulators over the value slices
@@ -382,16 +485,17 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
     for (int j = 0; j < NSL; ++j) {
         const int cj = SW * j;
         bar();  // the previous slice's buffers are free
-        for (int i = tid; i < DK * SW; i += kNT) {
-            const int r = i / SW, cc = i % SW;
-            sS0[r * LS + cc] = S0[r * DV + cj + cc];
-            sSe[r * LS + cc] = DSE[r * DV + cj + cc];
-        }
-        for (int i = tid; i < kC * SW; i += kNT) {
-            const int r = i / SW, cc = i % SW;
-            const bool in = r < L;
-            sO[r * LS + cc] = in ? scale * load_f32(dO + ((row0 + r) * Hv + hv) * DV + cj + cc) : 0.f;
-            sVv[r * LS + cc] = in ? load_f32(v + ((row0 + r) * Hv + hv) * DV + cj + cc) : 0.f;
+        {
+            Tile4<DK, SW> t0s, tes;
+            Tile4<kC, SW> tos, tvs;
+            t0s.load(S0 + cj, DV);
+            tes.load(DSE + cj, DV);
+            tos.load_in(dO, row0, Hv, hv, cj, DV, L, scale);
+            tvs.load_in(v, row0, Hv, hv, cj, DV, L);
+            t0s.store(sS0, LS);
+            tes.store(sSe, LS);
+            tos.store(sO, LS);
+            tvs.store(sVv, LS);
         }
         bar();
         // Delta = U - W S0 ; dDelta = P^T dO' + Kt dSe  (64 x 32 tiles)
@@ -442,8 +546,13 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
 
     // ---- phase 2: K, Q, and the terms through Tm, the decays and gamma
     float *sK = smem, *sQ = sK + kC * LK, *sX = sQ + kC * LK, *sY = sX + kC * LK;
-    load_rows<DK>(sK, LK, k, row0, Hk, hq, L);
-    load_rows<DK>(sQ, LK, q, row0, Hk, hq, L);
+    {
+        Tile4<kC, DK> tk, tq;
+        tk.load_in(k, row0, Hk, hq, 0, DK, L);
+        tq.load_in(q, row0, Hk, hq, 0, DK, L);
+        tk.store(sK, LK);
+        tq.store(sQ, LK);
+    }
 #pragma unroll
     for (int i = 0; i < TMK; ++i)
 #pragma unroll
@@ -616,8 +725,11 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
 
 }  // namespace
 
+// 16-byte aligned q, k, v and dO (their rows are read four elements at a time)
 bool backward_chunk_supports(const BackwardArgs &a) {
-    return (a.dk_ == 64 || a.dk_ == 128) && (a.dv_ == 64 || a.dv_ == 128) && a.T > 0;
+    auto al = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    return (a.dk_ == 64 || a.dk_ == 128) && (a.dv_ == 64 || a.dv_ == 128) && a.T > 0 &&
+           al(a.q) && al(a.k) && al(a.v) && al(a.dO);
 }
 
 size_t backward_chunk_workspace(int B, int T, int Hk, int Hv, int dk, int dv) {

@@ -46,35 +46,6 @@ __device__ __forceinline__ float vload1(const float *p) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, 0));
 }
 
-// Register-tile product: acc[i][j] += sum_k A(row_i, k) B(k, col_j), row_i = ty + i NY,
-// col_j = tx + j NX with (ty, tx) = (tid / NX, tid % NX) and NY = 256 / NX.  A(r, k) = A[r ar
-// + k ak], B(k, c) = B[k bk + c bc] (strides allow transposed operands).
-template <int TM, int TN, int NX>
-__device__ __forceinline__ void mm(float (&acc)[TM][TN], const float *A, int ar, int ak,
-                                   const float *B, int bk, int bc, int K) {
-    constexpr int NY = kNT / NX;
-    const int tid = threadIdx.x, ty = tid / NX, tx = tid % NX;
-    const float *a0 = A + ty * ar;
-    const float *b0 = B + tx * bc;
-#pragma unroll 4
-    for (int k = 0; k < K; ++k) {
-        float a[TM], b[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) a[i] = a0[i * NY * ar + k * ak];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) b[j] = b0[k * bk + j * NX * bc];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
-    }
-}
-template <int TM, int TN> __device__ __forceinline__ void zero(float (&a)[TM][TN]) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) a[i][j] = 0.f;
-}
 // sum over the NX consecutive lanes of a tile row
 template <int NX> __device__ __forceinline__ float row_sum(float x) {
 #pragma unroll
@@ -151,6 +122,14 @@ template <int ROWS, int COLS> struct Tile4 {
             v[i] = make_float4(m * x.x, m * x.y, m * x.z, m * x.w);
         }
     }
+    // to LDS rows of stride ld, a multiple of 4 (16-byte writes)
+    __device__ __forceinline__ void store4(float *dst, int ld) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int idx = (i * kNT + threadIdx.x) * 4, r = idx / COLS, c = idx - r * COLS;
+            *reinterpret_cast<float4 *>(dst + r * ld + c) = v[i];
+        }
+    }
     __device__ __forceinline__ void store(float *dst, int ld) const {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
@@ -170,21 +149,27 @@ template <int ROWS, int COLS> struct Tile4 {
 };
 
 // ---------------------------------------------------------------------------------------
+// bprep_kernel: one workgroup per (chain, chunk).  The products on the matrix cores (fp32),
+// wavefront w owning row block w; Tm by forward substitution, one column per thread.
 template <int DK, int DV, typename TI>
-__global__ void __launch_bounds__(kNT)
+// one workgroup per compute unit (LDS), so every wavefront may use the whole register file
+__global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bprep_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__restrict__ v,
              const TI *__restrict__ beta, const TI *__restrict__ g, float *__restrict__ rec,
              int T, int Hk, int Hv, int nch) {
     using F = CB<DK, DV>;
-    constexpr int LK = F::LK, LV = F::LV, LC = F::LC;
-    __shared__ float sK[kC * LK], sQ[kC * LK], sV[kC * LV], sA[kC * LC], sT[kC * LC];
-    __shared__ float sgam[kC], sbeta[kC];
+    constexpr int LK4 = DK + 4, LV16 = DV + 16, LC4 = kC + 4, LC1 = kC + 1;
+    __shared__ __attribute__((aligned(16))) float sK[kC * LK4], sQ[kC * LK4], sV[kC * LV16],
+        sT[kC * LC4];
+    __shared__ float sA[kC * LC1], sgam[kC], sbeta[kC], sX[4][16 * 17];
     const int chain = blockIdx.x / nch, c = blockIdx.x - chain * nch;
     const int b = chain / Hv, hv = chain - b * Hv, hq = hv / (Hv / Hk);
     const int t0 = c * kC, L = min(kC, T - t0);
     const size_t row0 = static_cast<size_t>(b) * T + t0;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, mi = lane & 15, kq = lane >> 4;
+    const int rb = 16 * w + 4 * kq;
     float *R = rec + (static_cast<size_t>(chain) * nch + c) * F::REC;
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
 
     {
         Tile4<kC, DK> tk, tq;
@@ -197,9 +182,9 @@ bprep_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
             gg = load_f32(g + (row0 + tid) * Hv + hv);
             bb = load_f32(beta + (row0 + tid) * Hv + hv);
         }
-        tk.store(sK, LK);
-        tq.store(sQ, LK);
-        tv.store(sV, LV);
+        tk.store(sK, LK4);
+        tq.store(sQ, LK4);
+        tv.store(sV, LV16);
         if (tid < 64) {
             sgam[tid] = wave_scan(gg, tid);
             sbeta[tid] = bb;
@@ -207,75 +192,79 @@ bprep_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
     }
     bar();
     const float glast = sgam[kC - 1];
-    // K K^T and Q K^T (64 x 64 tiles), A and P
-    {
-        float kk[4][4], qk[4][4];
-        zero(kk);
-        zero(qk);
-        mm<4, 4, 16>(kk, sK, LK, 1, sK, 1, LK, DK);
-        mm<4, 4, 16>(qk, sQ, LK, 1, sK, 1, LK, DK);
-        const int ty = tid / 16, tx = tid % 16;
+    // K K^T and Q K^T (row block w), then A (strictly lower) and P (lower) with the decays
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+    for (int bj = 0; bj < 4; ++bj) {
+        const f32x4 kk = mfma_blk(z4, sK + 16 * w * LK4, LK4, 1, sK + 16 * bj * LK4, 1, LK4, DK);
+        const f32x4 qk = mfma_blk(z4, sQ + 16 * w * LK4, LK4, 1, sK + 16 * bj * LK4, 1, LK4, DK);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = ty + 16 * i, s = tx + 16 * j;
-                const float d = s <= r ? __expf(sgam[r] - sgam[s]) : 0.f;
-                sA[r * LC + s] = s < r ? sbeta[r] * kk[i][j] * d : 0.f;
-                R[F::OFF_P + r * kC + s] = qk[i][j] * d;
-            }
+        for (int i = 0; i < 4; ++i) {
+            const int r = rb + i, s = 16 * bj + mi;
+            const float d = s <= r ? __expf(sgam[r] - sgam[s]) : 0.f;
+            sA[r * LC1 + s] = s < r ? sbeta[r] * kk[i] * d : 0.f;
+            R[F::OFF_P + r * kC + s] = qk[i] * d;
+        }
     }
     bar();
-    // Tm = (I + A)^-1 by forward substitution, one column per thread (rows in order)
+    // Tm = (I + A)^-1 (A strictly lower) by 16 x 16 blocks: the four diagonal blocks by forward
+    // substitution, one column per thread; then block rows 1..3 in order on the matrix cores,
+    // T_ij = -T_ii sum_{j <= k < i} A_ik T_kj, wavefront w forming block column w.
+    for (int i = tid; i < kC * LC4; i += kNT) sT[i] = 0.f;
+    bar();
     if (tid < kC) {
-        const int j = tid;
-        for (int r = 0; r < kC; ++r) {
+        const int o = 16 * (tid >> 4), j = tid & 15;
+        for (int r = j; r < 16; ++r) {
             float x = r == j ? 1.f : 0.f;
-            for (int s = j; s < r; ++s) x -= sA[r * LC + s] * sT[s * LC + j];
-            sT[r * LC + j] = r >= j ? x : 0.f;
+            for (int s = j; s < r; ++s) x -= sA[(o + r) * LC1 + o + s] * sT[(o + s) * LC4 + o + j];
+            sT[(o + r) * LC4 + o + j] = x;
         }
+    }
+    bar();
+    for (int bi = 1; bi < 4; ++bi) {
+        if (w < bi) {
+            f32x4 x = z4;
+            for (int bk = w; bk < bi; ++bk)
+                x = mfma_blk(x, sA + 16 * bi * LC1 + 16 * bk, LC1, 1, sT + 16 * bk * LC4 + 16 * w,
+                             LC4, 1, 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sX[w][(4 * kq + i) * 17 + mi] = x[i];
+            // the same wavefront reads its block back: LDS operations of a wavefront are in order
+            const f32x4 t = mfma_blk(z4, sT + 16 * bi * LC4 + 16 * bi, LC4, 1, sX[w], 17, 1, 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sT[(16 * bi + 4 * kq + i) * LC4 + 16 * w + mi] = -t[i];
+        }
+        bar();
     }
     // Gm Q and Kt to the records; then sQ <- beta Gm K (W's right factor), sV <- beta V
     for (int i = tid; i < kC * DK; i += kNT) {
         const int r = i / DK, cc = i - r * DK;
-        R[F::OFF_GQ + i] = __expf(sgam[r]) * sQ[r * LK + cc];
-        R[F::OFF_KT + i] = __expf(glast - sgam[r]) * sK[r * LK + cc];
+        R[F::OFF_GQ + i] = __expf(sgam[r]) * sQ[r * LK4 + cc];
+        R[F::OFF_KT + i] = __expf(glast - sgam[r]) * sK[r * LK4 + cc];
     }
     bar();
     for (int i = tid; i < kC * DK; i += kNT) {
         const int r = i / DK, cc = i - r * DK;
-        sQ[r * LK + cc] = sbeta[r] * __expf(sgam[r]) * sK[r * LK + cc];
+        sQ[r * LK4 + cc] = sbeta[r] * __expf(sgam[r]) * sK[r * LK4 + cc];
     }
     for (int i = tid; i < kC * DV; i += kNT) {
         const int r = i / DV, cc = i - r * DV;
-        sV[r * LV + cc] *= sbeta[r];
+        sV[r * LV16 + cc] *= sbeta[r];
     }
     bar();
-    // U = Tm (beta V), W = Tm (beta Gm K)
-    {
-        constexpr int NXV = DV / 4, TMV = kC / (kNT / NXV);
-        float u[TMV][4];
-        zero(u);
-        mm<TMV, 4, NXV>(u, sT, LC, 1, sV, LV, 1, kC);
-        const int ty = tid / NXV, tx = tid % NXV;
+    // U = Tm (beta V), W = Tm (beta Gm K)  (row block w)
 #pragma unroll
-        for (int i = 0; i < TMV; ++i)
+    for (int bj = 0; bj < DV / 16; ++bj) {
+        const f32x4 u = mfma_blk(z4, sT + 16 * w * LC4, LC4, 1, sV + 16 * bj, LV16, 1, kC);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                R[F::OFF_U + (ty + i * (kNT / NXV)) * DV + tx + j * NXV] = u[i][j];
+        for (int i = 0; i < 4; ++i) R[F::OFF_U + (rb + i) * DV + 16 * bj + mi] = u[i];
     }
-    {
-        float w[F::TMK][4];
-        zero(w);
-        mm<F::TMK, 4, F::NXK>(w, sT, LC, 1, sQ, LK, 1, kC);
-        const int ty = tid / F::NXK, tx = tid % F::NXK;
 #pragma unroll
-        for (int i = 0; i < F::TMK; ++i)
+    for (int bj = 0; bj < DK / 16; ++bj) {
+        const f32x4 x = mfma_blk(z4, sT + 16 * w * LC4, LC4, 1, sQ + 16 * bj, LK4, 1, kC);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                R[F::OFF_W + (ty + i * (kNT / F::NXK)) * DK + tx + j * F::NXK] = w[i][j];
+        for (int i = 0; i < 4; ++i) R[F::OFF_W + (rb + i) * DK + 16 * bj + mi] = x[i];
     }
-    for (int i = tid; i < kC * kC; i += kNT) R[F::OFF_T + i] = sT[(i / kC) * LC + (i % kC)];
+    for (int i = tid; i < kC * kC; i += kNT) R[F::OFF_T + i] = sT[(i / kC) * LC4 + (i % kC)];
     if (tid == 0) R[F::OFF_EL] = __expf(glast);
 }
 
@@ -286,7 +275,8 @@ bprep_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
 // are chosen per operand orientation so that a product's 64 lanes read 64 different banks
 // (stride = 4 mod 64 floats where a lane group walks rows, 16 mod 64 where it walks columns).
 template <int DK, int DV, typename TD>
-__global__ void __launch_bounds__(kNT)
+// one workgroup per compute unit (LDS), so every wavefront may use the whole register file
+__global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
              const float *__restrict__ s0, const float *__restrict__ dST,
              float *__restrict__ Sc, float *__restrict__ dSe, float *__restrict__ dS0, int T,
@@ -295,8 +285,8 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
     constexpr int NSL = DV / 16;
     constexpr int L4 = DK + 4, L16 = DK + 16, LP = kC + 16;  // strides (see above)
     constexpr int NRB = DK / 16 / 4;                          // DK-row blocks per wavefront
-    __shared__ float sM1[kC * L16], sM2[kC * L16], sM3[kC * L16], sP[kC * LP];
-    __shared__ float sS[DK * 16], sD[kC * 16], sO[kC * 16];
+    __shared__ __attribute__((aligned(16))) float sM1[kC * L16], sM2[kC * L16], sM3[kC * L16],
+        sP[kC * LP], sS[DK * 16], sD[kC * 16], sO[kC * 16];
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, mi = lane & 15, kq = lane >> 4;
     const bool fwd = blockIdx.x < chains * NSL;
     const int idx = fwd ? blockIdx.x : blockIdx.x - chains * NSL;
@@ -423,8 +413,12 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
 }
 
 // ---------------------------------------------------------------------------------------
+// bgrad_kernel: one workgroup per (chain, chunk).  All products on the matrix cores (fp32):
+// wavefront w owns row block w (rows 16w..16w+15) of every 64 x 64 and 64 x DK product, so its
+// lane l holds rows 16w + 4 (l/16) + i, i < 4, of column 16 bj + l%16 of column block bj.
 template <int DK, int DV, typename TI, typename TD>
-__global__ void __launch_bounds__(kNT)
+// one workgroup per compute unit (LDS), so every wavefront may use the whole register file
+__global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__restrict__ v,
              const TI *__restrict__ beta, const TI *__restrict__ g, const TD *__restrict__ dO,
              const float *__restrict__ rec, const float *__restrict__ Sc,
@@ -433,28 +427,29 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
              float *__restrict__ dbeta, float *__restrict__ dg, int T, int Hk, int Hv, int nch,
              float scale) {
     using F = CB<DK, DV>;
-    constexpr int LK = F::LK, LC = F::LC, SW = 32, LS = SW + 1, NSL = DV / SW;
-    constexpr int NXK = F::NXK, TMK = F::TMK, NYK = kNT / NXK;
-    // phase 1: W, P, Tm + one value slice; phase 2 reuses the slice area and W for K, Q, ...
-    constexpr int PH1 = kC * LK + 2 * DK * LS + 4 * kC * LS;       // W + slice buffers
-    constexpr int PH2 = 3 * kC * LK + kC * LC;                     // K, Q, X + Y
-    constexpr int BIG = PH1 > PH2 ? PH1 : PH2;
-    __shared__ float smem[BIG + 2 * kC * LC];
-    __shared__ float sgam[kC], sbeta[kC], sv[8][kC];
-    float *sP = smem + BIG, *sT = sP + kC * LC;
-    float *sW = smem, *sS0 = sW + kC * LK, *sSe = sS0 + DK * LS, *sO = sSe + DK * LS;
+    constexpr int SW = 16, NSL = DV / SW, NBK = DK / 16;
+    constexpr int LK4 = DK + 4, LC16 = kC + 16, LC4 = kC + 4, LS = SW + 4;
+    constexpr int P1 = kC * LK4 + 2 * DK * LS + 4 * kC * LS;  // W + one value slice
+    constexpr int P2 = 3 * kC * LK4;                          // K, Q, dW / (dKK + dKK^T)
+    constexpr int BIG = P1 > P2 ? P1 : P2;
+    __shared__ __attribute__((aligned(16))) float smem[BIG + 2 * kC * LC16];
+    __shared__ float sgam[kC], sbeta[kC], sv[8][kC], scol[4][kC];
+    float *sPY = smem + BIG;       // P (phase 1), then a 64 x 64 scratch Y (phase 2)
+    float *sT = sPY + kC * LC16;   // Tm
+    float *sW = smem, *sS0 = sW + kC * LK4, *sSe = sS0 + DK * LS, *sO = sSe + DK * LS;
     float *sVv = sO + kC * LS, *sD = sVv + kC * LS, *sdD = sD + kC * LS;
 
     const int chain = blockIdx.x / nch, c = blockIdx.x - chain * nch;
     const int b = chain / Hv, hv = chain - b * Hv, hq = hv / (Hv / Hk);
     const int t0 = c * kC, L = min(kC, T - t0);
     const size_t row0 = static_cast<size_t>(b) * T + t0;
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, mi = lane & 15, kq = lane >> 4;
+    const int rb = 16 * w + 4 * kq;  // this lane's first row
     const float *R = rec + (static_cast<size_t>(chain) * nch + c) * F::REC;
     const size_t SS = static_cast<size_t>(DK) * DV;
     const float *S0 = Sc + (static_cast<size_t>(chain) * nch + c) * SS;
     const float *DSE = dSe + (static_cast<size_t>(chain) * nch + c) * SS;
-
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
     {
         Tile4<kC, DK> tw;
         Tile4<kC, kC> tp, tt;
@@ -466,21 +461,22 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
             gg = load_f32(g + (row0 + tid) * Hv + hv);
             bb = load_f32(beta + (row0 + tid) * Hv + hv);
         }
-        tw.store(sW, LK);
-        tp.store(sP, LC);
-        tt.store(sT, LC);
+        tw.store4(sW, LK4);
+        tp.store4(sPY, LC16);
+        tt.store4(sT, LC16);
         if (tid < 64) {
             sgam[tid] = wave_scan(gg, tid);
             sbeta[tid] = bb;
         }
     }
 
-    // accumulators over the value slices
-    float dGQ[TMK][4], dKt[TMK][4], dW[TMK][4], dP[4][4], dTv[4][4];
-    zero(dGQ); zero(dKt); zero(dW); zero(dP); zero(dTv);
+    // accumulators over the value slices (row block w)
+    f32x4 aGQ[NBK], aKt[NBK], aW[NBK], aP[4], aTv[4];
+#pragma unroll
+    for (int j = 0; j < NBK; ++j) aGQ[j] = aKt[j] = aW[j] = z4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) aP[j] = aTv[j] = z4;
     float dglast = 0.f, dbv[4] = {0.f, 0.f, 0.f, 0.f};
-    const int ty16 = tid / 16, tx16 = tid % 16;            // 64 x 64 and 64 x 32 tiles
-    const int tyk = tid / NXK, txk = tid % NXK;            // 64 x DK tiles
 
     for (int j = 0; j < NSL; ++j) {
         const int cj = SW * j;
@@ -492,223 +488,209 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
             tes.load(DSE + cj, DV);
             tos.load_in(dO, row0, Hv, hv, cj, DV, L, scale);
             tvs.load_in(v, row0, Hv, hv, cj, DV, L);
-            t0s.store(sS0, LS);
-            tes.store(sSe, LS);
-            tos.store(sO, LS);
-            tvs.store(sVv, LS);
+            t0s.store4(sS0, LS);
+            tes.store4(sSe, LS);
+            tos.store4(sO, LS);
+            tvs.store4(sVv, LS);
         }
         bar();
-        // Delta = U - W S0 ; dDelta = P^T dO' + Kt dSe  (64 x 32 tiles)
+        // Delta = U - W S0 ; dDelta = P^T dO' + Kt dSe   (row block w, 16 columns)
         {
-            float d[4][2], e[4][2];
-            zero(d);
-            zero(e);
-            mm<4, 2, 16>(d, sW, LK, 1, sS0, LS, 1, DK);
-            mm<4, 2, 16>(e, sP, 1, LC, sO, LS, 1, kC);
-            mm<4, 2, 16>(e, R + F::OFF_KT, DK, 1, sSe, LS, 1, DK);
+            const f32x4 d = mfma_blk(z4, sW + 16 * w * LK4, LK4, 1, sS0, LS, 1, DK);
+            f32x4 e = mfma_blk(z4, sPY + 16 * w, 1, LC16, sO, LS, 1, kC);
+            e = mfma_blk(e, R + F::OFF_KT + 16 * w * DK, DK, 1, sSe, LS, 1, DK);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    const int r = ty16 + 16 * i, cc = tx16 + 16 * jj;
-                    sD[r * LS + cc] = R[F::OFF_U + r * DV + cj + cc] - d[i][jj];
-                    sdD[r * LS + cc] = e[i][jj];
-                }
+            for (int i = 0; i < 4; ++i) {
+                const int r = rb + i;
+                sD[r * LS + mi] = R[F::OFF_U + r * DV + cj + mi] - d[i];
+                sdD[r * LS + mi] = e[i];
+            }
         }
-        for (int i = tid; i < DK * SW; i += kNT) dglast += sS0[(i / SW) * LS + i % SW] * sSe[(i / SW) * LS + i % SW];
+        for (int i = tid; i < DK * SW; i += kNT)
+            dglast += sS0[(i / SW) * LS + i % SW] * sSe[(i / SW) * LS + i % SW];
         bar();
         // dBv = Tm^T dDelta -> dv = beta dBv, dbeta += rowsum(dBv o V)
         {
-            float x[4][2];
-            zero(x);
-            mm<4, 2, 16>(x, sT, 1, LC, sdD, LS, 1, kC);
+            const f32x4 x = mfma_blk(z4, sT + 16 * w, 1, LC16, sdD, LS, 1, kC);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = ty16 + 16 * i;
-                float rs = 0.f;
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    const int cc = tx16 + 16 * jj;
-                    rs += x[i][jj] * sVv[r * LS + cc];
-                    if (r < L) dv_out[((row0 + r) * Hv + hv) * DV + cj + cc] = sbeta[r] * x[i][jj];
-                }
-                dbv[i] += row_sum<16>(rs);
+                const int r = rb + i;
+                if (r < L) dv_out[((row0 + r) * Hv + hv) * DV + cj + mi] = sbeta[r] * x[i];
+                dbv[i] += row_sum<16>(x[i] * sVv[r * LS + mi]);
             }
         }
-        // the partial sums over this slice's value columns
-        mm<TMK, 4, NXK>(dGQ, sO, LS, 1, sS0, 1, LS, SW);    // dO' S0^T
-        mm<TMK, 4, NXK>(dKt, sD, LS, 1, sSe, 1, LS, SW);    // Delta dSe^T
-        mm<TMK, 4, NXK>(dW, sdD, LS, 1, sS0, 1, LS, SW);    // dDelta S0^T   (dW = minus this)
-        mm<4, 4, 16>(dP, sO, LS, 1, sD, 1, LS, SW);         // dO' Delta^T
-        mm<4, 4, 16>(dTv, sdD, LS, 1, sVv, 1, LS, SW);      // dDelta V^T    (times beta_col)
+        // the partial sums over this slice's value columns (K = 16)
+#pragma unroll
+        for (int bj = 0; bj < NBK; ++bj) {
+            aGQ[bj] = mfma_blk(aGQ[bj], sO + 16 * w * LS, LS, 1, sS0 + 16 * bj * LS, 1, LS, SW);
+            aKt[bj] = mfma_blk(aKt[bj], sD + 16 * w * LS, LS, 1, sSe + 16 * bj * LS, 1, LS, SW);
+            aW[bj] = mfma_blk(aW[bj], sdD + 16 * w * LS, LS, 1, sS0 + 16 * bj * LS, 1, LS, SW);
+        }
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) {
+            aP[bj] = mfma_blk(aP[bj], sO + 16 * w * LS, LS, 1, sD + 16 * bj * LS, 1, LS, SW);
+            aTv[bj] = mfma_blk(aTv[bj], sdD + 16 * w * LS, LS, 1, sVv + 16 * bj * LS, 1, LS, SW);
+        }
     }
     bar();
 
     // ---- phase 2: K, Q, and the terms through Tm, the decays and gamma
-    float *sK = smem, *sQ = sK + kC * LK, *sX = sQ + kC * LK, *sY = sX + kC * LK;
+    float *sK = smem, *sQ = sK + kC * LK4, *sX = sQ + kC * LK4, *sY = sPY;
     {
         Tile4<kC, DK> tk, tq;
         tk.load_in(k, row0, Hk, hq, 0, DK, L);
         tq.load_in(q, row0, Hk, hq, 0, DK, L);
-        tk.store(sK, LK);
-        tq.store(sQ, LK);
+        tk.store4(sK, LK4);
+        tq.store4(sQ, LK4);
     }
 #pragma unroll
-    for (int i = 0; i < TMK; ++i)
+    for (int bj = 0; bj < NBK; ++bj)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) sX[(tyk + NYK * i) * LK + txk + NXK * jj] = -dW[i][jj];
+        for (int i = 0; i < 4; ++i) sX[(rb + i) * LK4 + 16 * bj + mi] = -aW[bj][i];  // dW
     bar();
     const float glast = sgam[kC - 1];
-    auto Gm = [&](int r) { return __expf(sgam[r]); };
-    auto Dm = [&](int r, int s) { return s <= r ? __expf(sgam[r] - sgam[s]) : 0.f; };
-
-    float kk[4][4], qk[4][4], dT[4][4];
-    zero(kk); zero(qk); zero(dT);
-    mm<4, 4, 16>(kk, sK, LK, 1, sK, 1, LK, DK);
-    mm<4, 4, 16>(qk, sQ, LK, 1, sK, 1, LK, DK);
-    mm<4, 4, 16>(dT, sX, LK, 1, sK, 1, LK, DK);  // dW K^T  (times beta Gm of the column)
+    f32x4 aKK[4], aQK[4], aT[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int bj = 0; bj < 4; ++bj) {
+        aKK[bj] = mfma_blk(z4, sK + 16 * w * LK4, LK4, 1, sK + 16 * bj * LK4, 1, LK4, DK);
+        aQK[bj] = mfma_blk(z4, sQ + 16 * w * LK4, LK4, 1, sK + 16 * bj * LK4, 1, LK4, DK);
+        aT[bj] = mfma_blk(z4, sX + 16 * w * LK4, LK4, 1, sK + 16 * bj * LK4, 1, LK4, DK);  // dW K^T
+    }
+    f32x4 aBk[NBK];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int cc = tx16 + 16 * jj;
-            dT[i][jj] = sbeta[cc] * (dTv[i][jj] + Gm(cc) * dT[i][jj]);
+    for (int bj = 0; bj < NBK; ++bj)
+        aBk[bj] = mfma_blk(z4, sT + 16 * w, 1, LC16, sX + 16 * bj, LK4, 1, kC);  // Tm^T dW
+    // dTm = beta_col (dDelta V^T + Gm_col dW K^T) -> Y
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+        const int s = 16 * bj + mi;
+        const float bs = sbeta[s], gs = __expf(sgam[s]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sY[(rb + i) * LC16 + s] = bs * (aTv[bj][i] + gs * aT[bj][i]);
+    }
+    bar();
+    f32x4 aM[4];
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) aM[bj] = mfma_blk(z4, sT + 16 * w, 1, LC16, sY + 16 * bj, LC16, 1, kC);
+    bar();
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sY[(rb + i) * LC16 + 16 * bj + mi] = aM[bj][i];
+    bar();
+    f32x4 aA[4];
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) aA[bj] = mfma_blk(z4, sY + 16 * w * LC16, LC16, 1, sT + 16 * bj * LC16, 1, LC16, kC);
+    // per-element terms; row and column sums of the decay gradient E = dD o D
+    f32x4 aKKd[4], aQKd[4];
+    float rE[4] = {0.f, 0.f, 0.f, 0.f}, rA[4] = {0.f, 0.f, 0.f, 0.f}, cE[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = rb + i, s = 16 * bj + mi;
+            const float d = s <= r ? __expf(sgam[r] - sgam[s]) : 0.f;
+            const float a = s < r ? -aA[bj][i] : 0.f;  // dA (strictly lower)
+            const float p = s <= r ? aP[bj][i] : 0.f;  // dP (lower)
+            const float dGs = sbeta[r] * a;
+            rA[i] += a * aKK[bj][i] * d;
+            aKKd[bj][i] = dGs * d;
+            aQKd[bj][i] = p * d;
+            const float e = (dGs * aKK[bj][i] + p * aQK[bj][i]) * d;
+            rE[i] += e;
+            cE[bj] += e;
         }
-    float dBk[TMK][4];
-    zero(dBk);
-    mm<TMK, 4, NXK>(dBk, sT, 1, LC, sX, LK, 1, kC);  // Tm^T dW
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) sY[(ty16 + 16 * i) * LC + tx16 + 16 * jj] = dT[i][jj];
-    bar();
-    float m1[4][4];
-    zero(m1);
-    mm<4, 4, 16>(m1, sT, 1, LC, sY, LC, 1, kC);  // Tm^T dTm
-    bar();
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) sY[(ty16 + 16 * i) * LC + tx16 + 16 * jj] = m1[i][jj];
-    bar();
-    float dA[4][4];
-    zero(dA);
-    mm<4, 4, 16>(dA, sY, LC, 1, sT, 1, LC, kC);  // (Tm^T dTm) Tm^T
-    // per-element terms of the 64 x 64 tiles; the row and column sums of the decay gradient
-    float dKK[4][4], dQK[4][4], rE[4], rA[4], cE[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = ty16 + 16 * i;
-        rE[i] = 0.f;
-        rA[i] = 0.f;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int s = tx16 + 16 * jj;
-            const float d = Dm(r, s);
-            const float a = s < r ? -dA[i][jj] : 0.f;       // dA (strictly lower)
-            const float p = s <= r ? dP[i][jj] : 0.f;       // dP (lower)
-            const float dGs = sbeta[r] * a;
-            rA[i] += a * kk[i][jj] * d;                      // dbeta: dA o (K K^T o D)
-            dKK[i][jj] = dGs * d;
-            dQK[i][jj] = p * d;
-            const float e = (dGs * kk[i][jj] + p * qk[i][jj]) * d;
-            rE[i] += e;
-            cE[jj] += e;
-        }
         rE[i] = row_sum<16>(rE[i]);
         rA[i] = row_sum<16>(rA[i]);
     }
-    // column sums of E over the 16 row groups: through LDS (each (ty, col) slot written once)
-    bar();
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) sY[ty16 * LC + tx16 + 16 * jj] = cE[jj];
-    if (tx16 == 0)
+    for (int bj = 0; bj < 4; ++bj) {
+        cE[bj] += __shfl_xor(cE[bj], 16);
+        cE[bj] += __shfl_xor(cE[bj], 32);
+    }
+    bar();  // Y (M1) is no longer read
+    if (kq == 0)
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) scol[w][16 * bj + mi] = cE[bj];
+    if (mi == 0)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            sv[0][ty16 + 16 * i] = rE[i];
-            sv[1][ty16 + 16 * i] = rA[i];
-            sv[2][ty16 + 16 * i] = dbv[i];
+            sv[0][rb + i] = rE[i];
+            sv[1][rb + i] = rA[i];
+            sv[2][rb + i] = dbv[i];
         }
-    bar();
-    if (tid < kC) {
-        float s = 0.f;
-        for (int y = 0; y < 16; ++y) s += sY[y * LC + tid];
-        sv[3][tid] = s;
-    }
-    bar();
-    // dKK + dKK^T to sX (as 64 x 64), dQK to sY
+    // dKK -> Y, then (dKK + dKK^T) -> X (64 x 64, stride LC4; dW is no longer read)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) sY[(ty16 + 16 * i) * LC + tx16 + 16 * jj] = dKK[i][jj];
+        for (int i = 0; i < 4; ++i) sY[(rb + i) * LC16 + 16 * bj + mi] = aKKd[bj][i];
     bar();
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int r = ty16 + 16 * i, s = tx16 + 16 * jj;
-            sX[r * LC + s] = dKK[i][jj] + sY[s * LC + r];
+        for (int i = 0; i < 4; ++i) {
+            const int r = rb + i, s = 16 * bj + mi;
+            sX[r * LC4 + s] = aKKd[bj][i] + sY[s * LC16 + r];
         }
     bar();
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) sY[(ty16 + 16 * i) * LC + tx16 + 16 * jj] = dQK[i][jj];
+        for (int i = 0; i < 4; ++i) sY[(rb + i) * LC16 + 16 * bj + mi] = aQKd[bj][i];
     bar();
     // dK = (dKK + dKK^T) K + dQK^T Q + e^(glast - gamma) dKt + beta Gm dBk ; dQ = dQK K + Gm dGQ
-    float dK[TMK][4], dQ[TMK][4];
-    zero(dK);
-    zero(dQ);
-    mm<TMK, 4, NXK>(dK, sX, LC, 1, sK, LK, 1, kC);
-    mm<TMK, 4, NXK>(dK, sY, 1, LC, sQ, LK, 1, kC);
-    mm<TMK, 4, NXK>(dQ, sY, LC, 1, sK, LK, 1, kC);
     float *dqo = dq_part + (row0 * Hv + hv) * DK;  // [rows][Hv][DK] parts (G = 1: the output)
     float *dko = dk_part + (row0 * Hv + hv) * DK;
-    float rq[TMK], rk[TMK], rb[TMK];
+    float sq[4] = {0.f, 0.f, 0.f, 0.f}, sk[4] = {0.f, 0.f, 0.f, 0.f}, sb[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < TMK; ++i) {
-        const int r = tyk + NYK * i;
-        const float gm = Gm(r), ekt = __expf(glast - sgam[r]), bg = sbeta[r] * gm;
-        float sq = 0.f, sk = 0.f, sb = 0.f;
+    for (int bj = 0; bj < NBK; ++bj) {
+        f32x4 dk4 = mfma_blk(z4, sX + 16 * w * LC4, LC4, 1, sK + 16 * bj, LK4, 1, kC);
+        dk4 = mfma_blk(dk4, sY + 16 * w, 1, LC16, sQ + 16 * bj, LK4, 1, kC);
+        const f32x4 dq4 = mfma_blk(z4, sY + 16 * w * LC16, LC16, 1, sK + 16 * bj, LK4, 1, kC);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int cc = txk + NXK * jj;
-            const float kv = sK[r * LK + cc], qv = sQ[r * LK + cc];
-            const float dkv = dK[i][jj] + ekt * dKt[i][jj] + bg * dBk[i][jj];
-            const float dqv = dQ[i][jj] + gm * dGQ[i][jj];
-            sq += dGQ[i][jj] * qv;       // rowsum(dGQ o Q)
-            sk += dKt[i][jj] * kv;       // rowsum(dKt o K)
-            sb += dBk[i][jj] * kv;       // rowsum(dBk o K)
+        for (int i = 0; i < 4; ++i) {
+            const int r = rb + i, cc = 16 * bj + mi;
+            const float gm = __expf(sgam[r]), ekt = __expf(glast - sgam[r]);
+            const float kv = sK[r * LK4 + cc], qv = sQ[r * LK4 + cc];
+            const float dkv = dk4[i] + ekt * aKt[bj][i] + sbeta[r] * gm * aBk[bj][i];
+            const float dqv = dq4[i] + gm * aGQ[bj][i];
+            sq[i] += aGQ[bj][i] * qv;  // rowsum(dGQ o Q)
+            sk[i] += aKt[bj][i] * kv;  // rowsum(dKt o K)
+            sb[i] += aBk[bj][i] * kv;  // rowsum(dBk o K)
             if (r < L) {
                 dko[static_cast<size_t>(r) * Hv * DK + cc] = dkv;
                 dqo[static_cast<size_t>(r) * Hv * DK + cc] = dqv;
             }
         }
-        rq[i] = row_sum<NXK>(sq) * gm;
-        rk[i] = row_sum<NXK>(sk) * ekt;
-        rb[i] = row_sum<NXK>(sb) * gm;
     }
-    if (txk == 0)
 #pragma unroll
-        for (int i = 0; i < TMK; ++i) {
-            const int r = tyk + NYK * i;
-            sv[4][r] = rq[i];
-            sv[5][r] = rk[i];
-            sv[6][r] = rb[i];
+    for (int i = 0; i < 4; ++i) {
+        const int r = rb + i;
+        const float gm = __expf(sgam[r]), ekt = __expf(glast - sgam[r]);
+        const float a = row_sum<16>(sq[i]) * gm, bk = row_sum<16>(sk[i]) * ekt,
+                    cb = row_sum<16>(sb[i]) * gm;
+        if (mi == 0) {
+            sv[4][r] = a;
+            sv[5][r] = bk;
+            sv[6][r] = cb;
         }
+    }
     // <dSe, S0> summed over the workgroup
     float dl = dglast;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) dl += __shfl_xor(dl, off);
-    if (lane == 0) sv[7][tid >> 6] = dl;
+    if (lane == 0) sv[7][w] = dl;
     bar();
     if (tid < kC) {
         const int r = tid;
         float tsum = sv[5][r];
         for (int off = 1; off < 64; off <<= 1) tsum += __shfl_xor(tsum, off);
         const float dsx = sv[7][0] + sv[7][1] + sv[7][2] + sv[7][3];
+        const float colE = scol[0][r] + scol[1][r] + scol[2][r] + scol[3][r];
         const float bt = sbeta[r];
-        float dgam = sv[4][r] - sv[5][r] + bt * sv[6][r] + sv[0][r] - sv[3][r];
+        float dgam = sv[4][r] - sv[5][r] + bt * sv[6][r] + sv[0][r] - colE;
         if (r == kC - 1) dgam += __expf(glast) * dsx + tsum;
         const float db = sv[2][r] + sv[1][r] + sv[6][r];
         // dg = reverse cumulative sum of dgamma within the chunk

@@ -207,11 +207,12 @@ size_t gdn_chunk_fwd_varlen_workspace_size(int num_seqs, int T, int Hk, int Hv, 
  *   dbeta, dg      [B, T, Hv]       (dg: gradient w.r.t. g = log alpha)
  *   d_initial_state [B, Hv, dk, dv] or NULL to skip
  * Outputs must not overlap each other or any input.  The workspace (at least
- * gdn_backward_workspace_size(...) bytes, 256-byte aligned) holds a state checkpoint every
- * 64 tokens per chain, one block of recomputed states per chain and, when a chain is split
- * into slices of 16 state columns (dv > 16) or with grouped heads, the per-slice and
- * per-value-head parts of dq, dk, dbeta and dg.  Supported: dk, dv in {16, 32, 64, 128}; in_dtype and
- * dout_dtype GDN_F32 or GDN_BF16.  Deterministic (no atomics).  B = 0 is a no-op.
+ * gdn_backward_workspace_size(...) bytes, 256-byte aligned) holds the intermediate results:
+ * for dk, dv in {64, 128} with 16-byte-aligned q, k, v and d_o, the chunk-parallel path's
+ * per-chunk records, chunk-start states and chunk-end gradients; otherwise the token-recurrent
+ * path's state checkpoints every 64 tokens, one block of recomputed states per chain and the
+ * per-slice parts of dq, dk, dbeta and dg.  Supported: dk, dv in {16, 32, 64, 128}; in_dtype
+ * and dout_dtype GDN_F32 or GDN_BF16.  Deterministic (no atomics).  B = 0 is a no-op.
  */
 size_t gdn_backward_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv);
 gdn_status_t gdn_backward(const void *q, const void *k, const void *v, const void *beta,

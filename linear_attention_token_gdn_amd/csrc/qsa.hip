@@ -264,6 +264,7 @@ typedef Nv<4> NV4;
 
 constexpr int kHistWords = kTok * 256 + 64;  // 16 histograms of 256 bins, 64 dummy counters
 constexpr unsigned kOob = 0x7ffffff0u;       // a buffer offset past any range: store dropped
+constexpr int kCand = 64;                    // most keys a query may gather in the last sweep
 
 template <int D, bool IMP>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -274,7 +275,8 @@ select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
     constexpr int KD = D / 32;
     __shared__ unsigned s_hist[kHistWords];
     __shared__ unsigned s_lo[kTok], s_hi[kTok];
-    __shared__ int s_shift[kTok], s_krem[kTok], s_kt[kTok], s_act[kTok];
+    __shared__ int s_shift[kTok], s_krem[kTok], s_kt[kTok], s_act[kTok], s_coll[kTok],
+        s_ncand[kTok];
 
     const int lane = threadIdx.x, g = lane >> 4, c = lane & 15;
     const int ntt = (T + kTok - 1) / kTok;
@@ -427,6 +429,9 @@ select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
     //      kept (count == krem) or the range is one value (keep its first krem copies in index
     //      order).  In the end a block is kept if key >= hi, or lo <= key < hi among the first
     //      kt such blocks; a query with at most nsel eligible blocks keeps all (lo = hi = 0).
+    //      A query whose range holds at most kCand keys stops early ("gathers"): the last sweep
+    //      writes its blocks with key >= hi and collects the in-range (key, block) pairs in
+    //      LDS, and a merge afterwards ranks them and inserts the krem best in index order.
     //
     //      The first pass bins by 1/16 of a binade over the 16 binades below 4.004 / nsel: the
     //      importances of a query sum to 4 (four distributions), so the nsel-th largest cannot
@@ -441,6 +446,8 @@ select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
         s_kt[lane] = 0x7fffffff;
         s_krem[lane] = nsel;
         s_act[lane] = nelig(t0 + lane) > nsel;
+        s_coll[lane] = 0;
+        s_ncand[lane] = 0;
     }
     for (int pass = 0; pass < 5; ++pass) {
         __syncthreads();
@@ -545,6 +552,11 @@ select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
                 } else if (w == 1u || pass == 4) {
                     s_kt[tk] = left;        // one key value: its first `left` copies
                     s_act[tk] = 0;
+                } else if (cnt <= kCand) {
+                    s_coll[tk] = 1;         // few keys left in the range: gather and rank them
+                    s_ncand[tk] = cnt;
+                    s_kt[tk] = 0;
+                    s_act[tk] = 0;
                 }
             }
         }
@@ -554,6 +566,7 @@ select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
     // ---- last sweep: write the kept blocks in ascending order (and the importance)
     unsigned lo[4], wd[4], hi[4];
     int kt[4], cnt[4], ties[4];
+    bool coll[4];
     int anytie = 0;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
@@ -562,9 +575,13 @@ select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
         hi[a] = s_hi[tk];
         wd[a] = hi[a] - lo[a];
         kt[a] = s_kt[tk];
+        coll[a] = s_coll[tk] != 0;
         cnt[a] = 0;
         ties[a] = 0;
     }
+    // gathered pairs of query tl: keys at s_hist[tl * kCand + i], blocks kTok * kCand further
+    unsigned *const s_ck = s_hist;
+    int *const s_cj = reinterpret_cast<int *>(s_hist + kTok * kCand);
 #pragma unroll
     for (int tk = 0; tk < kTok; ++tk) anytie |= s_kt[tk] != 0x7fffffff;
     const int rows = min(kTok, T - t0);
@@ -588,7 +605,12 @@ select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
             if (TIES) {
                 const bool inr = el && key - lo[a] < wd[a];
                 meq = __ballot(inr);
-                take = take || (inr && ties[a] + group_below(meq, g, c) < kt[a]);
+                const int tpos = ties[a] + group_below(meq, g, c);
+                take = take || (inr && tpos < kt[a]);
+                if (coll[a] && inr) {  // at most kCand in-range keys: tpos < kCand
+                    s_ck[(4 * a + g) * kCand + tpos] = key;
+                    s_cj[(4 * a + g) * kCand + tpos] = j;
+                }
             } else {
                 take = take || (el && key - lo[a] < wd[a]);
             }
@@ -616,9 +638,51 @@ select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
         const int t = t0 + 4 * a + g;
         if (t >= T) continue;
         const size_t rowo = static_cast<size_t>(b) * T + t;
-        for (int p = cnt[a] + c; p < nsel; p += 16) sel[rowo * nsel + p] = -1;
+        if (!coll[a])  // a gathering query fills all nsel slots in the merge
+            for (int p = cnt[a] + c; p < nsel; p += 16) sel[rowo * nsel + p] = -1;
         if (IMP)
             for (int j = 16 * ntj + c; j < nb; j += 16) imp[rowo * nb + j] = 0.f;
+    }
+
+    // ---- merge of the gathering queries, one row per step with the whole wavefront: the
+    //      row holds its nd = nsel - krem blocks with key >= hi in ascending order; of its nc
+    //      gathered pairs (ascending block order) the krem of smallest rank (larger key first,
+    //      then lower block) are chosen, and the two sorted lists are interleaved in place.
+    //      The kept blocks only move right, so they go in 64-entry chunks from the end of the
+    //      row (no chunk lands on one still unread), and the chosen pairs are stored last.
+    __syncthreads();
+    __threadfence_block();  // the row's own stores above are visible to every lane
+    for (int tl = 0; tl < kTok; ++tl) {
+        if (!s_coll[tl]) continue;  // only set for rows t0 + tl < T with > nsel eligible blocks
+        int32_t *const row = sel + (static_cast<size_t>(b) * T + t0 + tl) * nsel;
+        const int left = s_krem[tl], nd = nsel - left, nc = s_ncand[tl];
+        const unsigned *ck = s_ck + tl * kCand;
+        const int *cj = s_cj + tl * kCand;
+        const unsigned myk = lane < nc ? ck[lane] : 0u;
+        int rank = 0;
+        for (int m = 0; m < nc; ++m) {
+            const unsigned km = ck[m];
+            rank += km > myk || (km == myk && m < lane);
+        }
+        const unsigned long long chosen = __ballot(lane < nc && rank < left);
+        int below = 0;  // for a chosen lane: kept blocks with a lower index than its own
+        for (int p0 = (nd - 1) & ~63; p0 >= 0; p0 -= 64) {
+            const int p = p0 + lane;
+            const int jd = p < nd ? row[p] : 0x7fffffff;
+            int add = 0;  // chosen blocks below jd
+            for (unsigned long long mk = chosen; mk != 0ull; mk &= mk - 1ull) {
+                const int m = __ffsll(static_cast<long long>(mk)) - 1;
+                const int jc = cj[m];
+                add += jc < jd;
+                const int n = __popcll(__ballot(jd < jc));
+                below += lane == m ? n : 0;
+            }
+            if (p < nd) row[p + add] = jd;
+        }
+        if ((chosen >> lane) & 1ull) {
+            const int before = __popcll(chosen & ((1ull << lane) - 1ull));
+            row[before + below] = cj[lane];
+        }
     }
 }
 

@@ -133,6 +133,12 @@ def test_qsa_shapes(r, nsel, rope_dims):
                   seed=810 + r + nsel)
 
 
+def test_qsa_large_budget():
+    """More kept blocks than one wavefront holds eleven times over (nsel = 700 of up to 1500):
+    rows that finish by ranking a few gathered keys merge them into long kept lists."""
+    run_and_check(B=1, T=1500, d=64, dtype="bf16", r=1, nsel=700, rope_dims=64, seed=815)
+
+
 @pytest.mark.parametrize("T", [1, 3, 4, 15, 16, 17])
 def test_qsa_tiny_lengths(T):
     """Fewer tokens than a block or a query tile: the last token sees the short last block."""

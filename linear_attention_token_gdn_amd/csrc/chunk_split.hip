@@ -348,19 +348,25 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 
 // ---------------------------------------------------------------------------------------
 // scan_kernel: one workgroup per (chain, 16-column tile of the state), chunks in order.
-// Only the state's own dependency chain runs here:
+// NWV "state" wavefronts run only the state's own dependency chain:
 //     Delta = U - W S ,    S <- e^gamma_last S + (K^T dec) Delta
-// and each chunk's starting state is written out (as the fp16 B-operand fragments the MFMAs
-// use) for out_kernel, which forms the outputs in parallel over all chunks.
+// and NR "output" wavefronts (one per 16-row block of a chunk) form the outputs of the chunk
+// the state wavefronts have just finished, from that chunk's starting state and Delta, which
+// the state wavefronts leave in LDS:
+//     O = scale ((e^gamma Q) S_c + P Delta)
+// The output wavefronts stay one chunk behind and keep step with the two workgroup barriers
+// of every chunk; their products run while the state wavefronts of the same SIMD sum partial
+// products (vector and LDS work), so the state chain hardly waits for them, and neither the
+// starting states nor Delta ever go through HBM.
 //
-// The workgroup's NWV = D/32 wavefronts split the state's rows: wavefront w keeps rows
-// 32w .. 32w+31 of the tile and needs only the matching slices of the chunk operands
-// (columns 32w.. of -W, rows 32w.. of K^T dec: 8 KiB per chunk at D = 128, C = 64), which
-// it streams straight into registers, several chunks ahead.  One wavefront alone streams at
-// most about 48 GB/s on MI355X and one compute unit about 145 GB/s, so splitting the
-// operand stream four ways is what shortens a chunk on the sequential path.  The partial
-// products W[:, 32w..] S[32w.., :] are summed through LDS (each wavefront finishes some row
-// blocks of Delta), and every wavefront then reads the whole of Delta back.
+// The state wavefronts split the state's rows: wavefront w keeps rows 32w .. 32w+31 of the
+// tile and needs only the matching slices of the chunk operands (columns 32w.. of -W, rows
+// 32w.. of K^T dec: 8 KiB per chunk at D = 128, C = 64), which it streams straight into
+// registers, several chunks ahead.  One wavefront alone streams at most about 48 GB/s on
+// MI355X and one compute unit about 145 GB/s, so splitting the operand stream four ways is
+// what shortens a chunk on the sequential path.  The partial products W[:, 32w..] S[32w.., :]
+// are summed through LDS (each wavefront finishes some row blocks of Delta), and every
+// wavefront then reads the whole of Delta back.
 
 // Workgroup barrier that waits only for this wave's LDS traffic (not for global memory).
 __device__ __forceinline__ void lds_barrier() {
@@ -381,40 +387,117 @@ __device__ __forceinline__ void chain_tile_map(int blk, int nblk, int ntile, int
 
 template <int D, int C> struct ScanCfg {
     using F = SplitCfg<D, C>;
-    static constexpr int NWV = F::KD;                      // wavefronts: 32 state rows each
+    static constexpr int NWV = F::KD;                      // state wavefronts: 32 rows each
+    static constexpr int NWO = F::NR;                      // output wavefronts: 16 rows each
     static constexpr int NRW = (F::NR + NWV - 1) / NWV;    // Delta row blocks finished per wave
-    static constexpr int LOADS = F::NR + 2 * F::KC + NRW + 1;  // global loads per chunk and wave
-    static constexpr int DEPTH = 6; // chunks in flight
-    static constexpr int SFR = F::KD;                      // 1 KiB blocks of one tile's start state
-    static constexpr size_t SREC = static_cast<size_t>(SFR) * 1024;
+    static constexpr int DEPTH = 4;                        // chunks of operands in flight
     static_assert(DEPTH >= 2, "scan pipeline depth");
 };
 
-template <int D, int C> struct ScanOps {  // one wave's operands of one chunk
+template <int D, int C> struct ScanOps {  // one state wave's operands of one chunk
     f16x8 wf[SplitCfg<D, C>::NR];          // -W, rows 16a.., k-step w
     f16x8 kf[2][SplitCfg<D, C>::KC];       // K^T dec, row blocks 2w, 2w+1
     f16x4 uf[ScanCfg<D, C>::NRW];          // U of this tile, the row blocks this wave finishes
     float gc;                              // e^gamma_last of the chunk
 };
 
-template <int D, int C>
-__global__ void __launch_bounds__((64 * ScanCfg<D, C>::NWV)) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int D, int C> struct OutOps {   // one output wave's operands of one chunk
+    f16x8 qf[SplitCfg<D, C>::KD];          // e^gamma Q, row block a
+    f16x8 pf[SplitCfg<D, C>::KC];          // P, row block a
+};
+
+template <int D, int C, typename TO>
+__global__ void __launch_bounds__(64 * (ScanCfg<D, C>::NWV + ScanCfg<D, C>::NWO))
 scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchunk,
-            unsigned char *__restrict__ sws, const float *__restrict__ s0,
-            float *__restrict__ sT, int nchunks) {
+            const float *__restrict__ s0, float *__restrict__ sT, TO *__restrict__ o,
+            int T, int Hv, int nchunks, float scale) {
     using F = SplitCfg<D, C>;
     using SC = ScanCfg<D, C>;
     constexpr int NR = F::NR, NI = F::NI, KD = F::KD, KC = F::KC;
     constexpr int NWV = SC::NWV, NRW = SC::NRW, DEPTH = SC::DEPTH;
     __shared__ f32x4 s_part[NWV][NR][64];  // partial Delta blocks, accumulator layout
     __shared__ f16x4 s_dlt[NR][64];         // Delta, fp16, accumulator layout
+    __shared__ f16x8 s_st[2][NWV][64];      // starting state of the chunk, B fragments (by parity)
     const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    __builtin_assume(w >= 0 && w < NWV);
+    __builtin_assume(w >= 0 && w < NWV + SC::NWO);
     int chain, jt;
     chain_tile_map(blockIdx.x, gridDim.x, NI, chain, jt);
     const int col = 16 * jt + li;
+    const unsigned char *rec0 = ws + static_cast<size_t>(chain) * nchunks * F::REC;
 
+    if (w >= NWV) {
+        // ---- output wavefront: row block a of every chunk, one chunk behind the state
+        const int a = w - NWV;
+        const int b = chain / Hv, hv = chain - b * Hv;
+        auto load = [&](OutOps<D, C> &op, int cc) {
+            const unsigned char *r = rec0 + static_cast<size_t>(cc) * F::REC;
+#pragma unroll
+            for (int kk = 0; kk < KD; ++kk)
+                op.qf[kk] = *reinterpret_cast<const f16x8 *>(r + F::OFF_Q + ((a * KD + kk) * 64 + lane) * 16);
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc)
+                op.pf[kc] = *reinterpret_cast<const f16x8 *>(r + F::OFF_P + ((a * KC + kc) * 64 + lane) * 16);
+        };
+        f16x8 bS[KD], bD[KC];  // chunk c - 1's starting state and Delta, read from LDS
+        auto emit = [&](const OutOps<D, C> &op, int c) {
+            f32x4 O = zero4();
+#pragma unroll
+            for (int kk = 0; kk < KD; ++kk) O = mma_f16_k32(op.qf[kk], bS[kk], O);
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc)
+                if (32 * kc <= 16 * a + 15) O = mma_f16_k32(op.pf[kc], bD[kc], O);
+            const int t0 = c * C, L = min(C, T - t0);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int r = 16 * a + 4 * lg + rr;
+                if (r < L)
+                    store_f32(o + ((static_cast<size_t>(b) * T + t0 + r) * Hv + hv) * D + col,
+                              scale * O[rr]);
+            }
+        };
+        // step c: barrier 1 of chunk c (its starting state is in LDS), then the outputs of
+        // chunk c - 1, barrier 2 (its Delta is in LDS), then both read into registers; they
+        // must be read before barrier 1 of chunk c + 1, after which Delta is overwritten
+        auto step = [&](const OutOps<D, C> &prev, int c) {
+            lds_barrier();
+            if (c > 0) emit(prev, c - 1);
+            lds_barrier();
+#pragma unroll
+            for (int kk = 0; kk < KD; ++kk) bS[kk] = s_st[c & 1][kk][lane];
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) bD[kc] = cat(s_dlt[2 * kc][lane], s_dlt[2 * kc + 1][lane]);
+        };
+        constexpr int RO = 3;  // ring of operand sets; slot (c mod RO) holds chunk c
+        OutOps<D, C> ring[RO];
+#pragma unroll
+        for (int s = 0; s < RO; ++s) load(ring[s], min(s, nchunks - 1));
+        // chunk c uses slot c mod RO in emit, one step later than its barriers
+        int c0 = 0;
+        for (; c0 + RO <= nchunks; c0 += RO) {
+#pragma unroll
+            for (int s = 0; s < RO; ++s) {
+                const int c = c0 + s;
+                step(ring[(s + RO - 1) % RO], c);            // emits chunk c - 1
+                if (c > 0) load(ring[(s + RO - 1) % RO], min(c - 1 + RO, nchunks - 1));
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < RO; ++s)
+            if (c0 + s < nchunks) {
+                const int c = c0 + s;
+                step(ring[(s + RO - 1) % RO], c);
+                if (c > 0) load(ring[(s + RO - 1) % RO], min(c - 1 + RO, nchunks - 1));
+            }
+        // the last chunk (constant ring indices only: a computed one would put the ring in
+        // scratch memory)
+#pragma unroll
+        for (int s = 0; s < RO; ++s)
+            if ((nchunks - 1) % RO == s) emit(ring[s], nchunks - 1);
+        return;
+    }
+
+    // ---- state wavefront w
     f32x4 S[2];  // rows 32w + 16i + 4lg + rr of column col
     const size_t sbase = static_cast<size_t>(chain) * D * D;
     if (s0 != nullptr) {  // one branch, so that all loads are in flight together
@@ -426,40 +509,36 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
     } else {
         S[0] = S[1] = zero4();
     }
-
-    const unsigned char *rec0 = ws + static_cast<size_t>(chain) * nchunks * F::REC;
-    unsigned char *srec0 = sws + (static_cast<size_t>(chain) * nchunks * NI + jt) * SC::SREC +
-                           w * 1024 + lane * 16;
     // this chain's per-chunk decays (raw buffer, 32-bit data format; reads past the end give 0)
     const __amdgpu_buffer_rsrc_t gsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float *>(gchunk + static_cast<size_t>(chain) * nchunks), 0, 4 * nchunks,
         0x00020000);
-    auto load = [&](ScanOps<D, C> &o, int cc) {
+    auto load = [&](ScanOps<D, C> &op, int cc) {
         const unsigned char *r = rec0 + static_cast<size_t>(cc) * F::REC;
 #pragma unroll
         for (int a = 0; a < NR; ++a)
-            o.wf[a] = *reinterpret_cast<const f16x8 *>(r + F::OFF_W + ((a * KD + w) * 64 + lane) * 16);
+            op.wf[a] = *reinterpret_cast<const f16x8 *>(r + F::OFF_W + ((a * KD + w) * 64 + lane) * 16);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc)
-                o.kf[i][kc] = *reinterpret_cast<const f16x8 *>(
+                op.kf[i][kc] = *reinterpret_cast<const f16x8 *>(
                     r + F::OFF_K + (((2 * w + i) * KC + kc) * 64 + lane) * 16);
 #pragma unroll
         for (int j = 0; j < NRW; ++j) {
             const int a = min(w + j * NWV, NR - 1);  // clamped: loaded but unused past NR
-            o.uf[j] = *reinterpret_cast<const f16x4 *>(r + F::OFF_U + ((jt * NR + a) * 64 + lane) * 8);
+            op.uf[j] = *reinterpret_cast<const f16x4 *>(r + F::OFF_U + ((jt * NR + a) * 64 + lane) * 8);
         }
         // through a buffer descriptor, so that it stays a vector-memory load: a scalar load
         // still in flight would hold up every LDS wait, which counts scalar loads too
-        o.gc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gsrc, 0, 4 * cc, 0));
+        op.gc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gsrc, 0, 4 * cc, 0));
     };
-    auto step = [&](const ScanOps<D, C> &o, int c) {
+    auto step = [&](const ScanOps<D, C> &op, int c) {
         const f16x8 bS = cat(h4(S[0]), h4(S[1]));  // k-step w of the B operand S
-        *reinterpret_cast<f16x8 *>(srec0 + static_cast<size_t>(c) * NI * SC::SREC) = bS;
+        s_st[c & 1][w][lane] = bS;                  // for the output wavefronts
         f32x4 pa[NR];
 #pragma unroll
-        for (int a = 0; a < NR; ++a) pa[a] = mma_f16_k32(o.wf[a], bS, zero4());
+        for (int a = 0; a < NR; ++a) pa[a] = mma_f16_k32(op.wf[a], bS, zero4());
 #pragma unroll
         for (int a = 0; a < NR; ++a) s_part[w][a][lane] = pa[a];
         // the independent products back to back, then their LDS writes
@@ -475,8 +554,8 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
                 for (int v = 0; v < NWV; ++v) p[v] = s_part[v][a][lane];
                 // issue all the partial reads before any of the adds that use them
                 __builtin_amdgcn_sched_group_barrier(0x100, NWV, 0);
-                f32x4 d = f32x4{float(o.uf[j][0]), float(o.uf[j][1]), float(o.uf[j][2]),
-                                float(o.uf[j][3])};
+                f32x4 d = f32x4{float(op.uf[j][0]), float(op.uf[j][1]), float(op.uf[j][2]),
+                                float(op.uf[j][3])};
 #pragma unroll
                 for (int v = 0; v < NWV; ++v) d += p[v];
                 s_dlt[a][lane] = h4(d);
@@ -488,9 +567,9 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
         for (int kc = 0; kc < KC; ++kc) bD[kc] = cat(s_dlt[2 * kc][lane], s_dlt[2 * kc + 1][lane]);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            S[i] *= o.gc;
+            S[i] *= op.gc;
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) S[i] = mma_f16_k32(o.kf[i][kc], bD[kc], S[i]);
+            for (int kc = 0; kc < KC; ++kc) S[i] = mma_f16_k32(op.kf[i][kc], bD[kc], S[i]);
         }
     };
 
@@ -520,91 +599,19 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
     }
 }
 
-// ---------------------------------------------------------------------------------------
-// out_kernel: one wavefront per (chain, chunk, 16-column tile), all independent:
-//     Delta = U - W S_c  (the same fp16 operands and order as the scan, so the same values)
-//     O     = scale ((e^gamma Q) S_c + P Delta)
-template <int D, int C, typename TO>
-__global__ void __launch_bounds__(64)
-out_kernel(const unsigned char *__restrict__ ws, const unsigned char *__restrict__ sws,
-           TO *__restrict__ o, int T, int Hv, int nchunks, float scale) {
-    using F = SplitCfg<D, C>;
-    using SC = ScanCfg<D, C>;
-    constexpr int NR = F::NR, NI = F::NI, KD = F::KD, KC = F::KC;
-    const int lane = threadIdx.x, li = lane & 15, lg = lane >> 4;
-    // blocks: consecutive blocks share (chain, chunk), so its record stays in one L2
-    int cc_idx, jt;
-    chain_tile_map(blockIdx.x, gridDim.x, NI, cc_idx, jt);
-    const int chain = cc_idx / nchunks, c = cc_idx - chain * nchunks;
-    const int b = chain / Hv, hv = chain - b * Hv;
-    const int col = 16 * jt + li;
-    const int t0 = c * C, L = min(C, T - t0);
-    const unsigned char *rec = ws + (static_cast<size_t>(chain) * nchunks + c) * F::REC;
-    const unsigned char *srec = sws + ((static_cast<size_t>(chain) * nchunks + c) * NI + jt) * SC::SREC;
-    auto frag = [&](size_t off, int idx) {
-        return *reinterpret_cast<const f16x8 *>(rec + off + (static_cast<size_t>(idx) * 64 + lane) * 16);
-    };
-    f16x8 bS[KD], wf[NR][KD], qf[NR][KD], pf[NR][KC];
-    f16x4 uf[NR];
-#pragma unroll
-    for (int kk = 0; kk < KD; ++kk)
-        bS[kk] = *reinterpret_cast<const f16x8 *>(srec + kk * 1024 + lane * 16);
-#pragma unroll
-    for (int a = 0; a < NR; ++a) {
-        uf[a] = *reinterpret_cast<const f16x4 *>(rec + F::OFF_U + ((jt * NR + a) * 64 + lane) * 8);
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk) {
-            wf[a][kk] = frag(F::OFF_W, a * KD + kk);
-            qf[a][kk] = frag(F::OFF_Q, a * KD + kk);
-        }
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) pf[a][kc] = frag(F::OFF_P, a * KC + kc);
-    }
-    f32x4 Dl[NR], O[NR];
-#pragma unroll
-    for (int a = 0; a < NR; ++a) {
-        Dl[a] = f32x4{float(uf[a][0]), float(uf[a][1]), float(uf[a][2]), float(uf[a][3])};
-        O[a] = zero4();
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk) {
-            Dl[a] = mma_f16_k32(wf[a][kk], bS[kk], Dl[a]);
-            O[a] = mma_f16_k32(qf[a][kk], bS[kk], O[a]);
-        }
-    }
-    f16x8 bD[KC];
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) bD[kc] = cat(h4(Dl[2 * kc]), h4(Dl[2 * kc + 1]));
-#pragma unroll
-    for (int a = 0; a < NR; ++a) {
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-            if (32 * kc <= 16 * a + 15) O[a] = mma_f16_k32(pf[a][kc], bD[kc], O[a]);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int r = 16 * a + 4 * lg + rr;
-            if (r < L)
-                store_f32(o + ((static_cast<size_t>(b) * T + t0 + r) * Hv + hv) * D + col,
-                          scale * O[a][rr]);
-        }
-    }
-}
-
 template <int D, int C> size_t split_ws_bytes(int B, int T, int Hv) {
     const size_t nch = static_cast<size_t>((T + C - 1) / C);
     const size_t chains = static_cast<size_t>(B) * Hv;
-    // operand records | per-chunk decays (padded to 256 B) | per-(chunk, tile) start states
-    const size_t gbytes = (chains * nch * sizeof(float) + 255) / 256 * 256;
-    return chains * nch * SplitCfg<D, C>::REC + gbytes +
-           chains * nch * (D / 16) * ScanCfg<D, C>::SREC;
+    // operand records | per-chunk decays
+    return chains * nch * SplitCfg<D, C>::REC + chains * nch * sizeof(float);
 }
 
 template <int D, int C, typename TO> hipError_t launch_split_typed(const PrefillArgs &a) {
+    using SC = ScanCfg<D, C>;
     const int nch = (a.T + C - 1) / C;
     const size_t chains = static_cast<size_t>(a.B) * a.Hv;
     unsigned char *ws = static_cast<unsigned char *>(a.ws);
     float *gch = reinterpret_cast<float *>(ws + chains * nch * SplitCfg<D, C>::REC);
-    unsigned char *sws = ws + chains * nch * SplitCfg<D, C>::REC +
-                         (chains * nch * sizeof(float) + 255) / 256 * 256;
     auto prep = (a.flags & GDN_QK_L2NORM) ? prep_kernel<D, C, true> : prep_kernel<D, C, false>;
     hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(chains * nch)), dim3(64), 0, a.stream,
                        static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
@@ -612,13 +619,9 @@ template <int D, int C, typename TO> hipError_t launch_split_typed(const Prefill
                        static_cast<const bf16_t *>(a.g), ws, gch, a.T, a.Hk, a.Hv, nch, a.flags);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_kernel<D, C>), dim3(static_cast<unsigned>(chains * (D / 16))),
-                       dim3(64 * ScanCfg<D, C>::NWV), 0, a.stream, ws, gch, sws, a.s0, a.sT, nch);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((out_kernel<D, C, TO>), dim3(static_cast<unsigned>(chains * nch * (D / 16))),
-                       dim3(64), 0, a.stream, ws, sws, static_cast<TO *>(a.o), a.T, a.Hv, nch,
-                       a.scale);
+    hipLaunchKernelGGL((scan_kernel<D, C, TO>), dim3(static_cast<unsigned>(chains * (D / 16))),
+                       dim3(64 * (SC::NWV + SC::NWO)), 0, a.stream, ws, gch, a.s0, a.sT,
+                       static_cast<TO *>(a.o), a.T, a.Hv, nch, a.scale);
     return hipGetLastError();
 }
 

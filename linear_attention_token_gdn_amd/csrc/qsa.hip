@@ -265,6 +265,7 @@ typedef Nv<4> NV4;
 constexpr int kHistWords = kTok * 256 + 64;  // 16 histograms of 256 bins, 64 dummy counters
 constexpr unsigned kOob = 0x7ffffff0u;       // a buffer offset past any range: store dropped
 constexpr int kCand = 64;                    // most keys a query may gather in the last sweep
+constexpr int kPer = 8;                      // kept blocks per lane the merge holds in registers
 
 template <int D, bool IMP>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -646,43 +647,64 @@ select_kernel(const f16 *__restrict__ q16, const float *__restrict__ qinv,
 
     // ---- merge of the gathering queries, one row per step with the whole wavefront: the
     //      row holds its nd = nsel - krem blocks with key >= hi in ascending order; of its nc
-    //      gathered pairs (ascending block order) the krem of smallest rank (larger key first,
-    //      then lower block) are chosen, and the two sorted lists are interleaved in place.
-    //      The kept blocks only move right, so they go in 64-entry chunks from the end of the
-    //      row (no chunk lands on one still unread), and the chosen pairs are stored last.
+    //      gathered pairs (ascending block order, lane i holds pair i) the krem of smallest
+    //      rank (larger key first, then lower block) are chosen, and the two sorted lists are
+    //      interleaved in place.  Up to 64 * kPer kept blocks are read into registers at once;
+    //      a longer row goes in 64-entry chunks from its end (the kept blocks only move right,
+    //      so no chunk lands on one still unread).  The chosen pairs are stored last.
     __syncthreads();
     __threadfence_block();  // the row's own stores above are visible to every lane
     for (int tl = 0; tl < kTok; ++tl) {
         if (!s_coll[tl]) continue;  // only set for rows t0 + tl < T with > nsel eligible blocks
         int32_t *const row = sel + (static_cast<size_t>(b) * T + t0 + tl) * nsel;
         const int left = s_krem[tl], nd = nsel - left, nc = s_ncand[tl];
-        const unsigned *ck = s_ck + tl * kCand;
-        const int *cj = s_cj + tl * kCand;
-        const unsigned myk = lane < nc ? ck[lane] : 0u;
+        const unsigned myk = lane < nc ? s_ck[tl * kCand + lane] : 0u;
+        const int myj = lane < nc ? s_cj[tl * kCand + lane] : 0;
         int rank = 0;
         for (int m = 0; m < nc; ++m) {
-            const unsigned km = ck[m];
+            const unsigned km = __builtin_amdgcn_readlane(myk, m);
             rank += km > myk || (km == myk && m < lane);
         }
         const unsigned long long chosen = __ballot(lane < nc && rank < left);
         int below = 0;  // for a chosen lane: kept blocks with a lower index than its own
-        for (int p0 = (nd - 1) & ~63; p0 >= 0; p0 -= 64) {
-            const int p = p0 + lane;
-            const int jd = p < nd ? row[p] : 0x7fffffff;
-            int add = 0;  // chosen blocks below jd
+        // one batch of kept blocks: add[s] = chosen blocks below jd[s]; below += kept blocks
+        // of the batch under each chosen block
+        auto count = [&](const int *jd, int *add, int n) {
             for (unsigned long long mk = chosen; mk != 0ull; mk &= mk - 1ull) {
                 const int m = __ffsll(static_cast<long long>(mk)) - 1;
-                const int jc = cj[m];
-                add += jc < jd;
-                const int n = __popcll(__ballot(jd < jc));
-                below += lane == m ? n : 0;
+                const int jc = __builtin_amdgcn_readlane(myj, m);
+                int lt = 0;
+                for (int s = 0; s < n; ++s) {
+                    add[s] += jc < jd[s];
+                    lt += __popcll(__ballot(jd[s] < jc));
+                }
+                below += lane == m ? lt : 0;
             }
-            if (p < nd) row[p + add] = jd;
+        };
+        if (nd <= 64 * kPer) {
+            int jd[kPer], add[kPer];
+#pragma unroll
+            for (int s = 0; s < kPer; ++s) {
+                const int p = lane + 64 * s;
+                jd[s] = p < nd ? row[p] : 0x7fffffff;
+                add[s] = 0;
+            }
+            count(jd, add, kPer);
+#pragma unroll
+            for (int s = 0; s < kPer; ++s) {
+                const int p = lane + 64 * s;
+                if (p < nd) row[p + add[s]] = jd[s];
+            }
+        } else {
+            for (int p0 = (nd - 1) & ~63; p0 >= 0; p0 -= 64) {
+                const int p = p0 + lane;
+                int jd[1] = {p < nd ? row[p] : 0x7fffffff}, add[1] = {0};
+                count(jd, add, 1);
+                if (p < nd) row[p + add[0]] = jd[0];
+            }
         }
-        if ((chosen >> lane) & 1ull) {
-            const int before = __popcll(chosen & ((1ull << lane) - 1ull));
-            row[before + below] = cj[lane];
-        }
+        if ((chosen >> lane) & 1ull)
+            row[__popcll(chosen & ((1ull << lane) - 1ull)) + below] = myj;
     }
 }
 

@@ -134,12 +134,48 @@ def _cpu_model():
     return "unknown"
 
 
+# ------------------------------------------------------------------ timing events
+class HipEvent:
+    """A HIP timing event recorded on a given stream, created with hipEventDisableSystemFence:
+    recording it issues no system-scope fence, so the cache writeback and invalidation such a
+    fence costs are not added to (or imposed on) the work being timed.  Same interface as
+    torch.cuda.Event for what this script uses: record(stream), elapsed_time(other) in ms."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        if HipEvent._hip is None:
+            HipEvent._hip = ctypes.CDLL("libamdhip64.so")
+        self._ct = ctypes
+        self._e = ctypes.c_void_p()
+        rc = HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(self._e),
+                                                   ctypes.c_uint(self.DISABLE_SYSTEM_FENCE))
+        if rc != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed (%d)" % rc)
+
+    def record(self, stream):
+        rc = HipEvent._hip.hipEventRecord(self._e, self._ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed (%d)" % rc)
+
+    def elapsed_time(self, other):
+        ms = self._ct.c_float()
+        rc = HipEvent._hip.hipEventElapsedTime(self._ct.byref(ms), self._e, other._e)
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed (%d)" % rc)
+        return ms.value
+
+    def __del__(self):
+        if HipEvent._hip is not None and self._e:
+            HipEvent._hip.hipEventDestroy(self._e)
+
+
 # ------------------------------------------------------------------ prologue / packed sequences
 def _time(torch, stream, fn, reps=10):
     fn()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
+    evs = [(HipEvent(), HipEvent()) for _ in range(reps)]
     for e0, e1 in evs:
         e0.record(stream)
         fn()
@@ -337,7 +373,7 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[HipEvent() for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s in range(args.steps):
@@ -354,13 +390,21 @@ def main():
 
     pre_ms = [e[0].elapsed_time(e[1]) for e in ev]
     pre_mean = sum(pre_ms) / len(pre_ms)
+    # the same call ten times back to back between one pair of events, with no decode traffic
+    # around it (reported beside the in-step figure, which follows 64 decode launches)
+    b2b = [HipEvent(), HipEvent()]
+    b2b[0].record(stream)
+    for _ in range(10):
+        prefill()
+    b2b[1].record(stream)
+    torch.cuda.synchronize()
+    b2b_ms = b2b[0].elapsed_time(b2b[1]) / 10
     flops = prefill_flops(B, T, Hk, Hv, dk, dv, C)
     pbytes = prefill_bytes(B, T, Hk, Hv, dk, dv, has_s0=pre_inp.s0 is not None)
     pre_tflops = flops / (pre_mean * 1e-3) / 1e12
     pre_gbs = pbytes / (pre_mean * 1e-3) / 1e9
     plan = gdn.gdn_chunk_fwd_plan(B, T, Hk, Hv, dk, dv, C, gdn.GDN_BF16)
-    pre_kernels = {"split": "prep_kernel<%d,%d,false> + scan_kernel<%d,%d> + out_kernel<%d,%d,float>"
-                            % (dk, C, dk, C, dk, C),
+    pre_kernels = {"split": "prep_kernel<%d,%d,false> + scan_kernel<%d,%d,float>" % (dk, C, dk, C),
                    "fused": "chunk_kernel<%d,%d,float>" % (dk, C)}.get(plan, plan)
     rooflines = {
         "prefill": {
@@ -410,8 +454,7 @@ def main():
             call = lambda: gdn.decode_tokens(mq, mk, mv, mb, mg, state, state_out=dst, o=mo)
             call()
             torch.cuda.synchronize()
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(5)]
+            evs = [(HipEvent(), HipEvent()) for _ in range(5)]
             for e0, e1 in evs:
                 e0.record(stream)
                 call()
@@ -449,7 +492,9 @@ def main():
         "prefill": {"tokens_per_s": round(B * T / (pre_mean * 1e-3), 1),
                     "ms": round(pre_mean, 4), "TFLOPs": round(pre_tflops, 2),
                     "frac_bf16_mfma_peak": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                    "GBps": round(pre_gbs, 1), "frac_hbm_peak": round(pre_gbs / HBM_PEAK_GBS, 4)},
+                    "GBps": round(pre_gbs, 1), "frac_hbm_peak": round(pre_gbs / HBM_PEAK_GBS, 4),
+                    "back_to_back_ms": round(b2b_ms, 4),
+                    "back_to_back_tokens_per_s": round(B * T / (b2b_ms * 1e-3), 1)},
         "decode": result_decode,
         "decode_tokens": multi,
         "prologue_and_packed": extras,

@@ -355,9 +355,7 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 // the state wavefronts leave in LDS:
 //     O = scale ((e^gamma Q) S_c + P Delta)
 // The output wavefronts stay one chunk behind and keep step with the two workgroup barriers
-// of every chunk; their products run while the state wavefronts of the same SIMD sum partial
-// products (vector and LDS work), so the state chain hardly waits for them, and neither the
-// starting states nor Delta ever go through HBM.
+// of every chunk, so neither the starting states nor Delta ever go through HBM.
 //
 // The state wavefronts split the state's rows: wavefront w keeps rows 32w .. 32w+31 of the
 // tile and needs only the matching slices of the chunk operands (columns 32w.. of -W, rows
@@ -456,17 +454,23 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
                               scale * O[rr]);
             }
         };
-        // step c: barrier 1 of chunk c (its starting state is in LDS), then the outputs of
-        // chunk c - 1, barrier 2 (its Delta is in LDS), then both read into registers; they
-        // must be read before barrier 1 of chunk c + 1, after which Delta is overwritten
+        // step c: barriers 1 (chunk c's starting state is in LDS) and 2 (its Delta is), then
+        // both are read into registers -- before barrier 1 of chunk c + 1, after which Delta
+        // is overwritten -- and chunk c - 1's outputs are formed meanwhile: in the state
+        // wavefronts' longest phase, not in the short one between the two barriers
         auto step = [&](const OutOps<D, C> &prev, int c) {
             lds_barrier();
-            if (c > 0) emit(prev, c - 1);
             lds_barrier();
+            f16x8 nS[KD], nD[KC];
 #pragma unroll
-            for (int kk = 0; kk < KD; ++kk) bS[kk] = s_st[c & 1][kk][lane];
+            for (int kk = 0; kk < KD; ++kk) nS[kk] = s_st[c & 1][kk][lane];
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) bD[kc] = cat(s_dlt[2 * kc][lane], s_dlt[2 * kc + 1][lane]);
+            for (int kc = 0; kc < KC; ++kc) nD[kc] = cat(s_dlt[2 * kc][lane], s_dlt[2 * kc + 1][lane]);
+            if (c > 0) emit(prev, c - 1);
+#pragma unroll
+            for (int kk = 0; kk < KD; ++kk) bS[kk] = nS[kk];
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) bD[kc] = nD[kc];
         };
         constexpr int RO = 3;  // ring of operand sets; slot (c mod RO) holds chunk c
         OutOps<D, C> ring[RO];

@@ -25,6 +25,8 @@
 // accumulator-layout tile takes that tile's registers as its A operand unchanged.
 #include "gdn_internal.h"
 
+#include <atomic>
+
 namespace gdn {
 namespace {
 
@@ -96,7 +98,11 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     __shared__ __attribute__((aligned(16))) f16 s_td[NR][16][20];     // their inverses (fp16)
 
     const int lane = threadIdx.x, li = lane & 15, lg = lane >> 4;
-    const int chain = blockIdx.x / nchunks, c = blockIdx.x - chain * nchunks;
+    // chunk-major grid: consecutive blocks are the chains of one chunk, so with a multiple of
+    // 8 chains a chain's records are all written from the XCD (block index mod 8) on which the
+    // scan kernel runs that chain
+    const int nchains = gridDim.x / nchunks;
+    const int c = blockIdx.x / nchains, chain = blockIdx.x - c * nchains;
     const int G = Hv / Hk;
     const int b = chain / Hv, hv = chain - b * Hv, hq = hv / G;
     const int t0 = c * C, L = min(C, T - t0);
@@ -389,8 +395,85 @@ template <int D, int C> struct ScanCfg {
     static constexpr int NWO = F::NR;                      // output wavefronts: 16 rows each
     static constexpr int NRW = (F::NR + NWV - 1) / NWV;    // Delta row blocks finished per wave
     static constexpr int DEPTH = 4;                        // chunks of operands in flight
+    static constexpr int NPF = 2;                          // prefetch workgroups per chain
+    static constexpr int PFD = 12;                         // chunks the prefetch runs ahead
     static_assert(DEPTH >= 2, "scan pipeline depth");
 };
+
+// Prefetch workgroups (launched with the scan, after its workgroups, on otherwise idle compute
+// units of the chain's XCD): they touch one dword of every 128-byte line of the records the
+// scan will read a few chunks later, so that the scan's own loads hit that XCD's L2 instead of
+// waiting on HBM.  A compute unit keeps only so many misses in flight, so at HBM latency one
+// scan workgroup streams far below its issue rate; the prefetch moves that latency to other
+// compute units.  Pacing: the scan publishes the chunk it is on, in a 256-byte line of its own
+// per chain (with the launch's epoch, so that stale values of an earlier call are ignored).
+// The prefetch workgroup takes chunks in groups of one per wavefront: wavefront 0 polls, with
+// a pause between polls, until the whole group is within PFD chunks of the scan, then every
+// wavefront loads its chunk's share of the lines and waits for it.  It is only a hint: the
+// scan never waits for it, and a prefetch workgroup gives up after a bounded number of polls.
+constexpr int kProgStride = 32;  // unsigned long longs per chain's progress word (256 B)
+
+template <int D, int C>
+__device__ void prefetch_records(const unsigned char *__restrict__ ws,
+                                 unsigned long long *__restrict__ prog, unsigned epoch,
+                                 int nchunks, int nchains, int p, int w, int nwaves, int lane,
+                                 int *s_done) {
+    using F = SplitCfg<D, C>;
+    using SC = ScanCfg<D, C>;
+    constexpr int LINES = static_cast<int>(F::REC / 128);
+    constexpr int PER = (LINES + SC::NPF - 1) / SC::NPF;  // lines per prefetch workgroup
+    constexpr int NLD = (PER + 63) / 64;                  // loads per wavefront and chunk
+    constexpr int kMaxPolls = 1 << 16;
+    int chain, part;
+    if (nchains % 8 == 0) {  // same XCD as the chain's scan workgroups (block index mod 8)
+        const int q = p >> 3;
+        chain = (p & 7) + 8 * (q / SC::NPF);
+        part = q % SC::NPF;
+    } else {
+        chain = p % nchains;
+        part = p / nchains;
+    }
+    const unsigned char *rec0 = ws + static_cast<size_t>(chain) * nchunks * F::REC;
+    unsigned long long *pw = prog + static_cast<size_t>(chain) * kProgStride;
+    unsigned acc = 0;
+    int polls = 0;
+    for (int n0 = 0; n0 < nchunks; n0 += nwaves) {
+        if (w == 0) {
+            int done = 0;
+            for (;;) {
+                const unsigned long long pv =
+                    __hip_atomic_load(pw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                done = static_cast<unsigned>(pv >> 32) == epoch ? static_cast<int>(pv & 0xffffffffu) : 0;
+                if (n0 + nwaves - 1 < done + SC::PFD) break;
+                if (++polls > kMaxPolls) {
+                    done = -1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(16);
+            }
+            if (lane == 0) *s_done = done;
+        }
+        __syncthreads();
+        const int done = *s_done;
+        if (done < 0) break;  // the same for every wavefront
+        const int n = n0 + w;
+        if (n < nchunks && n >= done) {
+            const unsigned char *r = rec0 + static_cast<size_t>(n) * F::REC;
+            unsigned v[NLD];
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                const int line = min(part * PER + 64 * i + lane, LINES - 1);
+                v[i] = *reinterpret_cast<const unsigned *>(r + static_cast<size_t>(line) * 128);
+            }
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) acc ^= v[i];
+        }
+        __syncthreads();  // every wavefront has read *s_done (and its loads are back)
+    }
+    asm volatile("" ::"v"(acc));
+}
+
+
 
 template <int D, int C> struct ScanOps {  // one state wave's operands of one chunk
     f16x8 wf[SplitCfg<D, C>::NR];          // -W, rows 16a.., k-step w
@@ -408,7 +491,8 @@ template <int D, int C, typename TO>
 __global__ void __launch_bounds__(64 * (ScanCfg<D, C>::NWV + ScanCfg<D, C>::NWO))
 scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchunk,
             const float *__restrict__ s0, float *__restrict__ sT, TO *__restrict__ o,
-            int T, int Hv, int nchunks, float scale) {
+            int T, int Hv, int nchunks, float scale, unsigned long long *__restrict__ prog,
+            unsigned epoch, int nscan) {
     using F = SplitCfg<D, C>;
     using SC = ScanCfg<D, C>;
     constexpr int NR = F::NR, NI = F::NI, KD = F::KD, KC = F::KC;
@@ -419,8 +503,13 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
     const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     __builtin_assume(w >= 0 && w < NWV + SC::NWO);
+    if (static_cast<int>(blockIdx.x) >= nscan) {
+        prefetch_records<D, C>(ws, prog, epoch, nchunks, nscan / NI, blockIdx.x - nscan, w,
+                               NWV + SC::NWO, lane, reinterpret_cast<int *>(&s_st[0][0][0]));
+        return;
+    }
     int chain, jt;
-    chain_tile_map(blockIdx.x, gridDim.x, NI, chain, jt);
+    chain_tile_map(blockIdx.x, nscan, NI, chain, jt);
     const int col = 16 * jt + li;
     const unsigned char *rec0 = ws + static_cast<size_t>(chain) * nchunks * F::REC;
 
@@ -458,9 +547,14 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
         // both are read into registers -- before barrier 1 of chunk c + 1, after which Delta
         // is overwritten -- and chunk c - 1's outputs are formed meanwhile: in the state
         // wavefronts' longest phase, not in the short one between the two barriers
+        const bool publish = prog != nullptr && a == 0 && jt == 0;
         auto step = [&](const OutOps<D, C> &prev, int c) {
             lds_barrier();
             lds_barrier();
+            if (publish && lane == 0)  // the state wavefronts are on chunk c
+                __hip_atomic_store(prog + static_cast<size_t>(chain) * kProgStride,
+                                   (static_cast<unsigned long long>(epoch) << 32) | c,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             f16x8 nS[KD], nD[KC];
 #pragma unroll
             for (int kk = 0; kk < KD; ++kk) nS[kk] = s_st[c & 1][kk][lane];
@@ -606,8 +700,9 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
 template <int D, int C> size_t split_ws_bytes(int B, int T, int Hv) {
     const size_t nch = static_cast<size_t>((T + C - 1) / C);
     const size_t chains = static_cast<size_t>(B) * Hv;
-    // operand records | per-chunk decays
-    return chains * nch * SplitCfg<D, C>::REC + chains * nch * sizeof(float);
+    // operand records | per-chunk decays | per-chain scan progress (256 B each, aligned)
+    return chains * nch * SplitCfg<D, C>::REC + (chains * nch * sizeof(float) + 255) / 256 * 256 +
+           chains * kProgStride * sizeof(unsigned long long);
 }
 
 template <int D, int C, typename TO> hipError_t launch_split_typed(const PrefillArgs &a) {
@@ -623,9 +718,18 @@ template <int D, int C, typename TO> hipError_t launch_split_typed(const Prefill
                        static_cast<const bf16_t *>(a.g), ws, gch, a.T, a.Hk, a.Hv, nch, a.flags);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_kernel<D, C, TO>), dim3(static_cast<unsigned>(chains * (D / 16))),
+    unsigned long long *prog = reinterpret_cast<unsigned long long *>(
+        ws + chains * nch * SplitCfg<D, C>::REC + (chains * nch * sizeof(float) + 255) / 256 * 256);
+    // prefetch workgroups only where the scan leaves compute units idle (one workgroup of
+    // either kind fills a compute unit's registers)
+    const size_t nscan = chains * (D / 16);
+    const size_t npf = chains * (D / 16 + SC::NPF) <= 256 ? chains * SC::NPF : 0;
+    static std::atomic<unsigned> launches{0};
+    const unsigned epoch = launches.fetch_add(1, std::memory_order_relaxed) + 1;
+    hipLaunchKernelGGL((scan_kernel<D, C, TO>), dim3(static_cast<unsigned>(nscan + npf)),
                        dim3(64 * (SC::NWV + SC::NWO)), 0, a.stream, ws, gch, a.s0, a.sT,
-                       static_cast<TO *>(a.o), a.T, a.Hv, nch, a.scale);
+                       static_cast<TO *>(a.o), a.T, a.Hv, nch, a.scale, npf ? prog : nullptr,
+                       epoch, static_cast<int>(nscan));
     return hipGetLastError();
 }
 

@@ -1,4 +1,4 @@
-// chunk_split.hip -- three-kernel chunk-parallel prefill for shapes with few (b, hv) chains.
+// chunk_split.hip -- two-kernel chunk-parallel prefill for shapes with few (b, hv) chains.
 //
 // Same exact rewriting of Eq. (1) of the explainer page "論文解説: Qwen3.8-Next の設計"
 // (ta-paperlens.web.app, section "GDNの中身") as chunk_mfma.hip:
@@ -11,10 +11,10 @@
 //
 // Everything that does not depend on the state S is computed by prep_kernel, fully in
 // parallel over (chunk, chain), one wavefront each; scan_kernel then walks the chunks of one
-// chain in order for one 16-column tile of the state.  This trades extra HBM traffic (the
-// per-chunk operands go through a workspace) for parallelism: a chain of T/C chunks no longer
-// waits for the per-chunk triangular solve, which is what bounds a single-pass kernel when
-// there are fewer chains than compute units.
+// chain in order for one 16-column tile of the state, and forms the outputs as it goes.
+// This trades extra HBM traffic (the per-chunk operands go through a workspace) for
+// parallelism: a chain of T/C chunks no longer waits for the per-chunk triangular solve,
+// which is what bounds a single-pass kernel when there are fewer chains than compute units.
 //
 // The workspace holds, per (chain, chunk), the scan kernel's MFMA operands already in
 // fragment order -- for every 16x16x32 A operand one 1 KiB block, lane-major, 16 bytes per

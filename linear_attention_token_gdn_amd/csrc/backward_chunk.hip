@@ -26,6 +26,8 @@
 // uses the full-size formulas.  No atomics: deterministic.
 #include "gdn_internal.h"
 
+#include <type_traits>
+
 namespace gdn {
 namespace {
 
@@ -67,6 +69,54 @@ __device__ __forceinline__ f32x4 mfma_blk(f32x4 acc, const float *A, int ar, int
     for (int k = 0; k < K; k += 4)
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[k * ak], b[k * bk], acc, 0, 0, 0);
     return acc;
+}
+
+typedef _Float16 f16x8h __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4h __attribute__((ext_vector_type(4)));
+
+// The same 16 x 16 output block with fp16 operands (rounded from the fp32 values in LDS) and
+// fp32 accumulation: one v_mfma_f32_16x16x32_f16 per 32 k (16x16x16 for K = 16), whose lane
+// l supplies A(l%16, k + 8 (l/16) + e) and B(k + 8 (l/16) + e, l%16), e < 8, and holds the
+// same D(4 (l/16) + i, l%16) as the fp32 form.  Used for bf16 inputs only.
+__device__ __forceinline__ f32x4 mfma_blk_h(f32x4 acc, const float *A, int ar, int ak,
+                                            const float *B, int bk, int bc, int K) {
+    const int lane = threadIdx.x & 63, mi = lane & 15, kq = lane >> 4;
+    if (K % 32 == 0) {
+        const float *a = A + mi * ar + 8 * kq * ak;
+        const float *b = B + 8 * kq * bk + mi * bc;
+#pragma unroll 4
+        for (int k = 0; k < K; k += 32) {
+            f16x8h af, bf;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                af[e] = static_cast<_Float16>(a[(k + e) * ak]);
+                bf[e] = static_cast<_Float16>(b[(k + e) * bk]);
+            }
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, acc, 0, 0, 0);
+        }
+        return acc;
+    }
+    if (K == 16) {
+        const float *a = A + mi * ar + 4 * kq * ak;
+        const float *b = B + 4 * kq * bk + mi * bc;
+        f16x4h af, bf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            af[e] = static_cast<_Float16>(a[e * ak]);
+            bf[e] = static_cast<_Float16>(b[e * bk]);
+        }
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(af, bf, acc, 0, 0, 0);
+    }
+    return mfma_blk(acc, A, ar, ak, B, bk, bc, K);
+}
+// fp16 operands (H) or fp32 operands
+template <bool H>
+__device__ __forceinline__ f32x4 mfma_p(f32x4 acc, const float *A, int ar, int ak,
+                                        const float *B, int bk, int bc, int K) {
+    if constexpr (H)
+        return mfma_blk_h(acc, A, ar, ak, B, bk, bc, K);
+    else
+        return mfma_blk(acc, A, ar, ak, B, bk, bc, K);
 }
 
 template <int DK, int DV> struct CB {
@@ -158,6 +208,7 @@ bprep_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
              const TI *__restrict__ beta, const TI *__restrict__ g, float *__restrict__ rec,
              int T, int Hk, int Hv, int nch) {
     using F = CB<DK, DV>;
+    constexpr bool HP = std::is_same<TI, bf16_t>::value;  // fp16 operands for bf16 inputs
     constexpr int LK4 = DK + 4, LV16 = DV + 16, LC4 = kC + 4, LC1 = kC + 1;
     __shared__ __attribute__((aligned(16))) float sK[kC * LK4], sQ[kC * LK4], sV[kC * LV16],
         sT[kC * LC4];
@@ -195,8 +246,8 @@ bprep_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
     // K K^T and Q K^T (row block w), then A (strictly lower) and P (lower) with the decays
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) {
-        const f32x4 kk = mfma_blk(z4, sK + 16 * w * LK4, LK4, 1, sK + 16 * bj * LK4, 1, LK4, DK);
-        const f32x4 qk = mfma_blk(z4, sQ + 16 * w * LK4, LK4, 1, sK + 16 * bj * LK4, 1, LK4, DK);
+        const f32x4 kk = mfma_p<HP>(z4, sK + 16 * w * LK4, LK4, 1, sK + 16 * bj * LK4, 1, LK4, DK);
+        const f32x4 qk = mfma_p<HP>(z4, sQ + 16 * w * LK4, LK4, 1, sK + 16 * bj * LK4, 1, LK4, DK);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = rb + i, s = 16 * bj + mi;
@@ -224,12 +275,12 @@ bprep_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
         if (w < bi) {
             f32x4 x = z4;
             for (int bk = w; bk < bi; ++bk)
-                x = mfma_blk(x, sA + 16 * bi * LC1 + 16 * bk, LC1, 1, sT + 16 * bk * LC4 + 16 * w,
+                x = mfma_p<HP>(x, sA + 16 * bi * LC1 + 16 * bk, LC1, 1, sT + 16 * bk * LC4 + 16 * w,
                              LC4, 1, 16);
 #pragma unroll
             for (int i = 0; i < 4; ++i) sX[w][(4 * kq + i) * 17 + mi] = x[i];
             // the same wavefront reads its block back: LDS operations of a wavefront are in order
-            const f32x4 t = mfma_blk(z4, sT + 16 * bi * LC4 + 16 * bi, LC4, 1, sX[w], 17, 1, 16);
+            const f32x4 t = mfma_p<HP>(z4, sT + 16 * bi * LC4 + 16 * bi, LC4, 1, sX[w], 17, 1, 16);
 #pragma unroll
             for (int i = 0; i < 4; ++i) sT[(16 * bi + 4 * kq + i) * LC4 + 16 * w + mi] = -t[i];
         }
@@ -254,13 +305,13 @@ bprep_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
     // U = Tm (beta V), W = Tm (beta Gm K)  (row block w)
 #pragma unroll
     for (int bj = 0; bj < DV / 16; ++bj) {
-        const f32x4 u = mfma_blk(z4, sT + 16 * w * LC4, LC4, 1, sV + 16 * bj, LV16, 1, kC);
+        const f32x4 u = mfma_p<HP>(z4, sT + 16 * w * LC4, LC4, 1, sV + 16 * bj, LV16, 1, kC);
 #pragma unroll
         for (int i = 0; i < 4; ++i) R[F::OFF_U + (rb + i) * DV + 16 * bj + mi] = u[i];
     }
 #pragma unroll
     for (int bj = 0; bj < DK / 16; ++bj) {
-        const f32x4 x = mfma_blk(z4, sT + 16 * w * LC4, LC4, 1, sQ + 16 * bj, LK4, 1, kC);
+        const f32x4 x = mfma_p<HP>(z4, sT + 16 * w * LC4, LC4, 1, sQ + 16 * bj, LK4, 1, kC);
 #pragma unroll
         for (int i = 0; i < 4; ++i) R[F::OFF_W + (rb + i) * DK + 16 * bj + mi] = x[i];
     }
@@ -274,7 +325,7 @@ bprep_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
 // matrix cores (fp32), each wavefront owning whole 16 x 16 output blocks; the LDS row strides
 // are chosen per operand orientation so that a product's 64 lanes read 64 different banks
 // (stride = 4 mod 64 floats where a lane group walks rows, 16 mod 64 where it walks columns).
-template <int DK, int DV, typename TD>
+template <int DK, int DV, typename TD, bool HP>
 // one workgroup per compute unit (LDS), so every wavefront may use the whole register file
 __global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
@@ -332,7 +383,7 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
             const float eln = vload1(recp(min(c + 1, nch - 1)) + F::OFF_EL);
             // Delta = U - W S: wavefront w, rows 16w..16w+15
             {
-                const f32x4 d = mfma_blk(z4, sM1 + 16 * w * L4, L4, 1, sS, 16, 1, DK);
+                const f32x4 d = mfma_p<HP>(z4, sM1 + 16 * w * L4, L4, 1, sS, 16, 1, DK);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int o = (16 * w + 4 * kq + i) * 16 + mi;
@@ -344,7 +395,7 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
 #pragma unroll
             for (int j = 0; j < NRB; ++j) {
                 const int m0 = 16 * (w + 4 * j);
-                const f32x4 u = mfma_blk(z4, sM2 + m0, 1, L16, sD, 16, 1, kC);
+                const f32x4 u = mfma_p<HP>(z4, sM2 + m0, 1, L16, sD, 16, 1, kC);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float &x = sS[(m0 + 4 * kq + i) * 16 + mi];
@@ -385,8 +436,8 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
             const float eln = vload1(recp(max(c - 1, 0)) + F::OFF_EL);
             // dDelta = P^T dO' + Kt dS: wavefront w, rows 16w..
             {
-                f32x4 d = mfma_blk(z4, sP + 16 * w, 1, LP, sO, 16, 1, kC);
-                d = mfma_blk(d, sM1 + 16 * w * L4, L4, 1, sS, 16, 1, DK);
+                f32x4 d = mfma_p<HP>(z4, sP + 16 * w, 1, LP, sO, 16, 1, kC);
+                d = mfma_p<HP>(d, sM1 + 16 * w * L4, L4, 1, sS, 16, 1, DK);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sD[(16 * w + 4 * kq + i) * 16 + mi] = d[i];
             }
@@ -395,8 +446,8 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
 #pragma unroll
             for (int j = 0; j < NRB; ++j) {
                 const int m0 = 16 * (w + 4 * j);
-                const f32x4 u = mfma_blk(z4, sM2 + m0, 1, L16, sO, 16, 1, kC);
-                const f32x4 x = mfma_blk(z4, sM3 + m0, 1, L16, sD, 16, 1, kC);
+                const f32x4 u = mfma_p<HP>(z4, sM2 + m0, 1, L16, sO, 16, 1, kC);
+                const f32x4 x = mfma_p<HP>(z4, sM3 + m0, 1, L16, sD, 16, 1, kC);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float &y = sS[(m0 + 4 * kq + i) * 16 + mi];
@@ -427,6 +478,7 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
              float *__restrict__ dbeta, float *__restrict__ dg, int T, int Hk, int Hv, int nch,
              float scale) {
     using F = CB<DK, DV>;
+    constexpr bool HP = std::is_same<TI, bf16_t>::value;  // fp16 operands for bf16 inputs
     constexpr int SW = 16, NSL = DV / SW, NBK = DK / 16;
     constexpr int LK4 = DK + 4, LC16 = kC + 16, LC4 = kC + 4, LS = SW + 4;
     constexpr int P1 = kC * LK4 + 2 * DK * LS + 4 * kC * LS;  // W + one value slice
@@ -496,9 +548,9 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
         bar();
         // Delta = U - W S0 ; dDelta = P^T dO' + Kt dSe   (row block w, 16 columns)
         {
-            const f32x4 d = mfma_blk(z4, sW + 16 * w * LK4, LK4, 1, sS0, LS, 1, DK);
-            f32x4 e = mfma_blk(z4, sPY + 16 * w, 1, LC16, sO, LS, 1, kC);
-            e = mfma_blk(e, R + F::OFF_KT + 16 * w * DK, DK, 1, sSe, LS, 1, DK);
+            const f32x4 d = mfma_p<HP>(z4, sW + 16 * w * LK4, LK4, 1, sS0, LS, 1, DK);
+            f32x4 e = mfma_p<HP>(z4, sPY + 16 * w, 1, LC16, sO, LS, 1, kC);
+            e = mfma_p<HP>(e, R + F::OFF_KT + 16 * w * DK, DK, 1, sSe, LS, 1, DK);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = rb + i;
@@ -511,7 +563,7 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
         bar();
         // dBv = Tm^T dDelta -> dv = beta dBv, dbeta += rowsum(dBv o V)
         {
-            const f32x4 x = mfma_blk(z4, sT + 16 * w, 1, LC16, sdD, LS, 1, kC);
+            const f32x4 x = mfma_p<HP>(z4, sT + 16 * w, 1, LC16, sdD, LS, 1, kC);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = rb + i;
@@ -522,14 +574,14 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
         // the partial sums over this slice's value columns (K = 16)
 #pragma unroll
         for (int bj = 0; bj < NBK; ++bj) {
-            aGQ[bj] = mfma_blk(aGQ[bj], sO + 16 * w * LS, LS, 1, sS0 + 16 * bj * LS, 1, LS, SW);
-            aKt[bj] = mfma_blk(aKt[bj], sD + 16 * w * LS, LS, 1, sSe + 16 * bj * LS, 1, LS, SW);
-            aW[bj] = mfma_blk(aW[bj], sdD + 16 * w * LS, LS, 1, sS0 + 16 * bj * LS, 1, LS, SW);
+            aGQ[bj] = mfma_p<HP>(aGQ[bj], sO + 16 * w * LS, LS, 1, sS0 + 16 * bj * LS, 1, LS, SW);
+            aKt[bj] = mfma_p<HP>(aKt[bj], sD + 16 * w * LS, LS, 1, sSe + 16 * bj * LS, 1, LS, SW);
+            aW[bj] = mfma_p<HP>(aW[bj], sdD + 16 * w * LS, LS, 1, sS0 + 16 * bj * LS, 1, LS, SW);
         }
 #pragma unroll
         for (int bj = 0; bj < 4; ++bj) {
-            aP[bj] = mfma_blk(aP[bj], sO + 16 * w * LS, LS, 1, sD + 16 * bj * LS, 1, LS, SW);
-            aTv[bj] = mfma_blk(aTv[bj], sdD + 16 * w * LS, LS, 1, sVv + 16 * bj * LS, 1, LS, SW);
+            aP[bj] = mfma_p<HP>(aP[bj], sO + 16 * w * LS, LS, 1, sD + 16 * bj * LS, 1, LS, SW);
+            aTv[bj] = mfma_p<HP>(aTv[bj], sdD + 16 * w * LS, LS, 1, sVv + 16 * bj * LS, 1, LS, SW);
         }
     }
     bar();
@@ -552,14 +604,14 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
     f32x4 aKK[4], aQK[4], aT[4];
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) {
-        aKK[bj] = mfma_blk(z4, sK + 16 * w * LK4, LK4, 1, sK + 16 * bj * LK4, 1, LK4, DK);
-        aQK[bj] = mfma_blk(z4, sQ + 16 * w * LK4, LK4, 1, sK + 16 * bj * LK4, 1, LK4, DK);
-        aT[bj] = mfma_blk(z4, sX + 16 * w * LK4, LK4, 1, sK + 16 * bj * LK4, 1, LK4, DK);  // dW K^T
+        aKK[bj] = mfma_p<HP>(z4, sK + 16 * w * LK4, LK4, 1, sK + 16 * bj * LK4, 1, LK4, DK);
+        aQK[bj] = mfma_p<HP>(z4, sQ + 16 * w * LK4, LK4, 1, sK + 16 * bj * LK4, 1, LK4, DK);
+        aT[bj] = mfma_p<HP>(z4, sX + 16 * w * LK4, LK4, 1, sK + 16 * bj * LK4, 1, LK4, DK);  // dW K^T
     }
     f32x4 aBk[NBK];
 #pragma unroll
     for (int bj = 0; bj < NBK; ++bj)
-        aBk[bj] = mfma_blk(z4, sT + 16 * w, 1, LC16, sX + 16 * bj, LK4, 1, kC);  // Tm^T dW
+        aBk[bj] = mfma_p<HP>(z4, sT + 16 * w, 1, LC16, sX + 16 * bj, LK4, 1, kC);  // Tm^T dW
     // dTm = beta_col (dDelta V^T + Gm_col dW K^T) -> Y
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) {
@@ -571,7 +623,7 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
     bar();
     f32x4 aM[4];
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) aM[bj] = mfma_blk(z4, sT + 16 * w, 1, LC16, sY + 16 * bj, LC16, 1, kC);
+    for (int bj = 0; bj < 4; ++bj) aM[bj] = mfma_p<HP>(z4, sT + 16 * w, 1, LC16, sY + 16 * bj, LC16, 1, kC);
     bar();
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj)
@@ -580,7 +632,7 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
     bar();
     f32x4 aA[4];
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) aA[bj] = mfma_blk(z4, sY + 16 * w * LC16, LC16, 1, sT + 16 * bj * LC16, 1, LC16, kC);
+    for (int bj = 0; bj < 4; ++bj) aA[bj] = mfma_p<HP>(z4, sY + 16 * w * LC16, LC16, 1, sT + 16 * bj * LC16, 1, LC16, kC);
     // per-element terms; row and column sums of the decay gradient E = dD o D
     f32x4 aKKd[4], aQKd[4];
     float rE[4] = {0.f, 0.f, 0.f, 0.f}, rA[4] = {0.f, 0.f, 0.f, 0.f}, cE[4] = {0.f, 0.f, 0.f, 0.f};
@@ -646,9 +698,9 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
     float sq[4] = {0.f, 0.f, 0.f, 0.f}, sk[4] = {0.f, 0.f, 0.f, 0.f}, sb[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int bj = 0; bj < NBK; ++bj) {
-        f32x4 dk4 = mfma_blk(z4, sX + 16 * w * LC4, LC4, 1, sK + 16 * bj, LK4, 1, kC);
-        dk4 = mfma_blk(dk4, sY + 16 * w, 1, LC16, sQ + 16 * bj, LK4, 1, kC);
-        const f32x4 dq4 = mfma_blk(z4, sY + 16 * w * LC16, LC16, 1, sK + 16 * bj, LK4, 1, kC);
+        f32x4 dk4 = mfma_p<HP>(z4, sX + 16 * w * LC4, LC4, 1, sK + 16 * bj, LK4, 1, kC);
+        dk4 = mfma_p<HP>(dk4, sY + 16 * w, 1, LC16, sQ + 16 * bj, LK4, 1, kC);
+        const f32x4 dq4 = mfma_p<HP>(z4, sY + 16 * w * LC16, LC16, 1, sK + 16 * bj, LK4, 1, kC);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = rb + i, cc = 16 * bj + mi;
@@ -740,7 +792,7 @@ hipError_t launch_chunk_typed(const BackwardArgs &a) {
                        static_cast<const TI *>(a.q), static_cast<const TI *>(a.k),
                        static_cast<const TI *>(a.v), static_cast<const TI *>(a.beta),
                        static_cast<const TI *>(a.g), rec, a.T, a.Hk, a.Hv, nch);
-    hipLaunchKernelGGL((bscan_kernel<DK, DV, TD>), dim3(static_cast<unsigned>(2 * chains * (DV / 16))),
+    hipLaunchKernelGGL((bscan_kernel<DK, DV, TD, std::is_same<TI, bf16_t>::value>), dim3(static_cast<unsigned>(2 * chains * (DV / 16))),
                        dim3(kNT), 0, a.stream, rec, static_cast<const TD *>(a.dO), a.s0, a.dST,
                        Sc, dSe, a.dS0, a.T, a.Hv, nch, static_cast<int>(chains), a.scale);
     hipLaunchKernelGGL((bgrad_kernel<DK, DV, TI, TD>), dim3(grid), dim3(kNT), 0, a.stream,

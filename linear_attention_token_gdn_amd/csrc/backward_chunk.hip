@@ -75,52 +75,74 @@ typedef _Float16 f16x8h __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4h __attribute__((ext_vector_type(4)));
 
 // The same 16 x 16 output block with fp16 operands (rounded from the fp32 values in LDS) and
-// fp32 accumulation: one v_mfma_f32_16x16x32_f16 per 32 k (16x16x16 for K = 16), whose lane
-// l supplies A(l%16, k + 8 (l/16) + e) and B(k + 8 (l/16) + e, l%16), e < 8, and holds the
-// same D(4 (l/16) + i, l%16) as the fp32 form.  Used for bf16 inputs only.
-__device__ __forceinline__ f32x4 mfma_blk_h(f32x4 acc, const float *A, int ar, int ak,
-                                            const float *B, int bk, int bc, int K) {
+// fp32 accumulation: one v_mfma_f32_16x16x32_f16 per 32 k (16x16x16 for K = 16), holding the
+// same D(4 (l/16) + i, l%16) as the fp32 form.  The order of k inside one product is free as
+// long as A and B agree: lane l supplies either the 8 consecutive k + 8 (l/16) + e (IL false:
+// wide LDS reads where operands are contiguous in k) or k + l/16 + 4e (IL true: the same
+// addresses per instruction as the fp32 form, hence the same LDS banks, for which the row
+// strides were chosen).  Which is faster was measured per kernel.  Used for bf16 inputs only.
+template <bool IL, typename TA, typename TB>
+__device__ __forceinline__ f32x4 mfma_blk_h(f32x4 acc, const TA *A, int ar, int ak,
+                                            const TB *B, int bk, int bc, int K) {
     const int lane = threadIdx.x & 63, mi = lane & 15, kq = lane >> 4;
     if (K % 32 == 0) {
-        const float *a = A + mi * ar + 8 * kq * ak;
-        const float *b = B + 8 * kq * bk + mi * bc;
+        constexpr int ks = IL ? 4 : 1;  // step between a lane's k
+        const TA *a = A + mi * ar + (IL ? kq : 8 * kq) * ak;
+        const TB *b = B + (IL ? kq : 8 * kq) * bk + mi * bc;
 #pragma unroll 4
         for (int k = 0; k < K; k += 32) {
             f16x8h af, bf;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                af[e] = static_cast<_Float16>(a[(k + e) * ak]);
-                bf[e] = static_cast<_Float16>(b[(k + e) * bk]);
+                af[e] = static_cast<_Float16>(a[(k + ks * e) * ak]);
+                bf[e] = static_cast<_Float16>(b[(k + ks * e) * bk]);
             }
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, acc, 0, 0, 0);
         }
         return acc;
     }
     if (K == 16) {
-        const float *a = A + mi * ar + 4 * kq * ak;
-        const float *b = B + 4 * kq * bk + mi * bc;
+        const TA *a = A + mi * ar + (IL ? kq : 4 * kq) * ak;
+        const TB *b = B + (IL ? kq : 4 * kq) * bk + mi * bc;
         f16x4h af, bf;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            af[e] = static_cast<_Float16>(a[e * ak]);
-            bf[e] = static_cast<_Float16>(b[e * bk]);
+            af[e] = static_cast<_Float16>(a[(IL ? 4 * e : e) * ak]);
+            bf[e] = static_cast<_Float16>(b[(IL ? 4 * e : e) * bk]);
         }
         return __builtin_amdgcn_mfma_f32_16x16x16f16(af, bf, acc, 0, 0, 0);
     }
-    return mfma_blk(acc, A, ar, ak, B, bk, bc, K);
+    // any other K (none is used): fp32 operands, four k at a time
+    const TA *a = A + mi * ar + kq * ak;
+    const TB *b = B + kq * bk + mi * bc;
+    for (int k = 0; k < K; k += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(static_cast<float>(a[k * ak]),
+                                                   static_cast<float>(b[k * bk]), acc, 0, 0, 0);
+    return acc;
 }
-// fp16 operands (H) or fp32 operands
-template <bool H>
-__device__ __forceinline__ f32x4 mfma_p(f32x4 acc, const float *A, int ar, int ak,
-                                        const float *B, int bk, int bc, int K) {
+// fp16 operands (H, k order IL) or fp32 operands
+template <bool H, bool IL = false, typename TA, typename TB>
+__device__ __forceinline__ f32x4 mfma_p(f32x4 acc, const TA *A, int ar, int ak,
+                                        const TB *B, int bk, int bc, int K) {
     if constexpr (H)
-        return mfma_blk_h(acc, A, ar, ak, B, bk, bc, K);
+        return mfma_blk_h<IL>(acc, A, ar, ak, B, bk, bc, K);
     else
         return mfma_blk(acc, A, ar, ak, B, bk, bc, K);
 }
 
+// Record element type: fp16 for bf16 inputs (the matrix cores take fp16 operands there), fp32
+// otherwise.  e^gamma_last is an fp32 value in either case (at OFF_EL, 4-byte aligned).
+template <bool H> using RecT = typename std::conditional<H, _Float16, float>::type;
+template <typename RT> __device__ __forceinline__ RT *rec_at(float *base, size_t idx, size_t rec) {
+    return reinterpret_cast<RT *>(base) + idx * rec;
+}
+template <typename RT>
+__device__ __forceinline__ const RT *rec_at(const float *base, size_t idx, size_t rec) {
+    return reinterpret_cast<const RT *>(base) + idx * rec;
+}
+
 template <int DK, int DV> struct CB {
-    // records per (chain, chunk), fp32, row-major
+    // records per (chain, chunk), row-major, in elements of the record type
     static constexpr size_t OFF_W = 0;                          // [C][DK]
     static constexpr size_t OFF_U = OFF_W + kC * DK;            // [C][DV]
     static constexpr size_t OFF_KT = OFF_U + kC * DV;           // [C][DK]
@@ -157,6 +179,16 @@ template <int ROWS, int COLS> struct Tile4 {
             const int idx = (i * kNT + threadIdx.x) * 4, r = idx / COLS, c = idx - r * COLS;
             v[i] = *reinterpret_cast<const float4 *>(src + static_cast<size_t>(r) * sld + c);
             v[i].x *= mul; v[i].y *= mul; v[i].z *= mul; v[i].w *= mul;
+        }
+    }
+    // the same from an fp16 matrix (8-byte loads)
+    __device__ __forceinline__ void load(const _Float16 *src, int sld, float mul = 1.f) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int idx = (i * kNT + threadIdx.x) * 4, r = idx / COLS, c = idx - r * COLS;
+            const f16x4h h = *reinterpret_cast<const f16x4h *>(src + static_cast<size_t>(r) * sld + c);
+            v[i] = make_float4(mul * float(h[0]), mul * float(h[1]), mul * float(h[2]),
+                               mul * float(h[3]));
         }
     }
     // rows of a [.., H, D] input tensor (any stored type) at head h; zero past L
@@ -198,6 +230,31 @@ template <int ROWS, int COLS> struct Tile4 {
     }
 };
 
+// A ROWS x COLS tile of a row-major record matrix kept in registers as stored (fp16 or fp32),
+// 4 elements per 8- or 16-byte load, written to LDS as fp32.
+template <int ROWS, int COLS, typename RT> struct TileR {
+    static constexpr int N = ROWS * COLS / 4 / kNT;
+    static_assert(N * 4 * kNT == ROWS * COLS, "tile must split evenly over the threads");
+    using V = typename std::conditional<std::is_same<RT, float>::value, f32x4, f16x4h>::type;
+    V v[N];
+    __device__ __forceinline__ void load(const RT *src, int sld) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int idx = (i * kNT + threadIdx.x) * 4, r = idx / COLS, c = idx - r * COLS;
+            v[i] = *reinterpret_cast<const V *>(src + static_cast<size_t>(r) * sld + c);
+        }
+    }
+    __device__ __forceinline__ void store(float *dst, int ld) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int idx = (i * kNT + threadIdx.x) * 4, r = idx / COLS, c = idx - r * COLS;
+            float *d = dst + r * ld + c;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d[e] = static_cast<float>(v[i][e]);
+        }
+    }
+};
+
 // ---------------------------------------------------------------------------------------
 // bprep_kernel: one workgroup per (chain, chunk).  The products on the matrix cores (fp32),
 // wavefront w owning row block w; Tm by forward substitution, one column per thread.
@@ -219,7 +276,8 @@ bprep_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
     const size_t row0 = static_cast<size_t>(b) * T + t0;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, mi = lane & 15, kq = lane >> 4;
     const int rb = 16 * w + 4 * kq;
-    float *R = rec + (static_cast<size_t>(chain) * nch + c) * F::REC;
+    using RT = RecT<HP>;
+    RT *R = rec_at<RT>(rec, static_cast<size_t>(chain) * nch + c, F::REC);
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
 
     {
@@ -253,7 +311,7 @@ bprep_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
             const int r = rb + i, s = 16 * bj + mi;
             const float d = s <= r ? __expf(sgam[r] - sgam[s]) : 0.f;
             sA[r * LC1 + s] = s < r ? sbeta[r] * kk[i] * d : 0.f;
-            R[F::OFF_P + r * kC + s] = qk[i] * d;
+            R[F::OFF_P + r * kC + s] = static_cast<RT>(qk[i] * d);
         }
     }
     bar();
@@ -289,8 +347,8 @@ bprep_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
     // Gm Q and Kt to the records; then sQ <- beta Gm K (W's right factor), sV <- beta V
     for (int i = tid; i < kC * DK; i += kNT) {
         const int r = i / DK, cc = i - r * DK;
-        R[F::OFF_GQ + i] = __expf(sgam[r]) * sQ[r * LK4 + cc];
-        R[F::OFF_KT + i] = __expf(glast - sgam[r]) * sK[r * LK4 + cc];
+        R[F::OFF_GQ + i] = static_cast<RT>(__expf(sgam[r]) * sQ[r * LK4 + cc]);
+        R[F::OFF_KT + i] = static_cast<RT>(__expf(glast - sgam[r]) * sK[r * LK4 + cc]);
     }
     bar();
     for (int i = tid; i < kC * DK; i += kNT) {
@@ -307,16 +365,16 @@ bprep_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
     for (int bj = 0; bj < DV / 16; ++bj) {
         const f32x4 u = mfma_p<HP>(z4, sT + 16 * w * LC4, LC4, 1, sV + 16 * bj, LV16, 1, kC);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) R[F::OFF_U + (rb + i) * DV + 16 * bj + mi] = u[i];
+        for (int i = 0; i < 4; ++i) R[F::OFF_U + (rb + i) * DV + 16 * bj + mi] = static_cast<RT>(u[i]);
     }
 #pragma unroll
     for (int bj = 0; bj < DK / 16; ++bj) {
         const f32x4 x = mfma_p<HP>(z4, sT + 16 * w * LC4, LC4, 1, sQ + 16 * bj, LK4, 1, kC);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) R[F::OFF_W + (rb + i) * DK + 16 * bj + mi] = x[i];
+        for (int i = 0; i < 4; ++i) R[F::OFF_W + (rb + i) * DK + 16 * bj + mi] = static_cast<RT>(x[i]);
     }
-    for (int i = tid; i < kC * kC; i += kNT) R[F::OFF_T + i] = sT[(i / kC) * LC4 + (i % kC)];
-    if (tid == 0) R[F::OFF_EL] = __expf(glast);
+    for (int i = tid; i < kC * kC; i += kNT) R[F::OFF_T + i] = static_cast<RT>(sT[(i / kC) * LC4 + (i % kC)]);
+    if (tid == 0) *reinterpret_cast<float *>(R + F::OFF_EL) = __expf(glast);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -355,35 +413,40 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
             dst[r * DV + col0 + cc] = sS[i];
         }
     };
-    auto recp = [&](int c) { return rec + (static_cast<size_t>(chain) * nch + c) * F::REC; };
+    using RT = RecT<HP>;
+    auto recp = [&](int c) { return rec_at<RT>(rec, static_cast<size_t>(chain) * nch + c, F::REC); };
+    auto elp = [&](int c) { return reinterpret_cast<const float *>(recp(c) + F::OFF_EL); };
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-    // The next chunk's operands are loaded into registers while this chunk is computed, then
-    // written to LDS: the sequential chain never waits for a record fetch.
+    // The operands of chunks c + 1 and c + 2 are in registers (two sets, alternating) while
+    // chunk c is computed, and are written to LDS at the end of a step: the sequential chain
+    // waits for no record fetch as long as a fetch takes less than two steps.
     if (fwd) {
-        Tile4<kC, DK> nW, nK;
-        Tile4<kC, 16> nU;
-        auto fetch = [&](int c) {
-            const float *R = recp(c);
-            nW.load(R + F::OFF_W, DK);
-            nK.load(R + F::OFF_KT, DK);
-            nU.load(R + F::OFF_U + col0, DV);
+        struct Set {
+            TileR<kC, DK, RT> W, K;
+            TileR<kC, 16, RT> U;
+            float el;
+        } sa, sb;
+        auto fetch = [&](Set &x, int c) {
+            c = min(c, nch - 1);
+            const RT *R = recp(c);
+            x.W.load(R + F::OFF_W, DK);
+            x.K.load(R + F::OFF_KT, DK);
+            x.U.load(R + F::OFF_U + col0, DV);
+            x.el = vload1(elp(c));
         };
-        auto put = [&]() {
-            nW.store(sM1, L4);   // A, rows walked by lanes
-            nK.store(sM2, L16);  // A transposed
-            nU.store(sO, 16);
+        float el = 0.f;
+        auto put = [&](const Set &x) {
+            x.W.store(sM1, L4);   // A, rows walked by lanes
+            x.K.store(sM2, L16);  // A transposed
+            x.U.store(sO, 16);
+            el = x.el;
         };
-        fetch(0);
-        float el = vload1(recp(0) + F::OFF_EL);
-        put();
-        for (int c = 0; c < nch; ++c) {
+        auto step = [&](int c) {
             lds_bar();
             save_state(Sc + (static_cast<size_t>(chain) * nch + c) * SS);
-            fetch(min(c + 1, nch - 1));
-            const float eln = vload1(recp(min(c + 1, nch - 1)) + F::OFF_EL);
             // Delta = U - W S: wavefront w, rows 16w..16w+15
             {
-                const f32x4 d = mfma_p<HP>(z4, sM1 + 16 * w * L4, L4, 1, sS, 16, 1, DK);
+                const f32x4 d = mfma_p<HP, true>(z4, sM1 + 16 * w * L4, L4, 1, sS, 16, 1, DK);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int o = (16 * w + 4 * kq + i) * 16 + mi;
@@ -395,7 +458,7 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
 #pragma unroll
             for (int j = 0; j < NRB; ++j) {
                 const int m0 = 16 * (w + 4 * j);
-                const f32x4 u = mfma_p<HP>(z4, sM2 + m0, 1, L16, sD, 16, 1, kC);
+                const f32x4 u = mfma_p<HP, true>(z4, sM2 + m0, 1, L16, sD, 16, 1, kC);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float &x = sS[(m0 + 4 * kq + i) * 16 + mi];
@@ -403,41 +466,55 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
                 }
             }
             lds_bar();
-            put();
-            el = eln;
+        };
+        fetch(sa, 0);
+        put(sa);
+        fetch(sa, 1);
+        fetch(sb, 2);
+        for (int c = 0; c < nch; c += 2) {
+            step(c);
+            put(sa);  // chunk c + 1
+            fetch(sa, c + 3);
+            if (c + 1 < nch) {
+                step(c + 1);
+                put(sb);  // chunk c + 2
+                fetch(sb, c + 4);
+            }
         }
     } else {
-        Tile4<kC, kC> nP;
-        Tile4<kC, DK> nK, nG, nW;
-        Tile4<kC, 16> nO;
-        auto fetch = [&](int c) {
-            const float *R = recp(c);
-            nP.load(R + F::OFF_P, kC);
-            nK.load(R + F::OFF_KT, DK);
-            nG.load(R + F::OFF_GQ, DK);
-            nW.load(R + F::OFF_W, DK);
-            nO.load_in(dO, static_cast<size_t>(b) * T + c * kC, Hv, hv, col0, DV,
-                       min(kC, T - c * kC), scale);
+        struct Set {
+            TileR<kC, kC, RT> P;
+            TileR<kC, DK, RT> K, G, W;
+            Tile4<kC, 16> O;
+            float el;
+        } sa, sb;
+        auto fetch = [&](Set &x, int c) {
+            c = max(c, 0);
+            const RT *R = recp(c);
+            x.P.load(R + F::OFF_P, kC);
+            x.K.load(R + F::OFF_KT, DK);
+            x.G.load(R + F::OFF_GQ, DK);
+            x.W.load(R + F::OFF_W, DK);
+            x.O.load_in(dO, static_cast<size_t>(b) * T + c * kC, Hv, hv, col0, DV,
+                        min(kC, T - c * kC), scale);
+            x.el = vload1(elp(c));
         };
-        auto put = [&]() {
-            nP.store(sP, LP);    // A transposed
-            nK.store(sM1, L4);   // A
-            nG.store(sM2, L16);  // A transposed
-            nW.store(sM3, L16);  // A transposed
-            nO.store(sO, 16);
+        float el = 0.f;
+        auto put = [&](const Set &x) {
+            x.P.store(sP, LP);    // A transposed
+            x.K.store(sM1, L4);   // A
+            x.G.store(sM2, L16);  // A transposed
+            x.W.store(sM3, L16);  // A transposed
+            x.O.store(sO, 16);
+            el = x.el;
         };
-        fetch(nch - 1);
-        float el = vload1(recp(nch - 1) + F::OFF_EL);
-        put();
-        for (int c = nch - 1; c >= 0; --c) {
+        auto step = [&](int c) {
             lds_bar();
             save_state(dSe + (static_cast<size_t>(chain) * nch + c) * SS);
-            fetch(max(c - 1, 0));
-            const float eln = vload1(recp(max(c - 1, 0)) + F::OFF_EL);
             // dDelta = P^T dO' + Kt dS: wavefront w, rows 16w..
             {
-                f32x4 d = mfma_p<HP>(z4, sP + 16 * w, 1, LP, sO, 16, 1, kC);
-                d = mfma_p<HP>(d, sM1 + 16 * w * L4, L4, 1, sS, 16, 1, DK);
+                f32x4 d = mfma_p<HP, true>(z4, sP + 16 * w, 1, LP, sO, 16, 1, kC);
+                d = mfma_p<HP, true>(d, sM1 + 16 * w * L4, L4, 1, sS, 16, 1, DK);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sD[(16 * w + 4 * kq + i) * 16 + mi] = d[i];
             }
@@ -446,8 +523,8 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
 #pragma unroll
             for (int j = 0; j < NRB; ++j) {
                 const int m0 = 16 * (w + 4 * j);
-                const f32x4 u = mfma_p<HP>(z4, sM2 + m0, 1, L16, sO, 16, 1, kC);
-                const f32x4 x = mfma_p<HP>(z4, sM3 + m0, 1, L16, sD, 16, 1, kC);
+                const f32x4 u = mfma_p<HP, true>(z4, sM2 + m0, 1, L16, sO, 16, 1, kC);
+                const f32x4 x = mfma_p<HP, true>(z4, sM3 + m0, 1, L16, sD, 16, 1, kC);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float &y = sS[(m0 + 4 * kq + i) * 16 + mi];
@@ -455,8 +532,20 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
                 }
             }
             lds_bar();
-            put();
-            el = eln;
+        };
+        fetch(sa, nch - 1);
+        put(sa);
+        fetch(sa, nch - 2);
+        fetch(sb, nch - 3);
+        for (int c = nch - 1; c >= 0; c -= 2) {
+            step(c);
+            put(sa);  // chunk c - 1
+            fetch(sa, c - 3);
+            if (c - 1 >= 0) {
+                step(c - 1);
+                put(sb);  // chunk c - 2
+                fetch(sb, c - 4);
+            }
         }
         bar();
         if (dS0 != nullptr) save_state(dS0 + chain * SS);
@@ -497,7 +586,8 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
     const size_t row0 = static_cast<size_t>(b) * T + t0;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, mi = lane & 15, kq = lane >> 4;
     const int rb = 16 * w + 4 * kq;  // this lane's first row
-    const float *R = rec + (static_cast<size_t>(chain) * nch + c) * F::REC;
+    using RT = RecT<HP>;
+    const RT *R = rec_at<RT>(rec, static_cast<size_t>(chain) * nch + c, F::REC);
     const size_t SS = static_cast<size_t>(DK) * DV;
     const float *S0 = Sc + (static_cast<size_t>(chain) * nch + c) * SS;
     const float *DSE = dSe + (static_cast<size_t>(chain) * nch + c) * SS;
@@ -554,7 +644,7 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = rb + i;
-                sD[r * LS + mi] = R[F::OFF_U + r * DV + cj + mi] - d[i];
+                sD[r * LS + mi] = static_cast<float>(R[F::OFF_U + r * DV + cj + mi]) - d[i];
                 sdD[r * LS + mi] = e[i];
             }
         }

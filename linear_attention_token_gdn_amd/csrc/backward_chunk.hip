@@ -244,13 +244,14 @@ template <int ROWS, int COLS, typename RT> struct TileR {
             v[i] = *reinterpret_cast<const V *>(src + static_cast<size_t>(r) * sld + c);
         }
     }
+    // ld and dst 16-byte aligned: one 16-byte LDS write per 4 elements
     __device__ __forceinline__ void store(float *dst, int ld) const {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int idx = (i * kNT + threadIdx.x) * 4, r = idx / COLS, c = idx - r * COLS;
-            float *d = dst + r * ld + c;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) d[e] = static_cast<float>(v[i][e]);
+            *reinterpret_cast<f32x4 *>(dst + r * ld + c) =
+                f32x4{static_cast<float>(v[i][0]), static_cast<float>(v[i][1]),
+                      static_cast<float>(v[i][2]), static_cast<float>(v[i][3])};
         }
     }
 };

@@ -25,8 +25,6 @@
 // accumulator-layout tile takes that tile's registers as its A operand unchanged.
 #include "gdn_internal.h"
 
-#include <atomic>
-
 namespace gdn {
 namespace {
 
@@ -56,6 +54,8 @@ __device__ __forceinline__ f16x8 cat(f16x4 lo, f16x4 hi) {
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+constexpr int kProgStride = 32;  // unsigned long longs per chain's scan-progress word (256 B)
+
 template <int D, int C> struct SplitCfg {
     static constexpr int NR = C / 16;  // 16-row blocks of a chunk
     static constexpr int NI = D / 16;  // 16-wide tiles of a head dimension
@@ -81,7 +81,8 @@ __global__ void __launch_bounds__(64)
 prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             const bf16_t *__restrict__ v, const bf16_t *__restrict__ beta,
             const bf16_t *__restrict__ g, unsigned char *__restrict__ ws,
-            float *__restrict__ gchunk, int T, int Hk, int Hv, int nchunks, unsigned flags) {
+            float *__restrict__ gchunk, unsigned long long *__restrict__ prog, int T, int Hk,
+            int Hv, int nchunks, unsigned flags) {
     using F = SplitCfg<D, C>;
     constexpr int NR = F::NR, KD = F::KD;
     // products with a K or Q operand: bf16 inputs as stored, or fp16 once normalised
@@ -103,6 +104,9 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     // scan kernel runs that chain
     const int nchains = gridDim.x / nchunks;
     const int c = blockIdx.x / nchains, chain = blockIdx.x - c * nchains;
+    // the scan kernel's progress words start at chunk 0 (it runs after this kernel completes)
+    if (prog != nullptr && blockIdx.x == 0)
+        for (int i = threadIdx.x; i < nchains; i += 64) prog[static_cast<size_t>(i) * kProgStride] = 0ull;
     const int G = Hv / Hk;
     const int b = chain / Hv, hv = chain - b * Hv, hq = hv / G;
     const int t0 = c * C, L = min(C, T - t0);
@@ -406,18 +410,16 @@ template <int D, int C> struct ScanCfg {
 // waiting on HBM.  A compute unit keeps only so many misses in flight, so at HBM latency one
 // scan workgroup streams far below its issue rate; the prefetch moves that latency to other
 // compute units.  Pacing: the scan publishes the chunk it is on, in a 256-byte line of its own
-// per chain (with the launch's epoch, so that stale values of an earlier call are ignored).
+// per chain (cleared by prep_kernel, which runs just before).
 // The prefetch workgroup takes chunks in groups of one per wavefront: wavefront 0 polls, with
 // a pause between polls, until the whole group is within PFD chunks of the scan, then every
 // wavefront loads its chunk's share of the lines and waits for it.  It is only a hint: the
 // scan never waits for it, and a prefetch workgroup gives up after a bounded number of polls.
-constexpr int kProgStride = 32;  // unsigned long longs per chain's progress word (256 B)
 
 template <int D, int C>
 __device__ void prefetch_records(const unsigned char *__restrict__ ws,
-                                 unsigned long long *__restrict__ prog, unsigned epoch,
-                                 int nchunks, int nchains, int p, int w, int nwaves, int lane,
-                                 int *s_done) {
+                                 unsigned long long *__restrict__ prog, int nchunks,
+                                 int nchains, int p, int w, int nwaves, int lane, int *s_done) {
     using F = SplitCfg<D, C>;
     using SC = ScanCfg<D, C>;
     constexpr int LINES = static_cast<int>(F::REC / 128);
@@ -441,9 +443,8 @@ __device__ void prefetch_records(const unsigned char *__restrict__ ws,
         if (w == 0) {
             int done = 0;
             for (;;) {
-                const unsigned long long pv =
-                    __hip_atomic_load(pw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                done = static_cast<unsigned>(pv >> 32) == epoch ? static_cast<int>(pv & 0xffffffffu) : 0;
+                done = static_cast<int>(
+                    __hip_atomic_load(pw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
                 if (n0 + nwaves - 1 < done + SC::PFD) break;
                 if (++polls > kMaxPolls) {
                     done = -1;
@@ -492,7 +493,7 @@ __global__ void __launch_bounds__(64 * (ScanCfg<D, C>::NWV + ScanCfg<D, C>::NWO)
 scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchunk,
             const float *__restrict__ s0, float *__restrict__ sT, TO *__restrict__ o,
             int T, int Hv, int nchunks, float scale, unsigned long long *__restrict__ prog,
-            unsigned epoch, int nscan) {
+            int nscan) {
     using F = SplitCfg<D, C>;
     using SC = ScanCfg<D, C>;
     constexpr int NR = F::NR, NI = F::NI, KD = F::KD, KC = F::KC;
@@ -504,7 +505,7 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     __builtin_assume(w >= 0 && w < NWV + SC::NWO);
     if (static_cast<int>(blockIdx.x) >= nscan) {
-        prefetch_records<D, C>(ws, prog, epoch, nchunks, nscan / NI, blockIdx.x - nscan, w,
+        prefetch_records<D, C>(ws, prog, nchunks, nscan / NI, blockIdx.x - nscan, w,
                                NWV + SC::NWO, lane, reinterpret_cast<int *>(&s_st[0][0][0]));
         return;
     }
@@ -553,8 +554,8 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
             lds_barrier();
             if (publish && lane == 0)  // the state wavefronts are on chunk c
                 __hip_atomic_store(prog + static_cast<size_t>(chain) * kProgStride,
-                                   (static_cast<unsigned long long>(epoch) << 32) | c,
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                   static_cast<unsigned long long>(c), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
             f16x8 nS[KD], nD[KC];
 #pragma unroll
             for (int kk = 0; kk < KD; ++kk) nS[kk] = s_st[c & 1][kk][lane];
@@ -711,25 +712,24 @@ template <int D, int C, typename TO> hipError_t launch_split_typed(const Prefill
     const size_t chains = static_cast<size_t>(a.B) * a.Hv;
     unsigned char *ws = static_cast<unsigned char *>(a.ws);
     float *gch = reinterpret_cast<float *>(ws + chains * nch * SplitCfg<D, C>::REC);
-    auto prep = (a.flags & GDN_QK_L2NORM) ? prep_kernel<D, C, true> : prep_kernel<D, C, false>;
-    hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(chains * nch)), dim3(64), 0, a.stream,
-                       static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
-                       static_cast<const bf16_t *>(a.v), static_cast<const bf16_t *>(a.beta),
-                       static_cast<const bf16_t *>(a.g), ws, gch, a.T, a.Hk, a.Hv, nch, a.flags);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     unsigned long long *prog = reinterpret_cast<unsigned long long *>(
         ws + chains * nch * SplitCfg<D, C>::REC + (chains * nch * sizeof(float) + 255) / 256 * 256);
     // prefetch workgroups only where the scan leaves compute units idle (one workgroup of
     // either kind fills a compute unit's registers)
     const size_t nscan = chains * (D / 16);
     const size_t npf = chains * (D / 16 + SC::NPF) <= 256 ? chains * SC::NPF : 0;
-    static std::atomic<unsigned> launches{0};
-    const unsigned epoch = launches.fetch_add(1, std::memory_order_relaxed) + 1;
+    auto prep = (a.flags & GDN_QK_L2NORM) ? prep_kernel<D, C, true> : prep_kernel<D, C, false>;
+    hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(chains * nch)), dim3(64), 0, a.stream,
+                       static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
+                       static_cast<const bf16_t *>(a.v), static_cast<const bf16_t *>(a.beta),
+                       static_cast<const bf16_t *>(a.g), ws, gch, npf ? prog : nullptr, a.T,
+                       a.Hk, a.Hv, nch, a.flags);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((scan_kernel<D, C, TO>), dim3(static_cast<unsigned>(nscan + npf)),
                        dim3(64 * (SC::NWV + SC::NWO)), 0, a.stream, ws, gch, a.s0, a.sT,
                        static_cast<TO *>(a.o), a.T, a.Hv, nch, a.scale, npf ? prog : nullptr,
-                       epoch, static_cast<int>(nscan));
+                       static_cast<int>(nscan));
     return hipGetLastError();
 }
 

@@ -15,7 +15,10 @@ gdn_decode_tokens over T = 2, 4, 8 tokens of the decode workload per call (one r
 write of every state per call; in place, and for T = 8 also into a separate output state, as a
 verifier keeping the old state would call it); "prologue_and_packed" reports the prefill with
 the fused input prologue and a packed batch of 32 variable-length sequences; "qsa_indexer"
-reports the QSA compressed indexer (gdn_qsa_index) on a 65536-token sequence.
+reports the QSA compressed indexer (gdn_qsa_index) on a 65536-token sequence;
+"prefill_other_workloads" times workloads 2 (batched, grouped heads) and 3 (262,144 tokens);
+"measured_peaks" reports what a plain device copy and a dense bf16 matrix product reach in the
+same run.
 """
 from __future__ import annotations
 
@@ -169,6 +172,98 @@ class HipEvent:
     def __del__(self):
         if HipEvent._hip is not None and self._e:
             HipEvent._hip.hipEventDestroy(self._e)
+
+
+# ------------------------------------------------------------------ the other prefill workloads
+def prefill_configs(gdn, torch, dev, stream, names=(2, 3)):
+    """Workloads 2 (8 x 8192 tokens, 16 q/k and 32 v heads, initial state) and 3 (262,144
+    tokens, 16 heads, long-memory gates): one call each, median of 3, with 1 GiB written between
+    calls so that nothing stays in the last-level cache.  Timing inputs are drawn on the GPU
+    with the recipe's distributions (q, k ~ N(0,1) then L2-normalised per head, v ~ N(0,1),
+    beta = sigmoid(N(0,1)), log alpha = -U(lo, hi), S0 ~ N(0, 0.02^2)); parity is tested on
+    the recipe's own seeded draws."""
+    from gdn_inputs import CONFIGS
+    out = {}
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    for idx in names:
+        c = CONFIGS[idx]
+        B, T, Hk, Hv, dk, dv, C = (c[k_] for k_ in ("B", "T", "Hk", "Hv", "dk", "dv", "chunk"))
+        g = torch.Generator(device=dev)
+        g.manual_seed(1000 + idx)
+        nrm = torch.nn.functional.normalize
+        q = nrm(torch.randn(B, T, Hk, dk, device=dev, generator=g), dim=-1).to(torch.bfloat16)
+        k = nrm(torch.randn(B, T, Hk, dk, device=dev, generator=g), dim=-1).to(torch.bfloat16)
+        v = torch.randn(B, T, Hv, dv, device=dev, generator=g).to(torch.bfloat16)
+        beta = torch.sigmoid(torch.randn(B, T, Hv, device=dev, generator=g)).to(torch.bfloat16)
+        lo, hi = c["g_range"]
+        gg = (-(torch.rand(B, T, Hv, device=dev, generator=g) * (hi - lo) + lo)).to(torch.bfloat16)
+        s0 = None if c["s0_std"] is None else \
+            torch.randn(B, Hv, dk, dv, device=dev, generator=g) * c["s0_std"]
+        o = torch.empty(B, T, Hv, dv, dtype=torch.float32, device=dev)
+        fs = torch.empty(B, Hv, dk, dv, dtype=torch.float32, device=dev)
+        call = lambda: gdn.chunk_fwd(q, k, v, beta, gg, initial_state=s0, chunk=C, o=o,
+                                     final_state=fs)
+        call()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            flush.fill_(1.0)
+            e0, e1 = HipEvent(), HipEvent()
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[1]
+        fl = prefill_flops(B, T, Hk, Hv, dk, dv, C)
+        by = prefill_bytes(B, T, Hk, Hv, dk, dv, has_s0=s0 is not None)
+        out[c["name"]] = {
+            "plan": gdn.gdn_chunk_fwd_plan(B, T, Hk, Hv, dk, dv, C, gdn.GDN_BF16),
+            "ms": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+            "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 2),
+            "frac_bf16_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "GBps": round(by / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "frac_binding_roofline": round(max(by / (HBM_PEAK_GBS * 1e9),
+                                               fl / (MFMA_BF16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3), 4),
+            "algorithmic_flops": fl, "algorithmic_bytes": by}
+        del q, k, v, beta, gg, s0, o, fs
+        torch.cuda.synchronize()
+    del flush
+    return out
+
+
+# ------------------------------------------------------------------ peaks measured in the same run
+def measured_peaks(torch, dev, stream):
+    """What this GPU reaches on plain work, beside the vendor peaks: a 1 GiB device-to-device
+    copy (read + write, GB/s) and a dense 8192^3 bf16 matrix product through torch/hipBLASLt
+    (TFLOP/s, contiguous operands)."""
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        evs = [(HipEvent(), HipEvent()) for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return sorted(e0.elapsed_time(e1) for e0, e1 in evs)[reps // 2]
+    n = 1 << 28
+    src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    copy_ms = timed(lambda: dst.copy_(src))
+    del src, dst
+    m = 8192
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    a = torch.randn(m, m, device=dev, generator=g).to(torch.bfloat16)
+    b = torch.randn(m, m, device=dev, generator=g).to(torch.bfloat16)
+    mm_ms = timed(lambda: torch.matmul(a, b))
+    del a, b
+    torch.cuda.synchronize()
+    return {"copy_GBps": round(2 * n * 4 / (copy_ms * 1e-3) / 1e9, 1),
+            "bf16_gemm_TFLOPs": round(2 * m ** 3 / (mm_ms * 1e-3) / 1e12, 1),
+            "what": "median of 5: 1 GiB device copy; 8192 x 8192 x 8192 bf16 torch.matmul"}
 
 
 # ------------------------------------------------------------------ prologue / packed sequences
@@ -390,6 +485,7 @@ def main():
 
     pre_ms = [e[0].elapsed_time(e[1]) for e in ev]
     pre_mean = sum(pre_ms) / len(pre_ms)
+    pre_sorted = sorted(pre_ms)
     # the same call ten times back to back between one pair of events, with no decode traffic
     # around it (reported beside the in-step figure, which follows 64 decode launches)
     b2b = [HipEvent(), HipEvent()]
@@ -434,6 +530,7 @@ def main():
         }
         result_decode = {
             "state_GBps": round(st_gbs, 1), "frac_hbm_peak": round(st_gbs / HBM_PEAK_GBS, 4),
+            "total_GBps": round(tot_gbs, 1),
             "us_per_step": round(dec_mean * 1e3, 2), "tokens_per_s": round(dc["B"] / (dec_mean * 1e-3), 1),
             "state_bytes_per_step": sbytes, "steps_per_bench_step": nsteps_dec,
         }
@@ -473,6 +570,12 @@ def main():
     extras = None if args.no_extras else prologue_and_packed(gdn, torch, dev, stream, pt, pc, o, fs)
     qsa = None if args.no_extras else qsa_indexer(gdn, torch, dev, stream,
                                                    with_cpu=not args.no_cpu_baseline)
+    others = None if args.no_extras else prefill_configs(gdn, torch, dev, stream)
+    peaks = None if args.no_extras else measured_peaks(torch, dev, stream)
+    if result_decode is not None and peaks is not None:
+        result_decode["frac_measured_copy"] = round(result_decode["total_GBps"] / peaks["copy_GBps"], 4)
+    # the binding roofline of the prefill: the larger of its HBM and MFMA times at peak
+    t_bind = max(pbytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
 
     line = {
         "metric": "GDN prefill tokens/s + % bf16 MFMA peak; decode state GB/s % HBM peak",
@@ -494,11 +597,20 @@ def main():
                     "frac_bf16_mfma_peak": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                     "GBps": round(pre_gbs, 1), "frac_hbm_peak": round(pre_gbs / HBM_PEAK_GBS, 4),
                     "back_to_back_ms": round(b2b_ms, 4),
-                    "back_to_back_tokens_per_s": round(B * T / (b2b_ms * 1e-3), 1)},
+                    "back_to_back_tokens_per_s": round(B * T / (b2b_ms * 1e-3), 1),
+                    "ms_median": round(pre_sorted[len(pre_sorted) // 2], 4),
+                    "ms_min": round(pre_sorted[0], 4),
+                    "frac_binding_roofline": round(t_bind / (pre_mean * 1e-3), 4),
+                    "frac_measured_gemm": None if peaks is None else
+                    round(pre_tflops / peaks["bf16_gemm_TFLOPs"], 4),
+                    "frac_measured_copy": None if peaks is None else
+                    round(pre_gbs / peaks["copy_GBps"], 4)},
         "decode": result_decode,
         "decode_tokens": multi,
         "prologue_and_packed": extras,
         "qsa_indexer": qsa,
+        "prefill_other_workloads": others,
+        "measured_peaks": peaks,
         "roofline": dict(rooflines[dom], kernel_role=dom),
         "rooflines": rooflines,
     }

@@ -84,9 +84,9 @@ size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv
 
 /*
  * Which kernels gdn_chunk_fwd runs for these sizes: "split" (a prep kernel parallel over
- * chunks, a state-scan kernel per chain, then an output kernel parallel over chunks, all
- * through the workspace), "fused" (one kernel per chain), "recurrent" (token by token; the
- * fp32 path) or "invalid".  Static string.
+ * chunks, whose per-chunk operands go through the workspace, then a state-scan kernel per
+ * chain and 16-column state tile that also forms the outputs), "fused" (one kernel per
+ * chain), "recurrent" (token by token; the fp32 path) or "invalid".  Static string.
  */
 const char *gdn_chunk_fwd_plan(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
                                gdn_dtype_t in_dtype);
@@ -109,6 +109,12 @@ const char *gdn_chunk_fwd_plan(int B, int T, int Hk, int Hv, int dk, int dv, int
  *
  * Supported: dk, dv in {16, 32, 64, 128}.  T = 0 writes final_state = initial_state
  * (or zeros) and nothing else.  B = 0 is a no-op.
+ *
+ * Precision: bf16 inputs run on the matrix cores with fp16 (or bf16) operands and fp32
+ * accumulation -- q and k (unit rows) and v are converted to fp16, so v must lie within fp16
+ * range; derived operands (U, W, the state S, Delta, P) are rounded to fp16 for each product;
+ * every sum and the fp32 state itself are never rounded.  fp32 inputs run the token-recurrent
+ * kernel in fp32.
  */
 gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v, const void *beta,
                            const void *g, const float *initial_state, void *o,
@@ -213,6 +219,10 @@ size_t gdn_chunk_fwd_varlen_workspace_size(int num_seqs, int T, int Hk, int Hv, 
  * path's state checkpoints every 64 tokens, one block of recomputed states per chain and the
  * per-slice parts of dq, dk, dbeta and dg.  Supported: dk, dv in {16, 32, 64, 128}; in_dtype
  * and dout_dtype GDN_F32 or GDN_BF16.  Deterministic (no atomics).  B = 0 is a no-op.
+ * Precision: fp32 inputs compute in fp32 throughout.  bf16 inputs on the chunk-parallel path
+ * keep the per-chunk records in fp16 and take fp16 operands with fp32 accumulation on the
+ * matrix cores (values must lie within fp16 range); the states, e^gamma_last and every sum
+ * stay fp32.
  */
 size_t gdn_backward_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv);
 gdn_status_t gdn_backward(const void *q, const void *k, const void *v, const void *beta,

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -187,8 +187,10 @@ gdn_status_t gdn_decode_tokens(const void *q, const void *k, const void *v, cons
  *   flags        GDN_QK_L2NORM | GDN_BETA_LOGIT | GDN_G_LOGIT (or 0); other bits are invalid
  *
  * Every other argument, alignment rule and error is as for gdn_chunk_fwd.  Packed sequences
- * run the single-pass kernels ("fused", or "recurrent" for fp32 and odd head sizes), which
- * need no workspace.
+ * run the plan that gdn_chunk_fwd_plan names for B = num_seqs and the same T (the total):
+ * "split" for few (sequence, head) chains -- its workspace holds one record per chunk
+ * plus at most one unused record per sequence and head -- else "fused", or "recurrent" for
+ * fp32 inputs and head sizes the chunked kernels do not take.
  */
 gdn_status_t gdn_chunk_fwd_varlen(const void *q, const void *k, const void *v, const void *beta,
                                   const void *g, const float *initial_state, void *o,
@@ -197,7 +199,10 @@ gdn_status_t gdn_chunk_fwd_varlen(const void *q, const void *k, const void *v, c
                                   unsigned flags, gdn_dtype_t in_dtype, gdn_dtype_t out_dtype,
                                   void *workspace, size_t workspace_bytes, void *stream);
 
-/* Workspace bytes of gdn_chunk_fwd_varlen: packed != 0 for cu_seqlens != NULL (then 0). */
+/*
+ * Workspace bytes of gdn_chunk_fwd_varlen (0 means none): packed != 0 for cu_seqlens != NULL.
+ * The packed size depends on num_seqs and the total T only, not on the offsets.
+ */
 size_t gdn_chunk_fwd_varlen_workspace_size(int num_seqs, int T, int Hk, int Hv, int dk, int dv,
                                            int chunk, gdn_dtype_t in_dtype, int packed);
 

@@ -25,6 +25,7 @@ import os
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libgdn.so")
 
+ABI_VERSION = 4  # the GDN_ABI_VERSION of include/gdn.h that these signatures follow
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
 GDN_F32, GDN_BF16 = 0, 1
 GDN_QK_L2NORM, GDN_BETA_LOGIT, GDN_G_LOGIT = 1, 2, 4  # input prologue flags
@@ -83,6 +84,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_qsa_workspace_size.restype = sz
     lib.gdn_qsa_index.argtypes = [vp, vp, vp, vp] + [i] * 7 + [f, f, i, vp, sz, vp]
     lib.gdn_qsa_index.restype = i
+    if lib.gdn_abi_version() != ABI_VERSION:
+        raise RuntimeError("libgdn.so has ABI version %d, this binding expects %d; rebuild it "
+                           "with `python -m linear_attention_token_gdn_amd.build`"
+                           % (lib.gdn_abi_version(), ABI_VERSION))
     _lib = lib
     return lib
 

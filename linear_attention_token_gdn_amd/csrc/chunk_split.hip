@@ -56,6 +56,29 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 constexpr int kProgStride = 32;  // unsigned long longs per chain's scan-progress word (256 B)
 
+// Rows and workspace records of one chain (sequence s, v head hv).  Dense batches
+// (cu == nullptr): sequence s is rows sT .. sT + T - 1, and the chain's nrec = ceil(T / C)
+// records are consecutive from chain * nrec.  Packed sequences: head hv owns
+// nrec = floor(T / C) + num_seqs record slots, and sequence s (starting at row a_s) takes
+// the slots from floor(a_s / C) + s on.  Since ceil(len / C) <= floor((a_s mod C + len) / C)
+// + 1, consecutive sequences never share a slot and the last one ends below nrec (for any
+// offsets, as seq_range clamps them into [0, T]).
+struct ChainSpan {
+    size_t row0, rec0;  // first token row; first record
+    int len, nch;       // tokens; chunks
+};
+template <int C>
+__device__ __forceinline__ ChainSpan chain_span(const int32_t *cu, int T, int Hv, int nrec,
+                                                int chain) {
+    const int s = chain / Hv, hv = chain - s * Hv;
+    ChainSpan r;
+    seq_range(cu, T, s, r.row0, r.len);
+    r.nch = (r.len + C - 1) / C;
+    r.rec0 = cu == nullptr ? static_cast<size_t>(chain) * nrec
+                           : static_cast<size_t>(hv) * nrec + r.row0 / C + s;
+    return r;
+}
+
 template <int D, int C> struct SplitCfg {
     static constexpr int NR = C / 16;  // 16-row blocks of a chunk
     static constexpr int NI = D / 16;  // 16-wide tiles of a head dimension
@@ -73,16 +96,18 @@ template <int D, int C> struct SplitCfg {
 };
 
 // ---------------------------------------------------------------------------------------
-// prep_kernel: one wavefront per (chain, chunk).  NORM: q and k are L2-normalised per row
-// here (then held as fp16 for the matrix cores, since the normalised values are not bf16);
-// flags: the gate transforms of the input prologue.
+// prep_kernel: one wavefront per (chain, chunk) -- per record slot and head for packed
+// sequences, where slots past a sequence's chunks have nothing to do.  NORM: q and k are
+// L2-normalised per row here (then held as fp16 for the matrix cores, since the normalised
+// values are not bf16); flags: the gate transforms of the input prologue.
 template <int D, int C, bool NORM>
 __global__ void __launch_bounds__(64)
 prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             const bf16_t *__restrict__ v, const bf16_t *__restrict__ beta,
             const bf16_t *__restrict__ g, unsigned char *__restrict__ ws,
-            float *__restrict__ gchunk, unsigned long long *__restrict__ prog, int T, int Hk,
-            int Hv, int nchunks, unsigned flags) {
+            float *__restrict__ gchunk, unsigned long long *__restrict__ prog,
+            const int32_t *__restrict__ cu, int nseq, int T, int Hk, int Hv, int nrec,
+            unsigned flags) {
     using F = SplitCfg<D, C>;
     constexpr int NR = F::NR, KD = F::KD;
     // products with a K or Q operand: bf16 inputs as stored, or fp16 once normalised
@@ -99,24 +124,44 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     __shared__ __attribute__((aligned(16))) f16 s_td[NR][16][20];     // their inverses (fp16)
 
     const int lane = threadIdx.x, li = lane & 15, lg = lane >> 4;
-    // chunk-major grid: consecutive blocks are the chains of one chunk, so with a multiple of
-    // 8 chains a chain's records are all written from the XCD (block index mod 8) on which the
-    // scan kernel runs that chain
-    const int nchains = gridDim.x / nchunks;
-    const int c = blockIdx.x / nchains, chain = blockIdx.x - c * nchains;
+    // chunk-major grid: consecutive blocks are the chains of one chunk (the heads of one slot),
+    // so with a multiple of 8 chains (heads) a chain's records are all written from the XCD
+    // (block index mod 8) on which the scan kernel runs that chain
+    const int nchains = nseq * Hv;
     // the scan kernel's progress words start at chunk 0 (it runs after this kernel completes)
     if (prog != nullptr && blockIdx.x == 0)
         for (int i = threadIdx.x; i < nchains; i += 64) prog[static_cast<size_t>(i) * kProgStride] = 0ull;
+    int c, chain;
+    if (cu == nullptr) {
+        c = blockIdx.x / nchains;
+        chain = blockIdx.x - c * nchains;
+    } else {
+        // the sequence whose slots start last at or before this slot (the slot starts
+        // floor(a_s / C) + s increase with s)
+        const int slot = blockIdx.x / Hv, h = blockIdx.x - slot * Hv;
+        int s = -1;
+        for (int i0 = 0; i0 < nseq; i0 += 64) {
+            const int i = i0 + lane;
+            const bool le = i < nseq && min(max(cu[i], 0), T) / C + i <= slot;
+            const unsigned long long m = __ballot(le);
+            if (m != 0ull) s = i0 + 63 - __clzll(static_cast<long long>(m));
+        }
+        if (s < 0) return;
+        chain = s * Hv + h;
+        c = slot - (min(max(cu[s], 0), T) / C + s);  // the chunk of sequence s in this slot
+    }
+    const ChainSpan sp = chain_span<C>(cu, T, Hv, nrec, chain);
+    if (c >= sp.nch) return;  // a slot no chunk uses
     const int G = Hv / Hk;
-    const int b = chain / Hv, hv = chain - b * Hv, hq = hv / G;
-    const int t0 = c * C, L = min(C, T - t0);
-    unsigned char *rec = ws + (static_cast<size_t>(chain) * nchunks + c) * F::REC;
+    const int hv = chain % Hv, hq = hv / G;
+    const int t0 = c * C, L = min(C, sp.len - t0);
+    unsigned char *rec = ws + (sp.rec0 + c) * F::REC;
 
     // ---- gate loads first: the vector-memory counter is in order, so their wait below
     //      does not include the K, Q, V loads issued after them
     // (index clamped into the chunk so that the loads need no branch; rows past L are zeroed
     // where the values are first used)
-    const size_t gi = (static_cast<size_t>(b) * T + t0 + min(lane, L - 1)) * Hv + hv;
+    const size_t gi = (sp.row0 + t0 + min(lane, L - 1)) * Hv + hv;
     const bf16_t g_raw = g[gi], b_raw = beta[gi];
     __builtin_amdgcn_sched_barrier(0);  // keep these two loads ahead of the ones below
     // ---- row fragments of K, Q, V (lane: row 16a + li, columns 32kk + 8lg .. +7), bf16
@@ -126,7 +171,7 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
     for (int a = 0; a < NR; ++a) {
         const int r = 16 * a + li;
-        const size_t row = static_cast<size_t>(b) * T + t0 + min(r, L - 1);
+        const size_t row = sp.row0 + t0 + min(r, L - 1);
 #pragma unroll
         for (int kk = 0; kk < KD; ++kk) {
             const size_t oq = (row * Hk + hq) * D + 32 * kk + 8 * lg;
@@ -188,7 +233,7 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         s_Gam[lane] = __expf(gv);
         s_dec[lane] = __expf(glast - gv);
         s_bet[lane] = bv;
-        if (lane == 0) gchunk[static_cast<size_t>(chain) * nchunks + c] = __expf(glast);
+        if (lane == 0) gchunk[sp.rec0 + c] = __expf(glast);
     }
     __syncthreads();
     // gate values in registers: accumulator-layout rows 16a + 4lg + rr (one 16-byte read
@@ -418,7 +463,8 @@ template <int D, int C> struct ScanCfg {
 
 template <int D, int C>
 __device__ void prefetch_records(const unsigned char *__restrict__ ws,
-                                 unsigned long long *__restrict__ prog, int nchunks,
+                                 unsigned long long *__restrict__ prog,
+                                 const int32_t *__restrict__ cu, int T, int Hv, int nrec,
                                  int nchains, int p, int w, int nwaves, int lane, int *s_done) {
     using F = SplitCfg<D, C>;
     using SC = ScanCfg<D, C>;
@@ -435,7 +481,9 @@ __device__ void prefetch_records(const unsigned char *__restrict__ ws,
         chain = p % nchains;
         part = p / nchains;
     }
-    const unsigned char *rec0 = ws + static_cast<size_t>(chain) * nchunks * F::REC;
+    const ChainSpan sp = chain_span<C>(cu, T, Hv, nrec, chain);
+    const int nchunks = sp.nch;
+    const unsigned char *rec0 = ws + sp.rec0 * F::REC;
     unsigned long long *pw = prog + static_cast<size_t>(chain) * kProgStride;
     unsigned acc = 0;
     int polls = 0;
@@ -492,8 +540,8 @@ template <int D, int C, typename TO>
 __global__ void __launch_bounds__(64 * (ScanCfg<D, C>::NWV + ScanCfg<D, C>::NWO))
 scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchunk,
             const float *__restrict__ s0, float *__restrict__ sT, TO *__restrict__ o,
-            int T, int Hv, int nchunks, float scale, unsigned long long *__restrict__ prog,
-            int nscan) {
+            const int32_t *__restrict__ cu, int T, int Hv, int nrec, float scale,
+            unsigned long long *__restrict__ prog, int nscan) {
     using F = SplitCfg<D, C>;
     using SC = ScanCfg<D, C>;
     constexpr int NR = F::NR, NI = F::NI, KD = F::KD, KC = F::KC;
@@ -505,19 +553,22 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     __builtin_assume(w >= 0 && w < NWV + SC::NWO);
     if (static_cast<int>(blockIdx.x) >= nscan) {
-        prefetch_records<D, C>(ws, prog, nchunks, nscan / NI, blockIdx.x - nscan, w,
+        prefetch_records<D, C>(ws, prog, cu, T, Hv, nrec, nscan / NI, blockIdx.x - nscan, w,
                                NWV + SC::NWO, lane, reinterpret_cast<int *>(&s_st[0][0][0]));
         return;
     }
     int chain, jt;
     chain_tile_map(blockIdx.x, nscan, NI, chain, jt);
     const int col = 16 * jt + li;
-    const unsigned char *rec0 = ws + static_cast<size_t>(chain) * nchunks * F::REC;
+    const ChainSpan sp = chain_span<C>(cu, T, Hv, nrec, chain);
+    const int nchunks = sp.nch;  // 0 for an empty sequence: final state = initial state
+    const unsigned char *rec0 = ws + sp.rec0 * F::REC;
 
     if (w >= NWV) {
         // ---- output wavefront: row block a of every chunk, one chunk behind the state
+        if (nchunks == 0) return;
         const int a = w - NWV;
-        const int b = chain / Hv, hv = chain - b * Hv;
+        const int hv = chain % Hv;
         auto load = [&](OutOps<D, C> &op, int cc) {
             const unsigned char *r = rec0 + static_cast<size_t>(cc) * F::REC;
 #pragma unroll
@@ -535,12 +586,12 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc)
                 if (32 * kc <= 16 * a + 15) O = mma_f16_k32(op.pf[kc], bD[kc], O);
-            const int t0 = c * C, L = min(C, T - t0);
+            const int t0 = c * C, L = min(C, sp.len - t0);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int r = 16 * a + 4 * lg + rr;
                 if (r < L)
-                    store_f32(o + ((static_cast<size_t>(b) * T + t0 + r) * Hv + hv) * D + col,
+                    store_f32(o + ((sp.row0 + t0 + r) * Hv + hv) * D + col,
                               scale * O[rr]);
             }
         };
@@ -610,7 +661,7 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
     }
     // this chain's per-chunk decays (raw buffer, 32-bit data format; reads past the end give 0)
     const __amdgpu_buffer_rsrc_t gsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(gchunk + static_cast<size_t>(chain) * nchunks), 0, 4 * nchunks,
+        const_cast<float *>(gchunk + sp.rec0), 0, 4 * nchunks,
         0x00020000);
     auto load = [&](ScanOps<D, C> &op, int cc) {
         const unsigned char *r = rec0 + static_cast<size_t>(cc) * F::REC;
@@ -672,23 +723,25 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
         }
     };
 
-    // Ring of DEPTH chunks of operands in registers.  The main loop is branch-free, so the
-    // compiler's vector-memory waits stay exact (each step waits only for its own chunk's
-    // loads, issued DEPTH steps earlier); loads past the last chunk re-read the last chunk.
-    ScanOps<D, C> ring[DEPTH];
+    if (nchunks > 0) {
+        // Ring of DEPTH chunks of operands in registers.  The main loop is branch-free, so the
+        // compiler's vector-memory waits stay exact (each step waits only for its own chunk's
+        // loads, issued DEPTH steps earlier); loads past the last chunk re-read the last chunk.
+        ScanOps<D, C> ring[DEPTH];
 #pragma unroll
-    for (int s = 0; s < DEPTH; ++s) load(ring[s], min(s, nchunks - 1));
-    int c0 = 0;
-    for (; c0 + DEPTH <= nchunks; c0 += DEPTH) {
+        for (int s = 0; s < DEPTH; ++s) load(ring[s], min(s, nchunks - 1));
+        int c0 = 0;
+        for (; c0 + DEPTH <= nchunks; c0 += DEPTH) {
 #pragma unroll
-        for (int s = 0; s < DEPTH; ++s) {
-            step(ring[s], c0 + s);
-            load(ring[s], min(c0 + s + DEPTH, nchunks - 1));
+            for (int s = 0; s < DEPTH; ++s) {
+                step(ring[s], c0 + s);
+                load(ring[s], min(c0 + s + DEPTH, nchunks - 1));
+            }
         }
-    }
 #pragma unroll
-    for (int s = 0; s < DEPTH; ++s)
-        if (c0 + s < nchunks) step(ring[s], c0 + s);
+        for (int s = 0; s < DEPTH; ++s)
+            if (c0 + s < nchunks) step(ring[s], c0 + s);
+    }
     if (sT) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -698,38 +751,45 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
     }
 }
 
-template <int D, int C> size_t split_ws_bytes(int B, int T, int Hv) {
-    const size_t nch = static_cast<size_t>((T + C - 1) / C);
-    const size_t chains = static_cast<size_t>(B) * Hv;
+// Records per chain (dense) or per head (packed sequences), and in all.
+template <int C> int split_nrec(const PrefillArgs &a) {
+    return a.cu == nullptr ? (a.T + C - 1) / C : a.T / C + a.B;
+}
+template <int C> size_t split_records(const PrefillArgs &a) {
+    return static_cast<size_t>(split_nrec<C>(a)) * a.Hv * (a.cu == nullptr ? a.B : 1);
+}
+
+template <int D, int C> size_t split_ws_bytes(const PrefillArgs &a) {
+    const size_t nrec = split_records<C>(a), chains = static_cast<size_t>(a.B) * a.Hv;
     // operand records | per-chunk decays | per-chain scan progress (256 B each, aligned)
-    return chains * nch * SplitCfg<D, C>::REC + (chains * nch * sizeof(float) + 255) / 256 * 256 +
+    return nrec * SplitCfg<D, C>::REC + (nrec * sizeof(float) + 255) / 256 * 256 +
            chains * kProgStride * sizeof(unsigned long long);
 }
 
 template <int D, int C, typename TO> hipError_t launch_split_typed(const PrefillArgs &a) {
     using SC = ScanCfg<D, C>;
-    const int nch = (a.T + C - 1) / C;
-    const size_t chains = static_cast<size_t>(a.B) * a.Hv;
+    const int nrec = split_nrec<C>(a);
+    const size_t recs = split_records<C>(a), chains = static_cast<size_t>(a.B) * a.Hv;
     unsigned char *ws = static_cast<unsigned char *>(a.ws);
-    float *gch = reinterpret_cast<float *>(ws + chains * nch * SplitCfg<D, C>::REC);
+    float *gch = reinterpret_cast<float *>(ws + recs * SplitCfg<D, C>::REC);
     unsigned long long *prog = reinterpret_cast<unsigned long long *>(
-        ws + chains * nch * SplitCfg<D, C>::REC + (chains * nch * sizeof(float) + 255) / 256 * 256);
+        ws + recs * SplitCfg<D, C>::REC + (recs * sizeof(float) + 255) / 256 * 256);
     // prefetch workgroups only where the scan leaves compute units idle (one workgroup of
     // either kind fills a compute unit's registers)
     const size_t nscan = chains * (D / 16);
     const size_t npf = chains * (D / 16 + SC::NPF) <= 256 ? chains * SC::NPF : 0;
     auto prep = (a.flags & GDN_QK_L2NORM) ? prep_kernel<D, C, true> : prep_kernel<D, C, false>;
-    hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(chains * nch)), dim3(64), 0, a.stream,
+    hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(recs)), dim3(64), 0, a.stream,
                        static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
                        static_cast<const bf16_t *>(a.v), static_cast<const bf16_t *>(a.beta),
-                       static_cast<const bf16_t *>(a.g), ws, gch, npf ? prog : nullptr, a.T,
-                       a.Hk, a.Hv, nch, a.flags);
+                       static_cast<const bf16_t *>(a.g), ws, gch, npf ? prog : nullptr, a.cu,
+                       a.B, a.T, a.Hk, a.Hv, nrec, a.flags);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((scan_kernel<D, C, TO>), dim3(static_cast<unsigned>(nscan + npf)),
                        dim3(64 * (SC::NWV + SC::NWO)), 0, a.stream, ws, gch, a.s0, a.sT,
-                       static_cast<TO *>(a.o), a.T, a.Hv, nch, a.scale, npf ? prog : nullptr,
-                       static_cast<int>(nscan));
+                       static_cast<TO *>(a.o), a.cu, a.T, a.Hv, nrec, a.scale,
+                       npf ? prog : nullptr, static_cast<int>(nscan));
     return hipGetLastError();
 }
 
@@ -741,17 +801,15 @@ template <int D, int C> hipError_t launch_split_out(const PrefillArgs &a) {
 }  // namespace
 
 bool chunk_split_supports(const PrefillArgs &a) {
-    return a.cu == nullptr && a.in_dt == GDN_BF16 && a.dk == a.dv && (a.dk == 64 || a.dk == 128) &&
+    return a.in_dt == GDN_BF16 && a.dk == a.dv && (a.dk == 64 || a.dk == 128) &&
            (a.chunk == 32 || a.chunk == 64);
 }
 
 size_t chunk_split_workspace(const PrefillArgs &a) {
     if (!chunk_split_supports(a)) return 0;
     if (a.dk == 128)
-        return a.chunk == 64 ? split_ws_bytes<128, 64>(a.B, a.T, a.Hv)
-                             : split_ws_bytes<128, 32>(a.B, a.T, a.Hv);
-    return a.chunk == 64 ? split_ws_bytes<64, 64>(a.B, a.T, a.Hv)
-                         : split_ws_bytes<64, 32>(a.B, a.T, a.Hv);
+        return a.chunk == 64 ? split_ws_bytes<128, 64>(a) : split_ws_bytes<128, 32>(a);
+    return a.chunk == 64 ? split_ws_bytes<64, 64>(a) : split_ws_bytes<64, 32>(a);
 }
 
 hipError_t launch_chunk_split(const PrefillArgs &a) {

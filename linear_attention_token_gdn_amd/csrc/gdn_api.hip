@@ -130,11 +130,15 @@ const char *gdn_chunk_fwd_plan(int B, int T, int Hk, int Hv, int dk, int dv, int
     }
 }
 
-size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
-                                    gdn_dtype_t in_dtype) {
+// Workspace bytes of the plan these sizes run; packed: offsets given (their values do not
+// matter: the bound on the record slots holds for any offsets).
+static size_t prefill_workspace(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
+                                gdn_dtype_t in_dtype, bool packed) {
+    static const int32_t kPackedTag = 0;  // a.cu only marks packed sequences here; never read
     gdn::PrefillArgs a = {};
     a.B = B; a.T = T; a.Hk = Hk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.chunk = chunk;
     a.in_dt = in_dtype; a.out_dt = GDN_F32;
+    a.cu = packed ? &kPackedTag : nullptr;
     if (B < 0 || T < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk != 0 || !dim_supported(dk) ||
         !dim_supported(dv) || (chunk != 16 && chunk != 32 && chunk != 64) || !dtype_known(in_dtype))
         return 0;
@@ -144,6 +148,11 @@ size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv
     case Variant::Fused: return gdn::chunk_mfma_workspace(a);
     default: return 0;
     }
+}
+
+size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
+                                    gdn_dtype_t in_dtype) {
+    return prefill_workspace(B, T, Hk, Hv, dk, dv, chunk, in_dtype, false);
 }
 
 gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v, const void *beta,
@@ -175,8 +184,7 @@ gdn_status_t gdn_chunk_fwd_varlen(const void *q, const void *k, const void *v, c
 
 size_t gdn_chunk_fwd_varlen_workspace_size(int num_seqs, int T, int Hk, int Hv, int dk, int dv,
                                            int chunk, gdn_dtype_t in_dtype, int packed) {
-    if (packed) return 0;  // packed sequences run the single-pass kernels, which need none
-    return gdn_chunk_fwd_workspace_size(num_seqs, T, Hk, Hv, dk, dv, chunk, in_dtype);
+    return prefill_workspace(num_seqs, T, Hk, Hv, dk, dv, chunk, in_dtype, packed != 0);
 }
 
 gdn_status_t gdn_decode_tokens(const void *q, const void *k, const void *v, const void *beta,

@@ -37,7 +37,9 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gdn.gdn_abi_version() == 3
+    with open(os.path.join(ROOT, "include", "gdn.h")) as f:
+        declared = int(re.search(r"#define GDN_ABI_VERSION (\d+)", f.read()).group(1))
+    assert gdn.gdn_abi_version() == declared == gdn.ABI_VERSION
     assert gdn.gdn_status_string(0) == "GDN_OK"
     assert gdn.gdn_status_string(1) == "GDN_ERR_INVALID_ARG"
     assert gdn.gdn_status_string(2) == "GDN_ERR_UNSUPPORTED"
@@ -199,10 +201,22 @@ def test_prefill_varlen_validation(lib, kw, status):
 
 
 def test_varlen_workspace(lib):
-    # packed sequences use the single-pass kernels: no workspace; dense = gdn_chunk_fwd's
-    assert gdn.gdn_chunk_fwd_varlen_workspace_size(4, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1) == 0
-    assert (gdn.gdn_chunk_fwd_varlen_workspace_size(1, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 0)
+    ws = gdn.gdn_chunk_fwd_varlen_workspace_size
+    # dense = gdn_chunk_fwd's
+    assert (ws(1, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 0)
             == gdn.gdn_chunk_fwd_workspace_size(1, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16))
+    # many chains: the single-pass kernel, no workspace, packed or not
+    assert gdn.gdn_chunk_fwd_plan(16, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16) == "fused"
+    assert ws(16, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1) == 0
+    # few chains: the split plan; packed sequences take one record slot per sequence and head
+    # beyond the chunks of the total length (records of 72 KiB at d = 128, C = 64; 4-byte
+    # decays per record, 256-aligned; a 256-byte progress word per chain)
+    assert gdn.gdn_chunk_fwd_plan(4, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16) == "split"
+    slots = 16 * (4096 // 64 + 4)
+    assert ws(4, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1) == (
+        slots * 73728 + (slots * 4 + 255) // 256 * 256 + 4 * 16 * 256)
+    assert ws(0, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1) == 0
+    assert ws(2, 4096, 16, 16, 128, 128, 64, gdn.GDN_F32, 1) == 0  # fp32: recurrent
 
 
 def backward_call(**kw):

@@ -62,14 +62,17 @@ LENGTHS = [64, 1, 0, 130, 63, 65, 200, 17]
 
 
 @pytest.mark.parametrize("flags", [0, ALL, 1, 6])
-@pytest.mark.parametrize("variant", ["default", "recurrent"])
+@pytest.mark.parametrize("variant", ["default", "fused", "recurrent"])
 def test_packed_bf16(flags, variant, monkeypatch):
+    """The default for these 32 (sequence, head) chains is the split plan."""
     if variant != "default":
         monkeypatch.setenv("GDN_FORCE_VARIANT", variant)
     gdn = gdn_mod()
     Hk, Hv, d = 2, 4, 128
     cu = np.concatenate([[0], np.cumsum(LENGTHS)]).astype(np.int64)
     T, N = int(cu[-1]), len(LENGTHS)
+    if variant == "default":
+        assert gdn.gdn_chunk_fwd_plan(N, T, Hk, Hv, d, d, 64, gdn.GDN_BF16) == "split"
     x, s0 = raw_inputs((T,), Hk, Hv, d, d, flags, "bf16", 700 + flags, (N, Hv, d, d))
     t = to_dev(x, "bf16")
     cu_t = torch.from_numpy(cu.astype(np.int32)).to(DEV)
@@ -119,6 +122,35 @@ def test_packed_without_states_and_all_empty():
     assert not sT[0].any() and not sT[2].any()  # empty sequences keep the zero state
 
 
+@pytest.mark.parametrize("chunk", [32, 64])
+@pytest.mark.parametrize("variant", ["fused", "split"])
+def test_packed_many_sequences(variant, chunk, monkeypatch):
+    """More than 64 sequences (the split prep finds a slot's sequence 64 offsets at a time),
+    many of them empty or of one token, bf16 outputs, a given initial state."""
+    monkeypatch.setenv("GDN_FORCE_VARIANT", variant)
+    gdn = gdn_mod()
+    rng = np.random.default_rng(750 + chunk)
+    lengths = rng.choice([0, 1, 2, chunk - 1, chunk, chunk + 1, 3 * chunk + 5], size=70)
+    lengths[:3] = 0  # leading empty sequences
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    T, N, Hk, Hv, d = int(cu[-1]), len(lengths), 1, 1, 64
+    x, s0 = raw_inputs((T,), Hk, Hv, d, d, ALL, "bf16", 751 + chunk, (N, Hv, d, d))
+    t = to_dev(x, "bf16")
+    o, sT = gdn.chunk_fwd_varlen(t["q"], t["k"], t["v"], t["beta"], t["g"],
+                                 cu_seqlens=torch.from_numpy(cu.astype(np.int32)).to(DEV),
+                                 initial_state=torch.from_numpy(s0).to(DEV), chunk=chunk,
+                                 scale=1.1, flags=ALL, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ro, rS = oracle.run_packed(x["q"], x["k"], x["v"], x["beta"], x["g"], cu, s0=s0, scale=1.1,
+                               flags=ALL)
+    # bf16 storage of o adds up to 2^-9 relative rounding on top of the fp32 result
+    oe = np.abs(o.float().cpu().numpy() - ro).max()
+    assert oe <= (2e-3 + 2 ** -8) * np.abs(ro).max(), ("many packed o " + variant, oe)
+    check(sT.cpu().numpy(), rS, "bf16", "many packed state " + variant)
+    empty = np.flatnonzero(lengths == 0)
+    assert torch.equal(sT[empty].cpu(), torch.from_numpy(s0[empty]))  # final = initial
+
+
 @pytest.mark.parametrize("variant", ["split", "fused", "recurrent"])
 def test_dense_with_prologue(variant, monkeypatch):
     """cu_seqlens = NULL: dense batches with the prologue, on every plan (split is the
@@ -140,7 +172,8 @@ def test_dense_with_prologue(variant, monkeypatch):
     check(sT.cpu().numpy(), rS, "bf16", "dense+prologue state " + variant)
 
 
-def test_packed_equals_dense_when_lengths_are_equal():
+@pytest.mark.parametrize("variant", ["fused", "split"])
+def test_packed_equals_dense_when_lengths_are_equal(variant):
     """Equal lengths: the packed call and the dense call run the same arithmetic per chain."""
     gdn = gdn_mod()
     B, T, Hk, Hv, d = 3, 100, 2, 4, 64
@@ -148,7 +181,7 @@ def test_packed_equals_dense_when_lengths_are_equal():
     t = to_dev(x, "bf16")
     s0_t = torch.from_numpy(s0).to(DEV)
     import os
-    os.environ["GDN_FORCE_VARIANT"] = "fused"
+    os.environ["GDN_FORCE_VARIANT"] = variant
     try:
         od, Sd = gdn.chunk_fwd_varlen(t["q"], t["k"], t["v"], t["beta"], t["g"],
                                       initial_state=s0_t, chunk=32, flags=ALL)

@@ -337,7 +337,7 @@ def prologue_and_packed(gdn, torch, dev, stream, pt, pc, o, fs):
     bwd_ms = _time(torch, stream, bwd, reps=3)
     res["backward"] = {"workload": pc["name"], "ms": round(bwd_ms, 3),
                        "tokens_per_s": round(B * T / (bwd_ms * 1e-3), 1),
-                       "kernel": "bprep_kernel + bscan_kernel + bgrad_kernel (chunk-parallel, fp32 MFMA)"}
+                       "kernel": "bprep_kernel + bscan_kernel + bgrad_kernel (chunk-parallel MFMA; fp16 operands for bf16 inputs)"}
     res["packed"] = {"sequences": 32, "tokens": Tp, "min_len": int(lengths.min()),
                      "max_len": int(lengths.max()), "heads": H, "d": d, "dtype": "bf16",
                      "flags": "qk_l2norm+beta_logit+g_logit",

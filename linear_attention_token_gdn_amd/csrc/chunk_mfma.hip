@@ -75,8 +75,14 @@ template <int D, int C> struct Cfg {
     static constexpr int NI = D / 16;       // 16-row tiles of the state (key index)
     static constexpr int KD = D / 32;       // 32-wide k-steps over the key index
     static constexpr int KC = C / 32;       // 32-wide k-steps over the chunk
-    static constexpr int PD = D + 8;        // padded LDS pitches (halves)
-    static constexpr int PC = C + 8;
+    // padded LDS pitches (halves).  Arrays read as 16-byte A-operand rows (q, k, -W over the
+    // head dimension; P, K^T over the chunk) take 16 extra halves: lanes li = 0..15 of one
+    // half-wavefront then read rows li and 16-byte slots 4lg (lg = 0, 1) from distinct banks
+    // (the row pitch is 8 mod 32 dwords).  v and A, read in 2- and 8-byte pieces, take 8.
+    static constexpr int PQ = D + 16;
+    static constexpr int PV = D + 8;
+    static constexpr int PT = C + 16;
+    static constexpr int PA = C + 8;
     static constexpr int PO = D + 4;        // output staging pitch (floats)
     static constexpr int NQ = C * D / 8 / NT;  // 16-byte pieces of q (or k, v) per thread
     static constexpr int NO = C * D / 4 / NT;  // 16-byte pieces of o per thread
@@ -84,15 +90,28 @@ template <int D, int C> struct Cfg {
     static_assert(NQ >= 1 && (C * D / 8) % NT == 0 && (C * D / 4) % NT == 0, "tiling");
 };
 
+// Columns of q, k, -W (head dimension) and of P, K^T (chunk index) are stored permuted within
+// each 32-wide k-step: index 16h + 4g + e (h < 2, g < 4, e < 4) sits at 8g + 4h + e.  The
+// 8 values a lane (li, g) feeds one 16x16x32 MFMA -- k = 4g..4g+3 of both 16-wide halves,
+// the order in which a B operand built from two accumulator tiles holds them -- are then
+// contiguous: one 16-byte LDS read instead of two 8-byte ones.  QK^T and KK^T sum over the
+// head dimension in the stored order on both sides, which is the same sum.
+__device__ __forceinline__ constexpr int kperm(int c) {
+    return (c & ~31) | (((c >> 2) & 3) << 3) | (((c >> 4) & 1) << 2) | (c & 3);
+}
+__device__ __forceinline__ constexpr int kunperm(int p) {
+    return (p & ~31) | (((p >> 2) & 1) << 4) | (((p >> 3) & 3) << 2) | (p & 3);
+}
+
 template <int D, int C> struct Smem {
     using F = Cfg<D, C>;
-    f16 q[C][F::PD];          // Q rows
-    f16 k[C][F::PD];          // K rows
-    f16 kt[D][F::PC];         // K^T
-    f16 v[C][F::PD];          // V rows
-    f16 p[C][F::PC];          // lower(Q K^T) o D
-    f16 wn[C][F::PD];         // -W
-    f16 an[C][F::PC];         // -A, off-diagonal 16x16 blocks (lower)
+    f16 q[C][F::PQ];          // Q rows (columns permuted)
+    f16 k[C][F::PQ];          // K rows (columns permuted)
+    f16 kt[D][F::PT];         // K^T (columns permuted)
+    f16 v[C][F::PV];          // V rows
+    f16 p[C][F::PT];          // lower(Q K^T) o D (columns permuted)
+    f16 wn[C][F::PQ];         // -W (columns permuted)
+    f16 an[C][F::PA];         // -A, off-diagonal 16x16 blocks (lower)
     f16 td[F::NR][16][24];    // inverses of the diagonal blocks of I + A, fp16
     float ad[F::NR][16][20];  // diagonal blocks of A, fp32
     float gam[C];             // gamma (chunk-local cumulative log-gate)
@@ -218,8 +237,12 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                 kh[e] = f16(ks * bf16_to_f32(pk[n][e]));
                 vh[e] = f16(bf16_to_f32(pv[n][e]));
             }
-            *reinterpret_cast<f16x8 *>(&sm.q[r][cc * 8]) = qh;
-            *reinterpret_cast<f16x8 *>(&sm.k[r][cc * 8]) = kh;
+            // columns 8cc .. 8cc+7 are two runs of 4 in the permuted order
+            const int c0 = kperm(cc * 8), c1 = kperm(cc * 8 + 4);
+            *reinterpret_cast<f16x4 *>(&sm.q[r][c0]) = f16x4{qh[0], qh[1], qh[2], qh[3]};
+            *reinterpret_cast<f16x4 *>(&sm.q[r][c1]) = f16x4{qh[4], qh[5], qh[6], qh[7]};
+            *reinterpret_cast<f16x4 *>(&sm.k[r][c0]) = f16x4{kh[0], kh[1], kh[2], kh[3]};
+            *reinterpret_cast<f16x4 *>(&sm.k[r][c1]) = f16x4{kh[4], kh[5], kh[6], kh[7]};
             *reinterpret_cast<f16x8 *>(&sm.v[r][cc * 8]) = vh;
         }
         if (wave == 0) {
@@ -281,7 +304,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                     const int r = 16 * rt + 4 * lg + rr;
                     const float d = (s <= r) ? __expf(gr[rr] - gs) : 0.f;
                     if (isq) {
-                        sm.p[r][s] = f16(acc[rr] * d);
+                        sm.p[r][kperm(s)] = f16(acc[rr] * d);
                     } else {
                         const float av = (s < r) ? br[rr] * d * acc[rr] : 0.f;
                         if (st == rt)
@@ -293,14 +316,15 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             }
             if (isq && rt + 1 < NR) {  // the tile right of the diagonal is read by P Delta
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) sm.p[16 * rt + 4 * lg + rr][16 * (rt + 1) + li] = f16(0.f);
+                for (int rr = 0; rr < 4; ++rr)
+                    sm.p[16 * rt + 4 * lg + rr][kperm(16 * (rt + 1) + li)] = f16(0.f);
             }
         }
         for (int idx = tid; idx < D * (C / 8); idx += NT) {
-            const int i = idx % D, s8 = idx / D;
-            f16x8 x;
+            const int i = idx % D, s8 = idx / D, ki = kperm(i);
+            f16x8 x;  // stored positions 8 s8 .. 8 s8 + 7 of row i of K^T
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = sm.k[s8 * 8 + e][i];
+            for (int e = 0; e < 8; ++e) x[e] = sm.k[kunperm(s8 * 8 + e)][ki];
             *reinterpret_cast<f16x8 *>(&sm.kt[i][s8 * 8]) = x;
         }
         lds_barrier();
@@ -326,7 +350,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         f32x4 U[NR], Wp[NR];
 #pragma unroll
         for (int a = 0; a < NR; ++a) {
-            const f16x4 kv4 = *reinterpret_cast<const f16x4 *>(&sm.kt[col][16 * a + 4 * lg]);
+            const f16x4 kv4 = *reinterpret_cast<const f16x4 *>(&sm.kt[col][kperm(16 * a + 4 * lg)]);
             f32x4 yu, yw;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
@@ -348,7 +372,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
         for (int a = 0; a < NR; ++a)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) sm.wn[16 * a + 4 * lg + rr][col] = f16(-Wp[a][rr]);
+            for (int rr = 0; rr < 4; ++rr) sm.wn[16 * a + 4 * lg + rr][kperm(col)] = f16(-Wp[a][rr]);
         lds_barrier();
 
         // ---- stage 4 (sequential part): Delta, O, next state
@@ -369,12 +393,8 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             O[rt] = zero4();
 #pragma unroll
             for (int kk = 0; kk < F::KD; ++kk) {
-                const f16 *wr = &sm.wn[16 * rt + li][32 * kk + 4 * lg];
-                const f16 *qr = &sm.q[16 * rt + li][32 * kk + 4 * lg];
-                const f16x8 aw = cat(*reinterpret_cast<const f16x4 *>(wr),
-                                     *reinterpret_cast<const f16x4 *>(wr + 16));
-                const f16x8 aq = cat(*reinterpret_cast<const f16x4 *>(qr),
-                                     *reinterpret_cast<const f16x4 *>(qr + 16));
+                const f16x8 aw = *reinterpret_cast<const f16x8 *>(&sm.wn[16 * rt + li][32 * kk + 8 * lg]);
+                const f16x8 aq = *reinterpret_cast<const f16x8 *>(&sm.q[16 * rt + li][32 * kk + 8 * lg]);
                 U[rt] = mma_k32(aw, bS[kk], U[rt]);
                 O[rt] = mma_k32(aq, bS[kk], O[rt]);
             }
@@ -399,12 +419,9 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         for (int rt = 0; rt < NR; ++rt) {
 #pragma unroll
             for (int kk = 0; kk < F::KC; ++kk)
-                if (32 * kk <= 16 * rt + 15) {
-                    const f16 *pr = &sm.p[16 * rt + li][32 * kk + 4 * lg];
-                    O[rt] = mma_k32(cat(*reinterpret_cast<const f16x4 *>(pr),
-                                        *reinterpret_cast<const f16x4 *>(pr + 16)),
+                if (32 * kk <= 16 * rt + 15)
+                    O[rt] = mma_k32(*reinterpret_cast<const f16x8 *>(&sm.p[16 * rt + li][32 * kk + 8 * lg]),
                                     bD[kk], O[rt]);
-                }
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) sm.ost[16 * rt + 4 * lg + rr][col] = scale * O[rt][rr];
         }
@@ -414,12 +431,9 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         for (int it = 0; it < F::NI; ++it) {
             S[it] *= GC;
 #pragma unroll
-            for (int kk = 0; kk < F::KC; ++kk) {
-                const f16 *kr = &sm.kt[16 * it + li][32 * kk + 4 * lg];
-                S[it] = mma_k32(cat(*reinterpret_cast<const f16x4 *>(kr),
-                                    *reinterpret_cast<const f16x4 *>(kr + 16)),
+            for (int kk = 0; kk < F::KC; ++kk)
+                S[it] = mma_k32(*reinterpret_cast<const f16x8 *>(&sm.kt[16 * it + li][32 * kk + 8 * lg]),
                                 bDs[kk], S[it]);
-            }
         }
     }
 

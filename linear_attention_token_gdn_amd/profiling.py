@@ -3,13 +3,20 @@
     python -m linear_attention_token_gdn_amd.profiling trace  <kernel_trace.csv> "<command>"
     python -m linear_attention_token_gdn_amd.profiling traffic <fetch_dir> <write_dir> \
            <copy_fetch_dir> <copy_write_dir> "<command>"
+    python -m linear_attention_token_gdn_amd.profiling mfma <label> <mfma_dir> <lds_dir> \
+           <algorithmic_flops_per_call> "<command>"
 
 `trace` prints a markdown table of per-kernel launch counts and durations (from a
 `rocprofv3 --kernel-trace` CSV).  `traffic` turns two counter passes over the benchmark
 (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`) and the same two passes over a plain 1 GiB copy
 into HBM bytes per launch: each counter is scaled by (known copy bytes / what the counter read
 for the copy).  It prints markdown and writes profiles/traffic.json, which bench.py reports
-while the kernel sources are unchanged.
+while the kernel sources are unchanged.  `mfma` reads one counter pass with
+`--pmc MfmaUtil MfmaFlopsF16 MfmaFlopsBF16 SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE` and one with
+`--pmc LdsBankConflict SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE` over a run of one prefill
+workload, prints per-kernel matrix-core busy time, matrix-core flops as issued (which include
+the redundant and selection products the kernels issue, so they exceed the algorithmic count)
+and LDS bank conflicts, and records them under <label> in profiles/mfma.json.
 """
 from __future__ import annotations
 
@@ -173,11 +180,76 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, command):
     return "\n".join(out)
 
 
+PREFILL_KERNELS = ("prep_kernel", "scan_kernel", "chunk_kernel")
+
+
+def mfma(label, mfma_dir, lds_dir, algo_flops, command):
+    """Matrix-core and LDS counters per kernel (medians over its launches)."""
+    algo_flops = float(algo_flops)
+    med = lambda d, n: statistics.median(d[n]) if n in d else 0.0
+    util = read_counter(mfma_dir, "MfmaUtil")
+    f16, bf16 = read_counter(mfma_dir, "MfmaFlopsF16"), read_counter(mfma_dir, "MfmaFlopsBF16")
+    f32 = read_counter(mfma_dir, "SQ_INSTS_VALU_MFMA_MOPS_F32")
+    gui = read_counter(mfma_dir, "GRBM_GUI_ACTIVE")
+    conf = read_counter(lds_dir, "LdsBankConflict")
+    cyc = read_counter(lds_dir, "SQ_LDS_BANK_CONFLICT")
+    act = read_counter(lds_dir, "SQ_LDS_IDX_ACTIVE")
+    out = ["Command: `%s`" % command, "",
+           "Counters per launch (medians over the launches of each kernel). Matrix-core busy is "
+           "rocprofv3's MfmaUtil (busy cycles of the matrix cores over GPU-active cycles of all "
+           "SIMDs); flops issued = 512 x the MFMA op counts; LDS conflicts per access is "
+           "LdsBankConflict.", "",
+           "| kernel | launches | MFMA busy % | MFMA flops issued (G) | of which f16 / bf16 / f32 (G) "
+           "| LDS conflicts / access | LDS conflict cycles % of LDS active |",
+           "|---|---|---|---|---|---|---|"]
+    rec = {"command": command, "kernels": {}}
+    pre = []
+    for name in sorted(util, key=lambda n: -med(gui, n)):
+        if name.startswith(("at::", "__amd", "Cijk")):  # torch, runtime and library kernels
+            continue
+        a, b, c = med(f16, name), med(bf16, name), 512.0 * med(f32, name)
+        lds_pct = 100.0 * med(cyc, name) / med(act, name) if med(act, name) > 0 else 0.0
+        out.append("| `%s` | %d | %.1f | %.3f | %.3f / %.3f / %.3f | %.4f | %.1f |" % (
+            _label(name), len(util[name]), med(util, name), (a + b + c) / 1e9, a / 1e9, b / 1e9,
+            c / 1e9, med(conf, name), lds_pct))
+        rec["kernels"][name] = {"mfma_busy_pct": med(util, name), "mfma_flops_issued": a + b + c,
+                                "gui_active": med(gui, name), "lds_conflicts_per_access":
+                                med(conf, name), "lds_conflict_cycles_pct": lds_pct}
+        if name.startswith(PREFILL_KERNELS):
+            pre.append(name)
+    if pre:
+        issued = sum(rec["kernels"][n]["mfma_flops_issued"] for n in pre)
+        w = sum(rec["kernels"][n]["gui_active"] for n in pre)
+        busy = sum(rec["kernels"][n]["mfma_busy_pct"] * rec["kernels"][n]["gui_active"]
+                   for n in pre) / w if w > 0 else 0.0
+        rec["prefill"] = {"kernels": pre, "mfma_flops_issued_per_call": issued,
+                          "algorithmic_flops_per_call": algo_flops,
+                          "issued_over_algorithmic": issued / algo_flops,
+                          "mfma_busy_pct_weighted": busy,
+                          "source_sha256_16": source_hash(SOURCES["prefill"])}
+        out += ["", "Prefill call (%s): %.3f G MFMA flops issued against %.3f G algorithmic "
+                "(x%.2f); matrix cores busy %.1f%% of the call's GPU-active time (kernels "
+                "weighted by their active cycles)." % (", ".join("`%s`" % n for n in pre),
+                                                        issued / 1e9, algo_flops / 1e9,
+                                                        issued / algo_flops, busy)]
+    path = os.path.join(ROOT, "profiles", "mfma.json")
+    allrec = {}
+    if os.path.exists(path):
+        with open(path) as fh:
+            allrec = json.load(fh)
+    allrec[label] = rec
+    with open(path, "w") as fh:
+        json.dump(allrec, fh, indent=1)
+    return "\n".join(out)
+
+
 def main(argv):
     if argv and argv[0] == "trace":
         print(trace_table(argv[1], argv[2]))
     elif argv and argv[0] == "traffic":
         print(traffic(*argv[1:6]))
+    elif argv and argv[0] == "mfma":
+        print(mfma(*argv[1:7]))
     else:
         print(__doc__)
         return 2

@@ -35,10 +35,15 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, vendor figure
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma.json")
 KERNEL_SOURCES = {
+    # the split plan (prep + scan), the fused kernel and decode, each with the shared header
     "prefill": [os.path.join(ROOT, "linear_attention_token_gdn_amd", "csrc", n)
-                for n in ("chunk_split.hip", "chunk_mfma.hip")],
-    "decode": [os.path.join(ROOT, "linear_attention_token_gdn_amd", "csrc", "decode.hip")],
+                for n in ("chunk_split.hip", "gdn_internal.h")],
+    "fused": [os.path.join(ROOT, "linear_attention_token_gdn_amd", "csrc", n)
+              for n in ("chunk_mfma.hip", "gdn_internal.h")],
+    "decode": [os.path.join(ROOT, "linear_attention_token_gdn_amd", "csrc", n)
+               for n in ("decode.hip", "gdn_internal.h")],
 }
 
 
@@ -91,6 +96,20 @@ def measured_traffic(kernel):
     if not rec or rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
         return None
     return rec.get("bytes_per_launch")
+
+
+def measured_mfma(label, sources):
+    """Matrix-core busy fraction and issued/algorithmic MFMA flops of one prefill workload from
+    the committed counter summary, or None when absent or taken on other kernel sources."""
+    try:
+        with open(MFMA_FILE) as fh:
+            rec = json.load(fh).get(label, {}).get("prefill")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[sources]):
+        return None
+    return {"mfma_busy_pct": round(rec["mfma_busy_pct_weighted"], 2),
+            "mfma_flops_issued_over_algorithmic": round(rec["issued_over_algorithmic"], 3)}
 
 
 # ------------------------------------------------------------------ CPU baseline (oracle)
@@ -217,8 +236,9 @@ def prefill_configs(gdn, torch, dev, stream, names=(2, 3)):
         ms = sorted(ts)[1]
         fl = prefill_flops(B, T, Hk, Hv, dk, dv, C)
         by = prefill_bytes(B, T, Hk, Hv, dk, dv, has_s0=s0 is not None)
+        plan = gdn.gdn_chunk_fwd_plan(B, T, Hk, Hv, dk, dv, C, gdn.GDN_BF16)
         out[c["name"]] = {
-            "plan": gdn.gdn_chunk_fwd_plan(B, T, Hk, Hv, dk, dv, C, gdn.GDN_BF16),
+            "plan": plan,
             "ms": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
             "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 2),
             "frac_bf16_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -226,7 +246,9 @@ def prefill_configs(gdn, torch, dev, stream, names=(2, 3)):
             "frac_hbm_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "frac_binding_roofline": round(max(by / (HBM_PEAK_GBS * 1e9),
                                                fl / (MFMA_BF16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3), 4),
-            "algorithmic_flops": fl, "algorithmic_bytes": by}
+            "algorithmic_flops": fl, "algorithmic_bytes": by,
+            "mfma_counters": measured_mfma("workload%d_%s" % (idx, plan),
+                                           "prefill" if plan == "split" else "fused")}
         del q, k, v, beta, gg, s0, o, fs
         torch.cuda.synchronize()
     del flush
@@ -506,11 +528,14 @@ def main():
         "prefill": {
             "kernel": pre_kernels, "plan": plan, "bound": "hbm",
             "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(pre_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("prefill"),
+            "frac": round(pre_gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("prefill" if plan == "split" else "fused"),
             "algorithmic_bytes": pbytes, "algorithmic_flops": flops,
             "mean_launch_ms": round(pre_mean, 4),
             "mfma_TFLOPs": round(pre_tflops, 2),
             "frac_bf16_mfma_peak": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "mfma_counters": measured_mfma("workload%d_%s" % (args.prefill_config, plan),
+                                           "prefill" if plan == "split" else "fused"),
         }
     }
     dom = "prefill"

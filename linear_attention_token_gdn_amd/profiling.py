@@ -30,9 +30,13 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SOURCES = {
+    # the split plan (prep + scan), the fused kernel and decode, each with the shared header
     "prefill": [os.path.join(ROOT, "linear_attention_token_gdn_amd", "csrc", n)
-                for n in ("chunk_split.hip", "chunk_mfma.hip")],
-    "decode": [os.path.join(ROOT, "linear_attention_token_gdn_amd", "csrc", "decode.hip")],
+                for n in ("chunk_split.hip", "gdn_internal.h")],
+    "fused": [os.path.join(ROOT, "linear_attention_token_gdn_amd", "csrc", n)
+              for n in ("chunk_mfma.hip", "gdn_internal.h")],
+    "decode": [os.path.join(ROOT, "linear_attention_token_gdn_amd", "csrc", n)
+               for n in ("decode.hip", "gdn_internal.h")],
 }
 
 
@@ -166,10 +170,11 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, command):
         out.append("| `%s` | %d | %.0f | %.0f | %.1f | %.1f |" % (
             _label(name), len(fetch.get(name, [])), f, w, rd / 1e6, wr / 1e6))
     rec = {"copy_scale_fetch": sf, "copy_scale_write": sw, "command": command}
-    pre = [n for n in res if n.startswith(("prep_kernel", "scan_kernel", "out_kernel", "chunk_kernel"))]
-    if pre:
-        rec["prefill"] = {"kernels": pre, "bytes_per_launch": sum(sum(res[n]) for n in pre),
-                          "source_sha256_16": source_hash(SOURCES["prefill"])}
+    for key, names in (("prefill", ("prep_kernel", "scan_kernel")), ("fused", ("chunk_kernel",))):
+        pre = [n for n in res if n.startswith(names)]
+        if pre:
+            rec[key] = {"kernels": pre, "bytes_per_launch": sum(sum(res[n]) for n in pre),
+                        "source_sha256_16": source_hash(SOURCES[key])}
     # the single-token decode kernel (MULTI = false) of the benchmark step
     dec = [n for n in res if n.startswith("decode_kernel") and n.endswith("false>")]
     if dec:
@@ -226,7 +231,9 @@ def mfma(label, mfma_dir, lds_dir, algo_flops, command):
                           "algorithmic_flops_per_call": algo_flops,
                           "issued_over_algorithmic": issued / algo_flops,
                           "mfma_busy_pct_weighted": busy,
-                          "source_sha256_16": source_hash(SOURCES["prefill"])}
+                          "source_sha256_16": source_hash(
+                              SOURCES["fused" if any(n.startswith("chunk_kernel") for n in pre)
+                                      else "prefill"])}
         out += ["", "Prefill call (%s): %.3f G MFMA flops issued against %.3f G algorithmic "
                 "(x%.2f); matrix cores busy %.1f%% of the call's GPU-active time (kernels "
                 "weighted by their active cycles)." % (", ".join("`%s`" % n for n in pre),

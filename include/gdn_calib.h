@@ -1,0 +1,44 @@
+/*
+ * gdn_calib.h -- two measurement kernels that give the attainable peaks of the GPU a
+ * benchmark compares against, in the same run: a streaming device copy (HBM) and a loop of
+ * independent fp16 matrix-core products.  They are not part of the GDN computation and live in
+ * their own library (libgdn_calib.so).
+ *
+ * Both enqueue on `stream` (a hipStream_t, or NULL for the default stream), allocate nothing,
+ * keep no state and return 0 on success, 1 for invalid arguments (nothing launched), 3 for a
+ * launch error.
+ */
+#ifndef GDN_CALIB_H
+#define GDN_CALIB_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * Copies `bytes` bytes of device memory from src to dst with 16-byte loads and stores over a
+ * grid of `blocks` workgroups of 256 threads (grid-stride).  variant 0: four loads in flight
+ * per thread; 1: eight; 2: eight, with non-temporal stores; 3: eight, in place (src == dst:
+ * every line is read and written back, the access pattern of an in-place state update);
+ * 4: each workgroup copies one contiguous slice of bytes / blocks, eight loads in flight.
+ * src and dst: device pointers, 16-byte aligned; not overlapping, except src == dst for
+ * variant 3; bytes a multiple of 32768 (of 32768 * blocks for variant 4).
+ */
+int gdn_calib_copy(const void *src, void *dst, size_t bytes, int blocks, int variant,
+                   void *stream);
+
+/*
+ * Runs `iters` rounds of 8 independent v_mfma_f32_16x16x32_f16 products per wavefront on
+ * `blocks` workgroups of 4 wavefronts; each thread writes one float (a sum of its accumulators)
+ * to out[blocks * 256].  Matrix-core flops performed: blocks * 4 * iters * 8 * 16384.
+ * out: device pointer to blocks * 256 floats.  1 <= iters <= 1 << 20.
+ */
+int gdn_calib_mfma(float *out, int blocks, int iters, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_CALIB_H */

@@ -293,3 +293,30 @@ def test_qsa_workspace_and_empty_calls(lib):
     assert gdn.gdn_qsa_workspace_size(0, 64, 4, 128, 4) == 0
     assert qsa_call(B=0) == gdn.GDN_OK
     assert qsa_call(T=0) == gdn.GDN_OK
+
+
+def test_calibration_library():
+    """libgdn_calib.so (the benchmark's attainable-peak kernels) exports what gdn_calib.h
+    declares and rejects bad arguments before launching anything."""
+    path = os.path.join(os.path.dirname(gdn.LIB_PATH), "libgdn_calib.so")
+    if not os.path.exists(path):
+        from linear_attention_token_gdn_amd import build
+        build.build()
+    cal = ctypes.CDLL(path)
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "gdn_calib.h")).read(),
+                  flags=re.S)
+    names = sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["gdn_calib_copy", "gdn_calib_mfma"]
+    for n in names:
+        assert isinstance(getattr(cal, n), ctypes._CFuncPtr), n
+    vp, sz, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    cal.gdn_calib_copy.argtypes = [vp, vp, sz, i, i, vp]
+    cal.gdn_calib_mfma.argtypes = [vp, i, i, vp]
+    assert cal.gdn_calib_copy(None, None, 32768, 64, 0, None) == 1
+    assert cal.gdn_calib_copy(1 << 20, 1 << 30, 16384, 64, 0, None) == 1   # not a multiple
+    assert cal.gdn_calib_copy(1 << 20, (1 << 20) + 32768, 65536, 64, 0, None) == 1  # overlap
+    assert cal.gdn_calib_copy(1 << 20, 1 << 30, 32768, 64, 5, None) == 1   # no such variant
+    assert cal.gdn_calib_copy(1 << 20, 1 << 30, 32768, 64, 4, None) == 1   # slices uneven
+    assert cal.gdn_calib_copy(1 << 20, 1 << 30, 32768, 64, 3, None) == 1   # in place: src == dst
+    assert cal.gdn_calib_mfma(None, 64, 16, None) == 1
+    assert cal.gdn_calib_mfma(1 << 20, 64, 0, None) == 1

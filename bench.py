@@ -388,6 +388,14 @@ def prologue_and_packed(gdn, torch, dev, stream, pt, pc, o, fs):
     packed = lambda: gdn.chunk_fwd_varlen(q, k, v, beta, ga, cu_seqlens=cu_t, chunk=64,
                                           flags=allf, o=ob, final_state=sb)
     packed_ms = _time(torch, stream, packed, reps=5)
+    # the same batch with the plan hint for uneven lengths (split plan; workspace allocated once)
+    hint = allf | gdn.GDN_PREFER_SPLIT
+    hws = torch.empty(max(1, gdn.gdn_chunk_fwd_varlen_workspace_size(32, Tp, H, H, d, d, 64,
+                                                                    gdn.GDN_BF16, 1, hint)),
+                      dtype=torch.uint8, device=dev)
+    packed_hint = lambda: gdn.chunk_fwd_varlen(q, k, v, beta, ga, cu_seqlens=cu_t, chunk=64,
+                                               flags=hint, o=ob, final_state=sb, workspace=hws)
+    packed_hint_ms = _time(torch, stream, packed_hint, reps=5)
     # backward of the prefill workload: all gradients, from a random gradient of o
     d_o = torch.randn(pt["v"].shape, device=dev, generator=g)
     bws = torch.empty(gdn.gdn_backward_workspace_size(B, T, pt["q"].shape[2], pt["v"].shape[2],
@@ -402,7 +410,11 @@ def prologue_and_packed(gdn, torch, dev, stream, pt, pc, o, fs):
     res["packed"] = {"sequences": 32, "tokens": Tp, "min_len": int(lengths.min()),
                      "max_len": int(lengths.max()), "heads": H, "d": d, "dtype": "bf16",
                      "flags": "qk_l2norm+beta_logit+g_logit",
-                     "ms": round(packed_ms, 4), "tokens_per_s": round(Tp / (packed_ms * 1e-3), 1)}
+                     "ms": round(packed_ms, 4), "tokens_per_s": round(Tp / (packed_ms * 1e-3), 1),
+                     "plan": "fused",
+                     "with_split_hint": {"ms": round(packed_hint_ms, 4),
+                                         "tokens_per_s": round(Tp / (packed_hint_ms * 1e-3), 1),
+                                         "plan": "split (GDN_PREFER_SPLIT)"}}
     return res
 
 

@@ -69,6 +69,17 @@ typedef enum gdn_dtype {
 #define GDN_BETA_LOGIT 2u
 #define GDN_G_LOGIT 4u
 
+/*
+ * Plan hint (gdn_chunk_fwd_varlen and gdn_chunk_fwd_varlen_workspace_size only): run the
+ * "split" plan whenever it takes the sizes (bf16 inputs, dk = dv in {64, 128}, chunk 32 or
+ * 64), whatever the number of chains.  Meant for packed batches of very uneven lengths (one
+ * long prompt among short ones): the single-pass kernel's time follows the longest sequence,
+ * the split plan's the total number of chunks.  The host never reads the offsets, so the
+ * library cannot tell such a batch from an even one by itself.  Results agree with the other
+ * plans to the stated precision; the workspace size must be queried with the same flags.
+ */
+#define GDN_PREFER_SPLIT 8u
+
 /* Returns GDN_ABI_VERSION of the built library. */
 int gdn_abi_version(void);
 
@@ -184,10 +195,12 @@ gdn_status_t gdn_decode_tokens(const void *q, const void *k, const void *v, cons
  *                final = initial.  The offsets are not read on the host: offsets outside
  *                [0, T] or decreasing are clamped on the device (wrong lengths, but no access
  *                outside the tensors).
- *   flags        GDN_QK_L2NORM | GDN_BETA_LOGIT | GDN_G_LOGIT (or 0); other bits are invalid
+ *   flags        GDN_QK_L2NORM | GDN_BETA_LOGIT | GDN_G_LOGIT | GDN_PREFER_SPLIT (or 0);
+ *                other bits are invalid
  *
  * Every other argument, alignment rule and error is as for gdn_chunk_fwd.  Packed sequences
- * run the plan that gdn_chunk_fwd_plan names for B = num_seqs and the same T (the total):
+ * run the plan that gdn_chunk_fwd_plan names for B = num_seqs and the same T (the total),
+ * or "split" with GDN_PREFER_SPLIT where it takes the sizes:
  * "split" for few (sequence, head) chains -- its workspace holds one record per chunk
  * plus at most one unused record per sequence and head -- else "fused", or "recurrent" for
  * fp32 inputs and head sizes the chunked kernels do not take.
@@ -200,11 +213,13 @@ gdn_status_t gdn_chunk_fwd_varlen(const void *q, const void *k, const void *v, c
                                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Workspace bytes of gdn_chunk_fwd_varlen (0 means none): packed != 0 for cu_seqlens != NULL.
- * The packed size depends on num_seqs and the total T only, not on the offsets.
+ * Workspace bytes of gdn_chunk_fwd_varlen (0 means none): packed != 0 for cu_seqlens != NULL;
+ * flags: those of the call (only GDN_PREFER_SPLIT changes the size).  The packed size depends
+ * on num_seqs and the total T only, not on the offsets.
  */
 size_t gdn_chunk_fwd_varlen_workspace_size(int num_seqs, int T, int Hk, int Hv, int dk, int dv,
-                                           int chunk, gdn_dtype_t in_dtype, int packed);
+                                           int chunk, gdn_dtype_t in_dtype, int packed,
+                                           unsigned flags);
 
 /*
  * Backward: the gradients of Eq. (1) over T tokens for every (b, hv) chain (training).

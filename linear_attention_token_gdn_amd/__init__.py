@@ -29,6 +29,7 @@ ABI_VERSION = 4  # the GDN_ABI_VERSION of include/gdn.h that these signatures fo
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
 GDN_F32, GDN_BF16 = 0, 1
 GDN_QK_L2NORM, GDN_BETA_LOGIT, GDN_G_LOGIT = 1, 2, 4  # input prologue flags
+GDN_PREFER_SPLIT = 8  # plan hint of the prefill with packed sequences
 EXPORTED_SYMBOLS = ("gdn_abi_version", "gdn_status_string", "gdn_chunk_fwd_workspace_size",
                     "gdn_chunk_fwd_plan", "gdn_chunk_fwd", "gdn_decode_step", "gdn_decode_tokens",
                     "gdn_chunk_fwd_varlen", "gdn_chunk_fwd_varlen_workspace_size",
@@ -74,7 +75,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_chunk_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f,
                                          u, i, i, vp, sz, vp]
     lib.gdn_chunk_fwd_varlen.restype = i
-    lib.gdn_chunk_fwd_varlen_workspace_size.argtypes = [i, i, i, i, i, i, i, i, i]
+    lib.gdn_chunk_fwd_varlen_workspace_size.argtypes = [i, i, i, i, i, i, i, i, i, ctypes.c_uint]
     lib.gdn_chunk_fwd_varlen_workspace_size.restype = sz
     lib.gdn_backward_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.gdn_backward_workspace_size.restype = sz
@@ -157,9 +158,9 @@ def gdn_qsa_index(q, k, sel, importance, B, T, Hq, d, r, nsel, rope_dims, rope_b
 
 
 def gdn_chunk_fwd_varlen_workspace_size(num_seqs, T, Hk, Hv, dk, dv, chunk, in_dtype,
-                                        packed) -> int:
+                                        packed, flags=0) -> int:
     return int(load_library().gdn_chunk_fwd_varlen_workspace_size(num_seqs, T, Hk, Hv, dk, dv,
-                                                                  chunk, in_dtype, packed))
+                                                                  chunk, in_dtype, packed, flags))
 
 
 def gdn_backward_workspace_size(B, T, Hk, Hv, dk, dv) -> int:
@@ -311,7 +312,8 @@ def chunk_fwd_varlen(q, k, v, beta, g, cu_seqlens=None, initial_state=None,
 
     Packed (``cu_seqlens`` an int32 device tensor of N+1 offsets): q, k: [T,Hk,dk]; v: [T,Hv,dv];
     beta, g: [T,Hv]; states [N,Hv,dk,dv].  Dense (``cu_seqlens`` None): the shapes of
-    ``chunk_fwd``.  ``flags``: GDN_QK_L2NORM | GDN_BETA_LOGIT | GDN_G_LOGIT.  Returns
+    ``chunk_fwd``.  ``flags``: GDN_QK_L2NORM | GDN_BETA_LOGIT | GDN_G_LOGIT, and the plan hint
+    GDN_PREFER_SPLIT for packed batches of very uneven lengths.  Returns
     (o, final_state or None)."""
     import torch
     lib = load_library()
@@ -344,7 +346,7 @@ def chunk_fwd_varlen(q, k, v, beta, g, cu_seqlens=None, initial_state=None,
         _check(final_state, "final_state", (nseq, Hv, dk, dv), torch.float32, dev)
     in_code, out_code = _dtype_code(dt), _dtype_code(out_dtype)
     need = int(lib.gdn_chunk_fwd_varlen_workspace_size(nseq, T, Hk, Hv, dk, dv, chunk, in_code,
-                                                       int(cu_seqlens is not None)))
+                                                       int(cu_seqlens is not None), int(flags)))
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -38,7 +38,8 @@ Variant choose_variant(const gdn::PrefillArgs &a) {
         if (strcmp(env, "split") == 0 && gdn::chunk_split_supports(a)) return Variant::Split;
     }
     const long chains = static_cast<long>(a.B) * a.Hv;
-    if (gdn::chunk_split_supports(a) && chains < kSplitBelowChains) return Variant::Split;
+    if (gdn::chunk_split_supports(a) && (chains < kSplitBelowChains || (a.flags & GDN_PREFER_SPLIT)))
+        return Variant::Split;
     if (gdn::chunk_mfma_supports(a)) return Variant::Fused;
     return Variant::Recurrent;
 }
@@ -66,7 +67,8 @@ static gdn_status_t check_prefill(const gdn::PrefillArgs &a) {
     if (!dtype_known(a.in_dt) || !dtype_known(a.out_dt)) return GDN_ERR_UNSUPPORTED;
     if (!dim_supported(a.dk) || !dim_supported(a.dv)) return GDN_ERR_UNSUPPORTED;
     if (a.chunk != 16 && a.chunk != 32 && a.chunk != 64) return GDN_ERR_UNSUPPORTED;
-    if (a.flags & ~(GDN_QK_L2NORM | GDN_BETA_LOGIT | GDN_G_LOGIT)) return GDN_ERR_INVALID_ARG;
+    if (a.flags & ~(GDN_QK_L2NORM | GDN_BETA_LOGIT | GDN_G_LOGIT | GDN_PREFER_SPLIT))
+        return GDN_ERR_INVALID_ARG;
     const size_t B = a.B, T = a.T, Hk = a.Hk, Hv = a.Hv, dk = a.dk, dv = a.dv;
     const size_t rows = a.cu ? T : B * T;  // token rows of the q, k, v, beta, g, o tensors
     const size_t ib = dtype_bytes(a.in_dt), ob = dtype_bytes(a.out_dt);
@@ -133,12 +135,13 @@ const char *gdn_chunk_fwd_plan(int B, int T, int Hk, int Hv, int dk, int dv, int
 // Workspace bytes of the plan these sizes run; packed: offsets given (their values do not
 // matter: the bound on the record slots holds for any offsets).
 static size_t prefill_workspace(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
-                                gdn_dtype_t in_dtype, bool packed) {
+                                gdn_dtype_t in_dtype, bool packed, unsigned flags) {
     static const int32_t kPackedTag = 0;  // a.cu only marks packed sequences here; never read
     gdn::PrefillArgs a = {};
     a.B = B; a.T = T; a.Hk = Hk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.chunk = chunk;
     a.in_dt = in_dtype; a.out_dt = GDN_F32;
     a.cu = packed ? &kPackedTag : nullptr;
+    a.flags = flags & GDN_PREFER_SPLIT;
     if (B < 0 || T < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk != 0 || !dim_supported(dk) ||
         !dim_supported(dv) || (chunk != 16 && chunk != 32 && chunk != 64) || !dtype_known(in_dtype))
         return 0;
@@ -152,7 +155,7 @@ static size_t prefill_workspace(int B, int T, int Hk, int Hv, int dk, int dv, in
 
 size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
                                     gdn_dtype_t in_dtype) {
-    return prefill_workspace(B, T, Hk, Hv, dk, dv, chunk, in_dtype, false);
+    return prefill_workspace(B, T, Hk, Hv, dk, dv, chunk, in_dtype, false, 0u);
 }
 
 gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v, const void *beta,
@@ -183,8 +186,9 @@ gdn_status_t gdn_chunk_fwd_varlen(const void *q, const void *k, const void *v, c
 }
 
 size_t gdn_chunk_fwd_varlen_workspace_size(int num_seqs, int T, int Hk, int Hv, int dk, int dv,
-                                           int chunk, gdn_dtype_t in_dtype, int packed) {
-    return prefill_workspace(num_seqs, T, Hk, Hv, dk, dv, chunk, in_dtype, packed != 0);
+                                           int chunk, gdn_dtype_t in_dtype, int packed,
+                                           unsigned flags) {
+    return prefill_workspace(num_seqs, T, Hk, Hv, dk, dv, chunk, in_dtype, packed != 0, flags);
 }
 
 gdn_status_t gdn_decode_tokens(const void *q, const void *k, const void *v, const void *beta,

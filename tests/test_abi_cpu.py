@@ -148,6 +148,7 @@ def decode_tokens(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(T=-1), gdn.GDN_ERR_INVALID_ARG),
+    (dict(flags=8), gdn.GDN_ERR_INVALID_ARG),  # the plan hint is for the prefill only
     (dict(Hv=3), gdn.GDN_ERR_INVALID_ARG),
     (dict(dv=48), gdn.GDN_ERR_UNSUPPORTED),
     (dict(out_dtype=7), gdn.GDN_ERR_UNSUPPORTED),
@@ -216,6 +217,11 @@ def test_varlen_workspace(lib):
     assert ws(4, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1) == (
         slots * 73728 + (slots * 4 + 255) // 256 * 256 + 4 * 16 * 256)
     assert ws(0, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1) == 0
+    # the plan hint: split for many chains too, with the same slot layout
+    slots = 16 * (4096 // 64 + 16)
+    assert ws(16, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1, gdn.GDN_PREFER_SPLIT) == (
+        slots * 73728 + (slots * 4 + 255) // 256 * 256 + 16 * 16 * 256)
+    assert ws(2, 4096, 16, 16, 128, 128, 64, gdn.GDN_F32, 1, gdn.GDN_PREFER_SPLIT) == 0
     assert ws(2, 4096, 16, 16, 128, 128, 64, gdn.GDN_F32, 1) == 0  # fp32: recurrent
 
 

@@ -61,10 +61,11 @@ def to_dev(d, dtype):
 LENGTHS = [64, 1, 0, 130, 63, 65, 200, 17]
 
 
-@pytest.mark.parametrize("flags", [0, ALL, 1, 6])
+@pytest.mark.parametrize("flags", [0, ALL, 1, 6, ALL | 8])
 @pytest.mark.parametrize("variant", ["default", "fused", "recurrent"])
 def test_packed_bf16(flags, variant, monkeypatch):
-    """The default for these 32 (sequence, head) chains is the split plan."""
+    """The default for these 32 (sequence, head) chains is the split plan; flag 8 is the plan
+    hint GDN_PREFER_SPLIT (split here anyway unless a variant is forced)."""
     if variant != "default":
         monkeypatch.setenv("GDN_FORCE_VARIANT", variant)
     gdn = gdn_mod()
@@ -123,24 +124,34 @@ def test_packed_without_states_and_all_empty():
 
 
 @pytest.mark.parametrize("chunk", [32, 64])
-@pytest.mark.parametrize("variant", ["fused", "split"])
+@pytest.mark.parametrize("variant", ["fused", "split", "hint"])
 def test_packed_many_sequences(variant, chunk, monkeypatch):
     """More than 64 sequences (the split prep finds a slot's sequence 64 offsets at a time),
-    many of them empty or of one token, bf16 outputs, a given initial state."""
-    monkeypatch.setenv("GDN_FORCE_VARIANT", variant)
+    many of them empty or of one token, bf16 outputs, a given initial state.  "hint": no forced
+    variant, the plan hint GDN_PREFER_SPLIT instead."""
+    if variant != "hint":
+        monkeypatch.setenv("GDN_FORCE_VARIANT", variant)
     gdn = gdn_mod()
     rng = np.random.default_rng(750 + chunk)
     lengths = rng.choice([0, 1, 2, chunk - 1, chunk, chunk + 1, 3 * chunk + 5], size=70)
     lengths[:3] = 0  # leading empty sequences
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
-    T, N, Hk, Hv, d = int(cu[-1]), len(lengths), 1, 1, 64
+    # 140 chains: the fused kernel by default, split only when forced or hinted
+    T, N, Hk, Hv, d = int(cu[-1]), len(lengths), 1, 2, 64
     x, s0 = raw_inputs((T,), Hk, Hv, d, d, ALL, "bf16", 751 + chunk, (N, Hv, d, d))
     t = to_dev(x, "bf16")
-    o, sT = gdn.chunk_fwd_varlen(t["q"], t["k"], t["v"], t["beta"], t["g"],
-                                 cu_seqlens=torch.from_numpy(cu.astype(np.int32)).to(DEV),
-                                 initial_state=torch.from_numpy(s0).to(DEV), chunk=chunk,
-                                 scale=1.1, flags=ALL, out_dtype=torch.bfloat16)
+    run = lambda flags: gdn.chunk_fwd_varlen(
+        t["q"], t["k"], t["v"], t["beta"], t["g"],
+        cu_seqlens=torch.from_numpy(cu.astype(np.int32)).to(DEV),
+        initial_state=torch.from_numpy(s0).to(DEV), chunk=chunk, scale=1.1, flags=flags,
+        out_dtype=torch.bfloat16)
+    o, sT = run(ALL | (gdn.GDN_PREFER_SPLIT if variant == "hint" else 0))
     torch.cuda.synchronize()
+    if variant == "hint":  # the hint runs exactly the split plan
+        monkeypatch.setenv("GDN_FORCE_VARIANT", "split")
+        o2, s2 = run(ALL)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o2) and torch.equal(sT, s2)
     ro, rS = oracle.run_packed(x["q"], x["k"], x["v"], x["beta"], x["g"], cu, s0=s0, scale=1.1,
                                flags=ALL)
     # bf16 storage of o adds up to 2^-9 relative rounding on top of the fp32 result

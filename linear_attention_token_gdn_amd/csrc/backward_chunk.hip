@@ -130,6 +130,51 @@ __device__ __forceinline__ f32x4 mfma_p(f32x4 acc, const TA *A, int ar, int ak,
         return mfma_blk(acc, A, ar, ak, B, bk, bc, K);
 }
 
+// One lane's A-operand values of a 16 x K block (A(m, k) = A[m ar + k], K a multiple of 32),
+// loaded once where the same block enters several products: in the order mfma_p<H> (IL false)
+// reads them -- k + 8 (l/16) + e, fp16, for H; k + l/16 in steps of 4, fp32, otherwise.
+template <bool H, int K> struct AFrag {
+    static constexpr int N = H ? K / 32 : K / 4;
+    typename std::conditional<H, f16x8h, float>::type v[N];
+    template <typename TA> __device__ __forceinline__ void load(const TA *A, int ar) {
+        const int lane = threadIdx.x & 63, mi = lane & 15, kq = lane >> 4;
+        if constexpr (H) {
+            const TA *a = A + mi * ar + 8 * kq;
+#pragma unroll
+            for (int n = 0; n < N; ++n)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[n][e] = static_cast<_Float16>(a[32 * n + e]);
+        } else {
+            const TA *a = A + mi * ar + kq;
+#pragma unroll
+            for (int n = 0; n < N; ++n) v[n] = static_cast<float>(a[4 * n]);
+        }
+    }
+};
+// acc += A B with A from registers (AFrag) and B(k, n) = B[k bk + n bc], as mfma_p<H>
+template <bool H, int K, typename TB>
+__device__ __forceinline__ f32x4 mfma_pre(f32x4 acc, const AFrag<H, K> &a, const TB *B, int bk,
+                                          int bc) {
+    const int lane = threadIdx.x & 63, mi = lane & 15, kq = lane >> 4;
+    if constexpr (H) {
+        const TB *b = B + 8 * kq * bk + mi * bc;
+#pragma unroll
+        for (int n = 0; n < AFrag<H, K>::N; ++n) {
+            f16x8h bf;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bf[e] = static_cast<_Float16>(b[(32 * n + e) * bk]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v[n], bf, acc, 0, 0, 0);
+        }
+    } else {
+        const TB *b = B + kq * bk + mi * bc;
+#pragma unroll
+        for (int n = 0; n < AFrag<H, K>::N; ++n)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[n], static_cast<float>(b[4 * n * bk]),
+                                                       acc, 0, 0, 0);
+    }
+    return acc;
+}
+
 // Record element type: fp16 for bf16 inputs (the matrix cores take fp16 operands there), fp32
 // otherwise.  e^gamma_last is an fp32 value in either case (at OFF_EL, 4-byte aligned).
 template <bool H> using RecT = typename std::conditional<H, _Float16, float>::type;
@@ -621,37 +666,53 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
     for (int j = 0; j < 4; ++j) aP[j] = aTv[j] = z4;
     float dglast = 0.f, dbv[4] = {0.f, 0.f, 0.f, 0.f};
 
+    // the value slices' tiles: slice j + 1's loads are in flight while slice j is computed
+    // (the barriers below wait for LDS only, so they do not wait for those loads)
+    Tile4<DK, SW> t0s, tes;
+    Tile4<kC, SW> tos, tvs;
+    float uf[4];  // U of this lane's rows in the slice's column
+    auto fetch = [&](int j) {
+        const int cj = SW * j;
+        t0s.load(S0 + cj, DV);
+        tes.load(DSE + cj, DV);
+        tos.load_in(dO, row0, Hv, hv, cj, DV, L, scale);
+        tvs.load_in(v, row0, Hv, hv, cj, DV, L);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) uf[i] = static_cast<float>(R[F::OFF_U + (rb + i) * DV + cj + mi]);
+    };
+    // Kt's row block w, the A operand of one product in every slice: read once.  With it and U
+    // fetched with the tiles, no global load is waited for inside a slice except the next
+    // slice's (the vector-memory counter is in order).
+    AFrag<HP, DK> ktw;
+    ktw.load(R + F::OFF_KT + 16 * w * DK, DK);
+    fetch(0);
     for (int j = 0; j < NSL; ++j) {
         const int cj = SW * j;
-        bar();  // the previous slice's buffers are free
-        {
-            Tile4<DK, SW> t0s, tes;
-            Tile4<kC, SW> tos, tvs;
-            t0s.load(S0 + cj, DV);
-            tes.load(DSE + cj, DV);
-            tos.load_in(dO, row0, Hv, hv, cj, DV, L, scale);
-            tvs.load_in(v, row0, Hv, hv, cj, DV, L);
-            t0s.store4(sS0, LS);
-            tes.store4(sSe, LS);
-            tos.store4(sO, LS);
-            tvs.store4(sVv, LS);
-        }
-        bar();
+        lds_bar();  // the previous slice's buffers are free
+        t0s.store4(sS0, LS);
+        tes.store4(sSe, LS);
+        tos.store4(sO, LS);
+        tvs.store4(sVv, LS);
+        float u[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = uf[i];
+        if (j + 1 < NSL) fetch(j + 1);
+        lds_bar();
         // Delta = U - W S0 ; dDelta = P^T dO' + Kt dSe   (row block w, 16 columns)
         {
             const f32x4 d = mfma_p<HP>(z4, sW + 16 * w * LK4, LK4, 1, sS0, LS, 1, DK);
             f32x4 e = mfma_p<HP>(z4, sPY + 16 * w, 1, LC16, sO, LS, 1, kC);
-            e = mfma_p<HP>(e, R + F::OFF_KT + 16 * w * DK, DK, 1, sSe, LS, 1, DK);
+            e = mfma_pre<HP, DK>(e, ktw, sSe, LS, 1);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = rb + i;
-                sD[r * LS + mi] = static_cast<float>(R[F::OFF_U + r * DV + cj + mi]) - d[i];
+                sD[r * LS + mi] = u[i] - d[i];
                 sdD[r * LS + mi] = e[i];
             }
         }
         for (int i = tid; i < DK * SW; i += kNT)
             dglast += sS0[(i / SW) * LS + i % SW] * sSe[(i / SW) * LS + i % SW];
-        bar();
+        lds_bar();
         // dBv = Tm^T dDelta -> dv = beta dBv, dbeta += rowsum(dBv o V)
         {
             const f32x4 x = mfma_p<HP>(z4, sT + 16 * w, 1, LC16, sdD, LS, 1, kC);
@@ -675,7 +736,7 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
             aTv[bj] = mfma_p<HP>(aTv[bj], sdD + 16 * w * LS, LS, 1, sVv + 16 * bj * LS, 1, LS, SW);
         }
     }
-    bar();
+    lds_bar();
 
     // ---- phase 2: K, Q, and the terms through Tm, the decays and gamma
     float *sK = smem, *sQ = sK + kC * LK4, *sX = sQ + kC * LK4, *sY = sPY;
@@ -690,7 +751,7 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
     for (int bj = 0; bj < NBK; ++bj)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sX[(rb + i) * LK4 + 16 * bj + mi] = -aW[bj][i];  // dW
-    bar();
+    lds_bar();
     const float glast = sgam[kC - 1];
     f32x4 aKK[4], aQK[4], aT[4];
 #pragma unroll
@@ -711,16 +772,16 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
 #pragma unroll
         for (int i = 0; i < 4; ++i) sY[(rb + i) * LC16 + s] = bs * (aTv[bj][i] + gs * aT[bj][i]);
     }
-    bar();
+    lds_bar();
     f32x4 aM[4];
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) aM[bj] = mfma_p<HP>(z4, sT + 16 * w, 1, LC16, sY + 16 * bj, LC16, 1, kC);
-    bar();
+    lds_bar();
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sY[(rb + i) * LC16 + 16 * bj + mi] = aM[bj][i];
-    bar();
+    lds_bar();
     f32x4 aA[4];
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) aA[bj] = mfma_p<HP>(z4, sY + 16 * w * LC16, LC16, 1, sT + 16 * bj * LC16, 1, LC16, kC);
@@ -753,7 +814,7 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
         cE[bj] += __shfl_xor(cE[bj], 16);
         cE[bj] += __shfl_xor(cE[bj], 32);
     }
-    bar();  // Y (M1) is no longer read
+    lds_bar();  // Y (M1) is no longer read
     if (kq == 0)
 #pragma unroll
         for (int bj = 0; bj < 4; ++bj) scol[w][16 * bj + mi] = cE[bj];
@@ -769,7 +830,7 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
     for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sY[(rb + i) * LC16 + 16 * bj + mi] = aKKd[bj][i];
-    bar();
+    lds_bar();
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
@@ -777,12 +838,12 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
             const int r = rb + i, s = 16 * bj + mi;
             sX[r * LC4 + s] = aKKd[bj][i] + sY[s * LC16 + r];
         }
-    bar();
+    lds_bar();
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sY[(rb + i) * LC16 + 16 * bj + mi] = aQKd[bj][i];
-    bar();
+    lds_bar();
     // dK = (dKK + dKK^T) K + dQK^T Q + e^(glast - gamma) dKt + beta Gm dBk ; dQ = dQK K + Gm dGQ
     float *dqo = dq_part + (row0 * Hv + hv) * DK;  // [rows][Hv][DK] parts (G = 1: the output)
     float *dko = dk_part + (row0 * Hv + hv) * DK;
@@ -825,7 +886,7 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) dl += __shfl_xor(dl, off);
     if (lane == 0) sv[7][w] = dl;
-    bar();
+    lds_bar();
     if (tid < kC) {
         const int r = tid;
         float tsum = sv[5][r];

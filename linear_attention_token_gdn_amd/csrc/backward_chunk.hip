@@ -289,6 +289,14 @@ template <int ROWS, int COLS, typename RT> struct TileR {
             v[i] = *reinterpret_cast<const V *>(src + static_cast<size_t>(r) * sld + c);
         }
     }
+    // as stored (no conversion): one 8- or 16-byte LDS write per 4 elements
+    __device__ __forceinline__ void store_raw(RT *dst, int ld) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int idx = (i * kNT + threadIdx.x) * 4, r = idx / COLS, c = idx - r * COLS;
+            *reinterpret_cast<V *>(dst + r * ld + c) = v[i];
+        }
+    }
     // ld and dst 16-byte aligned: one 16-byte LDS write per 4 elements
     __device__ __forceinline__ void store(float *dst, int ld) const {
 #pragma unroll
@@ -426,9 +434,11 @@ bprep_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
 // ---------------------------------------------------------------------------------------
 // bscan_kernel: blocks [0, chains * NSL) run the forward state chain, the rest the reverse
 // gradient chain; one block per (chain, 16-column slice).  The per-chunk products run on the
-// matrix cores (fp32), each wavefront owning whole 16 x 16 output blocks; the LDS row strides
-// are chosen per operand orientation so that a product's 64 lanes read 64 different banks
-// (stride = 4 mod 64 floats where a lane group walks rows, 16 mod 64 where it walks columns).
+// matrix cores, each wavefront owning whole 16 x 16 output blocks.  The record operands sit in
+// LDS as stored (fp16 for bf16 inputs, else fp32); their row strides are chosen per operand
+// orientation so that a product's 64 lanes read 64 different banks: 4 mod 64 floats (or
+// 8 mod 128 halves: lanes kq, kq + 1 share a dword) where a lane group walks rows, 16 mod 64
+// floats (or halves) where it walks columns.
 template <int DK, int DV, typename TD, bool HP>
 // one workgroup per compute unit (LDS), so every wavefront may use the whole register file
 __global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -438,10 +448,12 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
              int Hv, int nch, int chains, float scale) {
     using F = CB<DK, DV>;
     constexpr int NSL = DV / 16;
-    constexpr int L4 = DK + 4, L16 = DK + 16, LP = kC + 16;  // strides (see above)
+    using RE = RecT<HP>;                                       // record element type
+    constexpr int L4 = HP ? DK + 8 : DK + 4, L16 = DK + 16, LP = kC + 16;  // element strides
     constexpr int NRB = DK / 16 / 4;                          // DK-row blocks per wavefront
-    __shared__ __attribute__((aligned(16))) float sM1[kC * L16], sM2[kC * L16], sM3[kC * L16],
-        sP[kC * LP], sS[DK * 16], sD[kC * 16], sO[kC * 16];
+    __shared__ __attribute__((aligned(16))) RE sM1[kC * L16], sM2[kC * L16], sM3[kC * L16],
+        sP[kC * LP];
+    __shared__ __attribute__((aligned(16))) float sS[DK * 16], sD[kC * 16], sO[kC * 16];
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, mi = lane & 15, kq = lane >> 4;
     const bool fwd = blockIdx.x < chains * NSL;
     const int idx = fwd ? blockIdx.x : blockIdx.x - chains * NSL;
@@ -482,8 +494,8 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
         };
         float el = 0.f;
         auto put = [&](const Set &x) {
-            x.W.store(sM1, L4);   // A, rows walked by lanes
-            x.K.store(sM2, L16);  // A transposed
+            x.W.store_raw(sM1, L4);   // A, rows walked by lanes
+            x.K.store_raw(sM2, L16);  // A transposed
             x.U.store(sO, 16);
             el = x.el;
         };
@@ -547,10 +559,10 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
         };
         float el = 0.f;
         auto put = [&](const Set &x) {
-            x.P.store(sP, LP);    // A transposed
-            x.K.store(sM1, L4);   // A
-            x.G.store(sM2, L16);  // A transposed
-            x.W.store(sM3, L16);  // A transposed
+            x.P.store_raw(sP, LP);    // A transposed
+            x.K.store_raw(sM1, L4);   // A
+            x.G.store_raw(sM2, L16);  // A transposed
+            x.W.store_raw(sM3, L16);  // A transposed
             x.O.store(sO, 16);
             el = x.el;
         };

@@ -195,7 +195,7 @@ template <int DK, int DV> struct CB {
     static constexpr size_t OFF_P = OFF_GQ + kC * DK;           // [C][C]
     static constexpr size_t OFF_T = OFF_P + kC * kC;            // [C][C]
     static constexpr size_t OFF_EL = OFF_T + kC * kC;           // e^gamma_last
-    static constexpr size_t REC = OFF_EL + 4;
+    static constexpr size_t REC = OFF_EL + 8;  // a multiple of 8: 16-byte aligned records
     static constexpr int LK = DK + 1, LV = DV + 1, LC = kC + 1;  // padded LDS strides
     // 64 x DK register tiles
     static constexpr int NXK = DK / 4, TMK = kC / (kNT / NXK);
@@ -277,28 +277,31 @@ template <int ROWS, int COLS> struct Tile4 {
 
 // A ROWS x COLS tile of a row-major record matrix kept in registers as stored (fp16 or fp32),
 // 4 elements per 8- or 16-byte load, written to LDS as fp32.
-template <int ROWS, int COLS, typename RT> struct TileR {
-    static constexpr int N = ROWS * COLS / 4 / kNT;
-    static_assert(N * 4 * kNT == ROWS * COLS, "tile must split evenly over the threads");
-    using V = typename std::conditional<std::is_same<RT, float>::value, f32x4, f16x4h>::type;
+template <int ROWS, int COLS, typename RT, int E = 4> struct TileR {  // E elements per load
+    static constexpr int N = ROWS * COLS / E / kNT;
+    static_assert(N * E * kNT == ROWS * COLS, "tile must split evenly over the threads");
+    static_assert(E == 4 || (E == 8 && !std::is_same<RT, float>::value), "8 per load: fp16");
+    using V = typename std::conditional<std::is_same<RT, float>::value, f32x4,
+              typename std::conditional<E == 8, f16x8h, f16x4h>::type>::type;
     V v[N];
     __device__ __forceinline__ void load(const RT *src, int sld) {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const int idx = (i * kNT + threadIdx.x) * 4, r = idx / COLS, c = idx - r * COLS;
+            const int idx = (i * kNT + threadIdx.x) * E, r = idx / COLS, c = idx - r * COLS;
             v[i] = *reinterpret_cast<const V *>(src + static_cast<size_t>(r) * sld + c);
         }
     }
-    // as stored (no conversion): one 8- or 16-byte LDS write per 4 elements
+    // as stored (no conversion): one LDS write of E elements (8 or 16 bytes)
     __device__ __forceinline__ void store_raw(RT *dst, int ld) const {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const int idx = (i * kNT + threadIdx.x) * 4, r = idx / COLS, c = idx - r * COLS;
+            const int idx = (i * kNT + threadIdx.x) * E, r = idx / COLS, c = idx - r * COLS;
             *reinterpret_cast<V *>(dst + r * ld + c) = v[i];
         }
     }
     // ld and dst 16-byte aligned: one 16-byte LDS write per 4 elements
     __device__ __forceinline__ void store(float *dst, int ld) const {
+        static_assert(E == 4, "converting store: 4 elements per load");
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int idx = (i * kNT + threadIdx.x) * 4, r = idx / COLS, c = idx - r * COLS;
@@ -480,7 +483,7 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
     // waits for no record fetch as long as a fetch takes less than two steps.
     if (fwd) {
         struct Set {
-            TileR<kC, DK, RT> W, K;
+            TileR<kC, DK, RT, HP ? 8 : 4> W, K;  // 16-byte loads for fp16 records
             TileR<kC, 16, RT> U;
             float el;
         } sa, sb;
@@ -541,8 +544,8 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
         }
     } else {
         struct Set {
-            TileR<kC, kC, RT> P;
-            TileR<kC, DK, RT> K, G, W;
+            TileR<kC, kC, RT, HP ? 8 : 4> P;  // 16-byte loads for fp16 records
+            TileR<kC, DK, RT, HP ? 8 : 4> K, G, W;
             Tile4<kC, 16> O;
             float el;
         } sa, sb;
@@ -933,7 +936,7 @@ bool backward_chunk_supports(const BackwardArgs &a) {
 size_t backward_chunk_workspace(int B, int T, int Hk, int Hv, int dk, int dv) {
     const size_t chains = static_cast<size_t>(B) * Hv;
     const size_t nch = (static_cast<size_t>(T) + kC - 1) / kC;
-    const size_t rec = static_cast<size_t>(kC) * (3 * dk + dv + 2 * kC) + 4;
+    const size_t rec = static_cast<size_t>(kC) * (3 * dk + dv + 2 * kC) + 8;
     size_t bytes = chains * nch * (rec + 2 * static_cast<size_t>(dk) * dv) * 4;
     if (Hv != Hk) bytes += 2 * static_cast<size_t>(B) * T * Hv * dk * 4;
     return bytes;

@@ -275,6 +275,40 @@ template <int ROWS, int COLS> struct Tile4 {
     }
 };
 
+// Rows of a [.., H, D] input tensor kept in registers as loaded (fp32 or bf16 bits) with their
+// row masks, converted only when written to LDS: nothing waits for the loads until then.
+template <int ROWS, int COLS, typename TI> struct InTile {
+    static constexpr int N = ROWS * COLS / 4 / kNT;
+    static_assert(N * 4 * kNT == ROWS * COLS, "tile must split evenly over the threads");
+    using Raw = typename std::conditional<std::is_same<TI, float>::value, float4, uint2>::type;
+    Raw x[N];
+    float m[N];
+    __device__ __forceinline__ void load(const TI *src, size_t row0, int H, int h, int c0, int D,
+                                         int L, float mul) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int idx = (i * kNT + threadIdx.x) * 4, r = idx / COLS, c = idx - r * COLS;
+            x[i] = *reinterpret_cast<const Raw *>(src + ((row0 + min(r, L - 1)) * H + h) * D + c0 + c);
+            m[i] = r < L ? mul : 0.f;
+        }
+    }
+    __device__ __forceinline__ void store4(float *dst, int ld) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int idx = (i * kNT + threadIdx.x) * 4, r = idx / COLS, c = idx - r * COLS;
+            float4 f;
+            if constexpr (std::is_same<TI, float>::value) {
+                f = x[i];
+            } else {
+                f = make_float4(__uint_as_float(x[i].x << 16), __uint_as_float(x[i].x & 0xffff0000u),
+                                __uint_as_float(x[i].y << 16), __uint_as_float(x[i].y & 0xffff0000u));
+            }
+            *reinterpret_cast<float4 *>(dst + r * ld + c) =
+                make_float4(m[i] * f.x, m[i] * f.y, m[i] * f.z, m[i] * f.w);
+        }
+    }
+};
+
 // A ROWS x COLS tile of a row-major record matrix kept in registers as stored (fp16 or fp32),
 // 4 elements per 8- or 16-byte load, written to LDS as fp32.
 template <int ROWS, int COLS, typename RT, int E = 4> struct TileR {  // E elements per load
@@ -546,7 +580,7 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
         struct Set {
             TileR<kC, kC, RT, HP ? 8 : 4> P;  // 16-byte loads for fp16 records
             TileR<kC, DK, RT, HP ? 8 : 4> K, G, W;
-            Tile4<kC, 16> O;
+            InTile<kC, 16, TD> O;
             float el;
         } sa, sb;
         auto fetch = [&](Set &x, int c) {
@@ -556,7 +590,7 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
             x.K.load(R + F::OFF_KT, DK);
             x.G.load(R + F::OFF_GQ, DK);
             x.W.load(R + F::OFF_W, DK);
-            x.O.load_in(dO, static_cast<size_t>(b) * T + c * kC, Hv, hv, col0, DV,
+            x.O.load(dO, static_cast<size_t>(b) * T + c * kC, Hv, hv, col0, DV,
                         min(kC, T - c * kC), scale);
             x.el = vload1(elp(c));
         };
@@ -566,7 +600,7 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
             x.K.store_raw(sM1, L4);   // A
             x.G.store_raw(sM2, L16);  // A transposed
             x.W.store_raw(sM3, L16);  // A transposed
-            x.O.store(sO, 16);
+            x.O.store4(sO, 16);
             el = x.el;
         };
         auto step = [&](int c) {

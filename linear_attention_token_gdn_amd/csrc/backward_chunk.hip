@@ -582,17 +582,28 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
             TileR<kC, DK, RT, HP ? 8 : 4> K, G, W;
             InTile<kC, 16, TD> O;
             float el;
-        } sa, sb;
-        auto fetch = [&](Set &x, int c) {
+        } s0, s1, s2;
+        // chunk c's loads in three parts, issued at three points of an earlier chunk's step so
+        // that the wavefronts never stall on a long burst of load issues
+        auto fetch_part = [&](Set &x, int c, int part) {
             c = max(c, 0);
             const RT *R = recp(c);
-            x.P.load(R + F::OFF_P, kC);
-            x.K.load(R + F::OFF_KT, DK);
-            x.G.load(R + F::OFF_GQ, DK);
-            x.W.load(R + F::OFF_W, DK);
-            x.O.load(dO, static_cast<size_t>(b) * T + c * kC, Hv, hv, col0, DV,
-                        min(kC, T - c * kC), scale);
-            x.el = vload1(elp(c));
+            if (part == 0) {
+                x.P.load(R + F::OFF_P, kC);
+                x.O.load(dO, static_cast<size_t>(b) * T + c * kC, Hv, hv, col0, DV,
+                         min(kC, T - c * kC), scale);
+                x.el = vload1(elp(c));
+            } else if (part == 1) {
+                x.K.load(R + F::OFF_KT, DK);
+                x.G.load(R + F::OFF_GQ, DK);
+            } else {
+                x.W.load(R + F::OFF_W, DK);
+            }
+        };
+        auto fetch = [&](Set &x, int c) {
+            fetch_part(x, c, 0);
+            fetch_part(x, c, 1);
+            fetch_part(x, c, 2);
         };
         float el = 0.f;
         auto put = [&](const Set &x) {
@@ -603,9 +614,11 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
             x.O.store4(sO, 16);
             el = x.el;
         };
-        auto step = [&](int c) {
+        // step c, loading chunk c - 3 into the free set `ld` on the way
+        auto step = [&](int c, Set &ld) {
             lds_bar();
             save_state(dSe + (static_cast<size_t>(chain) * nch + c) * SS);
+            fetch_part(ld, c - 3, 0);
             // dDelta = P^T dO' + Kt dS: wavefront w, rows 16w..
             {
                 f32x4 d = mfma_p<HP, true>(z4, sP + 16 * w, 1, LP, sO, 16, 1, kC);
@@ -613,6 +626,7 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sD[(16 * w + 4 * kq + i) * 16 + mi] = d[i];
             }
+            fetch_part(ld, c - 3, 1);
             lds_bar();
             // dS <- e^gamma_last dS + (Gm Q)^T dO' - W^T dDelta
 #pragma unroll
@@ -626,20 +640,26 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
                     y = el * y + u[i] - x[i];
                 }
             }
+            fetch_part(ld, c - 3, 2);
             lds_bar();
         };
-        fetch(sa, nch - 1);
-        put(sa);
-        fetch(sa, nch - 2);
-        fetch(sb, nch - 3);
-        for (int c = nch - 1; c >= 0; c -= 2) {
-            step(c);
-            put(sa);  // chunk c - 1
-            fetch(sa, c - 3);
+        // Three sets in rotation: while chunk c is computed, chunk c - 1's set waits to be
+        // written to LDS, chunk c - 2's loads are in flight and chunk c's set (already in LDS)
+        // receives chunk c - 3.  Constant set names only (no indexed register arrays).
+        fetch(s0, nch - 1);
+        put(s0);
+        fetch(s1, nch - 2);
+        fetch(s2, nch - 3);
+        for (int c = nch - 1; c >= 0; c -= 3) {
+            step(c, s0);
+            put(s1);  // chunk c - 1
             if (c - 1 >= 0) {
-                step(c - 1);
-                put(sb);  // chunk c - 2
-                fetch(sb, c - 4);
+                step(c - 1, s1);
+                put(s2);  // chunk c - 2
+            }
+            if (c - 2 >= 0) {
+                step(c - 2, s2);
+                put(s0);  // chunk c - 3
             }
         }
         bar();

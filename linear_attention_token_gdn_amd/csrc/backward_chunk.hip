@@ -512,22 +512,34 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
     auto recp = [&](int c) { return rec_at<RT>(rec, static_cast<size_t>(chain) * nch + c, F::REC); };
     auto elp = [&](int c) { return reinterpret_cast<const float *>(recp(c) + F::OFF_EL); };
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-    // The operands of chunks c + 1 and c + 2 are in registers (two sets, alternating) while
-    // chunk c is computed, and are written to LDS at the end of a step: the sequential chain
-    // waits for no record fetch as long as a fetch takes less than two steps.
+    // The operands of the next three chunks are in registers (three sets in rotation) while
+    // chunk c is computed: the next chunk's set waits to be written to LDS at the end of the
+    // step, the one after is in flight, and the third is being loaded -- in three parts, at
+    // three points of the step, so that no wavefront stalls on a long burst of load issues.
+    // The sequential chain waits for no record fetch as long as a fetch takes under two steps.
     if (fwd) {
         struct Set {
             TileR<kC, DK, RT, HP ? 8 : 4> W, K;  // 16-byte loads for fp16 records
             TileR<kC, 16, RT> U;
             float el;
-        } sa, sb;
-        auto fetch = [&](Set &x, int c) {
+        } s0, s1, s2;
+        // chunk c's loads in three parts, issued at three points of an earlier chunk's step
+        auto fetch_part = [&](Set &x, int c, int part) {
             c = min(c, nch - 1);
             const RT *R = recp(c);
-            x.W.load(R + F::OFF_W, DK);
-            x.K.load(R + F::OFF_KT, DK);
-            x.U.load(R + F::OFF_U + col0, DV);
-            x.el = vload1(elp(c));
+            if (part == 0) {
+                x.U.load(R + F::OFF_U + col0, DV);
+                x.el = vload1(elp(c));
+            } else if (part == 1) {
+                x.K.load(R + F::OFF_KT, DK);
+            } else {
+                x.W.load(R + F::OFF_W, DK);
+            }
+        };
+        auto fetch = [&](Set &x, int c) {
+            fetch_part(x, c, 0);
+            fetch_part(x, c, 1);
+            fetch_part(x, c, 2);
         };
         float el = 0.f;
         auto put = [&](const Set &x) {
@@ -536,9 +548,11 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
             x.U.store(sO, 16);
             el = x.el;
         };
-        auto step = [&](int c) {
+        // step c, loading chunk c + 3 into the free set `ld` on the way
+        auto step = [&](int c, Set &ld) {
             lds_bar();
             save_state(Sc + (static_cast<size_t>(chain) * nch + c) * SS);
+            fetch_part(ld, c + 3, 0);
             // Delta = U - W S: wavefront w, rows 16w..16w+15
             {
                 const f32x4 d = mfma_p<HP, true>(z4, sM1 + 16 * w * L4, L4, 1, sS, 16, 1, DK);
@@ -548,6 +562,7 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
                     sD[o] = sO[o] - d[i];
                 }
             }
+            fetch_part(ld, c + 3, 1);
             lds_bar();
             // S <- e^gamma_last S + Kt^T Delta: row blocks w, w + 4, ...
 #pragma unroll
@@ -560,20 +575,24 @@ bscan_kernel(const float *__restrict__ rec, const TD *__restrict__ dO,
                     x = el * x + u[i];
                 }
             }
+            fetch_part(ld, c + 3, 2);
             lds_bar();
         };
-        fetch(sa, 0);
-        put(sa);
-        fetch(sa, 1);
-        fetch(sb, 2);
-        for (int c = 0; c < nch; c += 2) {
-            step(c);
-            put(sa);  // chunk c + 1
-            fetch(sa, c + 3);
+        // three sets in rotation, as in the reverse chain below
+        fetch(s0, 0);
+        put(s0);
+        fetch(s1, 1);
+        fetch(s2, 2);
+        for (int c = 0; c < nch; c += 3) {
+            step(c, s0);
+            put(s1);  // chunk c + 1
             if (c + 1 < nch) {
-                step(c + 1);
-                put(sb);  // chunk c + 2
-                fetch(sb, c + 4);
+                step(c + 1, s1);
+                put(s2);  // chunk c + 2
+            }
+            if (c + 2 < nch) {
+                step(c + 2, s2);
+                put(s0);  // chunk c + 3
             }
         }
     } else {

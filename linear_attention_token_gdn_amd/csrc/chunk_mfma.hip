@@ -273,41 +273,48 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         if (c + 1 < nchunks) prefetch(c + 1);
         lds_barrier();
 
-        // ---- stage 1: KK^T -> A, QK^T -> P (lower-triangular 16x16 tiles), and K^T.  The
-        //      2 NR (NR + 1) / 2 tiles are dealt to the wavefronts one by one (a row tile has
-        //      rt + 1 of them, so whole row tiles per wavefront would leave most of them idle
-        //      while the last row's wavefronts finish)
-        constexpr int NT1 = NR * (NR + 1) / 2;
-        for (int it = wave; it < 2 * NT1; it += F::NW) {
-            const bool isq = it >= NT1;
-            const int t = isq ? it - NT1 : it;
-            int rt = 0;
-            while ((rt + 1) * (rt + 2) / 2 <= t) ++rt;
-            const int st = t - rt * (rt + 1) / 2;
+        // ---- stage 1: KK^T -> A, QK^T -> P (lower-triangular 16x16 tiles), and K^T
+        for (int job = wave; job < 2 * NR; job += F::NW) {
+            const bool isq = job >= NR;
+            const int rt = isq ? job - NR : job;
             const f16 *arow = isq ? &sm.q[16 * rt + li][0] : &sm.k[16 * rt + li][0];
-            f32x4 acc = zero4();
+            f16x8 af[F::KD];
 #pragma unroll
             for (int kk = 0; kk < F::KD; ++kk)
-                acc = mma_k32(*reinterpret_cast<const f16x8 *>(arow + 32 * kk + 8 * lg),
-                              *reinterpret_cast<const f16x8 *>(&sm.k[16 * st + li][32 * kk + 8 * lg]),
-                              acc);
-            const int s = 16 * st + li;
-            const float gs = sm.gam[s];
+                af[kk] = *reinterpret_cast<const f16x8 *>(arow + 32 * kk + 8 * lg);
+            float gr[4], br[4];
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const int r = 16 * rt + 4 * lg + rr;
-                const float d = (s <= r) ? __expf(sm.gam[r] - gs) : 0.f;
-                if (isq) {
-                    sm.p[r][kperm(s)] = f16(acc[rr] * d);
-                } else {
-                    const float av = (s < r) ? sm.bet[r] * d * acc[rr] : 0.f;
-                    if (st == rt)
-                        sm.ad[rt][4 * lg + rr][li] = av;
-                    else
-                        sm.an[r][s] = f16(-av);
+                gr[rr] = sm.gam[16 * rt + 4 * lg + rr];
+                br[rr] = sm.bet[16 * rt + 4 * lg + rr];
+            }
+#pragma unroll
+            for (int st = 0; st < NR; ++st) {
+                if (st > rt) break;
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int kk = 0; kk < F::KD; ++kk)
+                    acc = mma_k32(af[kk],
+                                  *reinterpret_cast<const f16x8 *>(&sm.k[16 * st + li][32 * kk + 8 * lg]),
+                                  acc);
+                const int s = 16 * st + li;
+                const float gs = sm.gam[s];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int r = 16 * rt + 4 * lg + rr;
+                    const float d = (s <= r) ? __expf(gr[rr] - gs) : 0.f;
+                    if (isq) {
+                        sm.p[r][kperm(s)] = f16(acc[rr] * d);
+                    } else {
+                        const float av = (s < r) ? br[rr] * d * acc[rr] : 0.f;
+                        if (st == rt)
+                            sm.ad[rt][4 * lg + rr][li] = av;
+                        else
+                            sm.an[r][s] = f16(-av);
+                    }
                 }
             }
-            if (isq && st == rt && rt + 1 < NR) {  // the tile right of the diagonal is read by P Delta
+            if (isq && rt + 1 < NR) {  // the tile right of the diagonal is read by P Delta
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr)
                     sm.p[16 * rt + 4 * lg + rr][kperm(16 * (rt + 1) + li)] = f16(0.f);

@@ -412,12 +412,20 @@ bprep_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
     for (int i = tid; i < kC * LC4; i += kNT) sT[i] = 0.f;
     bar();
     if (tid < kC) {
+        // column j of the inverse of diagonal block o, in registers: x_r = [r == j] -
+        // sum_{s<r} A_rs x_s (x_s = 0 for s < j, so the terms below j add nothing); the block's
+        // entries of A are read as broadcasts, independently of x
         const int o = 16 * (tid >> 4), j = tid & 15;
-        for (int r = j; r < 16; ++r) {
-            float x = r == j ? 1.f : 0.f;
-            for (int s = j; s < r; ++s) x -= sA[(o + r) * LC1 + o + s] * sT[(o + s) * LC4 + o + j];
-            sT[(o + r) * LC4 + o + j] = x;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = r == j ? 1.f : 0.f;
+#pragma unroll
+            for (int s = 0; s < r; ++s) acc -= sA[(o + r) * LC1 + o + s] * x[s];
+            x[r] = acc;
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sT[(o + r) * LC4 + o + j] = x[r];
     }
     bar();
     for (int bi = 1; bi < 4; ++bi) {

@@ -710,7 +710,9 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
              float scale) {
     using F = CB<DK, DV>;
     constexpr bool HP = std::is_same<TI, bf16_t>::value;  // fp16 operands for bf16 inputs
-    constexpr int SW = 16, NSL = DV / SW, NBK = DK / 16;
+    // value slices of SW = 32 columns (CT = 2 tiles of 16): the products summed over the
+    // slice's columns run as 16x16x32 MFMAs, and a chunk takes DV / 32 slice steps
+    constexpr int SW = 32, CT = SW / 16, NSL = DV / SW, NBK = DK / 16;
     constexpr int LK4 = DK + 4, LC16 = kC + 16, LC4 = kC + 4, LS = SW + 4;
     constexpr int P1 = kC * LK4 + 2 * DK * LS + 4 * kC * LS;  // W + one value slice
     constexpr int P2 = 3 * kC * LK4;                          // K, Q, dW / (dKK + dKK^T)
@@ -766,7 +768,7 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
     // (the barriers below wait for LDS only, so they do not wait for those loads)
     Tile4<DK, SW> t0s, tes;
     Tile4<kC, SW> tos, tvs;
-    float uf[4];  // U of this lane's rows in the slice's column
+    float uf[CT][4];  // U of this lane's rows in the slice's columns 16 ct + mi
     auto fetch = [&](int j) {
         const int cj = SW * j;
         t0s.load(S0 + cj, DV);
@@ -774,7 +776,10 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
         tos.load_in(dO, row0, Hv, hv, cj, DV, L, scale);
         tvs.load_in(v, row0, Hv, hv, cj, DV, L);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) uf[i] = static_cast<float>(R[F::OFF_U + (rb + i) * DV + cj + mi]);
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                uf[ct][i] = static_cast<float>(R[F::OFF_U + (rb + i) * DV + cj + 16 * ct + mi]);
     };
     // Kt's row block w, the A operand of one product in every slice: read once.  With it and U
     // fetched with the tiles, no global load is waited for inside a slice except the next
@@ -782,6 +787,7 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
     AFrag<HP, DK> ktw;
     ktw.load(R + F::OFF_KT + 16 * w * DK, DK);
     fetch(0);
+#pragma unroll  // constant indices everywhere: the tiles stay in registers
     for (int j = 0; j < NSL; ++j) {
         const int cj = SW * j;
         lds_bar();  // the previous slice's buffers are free
@@ -789,37 +795,41 @@ bgrad_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__res
         tes.store4(sSe, LS);
         tos.store4(sO, LS);
         tvs.store4(sVv, LS);
-        float u[4];
+        float u[CT][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) u[i] = uf[i];
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) u[ct][i] = uf[ct][i];
         if (j + 1 < NSL) fetch(j + 1);
         lds_bar();
-        // Delta = U - W S0 ; dDelta = P^T dO' + Kt dSe   (row block w, 16 columns)
-        {
-            const f32x4 d = mfma_p<HP>(z4, sW + 16 * w * LK4, LK4, 1, sS0, LS, 1, DK);
-            f32x4 e = mfma_p<HP>(z4, sPY + 16 * w, 1, LC16, sO, LS, 1, kC);
-            e = mfma_pre<HP, DK>(e, ktw, sSe, LS, 1);
+        // Delta = U - W S0 ; dDelta = P^T dO' + Kt dSe   (row block w, column tile ct)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            const f32x4 d = mfma_p<HP>(z4, sW + 16 * w * LK4, LK4, 1, sS0 + 16 * ct, LS, 1, DK);
+            f32x4 e = mfma_p<HP>(z4, sPY + 16 * w, 1, LC16, sO + 16 * ct, LS, 1, kC);
+            e = mfma_pre<HP, DK>(e, ktw, sSe + 16 * ct, LS, 1);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = rb + i;
-                sD[r * LS + mi] = u[i] - d[i];
-                sdD[r * LS + mi] = e[i];
+                sD[r * LS + 16 * ct + mi] = u[ct][i] - d[i];
+                sdD[r * LS + 16 * ct + mi] = e[i];
             }
         }
         for (int i = tid; i < DK * SW; i += kNT)
             dglast += sS0[(i / SW) * LS + i % SW] * sSe[(i / SW) * LS + i % SW];
         lds_bar();
         // dBv = Tm^T dDelta -> dv = beta dBv, dbeta += rowsum(dBv o V)
-        {
-            const f32x4 x = mfma_p<HP>(z4, sT + 16 * w, 1, LC16, sdD, LS, 1, kC);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            const f32x4 x = mfma_p<HP>(z4, sT + 16 * w, 1, LC16, sdD + 16 * ct, LS, 1, kC);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = rb + i;
-                if (r < L) dv_out[((row0 + r) * Hv + hv) * DV + cj + mi] = sbeta[r] * x[i];
-                dbv[i] += row_sum<16>(x[i] * sVv[r * LS + mi]);
+                if (r < L) dv_out[((row0 + r) * Hv + hv) * DV + cj + 16 * ct + mi] = sbeta[r] * x[i];
+                dbv[i] += row_sum<16>(x[i] * sVv[r * LS + 16 * ct + mi]);
             }
         }
-        // the partial sums over this slice's value columns (K = 16)
+        // the partial sums over this slice's value columns (K = SW)
 #pragma unroll
         for (int bj = 0; bj < NBK; ++bj) {
             aGQ[bj] = mfma_p<HP>(aGQ[bj], sO + 16 * w * LS, LS, 1, sS0 + 16 * bj * LS, 1, LS, SW);

@@ -49,12 +49,15 @@ decode_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__re
               float *state_out, TO *__restrict__ o, int T, int Hk, int Hv, float scale,
               unsigned flags) {
     using Sh = DecodeShape<DK, DV>;
-    __shared__ float red_e[Sh::NW][DV];
-    __shared__ float red_f[Sh::NW][DV];
-    __shared__ float red_kq[Sh::NW];
-    __shared__ __attribute__((aligned(16))) float w_sh[DV];
+    // per-wavefront partial sums, double-buffered by token parity: each thread forms w for
+    // its own four columns from them, so one barrier per token suffices (token t + 2 reuses a
+    // buffer only after every thread has passed token t + 1's barrier, i.e. finished reading)
+    __shared__ __attribute__((aligned(16))) float red_e[2][Sh::NW][DV];
+    __shared__ __attribute__((aligned(16))) float red_f[2][Sh::NW][DV];
+    __shared__ float red_kq[2][Sh::NW];
     // the current block of tokens' inputs, fp32
-    __shared__ float t_k[kTokBlock][DK], t_q[kTokBlock][DK], t_v[kTokBlock][DV];
+    __shared__ __attribute__((aligned(16))) float t_k[kTokBlock][DK], t_q[kTokBlock][DK],
+        t_v[kTokBlock][DV];
     __shared__ float t_alpha[kTokBlock], t_beta[kTokBlock];
 
     const int head = blockIdx.x;  // b * Hv + hv
@@ -82,7 +85,8 @@ decode_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__re
     for (int t0 = 0; t0 < T; t0 += kTokBlock) {
         const int nt = MULTI ? min(kTokBlock, T - t0) : 1;
         // a single token reads its inputs straight into registers (no staging barrier)
-        float kr1[Sh::RPT], qr1[Sh::RPT], v1 = 0.f, a1 = 0.f, b1 = 0.f;
+        float kr1[Sh::RPT], qr1[Sh::RPT], a1 = 0.f, b1 = 0.f;
+        f32x4 v1 = {0.f, 0.f, 0.f, 0.f};  // columns 4 cg .. 4 cg + 3
         if constexpr (!MULTI) {
 #pragma unroll
             for (int m = 0; m < Sh::RPT; ++m) {
@@ -93,10 +97,12 @@ decode_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__re
             const size_t gi = tok0 * Hv + hv;
             a1 = expf(log_alpha_from_input(load_f32(g + gi), flags));
             b1 = beta_from_input(load_f32(beta + gi), flags);
-            if (tid < DV) v1 = load_f32(v + gi * DV + tid);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v1[c] = load_f32(v + gi * DV + 4 * cg + c);
         }
         // ---- stage the block's inputs (all loads of the block in flight together)
         if constexpr (MULTI) {
+        if (t0 > 0) lds_barrier();  // the previous block's last token is done reading t_*
         for (int i = tid; i < nt * DK; i += Sh::NT) {
             const int tt = i / DK, c = i - tt * DK;
             const size_t off = ((tok0 + t0 + tt) * Hk + hq) * DK + c;
@@ -155,31 +161,35 @@ decode_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__re
             }
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) kq += __shfl_xor(kq, off);
+            const int pb = (t0 + tt) & 1;
             if (lane < Sh::CG) {
-                red_e[wave][4 * cg + 0] = e.x; red_e[wave][4 * cg + 1] = e.y;
-                red_e[wave][4 * cg + 2] = e.z; red_e[wave][4 * cg + 3] = e.w;
-                red_f[wave][4 * cg + 0] = f.x; red_f[wave][4 * cg + 1] = f.y;
-                red_f[wave][4 * cg + 2] = f.z; red_f[wave][4 * cg + 3] = f.w;
+                *reinterpret_cast<f32x4 *>(&red_e[pb][wave][4 * cg]) = e;
+                *reinterpret_cast<f32x4 *>(&red_f[pb][wave][4 * cg]) = f;
             }
-            if (lane == 0) red_kq[wave] = kq;
+            if (lane == 0) red_kq[pb][wave] = kq;
             lds_barrier();
 
+            // w for this thread's columns (every row group forms the same values)
             const float alpha = MULTI ? t_alpha[tt] : a1;
-            if (tid < DV) {
-                float ej = 0.f, fj = 0.f, kqs = 0.f;
+            const float bt = MULTI ? t_beta[tt] : b1;
+            const f32x4 vv = MULTI ? *reinterpret_cast<const f32x4 *>(&t_v[tt][4 * cg]) : v1;
+            f32x4 ej = {0.f, 0.f, 0.f, 0.f}, fj = ej;
+            float kqs = 0.f;
 #pragma unroll
-                for (int w = 0; w < Sh::NW; ++w) {
-                    ej += red_e[w][tid];
-                    fj += red_f[w][tid];
-                    kqs += red_kq[w];
-                }
-                const float wj = MULTI ? t_beta[tt] * (t_v[tt][tid] - alpha * ej) : b1 * (v1 - alpha * ej);
-                w_sh[tid] = wj;
-                store_f32(o + ((tok0 + t0 + tt) * Hv + hv) * DV + tid, scale * (alpha * fj + kqs * wj));
+            for (int w = 0; w < Sh::NW; ++w) {
+                ej += *reinterpret_cast<const f32x4 *>(&red_e[pb][w][4 * cg]);
+                fj += *reinterpret_cast<const f32x4 *>(&red_f[pb][w][4 * cg]);
+                kqs += red_kq[pb][w];
             }
-            lds_barrier();  // also: every read of red_* above is done before the next token
-
-            const f32x4 w4 = reinterpret_cast<const f32x4 *>(w_sh)[cg];
+            f32x4 w4;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) w4[c] = bt * (vv[c] - alpha * ej[c]);
+            if (rg == 0) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    store_f32(o + ((tok0 + t0 + tt) * Hv + hv) * DV + 4 * cg + c,
+                              scale * (alpha * fj[c] + kqs * w4[c]));
+            }
 #pragma unroll
             for (int m = 0; m < Sh::RPT; ++m) {
                 s[m].x = alpha * s[m].x + kr[m] * w4.x;
@@ -188,8 +198,6 @@ decode_kernel(const TI *__restrict__ q, const TI *__restrict__ k, const TI *__re
                 s[m].w = alpha * s[m].w + kr[m] * w4.w;
             }
         }
-        // the next block overwrites the staged inputs: the last token's barrier above already
-        // ordered every read of t_* before this point
     }
     f32x4 *So = reinterpret_cast<f32x4 *>(state_out + sbase);
 #pragma unroll

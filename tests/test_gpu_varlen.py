@@ -224,3 +224,33 @@ def test_decode_tokens_with_prologue(T, flags):
                                s0=s0, scale=1.1, flags=flags)
     check(o.cpu().numpy().reshape(B * T, Hv, d), ro, "bf16", "decode prologue o T=%d" % T)
     check(S.cpu().numpy(), rS, "bf16", "decode prologue state T=%d" % T)
+
+
+@pytest.mark.parametrize("variant", ["split", "fused", "recurrent"])
+def test_malformed_offsets_stay_in_bounds(variant, monkeypatch):
+    """Offsets that decrease or leave [0, T] are clamped on the device: the call succeeds, every
+    access stays inside the tensors (and the split plan's record slots inside the workspace).
+    The per-chain kernels give each sequence the recurrence over its clamped range
+    a = clamp(cu[i], 0, T), b = min(max(cu[i+1], a), T).  The split plan's record slots of
+    overlapping sequences coincide (sequences 1 and 3 here), so there only sequence 0, whose
+    slots no other sequence claims, is checked.  Clamped ranges overlap, so the rows of o
+    (written by several sequences) are only checked to be finite."""
+    monkeypatch.setenv("GDN_FORCE_VARIANT", variant)
+    gdn = gdn_mod()
+    T, Hk, Hv, d = 300, 1, 2, 64
+    cu = np.array([0, 120, 80, 400, -5, 300], dtype=np.int64)
+    N = len(cu) - 1
+    x, s0 = raw_inputs((T,), Hk, Hv, d, d, ALL, "bf16", 760, (N, Hv, d, d))
+    t = to_dev(x, "bf16")
+    o, sT = gdn.chunk_fwd_varlen(t["q"], t["k"], t["v"], t["beta"], t["g"],
+                                 cu_seqlens=torch.from_numpy(cu.astype(np.int32)).to(DEV),
+                                 initial_state=torch.from_numpy(s0).to(DEV), chunk=64, flags=ALL)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
+    for i in (range(1) if variant == "split" else range(N)):
+        a = min(max(int(cu[i]), 0), T)
+        b = min(max(int(cu[i + 1]), a), T)
+        sl = {n: arr[a:b] for n, arr in x.items()}
+        _, rS = oracle.run_packed(sl["q"], sl["k"], sl["v"], sl["beta"], sl["g"],
+                                  np.array([0, b - a]), s0=s0[i:i + 1], flags=ALL)
+        check(sT[i:i + 1].cpu().numpy(), rS, "bf16", "clamped sequence %d state %s" % (i, variant))

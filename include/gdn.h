@@ -193,8 +193,8 @@ gdn_status_t gdn_decode_tokens(const void *q, const void *k, const void *v, cons
  *                and has its own state: initial_state / final_state [num_seqs, Hv, dk, dv]
  *                fp32.  Chunks never cross a sequence boundary; a sequence of length 0 gets
  *                final = initial.  The offsets are not read on the host: offsets outside
- *                [0, T] or decreasing are clamped on the device (wrong lengths, but no access
- *                outside the tensors).
+ *                [0, T] or decreasing are clamped on the device (wrong results for the
+ *                sequences concerned, but no access outside the tensors or the workspace).
  *   flags        GDN_QK_L2NORM | GDN_BETA_LOGIT | GDN_G_LOGIT | GDN_PREFER_SPLIT (or 0);
  *                other bits are invalid
  *

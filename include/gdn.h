@@ -122,10 +122,16 @@ const char *gdn_chunk_fwd_plan(int B, int T, int Hk, int Hv, int dk, int dv, int
  * (or zeros) and nothing else.  B = 0 is a no-op.
  *
  * Precision: bf16 inputs run on the matrix cores with fp16 (or bf16) operands and fp32
- * accumulation -- q and k (unit rows) and v are converted to fp16, so v must lie within fp16
- * range; derived operands (U, W, the state S, Delta, P) are rounded to fp16 for each product;
- * every sum and the fp32 state itself are never rounded.  fp32 inputs run the token-recurrent
- * kernel in fp32.
+ * accumulation.  q and k are taken as fp16 copies (exact for unit rows, whose entries are at
+ * most 1 in magnitude; rows far from unit norm with entries beyond fp16 range are outside the
+ * method's use and would overflow).  Derived operands (U, W, the state S, Delta, P) are
+ * rounded to fp16 for each product; every sum and the fp32 state itself are never rounded.
+ * The value side (v, U, Delta, S, o) is linear in (v, initial_state), so its fp16 copies carry
+ * a power of two per value column, chosen per chunk from the column's largest magnitude and
+ * taken back out of the fp32 results exactly: v and the state may have any magnitude that
+ * fp32 holds (the rounding is relative to each column's largest value in the chunk), and
+ * scaling v and initial_state by 2^n scales o and final_state by exactly 2^n.  fp32 inputs run
+ * the token-recurrent kernel in fp32.
  */
 gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v, const void *beta,
                            const void *g, const float *initial_state, void *o,

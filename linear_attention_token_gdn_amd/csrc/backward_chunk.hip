@@ -14,7 +14,9 @@
 // dTm = dU (beta V)^T + dW (beta Gm K)^T, dA = -strictly_lower(Tm^T dTm Tm^T), the decay
 // matrices through gamma, gamma through a reverse cumulative sum into dg).
 //
-// Four kernels, all in fp32:
+// Three kernels.  fp32 inputs compute in fp32 throughout (fp32 matrix-core products); bf16
+// inputs keep the per-chunk records in fp16 and take fp16 operands with fp32 accumulation on
+// the matrix cores, while the states, e^gamma_last and every sum stay fp32:
 //   bprep_kernel  per (chain, chunk): Tm, U, W, Kt, Gm Q, P, e^gamma_last -> records
 //   bscan_kernel  per (chain, 16 state columns): the forward chain of chunk-start states and,
 //                 in the other half of the grid, the reverse chain of chunk-end gradients dS

@@ -20,7 +20,7 @@
 //   * The D x D fp32 state lives in MFMA accumulator registers for the whole sequence;
 //     wavefront w owns value columns [16w, 16w + 16).
 //   * Q, K, V of the next chunk are prefetched into registers while the current chunk runs,
-//     then staged in LDS as fp16 (exact for normalised q/k; v must stay inside fp16 range).
+//     then staged in LDS: q and k as fp16 (exact for unit rows), v as stored (bf16).
 //   * KK^T and QK^T: v_mfma_f32_16x16x32_f16 on exact inputs, fp32 accumulation.
 //   * (I + A)^-1 is never formed: the 16x16 diagonal blocks are inverted in fp32 by forward
 //     substitution, and U, W come from a blocked forward substitution over 16-row blocks,
@@ -28,7 +28,11 @@
 //     solves its own two 16-column panels (of diag(beta) V and diag(beta e^gamma) K), so the
 //     solve needs no barrier.
 //   * Derived fp32 operands (W, S, Delta, P, X) are rounded to fp16 for the MFMAs; every sum
-//     accumulates in fp32 and the fp32 state itself is never rounded.
+//     accumulates in fp32 and the fp32 state itself is never rounded.  The value side (U,
+//     Delta, S, O) is linear in (v, S0) and column-separable, so each wavefront scales its
+//     columns' fp16 copies by a power of two chosen per chunk from the column's largest |S|
+//     and |beta v| (pow2_scale) and takes the scale back out of the fp32 results exactly: no
+//     magnitude of v or S0 overflows fp16 or sinks into its subnormals.
 //   * The accumulator layout (lane l holds rows 4(l/16)..4(l/16)+3 of column l%16) is fed
 //     straight back as a B operand, with the k index of the A operand permuted to match, so
 //     the state and the solve panels never leave registers.
@@ -108,7 +112,7 @@ template <int D, int C> struct Smem {
     f16 q[C][F::PQ];          // Q rows (columns permuted)
     f16 k[C][F::PQ];          // K rows (columns permuted)
     f16 kt[D][F::PT];         // K^T (columns permuted)
-    f16 v[C][F::PV];          // V rows
+    bf16_t v[C][F::PV];       // V rows (bf16, as stored)
     f16 p[C][F::PT];          // lower(Q K^T) o D (columns permuted)
     f16 wn[C][F::PQ];         // -W (columns permuted)
     f16 an[C][F::PA];         // -A, off-diagonal 16x16 blocks (lower)
@@ -230,12 +234,11 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                 qs = inv_norm_from_sumsq(qq);
                 ks = inv_norm_from_sumsq(kq);
             }
-            f16x8 qh, kh, vh;
+            f16x8 qh, kh;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 qh[e] = f16(qs * bf16_to_f32(pq[n][e]));
                 kh[e] = f16(ks * bf16_to_f32(pk[n][e]));
-                vh[e] = f16(bf16_to_f32(pv[n][e]));
             }
             // columns 8cc .. 8cc+7 are two runs of 4 in the permuted order
             const int c0 = kperm(cc * 8), c1 = kperm(cc * 8 + 4);
@@ -243,7 +246,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             *reinterpret_cast<f16x4 *>(&sm.q[r][c1]) = f16x4{qh[4], qh[5], qh[6], qh[7]};
             *reinterpret_cast<f16x4 *>(&sm.k[r][c0]) = f16x4{kh[0], kh[1], kh[2], kh[3]};
             *reinterpret_cast<f16x4 *>(&sm.k[r][c1]) = f16x4{kh[4], kh[5], kh[6], kh[7]};
-            *reinterpret_cast<f16x8 *>(&sm.v[r][cc * 8]) = vh;
+            *reinterpret_cast<u16x8 *>(&sm.v[r][cc * 8]) = pv[n];
         }
         if (wave == 0) {
             const int L = min(C, len - t0);  // rows past the end: g = beta = 0
@@ -347,6 +350,26 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         // ---- stage 3: blocked forward substitution for this wave's panels,
         //      U[:, 16w..] = (I+A)^-1 diag(beta) V[:, 16w..]  (kept in registers)
         //      W[:, 16w..] = (I+A)^-1 diag(beta e^gamma) K[:, 16w..]  (-W to LDS)
+        //      The value side of this column (U, Delta, S, O) is carried scaled by sig, a power
+        //      of two chosen from the column's largest |beta v| in the chunk and |S| at its start.
+        f32x4 yv[NR];
+        float vmax = 0.f;
+#pragma unroll
+        for (int a = 0; a < NR; ++a)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int r = 16 * a + 4 * lg + rr;
+                yv[a][rr] = sm.bet[r] * bf16_to_f32(sm.v[r][col]);
+                vmax = fmaxf(vmax, fabsf(yv[a][rr]));
+            }
+#pragma unroll
+        for (int it = 0; it < F::NI; ++it)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) vmax = fmaxf(vmax, fabsf(S[it][r]));
+        vmax = fmaxf(vmax, __shfl_xor(vmax, 16));  // the column's four lanes
+        vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
+        float sig, isig;
+        pow2_scale(vmax, sig, isig);
         f32x4 U[NR], Wp[NR];
 #pragma unroll
         for (int a = 0; a < NR; ++a) {
@@ -355,9 +378,8 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int r = 16 * a + 4 * lg + rr;
-                const float br = sm.bet[r];
-                yu[rr] = br * float(sm.v[r][col]);
-                yw[rr] = br * sm.Gam[r] * float(kv4[rr]);
+                yu[rr] = sig * yv[a][rr];
+                yw[rr] = sm.bet[r] * sm.Gam[r] * float(kv4[rr]);
             }
 #pragma unroll
             for (int cb = 0; cb < a; ++cb) {
@@ -375,16 +397,16 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             for (int rr = 0; rr < 4; ++rr) sm.wn[16 * a + 4 * lg + rr][kperm(col)] = f16(-Wp[a][rr]);
         lds_barrier();
 
-        // ---- stage 4 (sequential part): Delta, O, next state
-        // S as fp16 B operands over the key index: slot e < 4 -> tile 2kk row 4lg+e,
+        // ---- stage 4 (sequential part): Delta, O, next state -- U, Delta, O scaled by sig
+        // sig S as fp16 B operands over the key index: slot e < 4 -> tile 2kk row 4lg+e,
         // slot e >= 4 -> tile 2kk+1 row 4lg+e-4.  A operands read the matching k indices.
         f16x8 bS[F::KD];
 #pragma unroll
         for (int kk = 0; kk < F::KD; ++kk)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                bS[kk][e] = f16(S[2 * kk][e]);
-                bS[kk][4 + e] = f16(S[2 * kk + 1][e]);
+                bS[kk][e] = f16(sig * S[2 * kk][e]);
+                bS[kk][4 + e] = f16(sig * S[2 * kk + 1][e]);
             }
         // Delta = U + (-W) S   (accumulated onto U);  O = diag(e^gamma) Q S
         f32x4 O[NR];
@@ -415,6 +437,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                 bDs[kk][4 + e] = f16(d1 * sm.dec[s1i]);
             }
         // O += P Delta, staged for the store at the top of the next chunk
+        const float oscale = scale * isig;  // exact: isig is a power of two
 #pragma unroll
         for (int rt = 0; rt < NR; ++rt) {
 #pragma unroll
@@ -423,10 +446,11 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                     O[rt] = mma_k32(*reinterpret_cast<const f16x8 *>(&sm.p[16 * rt + li][32 * kk + 8 * lg]),
                                     bD[kk], O[rt]);
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) sm.ost[16 * rt + 4 * lg + rr][col] = scale * O[rt][rr];
+            for (int rr = 0; rr < 4; ++rr) sm.ost[16 * rt + 4 * lg + rr][col] = oscale * O[rt][rr];
         }
-        // S = e^gamma_last S + K^T diag(e^(gamma_last - gamma)) Delta
-        const float GC = sm.Gam[C - 1];
+        // S = e^gamma_last S + K^T diag(e^(gamma_last - gamma)) Delta, formed as
+        // (sig e^gamma_last S + K^T diag(..) (sig Delta)) / sig: every scaling is exact
+        const float GC = sm.Gam[C - 1] * sig;
 #pragma unroll
         for (int it = 0; it < F::NI; ++it) {
             S[it] *= GC;
@@ -434,6 +458,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             for (int kk = 0; kk < F::KC; ++kk)
                 S[it] = mma_k32(*reinterpret_cast<const f16x8 *>(&sm.kt[16 * it + li][32 * kk + 8 * lg]),
                                 bDs[kk], S[it]);
+            S[it] *= isig;
         }
     }
 

@@ -16,6 +16,13 @@
 // parallelism: a chain of T/C chunks no longer waits for the per-chunk triangular solve,
 // which is what bounds a single-pass kernel when there are fewer chains than compute units.
 //
+// Range: U, the state S and Delta scale with v and S0, so their fp16 copies carry powers of
+// two (pow2_scale): prep scales each chunk's U by one chosen from the chunk's largest |v| and
+// stores the inverse next to e^gamma_last; the scan's state wavefronts scale their rows of S
+// per column, and every reader of Delta (kept in fp32 in LDS) scales it per column.  Every
+// fp32 sum is taken back to the true scale exactly, so no magnitude of v or S0 overflows fp16
+// or sinks into its subnormals.
+//
 // The workspace holds, per (chain, chunk), the scan kernel's MFMA operands already in
 // fragment order -- for every 16x16x32 A operand one 1 KiB block, lane-major, 16 bytes per
 // lane -- so each operand reaches the scan kernel's registers with one coalesced 16-byte load
@@ -193,6 +200,24 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             Vf[a][kk] &= m;
         }
     }
+    float usig, uisig;  // U is stored as f16(usig * U); 1/usig goes next to e^gamma_last
+    // ---- the chunk's largest |v| (bf16 magnitudes order as their bit patterns without the
+    //      sign) sets usig
+    {
+        u16x8 vm = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int a = 0; a < NR; ++a)
+#pragma unroll
+            for (int kk = 0; kk < KD; ++kk) vm = __builtin_elementwise_max(vm, Vf[a][kk] & (uint16_t)0x7fff);
+        unsigned m = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = max(m, static_cast<unsigned>(vm[e]));
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) m = max(m, static_cast<unsigned>(__shfl_xor(static_cast<int>(m), off)));
+        m = __builtin_amdgcn_readfirstlane(m);  // the same in every lane
+        pow2_scale(__uint_as_float(m << 16), usig, uisig);
+        if (lane == 0) gchunk[2 * (sp.rec0 + c) + 1] = uisig;
+    }
     if constexpr (NORM) {
         // row 16a + li is spread over the lanes li + 16 lg and the KD fragments of each
 #pragma unroll
@@ -235,7 +260,7 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         s_Gam[lane] = __expf(gv);
         s_dec[lane] = __expf(glast - gv);
         s_bet[lane] = bv;
-        if (lane == 0) gchunk[sp.rec0 + c] = __expf(glast);
+        if (lane == 0) gchunk[2 * (sp.rec0 + c)] = __expf(glast);
     }
     __syncthreads();
     // gate values in registers: accumulator-layout rows 16a + 4lg + rr (one 16-byte read
@@ -267,7 +292,7 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             for (int kk = 0; kk < KD; ++kk) acc = mma_kq(Kf[cb][kk], Kf[a][kk], acc);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const int s = 16 * cb + 4 * lg + rr;
+                    const int s = 16 * cb + 4 * lg + rr;
                 const float av = (s < r) ? betR[a] * __expf(gamR[a] - gamA[cb][rr]) * acc[rr] : 0.f;
                 if (cb == a)
                     s_adT[a][4 * lg + rr][li] = av;  // A[r][s] of the diagonal block, stored [s][r]
@@ -367,7 +392,7 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                 f32x4 yu, yw;
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
-                    yu[rr] = betA[a][rr] * Vt[rr];
+                    yu[rr] = usig * betA[a][rr] * Vt[rr];
                     yw[rr] = betA[a][rr] * GamA[a][rr] * Kt[rr];
                     kt[a][rr] = f16(decA[a][rr] * Kt[rr]);
                 }
@@ -534,8 +559,8 @@ __device__ void prefetch_records(const unsigned char *__restrict__ ws,
 template <int D, int C> struct ScanOps {  // one state wave's operands of one chunk
     f16x8 wf[SplitCfg<D, C>::NR];          // -W, rows 16a.., k-step w
     f16x8 kf[2][SplitCfg<D, C>::KC];       // K^T dec, row blocks 2w, 2w+1
-    f16x4 uf[ScanCfg<D, C>::NRW];          // U of this tile, the row blocks this wave finishes
-    float gc;                              // e^gamma_last of the chunk
+    f16x4 uf[ScanCfg<D, C>::NRW];          // usig U of this tile, the row blocks this wave finishes
+    float gc, ui;                          // e^gamma_last of the chunk; 1/usig
 };
 
 template <int D, int C> struct OutOps {   // one output wave's operands of one chunk
@@ -554,8 +579,9 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
     constexpr int NR = F::NR, NI = F::NI, KD = F::KD, KC = F::KC;
     constexpr int NWV = SC::NWV, NRW = SC::NRW, DEPTH = SC::DEPTH;
     __shared__ f32x4 s_part[NWV][NR][64];  // partial Delta blocks, accumulator layout
-    __shared__ f16x4 s_dlt[NR][64];         // Delta, fp16, accumulator layout
-    __shared__ f16x8 s_st[2][NWV][64];      // starting state of the chunk, B fragments (by parity)
+    __shared__ f32x4 s_dlt[NR][64];         // Delta, fp32, accumulator layout
+    __shared__ f16x8 s_st[2][NWV][64];      // starting state of the chunk, B fragments (by parity),
+    __shared__ float s_sg[2][NWV][64];      //   scaled per column by 1 / (these)
     const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     __builtin_assume(w >= 0 && w < NWV + SC::NWO);
@@ -585,14 +611,29 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
             for (int kc = 0; kc < KC; ++kc)
                 op.pf[kc] = *reinterpret_cast<const f16x8 *>(r + F::OFF_P + ((a * KC + kc) * 64 + lane) * 16);
         };
-        f16x8 bS[KD], bD[KC];  // chunk c - 1's starting state and Delta, read from LDS
+        // chunk c - 1's starting state (scaled fp16 slices and their inverse scales) and Delta
+        f16x8 bS[KD];
+        float bG[KD];
+        f32x4 bDl[NR];
         auto emit = [&](const OutOps<D, C> &op, int c) {
             f32x4 O = zero4();
 #pragma unroll
-            for (int kk = 0; kk < KD; ++kk) O = mma_f16_k32(op.qf[kk], bS[kk], O);
+            for (int kk = 0; kk < KD; ++kk) O += bG[kk] * mma_f16_k32(op.qf[kk], bS[kk], zero4());
+            float m = 0.f;
+#pragma unroll
+            for (int b = 0; b < NR; ++b)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) m = fmaxf(m, fabsf(bDl[b][rr]));
+            m = fmaxf(m, __shfl_xor(m, 16));  // the column's four lanes
+            m = fmaxf(m, __shfl_xor(m, 32));
+            float sd, isd;
+            pow2_scale(m, sd, isd);
+            f32x4 OD = zero4();
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc)
-                if (32 * kc <= 16 * a + 15) O = mma_f16_k32(op.pf[kc], bD[kc], O);
+                if (32 * kc <= 16 * a + 15)
+                    OD = mma_f16_k32(op.pf[kc], cat(h4(sd * bDl[2 * kc]), h4(sd * bDl[2 * kc + 1])), OD);
+            O += isd * OD;
             const int t0 = c * C, L = min(C, sp.len - t0);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
@@ -614,16 +655,24 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
                 __hip_atomic_store(prog + static_cast<size_t>(chain) * kProgStride,
                                    static_cast<unsigned long long>(c), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-            f16x8 nS[KD], nD[KC];
+            f16x8 nS[KD];
+            float nG[KD];
+            f32x4 nD[NR];
 #pragma unroll
-            for (int kk = 0; kk < KD; ++kk) nS[kk] = s_st[c & 1][kk][lane];
+            for (int kk = 0; kk < KD; ++kk) {
+                nS[kk] = s_st[c & 1][kk][lane];
+                nG[kk] = s_sg[c & 1][kk][lane];
+            }
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) nD[kc] = cat(s_dlt[2 * kc][lane], s_dlt[2 * kc + 1][lane]);
+            for (int b = 0; b < NR; ++b) nD[b] = s_dlt[b][lane];
             if (c > 0) emit(prev, c - 1);
 #pragma unroll
-            for (int kk = 0; kk < KD; ++kk) bS[kk] = nS[kk];
+            for (int kk = 0; kk < KD; ++kk) {
+                bS[kk] = nS[kk];
+                bG[kk] = nG[kk];
+            }
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) bD[kc] = nD[kc];
+            for (int b = 0; b < NR; ++b) bDl[b] = nD[b];
         };
         constexpr int RO = 3;  // ring of operand sets; slot (c mod RO) holds chunk c
         OutOps<D, C> ring[RO];
@@ -666,9 +715,10 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
     } else {
         S[0] = S[1] = zero4();
     }
-    // this chain's per-chunk decays (raw buffer, 32-bit data format; reads past the end give 0)
+    // this chain's per-chunk decays and U scales (raw buffer, 32-bit data format; reads past
+    // the end give 0)
     const __amdgpu_buffer_rsrc_t gsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(gchunk + sp.rec0), 0, 4 * nchunks,
+        const_cast<float *>(gchunk + 2 * sp.rec0), 0, 8 * nchunks,
         0x00020000);
     auto load = [&](ScanOps<D, C> &op, int cc) {
         const unsigned char *r = rec0 + static_cast<size_t>(cc) * F::REC;
@@ -688,16 +738,28 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
         }
         // through a buffer descriptor, so that it stays a vector-memory load: a scalar load
         // still in flight would hold up every LDS wait, which counts scalar loads too
-        op.gc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gsrc, 0, 4 * cc, 0));
+        op.gc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gsrc, 0, 8 * cc, 0));
+        op.ui = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gsrc, 0, 8 * cc + 4, 0));
     };
     auto step = [&](const ScanOps<D, C> &op, int c) {
-        const f16x8 bS = cat(h4(S[0]), h4(S[1]));  // k-step w of the B operand S
-        s_st[c & 1][w][lane] = bS;                  // for the output wavefronts
+        // k-step w of the B operand S, scaled per column by a power of two
+        float m = 0.f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) m = fmaxf(m, fabsf(S[i][rr]));
+        m = fmaxf(m, __shfl_xor(m, 16));  // the column's four lanes
+        m = fmaxf(m, __shfl_xor(m, 32));
+        float sg, isg;
+        pow2_scale(m, sg, isg);
+        const f16x8 bS = cat(h4(sg * S[0]), h4(sg * S[1]));
+        s_st[c & 1][w][lane] = bS;  // for the output wavefronts
+        s_sg[c & 1][w][lane] = isg;
         f32x4 pa[NR];
 #pragma unroll
         for (int a = 0; a < NR; ++a) pa[a] = mma_f16_k32(op.wf[a], bS, zero4());
 #pragma unroll
-        for (int a = 0; a < NR; ++a) s_part[w][a][lane] = pa[a];
+        for (int a = 0; a < NR; ++a) s_part[w][a][lane] = isg * pa[a];
         // the independent products back to back, then their LDS writes
         __builtin_amdgcn_sched_group_barrier(0x008, NR, 0);
         __builtin_amdgcn_sched_group_barrier(0x200, NR, 0);
@@ -711,22 +773,37 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
                 for (int v = 0; v < NWV; ++v) p[v] = s_part[v][a][lane];
                 // issue all the partial reads before any of the adds that use them
                 __builtin_amdgcn_sched_group_barrier(0x100, NWV, 0);
-                f32x4 d = f32x4{float(op.uf[j][0]), float(op.uf[j][1]), float(op.uf[j][2]),
-                                float(op.uf[j][3])};
+                f32x4 d = op.ui * f32x4{float(op.uf[j][0]), float(op.uf[j][1]), float(op.uf[j][2]),
+                                        float(op.uf[j][3])};
 #pragma unroll
                 for (int v = 0; v < NWV; ++v) d += p[v];
-                s_dlt[a][lane] = h4(d);
+                s_dlt[a][lane] = d;
             }
         }
         lds_barrier();
+        // S = (sd e^gamma_last S + K^T dec (sd Delta)) / sd, sd a power of two per column
+        f32x4 dl[NR];
+        float md = 0.f;
+#pragma unroll
+        for (int b = 0; b < NR; ++b) {
+            dl[b] = s_dlt[b][lane];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) md = fmaxf(md, fabsf(dl[b][rr]));
+        }
+        md = fmaxf(md, __shfl_xor(md, 16));
+        md = fmaxf(md, __shfl_xor(md, 32));
+        float sd, isd;
+        pow2_scale(md, sd, isd);
         f16x8 bD[KC];
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) bD[kc] = cat(s_dlt[2 * kc][lane], s_dlt[2 * kc + 1][lane]);
+        for (int kc = 0; kc < KC; ++kc) bD[kc] = cat(h4(sd * dl[2 * kc]), h4(sd * dl[2 * kc + 1]));
+        const float gcs = op.gc * sd;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            S[i] *= op.gc;
+            S[i] *= gcs;
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) S[i] = mma_f16_k32(op.kf[i][kc], bD[kc], S[i]);
+            S[i] *= isd;
         }
     };
 
@@ -768,8 +845,8 @@ template <int C> size_t split_records(const PrefillArgs &a) {
 
 template <int D, int C> size_t split_ws_bytes(const PrefillArgs &a) {
     const size_t nrec = split_records<C>(a), chains = static_cast<size_t>(a.B) * a.Hv;
-    // operand records | per-chunk decays | per-chain scan progress (256 B each, aligned)
-    return nrec * SplitCfg<D, C>::REC + (nrec * sizeof(float) + 255) / 256 * 256 +
+    // operand records | per-chunk decays and U scales | per-chain scan progress (256 B each)
+    return nrec * SplitCfg<D, C>::REC + (nrec * 2 * sizeof(float) + 255) / 256 * 256 +
            chains * kProgStride * sizeof(unsigned long long);
 }
 
@@ -780,7 +857,7 @@ template <int D, int C, typename TO> hipError_t launch_split_typed(const Prefill
     unsigned char *ws = static_cast<unsigned char *>(a.ws);
     float *gch = reinterpret_cast<float *>(ws + recs * SplitCfg<D, C>::REC);
     unsigned long long *prog = reinterpret_cast<unsigned long long *>(
-        ws + recs * SplitCfg<D, C>::REC + (recs * sizeof(float) + 255) / 256 * 256);
+        ws + recs * SplitCfg<D, C>::REC + (recs * 2 * sizeof(float) + 255) / 256 * 256);
     // prefetch workgroups only where the scan leaves compute units idle (one workgroup of
     // either kind fills a compute unit's registers)
     const size_t nscan = chains * (D / 16);

@@ -151,6 +151,23 @@ __device__ __forceinline__ float inv_norm_from_sumsq(float ss) {
     return 1.f / fmaxf(sqrtf(ss), kNormEps);
 }
 
+// ---- power-of-two operand scaling for the fp16 matrix-core operands.  The value side of the
+//      rule (v, U, Delta, the state S and the output) is linear in (v, S0), and every value
+//      column j evolves on its own, so the fp16 copies of a column may carry any power of two
+//      sigma_j: products of scaled operands are exactly sigma_j times the unscaled ones, and
+//      multiplying fp32 results by sigma_j or 1/sigma_j is exact.  Given m = max |x| over the
+//      values to convert, pow2_scale returns sigma with m * sigma in [2^8, 2^9): far from
+//      fp16's overflow (65504) and from its subnormals (below 2^-14), whatever the magnitude
+//      of v and S0.  sigma = 1 for m = 0, Inf or NaN; the exponent is clamped to +-100 so that
+//      sigma and 1/sigma stay normal fp32 numbers.
+__device__ __forceinline__ void pow2_scale(float m, float &sigma, float &inv_sigma) {
+    const int eb = static_cast<int>((__float_as_uint(m) >> 23) & 0xffu);  // biased exponent
+    int e = 135 - eb;  // m in [2^(eb-127), 2^(eb-126))  ->  m * 2^e in [2^8, 2^9)
+    e = (eb == 0 || eb == 255) ? 0 : min(max(e, -100), 100);
+    sigma = __uint_as_float(static_cast<uint32_t>(127 + e) << 23);
+    inv_sigma = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
+}
+
 template <typename T> __device__ __forceinline__ void store_f32(T *p, float x);
 template <> __device__ __forceinline__ void store_f32<float>(float *p, float x) { *p = x; }
 template <> __device__ __forceinline__ void store_f32<bf16_t>(bf16_t *p, float x) {

@@ -209,33 +209,43 @@ def test_variants_agree_and_are_deterministic(monkeypatch):
 
 
 # ------------------------------------------------------------------ the workloads, full size
-def _sampled_config_check(idx, nsample):
-    """Run a prefill workload at its full size through the default dispatch; compare every
-    output and the final state of `nsample` sampled (b, hv) chains with the oracle."""
+def _full_config_check(idx, block):
+    """Run a prefill workload at its full size through the default dispatch and compare every
+    output and final state of every (b, hv) chain with the oracle, `block` chains per oracle
+    call (the bar applies to the whole tensor: eps and M are maxima over all chains)."""
     c = CONFIGS[idx]
     inp = config_inputs(idx)
     o, sT = run_prefill(inp, c["chunk"])
     nch = c["B"] * c["Hv"]
-    rng = np.random.Generator(np.random.PCG64(1000 + idx))
-    chains = np.arange(nch) if nsample >= nch else np.sort(rng.choice(nch, nsample, replace=False))
-    ro, rS = oracle_prefill(inp, chains=chains, use_init=inp.s0 is not None)
-    b, h = chains // c["Hv"], chains % c["Hv"]
-    e1 = check(o[b, :, h], ro, "bf16", c["name"] + " o")
-    e2 = check(sT[b, h], rS, "bf16", c["name"] + " final state")
-    print("%s: %d chains checked, o err %.2e (max %.2e), S err %.2e (max %.2e)"
-          % (c["name"], len(chains), e1[0], e1[1], e2[0], e2[1]))
+    eo = Mo = eS = MS = 0.0
+    for c0 in range(0, nch, block):
+        chains = np.arange(c0, min(nch, c0 + block))
+        ro, rS = oracle_prefill(inp, chains=chains, use_init=inp.s0 is not None)
+        for j, ch in enumerate(chains):
+            b, h = ch // c["Hv"], ch % c["Hv"]
+            eo = max(eo, float(np.abs(o[b, :, h] - ro[j]).max()))
+            Mo = max(Mo, float(np.abs(ro[j]).max()))
+            eS = max(eS, float(np.abs(sT[b, h] - rS[j]).max()))
+            MS = max(MS, float(np.abs(rS[j]).max()))
+        del ro, rS
+    print("%s: all %d chains, o err %.2e (max %.2e), S err %.2e (max %.2e)"
+          % (c["name"], nch, eo, Mo, eS, MS))
+    assert np.isfinite(o).all() and np.isfinite(sT).all()
+    assert eo <= 2e-3 * Mo, "%s o: %.3e > 2e-3 * %.3e" % (c["name"], eo, Mo)
+    assert eS <= 2e-3 * MS, "%s final state: %.3e > 2e-3 * %.3e" % (c["name"], eS, MS)
 
 
 def test_config1_full():
-    _sampled_config_check(1, 16)
+    _full_config_check(1, 16)
 
 
-def test_config2_sampled():
-    _sampled_config_check(2, 12)
+def test_config2_full():
+    _full_config_check(2, 64)
 
 
-def test_config3_sampled():
-    _sampled_config_check(3, 2)
+def test_config3_full():
+    """The 262,144-token workload: all 16 chains (about 620 GFLOP of fp64 on the host)."""
+    _full_config_check(3, 16)
 
 
 # ------------------------------------------------------------------ several tokens per decode call

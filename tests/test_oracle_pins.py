@@ -349,31 +349,6 @@ def test_decode_identity_and_equivalence():
     np.testing.assert_array_equal(st, S_run)
 
 
-# ---------------------------------------------------------------- P14: concept code reading
-def _concept_code_literal(q, k, v, beta, g):
-    """The explainer's three-line concept code taken literally: e = v - S^T k from the
-    undecayed state, then S = a S + b k e^T, y = S^T q."""
-    T, dk = k.shape
-    S = np.zeros((dk, v.shape[1]))
-    ys = []
-    for t in range(T):
-        e = v[t] - S.T @ k[t]
-        S = math.exp(g[t]) * S + beta[t] * np.outer(k[t], e)
-        ys.append(S.T @ q[t])
-    return np.array(ys)
-
-
-def test_concept_code_agrees_only_without_decay():
-    inp = make_inputs(1, 23, 1, 1, 8, 5, dtype="f32", seed=24)
-    args = [x[0, :, 0].astype(np.float64) for x in (inp.q, inp.k, inp.v, inp.beta)]
-    g0 = np.zeros(23)
-    o_a1, _ = oracle.run(inp.q, inp.k, inp.v, inp.beta, np.zeros_like(inp.g))
-    np.testing.assert_allclose(_concept_code_literal(*args, g0), o_a1[0, :, 0], rtol=1e-12, atol=1e-13)
-    o, _ = oracle.run(inp.q, inp.k, inp.v, inp.beta, inp.g)
-    lit = _concept_code_literal(*args, inp.g[0, :, 0].astype(np.float64))
-    assert np.abs(lit - o[0, :, 0]).max() > 1e-3
-
-
 # ---------------------------------------------------------------- degenerate sizes
 def test_empty_sequence_returns_initial_state():
     inp = make_inputs(2, 3, 1, 2, 4, 4, dtype="f32", s0_std=1.0, seed=25)
@@ -453,6 +428,50 @@ def test_l2norm_prologue_is_scale_invariant_and_normalises():
     # the only difference: numpy's normalised values rounded to fp32 (u = 6e-8)
     assert np.abs(o1 - o3).max() <= 1e-6 * np.abs(o1).max()
     assert np.abs(s1 - s3).max() <= 1e-6 * np.abs(s1).max()
+
+
+def test_l2norm_epsilon_clamp():
+    """GDN_QK_L2NORM divides by max(||x||, 1e-6): (i) a zero key makes its token a pure decay
+    (bitwise the same as beta = 0 there), (ii) a zero query reads out exactly 0, (iii) a row
+    of norm 1e-8 is scaled by 1e6 (to norm 0.01) -- the same as feeding x * 1e6 without the
+    prologue, and a hundredth of what plain normalisation would give."""
+    p = _packed([12], Hk=1, Hv=2, seed=905)
+    q, k, beta = p["q"].copy(), p["k"].copy(), p["beta"].copy()
+    # (i) zero key at token 4 vs beta = 0 at token 4
+    kz = k.copy()
+    kz[4] = 0.0
+    bz = beta.copy()
+    bz[4] = 0.0
+    oa, sa = oracle.run_packed(q, kz, p["v"], beta, p["g"], p["cu"], s0=p["s0"], flags=oracle.QK_L2NORM)
+    ob, sb = oracle.run_packed(q, k, p["v"], bz, p["g"], p["cu"], s0=p["s0"], flags=oracle.QK_L2NORM)
+    np.testing.assert_array_equal(oa, ob)
+    np.testing.assert_array_equal(sa, sb)
+    # (ii) zero query at token 6
+    qz = q.copy()
+    qz[6] = 0.0
+    oc, _ = oracle.run_packed(qz, k, p["v"], beta, p["g"], p["cu"], s0=p["s0"], flags=oracle.QK_L2NORM)
+    assert not oc[6].any()
+    # (iii) rows below the epsilon: query at token 3, key at token 8
+    tiny_q, tiny_k = q.copy(), k.copy()
+    tiny_q[3] *= np.float32(1e-8) / np.linalg.norm(tiny_q[3].astype(np.float64), axis=-1, keepdims=True).astype(np.float32)
+    tiny_k[8] *= np.float32(1e-8) / np.linalg.norm(tiny_k[8].astype(np.float64), axis=-1, keepdims=True).astype(np.float32)
+    od, sd = oracle.run_packed(tiny_q, tiny_k, p["v"], beta, p["g"], p["cu"], s0=p["s0"],
+                               flags=oracle.QK_L2NORM)
+    qn = q.astype(np.float64) / np.linalg.norm(q.astype(np.float64), axis=-1, keepdims=True)
+    kn = k.astype(np.float64) / np.linalg.norm(k.astype(np.float64), axis=-1, keepdims=True)
+    qn[3] = tiny_q[3].astype(np.float64) / 1e-6
+    kn[8] = tiny_k[8].astype(np.float64) / 1e-6
+    oe, se = oracle.run_packed(qn.astype(np.float32), kn.astype(np.float32), p["v"], beta, p["g"],
+                               p["cu"], s0=p["s0"])
+    assert np.abs(od - oe).max() <= 1e-6 * np.abs(od).max()
+    assert np.abs(sd - se).max() <= 1e-6 * np.abs(sd).max()
+    assert abs(np.linalg.norm(qn[3], axis=-1).max() - 0.01) < 1e-6
+    # plain normalisation of token 3's query would read out 100 times more
+    qu = qn.copy()
+    qu[3] /= np.linalg.norm(qu[3], axis=-1, keepdims=True)
+    of, _ = oracle.run_packed(qu.astype(np.float32), kn.astype(np.float32), p["v"], beta, p["g"],
+                              p["cu"], s0=p["s0"])
+    np.testing.assert_allclose(od[3] * 100.0, of[3], rtol=1e-5, atol=1e-9)
 
 
 def test_beta_logit_zero_is_one_half():

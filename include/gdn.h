@@ -23,8 +23,9 @@
  *   - The state layout is [B, Hv, dk, dv] fp32 (dv contiguous): S[b][hv][i][j] is the
  *     entry for key coordinate i and value coordinate j.
  *   - Ownership: the caller owns every buffer.  No call allocates device memory,
- *     keeps state between calls, or synchronises the host; every call only enqueues
- *     kernels on `stream` (a hipStream_t; NULL = the null stream) and returns.
+ *     keeps state between calls (apart from gdn_chunk_fwd_noalloc's static scratch), or
+ *     synchronises the host; every call only enqueues kernels on `stream` (a hipStream_t;
+ *     NULL = the null stream) and returns.
  *   - Errors: arguments are validated on the host before anything is enqueued; on an
  *     error nothing is launched and no output is touched.  Faults inside a kernel
  *     surface at the caller's next synchronisation of the stream.  NaN and Inf in the
@@ -42,14 +43,16 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 typedef enum gdn_status {
     GDN_OK = 0,
     GDN_ERR_INVALID_ARG = 1, /* null required pointer, negative size, misalignment, Hv % Hk != 0,
                                 o aliasing an input, workspace too small */
     GDN_ERR_UNSUPPORTED = 2, /* valid but not implemented: head sizes, chunk size or dtype pair */
-    GDN_ERR_HIP = 3          /* the HIP runtime refused a launch */
+    GDN_ERR_HIP = 3,         /* the HIP runtime refused a launch */
+    GDN_ERR_SCRATCH_TOO_SMALL = 4 /* gdn_chunk_fwd_noalloc: the sizes need more workspace than
+                                     its static scratch holds (GDN_NOALLOC_SCRATCH_BYTES) */
 } gdn_status_t;
 
 typedef enum gdn_dtype {
@@ -138,6 +141,29 @@ gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v, const vo
                            float *final_state, int B, int T, int Hk, int Hv, int dk, int dv,
                            int chunk, float scale, gdn_dtype_t in_dtype, gdn_dtype_t out_dtype,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_chunk_fwd for callers that cannot allocate device memory -- code being captured into a
+ * HIP graph, tight serving loops, harnesses that forbid hipMalloc: the same arguments without
+ * the workspace, the same kernels and results (bit for bit).  Where the plan needs a
+ * workspace (gdn_chunk_fwd_workspace_size(...) > 0) it uses a static scratch buffer of
+ * GDN_NOALLOC_SCRATCH_BYTES that the library holds in every GPU's memory from its load until
+ * the process ends; the call itself allocates nothing (no hipMalloc, no allocating library
+ * routine).  Sizes whose workspace exceeds GDN_NOALLOC_SCRATCH_BYTES return
+ * GDN_ERR_SCRATCH_TOO_SMALL before anything is launched (80 MiB holds the split plan's
+ * workspace for up to 1,100 chunk-heads at dk = dv = 128 and chunk 64, e.g. T = 4096 with 16
+ * heads).  Every call on one GPU shares that GPU's scratch and leaves its contents behind:
+ * calls that can run at the same time on one GPU (different streams without ordering between
+ * them, or different host threads) race and must be serialised by the caller.  The first
+ * call on each device looks up the scratch's device address once (hipGetSymbolAddress, with
+ * that device current), under a lock.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES (80ull << 20)
+gdn_status_t gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const void *beta,
+                                   const void *g, const float *initial_state, void *o,
+                                   float *final_state, int B, int T, int Hk, int Hv, int dk,
+                                   int dv, int chunk, float scale, gdn_dtype_t in_dtype,
+                                   gdn_dtype_t out_dtype, void *stream);
 
 /*
  * Decode: apply one token of Eq. (1) to every state in place and read it out.

@@ -14,7 +14,7 @@ The C entry points are exposed unchanged as ``gdn_chunk_fwd``, ``gdn_decode_step
 ``gdn_decode_tokens``, ``gdn_chunk_fwd_varlen``, ``gdn_chunk_fwd_varlen_workspace_size``,
 ``gdn_backward``, ``gdn_backward_workspace_size``, ``gdn_chunk_fwd_workspace_size``,
 ``gdn_qsa_index``, ``gdn_qsa_workspace_size``,
-``gdn_chunk_fwd_plan``,
+``gdn_chunk_fwd_plan``, ``gdn_chunk_fwd_noalloc``,
 ``gdn_status_string`` and ``gdn_abi_version``.
 """
 from __future__ import annotations
@@ -25,8 +25,10 @@ import os
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libgdn.so")
 
-ABI_VERSION = 4  # the GDN_ABI_VERSION of include/gdn.h that these signatures follow
+ABI_VERSION = 5  # the GDN_ABI_VERSION of include/gdn.h that these signatures follow
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
+GDN_ERR_SCRATCH_TOO_SMALL = 4
+GDN_NOALLOC_SCRATCH_BYTES = 80 << 20  # static scratch of gdn_chunk_fwd_noalloc
 GDN_F32, GDN_BF16 = 0, 1
 GDN_QK_L2NORM, GDN_BETA_LOGIT, GDN_G_LOGIT = 1, 2, 4  # input prologue flags
 GDN_PREFER_SPLIT = 8  # plan hint of the prefill with packed sequences
@@ -34,7 +36,7 @@ EXPORTED_SYMBOLS = ("gdn_abi_version", "gdn_status_string", "gdn_chunk_fwd_works
                     "gdn_chunk_fwd_plan", "gdn_chunk_fwd", "gdn_decode_step", "gdn_decode_tokens",
                     "gdn_chunk_fwd_varlen", "gdn_chunk_fwd_varlen_workspace_size",
                     "gdn_backward", "gdn_backward_workspace_size", "gdn_qsa_workspace_size",
-                    "gdn_qsa_index")
+                    "gdn_qsa_index", "gdn_chunk_fwd_noalloc")
 
 _lib = None
 
@@ -66,6 +68,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdn_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i,
                                   vp, sz, vp]
     lib.gdn_chunk_fwd.restype = i
+    lib.gdn_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f,
+                                          i, i, vp]
+    lib.gdn_chunk_fwd_noalloc.restype = i
     lib.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
     lib.gdn_decode_step.restype = i
     u = ctypes.c_uint
@@ -119,6 +124,15 @@ def gdn_chunk_fwd(q, k, v, beta, g, initial_state, o, final_state, B, T, Hk, Hv,
     return int(load_library().gdn_chunk_fwd(q, k, v, beta, g, initial_state, o, final_state, B, T,
                                             Hk, Hv, dk, dv, chunk, scale, in_dtype, out_dtype,
                                             workspace, workspace_bytes, stream))
+
+
+def gdn_chunk_fwd_noalloc(q, k, v, beta, g, initial_state, o, final_state, B, T, Hk, Hv, dk, dv,
+                          chunk, scale, in_dtype, out_dtype, stream) -> int:
+    """Raw call: pointer arguments are ints (device addresses) or None.  Uses the library's
+    static scratch instead of a workspace (nothing is allocated)."""
+    return int(load_library().gdn_chunk_fwd_noalloc(q, k, v, beta, g, initial_state, o,
+                                                    final_state, B, T, Hk, Hv, dk, dv, chunk,
+                                                    scale, in_dtype, out_dtype, stream))
 
 
 def gdn_decode_step(q, k, v, beta, g, state, o, B, Hk, Hv, dk, dv, scale, in_dtype, out_dtype,

@@ -1,11 +1,19 @@
 // gdn_api.hip -- the C ABI of libgdn.so (declared in include/gdn.h): host-side argument
-// validation and dispatch to the kernels.  Nothing here allocates device memory, keeps state
-// between calls or synchronises the host.
+// validation and dispatch to the kernels.  Nothing here allocates device memory or
+// synchronises the host.  The only state is the per-device address of the static scratch
+// buffer of gdn_chunk_fwd_noalloc, looked up once per device.
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "gdn_internal.h"
+
+// Scratch of gdn_chunk_fwd_noalloc (its workspace), for callers that cannot allocate: one copy
+// in every GPU's memory, held from the library's load until the process ends.  Host code uses
+// it only through the device address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -56,6 +64,9 @@ const char *gdn_status_string(gdn_status_t s) {
     case GDN_ERR_INVALID_ARG: return "GDN_ERR_INVALID_ARG";
     case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
     case GDN_ERR_HIP: return "GDN_ERR_HIP";
+    case GDN_ERR_SCRATCH_TOO_SMALL:
+        return "GDN_ERR_SCRATCH_TOO_SMALL (the sizes need more workspace than the "
+               "GDN_NOALLOC_SCRATCH_BYTES of gdn_chunk_fwd_noalloc's static scratch)";
     }
     return "GDN_ERR_UNKNOWN";
 }
@@ -93,6 +104,13 @@ static gdn_status_t check_prefill(const gdn::PrefillArgs &a) {
     return GDN_OK;
 }
 
+// Workspace bytes the plan `var` needs for a validated prefill with tokens.
+static size_t plan_workspace(const gdn::PrefillArgs &a, Variant var) {
+    return var == Variant::Split   ? gdn::chunk_split_workspace(a)
+           : var == Variant::Fused ? gdn::chunk_mfma_workspace(a)
+                                   : 0;
+}
+
 // The whole prefill: validation, the T = 0 case, workspace check and dispatch.
 static gdn_status_t run_prefill(gdn::PrefillArgs &a) {
     gdn_status_t st = check_prefill(a);
@@ -105,9 +123,7 @@ static gdn_status_t run_prefill(gdn::PrefillArgs &a) {
                                                                               : GDN_ERR_HIP;
     }
     const Variant var = choose_variant(a);
-    const size_t need = var == Variant::Split   ? gdn::chunk_split_workspace(a)
-                        : var == Variant::Fused ? gdn::chunk_mfma_workspace(a)
-                                                : 0;
+    const size_t need = plan_workspace(a, var);
     if (need > 0 && (a.ws == nullptr || a.ws_bytes < need)) return GDN_ERR_INVALID_ARG;
     if (need > 0 && !aligned(a.ws, 256)) return GDN_ERR_INVALID_ARG;
     hipError_t e = var == Variant::Split   ? gdn::launch_chunk_split(a)
@@ -182,6 +198,77 @@ gdn_status_t gdn_chunk_fwd_varlen(const void *q, const void *k, const void *v, c
     a.scale = scale; a.in_dt = in_dtype; a.out_dt = out_dtype;
     a.ws = workspace; a.ws_bytes = workspace_bytes;
     a.stream = static_cast<hipStream_t>(stream);
+    return run_prefill(a);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Device address of `scratch` on each device, looked up once per device (with that device
+// current) and kept until the process ends.
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mutex;
+void *g_scratch_addr[kMaxDevices];
+
+// The scratch address on the device that runs `stream` (the current device for the null
+// stream).
+hipError_t scratch_address(hipStream_t stream, void **addr) {
+    int cur = 0, dev = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    dev = cur;
+    if (stream != nullptr) {
+        e = hipStreamGetDevice(stream, &dev);
+        if (e != hipSuccess) return e;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_addr[dev] == nullptr) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_addr[dev] = p;
+    }
+    *addr = g_scratch_addr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status_t gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const void *beta,
+                                   const void *g, const float *initial_state, void *o,
+                                   float *final_state, int B, int T, int Hk, int Hv, int dk,
+                                   int dv, int chunk, float scale, gdn_dtype_t in_dtype,
+                                   gdn_dtype_t out_dtype, void *stream) {
+    gdn::PrefillArgs a;
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g;
+    a.s0 = initial_state; a.o = o; a.sT = final_state;
+    a.B = B; a.T = T; a.Hk = Hk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.chunk = chunk;
+    a.cu = nullptr; a.flags = 0u;
+    a.scale = scale; a.in_dt = in_dtype; a.out_dt = out_dtype;
+    a.ws = nullptr; a.ws_bytes = 0;
+    a.stream = static_cast<hipStream_t>(stream);
+    const gdn_status_t st = check_prefill(a);
+    if (st != GDN_OK) return st;
+    if (a.B > 0 && a.T > 0) {
+        const size_t need = plan_workspace(a, choose_variant(a));
+        if (need > GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_SCRATCH_TOO_SMALL;
+        if (need > 0) {
+            // whatever a kernel must find zeroed it clears itself (the split plan's prep kernel
+            // resets the scan's progress words), so no memset is needed
+            if (scratch_address(a.stream, &a.ws) != hipSuccess) return GDN_ERR_HIP;
+            a.ws_bytes = GDN_NOALLOC_SCRATCH_BYTES;
+        }
+    }
     return run_prefill(a);
 }
 

@@ -44,6 +44,7 @@ def test_version_and_status_strings(lib):
     assert gdn.gdn_status_string(1) == "GDN_ERR_INVALID_ARG"
     assert gdn.gdn_status_string(2) == "GDN_ERR_UNSUPPORTED"
     assert gdn.gdn_status_string(3) == "GDN_ERR_HIP"
+    assert gdn.gdn_status_string(4).startswith("GDN_ERR_SCRATCH_TOO_SMALL")
     assert gdn.gdn_status_string(99) == "GDN_ERR_UNKNOWN"
 
 
@@ -110,6 +111,42 @@ def test_prefill_validation(lib, kw, status):
 
 def test_prefill_empty_batch_is_noop(lib):
     assert prefill(B=0, q=None, k=None, v=None, beta=None, g=None, o=None) == gdn.GDN_OK
+
+
+def prefill_noalloc(**kw):
+    a = dict(q=P["q"], k=P["k"], v=P["v"], beta=P["beta"], g=P["g"], initial_state=P["s0"],
+             o=P["o"], final_state=P["sT"], B=1, T=64, Hk=2, Hv=2, dk=16, dv=16, chunk=16,
+             scale=1.0, in_dtype=gdn.GDN_BF16, out_dtype=gdn.GDN_F32, stream=None)
+    a.update(kw)
+    return gdn.gdn_chunk_fwd_noalloc(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hv=3), gdn.GDN_ERR_INVALID_ARG),
+    (dict(dk=48), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(q=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(o=P["q"] + 64), gdn.GDN_ERR_INVALID_ARG),
+])
+def test_noalloc_validation(lib, kw, status):
+    assert prefill_noalloc(**kw) == status
+
+
+def test_noalloc_rejects_workspace_beyond_its_scratch(lib):
+    """The split plan's workspace grows with the chunk count: T = 4096 with 16 heads (72 MiB)
+    fits the 80 MiB scratch, twice that does not -- rejected on the host, nothing launched."""
+    need = gdn.gdn_chunk_fwd_workspace_size(1, 8192, 16, 16, 128, 128, 64, gdn.GDN_BF16)
+    assert need > gdn.GDN_NOALLOC_SCRATCH_BYTES
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 4096, 16, 16, 128, 128, 64,
+                                            gdn.GDN_BF16) <= gdn.GDN_NOALLOC_SCRATCH_BYTES
+    assert prefill_noalloc(T=8192, Hk=16, Hv=16, dk=128, dv=128, chunk=64,
+                           initial_state=None, final_state=None) == gdn.GDN_ERR_SCRATCH_TOO_SMALL
+    assert prefill_noalloc(B=0, q=None, k=None, v=None, beta=None, g=None, o=None) == gdn.GDN_OK
+
+
+def test_noalloc_scratch_size_matches_the_header(lib):
+    text = open(HEADER).read()
+    m = re.search(r"#define GDN_NOALLOC_SCRATCH_BYTES \((\d+)ull << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == gdn.GDN_NOALLOC_SCRATCH_BYTES
 
 
 def decode(**kw):

@@ -1,11 +1,13 @@
 #!/usr/bin/env python3
 """Benchmark of the Gated DeltaNet hot path on one MI355X.
 
-One step = one gdn_chunk_fwd over the prefill workload (default: B=1, T=4096, 16 heads,
-dk=dv=128, chunk 64, bf16 inputs, fp32 output and state) followed by the decode workload: 64
-consecutive gdn_decode_step calls (B=256 sequences, 32 heads, dk=dv=128, fp32 state
-[256,32,128,128] updated in place, one pre-drawn token per call).  Inputs are seeded synthetic
-tensors (gdn_inputs.py), resident in HBM before the timed region.
+One step = one gdn_chunk_fwd over the prefill workload (default: the 262,144-token native
+context, B=1, 16 heads, dk=dv=128, chunk 64, bf16 inputs, long-memory gates, fp32 output and
+state) followed by the decode workload: 64 consecutive gdn_decode_step calls (B=256 sequences,
+32 heads, dk=dv=128, fp32 state [256,32,128,128] updated in place, one pre-drawn token per
+call).  Inputs are seeded synthetic tensors with the recipe's distributions (gdn_inputs.py;
+the long prefill's are drawn on the GPU with torch's generator), resident in HBM before the
+timed region.
 
 Prints ONE JSON line:  value = prefill tokens/s (B*T / mean prefill launch time), with the
 decode state GB/s, both kernels' rooflines (algorithmic bytes / measured launch time,
@@ -14,11 +16,13 @@ on the host cores as a reported CPU baseline.  Outside the step, "decode_tokens"
 gdn_decode_tokens over T = 2, 4, 8 tokens of the decode workload per call (one read and one
 write of every state per call; in place, and for T = 8 also into a separate output state, as a
 verifier keeping the old state would call it); "prologue_and_packed" reports the prefill with
-the fused input prologue and a packed batch of 32 variable-length sequences; "qsa_indexer"
-reports the QSA compressed indexer (gdn_qsa_index) on a 65536-token sequence;
-"prefill_other_workloads" times workloads 2 (batched, grouped heads) and 3 (262,144 tokens);
-"measured_peaks" reports what a plain device copy and a dense bf16 matrix product reach in the
-same run.
+the fused input prologue and a packed batch of 32 variable-length sequences, and the backward,
+all on the 4096-token workload; "qsa_indexer" reports the QSA compressed indexer
+(gdn_qsa_index) on a 65536-token sequence; "prefill_other_workloads" times the other prefill
+workloads (B=1 T=4096 H=16; B=8 T=8192 with grouped heads); "decode_cycled_states" times the
+decode step over four separate state buffers in turn, so that no state is still in the
+last-level cache when it is read again; "measured_peaks" reports what a plain device copy and a
+dense bf16 matrix product reach in the same run.
 """
 from __future__ import annotations
 
@@ -85,15 +89,17 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None when absent or
-    taken on a different version of the kernel source."""
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None when absent,
+    taken on another workload or on a different version of the kernel source."""
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh).get(kernel)
     except (OSError, ValueError):
         return None
     if not rec or rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    if rec.get("workload") != workload:
         return None
     return rec.get("bytes_per_launch")
 
@@ -113,17 +119,21 @@ def measured_mfma(label, sources):
 
 
 # ------------------------------------------------------------------ CPU baseline (oracle)
-def cpu_baseline(pre_inp, dec_inp, budget_s=30.0):
+def cpu_baseline(pre_inp, dec_inp, full_T, min_s=10.0):
+    """The fp64 oracle on the host cores: `pre_inp` is the prefill workload's first tokens (all
+    of its chains, drawn by the recipe), run repeatedly for at least `min_s` seconds; tokens/s
+    is per token of the whole sequence, the same unit as the GPU figure.  Plus one decode step
+    of the decode workload."""
     import numpy as np
     import oracle
     threads = min(16, len(os.sched_getaffinity(0)))
     B, T, Hk, Hv = pre_inp.q.shape[0], pre_inp.q.shape[1], pre_inp.q.shape[2], pre_inp.v.shape[2]
     reps, t = 0, time.perf_counter()
-    while True:  # repeat the whole workload until a few seconds of CPU time are sampled
+    while True:  # repeat the sample until min_s seconds of CPU time are taken
         oracle.run(pre_inp.q, pre_inp.k, pre_inp.v, pre_inp.beta, pre_inp.g, s0=pre_inp.s0,
                    nthreads=threads, want_state=True)
         reps += 1
-        if time.perf_counter() - t >= min(5.0, budget_s) or reps >= 50:
+        if time.perf_counter() - t >= min_s or reps >= 50:
             break
     pre_s = (time.perf_counter() - t) / reps
     # decode: one step of the decode workload (all 8192 states, fp64)
@@ -136,10 +146,11 @@ def cpu_baseline(pre_inp, dec_inp, budget_s=30.0):
     state_bytes_f32 = 2 * Bd * Hvd * dk * dv * 4
     return {
         "value": B * T / pre_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-        "sample": ("whole prefill workload (B=%d, T=%d, %d heads, fp64 token-by-token "
-                   "recurrence, %d independent chains), mean of %d runs: %.3f s each; plus one "
-                   "decode step of the decode workload in %.3f s" % (B, T, Hv, B * Hv, reps,
-                                                                      pre_s, dec_s)),
+        "host_cpu_count": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+        "sample": ("the first %d of the prefill workload's %d tokens, all %d chains (B=%d, %d "
+                   "heads; fp64 token-by-token recurrence, chains in parallel on %d threads), "
+                   "mean of %d runs: %.3f s each; plus one decode step of the decode workload in "
+                   "%.3f s" % (T, full_T, B * Hv, B, Hv, threads, reps, pre_s, dec_s)),
         "decode_state_GBps_fp32_equiv": state_bytes_f32 / dec_s / 1e9,
         "cpu_model": _cpu_model(),
     }
@@ -194,30 +205,40 @@ class HipEvent:
 
 
 # ------------------------------------------------------------------ the other prefill workloads
-def prefill_configs(gdn, torch, dev, stream, names=(2, 3)):
-    """Workloads 2 (8 x 8192 tokens, 16 q/k and 32 v heads, initial state) and 3 (262,144
-    tokens, 16 heads, long-memory gates): one call each, median of 3, with 1 GiB written between
-    calls so that nothing stays in the last-level cache.  Timing inputs are drawn on the GPU
-    with the recipe's distributions (q, k ~ N(0,1) then L2-normalised per head, v ~ N(0,1),
-    beta = sigmoid(N(0,1)), log alpha = -U(lo, hi), S0 ~ N(0, 0.02^2)); parity is tested on
-    the recipe's own seeded draws."""
+def gpu_inputs(torch, dev, idx):
+    """A prefill workload's inputs drawn on the GPU with the recipe's distributions (q, k ~
+    N(0,1) then L2-normalised per head, v ~ N(0,1), beta = sigmoid(N(0,1)), log alpha =
+    -U(lo, hi), S0 ~ N(0, std^2)), rounded to bf16; seed 1000 + workload index."""
+    from gdn_inputs import CONFIGS
+    c = CONFIGS[idx]
+    B, T, Hk, Hv, dk, dv = (c[k_] for k_ in ("B", "T", "Hk", "Hv", "dk", "dv"))
+    g = torch.Generator(device=dev)
+    g.manual_seed(1000 + idx)
+    nrm = torch.nn.functional.normalize
+    q = nrm(torch.randn(B, T, Hk, dk, device=dev, generator=g), dim=-1).to(torch.bfloat16)
+    k = nrm(torch.randn(B, T, Hk, dk, device=dev, generator=g), dim=-1).to(torch.bfloat16)
+    v = torch.randn(B, T, Hv, dv, device=dev, generator=g).to(torch.bfloat16)
+    beta = torch.sigmoid(torch.randn(B, T, Hv, device=dev, generator=g)).to(torch.bfloat16)
+    lo, hi = c["g_range"]
+    gg = (-(torch.rand(B, T, Hv, device=dev, generator=g) * (hi - lo) + lo)).to(torch.bfloat16)
+    s0 = None if c["s0_std"] is None else \
+        torch.randn(B, Hv, dk, dv, device=dev, generator=g) * c["s0_std"]
+    return {"q": q, "k": k, "v": v, "beta": beta, "g": gg, "s0": s0}
+
+
+def prefill_configs(gdn, torch, dev, stream, names=(1, 2)):
+    """The other prefill workloads (by default 1: 4,096 tokens, 16 heads; 2: 8 x 8192 tokens,
+    16 q/k and 32 v heads, initial state): one call each, median of 3, with 1 GiB written
+    between calls so that nothing stays in the last-level cache.  Timing inputs are drawn on
+    the GPU (gpu_inputs); parity is tested on the recipe's own seeded draws."""
     from gdn_inputs import CONFIGS
     out = {}
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     for idx in names:
         c = CONFIGS[idx]
         B, T, Hk, Hv, dk, dv, C = (c[k_] for k_ in ("B", "T", "Hk", "Hv", "dk", "dv", "chunk"))
-        g = torch.Generator(device=dev)
-        g.manual_seed(1000 + idx)
-        nrm = torch.nn.functional.normalize
-        q = nrm(torch.randn(B, T, Hk, dk, device=dev, generator=g), dim=-1).to(torch.bfloat16)
-        k = nrm(torch.randn(B, T, Hk, dk, device=dev, generator=g), dim=-1).to(torch.bfloat16)
-        v = torch.randn(B, T, Hv, dv, device=dev, generator=g).to(torch.bfloat16)
-        beta = torch.sigmoid(torch.randn(B, T, Hv, device=dev, generator=g)).to(torch.bfloat16)
-        lo, hi = c["g_range"]
-        gg = (-(torch.rand(B, T, Hv, device=dev, generator=g) * (hi - lo) + lo)).to(torch.bfloat16)
-        s0 = None if c["s0_std"] is None else \
-            torch.randn(B, Hv, dk, dv, device=dev, generator=g) * c["s0_std"]
+        x = gpu_inputs(torch, dev, idx)
+        q, k, v, beta, gg, s0 = (x[n] for n in ("q", "k", "v", "beta", "g", "s0"))
         o = torch.empty(B, T, Hv, dv, dtype=torch.float32, device=dev)
         fs = torch.empty(B, Hv, dk, dv, dtype=torch.float32, device=dev)
         call = lambda: gdn.chunk_fwd(q, k, v, beta, gg, initial_state=s0, chunk=C, o=o,
@@ -249,7 +270,7 @@ def prefill_configs(gdn, torch, dev, stream, names=(2, 3)):
             "algorithmic_flops": fl, "algorithmic_bytes": by,
             "mfma_counters": measured_mfma("workload%d_%s" % (idx, plan),
                                            "prefill" if plan == "split" else "fused")}
-        del q, k, v, beta, gg, s0, o, fs
+        del q, k, v, beta, gg, s0, o, fs, x
         torch.cuda.synchronize()
     del flush
     return out
@@ -425,8 +446,11 @@ def qsa_indexer(gdn, torch, dev, stream, with_cpu=True):
     """The QSA compressed indexer (gdn_qsa_index) on B=1, T=65536, 4 query heads and one key
     head of d=128 (bf16, seeded N(0,1)), r=4 (16384 blocks), 512 blocks (2048 tokens) kept,
     64 rotated dimensions.  The scoring and selection kernel is bound by the exponentials of
-    the softmax (4 per query-block pair per evaluation of the importance), so its roofline is
-    the vector units' exp rate; the fp64 oracle is timed on a sample of query rows."""
+    the softmax, so its roofline is the vector units' exp rate.  The method needs one
+    exponential per head and (query, block) pair, 4 per pair; the kernel evaluates them twice
+    (once for the softmax normaliser, once for the importance) rather than storing them, and
+    the roofline counts the 4 the method needs.  The fp64 oracle is timed on a sample of query
+    rows."""
     B, T, d, r, nsel = 1, 65536, 128, 4, 512
     g = torch.Generator(device=dev)
     g.manual_seed(21)
@@ -441,11 +465,12 @@ def qsa_indexer(gdn, torch, dev, stream, with_cpu=True):
     res = {"workload": "B=1 T=65536 Hq=4 d=128 r=4 nsel=512 rope_dims=64 bf16",
            "ms": round(ms, 3), "queries_per_s": round(B * T / (ms * 1e-3), 1),
            "scored_pairs_per_s": round(pairs / (ms * 1e-3), 1),
-           # the definition needs two evaluations per pair (softmax normaliser, importance)
+           # one exponential per head and pair; the kernel performs each twice
            "roofline": {"bound": "alu", "unit": "exp/s", "peak": EXP_PEAK_PER_S,
-                        "achieved": round(8 * pairs / (ms * 1e-3), 1),
-                        "frac": round(8 * pairs / (ms * 1e-3) / EXP_PEAK_PER_S, 4),
-                        "algorithmic_exps_per_pair": 8},
+                        "achieved": round(4 * pairs / (ms * 1e-3), 1),
+                        "frac": round(4 * pairs / (ms * 1e-3) / EXP_PEAK_PER_S, 4),
+                        "algorithmic_exps_per_pair": 4, "performed_exps_per_pair": 8,
+                        "frac_performed": round(8 * pairs / (ms * 1e-3) / EXP_PEAK_PER_S, 4)},
            "score_TFLOPs_one_pass": round(2 * 4 * d * pairs / (ms * 1e-3) / 1e12, 2)}
     if with_cpu:
         import numpy as np
@@ -471,9 +496,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--prefill-config", type=int, default=1, choices=[1, 2, 3],
-                    help="prefill workload: 1 = B1 T4096 H16 (default), 2 = B8 T8192 Hk16/Hv32, "
-                         "3 = B1 T262144 H16")
+    ap.add_argument("--prefill-config", type=int, default=3, choices=[1, 2, 3],
+                    help="prefill workload: 3 = B1 T262144 H16 (default, the native context), "
+                         "1 = B1 T4096 H16, 2 = B8 T8192 Hk16/Hv32")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=16384,
+                    help="tokens of the prefill workload (all its chains) the oracle runs for "
+                         "the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (known bytes, "
@@ -507,11 +535,10 @@ def main():
 
     pc = CONFIGS[args.prefill_config]
     dc = CONFIGS[4]
-    pre_inp = config_inputs(args.prefill_config)
     dec_inp = config_inputs(4)
 
     # ---- inputs resident in HBM
-    pt = pre_inp.to_torch(dev)
+    pt = gpu_inputs(torch, dev, args.prefill_config)
     B, T, Hk, Hv, dk, dv, C = pc["B"], pc["T"], pc["Hk"], pc["Hv"], pc["dk"], pc["dv"], pc["chunk"]
     o = torch.empty((B, T, Hv, dv), dtype=torch.float32, device=dev)
     fs = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
@@ -569,7 +596,7 @@ def main():
     torch.cuda.synchronize()
     b2b_ms = b2b[0].elapsed_time(b2b[1]) / 10
     flops = prefill_flops(B, T, Hk, Hv, dk, dv, C)
-    pbytes = prefill_bytes(B, T, Hk, Hv, dk, dv, has_s0=pre_inp.s0 is not None)
+    pbytes = prefill_bytes(B, T, Hk, Hv, dk, dv, has_s0=pt["s0"] is not None)
     pre_tflops = flops / (pre_mean * 1e-3) / 1e12
     pre_gbs = pbytes / (pre_mean * 1e-3) / 1e9
     plan = gdn.gdn_chunk_fwd_plan(B, T, Hk, Hv, dk, dv, C, gdn.GDN_BF16)
@@ -580,7 +607,8 @@ def main():
             "kernel": pre_kernels, "plan": plan, "bound": "hbm",
             "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(pre_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic("prefill" if plan == "split" else "fused"),
+            "traffic": measured_traffic("prefill" if plan == "split" else "fused",
+                                        "workload%d" % args.prefill_config),
             "algorithmic_bytes": pbytes, "algorithmic_flops": flops,
             "mean_launch_ms": round(pre_mean, 4),
             "mfma_TFLOPs": round(pre_tflops, 2),
@@ -601,7 +629,8 @@ def main():
             "kernel": "decode_kernel<%d,%d,bf16,float,false>" % (dc["dk"], dc["dv"]),
             "bound": "hbm",
             "achieved": round(tot_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(tot_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode"),
+            "frac": round(tot_gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("decode", "workload4"),
             "algorithmic_bytes": tbytes, "mean_launch_ms": round(dec_mean, 4),
         }
         result_decode = {
@@ -642,11 +671,44 @@ def main():
                                  "total_GBps": round(tb / (ms * 1e-3) / 1e9, 1),
                                  "frac_hbm_peak": round(tb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
-    # ---- the input prologue and packed sequences (not part of the step)
-    extras = None if args.no_extras else prologue_and_packed(gdn, torch, dev, stream, pt, pc, o, fs)
+    # ---- the decode step over four state buffers in turn (not part of the step): each 512 MiB
+    #      state is read again only after 1.5 GiB of other states, so the last-level cache
+    #      (about 256 MB) cannot hold it between its reads
+    cycled = None
+    if not args.no_decode and not args.no_extras:
+        states = [state] + [state.clone() for _ in range(3)]
+        call = lambda: [gdn.decode_step(dq[i], dk_[i], dv_[i], db[i], dg[i], states[i % 4], o=do)
+                        for i in range(nsteps_dec)]
+        call()
+        torch.cuda.synchronize()
+        e0, e1 = HipEvent(), HipEvent()
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / nsteps_dec * 1e3
+        sbytes, tbytes = decode_bytes(dc["B"], dc["Hk"], dc["Hv"], dc["dk"], dc["dv"])
+        cycled = {"us_per_step": round(us, 2), "state_GBps": round(sbytes / (us * 1e-6) / 1e9, 1),
+                  "total_GBps": round(tbytes / (us * 1e-6) / 1e9, 1),
+                  "frac_hbm_peak": round(tbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                  "what": "64 decode steps, step i on state buffer i mod 4 (4 x 512 MiB)"}
+        del states
+        torch.cuda.synchronize()
+
+    # ---- the input prologue, packed sequences and the backward, on the 4096-token workload
+    #      (not part of the step)
+    extras = None
+    if not args.no_extras:
+        xc = CONFIGS[1]
+        xt = config_inputs(1).to_torch(dev)
+        xo = torch.empty((xc["B"], xc["T"], xc["Hv"], xc["dv"]), dtype=torch.float32, device=dev)
+        xfs = torch.empty((xc["B"], xc["Hv"], xc["dk"], xc["dv"]), dtype=torch.float32, device=dev)
+        extras = prologue_and_packed(gdn, torch, dev, stream, xt, xc, xo, xfs)
+        del xt, xo, xfs
     qsa = None if args.no_extras else qsa_indexer(gdn, torch, dev, stream,
                                                    with_cpu=not args.no_cpu_baseline)
-    others = None if args.no_extras else prefill_configs(gdn, torch, dev, stream)
+    others = None if args.no_extras else prefill_configs(
+        gdn, torch, dev, stream, names=[i for i in (1, 2, 3) if i != args.prefill_config])
     peaks = None if args.no_extras else measured_peaks(torch, dev, stream)
     if result_decode is not None and peaks is not None:
         result_decode["frac_measured_copy"] = round(result_decode["total_GBps"] / peaks["copy_GBps"], 4)
@@ -661,7 +723,8 @@ def main():
         "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16 in, fp16 MFMA operands, fp32 accumulate/state",
-        "data": "synthetic (seeded, gdn_inputs recipe v1)",
+        "data": "synthetic, seeded: the recipe's distributions (gdn_inputs recipe v1); prefill "
+                "inputs drawn on the GPU with torch's generator, decode inputs by the recipe",
         "config": {
             "workload": pc["name"] + ("" if args.no_decode else " + " + dc["name"]),
             "prefill": {k_: pc[k_] for k_ in ("B", "T", "Hk", "Hv", "dk", "dv", "chunk", "dtype")},
@@ -684,6 +747,7 @@ def main():
                     "frac_measured_copy": None if peaks is None else
                     round(pre_gbs / peaks["copy_GBps"], 4)},
         "decode": result_decode,
+        "decode_cycled_states": cycled,
         "decode_tokens": multi,
         "prologue_and_packed": extras,
         "qsa_indexer": qsa,
@@ -693,7 +757,11 @@ def main():
         "rooflines": rooflines,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(pre_inp, dec_inp)
+        from gdn_inputs import make_inputs
+        ts = min(T, args.cpu_sample_tokens)
+        sample = make_inputs(B, ts, Hk, Hv, dk, dv, dtype=pc["dtype"], g_range=pc["g_range"],
+                             s0_std=pc["s0_std"], seed=pc["seed"])
+        line["cpu_baseline"] = cpu_baseline(sample, dec_inp, T)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

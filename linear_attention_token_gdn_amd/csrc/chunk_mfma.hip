@@ -366,8 +366,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         for (int it = 0; it < F::NI; ++it)
 #pragma unroll
             for (int r = 0; r < 4; ++r) vmax = fmaxf(vmax, fabsf(S[it][r]));
-        vmax = fmaxf(vmax, __shfl_xor(vmax, 16));  // the column's four lanes
-        vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
+        vmax = max_over_rows(vmax);  // the column's four lanes
         float sig, isig;
         pow2_scale(vmax, sig, isig);
         f32x4 U[NR], Wp[NR];

@@ -16,12 +16,18 @@
 // parallelism: a chain of T/C chunks no longer waits for the per-chunk triangular solve,
 // which is what bounds a single-pass kernel when there are fewer chains than compute units.
 //
-// Range: U, the state S and Delta scale with v and S0, so their fp16 copies carry powers of
-// two (pow2_scale): prep scales each chunk's U by one chosen from the chunk's largest |v| and
-// stores the inverse next to e^gamma_last; the scan's state wavefronts scale their rows of S
-// per column, and every reader of Delta (kept in fp32 in LDS) scales it per column.  Every
-// fp32 sum is taken back to the true scale exactly, so no magnitude of v or S0 overflows fp16
-// or sinks into its subnormals.
+// Range: U, the state S and Delta scale with v and S0, so their fp16 copies carry a power of
+// two (pow2_scale), taken back out of the fp32 sums exactly.  Prep scales each chunk's U by one
+// chosen from the chunk's largest |v|, and stores with e^gamma_last the inverse scale and three
+// bounds: um = max|U|, wm = D max|W| (>= every row sum of |W|) and nb = C sqrt(D) max|k| um
+// (>= every column 2-norm of K^T dec U).  The scan keeps its fp32 state pre-scaled by one power
+// of two per 16-column tile, chosen from a bound nu on the columns' 2-norms that needs no
+// reduction on the sequential path: for unit keys and beta in [0, 1] every token's map
+// S -> alpha (I - beta k k^T) S has 2-norm at most alpha, so a chunk multiplies a column's
+// 2-norm by at most e^gamma_last before adding at most nb:  nu' = e^gamma_last nu + nb, and
+// |Delta| <= um + wm nu.  The scaled operands then stay below 2^9 in magnitude (no fp16
+// overflow, whatever the magnitude of v and S0); a loose bound only lowers them, and values
+// stay exact to fp16's normal precision down to 2^-14.
 //
 // The workspace holds, per (chain, chunk), the scan kernel's MFMA operands already in
 // fragment order -- for every 16x16x32 A operand one 1 KiB block, lane-major, 16 bytes per
@@ -64,6 +70,8 @@ __device__ __forceinline__ f16x8 cat(f16x4 lo, f16x4 hi) {
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 constexpr int kProgStride = 32;  // unsigned long longs per chain's scan-progress word (256 B)
+// floats at the end of every record: e^gamma_last, 1/usig, um, wm, nb (see below), unused
+constexpr int kRecScalars = 8;
 
 // Rows and workspace records of one chain (sequence s, v head hv).  Dense batches
 // (cu == nullptr): sequence s is rows sT .. sT + T - 1, and the chain's nrec = ceil(T / C)
@@ -100,7 +108,8 @@ template <int D, int C> struct SplitCfg {
     static constexpr size_t OFF_K = OFF_Q + NR * KD * FRAG;   // K^T dec    [NI][KC]
     static constexpr size_t OFF_P = OFF_K + NI * KC * FRAG;   // P          [NR][KC]
     static constexpr size_t OFF_U = OFF_P + NR * KC * FRAG;   // U          [NI][NR] x 512 B
-    static constexpr size_t REC = OFF_U + NI * NR * 64 * 8;   // bytes per (chain, chunk)
+    static constexpr size_t OFF_S = OFF_U + NI * NR * 64 * 8;  // the chunk's scalars, one line
+    static constexpr size_t REC = OFF_S + 128;                  // bytes per (chain, chunk)
     static_assert((D == 64 || D == 128) && (C == 32 || C == 64), "split kernel shape");
 };
 
@@ -114,7 +123,7 @@ __global__ void __launch_bounds__(64)
 prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             const bf16_t *__restrict__ v, const bf16_t *__restrict__ beta,
             const bf16_t *__restrict__ g, unsigned char *__restrict__ ws,
-            float *__restrict__ gchunk, unsigned long long *__restrict__ prog,
+            unsigned long long *__restrict__ prog,
             const int32_t *__restrict__ cu, int nseq, int T, int Hk, int Hv, int nrec,
             unsigned flags) {
     using F = SplitCfg<D, C>;
@@ -201,6 +210,7 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         }
     }
     float usig, uisig;  // U is stored as f16(usig * U); 1/usig goes next to e^gamma_last
+    float kmax;         // max |k| over the chunk
     // ---- the chunk's largest |v| (bf16 magnitudes order as their bit patterns without the
     //      sign) sets usig
     {
@@ -216,7 +226,23 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         for (int off = 1; off < 64; off <<= 1) m = max(m, static_cast<unsigned>(__shfl_xor(static_cast<int>(m), off)));
         m = __builtin_amdgcn_readfirstlane(m);  // the same in every lane
         pow2_scale(__uint_as_float(m << 16), usig, uisig);
-        if (lane == 0) gchunk[2 * (sp.rec0 + c) + 1] = uisig;
+        if constexpr (NORM) {
+            kmax = 1.f;  // normalised rows: |k_i| <= 1
+        } else {
+            u16x8 km8 = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+            for (int a = 0; a < NR; ++a)
+#pragma unroll
+                for (int kk = 0; kk < KD; ++kk) km8 = __builtin_elementwise_max(km8, Kf[a][kk] & (uint16_t)0x7fff);
+            unsigned mk = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mk = max(mk, static_cast<unsigned>(km8[e]));
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1)
+                mk = max(mk, static_cast<unsigned>(__shfl_xor(static_cast<int>(mk), off)));
+            kmax = __uint_as_float(__builtin_amdgcn_readfirstlane(mk) << 16);
+        }
+        if (lane == 0) reinterpret_cast<float *>(rec + F::OFF_S)[1] = uisig;
     }
     if constexpr (NORM) {
         // row 16a + li is spread over the lanes li + 16 lg and the KD fragments of each
@@ -260,7 +286,7 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         s_Gam[lane] = __expf(gv);
         s_dec[lane] = __expf(glast - gv);
         s_bet[lane] = bv;
-        if (lane == 0) gchunk[2 * (sp.rec0 + c)] = __expf(glast);
+        if (lane == 0) reinterpret_cast<float *>(rec + F::OFF_S)[0] = __expf(glast);
     }
     __syncthreads();
     // gate values in registers: accumulator-layout rows 16a + 4lg + rr (one 16-byte read
@@ -371,7 +397,8 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             selkq[h][e] = on ? kOneKQ : 0;
         }
 
-    // per-lane row scalings (rows 16a + 4lg + rr of the accumulator layout)
+    // largest |usig U| and |W| of this lane's fp16 operands, as stored (packed fp16 maxima)
+    f16x4 umax4 = f16x4{f16(0.f), f16(0.f), f16(0.f), f16(0.f)}, wmax4 = umax4;
     // ---- panels: for every 16-column panel p = 2kk + h of the head dimension, the blocked
     //      forward substitution X_a = T_aa (R_a - sum_{cb<a} A_{a,cb} X_cb) for U (R =
     //      diag(beta) V) and W (R = diag(beta e^gamma) K), plus the scan kernel's Q and K^T
@@ -409,8 +436,11 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                 // (T_aa Y)^T = Y^T T_aa^T: lane holds W[16a + li][16p + 4lg + rr]
                 const f32x4 WxT = mma_f16_k16(yw16, tf[a], zero4());
                 wq[a][h] = f16x4{f16(-WxT[0]), f16(-WxT[1]), f16(-WxT[2]), f16(-WxT[3])};
+                wmax4 = __builtin_elementwise_max(wmax4, __builtin_elementwise_abs(wq[a][h]));
                 // U in accumulator layout: the scan kernel's initial Delta accumulator
-                *reinterpret_cast<f16x4 *>(rec + F::OFF_U + ((p * NR + a) * 64 + lane) * 8) = h4(Ux[a]);
+                const f16x4 u16 = h4(Ux[a]);
+                *reinterpret_cast<f16x4 *>(rec + F::OFF_U + ((p * NR + a) * 64 + lane) * 8) = u16;
+                umax4 = __builtin_elementwise_max(umax4, __builtin_elementwise_abs(u16));
             }
             // K^T diag(dec) fragments of row tile p: slots e<4 -> block 2kc, e>=4 -> 2kc+1
 #pragma unroll
@@ -425,6 +455,23 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             *reinterpret_cast<f16x8 *>(rec + F::OFF_Q + ((a * KD + kk) * 64 + lane) * 16) =
                 cat(qq[a][0], qq[a][1]);
         }
+    }
+    // ---- the chunk's bounds for the scan (K^T dec, stored in fp16, may round up by 2^-11:
+    //      covered by the factor-of-128 margin between the scaled operands and fp16's range)
+    float umax = fmaxf(fmaxf(float(umax4[0]), float(umax4[1])), fmaxf(float(umax4[2]), float(umax4[3])));
+    float wmax = fmaxf(fmaxf(float(wmax4[0]), float(wmax4[1])), fmaxf(float(wmax4[2]), float(wmax4[3])));
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        umax = fmaxf(umax, __shfl_xor(umax, off));
+        wmax = fmaxf(wmax, __shfl_xor(wmax, off));
+    }
+    if (lane == 0) {
+        float *sc = reinterpret_cast<float *>(rec + F::OFF_S);
+        sc[2] = umax * uisig;                  // max |U|
+        sc[3] = static_cast<float>(D) * wmax;  // >= max_r sum_i |W[r][i]|
+        // >= every column 2-norm of K^T dec U: ||K^T dec||_2 <= sqrt(C D) max|k|, ||U_j|| <=
+        //    sqrt(C) max|U|
+        sc[4] = static_cast<float>(C) * sqrtf(static_cast<float>(D)) * kmax * sc[2];
     }
 }
 
@@ -473,9 +520,9 @@ template <int D, int C> struct ScanCfg {
     static constexpr int DEPTH = 4;                        // chunks of operands in flight
     static constexpr int NPF = 4;                          // prefetch workgroups per chain
     // chunks the prefetch runs ahead: as many as keep the prefetched records of the chains
-    // sharing an XCD within ~2.25 MiB of its 4 MiB L2 (measured on the 262,144-token
+    // sharing an XCD within ~2.27 MiB of its 4 MiB L2 (measured on the 262,144-token
     // workload, 2 chains per XCD: 16 chunks ahead -15% against 12, 18 or more thrash)
-    static constexpr size_t kPrefetchBytesPerXcd = 2304 * 1024;
+    static constexpr size_t kPrefetchBytesPerXcd = 2320 * 1024;
     static constexpr int kMaxPfd = 16;
     static_assert(DEPTH >= 2, "scan pipeline depth");
 };
@@ -560,7 +607,7 @@ template <int D, int C> struct ScanOps {  // one state wave's operands of one ch
     f16x8 wf[SplitCfg<D, C>::NR];          // -W, rows 16a.., k-step w
     f16x8 kf[2][SplitCfg<D, C>::KC];       // K^T dec, row blocks 2w, 2w+1
     f16x4 uf[ScanCfg<D, C>::NRW];          // usig U of this tile, the row blocks this wave finishes
-    float gc, ui;                          // e^gamma_last of the chunk; 1/usig
+    float sc;                              // lane l: the chunk's scalar l mod kRecScalars
 };
 
 template <int D, int C> struct OutOps {   // one output wave's operands of one chunk
@@ -570,7 +617,7 @@ template <int D, int C> struct OutOps {   // one output wave's operands of one c
 
 template <int D, int C, typename TO>
 __global__ void __launch_bounds__(64 * (ScanCfg<D, C>::NWV + ScanCfg<D, C>::NWO))
-scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchunk,
+scan_kernel(const unsigned char *__restrict__ ws,
             const float *__restrict__ s0, float *__restrict__ sT, TO *__restrict__ o,
             const int32_t *__restrict__ cu, int T, int Hv, int nrec, float scale,
             unsigned long long *__restrict__ prog, int nscan, int pfd) {
@@ -578,10 +625,11 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
     using SC = ScanCfg<D, C>;
     constexpr int NR = F::NR, NI = F::NI, KD = F::KD, KC = F::KC;
     constexpr int NWV = SC::NWV, NRW = SC::NRW, DEPTH = SC::DEPTH;
-    __shared__ f32x4 s_part[NWV][NR][64];  // partial Delta blocks, accumulator layout
-    __shared__ f32x4 s_dlt[NR][64];         // Delta, fp32, accumulator layout
-    __shared__ f16x8 s_st[2][NWV][64];      // starting state of the chunk, B fragments (by parity),
-    __shared__ float s_sg[2][NWV][64];      //   scaled per column by 1 / (these)
+    __shared__ f32x4 s_part[NWV][NR][64];  // partial Delta blocks (scaled as the state)
+    __shared__ f16x4 s_dlt[NR][64];         // Delta, scaled as the next state, accumulator layout
+    __shared__ f16x8 s_st[2][NWV][64];      // starting state of the chunk, B fragments (by parity)
+    __shared__ float s_isg[2][64];          // 1 / the tile's state scale, chunk c in slot c & 1
+    __shared__ float s_nu0[NWV][64];        // initial state: each wave's column sums of squares
     const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     __builtin_assume(w >= 0 && w < NWV + SC::NWO);
@@ -599,6 +647,7 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
 
     if (w >= NWV) {
         // ---- output wavefront: row block a of every chunk, one chunk behind the state
+        lds_barrier();  // the state wavefronts' exchange of the initial state's maxima
         if (nchunks == 0) return;
         const int a = w - NWV;
         const int hv = chain % Hv;
@@ -611,29 +660,17 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
             for (int kc = 0; kc < KC; ++kc)
                 op.pf[kc] = *reinterpret_cast<const f16x8 *>(r + F::OFF_P + ((a * KC + kc) * 64 + lane) * 16);
         };
-        // chunk c - 1's starting state (scaled fp16 slices and their inverse scales) and Delta
-        f16x8 bS[KD];
-        float bG[KD];
-        f32x4 bDl[NR];
+        // chunk c - 1's starting state and Delta (scaled fp16) and their inverse scales
+        f16x8 bS[KD], bD[KC];
+        float bG, bI;
         auto emit = [&](const OutOps<D, C> &op, int c) {
-            f32x4 O = zero4();
+            f32x4 O = zero4(), OD = zero4();
 #pragma unroll
-            for (int kk = 0; kk < KD; ++kk) O += bG[kk] * mma_f16_k32(op.qf[kk], bS[kk], zero4());
-            float m = 0.f;
-#pragma unroll
-            for (int b = 0; b < NR; ++b)
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) m = fmaxf(m, fabsf(bDl[b][rr]));
-            m = fmaxf(m, __shfl_xor(m, 16));  // the column's four lanes
-            m = fmaxf(m, __shfl_xor(m, 32));
-            float sd, isd;
-            pow2_scale(m, sd, isd);
-            f32x4 OD = zero4();
+            for (int kk = 0; kk < KD; ++kk) O = mma_f16_k32(op.qf[kk], bS[kk], O);
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc)
-                if (32 * kc <= 16 * a + 15)
-                    OD = mma_f16_k32(op.pf[kc], cat(h4(sd * bDl[2 * kc]), h4(sd * bDl[2 * kc + 1])), OD);
-            O += isd * OD;
+                if (32 * kc <= 16 * a + 15) OD = mma_f16_k32(op.pf[kc], bD[kc], OD);
+            O = bG * O + bI * OD;
             const int t0 = c * C, L = min(C, sp.len - t0);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
@@ -655,24 +692,19 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
                 __hip_atomic_store(prog + static_cast<size_t>(chain) * kProgStride,
                                    static_cast<unsigned long long>(c), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-            f16x8 nS[KD];
-            float nG[KD];
-            f32x4 nD[NR];
+            f16x8 nS[KD], nD[KC];
 #pragma unroll
-            for (int kk = 0; kk < KD; ++kk) {
-                nS[kk] = s_st[c & 1][kk][lane];
-                nG[kk] = s_sg[c & 1][kk][lane];
-            }
+            for (int kk = 0; kk < KD; ++kk) nS[kk] = s_st[c & 1][kk][lane];
 #pragma unroll
-            for (int b = 0; b < NR; ++b) nD[b] = s_dlt[b][lane];
+            for (int kc = 0; kc < KC; ++kc) nD[kc] = cat(s_dlt[2 * kc][lane], s_dlt[2 * kc + 1][lane]);
+            const float nG = s_isg[c & 1][lane], nI = s_isg[(c + 1) & 1][lane];
             if (c > 0) emit(prev, c - 1);
 #pragma unroll
-            for (int kk = 0; kk < KD; ++kk) {
-                bS[kk] = nS[kk];
-                bG[kk] = nG[kk];
-            }
+            for (int kk = 0; kk < KD; ++kk) bS[kk] = nS[kk];
 #pragma unroll
-            for (int b = 0; b < NR; ++b) bDl[b] = nD[b];
+            for (int kc = 0; kc < KC; ++kc) bD[kc] = nD[kc];
+            bG = nG;
+            bI = nI;
         };
         constexpr int RO = 3;  // ring of operand sets; slot (c mod RO) holds chunk c
         OutOps<D, C> ring[RO];
@@ -703,8 +735,10 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
         return;
     }
 
-    // ---- state wavefront w
-    f32x4 S[2];  // rows 32w + 16i + 4lg + rr of column col
+    // ---- state wavefront w: rows 32w + 16i + 4lg + rr of column col, held in fp32 scaled by
+    //      sig (one power of two for the tile, isg = 1/sig)
+    __builtin_assume(w < NWV);
+    f32x4 S[2];
     const size_t sbase = static_cast<size_t>(chain) * D * D;
     if (s0 != nullptr) {  // one branch, so that all loads are in flight together
 #pragma unroll
@@ -715,11 +749,35 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
     } else {
         S[0] = S[1] = zero4();
     }
-    // this chain's per-chunk decays and U scales (raw buffer, 32-bit data format; reads past
-    // the end give 0)
-    const __amdgpu_buffer_rsrc_t gsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(gchunk + 2 * sp.rec0), 0, 8 * nchunks,
-        0x00020000);
+    float sig, isg;
+    float nu;  // bound on the 2-norm of every column of the tile at the start of the chunk
+    {
+        float q = 0.f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) q += S[i][rr] * S[i][rr];
+        // the column's sum of squares over its four lanes and all state waves (through LDS),
+        // then the tile's largest column 2-norm (rounded up a little for the fp32 sums)
+        const unsigned qu = __float_as_uint(q);
+        const auto a16 = __builtin_amdgcn_permlane16_swap(qu, qu, false, false);
+        q = __uint_as_float(a16[0]) + __uint_as_float(a16[1]);
+        const unsigned qv = __float_as_uint(q);
+        const auto a32 = __builtin_amdgcn_permlane32_swap(qv, qv, false, false);
+        s_nu0[w][lane] = __uint_as_float(a32[0]) + __uint_as_float(a32[1]);
+        lds_barrier();
+        float ss = 0.f;
+#pragma unroll
+        for (int v = 0; v < NWV; ++v) ss += s_nu0[v][lane];
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) ss = fmaxf(ss, __shfl_xor(ss, off));
+        nu = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ss)));
+        nu = 1.0001f * sqrtf(nu);
+        pow2_scale(nu, sig, isg);
+        S[0] *= sig;
+        S[1] *= sig;
+        s_isg[0][lane] = isg;  // every state wave writes the same
+    }
     auto load = [&](ScanOps<D, C> &op, int cc) {
         const unsigned char *r = rec0 + static_cast<size_t>(cc) * F::REC;
 #pragma unroll
@@ -736,33 +794,38 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
             const int a = min(w + j * NWV, NR - 1);  // clamped: loaded but unused past NR
             op.uf[j] = *reinterpret_cast<const f16x4 *>(r + F::OFF_U + ((jt * NR + a) * 64 + lane) * 8);
         }
-        // through a buffer descriptor, so that it stays a vector-memory load: a scalar load
-        // still in flight would hold up every LDS wait, which counts scalar loads too
-        op.gc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gsrc, 0, 8 * cc, 0));
-        op.ui = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gsrc, 0, 8 * cc + 4, 0));
+        // the chunk's scalars: lane l loads scalar l mod 8 of the record's last line (a vector
+        // load -- a scalar load still in flight would hold up every LDS wait, which counts
+        // scalar loads too), then every lane reads them from lanes 0..4
+        op.sc = reinterpret_cast<const float *>(r + F::OFF_S)[lane & (kRecScalars - 1)];
     };
     auto step = [&](const ScanOps<D, C> &op, int c) {
-        // k-step w of the B operand S, scaled per column by a power of two
-        float m = 0.f;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) m = fmaxf(m, fabsf(S[i][rr]));
-        m = fmaxf(m, __shfl_xor(m, 16));  // the column's four lanes
-        m = fmaxf(m, __shfl_xor(m, 32));
-        float sg, isg;
-        pow2_scale(m, sg, isg);
-        const f16x8 bS = cat(h4(sg * S[0]), h4(sg * S[1]));
+        // k-step w of the B operand S (already scaled by sig)
+        const f16x8 bS = cat(h4(S[0]), h4(S[1]));
         s_st[c & 1][w][lane] = bS;  // for the output wavefronts
-        s_sg[c & 1][w][lane] = isg;
         f32x4 pa[NR];
 #pragma unroll
         for (int a = 0; a < NR; ++a) pa[a] = mma_f16_k32(op.wf[a], bS, zero4());
 #pragma unroll
-        for (int a = 0; a < NR; ++a) s_part[w][a][lane] = isg * pa[a];
+        for (int a = 0; a < NR; ++a) s_part[w][a][lane] = pa[a];
         // the independent products back to back, then their LDS writes
         __builtin_amdgcn_sched_group_barrier(0x008, NR, 0);
         __builtin_amdgcn_sched_group_barrier(0x200, NR, 0);
+        // while they run: e^gamma_last, 1/usig, um, wm, nb of the chunk (loaded DEPTH chunks
+        // ago; the builtin moves 32-bit integers) and one scale sgn for Delta and the next state,
+        //   |Delta| <= bd = um + wm nu,   column norms of S_next <= e^gamma_last nu + nb
+        const int sci = __builtin_bit_cast(int, op.sc);
+        const float gc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(sci, 0));
+        const float ui = __builtin_bit_cast(float, __builtin_amdgcn_readlane(sci, 1));
+        const float um = __builtin_bit_cast(float, __builtin_amdgcn_readlane(sci, 2));
+        const float wm = __builtin_bit_cast(float, __builtin_amdgcn_readlane(sci, 3));
+        const float nb = __builtin_bit_cast(float, __builtin_amdgcn_readlane(sci, 4));
+        const float bd = um + wm * nu;
+        nu = gc * nu + nb;
+        float sgn, isgn;
+        pow2_scale(fmaxf(nu, bd), sgn, isgn);
+        const float fu = sgn * ui, fp = sgn * isg, f1 = gc * fp;  // exact: powers of two
+        s_isg[(c + 1) & 1][lane] = isgn;  // for the output wavefronts (every state wave alike)
         lds_barrier();
 #pragma unroll
         for (int j = 0; j < NRW; ++j) {
@@ -771,40 +834,29 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
                 f32x4 p[NWV];
 #pragma unroll
                 for (int v = 0; v < NWV; ++v) p[v] = s_part[v][a][lane];
-                // issue all the partial reads before any of the adds that use them
+                // issue all the partial reads before any of the sums that use them
                 __builtin_amdgcn_sched_group_barrier(0x100, NWV, 0);
-                f32x4 d = op.ui * f32x4{float(op.uf[j][0]), float(op.uf[j][1]), float(op.uf[j][2]),
-                                        float(op.uf[j][3])};
+                f32x4 ps = p[0];
 #pragma unroll
-                for (int v = 0; v < NWV; ++v) d += p[v];
-                s_dlt[a][lane] = d;
+                for (int v = 1; v < NWV; ++v) ps += p[v];
+                const f32x4 d = fu * f32x4{float(op.uf[j][0]), float(op.uf[j][1]),
+                                           float(op.uf[j][2]), float(op.uf[j][3])} + fp * ps;
+                s_dlt[a][lane] = h4(d);  // sgn Delta
             }
         }
         lds_barrier();
-        // S = (sd e^gamma_last S + K^T dec (sd Delta)) / sd, sd a power of two per column
-        f32x4 dl[NR];
-        float md = 0.f;
-#pragma unroll
-        for (int b = 0; b < NR; ++b) {
-            dl[b] = s_dlt[b][lane];
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) md = fmaxf(md, fabsf(dl[b][rr]));
-        }
-        md = fmaxf(md, __shfl_xor(md, 16));
-        md = fmaxf(md, __shfl_xor(md, 32));
-        float sd, isd;
-        pow2_scale(md, sd, isd);
+        // sgn S_next = sgn e^gamma_last S + K^T dec (sgn Delta): exact rescalings
         f16x8 bD[KC];
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) bD[kc] = cat(h4(sd * dl[2 * kc]), h4(sd * dl[2 * kc + 1]));
-        const float gcs = op.gc * sd;
+        for (int kc = 0; kc < KC; ++kc) bD[kc] = cat(s_dlt[2 * kc][lane], s_dlt[2 * kc + 1][lane]);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            S[i] *= gcs;
+            S[i] *= f1;
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) S[i] = mma_f16_k32(op.kf[i][kc], bD[kc], S[i]);
-            S[i] *= isd;
         }
+        sig = sgn;
+        isg = isgn;
     };
 
     if (nchunks > 0) {
@@ -831,7 +883,7 @@ scan_kernel(const unsigned char *__restrict__ ws, const float *__restrict__ gchu
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr)
-                sT[sbase + static_cast<size_t>(32 * w + 16 * i + 4 * lg + rr) * D + col] = S[i][rr];
+                sT[sbase + static_cast<size_t>(32 * w + 16 * i + 4 * lg + rr) * D + col] = isg * S[i][rr];
     }
 }
 
@@ -845,8 +897,8 @@ template <int C> size_t split_records(const PrefillArgs &a) {
 
 template <int D, int C> size_t split_ws_bytes(const PrefillArgs &a) {
     const size_t nrec = split_records<C>(a), chains = static_cast<size_t>(a.B) * a.Hv;
-    // operand records | per-chunk decays and U scales | per-chain scan progress (256 B each)
-    return nrec * SplitCfg<D, C>::REC + (nrec * 2 * sizeof(float) + 255) / 256 * 256 +
+    // operand records | per-chain scan progress (256 B each)
+    return nrec * SplitCfg<D, C>::REC +
            chains * kProgStride * sizeof(unsigned long long);
 }
 
@@ -855,9 +907,7 @@ template <int D, int C, typename TO> hipError_t launch_split_typed(const Prefill
     const int nrec = split_nrec<C>(a);
     const size_t recs = split_records<C>(a), chains = static_cast<size_t>(a.B) * a.Hv;
     unsigned char *ws = static_cast<unsigned char *>(a.ws);
-    float *gch = reinterpret_cast<float *>(ws + recs * SplitCfg<D, C>::REC);
-    unsigned long long *prog = reinterpret_cast<unsigned long long *>(
-        ws + recs * SplitCfg<D, C>::REC + (recs * 2 * sizeof(float) + 255) / 256 * 256);
+    unsigned long long *prog = reinterpret_cast<unsigned long long *>(ws + recs * SplitCfg<D, C>::REC);
     // prefetch workgroups only where the scan leaves compute units idle (one workgroup of
     // either kind fills a compute unit's registers)
     const size_t nscan = chains * (D / 16);
@@ -869,12 +919,12 @@ template <int D, int C, typename TO> hipError_t launch_split_typed(const Prefill
     hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(recs)), dim3(64), 0, a.stream,
                        static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
                        static_cast<const bf16_t *>(a.v), static_cast<const bf16_t *>(a.beta),
-                       static_cast<const bf16_t *>(a.g), ws, gch, npf ? prog : nullptr, a.cu,
+                       static_cast<const bf16_t *>(a.g), ws, npf ? prog : nullptr, a.cu,
                        a.B, a.T, a.Hk, a.Hv, nrec, a.flags);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((scan_kernel<D, C, TO>), dim3(static_cast<unsigned>(nscan + npf)),
-                       dim3(64 * (SC::NWV + SC::NWO)), 0, a.stream, ws, gch, a.s0, a.sT,
+                       dim3(64 * (SC::NWV + SC::NWO)), 0, a.stream, ws, a.s0, a.sT,
                        static_cast<TO *>(a.o), a.cu, a.T, a.Hv, nrec, a.scale,
                        npf ? prog : nullptr, static_cast<int>(nscan), pfd);
     return hipGetLastError();

@@ -162,10 +162,27 @@ __device__ __forceinline__ float inv_norm_from_sumsq(float ss) {
 //      sigma and 1/sigma stay normal fp32 numbers.
 __device__ __forceinline__ void pow2_scale(float m, float &sigma, float &inv_sigma) {
     const int eb = static_cast<int>((__float_as_uint(m) >> 23) & 0xffu);  // biased exponent
-    int e = 135 - eb;  // m in [2^(eb-127), 2^(eb-126))  ->  m * 2^e in [2^8, 2^9)
-    e = (eb == 0 || eb == 255) ? 0 : min(max(e, -100), 100);
+    // m in [2^(eb-127), 2^(eb-126))  ->  m * 2^e in [2^8, 2^9) for e = 135 - eb; arithmetic
+    // selects only (no branch on the value)
+    const int ok = static_cast<int>(static_cast<unsigned>(eb - 1) < 254u);  // not 0, Inf, NaN
+    const int e = ok * min(max(135 - eb, -100), 100);
     sigma = __uint_as_float(static_cast<uint32_t>(127 + e) << 23);
     inv_sigma = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
+}
+
+// Maximum over the four lanes l mod 16 + 16 r (r = 0..3) of a wavefront -- the four lanes of a
+// column in the 16x16 MFMA accumulator and B-operand layouts -- with two VALU lane swaps:
+// permlane16_swap exchanges rows 1, 3 of its first operand with rows 0, 2 of its second (a
+// row being 16 lanes), permlane32_swap the upper half of the first with the lower half of
+// the second; given the same value twice, the maximum of the two results is the maximum over
+// row pairs (0, 1), (2, 3), and then over halves.  No LDS round trip (ds_bpermute) involved.
+__device__ __forceinline__ float max_over_rows(float x) {
+    const unsigned u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const unsigned w = __float_as_uint(y);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 template <typename T> __device__ __forceinline__ void store_f32(T *p, float x);

@@ -2,7 +2,7 @@
 
     python -m linear_attention_token_gdn_amd.profiling trace  <kernel_trace.csv> "<command>"
     python -m linear_attention_token_gdn_amd.profiling traffic <fetch_dir> <write_dir> \
-           <copy_fetch_dir> <copy_write_dir> "<command>"
+           <copy_fetch_dir> <copy_write_dir> "<command>" <prefill_workload_label>
     python -m linear_attention_token_gdn_amd.profiling mfma <label> <mfma_dir> <lds_dir> \
            <algorithmic_flops_per_call> "<command>"
 
@@ -10,8 +10,9 @@
 `rocprofv3 --kernel-trace` CSV).  `traffic` turns two counter passes over the benchmark
 (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`) and the same two passes over a plain 1 GiB copy
 into HBM bytes per launch: each counter is scaled by (known copy bytes / what the counter read
-for the copy).  It prints markdown and writes profiles/traffic.json, which bench.py reports
-while the kernel sources are unchanged.  `mfma` reads one counter pass with
+for the copy).  It prints markdown and writes profiles/traffic.json (the prefill kernels'
+record labelled with the prefill workload, e.g. workload3; the decode kernel's with
+workload4), which bench.py reports while the kernel sources and the workload are unchanged.  `mfma` reads one counter pass with
 `--pmc MfmaUtil MfmaFlopsF16 MfmaFlopsBF16 SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE` and one with
 `--pmc LdsBankConflict SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE` over a run of one prefill
 workload, prints per-kernel matrix-core busy time, matrix-core flops as issued (which include
@@ -147,7 +148,7 @@ def read_counter(dirpath, counter):
     return by_kernel
 
 
-def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, command):
+def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, command, workload):
     fetch, write = read_counter(fetch_dir, "FETCH_SIZE"), read_counter(write_dir, "WRITE_SIZE")
     cf, cw = read_counter(cfetch_dir, "FETCH_SIZE"), read_counter(cwrite_dir, "WRITE_SIZE")
     copy_f = max(statistics.median(v) for v in cf.values())
@@ -174,11 +175,14 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, command):
         pre = [n for n in res if n.startswith(names)]
         if pre:
             rec[key] = {"kernels": pre, "bytes_per_launch": sum(sum(res[n]) for n in pre),
-                        "source_sha256_16": source_hash(SOURCES[key])}
+                        "read_bytes_per_launch": sum(res[n][0] for n in pre),
+                        "write_bytes_per_launch": sum(res[n][1] for n in pre),
+                        "workload": workload, "source_sha256_16": source_hash(SOURCES[key])}
     # the single-token decode kernel (MULTI = false) of the benchmark step
     dec = [n for n in res if n.startswith("decode_kernel") and n.endswith("false>")]
     if dec:
         rec["decode"] = {"kernels": dec, "bytes_per_launch": sum(sum(res[n]) for n in dec),
+                         "workload": "workload4",
                          "source_sha256_16": source_hash(SOURCES["decode"])}
     with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
         json.dump(rec, fh, indent=1)
@@ -254,7 +258,7 @@ def main(argv):
     if argv and argv[0] == "trace":
         print(trace_table(argv[1], argv[2]))
     elif argv and argv[0] == "traffic":
-        print(traffic(*argv[1:6]))
+        print(traffic(*argv[1:7]))
     elif argv and argv[0] == "mfma":
         print(mfma(*argv[1:7]))
     else:

@@ -247,17 +247,17 @@ def test_varlen_workspace(lib):
     assert gdn.gdn_chunk_fwd_plan(16, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16) == "fused"
     assert ws(16, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1) == 0
     # few chains: the split plan; packed sequences take one record slot per sequence and head
-    # beyond the chunks of the total length (records of 72 KiB at d = 128, C = 64; per record
-    # an 8-byte decay and U scale, 256-aligned; a 256-byte progress word per chain)
+    # beyond the chunks of the total length (records of 72 KiB + one 128-byte line of scalars
+    # at d = 128, C = 64; a 256-byte progress word per chain)
     assert gdn.gdn_chunk_fwd_plan(4, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16) == "split"
     slots = 16 * (4096 // 64 + 4)
     assert ws(4, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1) == (
-        slots * 73728 + (slots * 8 + 255) // 256 * 256 + 4 * 16 * 256)
+        slots * (73728 + 128) + 4 * 16 * 256)
     assert ws(0, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1) == 0
     # the plan hint: split for many chains too, with the same slot layout
     slots = 16 * (4096 // 64 + 16)
     assert ws(16, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1, gdn.GDN_PREFER_SPLIT) == (
-        slots * 73728 + (slots * 8 + 255) // 256 * 256 + 16 * 16 * 256)
+        slots * (73728 + 128) + 16 * 16 * 256)
     assert ws(2, 4096, 16, 16, 128, 128, 64, gdn.GDN_F32, 1, gdn.GDN_PREFER_SPLIT) == 0
     assert ws(2, 4096, 16, 16, 128, 128, 64, gdn.GDN_F32, 1) == 0  # fp32: recurrent
 

@@ -130,11 +130,14 @@ const char *gdn_chunk_fwd_plan(int B, int T, int Hk, int Hv, int dk, int dv, int
  * method's use and would overflow).  Derived operands (U, W, the state S, Delta, P) are
  * rounded to fp16 for each product; every sum and the fp32 state itself are never rounded.
  * The value side (v, U, Delta, S, o) is linear in (v, initial_state), so its fp16 copies carry
- * a power of two per value column, chosen per chunk from the column's largest magnitude and
- * taken back out of the fp32 results exactly: v and the state may have any magnitude that
- * fp32 holds (the rounding is relative to each column's largest value in the chunk), and
- * scaling v and initial_state by 2^n scales o and final_state by exactly 2^n.  fp32 inputs run
- * the token-recurrent kernel in fp32.
+ * a power of two, chosen per chunk and taken back out of the fp32 results exactly: v and the
+ * state may have any magnitude that fp32 holds, and scaling v and initial_state by 2^n scales
+ * o and final_state by exactly 2^n.  The single-pass plan takes the scale of each value column
+ * from its largest magnitude in the chunk; the split plan takes one per 16 value columns from
+ * a bound on the state's column norms that holds for keys of norm at most 1 (beta |k|^2 <= 2;
+ * unit keys rounded to bf16 qualify), so keys far above unit norm may overflow there -- pass
+ * GDN_QK_L2NORM (gdn_chunk_fwd_varlen) when the keys are not normalised.  fp32 inputs run the
+ * token-recurrent kernel in fp32.
  */
 gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v, const void *beta,
                            const void *g, const float *initial_state, void *o,

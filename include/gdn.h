@@ -51,13 +51,15 @@ typedef enum gdn_status {
                                 o aliasing an input, workspace too small */
     GDN_ERR_UNSUPPORTED = 2, /* valid but not implemented: head sizes, chunk size or dtype pair */
     GDN_ERR_HIP = 3,         /* the HIP runtime refused a launch */
-    GDN_ERR_SCRATCH_TOO_SMALL = 4 /* gdn_chunk_fwd_noalloc: the sizes need more workspace than
-                                     its static scratch holds (GDN_NOALLOC_SCRATCH_BYTES) */
+    GDN_ERR_SCRATCH_TOO_SMALL = 4, /* gdn_chunk_fwd_noalloc: the sizes need more workspace than
+                                      its static scratch holds (GDN_NOALLOC_SCRATCH_BYTES) */
+    GDN_STATUS_MAX_ = 0x7fffffff   /* not a status: makes every int a valid value in C++ */
 } gdn_status_t;
 
 typedef enum gdn_dtype {
     GDN_F32 = 0,
-    GDN_BF16 = 1
+    GDN_BF16 = 1,
+    GDN_DTYPE_MAX_ = 0x7fffffff    /* not a dtype: any int a caller passes is rejected, not UB */
 } gdn_dtype_t;
 
 /*

@@ -23,7 +23,8 @@ import ctypes
 import os
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libgdn.so")
+# GDN_LIBRARY: another build of the library (the sanitizer test loads an instrumented one)
+LIB_PATH = os.environ.get("GDN_LIBRARY") or os.path.join(PKG_DIR, "libgdn.so")
 
 ABI_VERSION = 5  # the GDN_ABI_VERSION of include/gdn.h that these signatures follow
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3

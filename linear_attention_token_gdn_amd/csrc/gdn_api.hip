@@ -67,6 +67,7 @@ const char *gdn_status_string(gdn_status_t s) {
     case GDN_ERR_SCRATCH_TOO_SMALL:
         return "GDN_ERR_SCRATCH_TOO_SMALL (the sizes need more workspace than the "
                "GDN_NOALLOC_SCRATCH_BYTES of gdn_chunk_fwd_noalloc's static scratch)";
+    default: break;
     }
     return "GDN_ERR_UNKNOWN";
 }

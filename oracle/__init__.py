@@ -23,7 +23,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdn_oracle.c")
-_LIB = os.path.join(_HERE, "libgdn_oracle.so")
+# GDN_ORACLE_LIB: another build of gdn_oracle.c (the sanitizer test loads an instrumented one)
+_LIB = os.environ.get("GDN_ORACLE_LIB") or os.path.join(_HERE, "libgdn_oracle.so")
 _lock = threading.Lock()
 _lib = None
 

@@ -341,7 +341,7 @@ def test_qsa_workspace_and_empty_calls(lib):
 def test_calibration_library():
     """libgdn_calib.so (the benchmark's attainable-peak kernels) exports what gdn_calib.h
     declares and rejects bad arguments before launching anything."""
-    path = os.path.join(os.path.dirname(gdn.LIB_PATH), "libgdn_calib.so")
+    path = os.path.join(gdn.PKG_DIR, "libgdn_calib.so")
     if not os.path.exists(path):
         from linear_attention_token_gdn_amd import build
         build.build()

@@ -313,7 +313,9 @@ def measured_peaks(torch, dev, stream):
     cal = ctypes.CDLL(os.path.join(ROOT, "linear_attention_token_gdn_amd", "libgdn_calib.so"))
     cal.gdn_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                    ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
-    cal.gdn_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    cal.gdn_calib_mfma_clock.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    cal.gdn_calib_wall_clock_khz.restype = ctypes.c_int
 
     def ok(rc):
         if rc != 0:
@@ -327,24 +329,46 @@ def measured_peaks(torch, dev, stream):
                                                      blocks, 3, stream.cuda_stream)))
                  for blocks in (1024, 2048, 4096))
     del src, dst
+    # the matrix-core loop in both product shapes (the same flops per round), with the engine
+    # clock each workgroup's wavefront 0 saw: shader-clock cycles over wall-clock ticks
     blocks, iters = 2048, 2048
     out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
-    mfma_ms = timed(lambda: ok(cal.gdn_calib_mfma(out.data_ptr(), blocks, iters,
-                                                  stream.cuda_stream)))
-    del out
+    clk = torch.zeros(2 * blocks, dtype=torch.int64, device=dev)
+    wall_khz = cal.gdn_calib_wall_clock_khz()
+    loop = {}
+    for form in (0, 1):
+        ms = timed(lambda: ok(cal.gdn_calib_mfma_clock(out.data_ptr(), clk.data_ptr(), blocks,
+                                                        iters, form, stream.cuda_stream)))
+        torch.cuda.synchronize()
+        c = clk.view(blocks, 2).double().cpu()
+        mhz = (c[:, 0] / c[:, 1]).median().item() * wall_khz / 1e3 if wall_khz > 0 else None
+        loop[form] = (ms, mhz)
+    del out, clk
     torch.cuda.synchronize()
+    mfma_ms = loop[0][0]
     res = {"torch_copy_GBps": round(2 * n * 4 / (copy_ms * 1e-3) / 1e9, 1),
            "hip_copy_GBps": round(2 * n * 4 / (hip_copy_ms * 1e-3) / 1e9, 1),
            "hip_inplace_update_GBps": round(2 * n * 4 / (upd_ms * 1e-3) / 1e9, 1),
            "bf16_gemm_TFLOPs": round(2 * m ** 3 / (mm_ms * 1e-3) / 1e12, 1),
            "fp16_mfma_loop_TFLOPs": round(blocks * 4 * iters * 8 * 16384 / (mfma_ms * 1e-3) / 1e12, 1),
+           "fp16_mfma32_loop_TFLOPs": round(blocks * 4 * iters * 4 * 32768 / (loop[1][0] * 1e-3) / 1e12, 1),
+           "mfma_loop_sclk_MHz": [None if loop[f][1] is None else round(loop[f][1]) for f in (0, 1)],
            "what": "median of 5: 1 GiB device copy (torch; calibration kernel, best of 3 grids "
                    "x 4 variants); "
                    "8192 x 8192 x 8192 bf16 torch.matmul; 8 independent 16x16x32 fp16 MFMA "
-                   "chains per wavefront, 8 wavefronts per SIMD"}
+                   "chains per wavefront (mfma32: 4 independent 32x32x16 chains), 8 wavefronts "
+                   "per SIMD; mfma_loop_sclk_MHz: the engine clock during each loop (median "
+                   "over workgroups of shader-clock cycles / wall-clock ticks)"}
+    # the loop against the nominal peak scaled to the clock it ran at (the nominal dense fp16
+    # peak assumes 2400 MHz)
+    for f, key in ((0, "fp16_mfma_loop_TFLOPs"), (1, "fp16_mfma32_loop_TFLOPs")):
+        if loop[f][1]:
+            res.setdefault("mfma_loop_frac_of_nominal_at_clock", []).append(
+                round(res[key] / (MFMA_BF16_PEAK_TFLOPS * loop[f][1] / 2400.0), 3))
     res["copy_GBps"] = max(res["torch_copy_GBps"], res["hip_copy_GBps"],
                            res["hip_inplace_update_GBps"])
-    res["mfma_TFLOPs"] = max(res["bf16_gemm_TFLOPs"], res["fp16_mfma_loop_TFLOPs"])
+    res["mfma_TFLOPs"] = max(res["bf16_gemm_TFLOPs"], res["fp16_mfma_loop_TFLOPs"],
+                             res["fp16_mfma32_loop_TFLOPs"])
     return res
 
 

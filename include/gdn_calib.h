@@ -37,6 +37,21 @@ int gdn_calib_copy(const void *src, void *dst, size_t bytes, int blocks, int var
  */
 int gdn_calib_mfma(float *out, int blocks, int iters, void *stream);
 
+/*
+ * The same loop with a clock record: form 0 runs 8 independent v_mfma_f32_16x16x32_f16 chains
+ * per wavefront (flops as above), form 1 four independent v_mfma_f32_32x32x16_f16 chains
+ * (blocks * 4 * iters * 4 * 32768 flops).  Wavefront 0 of workgroup b writes
+ * clk[2b] = shader-clock cycles and clk[2b + 1] = constant-rate wall-clock ticks spent in its
+ * loop; cycles / ticks * gdn_calib_wall_clock_khz() is the engine clock (kHz) during the loop.
+ * out: device pointer to blocks * 256 floats; clk: device pointer to 2 * blocks unsigned
+ * 64-bit integers.  1 <= iters <= 1 << 20, form 0 or 1.
+ */
+int gdn_calib_mfma_clock(float *out, unsigned long long *clk, int blocks, int iters, int form,
+                         void *stream);
+
+/* The rate of the constant wall clock of the current device in kHz, or -1 on error. */
+int gdn_calib_wall_clock_khz(void);
+
 #ifdef __cplusplus
 }
 #endif

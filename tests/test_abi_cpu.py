@@ -349,7 +349,8 @@ def test_calibration_library():
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "gdn_calib.h")).read(),
                   flags=re.S)
     names = sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
-    assert names == ["gdn_calib_copy", "gdn_calib_mfma"]
+    assert names == ["gdn_calib_copy", "gdn_calib_mfma", "gdn_calib_mfma_clock",
+                     "gdn_calib_wall_clock_khz"]
     for n in names:
         assert isinstance(getattr(cal, n), ctypes._CFuncPtr), n
     vp, sz, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
@@ -363,3 +364,7 @@ def test_calibration_library():
     assert cal.gdn_calib_copy(1 << 20, 1 << 30, 32768, 64, 3, None) == 1   # in place: src == dst
     assert cal.gdn_calib_mfma(None, 64, 16, None) == 1
     assert cal.gdn_calib_mfma(1 << 20, 64, 0, None) == 1
+    cal.gdn_calib_mfma_clock.argtypes = [vp, vp, i, i, i, vp]
+    assert cal.gdn_calib_mfma_clock(1 << 20, None, 64, 16, 0, None) == 1
+    assert cal.gdn_calib_mfma_clock(1 << 20, 1 << 30, 64, 16, 2, None) == 1  # no such form
+    assert cal.gdn_calib_mfma_clock(1 << 20, 1 << 30, 0, 16, 0, None) == 1

@@ -687,6 +687,9 @@ scan_kernel(const unsigned char *__restrict__ ws,
         const bool publish = prog != nullptr && a == 0 && jt == 0;
         auto step = [&](const OutOps<D, C> &prev, int c) {
             lds_barrier();
+            // the scales between the barriers: slot c & 1 is written again (for chunk c + 2)
+            // before barrier 1 of the next step, i.e. possibly before a read after barrier 2
+            const float nG = s_isg[c & 1][lane], nI = s_isg[(c + 1) & 1][lane];
             lds_barrier();
             if (publish && lane == 0)  // the state wavefronts are on chunk c
                 __hip_atomic_store(prog + static_cast<size_t>(chain) * kProgStride,
@@ -697,7 +700,6 @@ scan_kernel(const unsigned char *__restrict__ ws,
             for (int kk = 0; kk < KD; ++kk) nS[kk] = s_st[c & 1][kk][lane];
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) nD[kc] = cat(s_dlt[2 * kc][lane], s_dlt[2 * kc + 1][lane]);
-            const float nG = s_isg[c & 1][lane], nI = s_isg[(c + 1) & 1][lane];
             if (c > 0) emit(prev, c - 1);
 #pragma unroll
             for (int kk = 0; kk < KD; ++kk) bS[kk] = nS[kk];

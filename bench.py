@@ -667,12 +667,13 @@ def main():
             dom = "decode"
 
     # ---- several tokens per decode call (not part of the step): T tokens of the decode
-    #      workload applied with one read and one write of every state
+    #      workload applied with one read and one write of every state (token by token for
+    #      T < 5, as one chunk of the chunk form on the matrix cores from T = 5 on)
     multi = None
     if not args.no_decode:
         multi = {}
         st_out = torch.empty_like(state)
-        for Tn, in_place in ((2, True), (4, True), (8, True), (8, False)):
+        for Tn, in_place in ((2, True), (4, True), (8, True), (8, False), (16, True)):
             mq, mk, mv = (dt[n][:, :Tn].contiguous() for n in ("q", "k", "v"))
             mb, mg = (dt[n][:, :Tn].contiguous() for n in ("beta", "g"))
             mo = torch.empty((dc["B"], Tn, dc["Hv"], dc["dv"]), dtype=torch.float32, device=dev)
@@ -689,6 +690,7 @@ def main():
             ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
             sb, tb = decode_bytes(dc["B"], dc["Hk"], dc["Hv"], dc["dk"], dc["dv"], Tn)
             multi["T%d%s" % (Tn, "" if in_place else "_to_separate_state")] = {
+                                 "kernel": "token" if Tn < 5 else "chunk (matrix cores)",
                                  "us_per_call": round(ms * 1e3, 2),
                                  "tokens_per_s": round(dc["B"] * Tn / (ms * 1e-3), 1),
                                  "state_GBps": round(sb / (ms * 1e-3) / 1e9, 1),

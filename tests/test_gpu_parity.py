@@ -274,9 +274,10 @@ def test_decode_tokens_matches_oracle(T, dk, dv, dtype):
 
 
 def test_decode_tokens_equals_repeated_decode_steps():
-    """One call over T tokens performs exactly the arithmetic of T single-token calls."""
-    inp = make_inputs(4, 6, 2, 4, 128, 128, dtype="bf16", s0_std=0.02, seed=610)
-    o1, S1 = run_decode_steps(inp, 6, scale=0.7)
+    """Below the matrix-core form's threshold (T < 5) one call over T tokens performs exactly
+    the arithmetic of T single-token calls."""
+    inp = make_inputs(4, 3, 2, 4, 128, 128, dtype="bf16", s0_std=0.02, seed=610)
+    o1, S1 = run_decode_steps(inp, 3, scale=0.7)
     o2, S2, _ = run_decode_tokens(inp, scale=0.7, in_place=True)
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(S1, S2)

@@ -205,7 +205,14 @@ gdn_status_t gdn_decode_step(const void *q, const void *k, const void *v, const 
  *                               input or either state
  *
  * T = 0 copies state_in (or zeros) to state_out and touches nothing else.  Any T >= 0 is
- * accepted; the kernel walks the T tokens in order, so long runs belong to gdn_chunk_fwd.
+ * accepted.  Up to T = 4 (and for fp32 inputs, dk != dv, head sizes other than 64 and 128,
+ * or q, k, v not 16-byte aligned) the tokens are applied one after the other in fp32, exactly
+ * the arithmetic of T gdn_decode_step calls.  From T = 5 on, bf16 inputs with dk = dv in
+ * {64, 128} take the chunk form of Eq. (1) over chunks of up to 16 tokens: products with the
+ * state on the matrix cores from fp16 copies (power-of-two scaled per column, so v and the
+ * state may have any magnitude; |q|, |k| < 65504), the state itself updated in fp32; the
+ * precision is that of the bf16 chunk-parallel prefill.  Long runs still belong to
+ * gdn_chunk_fwd.
  * flags: the input prologue (GDN_QK_L2NORM | GDN_BETA_LOGIT | GDN_G_LOGIT, or 0).
  * Supported: dk, dv in {16, 32, 64, 128}.  B = 0 is a no-op.
  */

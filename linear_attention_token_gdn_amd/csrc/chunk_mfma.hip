@@ -117,7 +117,7 @@ template <int D, int C> struct Smem {
     f16 wn[C][F::PQ];         // -W (columns permuted)
     f16 an[C][F::PA];         // -A, off-diagonal 16x16 blocks (lower)
     f16 td[F::NR][16][24];    // inverses of the diagonal blocks of I + A, fp16
-    float ad[F::NR][16][20];  // diagonal blocks of A, fp32
+    float adT[F::NR][16][20]; // diagonal blocks of A, fp32, transposed: [block][col][row]
     float gam[C];             // gamma (chunk-local cumulative log-gate)
     float Gam[C];             // exp(gamma)
     float dec[C];             // exp(gamma_last - gamma)
@@ -311,7 +311,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                     } else {
                         const float av = (s < r) ? br[rr] * d * acc[rr] : 0.f;
                         if (st == rt)
-                            sm.ad[rt][4 * lg + rr][li] = av;
+                            sm.adT[rt][li][4 * lg + rr] = av;
                         else
                             sm.an[r][s] = f16(-av);
                     }
@@ -323,27 +323,39 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                     sm.p[16 * rt + 4 * lg + rr][kperm(16 * (rt + 1) + li)] = f16(0.f);
             }
         }
-        for (int idx = tid; idx < D * (C / 8); idx += NT) {
-            const int i = idx % D, s8 = idx / D, ki = kperm(i);
-            f16x8 x;  // stored positions 8 s8 .. 8 s8 + 7 of row i of K^T
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = sm.k[kunperm(s8 * 8 + e)][ki];
-            *reinterpret_cast<f16x8 *>(&sm.kt[i][s8 * 8]) = x;
-        }
         lds_barrier();
 
-        // ---- stage 2: inverse of each 16x16 diagonal block of I + A (forward substitution)
-        if (wave < NR && lane < 16) {
+        // ---- stage 2: wavefront 0 inverts the 16x16 diagonal blocks of I + A (lane (li, lg):
+        //      column li of block lg, forward substitution by columns: step s updates every
+        //      later row with x_s, so the dependent chain is 16 steps long); meanwhile the
+        //      other wavefronts build K^T for the state update and the W panels
+        if (wave == 0) {
             float x[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = (r == lane) ? 1.f : 0.f;
+            for (int r = 0; r < 16; ++r) x[r] = (r == li) ? 1.f : 0.f;
+            if (lg < NR) {
 #pragma unroll
-                for (int s = 0; s < r; ++s) acc -= sm.ad[wave][r][s] * x[s];
-                x[r] = acc;
+                for (int st = 0; st < 15; ++st) {
+                    float colv[16];
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const f32x4 t = *reinterpret_cast<const f32x4 *>(&sm.adT[lg][st][4 * r4]);
+                        colv[4 * r4] = t[0], colv[4 * r4 + 1] = t[1], colv[4 * r4 + 2] = t[2], colv[4 * r4 + 3] = t[3];
+                    }
+#pragma unroll
+                    for (int r = st + 1; r < 16; ++r) x[r] -= colv[r] * x[st];
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sm.td[lg][r][li] = f16(x[r]);
             }
+        } else {
+            for (int idx = tid - 64; idx < D * (C / 8); idx += NT - 64) {
+                const int i = idx % D, s8 = idx / D, ki = kperm(i);
+                f16x8 x;  // stored positions 8 s8 .. 8 s8 + 7 of row i of K^T
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sm.td[wave][r][lane] = f16(x[r]);
+                for (int e = 0; e < 8; ++e) x[e] = sm.k[kunperm(s8 * 8 + e)][ki];
+                *reinterpret_cast<f16x8 *>(&sm.kt[i][s8 * 8]) = x;
+            }
         }
         lds_barrier();
 

@@ -51,8 +51,9 @@ typedef enum gdn_status {
                                 o aliasing an input, workspace too small */
     GDN_ERR_UNSUPPORTED = 2, /* valid but not implemented: head sizes, chunk size or dtype pair */
     GDN_ERR_HIP = 3,         /* the HIP runtime refused a launch */
-    GDN_ERR_SCRATCH_TOO_SMALL = 4, /* gdn_chunk_fwd_noalloc: the sizes need more workspace than
-                                      its static scratch holds (GDN_NOALLOC_SCRATCH_BYTES) */
+    GDN_ERR_SCRATCH_TOO_SMALL = 4, /* gdn_chunk_fwd_noalloc: even one chunk per segment needs
+                                      more workspace than its static scratch holds
+                                      (GDN_NOALLOC_SCRATCH_BYTES) */
     GDN_STATUS_MAX_ = 0x7fffffff   /* not a status: makes every int a valid value in C++ */
 } gdn_status_t;
 
@@ -93,7 +94,11 @@ const char *gdn_status_string(gdn_status_t status);
 
 /*
  * Bytes of device workspace gdn_chunk_fwd needs for these sizes (0 means none; pass
- * workspace = NULL then).  Returns 0 for sizes gdn_chunk_fwd would reject.
+ * workspace = NULL then).  Returns 0 for sizes gdn_chunk_fwd would reject.  The "split" plan
+ * keeps per-chunk records there for a segment of chunks: at most 2 GiB of them (or the
+ * number of bytes the environment variable GDN_SPLIT_RECORD_BYTES gives), plus 256 B and one
+ * fp32 state per chain.  Longer sequences run segment after segment, with the state carried
+ * between them and the same results bit for bit, so the size stays bounded for any T.
  */
 size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
                                     gdn_dtype_t in_dtype);
@@ -154,10 +159,12 @@ gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v, const vo
  * workspace (gdn_chunk_fwd_workspace_size(...) > 0) it uses a static scratch buffer of
  * GDN_NOALLOC_SCRATCH_BYTES that the library holds in every GPU's memory from its load until
  * the process ends; the call itself allocates nothing (no hipMalloc, no allocating library
- * routine).  Sizes whose workspace exceeds GDN_NOALLOC_SCRATCH_BYTES return
- * GDN_ERR_SCRATCH_TOO_SMALL before anything is launched (80 MiB holds the split plan's
- * workspace for up to 1,100 chunk-heads at dk = dv = 128 and chunk 64, e.g. T = 4096 with 16
- * heads).  Every call on one GPU shares that GPU's scratch and leaves its contents behind:
+ * routine).  The split plan then runs in segments of as many chunks as the scratch holds
+ * (about 1,000 chunk-heads at dk = dv = 128 and chunk 64, e.g. 64 chunks of 16 heads): the
+ * same results, bit for bit, at any T, and slower than one pass for long sequences.  A size
+ * whose smallest workspace (one chunk per segment) exceeded GDN_NOALLOC_SCRATCH_BYTES would
+ * return GDN_ERR_SCRATCH_TOO_SMALL before anything is launched; no size the plans take comes
+ * near it.  Every call on one GPU shares that GPU's scratch and leaves its contents behind:
  * calls that can run at the same time on one GPU (different streams without ordering between
  * them, or different host threads) race and must be serialised by the caller.  The first
  * call on each device looks up the scratch's device address once (hipGetSymbolAddress, with

@@ -37,6 +37,7 @@
 // the accumulator (column) layout, and a product whose left factor is the transpose of an
 // accumulator-layout tile takes that tile's registers as its A operand unchanged.
 #include <algorithm>
+#include <stdlib.h>
 
 #include "gdn_internal.h"
 
@@ -73,26 +74,43 @@ constexpr int kProgStride = 32;  // unsigned long longs per chain's scan-progres
 // floats at the end of every record: e^gamma_last, 1/usig, um, wm, nb (see below), unused
 constexpr int kRecScalars = 8;
 
-// Rows and workspace records of one chain (sequence s, v head hv).  Dense batches
-// (cu == nullptr): sequence s is rows sT .. sT + T - 1, and the chain's nrec = ceil(T / C)
-// records are consecutive from chain * nrec.  Packed sequences: head hv owns
-// nrec = floor(T / C) + num_seqs record slots, and sequence s (starting at row a_s) takes
-// the slots from floor(a_s / C) + s on.  Since ceil(len / C) <= floor((a_s mod C + len) / C)
-// + 1, consecutive sequences never share a slot and the last one ends below nrec (for any
-// offsets, as seq_range clamps them into [0, T]).
+// Rows and record slots of one chain (sequence s, v head hv).  Every record belongs to a slot
+// position of a unit: dense batches (cu == nullptr) give each chain (the unit) nrec =
+// ceil(T / C) slots, chunk c in slot c.  Packed sequences give each head hv (the unit)
+// nrec = floor(T / C) + num_seqs slots, and sequence s (starting at row a_s) takes the slots
+// from floor(a_s / C) + s on.  Since ceil(len / C) <= floor((a_s mod C + len) / C) + 1,
+// consecutive sequences never share a slot and the last one ends below nrec (for any offsets,
+// as seq_range clamps them into [0, T]).
+// The kernels run over a segment of slot positions [lo, lo + L) at a time, L fixed by the
+// workspace: the record of slot position p of unit u sits at u L + p - lo, so the workspace
+// holds L slots of every unit whatever the sequence length.
 struct ChainSpan {
-    size_t row0, rec0;  // first token row; first record
-    int len, nch;       // tokens; chunks
+    size_t row0;    // first token row
+    int len, nch;   // tokens; chunks
+    int base;       // slot position of chunk 0
+    int unit;       // the chain (dense) or the head (packed) whose slots it uses
 };
 template <int C>
-__device__ __forceinline__ ChainSpan chain_span(const int32_t *cu, int T, int Hv, int nrec,
-                                                int chain) {
+__device__ __forceinline__ ChainSpan chain_span(const int32_t *cu, int T, int Hv, int chain) {
     const int s = chain / Hv, hv = chain - s * Hv;
     ChainSpan r;
     seq_range(cu, T, s, r.row0, r.len);
     r.nch = (r.len + C - 1) / C;
-    r.rec0 = cu == nullptr ? static_cast<size_t>(chain) * nrec
-                           : static_cast<size_t>(hv) * nrec + r.row0 / C + s;
+    r.base = cu == nullptr ? 0 : static_cast<int>(r.row0 / C) + s;
+    r.unit = cu == nullptr ? chain : hv;
+    return r;
+}
+// The chunks [cb, cb + n) of a chain that fall into the segment [lo, lo + L), and the address
+// of the record of chunk cb.
+struct SegSpan {
+    int cb, n;
+    size_t rec;  // record index of chunk cb in the workspace
+};
+__device__ __forceinline__ SegSpan seg_span(const ChainSpan &sp, int lo, int L) {
+    SegSpan r;
+    r.cb = max(0, lo - sp.base);
+    r.n = max(0, min(sp.nch, lo + L - sp.base) - r.cb);
+    r.rec = static_cast<size_t>(sp.unit) * L + (sp.base + r.cb - lo);
     return r;
 }
 
@@ -124,8 +142,8 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             const bf16_t *__restrict__ v, const bf16_t *__restrict__ beta,
             const bf16_t *__restrict__ g, unsigned char *__restrict__ ws,
             unsigned long long *__restrict__ prog,
-            const int32_t *__restrict__ cu, int nseq, int T, int Hk, int Hv, int nrec,
-            unsigned flags) {
+            const int32_t *__restrict__ cu, int nseq, int T, int Hk, int Hv, int seg_lo,
+            int seg_len, unsigned flags) {
     using F = SplitCfg<D, C>;
     constexpr int NR = F::NR, KD = F::KD;
     // products with a K or Q operand: bf16 inputs as stored, or fp16 once normalised
@@ -149,14 +167,17 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     // the scan kernel's progress words start at chunk 0 (it runs after this kernel completes)
     if (prog != nullptr && blockIdx.x == 0)
         for (int i = threadIdx.x; i < nchains; i += 64) prog[static_cast<size_t>(i) * kProgStride] = 0ull;
-    int c, chain;
+    // slot position seg_lo + pl of the segment; its record goes to unit * seg_len + pl
+    int c, chain, pl;
     if (cu == nullptr) {
-        c = blockIdx.x / nchains;
-        chain = blockIdx.x - c * nchains;
+        pl = blockIdx.x / nchains;
+        chain = blockIdx.x - pl * nchains;
+        c = seg_lo + pl;
     } else {
         // the sequence whose slots start last at or before this slot (the slot starts
         // floor(a_s / C) + s increase with s)
-        const int slot = blockIdx.x / Hv, h = blockIdx.x - slot * Hv;
+        pl = blockIdx.x / Hv;
+        const int slot = seg_lo + pl, h = blockIdx.x - pl * Hv;
         int s = -1;
         for (int i0 = 0; i0 < nseq; i0 += 64) {
             const int i = i0 + lane;
@@ -168,12 +189,12 @@ prep_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         chain = s * Hv + h;
         c = slot - (min(max(cu[s], 0), T) / C + s);  // the chunk of sequence s in this slot
     }
-    const ChainSpan sp = chain_span<C>(cu, T, Hv, nrec, chain);
+    const ChainSpan sp = chain_span<C>(cu, T, Hv, chain);
     if (c >= sp.nch) return;  // a slot no chunk uses
     const int G = Hv / Hk;
     const int hv = chain % Hv, hq = hv / G;
     const int t0 = c * C, L = min(C, sp.len - t0);
-    unsigned char *rec = ws + (sp.rec0 + c) * F::REC;
+    unsigned char *rec = ws + (static_cast<size_t>(sp.unit) * seg_len + pl) * F::REC;
 
     // ---- gate loads first: the vector-memory counter is in order, so their wait below
     //      does not include the K, Q, V loads issued after them
@@ -542,9 +563,9 @@ template <int D, int C> struct ScanCfg {
 template <int D, int C>
 __device__ void prefetch_records(const unsigned char *__restrict__ ws,
                                  unsigned long long *__restrict__ prog,
-                                 const int32_t *__restrict__ cu, int T, int Hv, int nrec,
-                                 int nchains, int p, int w, int nwaves, int lane, int *s_done,
-                                 int pfd) {
+                                 const int32_t *__restrict__ cu, int T, int Hv, int seg_lo,
+                                 int seg_len, int nchains, int p, int w, int nwaves, int lane,
+                                 int *s_done, int pfd) {
     using F = SplitCfg<D, C>;
     using SC = ScanCfg<D, C>;
     constexpr int LINES = static_cast<int>(F::REC / 128);
@@ -560,9 +581,9 @@ __device__ void prefetch_records(const unsigned char *__restrict__ ws,
         chain = p % nchains;
         part = p / nchains;
     }
-    const ChainSpan sp = chain_span<C>(cu, T, Hv, nrec, chain);
-    const int nchunks = sp.nch;
-    const unsigned char *rec0 = ws + sp.rec0 * F::REC;
+    const SegSpan sg = seg_span(chain_span<C>(cu, T, Hv, chain), seg_lo, seg_len);
+    const int nchunks = sg.n;
+    const unsigned char *rec0 = ws + sg.rec * F::REC;
     unsigned long long *pw = prog + static_cast<size_t>(chain) * kProgStride;
     unsigned acc = 0;
     int polls = 0;
@@ -617,9 +638,9 @@ template <int D, int C> struct OutOps {   // one output wave's operands of one c
 
 template <int D, int C, typename TO>
 __global__ void __launch_bounds__(64 * (ScanCfg<D, C>::NWV + ScanCfg<D, C>::NWO))
-scan_kernel(const unsigned char *__restrict__ ws,
-            const float *__restrict__ s0, float *__restrict__ sT, TO *__restrict__ o,
-            const int32_t *__restrict__ cu, int T, int Hv, int nrec, float scale,
+scan_kernel(const unsigned char *__restrict__ ws, const float *s0, float *carry,
+            float *__restrict__ nucarry, TO *__restrict__ o, const int32_t *__restrict__ cu,
+            int T, int Hv, int seg_lo, int seg_len, float scale,
             unsigned long long *__restrict__ prog, int nscan, int pfd) {
     using F = SplitCfg<D, C>;
     using SC = ScanCfg<D, C>;
@@ -634,16 +655,25 @@ scan_kernel(const unsigned char *__restrict__ ws,
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     __builtin_assume(w >= 0 && w < NWV + SC::NWO);
     if (static_cast<int>(blockIdx.x) >= nscan) {
-        prefetch_records<D, C>(ws, prog, cu, T, Hv, nrec, nscan / NI, blockIdx.x - nscan, w,
-                               NWV + SC::NWO, lane, reinterpret_cast<int *>(&s_st[0][0][0]), pfd);
+        prefetch_records<D, C>(ws, prog, cu, T, Hv, seg_lo, seg_len, nscan / NI,
+                               blockIdx.x - nscan, w, NWV + SC::NWO, lane,
+                               reinterpret_cast<int *>(&s_st[0][0][0]), pfd);
         return;
     }
     int chain, jt;
     chain_tile_map(blockIdx.x, nscan, NI, chain, jt);
     const int col = 16 * jt + li;
-    const ChainSpan sp = chain_span<C>(cu, T, Hv, nrec, chain);
-    const int nchunks = sp.nch;  // 0 for an empty sequence: final state = initial state
-    const unsigned char *rec0 = ws + sp.rec0 * F::REC;
+    const ChainSpan sp = chain_span<C>(cu, T, Hv, chain);
+    const SegSpan sg = seg_span(sp, seg_lo, seg_len);
+    // chunks cb .. cb + nchunks - 1 of the chain fall into this segment; none and not an empty
+    // sequence on the first segment (which copies its initial state): nothing to do here
+    const int cb = sg.cb, nchunks = sg.n;
+    if (nchunks == 0 && !(sp.nch == 0 && seg_lo == 0)) return;  // the whole workgroup
+    const unsigned char *rec0 = ws + sg.rec * F::REC;
+    // the state enters from s0 at the chain's first chunk, else from the previous segment's
+    // carry, and leaves through the carry (the final state after the last segment; may alias
+    // s0: a chain writes it only after reading its own)
+    const float *sin = cb == 0 ? s0 : carry;
 
     if (w >= NWV) {
         // ---- output wavefront: row block a of every chunk, one chunk behind the state
@@ -671,7 +701,7 @@ scan_kernel(const unsigned char *__restrict__ ws,
             for (int kc = 0; kc < KC; ++kc)
                 if (32 * kc <= 16 * a + 15) OD = mma_f16_k32(op.pf[kc], bD[kc], OD);
             O = bG * O + bI * OD;
-            const int t0 = c * C, L = min(C, sp.len - t0);
+            const int t0 = (cb + c) * C, L = min(C, sp.len - t0);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int r = 16 * a + 4 * lg + rr;
@@ -742,18 +772,29 @@ scan_kernel(const unsigned char *__restrict__ ws,
     __builtin_assume(w < NWV);
     f32x4 S[2];
     const size_t sbase = static_cast<size_t>(chain) * D * D;
-    if (s0 != nullptr) {  // one branch, so that all loads are in flight together
+    if (sin != nullptr) {  // one branch, so that all loads are in flight together
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr)
-                S[i][rr] = s0[sbase + static_cast<size_t>(32 * w + 16 * i + 4 * lg + rr) * D + col];
+                S[i][rr] = sin[sbase + static_cast<size_t>(32 * w + 16 * i + 4 * lg + rr) * D + col];
     } else {
         S[0] = S[1] = zero4();
     }
     float sig, isg;
     float nu;  // bound on the 2-norm of every column of the tile at the start of the chunk
-    {
+    // a later segment continues the chain with the bound and the scale it had: the same
+    // operands, bit for bit, as one pass over all chunks (nucarry: [chain][tile] {nu, sig})
+    float *nuc = nucarry != nullptr ? nucarry + 2 * (static_cast<size_t>(chain) * NI + jt) : nullptr;
+    if (cb > 0) {
+        nu = nuc[0];
+        sig = nuc[1];
+        isg = 1.f / sig;  // exact: a power of two
+        S[0] *= sig;
+        S[1] *= sig;
+        s_isg[0][lane] = isg;
+        lds_barrier();  // the output wavefronts' first barrier (the other branch's exchange)
+    } else {
         float q = 0.f;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -880,56 +921,97 @@ scan_kernel(const unsigned char *__restrict__ ws,
         for (int s = 0; s < DEPTH; ++s)
             if (c0 + s < nchunks) step(ring[s], c0 + s);
     }
-    if (sT) {
+    if (carry) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr)
-                sT[sbase + static_cast<size_t>(32 * w + 16 * i + 4 * lg + rr) * D + col] = isg * S[i][rr];
+                carry[sbase + static_cast<size_t>(32 * w + 16 * i + 4 * lg + rr) * D + col] = isg * S[i][rr];
+    }
+    if (nuc != nullptr && w == 0 && lane == 0) {
+        nuc[0] = nu;
+        nuc[1] = sig;
     }
 }
 
-// Records per chain (dense) or per head (packed sequences), and in all.
+// Record slots per unit: per chain (dense) or per head (packed sequences); units.
 template <int C> int split_nrec(const PrefillArgs &a) {
     return a.cu == nullptr ? (a.T + C - 1) / C : a.T / C + a.B;
 }
-template <int C> size_t split_records(const PrefillArgs &a) {
-    return static_cast<size_t>(split_nrec<C>(a)) * a.Hv * (a.cu == nullptr ? a.B : 1);
+inline size_t split_units(const PrefillArgs &a) {
+    return static_cast<size_t>(a.cu == nullptr ? a.B * a.Hv : a.Hv);
+}
+// The records the default workspace holds at most (2 GiB, or GDN_SPLIT_RECORD_BYTES when the
+// environment sets it, e.g. to test several segments on short inputs); longer sequences run
+// in segments.
+inline size_t split_record_bytes() {
+    const char *e = getenv("GDN_SPLIT_RECORD_BYTES");
+    const long long v = e != nullptr ? atoll(e) : 0;
+    return v > 0 ? static_cast<size_t>(v) : size_t(2) << 30;
 }
 
-template <int D, int C> size_t split_ws_bytes(const PrefillArgs &a) {
-    const size_t nrec = split_records<C>(a), chains = static_cast<size_t>(a.B) * a.Hv;
-    // operand records | per-chain scan progress (256 B each)
-    return nrec * SplitCfg<D, C>::REC +
-           chains * kProgStride * sizeof(unsigned long long);
+// Workspace: records of L slot positions of every unit | per-chain scan progress (256 B each)
+// | the state carried between segments (fp32, one per chain) | the scan's bound and scale
+// carried with it (two floats per chain and 16-column tile, padded to 256 B).
+template <int D, int C> size_t split_carry_scales_bytes(const PrefillArgs &a) {
+    const size_t n = static_cast<size_t>(a.B) * a.Hv * (D / 16) * 2 * sizeof(float);
+    return (n + 255) / 256 * 256;
+}
+template <int D, int C> size_t split_fixed_bytes(const PrefillArgs &a) {
+    const size_t chains = static_cast<size_t>(a.B) * a.Hv;
+    return chains * kProgStride * sizeof(unsigned long long) + chains * D * D * sizeof(float) +
+           split_carry_scales_bytes<D, C>(a);
+}
+template <int D, int C> size_t split_ws_bytes(const PrefillArgs &a, bool smallest) {
+    const size_t slot_row = split_units(a) * SplitCfg<D, C>::REC;
+    const size_t nrec = static_cast<size_t>(split_nrec<C>(a));
+    const size_t L = smallest ? 1 : std::min(nrec, std::max<size_t>(1, split_record_bytes() / slot_row));
+    return L * slot_row + split_fixed_bytes<D, C>(a);
 }
 
 template <int D, int C, typename TO> hipError_t launch_split_typed(const PrefillArgs &a) {
     using SC = ScanCfg<D, C>;
+    using F = SplitCfg<D, C>;
     const int nrec = split_nrec<C>(a);
-    const size_t recs = split_records<C>(a), chains = static_cast<size_t>(a.B) * a.Hv;
+    const size_t units = split_units(a), chains = static_cast<size_t>(a.B) * a.Hv;
+    // slot positions per segment: as many as the workspace holds (at least one, checked by
+    // the caller)
+    const size_t fixed = split_fixed_bytes<D, C>(a), slot_row = units * F::REC;
+    if (a.ws_bytes < fixed + slot_row) return hipErrorInvalidValue;
+    const int L = static_cast<int>(std::min<size_t>(nrec, (a.ws_bytes - fixed) / slot_row));
+    const int nseg = (nrec + L - 1) / L;
     unsigned char *ws = static_cast<unsigned char *>(a.ws);
-    unsigned long long *prog = reinterpret_cast<unsigned long long *>(ws + recs * SplitCfg<D, C>::REC);
+    unsigned long long *prog = reinterpret_cast<unsigned long long *>(ws + static_cast<size_t>(L) * slot_row);
+    float *carry_ws = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(prog) +
+                                                chains * kProgStride * sizeof(unsigned long long));
+    float *nucarry = nseg > 1 ? carry_ws + chains * D * D : nullptr;
+    // the state between segments: the final-state buffer if there is one, else the workspace's
+    float *carry = a.sT != nullptr ? a.sT : (nseg > 1 ? carry_ws : nullptr);
     // prefetch workgroups only where the scan leaves compute units idle (one workgroup of
     // either kind fills a compute unit's registers)
     const size_t nscan = chains * (D / 16);
     const size_t npf = chains * (D / 16 + SC::NPF) <= 256 ? chains * SC::NPF : 0;
     const size_t per_xcd = (chains + 7) / 8;  // chains whose records share one XCD's L2
     const int pfd = static_cast<int>(std::max<size_t>(
-        2, std::min<size_t>(SC::kMaxPfd, SC::kPrefetchBytesPerXcd / (per_xcd * SplitCfg<D, C>::REC))));
+        2, std::min<size_t>(SC::kMaxPfd, SC::kPrefetchBytesPerXcd / (per_xcd * F::REC))));
     auto prep = (a.flags & GDN_QK_L2NORM) ? prep_kernel<D, C, true> : prep_kernel<D, C, false>;
-    hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(recs)), dim3(64), 0, a.stream,
-                       static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
-                       static_cast<const bf16_t *>(a.v), static_cast<const bf16_t *>(a.beta),
-                       static_cast<const bf16_t *>(a.g), ws, npf ? prog : nullptr, a.cu,
-                       a.B, a.T, a.Hk, a.Hv, nrec, a.flags);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_kernel<D, C, TO>), dim3(static_cast<unsigned>(nscan + npf)),
-                       dim3(64 * (SC::NWV + SC::NWO)), 0, a.stream, ws, a.s0, a.sT,
-                       static_cast<TO *>(a.o), a.cu, a.T, a.Hv, nrec, a.scale,
-                       npf ? prog : nullptr, static_cast<int>(nscan), pfd);
-    return hipGetLastError();
+    for (int sg = 0; sg < nseg; ++sg) {
+        const int lo = sg * L, nslot = std::min(L, nrec - lo);
+        hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(units * nslot)), dim3(64), 0, a.stream,
+                           static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
+                           static_cast<const bf16_t *>(a.v), static_cast<const bf16_t *>(a.beta),
+                           static_cast<const bf16_t *>(a.g), ws, npf ? prog : nullptr, a.cu,
+                           a.B, a.T, a.Hk, a.Hv, lo, L, a.flags);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((scan_kernel<D, C, TO>), dim3(static_cast<unsigned>(nscan + npf)),
+                           dim3(64 * (SC::NWV + SC::NWO)), 0, a.stream, ws, a.s0, carry,
+                           nucarry, static_cast<TO *>(a.o), a.cu, a.T, a.Hv, lo, L, a.scale,
+                           npf ? prog : nullptr, static_cast<int>(nscan), pfd);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int D, int C> hipError_t launch_split_out(const PrefillArgs &a) {
@@ -944,11 +1026,12 @@ bool chunk_split_supports(const PrefillArgs &a) {
            (a.chunk == 32 || a.chunk == 64);
 }
 
-size_t chunk_split_workspace(const PrefillArgs &a) {
+size_t chunk_split_workspace(const PrefillArgs &a, bool smallest) {
     if (!chunk_split_supports(a)) return 0;
     if (a.dk == 128)
-        return a.chunk == 64 ? split_ws_bytes<128, 64>(a) : split_ws_bytes<128, 32>(a);
-    return a.chunk == 64 ? split_ws_bytes<64, 64>(a) : split_ws_bytes<64, 32>(a);
+        return a.chunk == 64 ? split_ws_bytes<128, 64>(a, smallest)
+                             : split_ws_bytes<128, 32>(a, smallest);
+    return a.chunk == 64 ? split_ws_bytes<64, 64>(a, smallest) : split_ws_bytes<64, 32>(a, smallest);
 }
 
 hipError_t launch_chunk_split(const PrefillArgs &a) {

@@ -105,15 +105,17 @@ static gdn_status_t check_prefill(const gdn::PrefillArgs &a) {
     return GDN_OK;
 }
 
-// Workspace bytes the plan `var` needs for a validated prefill with tokens.
-static size_t plan_workspace(const gdn::PrefillArgs &a, Variant var) {
-    return var == Variant::Split   ? gdn::chunk_split_workspace(a)
+// Workspace bytes the plan `var` needs for a validated prefill with tokens: the size the
+// workspace-size queries return, or (least) the smallest it runs with.
+static size_t plan_workspace(const gdn::PrefillArgs &a, Variant var, bool least = false) {
+    return var == Variant::Split   ? gdn::chunk_split_workspace(a, least)
            : var == Variant::Fused ? gdn::chunk_mfma_workspace(a)
                                    : 0;
 }
 
-// The whole prefill: validation, the T = 0 case, workspace check and dispatch.
-static gdn_status_t run_prefill(gdn::PrefillArgs &a) {
+// The whole prefill: validation, the T = 0 case, workspace check and dispatch.  least: the
+// workspace only has to hold the plan's smallest size (the allocation-free entry point).
+static gdn_status_t run_prefill(gdn::PrefillArgs &a, bool least = false) {
     gdn_status_t st = check_prefill(a);
     if (st != GDN_OK) return st;
     if (a.B == 0) return GDN_OK;
@@ -124,7 +126,7 @@ static gdn_status_t run_prefill(gdn::PrefillArgs &a) {
                                                                               : GDN_ERR_HIP;
     }
     const Variant var = choose_variant(a);
-    const size_t need = plan_workspace(a, var);
+    const size_t need = plan_workspace(a, var, least);
     if (need > 0 && (a.ws == nullptr || a.ws_bytes < need)) return GDN_ERR_INVALID_ARG;
     if (need > 0 && !aligned(a.ws, 256)) return GDN_ERR_INVALID_ARG;
     hipError_t e = var == Variant::Split   ? gdn::launch_chunk_split(a)
@@ -261,7 +263,8 @@ gdn_status_t gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v, 
     const gdn_status_t st = check_prefill(a);
     if (st != GDN_OK) return st;
     if (a.B > 0 && a.T > 0) {
-        const size_t need = plan_workspace(a, choose_variant(a));
+        // the split plan runs in segments of as many chunks as the scratch holds
+        const size_t need = plan_workspace(a, choose_variant(a), true);
         if (need > GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_SCRATCH_TOO_SMALL;
         if (need > 0) {
             // whatever a kernel must find zeroed it clears itself (the split plan's prep kernel
@@ -270,7 +273,7 @@ gdn_status_t gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v, 
             a.ws_bytes = GDN_NOALLOC_SCRATCH_BYTES;
         }
     }
-    return run_prefill(a);
+    return run_prefill(a, true);
 }
 
 size_t gdn_chunk_fwd_varlen_workspace_size(int num_seqs, int T, int Hk, int Hv, int dk, int dv,

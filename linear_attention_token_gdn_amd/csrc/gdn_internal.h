@@ -86,9 +86,13 @@ size_t chunk_mfma_workspace(const PrefillArgs &a);
 hipError_t launch_chunk_mfma(const PrefillArgs &a);
 
 // Two-kernel chunk-parallel form (a fully parallel prep kernel and a per-chain scan kernel
-// through a workspace) for shapes with fewer chains than compute units.
+// through a workspace) for shapes with fewer chains than compute units.  The workspace holds
+// the records of a segment of chunks; longer sequences run segment after segment, as many
+// chunks at a time as a.ws_bytes holds.  chunk_split_workspace: the size that keeps the
+// records to at most 2 GiB (smallest = false), or the least the plan runs with (one chunk
+// per segment).
 bool chunk_split_supports(const PrefillArgs &a);
-size_t chunk_split_workspace(const PrefillArgs &a);
+size_t chunk_split_workspace(const PrefillArgs &a, bool smallest = false);
 hipError_t launch_chunk_split(const PrefillArgs &a);
 
 // One streaming pass over the decode state.

@@ -131,15 +131,14 @@ def test_noalloc_validation(lib, kw, status):
     assert prefill_noalloc(**kw) == status
 
 
-def test_noalloc_rejects_workspace_beyond_its_scratch(lib):
-    """The split plan's workspace grows with the chunk count: T = 4096 with 16 heads (72 MiB)
-    fits the 80 MiB scratch, twice that does not -- rejected on the host, nothing launched."""
-    need = gdn.gdn_chunk_fwd_workspace_size(1, 8192, 16, 16, 128, 128, 64, gdn.GDN_BF16)
-    assert need > gdn.GDN_NOALLOC_SCRATCH_BYTES
-    assert gdn.gdn_chunk_fwd_workspace_size(1, 4096, 16, 16, 128, 128, 64,
-                                            gdn.GDN_BF16) <= gdn.GDN_NOALLOC_SCRATCH_BYTES
-    assert prefill_noalloc(T=8192, Hk=16, Hv=16, dk=128, dv=128, chunk=64,
-                           initial_state=None, final_state=None) == gdn.GDN_ERR_SCRATCH_TOO_SMALL
+def test_noalloc_scratch_holds_the_smallest_split_workspace(lib, monkeypatch):
+    """The split plan runs in segments of as many chunks as the scratch holds: its smallest
+    workspace (one chunk per segment) fits 80 MiB even at the largest chain count the plan
+    takes (127 chains at d = 128), so no size the plans run is refused for its length."""
+    monkeypatch.setenv("GDN_SPLIT_RECORD_BYTES", "1")
+    least = gdn.gdn_chunk_fwd_workspace_size(1, 1 << 20, 1, 127, 128, 128, 64, gdn.GDN_BF16)
+    assert gdn.gdn_chunk_fwd_plan(1, 1 << 20, 1, 127, 128, 128, 64, gdn.GDN_BF16) == "split"
+    assert 0 < least <= gdn.GDN_NOALLOC_SCRATCH_BYTES // 4
     assert prefill_noalloc(B=0, q=None, k=None, v=None, beta=None, g=None, o=None) == gdn.GDN_OK
 
 
@@ -238,6 +237,31 @@ def test_prefill_varlen_validation(lib, kw, status):
     assert prefill_varlen(**kw) == status
 
 
+def split_fixed(chains, d):
+    """The split plan's workspace beside its records: progress words, carried states and the
+    carried bound and scale of every 16-column tile."""
+    scales = chains * (d // 16) * 2 * 4
+    return chains * 256 + chains * d * d * 4 + (scales + 255) // 256 * 256
+
+
+def test_split_workspace_is_bounded(lib, monkeypatch):
+    """The split plan keeps at most 2 GiB of records (segments of chunks): the workspace of a
+    sequence of a million tokens is that of about 1,800 chunks, not of 16,384; the environment
+    cap lowers it, down to one chunk per segment."""
+    rec = 73728 + 128
+    big = gdn.gdn_chunk_fwd_workspace_size(1, 1 << 20, 16, 16, 128, 128, 64, gdn.GDN_BF16)
+    L = (2 << 30) // (16 * rec)
+    assert big == L * 16 * rec + split_fixed(16, 128)
+    short = gdn.gdn_chunk_fwd_workspace_size(1, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16)
+    assert short == 64 * 16 * rec + split_fixed(16, 128)  # all 64 chunks fit: one segment
+    monkeypatch.setenv("GDN_SPLIT_RECORD_BYTES", str(20 * 16 * rec))
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16) == (
+        20 * 16 * rec + split_fixed(16, 128))
+    monkeypatch.setenv("GDN_SPLIT_RECORD_BYTES", "1")
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16) == (
+        16 * rec + split_fixed(16, 128))
+
+
 def test_varlen_workspace(lib):
     ws = gdn.gdn_chunk_fwd_varlen_workspace_size
     # dense = gdn_chunk_fwd's
@@ -248,16 +272,17 @@ def test_varlen_workspace(lib):
     assert ws(16, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1) == 0
     # few chains: the split plan; packed sequences take one record slot per sequence and head
     # beyond the chunks of the total length (records of 72 KiB + one 128-byte line of scalars
-    # at d = 128, C = 64; a 256-byte progress word per chain)
+    # at d = 128, C = 64), plus per chain a 256-byte progress word, the fp32 state carried
+    # between segments and two floats per 16-column tile (padded to 256 B)
     assert gdn.gdn_chunk_fwd_plan(4, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16) == "split"
     slots = 16 * (4096 // 64 + 4)
     assert ws(4, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1) == (
-        slots * (73728 + 128) + 4 * 16 * 256)
+        slots * (73728 + 128) + split_fixed(4 * 16, 128))
     assert ws(0, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1) == 0
     # the plan hint: split for many chains too, with the same slot layout
     slots = 16 * (4096 // 64 + 16)
     assert ws(16, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1, gdn.GDN_PREFER_SPLIT) == (
-        slots * (73728 + 128) + 16 * 16 * 256)
+        slots * (73728 + 128) + split_fixed(16 * 16, 128))
     assert ws(2, 4096, 16, 16, 128, 128, 64, gdn.GDN_F32, 1, gdn.GDN_PREFER_SPLIT) == 0
     assert ws(2, 4096, 16, 16, 128, 128, 64, gdn.GDN_F32, 1) == 0  # fp32: recurrent
 

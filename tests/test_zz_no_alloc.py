@@ -2,8 +2,9 @@
 workspace is the library's static scratch) against gdn_chunk_fwd with a caller workspace, both
 through the C ABI on the same inputs: bit-identical outputs and final states, two calls in a
 row (the second smaller, so the scratch still holds the first call's records), a plan without a
-workspace, and a size beyond the scratch rejected without touching the outputs.  The outputs
-are also held to the oracle's bar (bf16 inputs: eps <= 2e-3 M).
+workspace, and an input whose records exceed the scratch, which runs in two segments there and
+in one with the caller's workspace.  The outputs are also held to the oracle's bar (bf16
+inputs: eps <= 2e-3 M).
 """
 import numpy as np
 import pytest
@@ -80,8 +81,13 @@ def test_noalloc_equals_the_workspace_entry_point():
     # 3: a plan without a workspace (many chains: the single-pass kernel)
     many = make_inputs(1, 200, 64, 128, 64, 64, dtype="bf16", s0_std=0.02, seed=992)
     _same(many, "fused")
-    # 4: beyond the scratch: rejected, outputs untouched
-    huge = make_inputs(1, 8192, 16, 16, 128, 128, dtype="bf16", seed=993)
-    st, o, s = _call(huge, noalloc=True)
-    assert st == gdn.GDN_ERR_SCRATCH_TOO_SMALL
-    assert np.isnan(o).all() and np.isnan(s).all()
+    # 4: records beyond the scratch (8192 tokens, 16 heads: 144 MiB in one pass): two
+    #    segments of chunks in the scratch, bit for bit the one-pass result
+    assert (gdn.gdn_chunk_fwd_workspace_size(1, 8192, 16, 16, 128, 128, 64, gdn.GDN_BF16)
+            > gdn.GDN_NOALLOC_SCRATCH_BYTES)
+    huge = make_inputs(1, 8192, 16, 16, 128, 128, dtype="bf16", s0_std=0.02, seed=993)
+    o, s = _same(huge, "split")
+    chains = np.array([3, 12])
+    ro, rS = oracle.run(huge.q, huge.k, huge.v, huge.beta, huge.g, s0=huge.s0, chains=chains)
+    check(o[0][:, chains].transpose(1, 0, 2), ro, "bf16", "noalloc o (T=8192)")
+    check(s[0][chains], rS, "bf16", "noalloc state (T=8192)")

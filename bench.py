@@ -90,8 +90,9 @@ def source_hash(paths):
 
 
 def measured_traffic(kernel, workload):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None when absent,
-    taken on another workload or on a different version of the kernel source."""
+    """HBM bytes per call (the prefill's launches together; one launch for the decode) from the
+    committed rocprofv3 --pmc summary, or None when absent, taken on another workload or on a
+    different version of the kernel source."""
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh).get(kernel)
@@ -101,7 +102,7 @@ def measured_traffic(kernel, workload):
         return None
     if rec.get("workload") != workload:
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("bytes_per_call", rec.get("bytes_per_launch"))
 
 
 def measured_mfma(label, sources):

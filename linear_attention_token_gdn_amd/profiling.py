@@ -2,9 +2,9 @@
 
     python -m linear_attention_token_gdn_amd.profiling trace  <kernel_trace.csv> "<command>"
     python -m linear_attention_token_gdn_amd.profiling traffic <fetch_dir> <write_dir> \
-           <copy_fetch_dir> <copy_write_dir> "<command>" <prefill_workload_label>
+           <copy_fetch_dir> <copy_write_dir> "<command>" <prefill_workload_label> [segments]
     python -m linear_attention_token_gdn_amd.profiling mfma <label> <mfma_dir> <lds_dir> \
-           <algorithmic_flops_per_call> "<command>"
+           <algorithmic_flops_per_call> "<command>" [segments]
 
 `trace` prints a markdown table of per-kernel launch counts and durations (from a
 `rocprofv3 --kernel-trace` CSV).  `traffic` turns two counter passes over the benchmark
@@ -12,7 +12,9 @@
 into HBM bytes per launch: each counter is scaled by (known copy bytes / what the counter read
 for the copy).  It prints markdown and writes profiles/traffic.json (the prefill kernels'
 record labelled with the prefill workload, e.g. workload3; the decode kernel's with
-workload4), which bench.py reports while the kernel sources and the workload are unchanged.  `mfma` reads one counter pass with
+workload4), which bench.py reports while the kernel sources and the workload are unchanged.
+A split-plan prefill that runs in `segments` segments launches prep and scan that many times
+per call; its record holds bytes per call (all their launches over the number of calls).  `mfma` reads one counter pass with
 `--pmc MfmaUtil MfmaFlopsF16 MfmaFlopsBF16 SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE` and one with
 `--pmc LdsBankConflict SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE` over a run of one prefill
 workload, prints per-kernel matrix-core busy time, matrix-core flops as issued (which include
@@ -148,7 +150,8 @@ def read_counter(dirpath, counter):
     return by_kernel
 
 
-def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, command, workload):
+def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, command, workload, segments="1"):
+    segments = int(segments)
     fetch, write = read_counter(fetch_dir, "FETCH_SIZE"), read_counter(write_dir, "WRITE_SIZE")
     cf, cw = read_counter(cfetch_dir, "FETCH_SIZE"), read_counter(cwrite_dir, "WRITE_SIZE")
     copy_f = max(statistics.median(v) for v in cf.values())
@@ -171,13 +174,21 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, command, workload):
         out.append("| `%s` | %d | %.0f | %.0f | %.1f | %.1f |" % (
             _label(name), len(fetch.get(name, [])), f, w, rd / 1e6, wr / 1e6))
     rec = {"copy_scale_fetch": sf, "copy_scale_write": sw, "command": command}
-    for key, names in (("prefill", ("prep_kernel", "scan_kernel")), ("fused", ("chunk_kernel",))):
+    for key, names, seg in (("prefill", ("prep_kernel", "scan_kernel"), segments),
+                            ("fused", ("chunk_kernel",), 1)):
         pre = [n for n in res if n.startswith(names)]
         if pre:
-            rec[key] = {"kernels": pre, "bytes_per_launch": sum(sum(res[n]) for n in pre),
-                        "read_bytes_per_launch": sum(res[n][0] for n in pre),
-                        "write_bytes_per_launch": sum(res[n][1] for n in pre),
+            # per call: every launch of these kernels over the number of calls (the launches of
+            # the last kernel of the call over the launches it makes per call)
+            calls = len(fetch.get(pre[-1], [])) / seg
+            rd = sum(sum(fetch.get(n, [])) for n in pre) * 1024 * sf / calls
+            wr = sum(sum(write.get(n, [])) for n in pre) * 1024 * sw / calls
+            rec[key] = {"kernels": pre, "bytes_per_call": rd + wr,
+                        "read_bytes_per_call": rd, "write_bytes_per_call": wr,
+                        "launches_per_call": {n: seg for n in pre},
                         "workload": workload, "source_sha256_16": source_hash(SOURCES[key])}
+            out += ["", "%s per call (%d launch(es) of each kernel per call): %.1f MB read, "
+                    "%.1f MB written" % (key, seg, rd / 1e6, wr / 1e6)]
     # the single-token decode kernel (MULTI = false) of the benchmark step
     dec = [n for n in res if n.startswith("decode_kernel") and n.endswith("false>")]
     if dec:
@@ -192,9 +203,12 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, command, workload):
 PREFILL_KERNELS = ("prep_kernel", "scan_kernel", "chunk_kernel")
 
 
-def mfma(label, mfma_dir, lds_dir, algo_flops, command):
-    """Matrix-core and LDS counters per kernel (medians over its launches)."""
+def mfma(label, mfma_dir, lds_dir, algo_flops, command, segments="1"):
+    """Matrix-core and LDS counters per kernel (medians over its launches); the prefill call's
+    totals sum every launch of its kernels over the number of calls (`segments` launches of
+    each kernel per call for a split-plan prefill in segments)."""
     algo_flops = float(algo_flops)
+    segments = int(segments)
     med = lambda d, n: statistics.median(d[n]) if n in d else 0.0
     util = read_counter(mfma_dir, "MfmaUtil")
     f16, bf16 = read_counter(mfma_dir, "MfmaFlopsF16"), read_counter(mfma_dir, "MfmaFlopsBF16")
@@ -227,10 +241,12 @@ def mfma(label, mfma_dir, lds_dir, algo_flops, command):
         if name.startswith(PREFILL_KERNELS):
             pre.append(name)
     if pre:
-        issued = sum(rec["kernels"][n]["mfma_flops_issued"] for n in pre)
-        w = sum(rec["kernels"][n]["gui_active"] for n in pre)
-        busy = sum(rec["kernels"][n]["mfma_busy_pct"] * rec["kernels"][n]["gui_active"]
-                   for n in pre) / w if w > 0 else 0.0
+        calls = len(util[pre[-1]]) / (segments if not pre[-1].startswith("chunk_kernel") else 1)
+        issued = sum(sum(f16.get(n, [])) + sum(bf16.get(n, [])) + 512.0 * sum(f32.get(n, []))
+                     for n in pre) / calls
+        w = sum(sum(gui.get(n, [])) for n in pre)
+        busy = sum(u * g for n in pre for u, g in zip(util.get(n, []), gui.get(n, []))) / w \
+            if w > 0 else 0.0
         rec["prefill"] = {"kernels": pre, "mfma_flops_issued_per_call": issued,
                           "algorithmic_flops_per_call": algo_flops,
                           "issued_over_algorithmic": issued / algo_flops,
@@ -258,9 +274,9 @@ def main(argv):
     if argv and argv[0] == "trace":
         print(trace_table(argv[1], argv[2]))
     elif argv and argv[0] == "traffic":
-        print(traffic(*argv[1:7]))
+        print(traffic(*argv[1:8]))
     elif argv and argv[0] == "mfma":
-        print(mfma(*argv[1:7]))
+        print(mfma(*argv[1:8]))
     else:
         print(__doc__)
         return 2

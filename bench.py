@@ -19,7 +19,10 @@ verifier keeping the old state would call it); "prologue_and_packed" reports the
 the fused input prologue and a packed batch of 32 variable-length sequences, and the backward,
 all on the 4096-token workload; "qsa_indexer" reports the QSA compressed indexer
 (gdn_qsa_index) on a 65536-token sequence; "prefill_other_workloads" times the other prefill
-workloads (B=1 T=4096 H=16; B=8 T=8192 with grouped heads); "decode_cycled_states" times the
+workloads (B=1 T=4096 H=16; B=8 T=8192 with grouped heads); "prefill_plans_compared" times
+the step's prefill workload under each chunk-parallel plan that takes it (split: per-chunk
+records through a workspace; segmented: segments of each chain in parallel, chained through
+their affine state maps); "decode_cycled_states" times the
 decode step over four separate state buffers in turn, so that no state is still in the
 last-level cache when it is read again; "measured_peaks" reports what a plain device copy and a
 dense bf16 matrix product reach in the same run.
@@ -46,6 +49,8 @@ KERNEL_SOURCES = {
                 for n in ("chunk_split.hip", "gdn_internal.h")],
     "fused": [os.path.join(ROOT, "linear_attention_token_gdn_amd", "csrc", n)
               for n in ("chunk_mfma.hip", "gdn_internal.h")],
+    "segmented": [os.path.join(ROOT, "linear_attention_token_gdn_amd", "csrc", n)
+                  for n in ("chunk_mfma.hip", "gdn_internal.h")],
     "decode": [os.path.join(ROOT, "linear_attention_token_gdn_amd", "csrc", n)
                for n in ("decode.hip", "gdn_internal.h")],
 }
@@ -270,11 +275,59 @@ def prefill_configs(gdn, torch, dev, stream, names=(1, 2)):
                                                fl / (MFMA_BF16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3), 4),
             "algorithmic_flops": fl, "algorithmic_bytes": by,
             "mfma_counters": measured_mfma("workload%d_%s" % (idx, plan),
-                                           "prefill" if plan == "split" else "fused")}
+                                           {"split": "prefill"}.get(plan, plan))}
         del q, k, v, beta, gg, s0, o, fs, x
         torch.cuda.synchronize()
     del flush
     return out
+
+
+def prefill_plans(gdn, torch, dev, stream, idx, plans=("split", "segmented")):
+    """One prefill workload under each chunk-parallel plan that takes it (GDN_FORCE_VARIANT),
+    one call each, median of 3, 1 GiB written between calls; inputs as gpu_inputs."""
+    from gdn_inputs import CONFIGS
+    c = CONFIGS[idx]
+    B, T, Hk, Hv, dk, dv, C = (c[k_] for k_ in ("B", "T", "Hk", "Hv", "dk", "dv", "chunk"))
+    x = gpu_inputs(torch, dev, idx)
+    o = torch.empty(B, T, Hv, dv, dtype=torch.float32, device=dev)
+    fs = torch.empty(B, Hv, dk, dv, dtype=torch.float32, device=dev)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    out = {}
+    old = os.environ.get("GDN_FORCE_VARIANT")
+    try:
+        for plan in plans:
+            os.environ["GDN_FORCE_VARIANT"] = plan
+            if gdn.gdn_chunk_fwd_plan(B, T, Hk, Hv, dk, dv, C, gdn.GDN_BF16) != plan:
+                continue
+            need = gdn.gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, C, gdn.GDN_BF16)
+            ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            call = lambda: gdn.chunk_fwd(x["q"], x["k"], x["v"], x["beta"], x["g"],
+                                         initial_state=x["s0"], chunk=C, o=o, final_state=fs,
+                                         workspace=ws)
+            call()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(3):
+                flush.fill_(1.0)
+                e0, e1 = HipEvent(), HipEvent()
+                e0.record(stream)
+                call()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            ms = sorted(ts)[1]
+            out[plan] = {"ms": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+                         "workspace_bytes": need}
+            del ws
+    finally:
+        if old is None:
+            os.environ.pop("GDN_FORCE_VARIANT", None)
+        else:
+            os.environ["GDN_FORCE_VARIANT"] = old
+    del x, o, fs, flush
+    torch.cuda.synchronize()
+    return {"workload": c["name"], "plans": out,
+            "default_plan": gdn.gdn_chunk_fwd_plan(B, T, Hk, Hv, dk, dv, C, gdn.GDN_BF16)}
 
 
 # ------------------------------------------------------------------ peaks measured in the same run
@@ -626,20 +679,22 @@ def main():
     pre_gbs = pbytes / (pre_mean * 1e-3) / 1e9
     plan = gdn.gdn_chunk_fwd_plan(B, T, Hk, Hv, dk, dv, C, gdn.GDN_BF16)
     pre_kernels = {"split": "prep_kernel<%d,%d,false> + scan_kernel<%d,%d,float>" % (dk, C, dk, C),
-                   "fused": "chunk_kernel<%d,%d,float>" % (dk, C)}.get(plan, plan)
+                   "fused": "chunk_kernel<%d,%d,float,0>" % (dk, C),
+                   "segmented": "chunk_kernel<%d,%d,float,1> + seg_combine_kernel<%d> + "
+                                "chunk_kernel<%d,%d,float,0>" % (dk, C, dk, dk, C)}.get(plan, plan)
+    src_key = {"split": "prefill"}.get(plan, plan)
     rooflines = {
         "prefill": {
             "kernel": pre_kernels, "plan": plan, "bound": "hbm",
             "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(pre_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic("prefill" if plan == "split" else "fused",
-                                        "workload%d" % args.prefill_config),
+            "traffic": measured_traffic(src_key, "workload%d" % args.prefill_config),
             "algorithmic_bytes": pbytes, "algorithmic_flops": flops,
             "mean_launch_ms": round(pre_mean, 4),
             "mfma_TFLOPs": round(pre_tflops, 2),
             "frac_bf16_mfma_peak": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
             "mfma_counters": measured_mfma("workload%d_%s" % (args.prefill_config, plan),
-                                           "prefill" if plan == "split" else "fused"),
+                                           src_key),
         }
     }
     dom = "prefill"
@@ -736,6 +791,7 @@ def main():
                                                    with_cpu=not args.no_cpu_baseline)
     others = None if args.no_extras else prefill_configs(
         gdn, torch, dev, stream, names=[i for i in (1, 2, 3) if i != args.prefill_config])
+    plans = None if args.no_extras else prefill_plans(gdn, torch, dev, stream, args.prefill_config)
     peaks = None if args.no_extras else measured_peaks(torch, dev, stream)
     if result_decode is not None and peaks is not None:
         result_decode["frac_measured_copy"] = round(result_decode["total_GBps"] / peaks["copy_GBps"], 4)
@@ -779,6 +835,7 @@ def main():
         "prologue_and_packed": extras,
         "qsa_indexer": qsa,
         "prefill_other_workloads": others,
+        "prefill_plans_compared": plans,
         "measured_peaks": peaks,
         "roofline": dict(rooflines[dom], kernel_role=dom),
         "rooflines": rooflines,

@@ -38,6 +38,9 @@
 //     the state and the solve panels never leave registers.
 //   * O is staged in LDS and written with coalesced 16-byte stores at the top of the next
 //     chunk, before the next prefetch is issued (the vector-memory counter is in-order).
+#include <algorithm>
+#include <stdlib.h>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -63,6 +66,11 @@ __device__ __forceinline__ f16x4 to_f16x4(f32x4 x) {
     return f16x4{f16(x[0]), f16(x[1]), f16(x[2]), f16(x[3])};
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+// x, as a value the compiler cannot see through (nothing derived from it moves above this)
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
 
 // Workgroup barrier that waits only for this wave's LDS traffic.  __syncthreads() also waits
 // for every outstanding global load and store, which would stall each chunk on the prefetch of
@@ -142,15 +150,28 @@ template <> __device__ __forceinline__ void store4<bf16_t>(bf16_t *p, f32x4 x) {
         u16x4{f32_to_bf16(x[0]), f32_to_bf16(x[1]), f32_to_bf16(x[2]), f32_to_bf16(x[3])};
 }
 
-template <int D, int C, typename TO>
+// MODE kOut: the prefill itself -- outputs o, and the final state.  MODE kTrans: the segment
+// transition of the segmented plan -- no outputs; besides the state N (from zero, or from s0
+// on segment 0) it carries M, started at the identity and advanced by the same chunk maps
+// without their value part:  M <- e^gamma_last M - K^T dec W M.  After the segment,
+// S_out = M S_in + N for any state S_in entering it (Eq. (1) is affine in the state).
+enum { kOut = 0, kTrans = 1 };
+
+// Units: blocks [p nchains, (p + 1) nchains) run segment p (chunks p seg_chunks .. of every
+// chain; one segment with seg_chunks >= the chunk count is the whole sequence).  kOut reads
+// its initial state at s0 + p s0_seg_stride + chain D^2 and writes the final state on the last
+// segment only; kTrans writes M, N of (segment p, chain) to mn + (p nchains + chain) 2 D^2.
+template <int D, int C, typename TO, int MODE>
 __global__ void __launch_bounds__((Cfg<D, C>::NT))
 chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
              const bf16_t *__restrict__ v, const bf16_t *__restrict__ beta,
              const bf16_t *__restrict__ g, const float *__restrict__ s0, TO *__restrict__ o,
              float *__restrict__ sT, int T, const int32_t *__restrict__ cu, unsigned flags,
-             int Hk, int Hv, float scale) {
+             int Hk, int Hv, float scale, int nchains, int seg_chunks, int nseg,
+             size_t s0_seg_stride, float *__restrict__ mn) {
     using F = Cfg<D, C>;
     constexpr int NT = F::NT, NR = F::NR;
+    constexpr bool TRANS = MODE == kTrans;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     Smem<D, C> &sm = *reinterpret_cast<Smem<D, C> *>(smem_raw);
 
@@ -158,25 +179,44 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 15, lg = lane >> 4;
     const int G = Hv / Hk;
-    const int chain = chain_of_block(blockIdx.x, gridDim.x, G);
+    const int seg = static_cast<int>(blockIdx.x) / nchains;
+    const int chain = chain_of_block(static_cast<int>(blockIdx.x) - seg * nchains, nchains, G);
     const int b = chain / Hv, hv = chain - b * Hv, hq = hv / G;
     const int col = 16 * wave + li;  // the state column this lane holds
-    size_t base;  // this sequence's first row and length
+    size_t base;  // this segment's first row and length
     int len;
-    seq_range(cu, T, b, base, len);
+    {
+        int len0;
+        seq_range(cu, T, b, base, len0);
+        const long start = static_cast<long>(seg) * seg_chunks * C;
+        len = static_cast<int>(max(0L, min(static_cast<long>(len0) - start,
+                                           static_cast<long>(seg_chunks) * C)));
+        base += static_cast<size_t>(min(start, static_cast<long>(len0)));
+    }
 
     // ---- the state: tile it holds rows 16it + 4lg + r of column `col`
     f32x4 S[F::NI];
     const size_t sbase = static_cast<size_t>(chain) * D * D;
-    if (s0 != nullptr) {  // one branch, so that all loads are in flight together
+    const float *sin = s0 == nullptr ? nullptr
+                       : TRANS       ? (seg == 0 ? s0 + sbase : nullptr)
+                                     : s0 + seg * s0_seg_stride + sbase;
+    if (sin != nullptr) {  // one branch, so that all loads are in flight together
 #pragma unroll
         for (int it = 0; it < F::NI; ++it)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                S[it][r] = s0[sbase + static_cast<size_t>(16 * it + 4 * lg + r) * D + col];
+                S[it][r] = sin[static_cast<size_t>(16 * it + 4 * lg + r) * D + col];
     } else {
 #pragma unroll
         for (int it = 0; it < F::NI; ++it) S[it] = zero4();
+    }
+    // kTrans: the transition M, tiles as S, from the identity
+    f32x4 M[TRANS ? F::NI : 1];
+    if constexpr (TRANS) {
+#pragma unroll
+        for (int it = 0; it < F::NI; ++it)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) M[it][r] = (16 * it + 4 * lg + r == col) ? 1.f : 0.f;
     }
 
     // ---- raw inputs of the next chunk, prefetched into registers (rows past the end read as 0)
@@ -193,7 +233,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             if (r < L) {
                 const size_t row = base + tt + r;
                 const size_t oq = (row * Hk + hq) * D + cc * 8, ov = (row * Hv + hv) * D + cc * 8;
-                pq[n] = *reinterpret_cast<const u16x8 *>(q + oq);
+                if constexpr (!TRANS) pq[n] = *reinterpret_cast<const u16x8 *>(q + oq);
                 pk[n] = *reinterpret_cast<const u16x8 *>(k + oq);
                 pv[n] = *reinterpret_cast<const u16x8 *>(v + ov);
             }
@@ -242,8 +282,10 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             }
             // columns 8cc .. 8cc+7 are two runs of 4 in the permuted order
             const int c0 = kperm(cc * 8), c1 = kperm(cc * 8 + 4);
-            *reinterpret_cast<f16x4 *>(&sm.q[r][c0]) = f16x4{qh[0], qh[1], qh[2], qh[3]};
-            *reinterpret_cast<f16x4 *>(&sm.q[r][c1]) = f16x4{qh[4], qh[5], qh[6], qh[7]};
+            if constexpr (!TRANS) {
+                *reinterpret_cast<f16x4 *>(&sm.q[r][c0]) = f16x4{qh[0], qh[1], qh[2], qh[3]};
+                *reinterpret_cast<f16x4 *>(&sm.q[r][c1]) = f16x4{qh[4], qh[5], qh[6], qh[7]};
+            }
             *reinterpret_cast<f16x4 *>(&sm.k[r][c0]) = f16x4{kh[0], kh[1], kh[2], kh[3]};
             *reinterpret_cast<f16x4 *>(&sm.k[r][c1]) = f16x4{kh[4], kh[5], kh[6], kh[7]};
             *reinterpret_cast<u16x8 *>(&sm.v[r][cc * 8]) = pv[n];
@@ -264,7 +306,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                 sm.bet[lane] = lane < L ? beta_from_input(bf16_to_f32(pb), flags) : 0.f;
             }
         }
-        if (c > 0) {
+        if (!TRANS && c > 0) {
             const int tp = t0 - C;  // the previous chunk is always a full one
 #pragma unroll
             for (int n = 0; n < F::NO; ++n) {
@@ -277,9 +319,18 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         lds_barrier();
 
         // ---- stage 1: KK^T -> A, QK^T -> P (lower-triangular 16x16 tiles), and K^T
+        {
+        const int li_ = li, lg_ = lg;
+        // kTrans needs only K K^T: row tile job % NR, column tiles of parity job / NR (two
+        // wavefronts per row tile instead of one for each of K and Q)
+        // (kTrans: the lane's row and column offsets are made opaque here, so that the compiler
+        // forms this stage's LDS addresses in the loop instead of keeping them in registers
+        // across it -- the transition's second state leaves no registers for that)
+        const int li = TRANS ? opaque(li_) : li_, lg = TRANS ? opaque(lg_) : lg_;
         for (int job = wave; job < 2 * NR; job += F::NW) {
-            const bool isq = job >= NR;
-            const int rt = isq ? job - NR : job;
+            const bool isq = !TRANS && job >= NR;
+            const int rt = job >= NR ? job - NR : job;
+            const int par = job >= NR ? 1 : 0;
             const f16 *arow = isq ? &sm.q[16 * rt + li][0] : &sm.k[16 * rt + li][0];
             f16x8 af[F::KD];
 #pragma unroll
@@ -294,6 +345,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
             for (int st = 0; st < NR; ++st) {
                 if (st > rt) break;
+                if (TRANS && (st & 1) != par) continue;
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int kk = 0; kk < F::KD; ++kk)
@@ -322,6 +374,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                 for (int rr = 0; rr < 4; ++rr)
                     sm.p[16 * rt + 4 * lg + rr][kperm(16 * (rt + 1) + li)] = f16(0.f);
             }
+        }
         }
         lds_barrier();
 
@@ -381,6 +434,15 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         vmax = max_over_rows(vmax);  // the column's four lanes
         float sig, isig;
         pow2_scale(vmax, sig, isig);
+        float sigm = 1.f, isigm = 1.f;  // kTrans: the same for the column of M
+        if constexpr (TRANS) {
+            float mmax = 0.f;
+#pragma unroll
+            for (int it = 0; it < F::NI; ++it)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) mmax = fmaxf(mmax, fabsf(M[it][r]));
+            pow2_scale(max_over_rows(mmax), sigm, isigm);
+        }
         f32x4 U[NR], Wp[NR];
 #pragma unroll
         for (int a = 0; a < NR; ++a) {
@@ -407,6 +469,59 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) sm.wn[16 * a + 4 * lg + rr][kperm(col)] = f16(-Wp[a][rr]);
         lds_barrier();
+
+        if constexpr (TRANS) {
+            // ---- stage 4 of the transition: N as the state (U - W N), M with no value part
+            //      (-W M); both updated through K^T diag(e^(gamma_last - gamma)), each column
+            //      scaled by its own power of two
+            // k-steps outermost, so that only one k-step of the B operands is live at a time
+            f32x4 DM[NR];
+#pragma unroll
+            for (int rt = 0; rt < NR; ++rt) DM[rt] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < F::KD; ++kk) {
+                f16x8 bS, bM;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    bS[e] = f16(sig * S[2 * kk][e]);
+                    bS[4 + e] = f16(sig * S[2 * kk + 1][e]);
+                    bM[e] = f16(sigm * M[2 * kk][e]);
+                    bM[4 + e] = f16(sigm * M[2 * kk + 1][e]);
+                }
+#pragma unroll
+                for (int rt = 0; rt < NR; ++rt) {
+                    const f16x8 aw = *reinterpret_cast<const f16x8 *>(&sm.wn[16 * rt + li][32 * kk + 8 * lg]);
+                    U[rt] = mma_k32(aw, bS, U[rt]);
+                    DM[rt] = mma_k32(aw, bM, DM[rt]);
+                }
+            }
+            f16x8 bDs[F::KC], bDm[F::KC];
+#pragma unroll
+            for (int kk = 0; kk < F::KC; ++kk)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s0i = 32 * kk + 4 * lg + e, s1i = s0i + 16;
+                    bDs[kk][e] = f16(U[2 * kk][e] * sm.dec[s0i]);
+                    bDs[kk][4 + e] = f16(U[2 * kk + 1][e] * sm.dec[s1i]);
+                    bDm[kk][e] = f16(DM[2 * kk][e] * sm.dec[s0i]);
+                    bDm[kk][4 + e] = f16(DM[2 * kk + 1][e] * sm.dec[s1i]);
+                }
+            const float GC = sm.Gam[C - 1] * sig, GM = sm.Gam[C - 1] * sigm;
+#pragma unroll
+            for (int it = 0; it < F::NI; ++it) {
+                S[it] *= GC;
+                M[it] *= GM;
+#pragma unroll
+                for (int kk = 0; kk < F::KC; ++kk) {
+                    const f16x8 ak = *reinterpret_cast<const f16x8 *>(&sm.kt[16 * it + li][32 * kk + 8 * lg]);
+                    S[it] = mma_k32(ak, bDs[kk], S[it]);
+                    M[it] = mma_k32(ak, bDm[kk], M[it]);
+                }
+                S[it] *= isig;
+                M[it] *= isigm;
+            }
+            continue;
+        }
 
         // ---- stage 4 (sequential part): Delta, O, next state -- U, Delta, O scaled by sig
         // sig S as fp16 B operands over the key index: slot e < 4 -> tile 2kk row 4lg+e,
@@ -473,6 +588,19 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         }
     }
 
+    if constexpr (TRANS) {  // M and N of the segment (addresses formed only here)
+        float *pm = mn + (static_cast<size_t>(seg) * nchains + chain) * 2 * D * D;
+        const int lgo = opaque(lg), colo = opaque(col);
+#pragma unroll
+        for (int it = 0; it < F::NI; ++it)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const size_t e = static_cast<size_t>(16 * it + 4 * lgo + r) * D + colo;
+                pm[e] = M[it][r];
+                pm[D * D + e] = S[it][r];
+            }
+        return;
+    }
     // ---- the last chunk's output (rows past T are not stored) and the final state
     lds_barrier();
     if (nchunks > 0) {
@@ -486,7 +614,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             }
         }
     }
-    if (sT) {
+    if (sT && seg == nseg - 1) {
 #pragma unroll
         for (int it = 0; it < F::NI; ++it)
 #pragma unroll
@@ -495,20 +623,148 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     }
 }
 
-template <int D, int C, typename TO> hipError_t launch_typed(const PrefillArgs &a) {
-    auto kern = chunk_kernel<D, C, TO>;
+// ---- segmented plan: the entry state of every segment from the transitions of the ones
+//      before it, in fp32.  entry[0] = S0 (or 0); segment 0's N already started from S0, so
+//      entry[1] = N_0; entry[p] = M_{p-1} entry[p-1] + N_{p-1}.  One workgroup of 4 wavefronts
+//      per (chain, 16-column tile); the products run on the fp32 matrix cores
+//      (v_mfma_f32_16x16x4_f32), wavefront w forming row tiles w TPW .. of the new state.  The
+//      state tile is kept in LDS in the accumulator layout, and k-step (t, r) of a product
+//      sums over rows 16 t + 4 j + r (j = 0..3): register r of accumulator tile t is then that
+//      k-step's B operand as it stands, and the matching A operand (columns 16 t + 4 j + r of
+//      M) is one 16-byte LDS read for r = 0..3.  M_{p+1} and N_{p+1} are loaded into registers
+//      while step p runs.
+template <int D> struct CombineSmem {
+    float m[D][D + 8];     // M_p, row-major; pitch 8 mod 32 dwords for the 16-byte A reads
+    f32x4 st[D / 16][64];  // the state tile: [row tile][lane], accumulator layout
+};
+
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+__global__ void __launch_bounds__(256)
+seg_combine_kernel(const float *s0, const float *__restrict__ mn, float *__restrict__ entry,
+                   int nchains, int nseg) {
+    constexpr int NT = D / 16, TPW = NT / 4;  // row tiles; per wavefront
+    constexpr int NM = D * D / 4 / 256;        // 16-byte pieces of M per thread
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    CombineSmem<D> &sm = *reinterpret_cast<CombineSmem<D> *>(smem_raw);
+    const int chain = blockIdx.x / NT, jt = blockIdx.x - chain * NT;
+    const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+    const int w = tid >> 6, col = 16 * jt + li;
+    const size_t DD = static_cast<size_t>(D) * D, cs = static_cast<size_t>(nchains) * DD;
+    const size_t sb = static_cast<size_t>(chain) * DD;
+    auto mp = [&](int p) { return mn + (static_cast<size_t>(p) * nchains + chain) * 2 * DD; };
+    auto at = [&](int t, int r) { return static_cast<size_t>(16 * t + 4 * lg + r) * D + col; };
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int t = w * TPW + i;
+        f32x4 x;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            entry[sb + at(t, r)] = s0 != nullptr ? s0[sb + at(t, r)] : 0.f;
+            x[r] = mp(0)[DD + at(t, r)];  // N_0
+            entry[cs + sb + at(t, r)] = x[r];
+        }
+        sm.st[t][lane] = x;
+    }
+    if (nseg <= 2) return;
+    f32x4 mr[NM], nx[TPW];
+    auto load_mn = [&](int p) {
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(mp(p));
+#pragma unroll
+        for (int n = 0; n < NM; ++n) mr[n] = src[tid + 256 * n];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) nx[i][r] = mp(p)[DD + at(w * TPW + i, r)];
+    };
+    auto stage_m = [&]() {
+#pragma unroll
+        for (int n = 0; n < NM; ++n) {
+            const int idx = tid + 256 * n, r = idx / (D / 4), c4 = idx - r * (D / 4);
+            *reinterpret_cast<f32x4 *>(&sm.m[r][4 * c4]) = mr[n];
+        }
+    };
+    load_mn(1);
+    stage_m();
+    for (int p = 1; p + 1 < nseg; ++p) {
+        __syncthreads();  // M_p and the state tile are in LDS
+        f32x4 acc[TPW][2];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            acc[i][0] = nx[i];
+            acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        if (p + 2 < nseg) load_mn(p + 1);  // consumed after this step's products
+        f32x4 bS[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) bS[t] = sm.st[t][lane];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const f32x4 a4 = *reinterpret_cast<const f32x4 *>(
+                    &sm.m[16 * (w * TPW + i) + li][16 * t + 4 * lg]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][t & 1] = mma_f32(a4[r], bS[t][r], acc[i][t & 1]);
+            }
+        __syncthreads();  // every wavefront is done reading M_p and the state tile
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int t = w * TPW + i;
+            const f32x4 x = acc[i][0] + acc[i][1];
+            sm.st[t][lane] = x;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) entry[(p + 1) * cs + sb + at(t, r)] = x[r];
+        }
+        if (p + 2 < nseg) stage_m();
+    }
+}
+
+template <int D, int C, typename TO, int MODE>
+hipError_t launch_mode(const PrefillArgs &a, unsigned nblk, int nchains, int seg_chunks,
+                       int nseg, const float *s0, size_t s0_seg_stride, float *mn) {
+    auto kern = chunk_kernel<D, C, TO, MODE>;
     const size_t lds = sizeof(Smem<D, C>);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    const unsigned nblk = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.Hv);
     hipLaunchKernelGGL(kern, dim3(nblk), dim3(Cfg<D, C>::NT), lds, a.stream,
                        static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
                        static_cast<const bf16_t *>(a.v), static_cast<const bf16_t *>(a.beta),
-                       static_cast<const bf16_t *>(a.g), a.s0, static_cast<TO *>(a.o), a.sT, a.T,
-                       a.cu, a.flags, a.Hk, a.Hv, a.scale);
+                       static_cast<const bf16_t *>(a.g), s0, static_cast<TO *>(a.o), a.sT, a.T,
+                       a.cu, a.flags, a.Hk, a.Hv, a.scale, nchains, seg_chunks, nseg,
+                       s0_seg_stride, mn);
     return hipGetLastError();
+}
+
+template <int D, int C, typename TO> hipError_t launch_typed(const PrefillArgs &a) {
+    const int nchains = a.B * a.Hv;
+    const SegGeom sg = seg_geometry(a);
+    if (sg.nseg <= 1)
+        return launch_mode<D, C, TO, kOut>(a, static_cast<unsigned>(nchains), nchains, 1 << 30,
+                                           1, a.s0, 0, nullptr);
+    // segmented: transitions of segments 0 .. nseg-2, their entry states, then every segment
+    const size_t DD = static_cast<size_t>(D) * D;
+    float *mn = static_cast<float *>(a.ws);
+    float *entry = mn + static_cast<size_t>(sg.nseg - 1) * nchains * 2 * DD;
+    hipError_t e = launch_mode<D, C, float, kTrans>(
+        a, static_cast<unsigned>((sg.nseg - 1) * nchains), nchains, sg.seg_chunks, sg.nseg, a.s0,
+        0, mn);
+    if (e != hipSuccess) return e;
+    const size_t clds = sizeof(CombineSmem<D>);
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(seg_combine_kernel<D>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(clds));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(seg_combine_kernel<D>, dim3(static_cast<unsigned>(nchains * (D / 16))),
+                       dim3(256), clds, a.stream, a.s0, mn, entry, nchains, sg.nseg);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return launch_mode<D, C, TO, kOut>(a, static_cast<unsigned>(sg.nseg * nchains), nchains,
+                                       sg.seg_chunks, sg.nseg, entry,
+                                       static_cast<size_t>(nchains) * DD, nullptr);
 }
 
 template <int D, int C> hipError_t launch_out(const PrefillArgs &a) {
@@ -526,7 +782,31 @@ bool chunk_mfma_supports(const PrefillArgs &a) {
            (a.chunk == 32 || a.chunk == 64);
 }
 
-size_t chunk_mfma_workspace(const PrefillArgs &) { return 0; }
+SegGeom seg_geometry(const PrefillArgs &a) {
+    SegGeom g{1, 1 << 30};
+    if (!a.seg || a.cu != nullptr || a.B <= 0 || a.T <= 0) return g;
+    const long nch = (static_cast<long>(a.T) + a.chunk - 1) / a.chunk;
+    const long chains = static_cast<long>(a.B) * a.Hv;
+    long len = 0;  // chunks per segment
+    const char *env = getenv("GDN_SEG_CHUNKS");
+    if (env != nullptr && atol(env) > 0) {
+        len = atol(env);  // a segment length pinned for tests and measurements
+    } else {
+        const long want = std::max(1L, kSegTargetUnits / chains);  // segments per chain
+        len = (nch + want - 1) / want;
+    }
+    len = std::min(len, nch);
+    g.nseg = static_cast<int>((nch + len - 1) / len);
+    g.seg_chunks = static_cast<int>(len);
+    return g;
+}
+
+size_t chunk_mfma_workspace(const PrefillArgs &a) {
+    const SegGeom sg = seg_geometry(a);
+    if (sg.nseg <= 1) return 0;
+    const size_t DD = static_cast<size_t>(a.dk) * a.dv, chains = static_cast<size_t>(a.B) * a.Hv;
+    return (static_cast<size_t>(sg.nseg - 1) * 2 + sg.nseg) * chains * DD * sizeof(float);
+}
 
 hipError_t launch_chunk_mfma(const PrefillArgs &a) {
     if (!chunk_mfma_supports(a)) return hipErrorNotSupported;

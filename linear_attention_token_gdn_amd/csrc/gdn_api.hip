@@ -30,13 +30,31 @@ bool overlap(const void *p, size_t n, const void *r, size_t m) {
     return a < b + m && b < a + n;
 }
 
-// Prefill variants.  GDN_FORCE_VARIANT=recurrent|fused|split pins one for A/B measurements
-// (a variant that does not support the sizes falls back to the default choice).
-enum class Variant { Recurrent, Fused, Split };
+// Prefill variants.  GDN_FORCE_VARIANT=recurrent|fused|split|segmented pins one for A/B
+// measurements (a variant that does not support the sizes falls back to the default choice).
+enum class Variant { Recurrent, Fused, Split, Segmented };
 
-// Below this many (b, hv) chains the single-pass kernel leaves most compute units idle and
-// the two-kernel form (parallel over chunks) is used.
+// Below this many (b, hv) chains the single-pass kernel leaves most compute units idle; chains
+// are then cut into segments run in parallel (dense inputs), or the two-kernel form (parallel
+// over chunks) is used (packed sequences, whose lengths the host does not know).
 constexpr long kSplitBelowChains = 128;
+
+bool segmented_supported(const gdn::PrefillArgs &a) {
+    if (!gdn::chunk_mfma_supports(a) || a.cu != nullptr) return false;
+    gdn::PrefillArgs s = a;
+    s.seg = true;
+    return gdn::seg_geometry(s).nseg > 1;
+}
+
+// The default choice for few chains: segments of at least kSegMinChunks chunks (or a length
+// pinned by GDN_SEG_CHUNKS).
+bool segmented_preferred(const gdn::PrefillArgs &a) {
+    if (!segmented_supported(a)) return false;
+    gdn::PrefillArgs s = a;
+    s.seg = true;
+    const char *env = getenv("GDN_SEG_CHUNKS");
+    return (env != nullptr && atol(env) > 0) || gdn::seg_geometry(s).seg_chunks >= gdn::kSegMinChunks;
+}
 
 Variant choose_variant(const gdn::PrefillArgs &a) {
     const char *env = getenv("GDN_FORCE_VARIANT");
@@ -44,12 +62,22 @@ Variant choose_variant(const gdn::PrefillArgs &a) {
         if (strcmp(env, "recurrent") == 0) return Variant::Recurrent;
         if (strcmp(env, "fused") == 0 && gdn::chunk_mfma_supports(a)) return Variant::Fused;
         if (strcmp(env, "split") == 0 && gdn::chunk_split_supports(a)) return Variant::Split;
+        if (strcmp(env, "segmented") == 0 && segmented_supported(a)) return Variant::Segmented;
     }
     const long chains = static_cast<long>(a.B) * a.Hv;
-    if (gdn::chunk_split_supports(a) && (chains < kSplitBelowChains || (a.flags & GDN_PREFER_SPLIT)))
-        return Variant::Split;
+    const bool few = chains < kSplitBelowChains;
+    if (gdn::chunk_split_supports(a) && (a.flags & GDN_PREFER_SPLIT)) return Variant::Split;
+    if (few && segmented_preferred(a)) return Variant::Segmented;
+    if (few && gdn::chunk_split_supports(a)) return Variant::Split;
     if (gdn::chunk_mfma_supports(a)) return Variant::Fused;
     return Variant::Recurrent;
+}
+
+// The arguments with the plan's own switches set.
+gdn::PrefillArgs for_plan(const gdn::PrefillArgs &a, Variant var) {
+    gdn::PrefillArgs r = a;
+    r.seg = var == Variant::Segmented;
+    return r;
 }
 
 }  // namespace
@@ -108,9 +136,10 @@ static gdn_status_t check_prefill(const gdn::PrefillArgs &a) {
 // Workspace bytes the plan `var` needs for a validated prefill with tokens: the size the
 // workspace-size queries return, or (least) the smallest it runs with.
 static size_t plan_workspace(const gdn::PrefillArgs &a, Variant var, bool least = false) {
-    return var == Variant::Split   ? gdn::chunk_split_workspace(a, least)
-           : var == Variant::Fused ? gdn::chunk_mfma_workspace(a)
-                                   : 0;
+    return var == Variant::Split ? gdn::chunk_split_workspace(a, least)
+           : var == Variant::Fused || var == Variant::Segmented
+               ? gdn::chunk_mfma_workspace(for_plan(a, var))
+               : 0;
 }
 
 // The whole prefill: validation, the T = 0 case, workspace check and dispatch.  least: the
@@ -129,9 +158,10 @@ static gdn_status_t run_prefill(gdn::PrefillArgs &a, bool least = false) {
     const size_t need = plan_workspace(a, var, least);
     if (need > 0 && (a.ws == nullptr || a.ws_bytes < need)) return GDN_ERR_INVALID_ARG;
     if (need > 0 && !aligned(a.ws, 256)) return GDN_ERR_INVALID_ARG;
-    hipError_t e = var == Variant::Split   ? gdn::launch_chunk_split(a)
-                   : var == Variant::Fused ? gdn::launch_chunk_mfma(a)
-                                           : gdn::launch_recurrent(a);
+    hipError_t e = var == Variant::Split ? gdn::launch_chunk_split(a)
+                   : var == Variant::Fused || var == Variant::Segmented
+                       ? gdn::launch_chunk_mfma(for_plan(a, var))
+                       : gdn::launch_recurrent(a);
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
@@ -147,6 +177,7 @@ const char *gdn_chunk_fwd_plan(int B, int T, int Hk, int Hv, int dk, int dv, int
     switch (choose_variant(a)) {
     case Variant::Split: return "split";
     case Variant::Fused: return "fused";
+    case Variant::Segmented: return "segmented";
     default: return "recurrent";
     }
 }
@@ -165,9 +196,11 @@ static size_t prefill_workspace(int B, int T, int Hk, int Hv, int dk, int dv, in
         !dim_supported(dv) || (chunk != 16 && chunk != 32 && chunk != 64) || !dtype_known(in_dtype))
         return 0;
     if (B == 0 || T == 0) return 0;
-    switch (choose_variant(a)) {
+    const Variant var = choose_variant(a);
+    switch (var) {
     case Variant::Split: return gdn::chunk_split_workspace(a);
-    case Variant::Fused: return gdn::chunk_mfma_workspace(a);
+    case Variant::Fused:
+    case Variant::Segmented: return gdn::chunk_mfma_workspace(for_plan(a, var));
     default: return 0;
     }
 }

@@ -25,6 +25,7 @@ struct PrefillArgs {
     void *ws;
     size_t ws_bytes;
     hipStream_t stream;
+    bool seg = false;  // the single-pass kernel runs the segmented plan (chunk_mfma.hip)
 };
 
 struct DecodeArgs {
@@ -81,6 +82,19 @@ hipError_t launch_qsa(const QsaArgs &a);
 hipError_t launch_recurrent(const PrefillArgs &a);
 
 // Chunk-parallel MFMA kernel for bf16 inputs.  supports() says whether the sizes are handled.
+// With a.seg (dense inputs), the segmented plan: every chain is cut into nseg segments of
+// seg_chunks chunks, run in parallel -- a transition pass (each segment's affine map of the
+// state), a sequential combine of those maps into every segment's entry state, then the
+// single-pass kernel over all segments.  Its workspace holds the maps and the entry states.
+struct SegGeom {
+    int nseg, seg_chunks;
+};
+constexpr long kSegTargetUnits = 256;  // (chain, segment) units at most: MI355X's CUs
+// Segments shorter than this many chunks lose to the two-kernel form (measured: 16 chains of
+// 4,096 tokens run in 4-chunk segments at 0.115 ms against 0.098 ms; of 8,192 tokens in 8-chunk
+// segments at 0.171 ms against 0.186 ms)
+constexpr long kSegMinChunks = 8;
+SegGeom seg_geometry(const PrefillArgs &a);
 bool chunk_mfma_supports(const PrefillArgs &a);
 size_t chunk_mfma_workspace(const PrefillArgs &a);
 hipError_t launch_chunk_mfma(const PrefillArgs &a);

@@ -14,7 +14,9 @@ for the copy).  It prints markdown and writes profiles/traffic.json (the prefill
 record labelled with the prefill workload, e.g. workload3; the decode kernel's with
 workload4), which bench.py reports while the kernel sources and the workload are unchanged.
 A split-plan prefill that runs in `segments` segments launches prep and scan that many times
-per call; its record holds bytes per call (all their launches over the number of calls).  `mfma` reads one counter pass with
+per call; its record holds bytes per call (all their launches over the number of calls).  The
+segmented plan's three kernels (transition pass, combine, single pass) launch once per call and
+are recorded together under "segmented".  `mfma` reads one counter pass with
 `--pmc MfmaUtil MfmaFlopsF16 MfmaFlopsBF16 SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE` and one with
 `--pmc LdsBankConflict SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE` over a run of one prefill
 workload, prints per-kernel matrix-core busy time, matrix-core flops as issued (which include
@@ -38,6 +40,9 @@ SOURCES = {
                 for n in ("chunk_split.hip", "gdn_internal.h")],
     "fused": [os.path.join(ROOT, "linear_attention_token_gdn_amd", "csrc", n)
               for n in ("chunk_mfma.hip", "gdn_internal.h")],
+    # the segmented plan: the fused kernel's file (transition pass, combine, single pass)
+    "segmented": [os.path.join(ROOT, "linear_attention_token_gdn_amd", "csrc", n)
+                  for n in ("chunk_mfma.hip", "gdn_internal.h")],
     "decode": [os.path.join(ROOT, "linear_attention_token_gdn_amd", "csrc", n)
                for n in ("decode.hip", "gdn_internal.h")],
 }
@@ -174,8 +179,10 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, command, workload, seg
         out.append("| `%s` | %d | %.0f | %.0f | %.1f | %.1f |" % (
             _label(name), len(fetch.get(name, [])), f, w, rd / 1e6, wr / 1e6))
     rec = {"copy_scale_fetch": sf, "copy_scale_write": sw, "command": command}
+    segmented = any(n.startswith("seg_combine_kernel") for n in res)
     for key, names, seg in (("prefill", ("prep_kernel", "scan_kernel"), segments),
-                            ("fused", ("chunk_kernel",), 1)):
+                            ("segmented" if segmented else "fused",
+                             ("chunk_kernel", "seg_combine_kernel"), 1)):
         pre = [n for n in res if n.startswith(names)]
         if pre:
             # per call: every launch of these kernels over the number of calls (the launches of
@@ -200,7 +207,7 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, command, workload, seg
     return "\n".join(out)
 
 
-PREFILL_KERNELS = ("prep_kernel", "scan_kernel", "chunk_kernel")
+PREFILL_KERNELS = ("prep_kernel", "scan_kernel", "chunk_kernel", "seg_combine_kernel")
 
 
 def mfma(label, mfma_dir, lds_dir, algo_flops, command, segments="1"):

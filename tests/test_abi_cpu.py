@@ -48,6 +48,28 @@ def test_version_and_status_strings(lib):
     assert gdn.gdn_status_string(99) == "GDN_ERR_UNKNOWN"
 
 
+def test_workspace_of_the_segmented_plan(lib, monkeypatch):
+    # per chain and segment: the fp32 transition M and state N of every segment but the last,
+    # and the entry state of every segment (d x d floats each); 256 / chains segments
+    D2 = 128 * 128 * 4
+    for B, T, H, nseg in ((1, 262144, 16, 16), (1, 8192, 16, 16), (4, 4096, 16, 4),
+                          (1, 1 << 20, 2, 128)):
+        chains = B * H
+        assert gdn.gdn_chunk_fwd_workspace_size(B, T, H, H, 128, 128, 64, gdn.GDN_BF16) == (
+            (2 * (nseg - 1) + nseg) * chains * D2)
+    # the largest: 256 units at d = 128 fit the allocation-free entry point's scratch
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 1 << 20, 1, 2, 128, 128, 64, gdn.GDN_BF16) \
+        <= gdn.GDN_NOALLOC_SCRATCH_BYTES
+    # a pinned segment length (tests): one chunk per segment
+    monkeypatch.setenv("GDN_SEG_CHUNKS", "1")
+    monkeypatch.setenv("GDN_FORCE_VARIANT", "segmented")
+    assert gdn.gdn_chunk_fwd_plan(1, 200, 2, 2, 64, 64, 64, gdn.GDN_BF16) == "segmented"
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 200, 2, 2, 64, 64, 64, gdn.GDN_BF16) == (
+        (2 * 3 + 4) * 2 * 64 * 64 * 4)
+    # one chunk in all: nothing to cut, the default plan
+    assert gdn.gdn_chunk_fwd_plan(1, 64, 2, 2, 64, 64, 64, gdn.GDN_BF16) == "split"
+
+
 def test_workspace_size_of_the_chunk_kernels(lib):
     # few chains: the prep + scan form needs a workspace; one float32 path needs none
     assert gdn.gdn_chunk_fwd_workspace_size(1, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16) > 16 * 64 * 65536
@@ -57,6 +79,11 @@ def test_workspace_size_of_the_chunk_kernels(lib):
 
 def test_plan(lib):
     assert gdn.gdn_chunk_fwd_plan(1, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16) == "split"
+    # few long chains: segments of >= 8 chunks, at most 256 (chain, segment) units
+    assert gdn.gdn_chunk_fwd_plan(1, 8192, 16, 16, 128, 128, 64, gdn.GDN_BF16) == "segmented"
+    assert gdn.gdn_chunk_fwd_plan(1, 262144, 16, 16, 128, 128, 64, gdn.GDN_BF16) == "segmented"
+    assert gdn.gdn_chunk_fwd_plan(4, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16) == "segmented"
+    assert gdn.gdn_chunk_fwd_plan(1, 262144, 16, 16, 128, 128, 64, gdn.GDN_F32) == "recurrent"
     assert gdn.gdn_chunk_fwd_plan(8, 8192, 16, 32, 128, 128, 64, gdn.GDN_BF16) == "fused"
     assert gdn.gdn_chunk_fwd_plan(1, 64, 2, 2, 16, 16, 16, gdn.GDN_F32) == "recurrent"
     assert gdn.gdn_chunk_fwd_plan(1, 64, 2, 2, 16, 32, 16, gdn.GDN_BF16) == "recurrent"
@@ -136,6 +163,7 @@ def test_noalloc_scratch_holds_the_smallest_split_workspace(lib, monkeypatch):
     workspace (one chunk per segment) fits 80 MiB even at the largest chain count the plan
     takes (127 chains at d = 128), so no size the plans run is refused for its length."""
     monkeypatch.setenv("GDN_SPLIT_RECORD_BYTES", "1")
+    monkeypatch.setenv("GDN_FORCE_VARIANT", "split")  # dense sizes like these run segmented
     least = gdn.gdn_chunk_fwd_workspace_size(1, 1 << 20, 1, 127, 128, 128, 64, gdn.GDN_BF16)
     assert gdn.gdn_chunk_fwd_plan(1, 1 << 20, 1, 127, 128, 128, 64, gdn.GDN_BF16) == "split"
     assert 0 < least <= gdn.GDN_NOALLOC_SCRATCH_BYTES // 4
@@ -249,6 +277,7 @@ def test_split_workspace_is_bounded(lib, monkeypatch):
     sequence of a million tokens is that of about 1,800 chunks, not of 16,384; the environment
     cap lowers it, down to one chunk per segment."""
     rec = 73728 + 128
+    monkeypatch.setenv("GDN_FORCE_VARIANT", "split")  # the default for these is segmented
     big = gdn.gdn_chunk_fwd_workspace_size(1, 1 << 20, 16, 16, 128, 128, 64, gdn.GDN_BF16)
     L = (2 << 30) // (16 * rec)
     assert big == L * 16 * rec + split_fixed(16, 128)
@@ -270,11 +299,11 @@ def test_varlen_workspace(lib):
     # many chains: the single-pass kernel, no workspace, packed or not
     assert gdn.gdn_chunk_fwd_plan(16, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16) == "fused"
     assert ws(16, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1) == 0
-    # few chains: the split plan; packed sequences take one record slot per sequence and head
-    # beyond the chunks of the total length (records of 72 KiB + one 128-byte line of scalars
-    # at d = 128, C = 64), plus per chain a 256-byte progress word, the fp32 state carried
-    # between segments and two floats per 16-column tile (padded to 256 B)
-    assert gdn.gdn_chunk_fwd_plan(4, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16) == "split"
+    # few chains, packed: the split plan (the segmented plan takes dense inputs only);
+    # packed sequences take one record slot per sequence and head beyond the chunks of the
+    # total length (records of 72 KiB + one 128-byte line of scalars at d = 128, C = 64), plus
+    # per chain a 256-byte progress word, the fp32 state carried between segments and two
+    # floats per 16-column tile (padded to 256 B)
     slots = 16 * (4096 // 64 + 4)
     assert ws(4, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1) == (
         slots * (73728 + 128) + split_fixed(4 * 16, 128))

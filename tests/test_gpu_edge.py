@@ -1,7 +1,7 @@
 """GPU parity on the special cases of the gated delta rule (explainer page "論文解説:
 Qwen3.8-Next の設計", ta-paperlens.web.app, section "GDNの中身", Eq. (1), with alpha and beta
-in their closed ranges) through both chunk-parallel plans and the decode kernel, against the
-fp64 oracle and, where Eq. (1) fixes the answer in closed form, against that answer too.
+in their closed ranges) through the three chunk-parallel plans (single pass, split, segmented)
+and the decode kernel, against the fp64 oracle and, where Eq. (1) fixes the answer in closed form, against that answer too.
 
 Cases: beta = 1 with basis keys (the written value is read back exactly, for any alpha and
 state); beta = 0 with g = 0 (the state is kept bit for bit); g = -60 (memoryless); one key
@@ -23,7 +23,7 @@ from parity import check
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-PLANS = ["fused", "split"]
+PLANS = ["fused", "split", "segmented"]
 ALL = 1 | 2 | 4  # GDN_QK_L2NORM | GDN_BETA_LOGIT | GDN_G_LOGIT
 
 
@@ -33,6 +33,14 @@ def _gpu():
         pytest.skip("no GPU")
     import linear_attention_token_gdn_amd as gdn
     gdn.load_library()
+
+
+def use_plan(monkeypatch, plan):
+    """Pin the prefill plan; the segmented one with one chunk per segment, so that every chunk
+    boundary is a segment boundary (transition, combine and entry state all exercised)."""
+    monkeypatch.setenv("GDN_FORCE_VARIANT", plan)
+    if plan == "segmented":
+        monkeypatch.setenv("GDN_SEG_CHUNKS", "1")
 
 
 def gdn_mod():
@@ -105,7 +113,7 @@ def test_beta_one_reads_back_the_written_value(plan, decay, monkeypatch):
     """beta = 1 and a unit key overwrite what the state holds under that key: with q_t = k_t
     the output is v_t exactly, for any alpha and any initial state (basis keys are exact in
     bf16; repeated keys are rewritten with their latest value)."""
-    monkeypatch.setenv("GDN_FORCE_VARIANT", plan)
+    use_plan(monkeypatch, plan)
     rng = np.random.default_rng(900 + decay)
     B, T, H, d = 1, 200, 2, 128
     k = basis_keys(rng, B, T, H, d)
@@ -149,7 +157,7 @@ def test_beta_zero_without_decay_keeps_the_state(plan, monkeypatch):
         np.testing.assert_array_equal(S2, inp.s0)
         check(o2, ro, "bf16", "beta=0 decode_tokens o")
     else:
-        monkeypatch.setenv("GDN_FORCE_VARIANT", plan)
+        use_plan(monkeypatch, plan)
         o, sT = prefill(inp)
     np.testing.assert_array_equal(sT, inp.s0)
     check(o, ro, "bf16", "beta=0 %s o" % plan)
@@ -167,7 +175,7 @@ def test_memoryless_gates(plan, monkeypatch):
         (o, sT), (o2, S2) = decode(inp)
         check_all("g=-60 decode_tokens", [("o", o2, ro), ("S", S2, rS)])
     else:
-        monkeypatch.setenv("GDN_FORCE_VARIANT", plan)
+        use_plan(monkeypatch, plan)
         o, sT = prefill(inp)
     check_all("g=-60 %s" % plan, [("o", o, ro), ("S", sT, rS)])
     # the closed-form limit, from the stored inputs (the state left by the last token)
@@ -184,7 +192,7 @@ def test_memoryless_gates(plan, monkeypatch):
 def test_repeated_and_near_parallel_keys(plan, kind, monkeypatch):
     """One key for a whole chunk (A is a full strictly lower triangle of beta_r e^(..)), or
     keys at cosine ~0.999 to a common direction, with random beta and a strong initial state."""
-    monkeypatch.setenv("GDN_FORCE_VARIANT", plan)
+    use_plan(monkeypatch, plan)
     rng = np.random.default_rng(930)
     B, T, H, d = 1, 190, 2, 128
     base = make_inputs(B, T, H, H, d, d, dtype="bf16", s0_std=0.3, seed=930)
@@ -208,7 +216,7 @@ def test_repeated_and_near_parallel_keys(plan, kind, monkeypatch):
 @pytest.mark.parametrize("plan", PLANS)
 def test_split_and_resume_through_the_final_state(plan, monkeypatch):
     """run(T1) then run(T2 | initial = final(T1)) = run(T1 + T2)."""
-    monkeypatch.setenv("GDN_FORCE_VARIANT", plan)
+    use_plan(monkeypatch, plan)
     inp = make_inputs(1, 250, 2, 4, 128, 128, dtype="bf16", s0_std=0.02, seed=940)
     T1 = 100  # not a multiple of the chunk: the first call ends in a partial chunk
 
@@ -239,7 +247,7 @@ def test_superposition_in_state_and_values(plan, monkeypatch):
     if plan == "decode":
         run = lambda x: decode(x)[0]
     else:
-        monkeypatch.setenv("GDN_FORCE_VARIANT", plan)
+        use_plan(monkeypatch, plan)
         run = prefill
     o, sT = run(inp)
     oa, Sa = run(only_s)
@@ -264,7 +272,7 @@ def test_power_of_two_scale_invariance(plan, k2, monkeypatch):
     if plan == "decode":
         run = lambda x: decode(x)[0]
     else:
-        monkeypatch.setenv("GDN_FORCE_VARIANT", plan)
+        use_plan(monkeypatch, plan)
         run = prefill
     o, sT = run(inp)
     ob, Sb = run(big)
@@ -286,7 +294,7 @@ def test_large_and_small_values_and_state(plan, mag, monkeypatch):
         (o, sT), (o2, S2) = decode(inp)
         check_all("|v|~%g decode_tokens" % mag, [("o", o2, ro), ("S", S2, rS)])
     else:
-        monkeypatch.setenv("GDN_FORCE_VARIANT", plan)
+        use_plan(monkeypatch, plan)
         o, sT = prefill(inp)
     check_all("|v|~%g %s" % (mag, plan), [("o", o, ro), ("S", sT, rS)])
 
@@ -322,7 +330,7 @@ def test_l2norm_epsilon_clamp(plan, monkeypatch):
                                   flags=ALL)
         o = o[0]
     else:
-        monkeypatch.setenv("GDN_FORCE_VARIANT", plan)
+        use_plan(monkeypatch, plan)
         o, sT = gdn.chunk_fwd_varlen(t["q"][None], t["k"][None], t["v"][None], t["beta"][None],
                                      t["g"][None], initial_state=s0_t, flags=ALL)
         o = o[0]

@@ -184,12 +184,14 @@ def test_decode_matches_prefill_path():
 
 
 # ------------------------------------------------------------------ chunk-parallel variants
-@pytest.mark.parametrize("variant", ["fused", "split"])
+@pytest.mark.parametrize("variant", ["fused", "split", "segmented"])
 @pytest.mark.parametrize("d,chunk", [(128, 64), (128, 32), (64, 64), (64, 32)])
 def test_chunk_variants(variant, d, chunk, monkeypatch):
-    """Both chunk-parallel kernels (single pass; prep + scan through a workspace) against the
-    oracle, with grouped heads, an initial state, a scale and a ragged last chunk."""
+    """The chunk-parallel plans (single pass; prep + scan through a workspace; segments of two
+    chunks run in parallel) against the oracle, with grouped heads, an initial state, a scale
+    and a ragged last chunk."""
     monkeypatch.setenv("GDN_FORCE_VARIANT", variant)
+    monkeypatch.setenv("GDN_SEG_CHUNKS", "2")
     inp = make_inputs(2, 157, 2, 4, d, d, dtype="bf16", s0_std=0.02, seed=500 + d + chunk)
     check_prefill(inp, chunk, scale=0.8, tag="%s d%d c%d" % (variant, d, chunk))
 
@@ -197,7 +199,8 @@ def test_chunk_variants(variant, d, chunk, monkeypatch):
 def test_variants_agree_and_are_deterministic(monkeypatch):
     inp = make_inputs(1, 300, 1, 2, 128, 128, dtype="bf16", s0_std=0.02, seed=510)
     res = {}
-    for variant in ("fused", "split"):
+    monkeypatch.setenv("GDN_SEG_CHUNKS", "2")
+    for variant in ("fused", "split", "segmented"):
         monkeypatch.setenv("GDN_FORCE_VARIANT", variant)
         a = run_prefill(inp, 64)
         b = run_prefill(inp, 64)
@@ -206,6 +209,7 @@ def test_variants_agree_and_are_deterministic(monkeypatch):
         res[variant] = a
     M = np.abs(res["fused"][0]).max()
     assert np.abs(res["fused"][0] - res["split"][0]).max() <= 2e-3 * M
+    assert np.abs(res["fused"][0] - res["segmented"][0]).max() <= 2e-3 * M
 
 
 # ------------------------------------------------------------------ the workloads, full size

@@ -2,8 +2,9 @@
 workspace is the library's static scratch) against gdn_chunk_fwd with a caller workspace, both
 through the C ABI on the same inputs: bit-identical outputs and final states, two calls in a
 row (the second smaller, so the scratch still holds the first call's records), a plan without a
-workspace, and an input whose records exceed the scratch, which runs in two segments there and
-in one with the caller's workspace.  The outputs are also held to the oracle's bar (bf16
+workspace, the segmented plan (transitions and entry states in the scratch), and a split-plan
+input whose records exceed the scratch, which runs in two segments there and in one with the
+caller's workspace.  The outputs are also held to the oracle's bar (bf16
 inputs: eps <= 2e-3 M).
 """
 import numpy as np
@@ -62,7 +63,7 @@ def _same(inp, plan):
     return o1, s1
 
 
-def test_noalloc_equals_the_workspace_entry_point():
+def test_noalloc_equals_the_workspace_entry_point(monkeypatch):
     import linear_attention_token_gdn_amd as gdn
     # 1: the 4096-token, 16-head prefill (split plan, 72 MiB of the 80 MiB scratch)
     big = make_inputs(1, 4096, 16, 16, 128, 128, dtype="bf16", seed=990)
@@ -81,13 +82,19 @@ def test_noalloc_equals_the_workspace_entry_point():
     # 3: a plan without a workspace (many chains: the single-pass kernel)
     many = make_inputs(1, 200, 64, 128, 64, 64, dtype="bf16", s0_std=0.02, seed=992)
     _same(many, "fused")
-    # 4: records beyond the scratch (8192 tokens, 16 heads: 144 MiB in one pass): two
-    #    segments of chunks in the scratch, bit for bit the one-pass result
-    assert (gdn.gdn_chunk_fwd_workspace_size(1, 8192, 16, 16, 128, 128, 64, gdn.GDN_BF16)
-            > gdn.GDN_NOALLOC_SCRATCH_BYTES)
+    # 4: the segmented plan (8192 tokens, 16 heads: 16 segments of 8 chunks per chain; its
+    #    transitions and entry states in 46 MiB of the scratch)
     huge = make_inputs(1, 8192, 16, 16, 128, 128, dtype="bf16", s0_std=0.02, seed=993)
-    o, s = _same(huge, "split")
+    o, s = _same(huge, "segmented")
     chains = np.array([3, 12])
     ro, rS = oracle.run(huge.q, huge.k, huge.v, huge.beta, huge.g, s0=huge.s0, chains=chains)
+    check(o[0][:, chains].transpose(1, 0, 2), ro, "bf16", "noalloc segmented o (T=8192)")
+    check(s[0][chains], rS, "bf16", "noalloc segmented state (T=8192)")
+    # 5: split records beyond the scratch (the same input: 144 MiB in one pass): two segments
+    #    of chunks in the scratch, bit for bit the one-pass result
+    monkeypatch.setenv("GDN_FORCE_VARIANT", "split")
+    assert (gdn.gdn_chunk_fwd_workspace_size(1, 8192, 16, 16, 128, 128, 64, gdn.GDN_BF16)
+            > gdn.GDN_NOALLOC_SCRATCH_BYTES)
+    o, s = _same(huge, "split")
     check(o[0][:, chains].transpose(1, 0, 2), ro, "bf16", "noalloc o (T=8192)")
     check(s[0][chains], rS, "bf16", "noalloc state (T=8192)")

@@ -66,6 +66,24 @@ __device__ __forceinline__ f16x4 to_f16x4(f32x4 x) {
     return f16x4{f16(x[0]), f16(x[1]), f16(x[2]), f16(x[3])};
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP: row shifts by 1, 2, 4, 8
+// within each row of 16 lanes, then the totals of rows 0 and 2 broadcast into rows 1 and 3
+// (row_bcast:15) and that of rows 0-1 into rows 2 and 3 (row_bcast:31).  Lanes with no source
+// add 0 (bound_ctrl), masked rows keep theirs.  No LDS permutes.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_or_zero(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 CTRL, ROWS, 0xf, true));
+}
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+    x += dpp_or_zero<0x111, 0xf>(x);  // row_shr:1
+    x += dpp_or_zero<0x112, 0xf>(x);  // row_shr:2
+    x += dpp_or_zero<0x114, 0xf>(x);  // row_shr:4
+    x += dpp_or_zero<0x118, 0xf>(x);  // row_shr:8
+    x += dpp_or_zero<0x142, 0xa>(x);  // row_bcast:15 into rows 1, 3
+    x += dpp_or_zero<0x143, 0xc>(x);  // row_bcast:31 into rows 2, 3
+    return x;
+}
 // x, as a value the compiler cannot see through (nothing derived from it moves above this)
 __device__ __forceinline__ int opaque(int x) {
     asm volatile("" : "+v"(x));
@@ -97,8 +115,8 @@ template <int D, int C> struct Cfg {
     static constexpr int PA = C + 8;
     static constexpr int PO = D + 4;        // output staging pitch (floats)
     static constexpr int NQ = C * D / 8 / NT;  // 16-byte pieces of q (or k, v) per thread
-    static constexpr int NO = C * D / 4 / NT;  // 16-byte pieces of o per thread
     static_assert((D == 64 || D == 128) && (C == 32 || C == 64), "chunk kernel shape");
+    static constexpr int NO = C * D / 4 / NT;  // 16-byte pieces of o per thread
     static_assert(NQ >= 1 && (C * D / 8) % NT == 0 && (C * D / 4) % NT == 0, "tiling");
 };
 
@@ -126,10 +144,12 @@ template <int D, int C> struct Smem {
     f16 an[C][F::PA];         // -A, off-diagonal 16x16 blocks (lower)
     f16 td[F::NR][16][24];    // inverses of the diagonal blocks of I + A, fp16
     float adT[F::NR][16][20]; // diagonal blocks of A, fp32, transposed: [block][col][row]
-    float gam[C];             // gamma (chunk-local cumulative log-gate)
-    float Gam[C];             // exp(gamma)
-    float dec[C];             // exp(gamma_last - gamma)
-    float bet[C];             // beta
+    // per-chunk gates, double-buffered by chunk parity (those of the next chunk are formed
+    // while this one runs)
+    float gam[2][C];          // gamma (chunk-local cumulative log-gate)
+    float Gam[2][C];          // exp(gamma)
+    float dec[2][C];          // exp(gamma_last - gamma)
+    float bet[2][C];          // beta
     float ost[C][F::PO];      // scaled output of the chunk, waiting to be stored
 };
 
@@ -240,17 +260,35 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         }
         pg = 0;
         pb = 0;
-        if (tid < L) {
-            const size_t gi = (base + tt + tid) * Hv + hv;
+        if (wave == 1 && lane < L) {  // the gates: wavefront 1 forms them (gates(), below)
+            const size_t gi = (base + tt + lane) * Hv + hv;
             pg = g[gi];
             pb = beta[gi];
         }
     };
+    // wavefront 1: the gates of chunk cidx into buffer cidx & 1, from pg, pb (rows past the end:
+    // g = beta = 0)
+    auto gates = [&](int cidx) {
+        const int L = min(C, len - cidx * C), gb = cidx & 1;
+        float gv = lane < L ? log_alpha_from_input(bf16_to_f32(pg), flags) : 0.f;
+        gv = wave_inclusive_sum(gv);  // inclusive prefix sum over the chunk
+        const float glast = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gv), C - 1));
+        if (lane < C) {
+            sm.gam[gb][lane] = gv;
+            sm.Gam[gb][lane] = __expf(gv);
+            sm.dec[gb][lane] = __expf(glast - gv);
+            sm.bet[gb][lane] = lane < L ? beta_from_input(bf16_to_f32(pb), flags) : 0.f;
+        }
+    };
 
     const int nchunks = (len + C - 1) / C;
-    if (nchunks > 0) prefetch(0);
+    if (nchunks > 0) {
+        prefetch(0);
+        if (wave == 1) gates(0);
+    }
     for (int c = 0; c < nchunks; ++c) {
-        const int t0 = c * C;
+        const int t0 = c * C, cb = c & 1;
         lds_barrier();  // the previous chunk is done with every LDS buffer
 
         // ---- stage 0: stage this chunk in LDS, store the previous chunk's output, prefetch
@@ -290,22 +328,6 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             *reinterpret_cast<f16x4 *>(&sm.k[r][c1]) = f16x4{kh[4], kh[5], kh[6], kh[7]};
             *reinterpret_cast<u16x8 *>(&sm.v[r][cc * 8]) = pv[n];
         }
-        if (wave == 0) {
-            const int L = min(C, len - t0);  // rows past the end: g = beta = 0
-            float gv = lane < L ? log_alpha_from_input(bf16_to_f32(pg), flags) : 0.f;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {  // inclusive prefix sum over the chunk
-                const float y = __shfl_up(gv, off);
-                if (lane >= off) gv += y;
-            }
-            const float glast = __shfl(gv, C - 1);
-            if (lane < C) {
-                sm.gam[lane] = gv;
-                sm.Gam[lane] = __expf(gv);
-                sm.dec[lane] = __expf(glast - gv);
-                sm.bet[lane] = lane < L ? beta_from_input(bf16_to_f32(pb), flags) : 0.f;
-            }
-        }
         if (!TRANS && c > 0) {
             const int tp = t0 - C;  // the previous chunk is always a full one
 #pragma unroll
@@ -321,15 +343,18 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         // ---- stage 1: KK^T -> A, QK^T -> P (lower-triangular 16x16 tiles), and K^T
         {
         const int li_ = li, lg_ = lg;
-        // kTrans needs only K K^T: row tile job % NR, column tiles of parity job / NR (two
-        // wavefronts per row tile instead of one for each of K and Q)
+        // Jobs: wavefront w < NR takes row tile w of K K^T; wavefront w >= NR row tile
+        // 2 NR - 1 - w of Q K^T (kTrans, which needs only K K^T: the same row tiles of K K^T, the
+        // columns of odd parity).  Wavefronts w and w + 4 share a SIMD, so each SIMD gets row
+        // tiles r and NR - 1 - r: (r + 1) + (NR - r) lower 16x16 tiles, the same for every SIMD
+        // (one SIMD holding both longest row tiles took twice as long).
         // (kTrans: the lane's row and column offsets are made opaque here, so that the compiler
         // forms this stage's LDS addresses in the loop instead of keeping them in registers
         // across it -- the transition's second state leaves no registers for that)
         const int li = TRANS ? opaque(li_) : li_, lg = TRANS ? opaque(lg_) : lg_;
         for (int job = wave; job < 2 * NR; job += F::NW) {
             const bool isq = !TRANS && job >= NR;
-            const int rt = job >= NR ? job - NR : job;
+            const int rt = job >= NR ? 2 * NR - 1 - job : job;
             const int par = job >= NR ? 1 : 0;
             const f16 *arow = isq ? &sm.q[16 * rt + li][0] : &sm.k[16 * rt + li][0];
             f16x8 af[F::KD];
@@ -339,8 +364,8 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             float gr[4], br[4];
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                gr[rr] = sm.gam[16 * rt + 4 * lg + rr];
-                br[rr] = sm.bet[16 * rt + 4 * lg + rr];
+                gr[rr] = sm.gam[cb][16 * rt + 4 * lg + rr];
+                br[rr] = sm.bet[cb][16 * rt + 4 * lg + rr];
             }
 #pragma unroll
             for (int st = 0; st < NR; ++st) {
@@ -353,7 +378,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                                   *reinterpret_cast<const f16x8 *>(&sm.k[16 * st + li][32 * kk + 8 * lg]),
                                   acc);
                 const int s = 16 * st + li;
-                const float gs = sm.gam[s];
+                const float gs = sm.gam[cb][s];
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
                     const int r = 16 * rt + 4 * lg + rr;
@@ -401,8 +426,12 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sm.td[lg][r][li] = f16(x[r]);
             }
-        } else {
-            for (int idx = tid - 64; idx < D * (C / 8); idx += NT - 64) {
+        } else if (F::NW < 8 || wave != 4) {
+            // (wavefront 4 shares wavefront 0's SIMD and leaves it to the inverses)
+            if (wave == 1 && c + 1 < nchunks) gates(c + 1);  // its inputs came with the prefetch
+            constexpr int NB = F::NW < 8 ? NT - 64 : NT - 128;  // threads building K^T
+            const int bt = tid - 64 - (F::NW >= 8 && wave > 4 ? 64 : 0);
+            for (int idx = bt; idx < D * (C / 8); idx += NB) {
                 const int i = idx % D, s8 = idx / D, ki = kperm(i);
                 f16x8 x;  // stored positions 8 s8 .. 8 s8 + 7 of row i of K^T
 #pragma unroll
@@ -424,7 +453,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int r = 16 * a + 4 * lg + rr;
-                yv[a][rr] = sm.bet[r] * bf16_to_f32(sm.v[r][col]);
+                yv[a][rr] = sm.bet[cb][r] * bf16_to_f32(sm.v[r][col]);
                 vmax = fmaxf(vmax, fabsf(yv[a][rr]));
             }
 #pragma unroll
@@ -452,7 +481,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             for (int rr = 0; rr < 4; ++rr) {
                 const int r = 16 * a + 4 * lg + rr;
                 yu[rr] = sig * yv[a][rr];
-                yw[rr] = sm.bet[r] * sm.Gam[r] * float(kv4[rr]);
+                yw[rr] = sm.bet[cb][r] * sm.Gam[cb][r] * float(kv4[rr]);
             }
 #pragma unroll
             for (int cb = 0; cb < a; ++cb) {
@@ -501,12 +530,12 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int s0i = 32 * kk + 4 * lg + e, s1i = s0i + 16;
-                    bDs[kk][e] = f16(U[2 * kk][e] * sm.dec[s0i]);
-                    bDs[kk][4 + e] = f16(U[2 * kk + 1][e] * sm.dec[s1i]);
-                    bDm[kk][e] = f16(DM[2 * kk][e] * sm.dec[s0i]);
-                    bDm[kk][4 + e] = f16(DM[2 * kk + 1][e] * sm.dec[s1i]);
+                    bDs[kk][e] = f16(U[2 * kk][e] * sm.dec[cb][s0i]);
+                    bDs[kk][4 + e] = f16(U[2 * kk + 1][e] * sm.dec[cb][s1i]);
+                    bDm[kk][e] = f16(DM[2 * kk][e] * sm.dec[cb][s0i]);
+                    bDm[kk][4 + e] = f16(DM[2 * kk + 1][e] * sm.dec[cb][s1i]);
                 }
-            const float GC = sm.Gam[C - 1] * sig, GM = sm.Gam[C - 1] * sigm;
+            const float GC = sm.Gam[cb][C - 1] * sig, GM = sm.Gam[cb][C - 1] * sigm;
 #pragma unroll
             for (int it = 0; it < F::NI; ++it) {
                 S[it] *= GC;
@@ -547,7 +576,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                 O[rt] = mma_k32(aq, bS[kk], O[rt]);
             }
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) O[rt][rr] *= sm.Gam[16 * rt + 4 * lg + rr];
+            for (int rr = 0; rr < 4; ++rr) O[rt][rr] *= sm.Gam[cb][16 * rt + 4 * lg + rr];
         }
         // Delta as fp16 B operands over the chunk index, plain and decayed to the chunk end
         f16x8 bD[F::KC], bDs[F::KC];
@@ -559,10 +588,12 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                 const float d0 = U[2 * kk][e], d1 = U[2 * kk + 1][e];
                 bD[kk][e] = f16(d0);
                 bD[kk][4 + e] = f16(d1);
-                bDs[kk][e] = f16(d0 * sm.dec[s0i]);
-                bDs[kk][4 + e] = f16(d1 * sm.dec[s1i]);
+                bDs[kk][e] = f16(d0 * sm.dec[cb][s0i]);
+                bDs[kk][4 + e] = f16(d1 * sm.dec[cb][s1i]);
             }
-        // O += P Delta, staged for the store at the top of the next chunk
+        // O += P Delta, staged in LDS for the coalesced store at the top of the next chunk
+        // (stored from the accumulators, 4-byte pieces of 4 rows per instruction, the call took
+        // 11% longer; stored in the next chunk from registers, 19%)
         const float oscale = scale * isig;  // exact: isig is a power of two
 #pragma unroll
         for (int rt = 0; rt < NR; ++rt) {
@@ -576,7 +607,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         }
         // S = e^gamma_last S + K^T diag(e^(gamma_last - gamma)) Delta, formed as
         // (sig e^gamma_last S + K^T diag(..) (sig Delta)) / sig: every scaling is exact
-        const float GC = sm.Gam[C - 1] * sig;
+        const float GC = sm.Gam[cb][C - 1] * sig;
 #pragma unroll
         for (int it = 0; it < F::NI; ++it) {
             S[it] *= GC;

@@ -98,16 +98,25 @@ const char *gdn_status_string(gdn_status_t status);
  * keeps per-chunk records there for a segment of chunks: at most 2 GiB of them (or the
  * number of bytes the environment variable GDN_SPLIT_RECORD_BYTES gives), plus 256 B and one
  * fp32 state per chain.  Longer sequences run segment after segment, with the state carried
- * between them and the same results bit for bit, so the size stays bounded for any T.
+ * between them and the same results bit for bit, so the size stays bounded for any T.  The
+ * "segmented" plan keeps three fp32 dk x dv matrices per (chain, segment) there: each
+ * segment's transition M and state N (all but the last segment) and its entry state; with at
+ * most 256 (chain, segment) units that is at most 48 MiB at dk = dv = 128, whatever T.
  */
 size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
                                     gdn_dtype_t in_dtype);
 
 /*
- * Which kernels gdn_chunk_fwd runs for these sizes: "split" (a prep kernel parallel over
- * chunks, whose per-chunk operands go through the workspace, then a state-scan kernel per
- * chain and 16-column state tile that also forms the outputs), "fused" (one kernel per
- * chain), "recurrent" (token by token; the fp32 path) or "invalid".  Static string.
+ * Which kernels gdn_chunk_fwd runs for these sizes: "fused" (one kernel per chain: 128 chains
+ * or more), "segmented" (fewer, long chains: every chain cut into segments of at least 8 chunks,
+ * at most 256 (chain, segment) units; a transition pass gives each segment's affine state map
+ * S_out = M S_in + N -- Eq. (1) is affine in the state -- a combine pass chains the maps into
+ * every segment's entry state in fp32, and the single-pass kernel then runs all segments from
+ * their entry states), "split" (fewer, shorter chains: a prep kernel parallel over chunks,
+ * whose per-chunk operands go through the workspace, then a state-scan kernel per chain and
+ * 16-column state tile that also forms the outputs), "recurrent" (token by token; the fp32
+ * path) or "invalid".  Packed sequences (gdn_chunk_fwd_varlen with offsets) never run
+ * "segmented": the host does not know their lengths.  Static string.
  */
 const char *gdn_chunk_fwd_plan(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
                                gdn_dtype_t in_dtype);
@@ -139,12 +148,13 @@ const char *gdn_chunk_fwd_plan(int B, int T, int Hk, int Hv, int dk, int dv, int
  * The value side (v, U, Delta, S, o) is linear in (v, initial_state), so its fp16 copies carry
  * a power of two, chosen per chunk and taken back out of the fp32 results exactly: v and the
  * state may have any magnitude that fp32 holds, and scaling v and initial_state by 2^n scales
- * o and final_state by exactly 2^n.  The single-pass plan takes the scale of each value column
- * from its largest magnitude in the chunk; the split plan takes one per 16 value columns from
- * a bound on the state's column norms that holds for keys of norm at most 1 (beta |k|^2 <= 2;
- * unit keys rounded to bf16 qualify), so keys far above unit norm may overflow there -- pass
- * GDN_QK_L2NORM (gdn_chunk_fwd_varlen) when the keys are not normalised.  fp32 inputs run the
- * token-recurrent kernel in fp32.
+ * o and final_state by exactly 2^n.  The single-pass and segmented plans take the scale of
+ * each value column (and of each column of a segment's transition M) from its largest
+ * magnitude in the chunk, and the segmented plan chains its segments in fp32; the split plan
+ * takes one scale per 16 value columns from a bound on the state's column norms that holds
+ * for keys of norm at most 1 (beta |k|^2 <= 2; unit keys rounded to bf16 qualify), so keys
+ * far above unit norm may overflow there -- pass GDN_QK_L2NORM (gdn_chunk_fwd_varlen) when the
+ * keys are not normalised.  fp32 inputs run the token-recurrent kernel in fp32.
  */
 gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v, const void *beta,
                            const void *g, const float *initial_state, void *o,
@@ -159,7 +169,8 @@ gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v, const vo
  * workspace (gdn_chunk_fwd_workspace_size(...) > 0) it uses a static scratch buffer of
  * GDN_NOALLOC_SCRATCH_BYTES that the library holds in every GPU's memory from its load until
  * the process ends; the call itself allocates nothing (no hipMalloc, no allocating library
- * routine).  The split plan then runs in segments of as many chunks as the scratch holds
+ * routine).  The segmented plan's maps and entry states always fit the scratch.  The split
+ * plan runs in segments of as many chunks as the scratch holds
  * (about 1,000 chunk-heads at dk = dv = 128 and chunk 64, e.g. 64 chunks of 16 heads): the
  * same results, bit for bit, at any T, and slower than one pass for long sequences.  A size
  * whose smallest workspace (one chunk per segment) exceeded GDN_NOALLOC_SCRATCH_BYTES would

@@ -38,6 +38,16 @@
 //     the state and the solve panels never leave registers.
 //   * O is staged in LDS and written with coalesced 16-byte stores at the top of the next
 //     chunk, before the next prefetch is issued (the vector-memory counter is in-order).
+//
+// Segmented plan (few, long chains).  The chunk maps above are affine in the state, so a
+// segment of chunks maps any entry state S_in to S_out = M S_in + N, with N its result from
+// the zero state and M = prod over its chunks of (e^gamma_last I - K^T dec W).  Every chain is
+// cut into nseg segments: the kernel in mode kTrans runs segments 0 .. nseg-2 in parallel and
+// returns (M, N) for each (segment 0's N starts from the initial state), seg_combine_kernel
+// chains them into every segment's entry state (fp32 matrix cores), and the kernel in mode
+// kOut then runs all segments in parallel from their entry states.  At most 256 (chain,
+// segment) units, one workgroup per compute unit: for 16 chains of 4,096 chunks, 16 segments
+// of 256 chunks per chain instead of one workgroup walking 4,096 chunks.
 #include <algorithm>
 #include <stdlib.h>
 

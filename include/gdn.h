@@ -115,8 +115,10 @@ size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv
  * their entry states), "split" (fewer, shorter chains: a prep kernel parallel over chunks,
  * whose per-chunk operands go through the workspace, then a state-scan kernel per chain and
  * 16-column state tile that also forms the outputs), "recurrent" (token by token; the fp32
- * path) or "invalid".  Packed sequences (gdn_chunk_fwd_varlen with offsets) never run
- * "segmented": the host does not know their lengths.  Static string.
+ * path) or "invalid".  Packed sequences (gdn_chunk_fwd_varlen with offsets) run "segmented"
+ * with every (sequence, head) chain in 256 / chains segments formed on the device from its own
+ * length, when the mean sequence (T / num_seqs, since the host does not read the offsets)
+ * gives segments of at least 8 chunks; GDN_PREFER_SPLIT keeps the split plan.  Static string.
  */
 const char *gdn_chunk_fwd_plan(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
                                gdn_dtype_t in_dtype);

@@ -187,8 +187,11 @@ template <> __device__ __forceinline__ void store4<bf16_t>(bf16_t *p, f32x4 x) {
 // S_out = M S_in + N for any state S_in entering it (Eq. (1) is affine in the state).
 enum { kOut = 0, kTrans = 1 };
 
-// Units: blocks [p nchains, (p + 1) nchains) run segment p (chunks p seg_chunks .. of every
-// chain; one segment with seg_chunks >= the chunk count is the whole sequence).  kOut reads
+// Units: blocks [p nchains, (p + 1) nchains) run segment p (chunks p L .. p L + L - 1 of every
+// chain, L = seg_chunks; seg_chunks = 0: L = ceil(chunks / nseg) from each chain's own length,
+// for packed sequences, whose lengths only the device knows; a segment past a chain's end is
+// empty: its transition is the identity; one segment with L >= the chunk count is the whole
+// sequence).  kOut reads
 // its initial state at s0 + p s0_seg_stride + chain D^2 and writes the final state on the last
 // segment only; kTrans writes M, N of (segment p, chain) to mn + (p nchains + chain) 2 D^2.
 template <int D, int C, typename TO, int MODE>
@@ -218,9 +221,10 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     {
         int len0;
         seq_range(cu, T, b, base, len0);
-        const long start = static_cast<long>(seg) * seg_chunks * C;
-        len = static_cast<int>(max(0L, min(static_cast<long>(len0) - start,
-                                           static_cast<long>(seg_chunks) * C)));
+        const long nch0 = (static_cast<long>(len0) + C - 1) / C;
+        const long L = seg_chunks > 0 ? seg_chunks : (nch0 + nseg - 1) / nseg;
+        const long start = static_cast<long>(seg) * L * C;
+        len = static_cast<int>(max(0L, min(static_cast<long>(len0) - start, L * C)));
         base += static_cast<size_t>(min(start, static_cast<long>(len0)));
     }
 
@@ -825,9 +829,14 @@ bool chunk_mfma_supports(const PrefillArgs &a) {
 
 SegGeom seg_geometry(const PrefillArgs &a) {
     SegGeom g{1, 1 << 30};
-    if (!a.seg || a.cu != nullptr || a.B <= 0 || a.T <= 0) return g;
+    if (!a.seg || a.B <= 0 || a.T <= 0) return g;
     const long nch = (static_cast<long>(a.T) + a.chunk - 1) / a.chunk;
     const long chains = static_cast<long>(a.B) * a.Hv;
+    if (a.cu != nullptr) {  // packed: every chain in the same number of segments, each chain's
+        g.nseg = static_cast<int>(std::max(1L, kSegTargetUnits / chains));  // own length
+        g.seg_chunks = 0;                                                  // on the device
+        return g;
+    }
     long len = 0;  // chunks per segment
     const char *env = getenv("GDN_SEG_CHUNKS");
     if (env != nullptr && atol(env) > 0) {

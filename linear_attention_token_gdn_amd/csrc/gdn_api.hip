@@ -34,26 +34,32 @@ bool overlap(const void *p, size_t n, const void *r, size_t m) {
 // measurements (a variant that does not support the sizes falls back to the default choice).
 enum class Variant { Recurrent, Fused, Split, Segmented };
 
-// Below this many (b, hv) chains the single-pass kernel leaves most compute units idle; chains
-// are then cut into segments run in parallel (dense inputs), or the two-kernel form (parallel
-// over chunks) is used (packed sequences, whose lengths the host does not know).
+// Below this many (b, hv) chains the single-pass kernel leaves most compute units idle; long
+// chains are then cut into segments run in parallel, shorter ones take the two-kernel form
+// (parallel over chunks).
 constexpr long kSplitBelowChains = 128;
 
 bool segmented_supported(const gdn::PrefillArgs &a) {
-    if (!gdn::chunk_mfma_supports(a) || a.cu != nullptr) return false;
+    if (!gdn::chunk_mfma_supports(a)) return false;
     gdn::PrefillArgs s = a;
     s.seg = true;
     return gdn::seg_geometry(s).nseg > 1;
 }
 
 // The default choice for few chains: segments of at least kSegMinChunks chunks (or a length
-// pinned by GDN_SEG_CHUNKS).
+// pinned by GDN_SEG_CHUNKS).  Packed sequences: judged on the mean length, T / num_seqs (the
+// host does not read the offsets).
 bool segmented_preferred(const gdn::PrefillArgs &a) {
     if (!segmented_supported(a)) return false;
     gdn::PrefillArgs s = a;
     s.seg = true;
+    const gdn::SegGeom sg = gdn::seg_geometry(s);
+    if (a.cu != nullptr) {
+        const long mean_chunks = static_cast<long>(a.T) / a.B / a.chunk;
+        return mean_chunks >= gdn::kSegMinChunks * sg.nseg;
+    }
     const char *env = getenv("GDN_SEG_CHUNKS");
-    return (env != nullptr && atol(env) > 0) || gdn::seg_geometry(s).seg_chunks >= gdn::kSegMinChunks;
+    return (env != nullptr && atol(env) > 0) || sg.seg_chunks >= gdn::kSegMinChunks;
 }
 
 Variant choose_variant(const gdn::PrefillArgs &a) {

@@ -82,9 +82,10 @@ hipError_t launch_qsa(const QsaArgs &a);
 hipError_t launch_recurrent(const PrefillArgs &a);
 
 // Chunk-parallel MFMA kernel for bf16 inputs.  supports() says whether the sizes are handled.
-// With a.seg (dense inputs), the segmented plan: every chain is cut into nseg segments of
-// seg_chunks chunks, run in parallel -- a transition pass (each segment's affine map of the
-// state), a sequential combine of those maps into every segment's entry state, then the
+// With a.seg, the segmented plan: every chain is cut into nseg segments of seg_chunks chunks
+// (packed sequences: seg_chunks = 0, each chain's segments of ceil(its chunks / nseg) chunks,
+// formed on the device), run in parallel -- a transition pass (each segment's affine map of
+// the state), a sequential combine of those maps into every segment's entry state, then the
 // single-pass kernel over all segments.  Its workspace holds the maps and the entry states.
 struct SegGeom {
     int nseg, seg_chunks;

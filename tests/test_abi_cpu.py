@@ -70,6 +70,20 @@ def test_workspace_of_the_segmented_plan(lib, monkeypatch):
     assert gdn.gdn_chunk_fwd_plan(1, 64, 2, 2, 64, 64, 64, gdn.GDN_BF16) == "split"
 
 
+def test_workspace_of_the_segmented_plan_packed(lib):
+    # packed sequences: 256 / chains segments per chain whatever their lengths (formed on the
+    # device); the plan is taken when the mean sequence has >= 8 chunks per segment
+    ws = gdn.gdn_chunk_fwd_varlen_workspace_size
+    D2 = 128 * 128 * 4
+    assert ws(2, 2 * 16384, 4, 4, 128, 128, 64, gdn.GDN_BF16, 1) == (2 * 31 + 32) * 8 * D2
+    assert ws(1, 262144, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1) == (2 * 15 + 16) * 16 * D2
+    # short on average: the split plan's records (one 72 KiB + 128 B record per chunk slot)
+    short = ws(8, 8 * 512, 4, 4, 128, 128, 64, gdn.GDN_BF16, 1)
+    assert short != (2 * 7 + 8) * 32 * D2 and short >= 4 * (4096 // 64 + 8) * (73728 + 128)
+    # the plan hint keeps the split plan
+    assert ws(1, 262144, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1, gdn.GDN_PREFER_SPLIT) > 1 << 30
+
+
 def test_workspace_size_of_the_chunk_kernels(lib):
     # few chains: the prep + scan form needs a workspace; one float32 path needs none
     assert gdn.gdn_chunk_fwd_workspace_size(1, 4096, 16, 16, 128, 128, 64, gdn.GDN_BF16) > 16 * 64 * 65536

@@ -149,3 +149,67 @@ def test_deterministic(monkeypatch):
     b = _run(inp)
     np.testing.assert_array_equal(a[0], b[0])
     np.testing.assert_array_equal(a[1], b[1])
+
+
+def _packed_inputs(lens, Hk, Hv, d, seed, flags):
+    rng = np.random.default_rng(seed)
+    T = int(sum(lens))
+    q = rng.standard_normal((T, Hk, d))
+    k = rng.standard_normal((T, Hk, d))
+    if not flags:
+        q /= np.linalg.norm(q, axis=-1, keepdims=True)
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, Hv, d))
+    bl = rng.standard_normal((T, Hv))
+    beta = bl if flags else 1 / (1 + np.exp(-bl))
+    al = rng.uniform(5.0, 9.0, (T, Hv))  # gates close to 1: the transitions matter
+    g = al if flags else -np.log1p(np.exp(-al))
+    from gdn_inputs import round_to
+    x = {n: round_to(a, "bf16") for n, a in (("q", q), ("k", k), ("v", v), ("beta", beta),
+                                            ("g", g))}
+    s0 = (rng.standard_normal((len(lens), Hv, d, d)) * 0.5).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    return x, s0, cu
+
+
+@pytest.mark.parametrize("flags", [0, 1 | 2 | 4])
+def test_packed_sequences(flags, monkeypatch):
+    """Packed sequences through the segmented plan: every (sequence, head) chain in the same
+    number of segments, each of ceil(its chunks / segments) chunks formed on the device --
+    long and short sequences, a one-token and an empty one (final state = initial state, every
+    segment empty)."""
+    import linear_attention_token_gdn_amd as gdn
+    monkeypatch.setenv("GDN_FORCE_VARIANT", "segmented")
+    lens = [1500, 0, 1, 700, 65, 2300]
+    x, s0, cu = _packed_inputs(lens, 1, 2, 128, seed=1700 + flags, flags=flags)
+    t = {n: torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(torch.bfloat16)
+         for n, a in x.items()}
+    cu_t = torch.from_numpy(cu.astype(np.int32)).to(DEV)
+    o, sT = gdn.chunk_fwd_varlen(t["q"], t["k"], t["v"], t["beta"], t["g"], cu_seqlens=cu_t,
+                                 initial_state=torch.from_numpy(s0).to(DEV), flags=flags)
+    torch.cuda.synchronize()
+    o, sT = o.double().cpu().numpy(), sT.double().cpu().numpy()
+    np.testing.assert_array_equal(sT[1], s0[1])  # the empty sequence
+    ro, rS = oracle.run_packed(x["q"], x["k"], x["v"], x["beta"], x["g"], cu, s0=s0,
+                               flags=flags)
+    check(o, ro, "bf16", "packed segmented o")
+    check(sT, rS, "bf16", "packed segmented state")
+
+
+def test_packed_default_plan_long_sequences():
+    """Few long packed sequences take the segmented plan by default (judged on the mean
+    length); the workspace query agrees with the dense call of the same sizes' plan."""
+    import linear_attention_token_gdn_amd as gdn
+    N, T, H = 2, 2 * 16384, 4  # 8 chains: 32 segments of 8 chunks per chain
+    wsz = gdn.gdn_chunk_fwd_varlen_workspace_size(N, T, H, H, 128, 128, 64, gdn.GDN_BF16, 1, 0)
+    assert wsz == (2 * 31 + 32) * N * H * 128 * 128 * 4
+    x, s0, cu = _packed_inputs([16384, 16384], H, H, 128, seed=1800, flags=0)
+    t = {n: torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(torch.bfloat16)
+         for n, a in x.items()}
+    cu_t = torch.from_numpy(cu.astype(np.int32)).to(DEV)
+    o, sT = gdn.chunk_fwd_varlen(t["q"], t["k"], t["v"], t["beta"], t["g"], cu_seqlens=cu_t,
+                                 initial_state=torch.from_numpy(s0).to(DEV))
+    torch.cuda.synchronize()
+    ro, rS = oracle.run_packed(x["q"], x["k"], x["v"], x["beta"], x["g"], cu, s0=s0)
+    check(o.double().cpu().numpy(), ro, "bf16", "packed default o")
+    check(sT.double().cpu().numpy(), rS, "bf16", "packed default state")

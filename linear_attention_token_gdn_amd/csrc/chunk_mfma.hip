@@ -50,6 +50,7 @@
 // of 256 chunks per chain instead of one workgroup walking 4,096 chunks.
 #include <algorithm>
 #include <stdlib.h>
+#include <type_traits>
 
 #include "gdn_internal.h"
 
@@ -98,6 +99,33 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
 __device__ __forceinline__ int opaque(int x) {
     asm volatile("" : "+v"(x));
     return x;
+}
+
+// Power-of-two exponents for the fp16 copies of a value column (pow2_scale's rule as an
+// exponent: m 2^e in [2^8, 2^9), e = 0 for m = 0, Inf or NaN, |e| <= 100).  A column carried at
+// 2^e keeps e while its largest magnitude m stays in [2^6, 2^9) at that scale: the upper end
+// keeps the fp16 operands as far from overflow as a fresh choice would, the lower end lets m
+// drift by 8x before the fp32 state has to be rescaled (fp16's relative precision is the same
+// over its normal range).
+__device__ __forceinline__ int pow2_exponent(float m) {
+    const int eb = static_cast<int>((__float_as_uint(m) >> 23) & 0xffu);
+    const int ok = static_cast<int>(static_cast<unsigned>(eb - 1) < 254u);
+    return ok * min(max(135 - eb, -100), 100);
+}
+__device__ __forceinline__ int next_exponent(float m, int e) {
+    const float ms = __builtin_amdgcn_ldexpf(m, e);
+    return (ms >= 64.f && ms < 512.f) ? e : pow2_exponent(m);
+}
+__device__ __forceinline__ float exp2i(int e) {  // 2^e for |e| <= 126
+    return __uint_as_float(static_cast<uint32_t>(127 + e) << 23);
+}
+// x 2^de for every lane; skipped when no lane of the wavefront changes its exponent
+template <int N> __device__ __forceinline__ void rescale(f32x4 (&x)[N], int de) {
+    if (__builtin_amdgcn_ballot_w64(de != 0) == 0) return;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[i][r] = __builtin_amdgcn_ldexpf(x[i][r], de);
 }
 
 // Workgroup barrier that waits only for this wave's LDS traffic.  __syncthreads() also waits
@@ -160,6 +188,7 @@ template <int D, int C> struct Smem {
     float Gam[2][C];          // exp(gamma)
     float dec[2][C];          // exp(gamma_last - gamma)
     float bet[2][C];          // beta
+    float bg[2][C];           // beta exp(gamma)
     float ost[C][F::PO];      // scaled output of the chunk, waiting to be stored
 };
 
@@ -228,8 +257,10 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         base += static_cast<size_t>(min(start, static_cast<long>(len0)));
     }
 
-    // ---- the state: tile it holds rows 16it + 4lg + r of column `col`
+    // ---- the state: tile it holds rows 16it + 4lg + r of column `col`, carried as 2^es S (es
+    //      per column, a power of two chosen as described at next_exponent; 0 at the start)
     f32x4 S[F::NI];
+    int es = 0;
     const size_t sbase = static_cast<size_t>(chain) * D * D;
     const float *sin = s0 == nullptr ? nullptr
                        : TRANS       ? (seg == 0 ? s0 + sbase : nullptr)
@@ -244,8 +275,9 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
         for (int it = 0; it < F::NI; ++it) S[it] = zero4();
     }
-    // kTrans: the transition M, tiles as S, from the identity
+    // kTrans: the transition M, tiles as S, from the identity, carried as 2^em M
     f32x4 M[TRANS ? F::NI : 1];
+    int em = 0;
     if constexpr (TRANS) {
 #pragma unroll
         for (int it = 0; it < F::NI; ++it)
@@ -289,10 +321,12 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         const float glast = __builtin_bit_cast(
             float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gv), C - 1));
         if (lane < C) {
+            const float eg = __expf(gv), bt = lane < L ? beta_from_input(bf16_to_f32(pb), flags) : 0.f;
             sm.gam[gb][lane] = gv;
-            sm.Gam[gb][lane] = __expf(gv);
+            sm.Gam[gb][lane] = eg;
             sm.dec[gb][lane] = __expf(glast - gv);
-            sm.bet[gb][lane] = lane < L ? beta_from_input(bf16_to_f32(pb), flags) : 0.f;
+            sm.bet[gb][lane] = bt;
+            sm.bg[gb][lane] = bt * eg;
         }
     };
 
@@ -306,42 +340,55 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         lds_barrier();  // the previous chunk is done with every LDS buffer
 
         // ---- stage 0: stage this chunk in LDS, store the previous chunk's output, prefetch
+        // (q and k rows scaled by 1 / their norm with GDN_QK_L2NORM, else converted as they are:
+        //  two copies of the conversion, so that the common case carries no unit multiply)
+        auto stage_rows = [&](auto l2n) {
 #pragma unroll
-        for (int n = 0; n < F::NQ; ++n) {
-            const int idx = tid + n * NT, r = idx / (D / 8), cc = idx - r * (D / 8);
-            float qs = 1.f, ks = 1.f;  // L2 normalisation: the D/8 consecutive lanes of a row
-            if (flags & GDN_QK_L2NORM) {
-                float qq = 0.f, kq = 0.f;
+            for (int n = 0; n < F::NQ; ++n) {
+                const int idx = tid + n * NT, r = idx / (D / 8), cc = idx - r * (D / 8);
+                f16x8 qh, kh;
+                if constexpr (decltype(l2n)::value) {
+                    // L2 normalisation: the D/8 consecutive lanes of a row
+                    float qq = 0.f, kq = 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float a = bf16_to_f32(pq[n][e]), c2 = bf16_to_f32(pk[n][e]);
-                    qq += a * a;
-                    kq += c2 * c2;
+                    for (int e = 0; e < 8; ++e) {
+                        const float a = bf16_to_f32(pq[n][e]), c2 = bf16_to_f32(pk[n][e]);
+                        qq += a * a;
+                        kq += c2 * c2;
+                    }
+#pragma unroll
+                    for (int off = 1; off < D / 8; off <<= 1) {
+                        qq += __shfl_xor(qq, off);
+                        kq += __shfl_xor(kq, off);
+                    }
+                    const float qs = inv_norm_from_sumsq(qq), ks = inv_norm_from_sumsq(kq);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        qh[e] = f16(qs * bf16_to_f32(pq[n][e]));
+                        kh[e] = f16(ks * bf16_to_f32(pk[n][e]));
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        qh[e] = f16(bf16_to_f32(pq[n][e]));
+                        kh[e] = f16(bf16_to_f32(pk[n][e]));
+                    }
                 }
-#pragma unroll
-                for (int off = 1; off < D / 8; off <<= 1) {
-                    qq += __shfl_xor(qq, off);
-                    kq += __shfl_xor(kq, off);
+                // columns 8cc .. 8cc+7 are two runs of 4 in the permuted order
+                const int c0 = kperm(cc * 8), c1 = kperm(cc * 8 + 4);
+                if constexpr (!TRANS) {
+                    *reinterpret_cast<f16x4 *>(&sm.q[r][c0]) = f16x4{qh[0], qh[1], qh[2], qh[3]};
+                    *reinterpret_cast<f16x4 *>(&sm.q[r][c1]) = f16x4{qh[4], qh[5], qh[6], qh[7]};
                 }
-                qs = inv_norm_from_sumsq(qq);
-                ks = inv_norm_from_sumsq(kq);
+                *reinterpret_cast<f16x4 *>(&sm.k[r][c0]) = f16x4{kh[0], kh[1], kh[2], kh[3]};
+                *reinterpret_cast<f16x4 *>(&sm.k[r][c1]) = f16x4{kh[4], kh[5], kh[6], kh[7]};
+                *reinterpret_cast<u16x8 *>(&sm.v[r][cc * 8]) = pv[n];
             }
-            f16x8 qh, kh;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                qh[e] = f16(qs * bf16_to_f32(pq[n][e]));
-                kh[e] = f16(ks * bf16_to_f32(pk[n][e]));
-            }
-            // columns 8cc .. 8cc+7 are two runs of 4 in the permuted order
-            const int c0 = kperm(cc * 8), c1 = kperm(cc * 8 + 4);
-            if constexpr (!TRANS) {
-                *reinterpret_cast<f16x4 *>(&sm.q[r][c0]) = f16x4{qh[0], qh[1], qh[2], qh[3]};
-                *reinterpret_cast<f16x4 *>(&sm.q[r][c1]) = f16x4{qh[4], qh[5], qh[6], qh[7]};
-            }
-            *reinterpret_cast<f16x4 *>(&sm.k[r][c0]) = f16x4{kh[0], kh[1], kh[2], kh[3]};
-            *reinterpret_cast<f16x4 *>(&sm.k[r][c1]) = f16x4{kh[4], kh[5], kh[6], kh[7]};
-            *reinterpret_cast<u16x8 *>(&sm.v[r][cc * 8]) = pv[n];
-        }
+        };
+        if (flags & GDN_QK_L2NORM)
+            stage_rows(std::true_type{});
+        else
+            stage_rows(std::false_type{});
         if (!TRANS && c > 0) {
             const int tp = t0 - C;  // the previous chunk is always a full one
 #pragma unroll
@@ -458,8 +505,8 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         // ---- stage 3: blocked forward substitution for this wave's panels,
         //      U[:, 16w..] = (I+A)^-1 diag(beta) V[:, 16w..]  (kept in registers)
         //      W[:, 16w..] = (I+A)^-1 diag(beta e^gamma) K[:, 16w..]  (-W to LDS)
-        //      The value side of this column (U, Delta, S, O) is carried scaled by sig, a power
-        //      of two chosen from the column's largest |beta v| in the chunk and |S| at its start.
+        //      The value side of this column (U, Delta, S, O) is carried scaled by sig = 2^es, from
+        //      the column's largest |beta v| in the chunk and |S| at its start (next_exponent).
         f32x4 yv[NR];
         float vmax = 0.f;
 #pragma unroll
@@ -470,21 +517,29 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                 yv[a][rr] = sm.bet[cb][r] * bf16_to_f32(sm.v[r][col]);
                 vmax = fmaxf(vmax, fabsf(yv[a][rr]));
             }
+        {
+            float smax = 0.f;
 #pragma unroll
-        for (int it = 0; it < F::NI; ++it)
+            for (int it = 0; it < F::NI; ++it)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) vmax = fmaxf(vmax, fabsf(S[it][r]));
-        vmax = max_over_rows(vmax);  // the column's four lanes
-        float sig, isig;
-        pow2_scale(vmax, sig, isig);
-        float sigm = 1.f, isigm = 1.f;  // kTrans: the same for the column of M
-        if constexpr (TRANS) {
+                for (int r = 0; r < 4; ++r) smax = fmaxf(smax, fabsf(S[it][r]));
+            // the column's four lanes; |S| = 2^-es |carried S|
+            vmax = max_over_rows(fmaxf(vmax, __builtin_amdgcn_ldexpf(smax, -es)));
+            const int en = next_exponent(vmax, es);
+            rescale(S, en - es);
+            es = en;
+        }
+        const float sig = exp2i(es), isig = exp2i(-es);
+        if constexpr (TRANS) {  // the same for the columns of M
             float mmax = 0.f;
 #pragma unroll
             for (int it = 0; it < F::NI; ++it)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) mmax = fmaxf(mmax, fabsf(M[it][r]));
-            pow2_scale(max_over_rows(mmax), sigm, isigm);
+            const float m = max_over_rows(__builtin_amdgcn_ldexpf(mmax, -em));
+            const int en = next_exponent(m, em);
+            rescale(M, en - em);
+            em = en;
         }
         f32x4 U[NR], Wp[NR];
 #pragma unroll
@@ -495,7 +550,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             for (int rr = 0; rr < 4; ++rr) {
                 const int r = 16 * a + 4 * lg + rr;
                 yu[rr] = sig * yv[a][rr];
-                yw[rr] = sm.bet[cb][r] * sm.Gam[cb][r] * float(kv4[rr]);
+                yw[rr] = sm.bg[cb][r] * float(kv4[rr]);
             }
 #pragma unroll
             for (int cb = 0; cb < a; ++cb) {
@@ -526,10 +581,10 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                 f16x8 bS, bM;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    bS[e] = f16(sig * S[2 * kk][e]);
-                    bS[4 + e] = f16(sig * S[2 * kk + 1][e]);
-                    bM[e] = f16(sigm * M[2 * kk][e]);
-                    bM[4 + e] = f16(sigm * M[2 * kk + 1][e]);
+                    bS[e] = f16(S[2 * kk][e]);
+                    bS[4 + e] = f16(S[2 * kk + 1][e]);
+                    bM[e] = f16(M[2 * kk][e]);
+                    bM[4 + e] = f16(M[2 * kk + 1][e]);
                 }
 #pragma unroll
                 for (int rt = 0; rt < NR; ++rt) {
@@ -549,24 +604,22 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                     bDm[kk][e] = f16(DM[2 * kk][e] * sm.dec[cb][s0i]);
                     bDm[kk][4 + e] = f16(DM[2 * kk + 1][e] * sm.dec[cb][s1i]);
                 }
-            const float GC = sm.Gam[cb][C - 1] * sig, GM = sm.Gam[cb][C - 1] * sigm;
+            const float GC = sm.Gam[cb][C - 1];
 #pragma unroll
             for (int it = 0; it < F::NI; ++it) {
                 S[it] *= GC;
-                M[it] *= GM;
+                M[it] *= GC;
 #pragma unroll
                 for (int kk = 0; kk < F::KC; ++kk) {
                     const f16x8 ak = *reinterpret_cast<const f16x8 *>(&sm.kt[16 * it + li][32 * kk + 8 * lg]);
                     S[it] = mma_k32(ak, bDs[kk], S[it]);
                     M[it] = mma_k32(ak, bDm[kk], M[it]);
                 }
-                S[it] *= isig;
-                M[it] *= isigm;
             }
             continue;
         }
 
-        // ---- stage 4 (sequential part): Delta, O, next state -- U, Delta, O scaled by sig
+        // ---- stage 4 (sequential part): Delta, O, next state -- U, Delta, O, S scaled by sig
         // sig S as fp16 B operands over the key index: slot e < 4 -> tile 2kk row 4lg+e,
         // slot e >= 4 -> tile 2kk+1 row 4lg+e-4.  A operands read the matching k indices.
         f16x8 bS[F::KD];
@@ -574,8 +627,8 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         for (int kk = 0; kk < F::KD; ++kk)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                bS[kk][e] = f16(sig * S[2 * kk][e]);
-                bS[kk][4 + e] = f16(sig * S[2 * kk + 1][e]);
+                bS[kk][e] = f16(S[2 * kk][e]);
+                bS[kk][4 + e] = f16(S[2 * kk + 1][e]);
             }
         // Delta = U + (-W) S   (accumulated onto U);  O = diag(e^gamma) Q S
         f32x4 O[NR];
@@ -619,9 +672,9 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) sm.ost[16 * rt + 4 * lg + rr][col] = oscale * O[rt][rr];
         }
-        // S = e^gamma_last S + K^T diag(e^(gamma_last - gamma)) Delta, formed as
-        // (sig e^gamma_last S + K^T diag(..) (sig Delta)) / sig: every scaling is exact
-        const float GC = sm.Gam[cb][C - 1] * sig;
+        // S = e^gamma_last S + K^T diag(e^(gamma_last - gamma)) Delta, all carried scaled by
+        // sig: sig S_next = e^gamma_last (sig S) + K^T diag(..) (sig Delta)
+        const float GC = sm.Gam[cb][C - 1];
 #pragma unroll
         for (int it = 0; it < F::NI; ++it) {
             S[it] *= GC;
@@ -629,7 +682,6 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             for (int kk = 0; kk < F::KC; ++kk)
                 S[it] = mma_k32(*reinterpret_cast<const f16x8 *>(&sm.kt[16 * it + li][32 * kk + 8 * lg]),
                                 bDs[kk], S[it]);
-            S[it] *= isig;
         }
     }
 
@@ -641,8 +693,8 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const size_t e = static_cast<size_t>(16 * it + 4 * lgo + r) * D + colo;
-                pm[e] = M[it][r];
-                pm[D * D + e] = S[it][r];
+                pm[e] = __builtin_amdgcn_ldexpf(M[it][r], -em);
+                pm[D * D + e] = __builtin_amdgcn_ldexpf(S[it][r], -es);
             }
         return;
     }
@@ -664,7 +716,8 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         for (int it = 0; it < F::NI; ++it)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                sT[sbase + static_cast<size_t>(16 * it + 4 * lg + r) * D + col] = S[it][r];
+                sT[sbase + static_cast<size_t>(16 * it + 4 * lg + r) * D + col] =
+                    __builtin_amdgcn_ldexpf(S[it][r], -es);
     }
 }
 

@@ -285,23 +285,36 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             for (int r = 0; r < 4; ++r) M[it][r] = (16 * it + 4 * lg + r == col) ? 1.f : 0.f;
     }
 
-    // ---- raw inputs of the next chunk, prefetched into registers (rows past the end read as 0)
+    // ---- raw inputs of coming chunks, prefetched into registers (rows past the end read as 0):
+    //      q one chunk ahead; k, v and the gate inputs two chunks ahead in kOut (staged in LDS a
+    //      chunk earlier than q, see stage 4), one in kTrans (staged in stage 0: its two states
+    //      leave no registers to stage them during stage 4)
     u16x8 pq[F::NQ], pk[F::NQ], pv[F::NQ];
     bf16_t pg = 0, pb = 0;
-    auto prefetch = [&](int cidx) {
+    auto prefetch_q = [&](int cidx) {
+        if constexpr (!TRANS) {
+            const int tt = cidx * C, L = min(C, len - tt);
+#pragma unroll
+            for (int n = 0; n < F::NQ; ++n) {
+                const int idx = tid + n * NT, r = idx / (D / 8), cc = idx - r * (D / 8);
+                pq[n] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+                if (r < L)
+                    pq[n] = *reinterpret_cast<const u16x8 *>(
+                        q + ((base + tt + r) * Hk + hq) * D + cc * 8);
+            }
+        }
+    };
+    auto prefetch_kv = [&](int cidx) {
         const int tt = cidx * C, L = min(C, len - tt);
 #pragma unroll
         for (int n = 0; n < F::NQ; ++n) {
             const int idx = tid + n * NT, r = idx / (D / 8), cc = idx - r * (D / 8);
-            pq[n] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            pk[n] = pq[n];
-            pv[n] = pq[n];
+            pk[n] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            pv[n] = pk[n];
             if (r < L) {
                 const size_t row = base + tt + r;
-                const size_t oq = (row * Hk + hq) * D + cc * 8, ov = (row * Hv + hv) * D + cc * 8;
-                if constexpr (!TRANS) pq[n] = *reinterpret_cast<const u16x8 *>(q + oq);
-                pk[n] = *reinterpret_cast<const u16x8 *>(k + oq);
-                pv[n] = *reinterpret_cast<const u16x8 *>(v + ov);
+                pk[n] = *reinterpret_cast<const u16x8 *>(k + (row * Hk + hq) * D + cc * 8);
+                pv[n] = *reinterpret_cast<const u16x8 *>(v + (row * Hv + hv) * D + cc * 8);
             }
         }
         pg = 0;
@@ -311,6 +324,56 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             pg = g[gi];
             pb = beta[gi];
         }
+    };
+    // One 8-column piece of a q or k row as fp16: scaled by 1 / the row's norm with
+    // GDN_QK_L2NORM (the D/8 consecutive lanes holding the row reduce its sum of squares), else
+    // converted as it is.  Two copies of each staging loop (l2n), so that the common case
+    // carries no unit multiply.
+    auto half_row = [&](const u16x8 &x, auto l2n) {
+        f16x8 h;
+        if constexpr (decltype(l2n)::value) {
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float a = bf16_to_f32(x[e]);
+                ss += a * a;
+            }
+#pragma unroll
+            for (int off = 1; off < D / 8; off <<= 1) ss += __shfl_xor(ss, off);
+            const float sc = inv_norm_from_sumsq(ss);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[e] = f16(sc * bf16_to_f32(x[e]));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[e] = f16(bf16_to_f32(x[e]));
+        }
+        return h;
+    };
+    // columns 8cc .. 8cc+7 of a q or k row are two runs of 4 in the permuted order
+    auto put_row = [&](f16 (*dst)[F::PQ], int r, int cc, f16x8 h) {
+        *reinterpret_cast<f16x4 *>(&dst[r][kperm(cc * 8)]) = f16x4{h[0], h[1], h[2], h[3]};
+        *reinterpret_cast<f16x4 *>(&dst[r][kperm(cc * 8 + 4)]) = f16x4{h[4], h[5], h[6], h[7]};
+    };
+    auto put_q = [&](auto l2n) {
+#pragma unroll
+        for (int n = 0; n < F::NQ; ++n) {
+            const int idx = tid + n * NT, r = idx / (D / 8), cc = idx - r * (D / 8);
+            put_row(sm.q, r, cc, half_row(pq[n], l2n));
+        }
+    };
+    auto put_kv = [&](auto l2n) {
+#pragma unroll
+        for (int n = 0; n < F::NQ; ++n) {
+            const int idx = tid + n * NT, r = idx / (D / 8), cc = idx - r * (D / 8);
+            put_row(sm.k, r, cc, half_row(pk[n], l2n));
+            *reinterpret_cast<u16x8 *>(&sm.v[r][cc * 8]) = pv[n];
+        }
+    };
+    auto with_norm = [&](auto &&f) {
+        if (flags & GDN_QK_L2NORM)
+            f(std::true_type{});
+        else
+            f(std::false_type{});
     };
     // wavefront 1: the gates of chunk cidx into buffer cidx & 1, from pg, pb (rows past the end:
     // g = beta = 0)
@@ -332,74 +395,36 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 
     const int nchunks = (len + C - 1) / C;
     if (nchunks > 0) {
-        prefetch(0);
+        prefetch_q(0);
+        prefetch_kv(0);
+        if constexpr (!TRANS) with_norm(put_kv);  // chunk 0's k and v (LDS is not in use yet)
         if (wave == 1) gates(0);
+        if constexpr (!TRANS) prefetch_kv(1);
     }
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = c * C, cb = c & 1;
         lds_barrier();  // the previous chunk is done with every LDS buffer
-
-        // ---- stage 0: stage this chunk in LDS, store the previous chunk's output, prefetch
-        // (q and k rows scaled by 1 / their norm with GDN_QK_L2NORM, else converted as they are:
-        //  two copies of the conversion, so that the common case carries no unit multiply)
-        auto stage_rows = [&](auto l2n) {
+        if constexpr (TRANS) {
+            // ---- stage 0 of the transition: this chunk's k and v in LDS, prefetch of the next
+            with_norm(put_kv);
+            if (c + 1 < nchunks) prefetch_kv(c + 1);
+            lds_barrier();
+        } else {
+            // ---- stage 0: stage this chunk's q in LDS, store the previous chunk's output, prefetch
+            //      the next q (this chunk's k and v were staged during the previous chunk)
+            with_norm(put_q);
+            if (c > 0) {
+                const int tp = t0 - C;  // the previous chunk is always a full one
 #pragma unroll
-            for (int n = 0; n < F::NQ; ++n) {
-                const int idx = tid + n * NT, r = idx / (D / 8), cc = idx - r * (D / 8);
-                f16x8 qh, kh;
-                if constexpr (decltype(l2n)::value) {
-                    // L2 normalisation: the D/8 consecutive lanes of a row
-                    float qq = 0.f, kq = 0.f;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float a = bf16_to_f32(pq[n][e]), c2 = bf16_to_f32(pk[n][e]);
-                        qq += a * a;
-                        kq += c2 * c2;
-                    }
-#pragma unroll
-                    for (int off = 1; off < D / 8; off <<= 1) {
-                        qq += __shfl_xor(qq, off);
-                        kq += __shfl_xor(kq, off);
-                    }
-                    const float qs = inv_norm_from_sumsq(qq), ks = inv_norm_from_sumsq(kq);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        qh[e] = f16(qs * bf16_to_f32(pq[n][e]));
-                        kh[e] = f16(ks * bf16_to_f32(pk[n][e]));
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        qh[e] = f16(bf16_to_f32(pq[n][e]));
-                        kh[e] = f16(bf16_to_f32(pk[n][e]));
-                    }
+                for (int n = 0; n < F::NO; ++n) {
+                    const int idx = tid + n * NT, r = idx / (D / 4), cc = idx - r * (D / 4);
+                    const f32x4 x = *reinterpret_cast<const f32x4 *>(&sm.ost[r][cc * 4]);
+                    store4<TO>(o + ((base + tp + r) * Hv + hv) * D + cc * 4, x);
                 }
-                // columns 8cc .. 8cc+7 are two runs of 4 in the permuted order
-                const int c0 = kperm(cc * 8), c1 = kperm(cc * 8 + 4);
-                if constexpr (!TRANS) {
-                    *reinterpret_cast<f16x4 *>(&sm.q[r][c0]) = f16x4{qh[0], qh[1], qh[2], qh[3]};
-                    *reinterpret_cast<f16x4 *>(&sm.q[r][c1]) = f16x4{qh[4], qh[5], qh[6], qh[7]};
-                }
-                *reinterpret_cast<f16x4 *>(&sm.k[r][c0]) = f16x4{kh[0], kh[1], kh[2], kh[3]};
-                *reinterpret_cast<f16x4 *>(&sm.k[r][c1]) = f16x4{kh[4], kh[5], kh[6], kh[7]};
-                *reinterpret_cast<u16x8 *>(&sm.v[r][cc * 8]) = pv[n];
             }
-        };
-        if (flags & GDN_QK_L2NORM)
-            stage_rows(std::true_type{});
-        else
-            stage_rows(std::false_type{});
-        if (!TRANS && c > 0) {
-            const int tp = t0 - C;  // the previous chunk is always a full one
-#pragma unroll
-            for (int n = 0; n < F::NO; ++n) {
-                const int idx = tid + n * NT, r = idx / (D / 4), cc = idx - r * (D / 4);
-                const f32x4 x = *reinterpret_cast<const f32x4 *>(&sm.ost[r][cc * 4]);
-                store4<TO>(o + ((base + tp + r) * Hv + hv) * D + cc * 4, x);
-            }
+            if (c + 1 < nchunks) prefetch_q(c + 1);
+            lds_barrier();
         }
-        if (c + 1 < nchunks) prefetch(c + 1);
-        lds_barrier();
 
         // ---- stage 1: KK^T -> A, QK^T -> P (lower-triangular 16x16 tiles), and K^T
         {
@@ -567,6 +592,15 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) sm.wn[16 * a + 4 * lg + rr][kperm(col)] = f16(-Wp[a][rr]);
         lds_barrier();
+
+        // ---- kOut: the next chunk's k and v into LDS (stage 3 was the last reader of this chunk's;
+        //      stage 4 reads neither), then the prefetch of the chunk after it -- all of it
+        //      independent of stage 4's products, free to interleave with them.  Past the last
+        //      chunk the rows are zero and nothing reads them.
+        if constexpr (!TRANS) {
+            with_norm(put_kv);
+            prefetch_kv(c + 2);
+        }
 
         if constexpr (TRANS) {
             // ---- stage 4 of the transition: N as the state (U - W N), M with no value part

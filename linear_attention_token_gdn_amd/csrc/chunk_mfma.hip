@@ -100,6 +100,15 @@ __device__ __forceinline__ int opaque(int x) {
     asm volatile("" : "+v"(x));
     return x;
 }
+// x, in hand here: the wait for a load into x happens at this point.  The compiler otherwise
+// keeps a load that only some wavefronts issue as outstanding in all of them and waits for it
+// -- that is, for every global access issued so far -- wherever its register is reused.
+__device__ __forceinline__ void settle(f32x4 &x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void settle(bf16_t &x) {
+    unsigned u = x;
+    asm volatile("" : "+v"(u));
+    x = static_cast<bf16_t>(u);
+}
 
 // Power-of-two exponents for the fp16 copies of a value column (pow2_scale's rule as an
 // exponent: m 2^e in [2^8, 2^9), e = 0 for m = 0, Inf or NaN, |e| <= 100).  A column carried at
@@ -271,6 +280,10 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 S[it][r] = sin[static_cast<size_t>(16 * it + 4 * lg + r) * D + col];
+        // in hand before the chunk loop, where a wait for them would wait for every global
+        // access in flight (the prefetches, the output stores)
+#pragma unroll
+        for (int it = 0; it < F::NI; ++it) settle(S[it]);
     } else {
 #pragma unroll
         for (int it = 0; it < F::NI; ++it) S[it] = zero4();
@@ -493,6 +506,8 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         //      column li of block lg, forward substitution by columns: step s updates every
         //      later row with x_s, so the dependent chain is 16 steps long); meanwhile the
         //      other wavefronts build K^T for the state update and the W panels
+        settle(pg);  // the next chunk's gate inputs (loaded by wavefront 1 only)
+        settle(pb);
         if (wave == 0) {
             float x[16];
 #pragma unroll

@@ -49,6 +49,7 @@
 // segment) units, one workgroup per compute unit: for 16 chains of 4,096 chunks, 16 segments
 // of 256 chunks per chain instead of one workgroup walking 4,096 chunks.
 #include <algorithm>
+#include <stddef.h>
 #include <stdlib.h>
 #include <type_traits>
 
@@ -223,7 +224,26 @@ template <> __device__ __forceinline__ void store4<bf16_t>(bf16_t *p, f32x4 x) {
 // on segment 0) it carries M, started at the identity and advanced by the same chunk maps
 // without their value part:  M <- e^gamma_last M - K^T dec W M.  After the segment,
 // S_out = M S_in + N for any state S_in entering it (Eq. (1) is affine in the state).
-enum { kOut = 0, kTrans = 1 };
+// MODE kTransTm: kTrans that also stores every chunk's (I + A)^-1 (below), for every segment
+// including the last; kOutTm: kOut that reads it back instead of forming it (no K K^T, no
+// diagonal-block inverses, no substitution, no W): Delta = Tm (diag(beta) V - diag(beta
+// e^gamma) K S), since U - W S = Tm diag(beta) V - Tm diag(beta e^gamma) K S.
+enum { kOut = 0, kTrans = 1, kOutTm = 2, kTransTm = 3 };
+
+// Tm = (I + A)^-1 of a chunk, kept between the two passes of the segmented plan: its NB lower
+// 16x16 blocks (a, cb), cb <= a, in the order a (a + 1) / 2 + cb, each as the 64 lanes' A
+// operands of v_mfma_f32_16x16x16_f16 (lane l: row 16a + l % 16, columns 16cb + 4 (l / 16)
+// .. + 3, four fp16 values): NB * 512 bytes per chunk.  The chunk of sequence b whose first
+// row is t0 (of all the token rows) takes slot t0 / C + b of head hv's tm_nslot slots
+// (sequences start anywhere, but the slots of sequence b end before the first of b + 1, so
+// slots never collide; tm_nslot = ceil(rows / C) + B).
+template <int C> struct TmGeom {
+    static constexpr int NR = C / 16, NB = NR * (NR + 1) / 2;
+    static constexpr int HALVES = NB * 256;  // per chunk
+};
+__device__ __forceinline__ constexpr int tri_row(int bi) {  // a of block bi = a (a + 1) / 2 + cb
+    return bi >= 6 ? 3 : bi >= 3 ? 2 : bi >= 1 ? 1 : 0;
+}
 
 // Units: blocks [p nchains, (p + 1) nchains) run segment p (chunks p L .. p L + L - 1 of every
 // chain, L = seg_chunks; seg_chunks = 0: L = ceil(chunks / nseg) from each chain's own length,
@@ -239,10 +259,14 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
              const bf16_t *__restrict__ g, const float *__restrict__ s0, TO *__restrict__ o,
              float *__restrict__ sT, int T, const int32_t *__restrict__ cu, unsigned flags,
              int Hk, int Hv, float scale, int nchains, int seg_chunks, int nseg,
-             size_t s0_seg_stride, float *__restrict__ mn) {
+             size_t s0_seg_stride, float *__restrict__ mn, uint16_t *__restrict__ tm,
+             int tm_nslot) {
     using F = Cfg<D, C>;
     constexpr int NT = F::NT, NR = F::NR;
-    constexpr bool TRANS = MODE == kTrans;
+    constexpr bool TRANS = MODE == kTrans || MODE == kTransTm;
+    constexpr bool TMW = MODE == kTransTm, TMR = MODE == kOutTm;
+    constexpr int NB = TmGeom<C>::NB, TMH = TmGeom<C>::HALVES;
+    constexpr int NTP = (NB * 32 + NT - 1) / NT;  // 16-byte pieces of Tm per thread
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     Smem<D, C> &sm = *reinterpret_cast<Smem<D, C> *>(smem_raw);
 
@@ -303,7 +327,13 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     //      chunk earlier than q, see stage 4), one in kTrans (staged in stage 0: its two states
     //      leave no registers to stage them during stage 4)
     u16x8 pq[F::NQ], pk[F::NQ], pv[F::NQ];
+    u16x8 ptm[TMR ? NTP : 1];  // kOutTm: the chunk's Tm, one chunk ahead (with q)
     bf16_t pg = 0, pb = 0;
+    // where chunk cidx's Tm record starts (in halves) in the tm records
+    auto tm_slot = [&](int cidx) {
+        return (static_cast<size_t>(hv) * tm_nslot + (base + static_cast<size_t>(cidx) * C) / C +
+                static_cast<size_t>(b)) * TMH;
+    };
     auto prefetch_q = [&](int cidx) {
         if constexpr (!TRANS) {
             const int tt = cidx * C, L = min(C, len - tt);
@@ -314,6 +344,15 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                 if (r < L)
                     pq[n] = *reinterpret_cast<const u16x8 *>(
                         q + ((base + tt + r) * Hk + hq) * D + cc * 8);
+            }
+        }
+        if constexpr (TMR) {
+            const uint16_t *src = tm + tm_slot(cidx);
+#pragma unroll
+            for (int n = 0; n < NTP; ++n) {
+                const int idx = tid + n * NT;
+                ptm[n] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+                if (idx < NB * 32) ptm[n] = *reinterpret_cast<const u16x8 *>(src + idx * 8);
             }
         }
     };
@@ -406,6 +445,25 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         }
     };
 
+    // Tm in LDS.  kTransTm: as rows (row r, column s at tmrow[r][s]), written by the panel
+    // solves of stage 3 into the output staging area that kTrans leaves unused, and stored as
+    // A-operand fragments by store_tm after the next barrier.  kOutTm: the fragments as
+    // stored, in the -A array that kOutTm leaves unused.
+    using SmemT = Smem<D, C>;
+    f16(*tmrow)[F::PA] = reinterpret_cast<f16(*)[F::PA]>(&sm.ost[0][0]);
+    f16 *tmf = &sm.an[0][0];
+    static_assert(sizeof(sm.ost) >= sizeof(f16) * C * F::PA && sizeof(sm.an) >= 2 * TMH &&
+                      offsetof(SmemT, ost) % 16 == 0 && offsetof(SmemT, an) % 16 == 0,
+                  "Tm staging");
+    auto store_tm = [&](int cidx) {
+        uint16_t *dst = tm + tm_slot(cidx);
+        for (int idx = tid; idx < NB * 64; idx += NT) {
+            const int bi = idx >> 6, l = idx & 63, a = tri_row(bi), cb = bi - a * (a + 1) / 2;
+            *reinterpret_cast<f16x4 *>(dst + idx * 4) =
+                *reinterpret_cast<const f16x4 *>(&tmrow[16 * a + (l & 15)][16 * cb + 4 * (l >> 4)]);
+        }
+    };
+
     const int nchunks = (len + C - 1) / C;
     if (nchunks > 0) {
         prefetch_q(0);
@@ -419,13 +477,23 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         lds_barrier();  // the previous chunk is done with every LDS buffer
         if constexpr (TRANS) {
             // ---- stage 0 of the transition: this chunk's k and v in LDS, prefetch of the next
+            //      (kTransTm: the previous chunk's Tm out of LDS)
             with_norm(put_kv);
             if (c + 1 < nchunks) prefetch_kv(c + 1);
+            if constexpr (TMW)
+                if (c > 0) store_tm(c - 1);
             lds_barrier();
         } else {
             // ---- stage 0: stage this chunk's q in LDS, store the previous chunk's output, prefetch
             //      the next q (this chunk's k and v were staged during the previous chunk)
             with_norm(put_q);
+            if constexpr (TMR) {
+#pragma unroll
+                for (int n = 0; n < NTP; ++n) {
+                    const int idx = tid + n * NT;
+                    if (idx < NB * 32) *reinterpret_cast<u16x8 *>(tmf + idx * 8) = ptm[n];
+                }
+            }
             if (c > 0) {
                 const int tp = t0 - C;  // the previous chunk is always a full one
 #pragma unroll
@@ -437,6 +505,139 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             }
             if (c + 1 < nchunks) prefetch_q(c + 1);
             lds_barrier();
+        }
+
+        if constexpr (TMR) {
+            // ---- kOutTm stage 1: P = lower(Q K^T) o D (tiles shared out over the wavefronts),
+            //      K^T (every thread), and per wavefront over its own columns: K S and Q S, and
+            //      R = diag(beta) V - diag(beta e^gamma) K S, all carried scaled by sig
+            settle(pg);  // the next chunk's gate inputs (loaded by wavefront 1 only)
+            settle(pb);
+            if (wave == 1 && c + 1 < nchunks) gates(c + 1);  // its inputs came with the prefetch
+            f32x4 yv[NR];
+            float vmax = 0.f;
+#pragma unroll
+            for (int a = 0; a < NR; ++a)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int r = 16 * a + 4 * lg + rr;
+                    yv[a][rr] = sm.bet[cb][r] * bf16_to_f32(sm.v[r][col]);
+                    vmax = fmaxf(vmax, fabsf(yv[a][rr]));
+                }
+            {
+                float smax = 0.f;
+#pragma unroll
+                for (int it = 0; it < F::NI; ++it)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) smax = fmaxf(smax, fabsf(S[it][r]));
+                vmax = max_over_rows(fmaxf(vmax, __builtin_amdgcn_ldexpf(smax, -es)));
+                const int en = next_exponent(vmax, es);
+                rescale(S, en - es);
+                es = en;
+            }
+            const float sig = exp2i(es), isig = exp2i(-es);
+            f16x8 bS[F::KD];
+#pragma unroll
+            for (int kk = 0; kk < F::KD; ++kk)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    bS[kk][e] = f16(S[2 * kk][e]);
+                    bS[kk][4 + e] = f16(S[2 * kk + 1][e]);
+                }
+            f32x4 R[NR], O[NR];
+#pragma unroll
+            for (int rt = 0; rt < NR; ++rt) {
+                f32x4 ks = zero4();
+                O[rt] = zero4();
+#pragma unroll
+                for (int kk = 0; kk < F::KD; ++kk) {
+                    const f16x8 ak = *reinterpret_cast<const f16x8 *>(&sm.k[16 * rt + li][32 * kk + 8 * lg]);
+                    const f16x8 aq = *reinterpret_cast<const f16x8 *>(&sm.q[16 * rt + li][32 * kk + 8 * lg]);
+                    ks = mma_k32(ak, bS[kk], ks);
+                    O[rt] = mma_k32(aq, bS[kk], O[rt]);
+                }
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int r = 16 * rt + 4 * lg + rr;
+                    O[rt][rr] *= sm.Gam[cb][r];
+                    R[rt][rr] = sig * yv[rt][rr] - sm.bg[cb][r] * ks[rr];
+                }
+            }
+            for (int j = wave; j < NB; j += F::NW) {  // P tile (rt, st), st <= rt
+                const int rt = tri_row(j), st = j - rt * (rt + 1) / 2;
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int kk = 0; kk < F::KD; ++kk)
+                    acc = mma_k32(*reinterpret_cast<const f16x8 *>(&sm.q[16 * rt + li][32 * kk + 8 * lg]),
+                                  *reinterpret_cast<const f16x8 *>(&sm.k[16 * st + li][32 * kk + 8 * lg]),
+                                  acc);
+                const int s = 16 * st + li;
+                const float gs = sm.gam[cb][s];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int r = 16 * rt + 4 * lg + rr;
+                    const float d = (s <= r) ? __expf(sm.gam[cb][r] - gs) : 0.f;
+                    sm.p[r][kperm(s)] = f16(acc[rr] * d);
+                    // the tile right of the diagonal is read by P Delta
+                    if (st == rt && rt + 1 < NR) sm.p[r][kperm(s + 16)] = f16(0.f);
+                }
+            }
+            for (int idx = tid; idx < D * (C / 8); idx += NT) {
+                const int i = idx % D, s8 = idx / D, ki = kperm(i);
+                f16x8 x;  // stored positions 8 s8 .. 8 s8 + 7 of row i of K^T
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = sm.k[kunperm(s8 * 8 + e)][ki];
+                *reinterpret_cast<f16x8 *>(&sm.kt[i][s8 * 8]) = x;
+            }
+            lds_barrier();
+
+            // ---- kOutTm stage 4: the next chunk's k and v into LDS (nothing below reads them),
+            //      the prefetch of the chunk after it; Delta = Tm R, O += P Delta, next state
+            with_norm(put_kv);
+            prefetch_kv(c + 2);
+            f32x4 Dl[NR];
+#pragma unroll
+            for (int a = 0; a < NR; ++a) {
+                Dl[a] = zero4();
+#pragma unroll
+                for (int cb2 = 0; cb2 <= a; ++cb2)
+                    Dl[a] = mma_k16(*reinterpret_cast<const f16x4 *>(
+                                        tmf + ((a * (a + 1) / 2 + cb2) * 64 + lane) * 4),
+                                    to_f16x4(R[cb2]), Dl[a]);
+            }
+            f16x8 bD[F::KC], bDs[F::KC];
+#pragma unroll
+            for (int kk = 0; kk < F::KC; ++kk)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s0i = 32 * kk + 4 * lg + e, s1i = s0i + 16;
+                    const float d0 = Dl[2 * kk][e], d1 = Dl[2 * kk + 1][e];
+                    bD[kk][e] = f16(d0);
+                    bD[kk][4 + e] = f16(d1);
+                    bDs[kk][e] = f16(d0 * sm.dec[cb][s0i]);
+                    bDs[kk][4 + e] = f16(d1 * sm.dec[cb][s1i]);
+                }
+            const float oscale = scale * isig;  // exact: isig is a power of two
+#pragma unroll
+            for (int rt = 0; rt < NR; ++rt) {
+#pragma unroll
+                for (int kk = 0; kk < F::KC; ++kk)
+                    if (32 * kk <= 16 * rt + 15)
+                        O[rt] = mma_k32(*reinterpret_cast<const f16x8 *>(&sm.p[16 * rt + li][32 * kk + 8 * lg]),
+                                        bD[kk], O[rt]);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) sm.ost[16 * rt + 4 * lg + rr][col] = oscale * O[rt][rr];
+            }
+            const float GC = sm.Gam[cb][C - 1];
+#pragma unroll
+            for (int it = 0; it < F::NI; ++it) {
+                S[it] *= GC;
+#pragma unroll
+                for (int kk = 0; kk < F::KC; ++kk)
+                    S[it] = mma_k32(*reinterpret_cast<const f16x8 *>(&sm.kt[16 * it + li][32 * kk + 8 * lg]),
+                                    bDs[kk], S[it]);
+            }
+            continue;
         }
 
         // ---- stage 1: KK^T -> A, QK^T -> P (lower-triangular 16x16 tiles), and K^T
@@ -582,25 +783,67 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             em = en;
         }
         f32x4 U[NR], Wp[NR];
+        // kTransTm: wavefront j < NR also solves column panel j of Tm = (I + A)^-1 in the same
+        // loop (a third chain beside U and W), X_a = T_aa (delta_aj I - sum_{cb < a} A_{a,cb}
+        // X_cb), X_a = 0 for a < j; into tmrow, stored after the next barrier.  (The other
+        // modes run the same loop without it, below.)
+        auto panels = [&](auto with_tm) {
+            constexpr bool WT = decltype(with_tm)::value;
+            f16x4 X[WT ? NR : 1];  // as the fp16 operands (and the stored values) they become
 #pragma unroll
-        for (int a = 0; a < NR; ++a) {
-            const f16x4 kv4 = *reinterpret_cast<const f16x4 *>(&sm.kt[col][kperm(16 * a + 4 * lg)]);
-            f32x4 yu, yw;
+            for (int a = 0; a < NR; ++a) {
+                const f16x4 kv4 = *reinterpret_cast<const f16x4 *>(&sm.kt[col][kperm(16 * a + 4 * lg)]);
+                f32x4 yu, yw, yx;
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int r = 16 * a + 4 * lg + rr;
-                yu[rr] = sig * yv[a][rr];
-                yw[rr] = sm.bg[cb][r] * float(kv4[rr]);
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int r = 16 * a + 4 * lg + rr;
+                    yu[rr] = sig * yv[a][rr];
+                    yw[rr] = sm.bg[cb][r] * float(kv4[rr]);
+                    if constexpr (WT) yx[rr] = (a == wave && 4 * lg + rr == li) ? 1.f : 0.f;
+                }
+#pragma unroll
+                for (int cb = 0; cb < a; ++cb) {
+                    const f16x4 an = *reinterpret_cast<const f16x4 *>(&sm.an[16 * a + li][16 * cb + 4 * lg]);
+                    yu = mma_k16(an, to_f16x4(U[cb]), yu);
+                    yw = mma_k16(an, to_f16x4(Wp[cb]), yw);
+                    if constexpr (WT) yx = mma_k16(an, X[cb], yx);
+                }
+                const f16x4 td = *reinterpret_cast<const f16x4 *>(&sm.td[a][li][4 * lg]);
+                U[a] = mma_k16(td, to_f16x4(yu), zero4());
+                Wp[a] = mma_k16(td, to_f16x4(yw), zero4());
+                if constexpr (WT) {
+                    X[a] = to_f16x4(mma_k16(td, to_f16x4(yx), zero4()));
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) tmrow[16 * a + 4 * lg + rr][16 * wave + li] = X[a][rr];
+                }
             }
+        };
+        if constexpr (TMW) {
+            if (wave < NR)
+                panels(std::true_type{});
+            else
+                panels(std::false_type{});
+        } else {
 #pragma unroll
-            for (int cb = 0; cb < a; ++cb) {
-                const f16x4 an = *reinterpret_cast<const f16x4 *>(&sm.an[16 * a + li][16 * cb + 4 * lg]);
-                yu = mma_k16(an, to_f16x4(U[cb]), yu);
-                yw = mma_k16(an, to_f16x4(Wp[cb]), yw);
+            for (int a = 0; a < NR; ++a) {
+                const f16x4 kv4 = *reinterpret_cast<const f16x4 *>(&sm.kt[col][kperm(16 * a + 4 * lg)]);
+                f32x4 yu, yw;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int r = 16 * a + 4 * lg + rr;
+                    yu[rr] = sig * yv[a][rr];
+                    yw[rr] = sm.bg[cb][r] * float(kv4[rr]);
+                }
+#pragma unroll
+                for (int cb = 0; cb < a; ++cb) {
+                    const f16x4 an = *reinterpret_cast<const f16x4 *>(&sm.an[16 * a + li][16 * cb + 4 * lg]);
+                    yu = mma_k16(an, to_f16x4(U[cb]), yu);
+                    yw = mma_k16(an, to_f16x4(Wp[cb]), yw);
+                }
+                const f16x4 td = *reinterpret_cast<const f16x4 *>(&sm.td[a][li][4 * lg]);
+                U[a] = mma_k16(td, to_f16x4(yu), zero4());
+                Wp[a] = mma_k16(td, to_f16x4(yw), zero4());
             }
-            const f16x4 td = *reinterpret_cast<const f16x4 *>(&sm.td[a][li][4 * lg]);
-            U[a] = mma_k16(td, to_f16x4(yu), zero4());
-            Wp[a] = mma_k16(td, to_f16x4(yw), zero4());
         }
 #pragma unroll
         for (int a = 0; a < NR; ++a)
@@ -735,6 +978,11 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     }
 
     if constexpr (TRANS) {  // M and N of the segment (addresses formed only here)
+        if constexpr (TMW) {  // the last chunk's Tm; the last segment's map is not needed
+            lds_barrier();
+            if (nchunks > 0) store_tm(nchunks - 1);
+            if (seg == nseg - 1) return;
+        }
         float *pm = mn + (static_cast<size_t>(seg) * nchains + chain) * 2 * D * D;
         const int lgo = opaque(lg), colo = opaque(col);
 #pragma unroll
@@ -870,9 +1118,28 @@ seg_combine_kernel(const float *s0, const float *__restrict__ mn, float *__restr
     }
 }
 
+// Workspace of the segmented plan: the maps M, N of segments 0 .. nseg-2 and every segment's
+// entry state (fp32), then -- optional: the plan runs without them, forming Tm twice -- the
+// Tm records (uint16 halves), tm_nslot slots per value head.
+size_t seg_map_bytes(const PrefillArgs &a, const SegGeom &sg) {
+    const size_t DD = static_cast<size_t>(a.dk) * a.dv, chains = static_cast<size_t>(a.B) * a.Hv;
+    return (static_cast<size_t>(sg.nseg - 1) * 2 + sg.nseg) * chains * DD * sizeof(float);
+}
+int seg_tm_slots(const PrefillArgs &a) {
+    const long rows = a.cu != nullptr ? a.T : static_cast<long>(a.B) * a.T;
+    return static_cast<int>((rows + a.chunk - 1) / a.chunk + a.B);
+}
+size_t seg_tm_bytes(const PrefillArgs &a) {
+    const char *env = getenv("GDN_SEG_NO_TM");  // A/B switch: form Tm in both passes
+    if (env != nullptr && atoi(env) != 0) return 0;
+    const size_t nr = a.chunk / 16;
+    return static_cast<size_t>(a.Hv) * seg_tm_slots(a) * (nr * (nr + 1) / 2) * 512;
+}
+
 template <int D, int C, typename TO, int MODE>
 hipError_t launch_mode(const PrefillArgs &a, unsigned nblk, int nchains, int seg_chunks,
-                       int nseg, const float *s0, size_t s0_seg_stride, float *mn) {
+                       int nseg, const float *s0, size_t s0_seg_stride, float *mn,
+                       uint16_t *tm = nullptr, int tm_nslot = 0) {
     auto kern = chunk_kernel<D, C, TO, MODE>;
     const size_t lds = sizeof(Smem<D, C>);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -884,7 +1151,7 @@ hipError_t launch_mode(const PrefillArgs &a, unsigned nblk, int nchains, int seg
                        static_cast<const bf16_t *>(a.v), static_cast<const bf16_t *>(a.beta),
                        static_cast<const bf16_t *>(a.g), s0, static_cast<TO *>(a.o), a.sT, a.T,
                        a.cu, a.flags, a.Hk, a.Hv, a.scale, nchains, seg_chunks, nseg,
-                       s0_seg_stride, mn);
+                       s0_seg_stride, mn, tm, tm_nslot);
     return hipGetLastError();
 }
 
@@ -894,13 +1161,24 @@ template <int D, int C, typename TO> hipError_t launch_typed(const PrefillArgs &
     if (sg.nseg <= 1)
         return launch_mode<D, C, TO, kOut>(a, static_cast<unsigned>(nchains), nchains, 1 << 30,
                                            1, a.s0, 0, nullptr);
-    // segmented: transitions of segments 0 .. nseg-2, their entry states, then every segment
+    // segmented: transitions of segments 0 .. nseg-2, their entry states, then every segment.
+    // With room for the Tm records (seg_tm_bytes), the transition pass also runs the last
+    // segment and stores every chunk's Tm for the output pass.
     const size_t DD = static_cast<size_t>(D) * D;
     float *mn = static_cast<float *>(a.ws);
     float *entry = mn + static_cast<size_t>(sg.nseg - 1) * nchains * 2 * DD;
-    hipError_t e = launch_mode<D, C, float, kTrans>(
-        a, static_cast<unsigned>((sg.nseg - 1) * nchains), nchains, sg.seg_chunks, sg.nseg, a.s0,
-        0, mn);
+    const size_t maps = seg_map_bytes(a, sg), tmb = seg_tm_bytes(a);
+    const bool use_tm = tmb > 0 && a.ws_bytes >= maps + tmb;
+    uint16_t *tm = use_tm ? reinterpret_cast<uint16_t *>(static_cast<unsigned char *>(a.ws) + maps)
+                          : nullptr;
+    const int tm_nslot = seg_tm_slots(a);
+    hipError_t e =
+        use_tm ? launch_mode<D, C, float, kTransTm>(a, static_cast<unsigned>(sg.nseg * nchains),
+                                                    nchains, sg.seg_chunks, sg.nseg, a.s0, 0, mn,
+                                                    tm, tm_nslot)
+               : launch_mode<D, C, float, kTrans>(
+                     a, static_cast<unsigned>((sg.nseg - 1) * nchains), nchains, sg.seg_chunks,
+                     sg.nseg, a.s0, 0, mn);
     if (e != hipSuccess) return e;
     const size_t clds = sizeof(CombineSmem<D>);
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(seg_combine_kernel<D>),
@@ -909,6 +1187,11 @@ template <int D, int C, typename TO> hipError_t launch_typed(const PrefillArgs &
     hipLaunchKernelGGL(seg_combine_kernel<D>, dim3(static_cast<unsigned>(nchains * (D / 16))),
                        dim3(256), clds, a.stream, a.s0, mn, entry, nchains, sg.nseg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (use_tm)
+        return launch_mode<D, C, TO, kOutTm>(a, static_cast<unsigned>(sg.nseg * nchains), nchains,
+                                             sg.seg_chunks, sg.nseg, entry,
+                                             static_cast<size_t>(nchains) * DD, nullptr, tm,
+                                             tm_nslot);
     return launch_mode<D, C, TO, kOut>(a, static_cast<unsigned>(sg.nseg * nchains), nchains,
                                        sg.seg_chunks, sg.nseg, entry,
                                        static_cast<size_t>(nchains) * DD, nullptr);
@@ -953,11 +1236,10 @@ SegGeom seg_geometry(const PrefillArgs &a) {
     return g;
 }
 
-size_t chunk_mfma_workspace(const PrefillArgs &a) {
+size_t chunk_mfma_workspace(const PrefillArgs &a, bool least) {
     const SegGeom sg = seg_geometry(a);
     if (sg.nseg <= 1) return 0;
-    const size_t DD = static_cast<size_t>(a.dk) * a.dv, chains = static_cast<size_t>(a.B) * a.Hv;
-    return (static_cast<size_t>(sg.nseg - 1) * 2 + sg.nseg) * chains * DD * sizeof(float);
+    return seg_map_bytes(a, sg) + (least ? 0 : seg_tm_bytes(a));
 }
 
 hipError_t launch_chunk_mfma(const PrefillArgs &a) {

@@ -144,7 +144,7 @@ static gdn_status_t check_prefill(const gdn::PrefillArgs &a) {
 static size_t plan_workspace(const gdn::PrefillArgs &a, Variant var, bool least = false) {
     return var == Variant::Split ? gdn::chunk_split_workspace(a, least)
            : var == Variant::Fused || var == Variant::Segmented
-               ? gdn::chunk_mfma_workspace(for_plan(a, var))
+               ? gdn::chunk_mfma_workspace(for_plan(a, var), least)
                : 0;
 }
 

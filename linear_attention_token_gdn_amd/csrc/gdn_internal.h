@@ -97,7 +97,10 @@ constexpr long kSegTargetUnits = 256;  // (chain, segment) units at most: MI355X
 constexpr long kSegMinChunks = 8;
 SegGeom seg_geometry(const PrefillArgs &a);
 bool chunk_mfma_supports(const PrefillArgs &a);
-size_t chunk_mfma_workspace(const PrefillArgs &a);
+// The segmented plan's workspace: the maps and entry states, plus (least = false) the per-chunk
+// (I + A)^-1 records that spare the output pass forming them; with only the former it runs
+// without the records.
+size_t chunk_mfma_workspace(const PrefillArgs &a, bool least = false);
 hipError_t launch_chunk_mfma(const PrefillArgs &a);
 
 // Two-kernel chunk-parallel form (a fully parallel prep kernel and a per-chain scan kernel

@@ -48,24 +48,40 @@ def test_version_and_status_strings(lib):
     assert gdn.gdn_status_string(99) == "GDN_ERR_UNKNOWN"
 
 
+def _tm_records(B, T, Hv, chunk, packed=False):
+    # one (I + A)^-1 record per chunk slot and value head: the NR (NR + 1) / 2 lower 16 x 16
+    # fp16 blocks (512 B each, NR = chunk / 16); ceil(rows / chunk) + B slots per head
+    rows = T if packed else B * T
+    nr = chunk // 16
+    return Hv * (-(-rows // chunk) + B) * nr * (nr + 1) // 2 * 512
+
+
 def test_workspace_of_the_segmented_plan(lib, monkeypatch):
     # per chain and segment: the fp32 transition M and state N of every segment but the last,
-    # and the entry state of every segment (d x d floats each); 256 / chains segments
+    # and the entry state of every segment (d x d floats each); 256 / chains segments; then
+    # the per-chunk (I + A)^-1 records (GDN_SEG_NO_TM: none)
     D2 = 128 * 128 * 4
     for B, T, H, nseg in ((1, 262144, 16, 16), (1, 8192, 16, 16), (4, 4096, 16, 4),
                           (1, 1 << 20, 2, 128)):
         chains = B * H
+        maps = (2 * (nseg - 1) + nseg) * chains * D2
         assert gdn.gdn_chunk_fwd_workspace_size(B, T, H, H, 128, 128, 64, gdn.GDN_BF16) == (
-            (2 * (nseg - 1) + nseg) * chains * D2)
-    # the largest: 256 units at d = 128 fit the allocation-free entry point's scratch
+            maps + _tm_records(B, T, H, 64))
+        monkeypatch.setenv("GDN_SEG_NO_TM", "1")
+        assert gdn.gdn_chunk_fwd_workspace_size(B, T, H, H, 128, 128, 64, gdn.GDN_BF16) == maps
+        monkeypatch.delenv("GDN_SEG_NO_TM")
+    # the largest maps: 256 units at d = 128 fit the allocation-free entry point's scratch (it
+    # runs without the records when they do not fit beside them)
+    monkeypatch.setenv("GDN_SEG_NO_TM", "1")
     assert gdn.gdn_chunk_fwd_workspace_size(1, 1 << 20, 1, 2, 128, 128, 64, gdn.GDN_BF16) \
         <= gdn.GDN_NOALLOC_SCRATCH_BYTES
+    monkeypatch.delenv("GDN_SEG_NO_TM")
     # a pinned segment length (tests): one chunk per segment
     monkeypatch.setenv("GDN_SEG_CHUNKS", "1")
     monkeypatch.setenv("GDN_FORCE_VARIANT", "segmented")
     assert gdn.gdn_chunk_fwd_plan(1, 200, 2, 2, 64, 64, 64, gdn.GDN_BF16) == "segmented"
     assert gdn.gdn_chunk_fwd_workspace_size(1, 200, 2, 2, 64, 64, 64, gdn.GDN_BF16) == (
-        (2 * 3 + 4) * 2 * 64 * 64 * 4)
+        (2 * 3 + 4) * 2 * 64 * 64 * 4 + _tm_records(1, 200, 2, 64))
     # one chunk in all: nothing to cut, the default plan
     assert gdn.gdn_chunk_fwd_plan(1, 64, 2, 2, 64, 64, 64, gdn.GDN_BF16) == "split"
 
@@ -75,8 +91,10 @@ def test_workspace_of_the_segmented_plan_packed(lib):
     # device); the plan is taken when the mean sequence has >= 8 chunks per segment
     ws = gdn.gdn_chunk_fwd_varlen_workspace_size
     D2 = 128 * 128 * 4
-    assert ws(2, 2 * 16384, 4, 4, 128, 128, 64, gdn.GDN_BF16, 1) == (2 * 31 + 32) * 8 * D2
-    assert ws(1, 262144, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1) == (2 * 15 + 16) * 16 * D2
+    assert ws(2, 2 * 16384, 4, 4, 128, 128, 64, gdn.GDN_BF16, 1) == (
+        (2 * 31 + 32) * 8 * D2 + _tm_records(2, 2 * 16384, 4, 64, packed=True))
+    assert ws(1, 262144, 16, 16, 128, 128, 64, gdn.GDN_BF16, 1) == (
+        (2 * 15 + 16) * 16 * D2 + _tm_records(1, 262144, 16, 64, packed=True))
     # short on average: the split plan's records (one 72 KiB + 128 B record per chunk slot)
     short = ws(8, 8 * 512, 4, 4, 128, 128, 64, gdn.GDN_BF16, 1)
     assert short != (2 * 7 + 8) * 32 * D2 and short >= 4 * (4096 // 64 + 8) * (73728 + 128)

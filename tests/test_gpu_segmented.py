@@ -59,26 +59,37 @@ def _long_memory(B, T, Hk, Hv, d, seed, s0_std=0.5):
                        g_range=(1e-5, 1e-3))
 
 
+def _tm_mode(tm, monkeypatch):
+    # "records": the transition pass stores every chunk's (I + A)^-1 and the output pass reads
+    # it (the default when the workspace holds the records); "formed": both passes form it
+    if tm == "formed":
+        monkeypatch.setenv("GDN_SEG_NO_TM", "1")
+
+
+@pytest.mark.parametrize("tm", ["records", "formed"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("chunk", [32, 64])
 @pytest.mark.parametrize("seg_chunks", [1, 3])
-def test_segmented_matches_oracle(d, chunk, seg_chunks, monkeypatch):
+def test_segmented_matches_oracle(d, chunk, seg_chunks, tm, monkeypatch):
     monkeypatch.setenv("GDN_FORCE_VARIANT", "segmented")
     monkeypatch.setenv("GDN_SEG_CHUNKS", str(seg_chunks))
+    _tm_mode(tm, monkeypatch)
     inp = _long_memory(2, 1000, 1, 2, d, seed=1100 + d + chunk + seg_chunks)
     assert _plan(inp, chunk) == "segmented"
     o, sT = _run(inp, chunk)
     ro, rS = oracle.run(inp.q, inp.k, inp.v, inp.beta, inp.g, s0=inp.s0)
-    tag = "segmented d%d C%d L%d" % (d, chunk, seg_chunks)
+    tag = "segmented d%d C%d L%d %s" % (d, chunk, seg_chunks, tm)
     check(o, ro, "bf16", tag + " o")
     check(sT, rS, "bf16", tag + " final state")
 
 
+@pytest.mark.parametrize("tm", ["records", "formed"])
 @pytest.mark.parametrize("T", [129, 192, 4 * 64, 4 * 64 + 1])
-def test_segment_boundaries(T, monkeypatch):
+def test_segment_boundaries(T, tm, monkeypatch):
     # two or more segments of two chunks; a last segment of one (possibly partial) chunk
     monkeypatch.setenv("GDN_FORCE_VARIANT", "segmented")
     monkeypatch.setenv("GDN_SEG_CHUNKS", "2")
+    _tm_mode(tm, monkeypatch)
     inp = _long_memory(1, T, 2, 2, 128, seed=1200 + T)
     assert _plan(inp) == "segmented"
     o, sT = _run(inp)
@@ -172,14 +183,16 @@ def _packed_inputs(lens, Hk, Hv, d, seed, flags):
     return x, s0, cu
 
 
+@pytest.mark.parametrize("tm", ["records", "formed"])
 @pytest.mark.parametrize("flags", [0, 1 | 2 | 4])
-def test_packed_sequences(flags, monkeypatch):
+def test_packed_sequences(flags, tm, monkeypatch):
     """Packed sequences through the segmented plan: every (sequence, head) chain in the same
     number of segments, each of ceil(its chunks / segments) chunks formed on the device --
     long and short sequences, a one-token and an empty one (final state = initial state, every
     segment empty)."""
     import linear_attention_token_gdn_amd as gdn
     monkeypatch.setenv("GDN_FORCE_VARIANT", "segmented")
+    _tm_mode(tm, monkeypatch)
     lens = [1500, 0, 1, 700, 65, 2300]
     x, s0, cu = _packed_inputs(lens, 1, 2, 128, seed=1700 + flags, flags=flags)
     t = {n: torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(torch.bfloat16)
@@ -202,7 +215,9 @@ def test_packed_default_plan_long_sequences():
     import linear_attention_token_gdn_amd as gdn
     N, T, H = 2, 2 * 16384, 4  # 8 chains: 32 segments of 8 chunks per chain
     wsz = gdn.gdn_chunk_fwd_varlen_workspace_size(N, T, H, H, 128, 128, 64, gdn.GDN_BF16, 1, 0)
-    assert wsz == (2 * 31 + 32) * N * H * 128 * 128 * 4
+    # the maps and entry states, then one (I + A)^-1 record (10 fp16 16 x 16 blocks) per chunk
+    # slot and head, T / 64 + N slots
+    assert wsz == (2 * 31 + 32) * N * H * 128 * 128 * 4 + H * (T // 64 + N) * 10 * 512
     x, s0, cu = _packed_inputs([16384, 16384], H, H, 128, seed=1800, flags=0)
     t = {n: torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(torch.bfloat16)
          for n, a in x.items()}

@@ -743,6 +743,143 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         }
         lds_barrier();
 
+        if constexpr (TMW) {
+            // ---- kTransTm stage 3, per wavefront over its own columns: the scales of N and M
+            //      for this chunk (as in stage 3 of the other modes), then R_N = diag(beta) V -
+            //      diag(beta e^gamma) K N and R_M = -diag(beta e^gamma) K M (fp16, as the
+            //      operands of stage 4 take them); then wavefront j < NR solves column panel j
+            //      of Tm = (I + A)^-1 by blocked substitution, X_a = T_aa (delta_aj I -
+            //      sum_{cb < a} A_{a,cb} X_cb) (X_a = 0 for a < j), into tmrow: read back in
+            //      stage 4 and stored after the next barrier
+            f16x4 RN[NR], RM[NR];
+            // (lane offsets made opaque, so that the compiler forms these stages' LDS addresses
+            // here instead of keeping them in registers across the chunk loop)
+            const int li = opaque(lane & 15), lg = opaque(lane >> 4);
+            auto rprod = [&]() {
+                f32x4 yv[NR];
+                float vmax = 0.f;
+#pragma unroll
+                for (int a = 0; a < NR; ++a)
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int r = 16 * a + 4 * lg + rr;
+                        yv[a][rr] = sm.bet[cb][r] * bf16_to_f32(sm.v[r][col]);
+                        vmax = fmaxf(vmax, fabsf(yv[a][rr]));
+                    }
+                float smax = 0.f, mmax = 0.f;
+#pragma unroll
+                for (int it = 0; it < F::NI; ++it)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        smax = fmaxf(smax, fabsf(S[it][r]));
+                        mmax = fmaxf(mmax, fabsf(M[it][r]));
+                    }
+                vmax = max_over_rows(fmaxf(vmax, __builtin_amdgcn_ldexpf(smax, -es)));
+                const int en = next_exponent(vmax, es);
+                rescale(S, en - es);
+                es = en;
+                const float mm = max_over_rows(__builtin_amdgcn_ldexpf(mmax, -em));
+                const int enm = next_exponent(mm, em);
+                rescale(M, enm - em);
+                em = enm;
+                // k-steps outermost, so that one k-step of the B operands is live at a time
+                f32x4 kn[NR], km[NR];
+#pragma unroll
+                for (int rt = 0; rt < NR; ++rt) {
+                    kn[rt] = zero4();
+                    km[rt] = zero4();
+                }
+#pragma unroll
+                for (int kk = 0; kk < F::KD; ++kk) {
+                    f16x8 bS, bM;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        bS[e] = f16(S[2 * kk][e]);
+                        bS[4 + e] = f16(S[2 * kk + 1][e]);
+                        bM[e] = f16(M[2 * kk][e]);
+                        bM[4 + e] = f16(M[2 * kk + 1][e]);
+                    }
+#pragma unroll
+                    for (int rt = 0; rt < NR; ++rt) {
+                        const f16x8 ak = *reinterpret_cast<const f16x8 *>(&sm.k[16 * rt + li][32 * kk + 8 * lg]);
+                        kn[rt] = mma_k32(ak, bS, kn[rt]);
+                        km[rt] = mma_k32(ak, bM, km[rt]);
+                    }
+                }
+                const float sig = exp2i(es);
+#pragma unroll
+                for (int rt = 0; rt < NR; ++rt) {
+                    f32x4 rn, rm;
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const float bgr = sm.bg[cb][16 * rt + 4 * lg + rr];
+                        rn[rr] = sig * yv[rt][rr] - bgr * kn[rt][rr];
+                        rm[rr] = -bgr * km[rt][rr];
+                    }
+                    RN[rt] = to_f16x4(rn);
+                    RM[rt] = to_f16x4(rm);
+                }
+            };
+            rprod();
+            if (wave < NR) {
+                f16x4 X[NR];  // as the fp16 operands (and the stored values) they become
+#pragma unroll
+                for (int a = 0; a < NR; ++a) {
+                    f32x4 yx;
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) yx[rr] = (a == wave && 4 * lg + rr == li) ? 1.f : 0.f;
+#pragma unroll
+                    for (int cb2 = 0; cb2 < a; ++cb2)
+                        yx = mma_k16(*reinterpret_cast<const f16x4 *>(&sm.an[16 * a + li][16 * cb2 + 4 * lg]),
+                                     X[cb2], yx);
+                    X[a] = to_f16x4(mma_k16(*reinterpret_cast<const f16x4 *>(&sm.td[a][li][4 * lg]),
+                                            to_f16x4(yx), zero4()));
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) tmrow[16 * a + 4 * lg + rr][16 * wave + li] = X[a][rr];
+                }
+            }
+            lds_barrier();
+
+            // ---- kTransTm stage 4: Delta_N = Tm R_N, Delta_M = Tm R_M, then N and M through
+            //      K^T diag(e^(gamma_last - gamma)) as in the other transition
+            f32x4 DN[NR], DM[NR];
+#pragma unroll
+            for (int a = 0; a < NR; ++a) {
+                DN[a] = zero4();
+                DM[a] = zero4();
+#pragma unroll
+                for (int cb2 = 0; cb2 <= a; ++cb2) {
+                    const f16x4 at = *reinterpret_cast<const f16x4 *>(&tmrow[16 * a + li][16 * cb2 + 4 * lg]);
+                    DN[a] = mma_k16(at, RN[cb2], DN[a]);
+                    DM[a] = mma_k16(at, RM[cb2], DM[a]);
+                }
+            }
+            f16x8 bDs[F::KC], bDm[F::KC];
+#pragma unroll
+            for (int kk = 0; kk < F::KC; ++kk)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s0i = 32 * kk + 4 * lg + e, s1i = s0i + 16;
+                    bDs[kk][e] = f16(DN[2 * kk][e] * sm.dec[cb][s0i]);
+                    bDs[kk][4 + e] = f16(DN[2 * kk + 1][e] * sm.dec[cb][s1i]);
+                    bDm[kk][e] = f16(DM[2 * kk][e] * sm.dec[cb][s0i]);
+                    bDm[kk][4 + e] = f16(DM[2 * kk + 1][e] * sm.dec[cb][s1i]);
+                }
+            const float GC = sm.Gam[cb][C - 1];
+#pragma unroll
+            for (int it = 0; it < F::NI; ++it) {
+                S[it] *= GC;
+                M[it] *= GC;
+#pragma unroll
+                for (int kk = 0; kk < F::KC; ++kk) {
+                    const f16x8 ak = *reinterpret_cast<const f16x8 *>(&sm.kt[16 * it + li][32 * kk + 8 * lg]);
+                    S[it] = mma_k32(ak, bDs[kk], S[it]);
+                    M[it] = mma_k32(ak, bDm[kk], M[it]);
+                }
+            }
+            continue;
+        }
+
         // ---- stage 3: blocked forward substitution for this wave's panels,
         //      U[:, 16w..] = (I+A)^-1 diag(beta) V[:, 16w..]  (kept in registers)
         //      W[:, 16w..] = (I+A)^-1 diag(beta e^gamma) K[:, 16w..]  (-W to LDS)
@@ -783,67 +920,25 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             em = en;
         }
         f32x4 U[NR], Wp[NR];
-        // kTransTm: wavefront j < NR also solves column panel j of Tm = (I + A)^-1 in the same
-        // loop (a third chain beside U and W), X_a = T_aa (delta_aj I - sum_{cb < a} A_{a,cb}
-        // X_cb), X_a = 0 for a < j; into tmrow, stored after the next barrier.  (The other
-        // modes run the same loop without it, below.)
-        auto panels = [&](auto with_tm) {
-            constexpr bool WT = decltype(with_tm)::value;
-            f16x4 X[WT ? NR : 1];  // as the fp16 operands (and the stored values) they become
 #pragma unroll
-            for (int a = 0; a < NR; ++a) {
-                const f16x4 kv4 = *reinterpret_cast<const f16x4 *>(&sm.kt[col][kperm(16 * a + 4 * lg)]);
-                f32x4 yu, yw, yx;
+        for (int a = 0; a < NR; ++a) {
+            const f16x4 kv4 = *reinterpret_cast<const f16x4 *>(&sm.kt[col][kperm(16 * a + 4 * lg)]);
+            f32x4 yu, yw;
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int r = 16 * a + 4 * lg + rr;
-                    yu[rr] = sig * yv[a][rr];
-                    yw[rr] = sm.bg[cb][r] * float(kv4[rr]);
-                    if constexpr (WT) yx[rr] = (a == wave && 4 * lg + rr == li) ? 1.f : 0.f;
-                }
-#pragma unroll
-                for (int cb = 0; cb < a; ++cb) {
-                    const f16x4 an = *reinterpret_cast<const f16x4 *>(&sm.an[16 * a + li][16 * cb + 4 * lg]);
-                    yu = mma_k16(an, to_f16x4(U[cb]), yu);
-                    yw = mma_k16(an, to_f16x4(Wp[cb]), yw);
-                    if constexpr (WT) yx = mma_k16(an, X[cb], yx);
-                }
-                const f16x4 td = *reinterpret_cast<const f16x4 *>(&sm.td[a][li][4 * lg]);
-                U[a] = mma_k16(td, to_f16x4(yu), zero4());
-                Wp[a] = mma_k16(td, to_f16x4(yw), zero4());
-                if constexpr (WT) {
-                    X[a] = to_f16x4(mma_k16(td, to_f16x4(yx), zero4()));
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) tmrow[16 * a + 4 * lg + rr][16 * wave + li] = X[a][rr];
-                }
+            for (int rr = 0; rr < 4; ++rr) {
+                const int r = 16 * a + 4 * lg + rr;
+                yu[rr] = sig * yv[a][rr];
+                yw[rr] = sm.bg[cb][r] * float(kv4[rr]);
             }
-        };
-        if constexpr (TMW) {
-            if (wave < NR)
-                panels(std::true_type{});
-            else
-                panels(std::false_type{});
-        } else {
 #pragma unroll
-            for (int a = 0; a < NR; ++a) {
-                const f16x4 kv4 = *reinterpret_cast<const f16x4 *>(&sm.kt[col][kperm(16 * a + 4 * lg)]);
-                f32x4 yu, yw;
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int r = 16 * a + 4 * lg + rr;
-                    yu[rr] = sig * yv[a][rr];
-                    yw[rr] = sm.bg[cb][r] * float(kv4[rr]);
-                }
-#pragma unroll
-                for (int cb = 0; cb < a; ++cb) {
-                    const f16x4 an = *reinterpret_cast<const f16x4 *>(&sm.an[16 * a + li][16 * cb + 4 * lg]);
-                    yu = mma_k16(an, to_f16x4(U[cb]), yu);
-                    yw = mma_k16(an, to_f16x4(Wp[cb]), yw);
-                }
-                const f16x4 td = *reinterpret_cast<const f16x4 *>(&sm.td[a][li][4 * lg]);
-                U[a] = mma_k16(td, to_f16x4(yu), zero4());
-                Wp[a] = mma_k16(td, to_f16x4(yw), zero4());
+            for (int cb = 0; cb < a; ++cb) {
+                const f16x4 an = *reinterpret_cast<const f16x4 *>(&sm.an[16 * a + li][16 * cb + 4 * lg]);
+                yu = mma_k16(an, to_f16x4(U[cb]), yu);
+                yw = mma_k16(an, to_f16x4(Wp[cb]), yw);
             }
+            const f16x4 td = *reinterpret_cast<const f16x4 *>(&sm.td[a][li][4 * lg]);
+            U[a] = mma_k16(td, to_f16x4(yu), zero4());
+            Wp[a] = mma_k16(td, to_f16x4(yw), zero4());
         }
 #pragma unroll
         for (int a = 0; a < NR; ++a)

@@ -282,9 +282,12 @@ def prefill_configs(gdn, torch, dev, stream, names=(1, 2)):
     return out
 
 
-def prefill_plans(gdn, torch, dev, stream, idx, plans=("split", "segmented")):
+def prefill_plans(gdn, torch, dev, stream, idx,
+                  plans=("split", "segmented", "segmented_formed")):
     """One prefill workload under each chunk-parallel plan that takes it (GDN_FORCE_VARIANT),
-    one call each, median of 3, 1 GiB written between calls; inputs as gpu_inputs."""
+    one call each, median of 3, 1 GiB written between calls; inputs as gpu_inputs.
+    "segmented_formed" is the segmented plan with GDN_SEG_NO_TM set: both of its passes form
+    every chunk's (I + A)^-1 instead of the output pass reading the transition pass's."""
     from gdn_inputs import CONFIGS
     c = CONFIGS[idx]
     B, T, Hk, Hv, dk, dv, C = (c[k_] for k_ in ("B", "T", "Hk", "Hv", "dk", "dv", "chunk"))
@@ -296,8 +299,13 @@ def prefill_plans(gdn, torch, dev, stream, idx, plans=("split", "segmented")):
     old = os.environ.get("GDN_FORCE_VARIANT")
     try:
         for plan in plans:
-            os.environ["GDN_FORCE_VARIANT"] = plan
-            if gdn.gdn_chunk_fwd_plan(B, T, Hk, Hv, dk, dv, C, gdn.GDN_BF16) != plan:
+            base = plan.replace("_formed", "")
+            os.environ["GDN_FORCE_VARIANT"] = base
+            if plan.endswith("_formed"):
+                os.environ["GDN_SEG_NO_TM"] = "1"
+            else:
+                os.environ.pop("GDN_SEG_NO_TM", None)
+            if gdn.gdn_chunk_fwd_plan(B, T, Hk, Hv, dk, dv, C, gdn.GDN_BF16) != base:
                 continue
             need = gdn.gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, C, gdn.GDN_BF16)
             ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -320,6 +328,7 @@ def prefill_plans(gdn, torch, dev, stream, idx, plans=("split", "segmented")):
                          "workspace_bytes": need}
             del ws
     finally:
+        os.environ.pop("GDN_SEG_NO_TM", None)
         if old is None:
             os.environ.pop("GDN_FORCE_VARIANT", None)
         else:
@@ -680,8 +689,12 @@ def main():
     plan = gdn.gdn_chunk_fwd_plan(B, T, Hk, Hv, dk, dv, C, gdn.GDN_BF16)
     pre_kernels = {"split": "prep_kernel<%d,%d,false> + scan_kernel<%d,%d,float>" % (dk, C, dk, C),
                    "fused": "chunk_kernel<%d,%d,float,0>" % (dk, C),
-                   "segmented": "chunk_kernel<%d,%d,float,1> + seg_combine_kernel<%d> + "
-                                "chunk_kernel<%d,%d,float,0>" % (dk, C, dk, dk, C)}.get(plan, plan)
+                   # the transition pass storing each chunk's (I + A)^-1, the combine, the
+                   # output pass reading it (modes 3 and 2; 1 and 0 with GDN_SEG_NO_TM)
+                   "segmented": "chunk_kernel<%d,%d,float,%d> + seg_combine_kernel<%d> + "
+                                "chunk_kernel<%d,%d,float,%d>" % (
+                                    dk, C, 1 if os.environ.get("GDN_SEG_NO_TM") else 3, dk, dk, C,
+                                    0 if os.environ.get("GDN_SEG_NO_TM") else 2)}.get(plan, plan)
     src_key = {"split": "prefill"}.get(plan, plan)
     rooflines = {
         "prefill": {

@@ -101,7 +101,13 @@ const char *gdn_status_string(gdn_status_t status);
  * between them and the same results bit for bit, so the size stays bounded for any T.  The
  * "segmented" plan keeps three fp32 dk x dv matrices per (chain, segment) there: each
  * segment's transition M and state N (all but the last segment) and its entry state; with at
- * most 256 (chain, segment) units that is at most 48 MiB at dk = dv = 128, whatever T.
+ * most 256 (chain, segment) units that is at most 48 MiB at dk = dv = 128, whatever T.  After
+ * them it keeps every chunk's (I + A)^-1 (the unit-lower-triangular inverse of the chunk's
+ * WY/UT transform) as fp16, its (chunk/16)(chunk/16 + 1)/2 lower 16 x 16 blocks of 512 B
+ * (5 KiB at chunk 64), in ceil(rows / chunk) + B slots per value head (rows = B T, or T for
+ * packed sequences): the transition pass stores it and the output pass reads it instead of
+ * forming it again (320 MiB for 262,144 tokens x 16 heads).  With the environment variable
+ * GDN_SEG_NO_TM=1 both passes form it and the size is the maps' alone.
  */
 size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
                                     gdn_dtype_t in_dtype);
@@ -167,11 +173,14 @@ gdn_status_t gdn_chunk_fwd(const void *q, const void *k, const void *v, const vo
 /*
  * gdn_chunk_fwd for callers that cannot allocate device memory -- code being captured into a
  * HIP graph, tight serving loops, harnesses that forbid hipMalloc: the same arguments without
- * the workspace, the same kernels and results (bit for bit).  Where the plan needs a
+ * the workspace, the same plan, and the same results bit for bit wherever the plan's whole
+ * workspace fits the scratch.  Where the plan needs a
  * workspace (gdn_chunk_fwd_workspace_size(...) > 0) it uses a static scratch buffer of
  * GDN_NOALLOC_SCRATCH_BYTES that the library holds in every GPU's memory from its load until
  * the process ends; the call itself allocates nothing (no hipMalloc, no allocating library
- * routine).  The segmented plan's maps and entry states always fit the scratch.  The split
+ * routine).  The segmented plan's maps and entry states always fit the scratch; where its
+ * per-chunk (I + A)^-1 records do not fit beside them, both of its passes form that inverse
+ * instead (results to the same precision bar, not the same bits).  The split
  * plan runs in segments of as many chunks as the scratch holds
  * (about 1,000 chunk-heads at dk = dv = 128 and chunk 64, e.g. 64 chunks of 16 heads): the
  * same results, bit for bit, at any T, and slower than one pass for long sequences.  A size

@@ -48,6 +48,12 @@
 // kOut then runs all segments in parallel from their entry states.  At most 256 (chain,
 // segment) units, one workgroup per compute unit: for 16 chains of 4,096 chunks, 16 segments
 // of 256 chunks per chain instead of one workgroup walking 4,096 chunks.
+//   Both passes need every chunk's Tm = (I + A)^-1.  With room for it in the workspace, the
+// transition (mode kTransTm, then over all nseg segments) forms it once and stores it, and the
+// output pass (kOutTm) reads it back.  Neither pass then forms U or W: since U - W S =
+// Tm (diag(beta) V - diag(beta e^gamma) K S), the state products run on K (already in LDS)
+// and Delta = Tm R is one dense product; the output pass also skips K K^T, the diagonal-block
+// inverses and the substitution, and needs 3 barriers per chunk instead of 5.
 #include <algorithm>
 #include <stddef.h>
 #include <stdlib.h>

@@ -86,7 +86,9 @@ hipError_t launch_recurrent(const PrefillArgs &a);
 // (packed sequences: seg_chunks = 0, each chain's segments of ceil(its chunks / nseg) chunks,
 // formed on the device), run in parallel -- a transition pass (each segment's affine map of
 // the state), a sequential combine of those maps into every segment's entry state, then the
-// single-pass kernel over all segments.  Its workspace holds the maps and the entry states.
+// single-pass kernel over all segments.  Its workspace holds the maps and the entry states,
+// then (when it has room for them) every chunk's (I + A)^-1, which the transition pass stores
+// and the single pass reads instead of forming it.
 struct SegGeom {
     int nseg, seg_chunks;
 };

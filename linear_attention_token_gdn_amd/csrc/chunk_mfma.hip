@@ -273,6 +273,12 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     constexpr bool TMW = MODE == kTransTm, TMR = MODE == kOutTm;
     constexpr int NB = TmGeom<C>::NB, TMH = TmGeom<C>::HALVES;
     constexpr int NTP = (NB * 32 + NT - 1) / NT;  // 16-byte pieces of Tm per thread
+    // The wavefront that loads the gate inputs and forms the gates: 1 (it has no stage-2
+    // inverses); kOutTm: the last, which has the fewest P tiles in stage 1
+    constexpr int GW = TMR ? F::NW - 1 : 1;
+    // kOutTm: the wavefronts w >= KTW build K^T in stage 1 (the P tiles are dealt out in turn,
+    // so the first NB mod NW wavefronts have one more; they leave K^T to the others)
+    constexpr int KTW = NB % F::NW;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     Smem<D, C> &sm = *reinterpret_cast<Smem<D, C> *>(smem_raw);
 
@@ -377,7 +383,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         }
         pg = 0;
         pb = 0;
-        if (wave == 1 && lane < L) {  // the gates: wavefront 1 forms them (gates(), below)
+        if (wave == GW && lane < L) {  // the gates: wavefront GW forms them (gates(), below)
             const size_t gi = (base + tt + lane) * Hv + hv;
             pg = g[gi];
             pb = beta[gi];
@@ -433,7 +439,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         else
             f(std::false_type{});
     };
-    // wavefront 1: the gates of chunk cidx into buffer cidx & 1, from pg, pb (rows past the end:
+    // wavefront GW: the gates of chunk cidx into buffer cidx & 1, from pg, pb (rows past the end:
     // g = beta = 0)
     auto gates = [&](int cidx) {
         const int L = min(C, len - cidx * C), gb = cidx & 1;
@@ -475,7 +481,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         prefetch_q(0);
         prefetch_kv(0);
         if constexpr (!TRANS) with_norm(put_kv);  // chunk 0's k and v (LDS is not in use yet)
-        if (wave == 1) gates(0);
+        if (wave == GW) gates(0);
         if constexpr (!TRANS) prefetch_kv(1);
     }
     for (int c = 0; c < nchunks; ++c) {
@@ -515,11 +521,12 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 
         if constexpr (TMR) {
             // ---- kOutTm stage 1: P = lower(Q K^T) o D (tiles shared out over the wavefronts),
-            //      K^T (every thread), and per wavefront over its own columns: K S and Q S, and
-            //      R = diag(beta) V - diag(beta e^gamma) K S, all carried scaled by sig
-            settle(pg);  // the next chunk's gate inputs (loaded by wavefront 1 only)
+            //      K^T (by the wavefronts w >= KTW), and per wavefront over its own columns:
+            //      K S and Q S, and R = diag(beta) V - diag(beta e^gamma) K S, all carried
+            //      scaled by sig
+            settle(pg);  // the next chunk's gate inputs (loaded by wavefront GW only)
             settle(pb);
-            if (wave == 1 && c + 1 < nchunks) gates(c + 1);  // its inputs came with the prefetch
+            if (wave == GW && c + 1 < nchunks) gates(c + 1);  // its inputs came with the prefetch
             f32x4 yv[NR];
             float vmax = 0.f;
 #pragma unroll
@@ -588,7 +595,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                     if (st == rt && rt + 1 < NR) sm.p[r][kperm(s + 16)] = f16(0.f);
                 }
             }
-            for (int idx = tid; idx < D * (C / 8); idx += NT) {
+            for (int idx = tid - 64 * KTW; idx >= 0 && idx < D * (C / 8); idx += NT - 64 * KTW) {
                 const int i = idx % D, s8 = idx / D, ki = kperm(i);
                 f16x8 x;  // stored positions 8 s8 .. 8 s8 + 7 of row i of K^T
 #pragma unroll
@@ -713,7 +720,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         //      column li of block lg, forward substitution by columns: step s updates every
         //      later row with x_s, so the dependent chain is 16 steps long); meanwhile the
         //      other wavefronts build K^T for the state update and the W panels
-        settle(pg);  // the next chunk's gate inputs (loaded by wavefront 1 only)
+        settle(pg);  // the next chunk's gate inputs (loaded by wavefront GW only)
         settle(pb);
         if (wave == 0) {
             float x[16];

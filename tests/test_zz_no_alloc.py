@@ -2,7 +2,9 @@
 workspace is the library's static scratch) against gdn_chunk_fwd with a caller workspace, both
 through the C ABI on the same inputs: bit-identical outputs and final states, two calls in a
 row (the second smaller, so the scratch still holds the first call's records), a plan without a
-workspace, the segmented plan (transitions and entry states in the scratch), and a split-plan
+workspace, the segmented plan (transitions, entry states and per-chunk (I + A)^-1 records in
+the scratch; and, where the records do not fit, the same plan forming that inverse in both
+passes, as gdn_chunk_fwd does under GDN_SEG_NO_TM), and a split-plan
 input whose records exceed the scratch, which runs in two segments there and in one with the
 caller's workspace.  The outputs are also held to the oracle's bar (bf16
 inputs: eps <= 2e-3 M).
@@ -90,6 +92,25 @@ def test_noalloc_equals_the_workspace_entry_point(monkeypatch):
     ro, rS = oracle.run(huge.q, huge.k, huge.v, huge.beta, huge.g, s0=huge.s0, chains=chains)
     check(o[0][:, chains].transpose(1, 0, 2), ro, "bf16", "noalloc segmented o (T=8192)")
     check(s[0][chains], rS, "bf16", "noalloc segmented state (T=8192)")
+    # 4b: the segmented plan where the per-chunk (I + A)^-1 records do not fit beside the maps
+    #     in the scratch (32,768 tokens, 16 heads: 46 MiB of maps + 42 MiB of records): both
+    #     passes form the inverse instead -- bit for bit gdn_chunk_fwd with GDN_SEG_NO_TM
+    long_ = make_inputs(1, 32768, 16, 16, 128, 128, dtype="bf16", s0_std=0.02, seed=994)
+    need = gdn.gdn_chunk_fwd_workspace_size(1, 32768, 16, 16, 128, 128, 64, gdn.GDN_BF16)
+    assert need > gdn.GDN_NOALLOC_SCRATCH_BYTES
+    st1, o1, s1 = _call(long_, noalloc=True)
+    monkeypatch.setenv("GDN_SEG_NO_TM", "1")
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 32768, 16, 16, 128, 128, 64, gdn.GDN_BF16) \
+        <= gdn.GDN_NOALLOC_SCRATCH_BYTES
+    st2, o2, s2 = _call(long_, noalloc=False)
+    monkeypatch.delenv("GDN_SEG_NO_TM")
+    assert st1 == gdn.GDN_OK and st2 == gdn.GDN_OK, (st1, st2)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(s1, s2)
+    lc = np.array([5])
+    rlo, rlS = oracle.run(long_.q, long_.k, long_.v, long_.beta, long_.g, s0=long_.s0, chains=lc)
+    check(o1[0][:, lc].transpose(1, 0, 2), rlo, "bf16", "noalloc segmented o (T=32768)")
+    check(s1[0][lc], rlS, "bf16", "noalloc segmented state (T=32768)")
     # 5: split records beyond the scratch (the same input: 144 MiB in one pass): two segments
     #    of chunks in the scratch, bit for bit the one-pass result
     monkeypatch.setenv("GDN_FORCE_VARIANT", "split")

@@ -467,12 +467,13 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     static_assert(sizeof(sm.ost) >= sizeof(f16) * C * F::PA && sizeof(sm.an) >= 2 * TMH &&
                       offsetof(SmemT, ost) % 16 == 0 && offsetof(SmemT, an) % 16 == 0,
                   "Tm staging");
-    auto store_tm = [&](int cidx) {
+    auto store_tm = [&](int cidx) {  // 16-byte pieces: the fragments of lanes 2p', 2p' + 1
         uint16_t *dst = tm + tm_slot(cidx);
-        for (int idx = tid; idx < NB * 64; idx += NT) {
-            const int bi = idx >> 6, l = idx & 63, a = tri_row(bi), cb = bi - a * (a + 1) / 2;
-            *reinterpret_cast<f16x4 *>(dst + idx * 4) =
-                *reinterpret_cast<const f16x4 *>(&tmrow[16 * a + (l & 15)][16 * cb + 4 * (l >> 4)]);
+        for (int idx = tid; idx < NB * 32; idx += NT) {
+            const int bi = idx >> 5, l = 2 * (idx & 31), a = tri_row(bi), cb = bi - a * (a + 1) / 2;
+            const f16 *src = &tmrow[16 * a + (l & 15)][16 * cb + 4 * (l >> 4)];
+            *reinterpret_cast<f16x8 *>(dst + idx * 8) =
+                cat(*reinterpret_cast<const f16x4 *>(src), *reinterpret_cast<const f16x4 *>(src + F::PA));
         }
     };
 

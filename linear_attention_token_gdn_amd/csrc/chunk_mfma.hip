@@ -102,6 +102,17 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
     x += dpp_or_zero<0x143, 0xc>(x);  // row_bcast:31 into rows 2, 3
     return x;
 }
+// v of lane N of each group of four lanes, in all four (DPP quad_perm [N, N, N, N])
+template <int N> __device__ __forceinline__ float quad_bcast(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 N * 0x55, 0xf, 0xf, false));
+}
+template <int N, typename Fn, int I = 0> __device__ __forceinline__ void static_for(Fn &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, Fn, I + 1>(static_cast<Fn &&>(f));
+    }
+}
 // x, as a value the compiler cannot see through (nothing derived from it moves above this)
 __device__ __forceinline__ int opaque(int x) {
     asm volatile("" : "+v"(x));
@@ -717,42 +728,75 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         }
         lds_barrier();
 
-        // ---- stage 2: wavefront 0 inverts the 16x16 diagonal blocks of I + A (lane (li, lg):
-        //      column li of block lg, forward substitution by columns: step s updates every
-        //      later row with x_s, so the dependent chain is 16 steps long); meanwhile the
-        //      other wavefronts build K^T for the state update and the W panels
+        // ---- stage 2: the inverses of the 16x16 diagonal blocks of I + A (fp32 forward
+        //      substitution by columns: step s updates every later row with x_s, a dependent
+        //      chain of 15 steps), and K^T for the state update and the W panels.  With 8
+        //      wavefronts, wavefronts 4 .. 4 + NR - 1 take one block each, four lanes a column;
+        //      with 4, wavefront 0 takes them all, one lane a column, while the others build
+        //      K^T
         settle(pg);  // the next chunk's gate inputs (loaded by wavefront GW only)
         settle(pb);
-        if (wave == 0) {
-            float x[16];
+        if constexpr (F::NW == 8) {
+            // wavefront 4 + b inverts block b: lane l holds rows 4q .. 4q + 3 (q = l mod 4) of
+            // column j = l / 4, so a column is a DPP quad.  Step s: x_s from lane s / 4 of the
+            // quad, then x_r -= A[r][s] x_s for the lane's four rows (A[r][s] = 0 for r <= s,
+            // so no lane needs a mask): 15 steps of one broadcast and four FMAs.  Then every
+            // thread builds its share of K^T (the inverting wavefronts after their blocks)
+            if (wave >= 4 && wave < 4 + NR) {
+                const int bb = wave - 4, j = lane >> 2, q = lane & 3;
+                float x[4];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) x[r] = (r == li) ? 1.f : 0.f;
-            if (lg < NR) {
+                for (int i = 0; i < 4; ++i) x[i] = (4 * q + i == j) ? 1.f : 0.f;
+                f32x4 a[15];  // A[4q + i][s], every s, loaded before the chain starts
 #pragma unroll
-                for (int st = 0; st < 15; ++st) {
-                    float colv[16];
+                for (int st = 0; st < 15; ++st)
+                    a[st] = *reinterpret_cast<const f32x4 *>(&sm.adT[bb][st][4 * q]);
+                static_for<15>([&](auto stc) {
+                    constexpr int st = decltype(stc)::value;
+                    const float xs = quad_bcast<st / 4>(x[st % 4]);
 #pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        const f32x4 t = *reinterpret_cast<const f32x4 *>(&sm.adT[lg][st][4 * r4]);
-                        colv[4 * r4] = t[0], colv[4 * r4 + 1] = t[1], colv[4 * r4 + 2] = t[2], colv[4 * r4 + 3] = t[3];
-                    }
+                    for (int i = 0; i < 4; ++i) x[i] -= a[st][i] * xs;
+                });
 #pragma unroll
-                    for (int r = st + 1; r < 16; ++r) x[r] -= colv[r] * x[st];
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sm.td[lg][r][li] = f16(x[r]);
+                for (int i = 0; i < 4; ++i) sm.td[bb][4 * q + i][j] = f16(x[i]);
             }
-        } else if (F::NW < 8 || wave != 4) {
-            // (wavefront 4 shares wavefront 0's SIMD and leaves it to the inverses)
             if (wave == 1 && c + 1 < nchunks) gates(c + 1);  // its inputs came with the prefetch
-            constexpr int NB = F::NW < 8 ? NT - 64 : NT - 128;  // threads building K^T
-            const int bt = tid - 64 - (F::NW >= 8 && wave > 4 ? 64 : 0);
-            for (int idx = bt; idx < D * (C / 8); idx += NB) {
+            for (int idx = tid; idx < D * (C / 8); idx += NT) {
                 const int i = idx % D, s8 = idx / D, ki = kperm(i);
                 f16x8 x;  // stored positions 8 s8 .. 8 s8 + 7 of row i of K^T
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[e] = sm.k[kunperm(s8 * 8 + e)][ki];
                 *reinterpret_cast<f16x8 *>(&sm.kt[i][s8 * 8]) = x;
+            }
+        } else {
+            if (wave == 0) {
+                float x[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) x[r] = (r == li) ? 1.f : 0.f;
+                if (lg < NR) {
+#pragma unroll
+                    for (int st = 0; st < 15; ++st) {
+                        float colv[16];
+#pragma unroll
+                        for (int r4 = 0; r4 < 4; ++r4) {
+                            const f32x4 t = *reinterpret_cast<const f32x4 *>(&sm.adT[lg][st][4 * r4]);
+                            colv[4 * r4] = t[0], colv[4 * r4 + 1] = t[1], colv[4 * r4 + 2] = t[2], colv[4 * r4 + 3] = t[3];
+                        }
+#pragma unroll
+                        for (int r = st + 1; r < 16; ++r) x[r] -= colv[r] * x[st];
+                    }
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sm.td[lg][r][li] = f16(x[r]);
+                }
+            } else {
+                if (wave == 1 && c + 1 < nchunks) gates(c + 1);  // its inputs came with the prefetch
+                for (int idx = tid - 64; idx < D * (C / 8); idx += NT - 64) {
+                    const int i = idx % D, s8 = idx / D, ki = kperm(i);
+                    f16x8 x;  // stored positions 8 s8 .. 8 s8 + 7 of row i of K^T
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = sm.k[kunperm(s8 * 8 + e)][ki];
+                    *reinterpret_cast<f16x8 *>(&sm.kt[i][s8 * 8]) = x;
+                }
             }
         }
         lds_barrier();

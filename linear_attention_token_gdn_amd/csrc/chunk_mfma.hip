@@ -284,9 +284,10 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     constexpr bool TMW = MODE == kTransTm, TMR = MODE == kOutTm;
     constexpr int NB = TmGeom<C>::NB, TMH = TmGeom<C>::HALVES;
     constexpr int NTP = (NB * 32 + NT - 1) / NT;  // 16-byte pieces of Tm per thread
-    // The wavefront that loads the gate inputs and forms the gates: 1 (it has no stage-2
-    // inverses); kOutTm: the last, which has the fewest P tiles in stage 1
-    constexpr int GW = TMR ? F::NW - 1 : 1;
+    // The wavefront that loads the gate inputs and forms the gates: the last with 8 wavefronts
+    // (kOutTm: it has the fewest P tiles in stage 1; else it inverts one diagonal block in
+    // stage 2, the shortest job there), 1 with 4 (wavefront 0 inverts in stage 2)
+    constexpr int GW = TMR || F::NW == 8 ? F::NW - 1 : 1;
     // kOutTm: the wavefronts w >= KTW build K^T in stage 1 (the P tiles are dealt out in turn,
     // so the first NB mod NW wavefronts have one more; they leave K^T to the others)
     constexpr int KTW = NB % F::NW;
@@ -740,8 +741,8 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             // wavefront 4 + b inverts block b: lane l holds rows 4q .. 4q + 3 (q = l mod 4) of
             // column j = l / 4, so a column is a DPP quad.  Step s: x_s from lane s / 4 of the
             // quad, then x_r -= A[r][s] x_s for the lane's four rows (A[r][s] = 0 for r <= s,
-            // so no lane needs a mask): 15 steps of one broadcast and four FMAs.  Then every
-            // thread builds its share of K^T (the inverting wavefronts after their blocks)
+            // so no lane needs a mask): 15 steps of one broadcast and four FMAs.  The other
+            // wavefronts build K^T meanwhile
             if (wave >= 4 && wave < 4 + NR) {
                 const int bb = wave - 4, j = lane >> 2, q = lane & 3;
                 float x[4];
@@ -760,8 +761,11 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sm.td[bb][4 * q + i][j] = f16(x[i]);
             }
-            if (wave == 1 && c + 1 < nchunks) gates(c + 1);  // its inputs came with the prefetch
-            for (int idx = tid; idx < D * (C / 8); idx += NT) {
+            if (wave == GW && c + 1 < nchunks) gates(c + 1);  // its inputs came with the prefetch
+            // K^T by the wavefronts that invert nothing (0 .. 3 and 4 + NR ..)
+            const int kb = wave < 4 ? tid : tid - 64 * NR;
+            for (int idx = kb; (wave < 4 || wave >= 4 + NR) && idx < D * (C / 8);
+                 idx += NT - 64 * NR) {
                 const int i = idx % D, s8 = idx / D, ki = kperm(i);
                 f16x8 x;  // stored positions 8 s8 .. 8 s8 + 7 of row i of K^T
 #pragma unroll
@@ -789,7 +793,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                     for (int r = 0; r < 16; ++r) sm.td[lg][r][li] = f16(x[r]);
                 }
             } else {
-                if (wave == 1 && c + 1 < nchunks) gates(c + 1);  // its inputs came with the prefetch
+                if (wave == GW && c + 1 < nchunks) gates(c + 1);  // its inputs came with the prefetch
                 for (int idx = tid - 64; idx < D * (C / 8); idx += NT - 64) {
                     const int i = idx % D, s8 = idx / D, ki = kperm(i);
                     f16x8 x;  // stored positions 8 s8 .. 8 s8 + 7 of row i of K^T

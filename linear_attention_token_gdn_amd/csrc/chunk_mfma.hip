@@ -693,16 +693,9 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                 gr[rr] = sm.gam[cb][16 * rt + 4 * lg + rr];
                 br[rr] = sm.bet[cb][16 * rt + 4 * lg + rr];
             }
-#pragma unroll
-            for (int st = 0; st < NR; ++st) {
-                if (st > rt) break;
-                if (TRANS && (st & 1) != par) continue;
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int kk = 0; kk < F::KD; ++kk)
-                    acc = mma_k32(af[kk],
-                                  *reinterpret_cast<const f16x8 *>(&sm.k[16 * st + li][32 * kk + 8 * lg]),
-                                  acc);
+            // the decayed, scaled tile (rt, st) into LDS: P (isq), else -A off the diagonal and
+            // A on it (fp32, transposed)
+            auto put_tile = [&](int st, const f32x4 &acc) {
                 const int s = 16 * st + li;
                 const float gs = sm.gam[cb][s];
 #pragma unroll
@@ -719,6 +712,32 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                             sm.an[r][s] = f16(-av);
                     }
                 }
+            };
+            if constexpr (TRANS) {
+                // the job's tiles st = par and par + 2 (those <= rt), both products issued before
+                // either tile is stored (a tile past rt is computed on row NR - 1 and dropped)
+                const int st0 = par, st1 = par + 2;
+                const int k0 = min(st0, NR - 1), k1 = min(st1, NR - 1);
+                f32x4 a0 = zero4(), a1 = zero4();
+#pragma unroll
+                for (int kk = 0; kk < F::KD; ++kk) {
+                    a0 = mma_k32(af[kk], *reinterpret_cast<const f16x8 *>(&sm.k[16 * k0 + li][32 * kk + 8 * lg]), a0);
+                    a1 = mma_k32(af[kk], *reinterpret_cast<const f16x8 *>(&sm.k[16 * k1 + li][32 * kk + 8 * lg]), a1);
+                }
+                if (st0 <= rt) put_tile(st0, a0);
+                if (st1 <= rt) put_tile(st1, a1);
+                continue;
+            }
+#pragma unroll
+            for (int st = 0; st < NR; ++st) {
+                if (st > rt) break;
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int kk = 0; kk < F::KD; ++kk)
+                    acc = mma_k32(af[kk],
+                                  *reinterpret_cast<const f16x8 *>(&sm.k[16 * st + li][32 * kk + 8 * lg]),
+                                  acc);
+                put_tile(st, acc);
             }
             if (isq && rt + 1 < NR) {  // the tile right of the diagonal is read by P Delta
 #pragma unroll

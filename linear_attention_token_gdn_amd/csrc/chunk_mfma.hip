@@ -903,6 +903,16 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             };
             rprod();
             if (wave < NR) {
+                // the blocks' A operands, loaded before the chain starts
+                f16x4 anb[NB], tdb[NR];
+#pragma unroll
+                for (int a = 0; a < NR; ++a) {
+                    tdb[a] = *reinterpret_cast<const f16x4 *>(&sm.td[a][li][4 * lg]);
+#pragma unroll
+                    for (int cb2 = 0; cb2 < a; ++cb2)
+                        anb[a * (a - 1) / 2 + cb2] =
+                            *reinterpret_cast<const f16x4 *>(&sm.an[16 * a + li][16 * cb2 + 4 * lg]);
+                }
                 f16x4 X[NR];  // as the fp16 operands (and the stored values) they become
 #pragma unroll
                 for (int a = 0; a < NR; ++a) {
@@ -910,11 +920,8 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) yx[rr] = (a == wave && 4 * lg + rr == li) ? 1.f : 0.f;
 #pragma unroll
-                    for (int cb2 = 0; cb2 < a; ++cb2)
-                        yx = mma_k16(*reinterpret_cast<const f16x4 *>(&sm.an[16 * a + li][16 * cb2 + 4 * lg]),
-                                     X[cb2], yx);
-                    X[a] = to_f16x4(mma_k16(*reinterpret_cast<const f16x4 *>(&sm.td[a][li][4 * lg]),
-                                            to_f16x4(yx), zero4()));
+                    for (int cb2 = 0; cb2 < a; ++cb2) yx = mma_k16(anb[a * (a - 1) / 2 + cb2], X[cb2], yx);
+                    X[a] = to_f16x4(mma_k16(tdb[a], to_f16x4(yx), zero4()));
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) tmrow[16 * a + 4 * lg + rr][16 * wave + li] = X[a][rr];
                 }

@@ -288,9 +288,12 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     // (kOutTm: it has the fewest P tiles in stage 1; else it inverts one diagonal block in
     // stage 2, the shortest job there), 1 with 4 (wavefront 0 inverts in stage 2)
     constexpr int GW = TMR || F::NW == 8 ? F::NW - 1 : 1;
-    // kOutTm: the wavefronts w >= KTW build K^T in stage 1 (the P tiles are dealt out in turn,
-    // so the first NB mod NW wavefronts have one more; they leave K^T to the others)
-    constexpr int KTW = NB % F::NW;
+    // kOutTm stage 1: the P tiles are dealt out in turn, so the first NB mod NW wavefronts have
+    // one more; with NB = 10 tiles over 8 wavefronts (C = 64, D = 128: PAIRP) wavefronts 6
+    // and 7 take two tiles of row 3 each on one Q operand instead.  K^T is built by the
+    // wavefronts w in [KTW, KTE), those with one tile.
+    constexpr bool PAIRP = NB == 10 && F::NW == 8;
+    constexpr int KTW = PAIRP ? 0 : NB % F::NW, KTE = PAIRP ? 6 : F::NW;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     Smem<D, C> &sm = *reinterpret_cast<Smem<D, C> *>(smem_raw);
 
@@ -540,6 +543,10 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             settle(pg);  // the next chunk's gate inputs (loaded by wavefront GW only)
             settle(pb);
             if (wave == GW && c + 1 < nchunks) gates(c + 1);  // its inputs came with the prefetch
+            // (lane offsets made opaque: the LDS addresses of this stage and stage 4 are formed
+            // here, not kept in registers across the chunk loop)
+            const int li = opaque(lane & 15), lg = opaque(lane >> 4);
+            const int col = 16 * wave + li;
             f32x4 yv[NR];
             float vmax = 0.f;
 #pragma unroll
@@ -589,14 +596,8 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                     R[rt][rr] = sig * yv[rt][rr] - sm.bg[cb][r] * ks[rr];
                 }
             }
-            for (int j = wave; j < NB; j += F::NW) {  // P tile (rt, st), st <= rt
-                const int rt = tri_row(j), st = j - rt * (rt + 1) / 2;
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int kk = 0; kk < F::KD; ++kk)
-                    acc = mma_k32(*reinterpret_cast<const f16x8 *>(&sm.q[16 * rt + li][32 * kk + 8 * lg]),
-                                  *reinterpret_cast<const f16x8 *>(&sm.k[16 * st + li][32 * kk + 8 * lg]),
-                                  acc);
+            // P tile (rt, st), st <= rt: the decayed, masked fp16 values into LDS
+            auto pput = [&](int rt, int st, const f32x4 &acc) {
                 const int s = 16 * st + li;
                 const float gs = sm.gam[cb][s];
 #pragma unroll
@@ -607,8 +608,45 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                     // the tile right of the diagonal is read by P Delta
                     if (st == rt && rt + 1 < NR) sm.p[r][kperm(s + 16)] = f16(0.f);
                 }
+            };
+            if constexpr (PAIRP) {
+                // wavefront w < 6 takes tile w (triangle order); wavefronts 6 and 7 the pairs
+                // (3, 0..1) and (3, 2..3), one Q operand feeding both products
+                if (wave < 6) {
+                    const int rt = tri_row(wave), st = wave - rt * (rt + 1) / 2;
+                    f32x4 acc = zero4();
+#pragma unroll
+                    for (int kk = 0; kk < F::KD; ++kk)
+                        acc = mma_k32(*reinterpret_cast<const f16x8 *>(&sm.q[16 * rt + li][32 * kk + 8 * lg]),
+                                      *reinterpret_cast<const f16x8 *>(&sm.k[16 * st + li][32 * kk + 8 * lg]),
+                                      acc);
+                    pput(rt, st, acc);
+                } else {
+                    const int st = 2 * (wave - 6);
+                    f32x4 a0 = zero4(), a1 = zero4();
+#pragma unroll
+                    for (int kk = 0; kk < F::KD; ++kk) {
+                        const f16x8 aq = *reinterpret_cast<const f16x8 *>(&sm.q[48 + li][32 * kk + 8 * lg]);
+                        a0 = mma_k32(aq, *reinterpret_cast<const f16x8 *>(&sm.k[16 * st + li][32 * kk + 8 * lg]), a0);
+                        a1 = mma_k32(aq, *reinterpret_cast<const f16x8 *>(&sm.k[16 * st + 16 + li][32 * kk + 8 * lg]), a1);
+                    }
+                    pput(3, st, a0);
+                    pput(3, st + 1, a1);
+                }
+            } else {
+                for (int j = wave; j < NB; j += F::NW) {
+                    const int rt = tri_row(j), st = j - rt * (rt + 1) / 2;
+                    f32x4 acc = zero4();
+#pragma unroll
+                    for (int kk = 0; kk < F::KD; ++kk)
+                        acc = mma_k32(*reinterpret_cast<const f16x8 *>(&sm.q[16 * rt + li][32 * kk + 8 * lg]),
+                                      *reinterpret_cast<const f16x8 *>(&sm.k[16 * st + li][32 * kk + 8 * lg]),
+                                      acc);
+                    pput(rt, st, acc);
+                }
             }
-            for (int idx = tid - 64 * KTW; idx >= 0 && idx < D * (C / 8); idx += NT - 64 * KTW) {
+            for (int idx = tid - 64 * KTW; idx >= 0 && idx < D * (C / 8) && wave < KTE;
+                 idx += NT - 64 * KTW - 64 * (F::NW - KTE)) {
                 const int i = idx % D, s8 = idx / D, ki = kperm(i);
                 f16x8 x;  // stored positions 8 s8 .. 8 s8 + 7 of row i of K^T
 #pragma unroll

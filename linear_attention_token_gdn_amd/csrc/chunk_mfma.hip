@@ -350,9 +350,9 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     }
 
     // ---- raw inputs of coming chunks, prefetched into registers (rows past the end read as 0):
-    //      q one chunk ahead; k, v and the gate inputs two chunks ahead in kOut (staged in LDS a
-    //      chunk earlier than q, see stage 4), one in kTrans (staged in stage 0: its two states
-    //      leave no registers to stage them during stage 4)
+    //      q one chunk ahead; k, v and the gate inputs two chunks ahead in kOut, kOutTm and
+    //      kTransTm (staged in LDS a chunk earlier than q, see stage 4), one in kTrans (staged
+    //      in stage 0: its two states leave no registers to stage them during stage 4)
     u16x8 pq[F::NQ], pk[F::NQ], pv[F::NQ];
     u16x8 ptm[TMR ? NTP : 1];  // kOutTm: the chunk's Tm, one chunk ahead (with q)
     bf16_t pg = 0, pb = 0;
@@ -496,20 +496,22 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     if (nchunks > 0) {
         prefetch_q(0);
         prefetch_kv(0);
-        if constexpr (!TRANS) with_norm(put_kv);  // chunk 0's k and v (LDS is not in use yet)
+        if constexpr (!TRANS || TMW) with_norm(put_kv);  // chunk 0's k, v (LDS is not in use yet)
         if (wave == GW) gates(0);
-        if constexpr (!TRANS) prefetch_kv(1);
+        if constexpr (!TRANS || TMW) prefetch_kv(1);
     }
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = c * C, cb = c & 1;
         lds_barrier();  // the previous chunk is done with every LDS buffer
-        if constexpr (TRANS) {
+        if constexpr (TMW) {
+            // ---- stage 0 of kTransTm: the previous chunk's Tm out of LDS (this chunk's k and v
+            //      were staged in stage 4 of the previous one; stage 3 next writes Tm two barriers
+            //      from here, so this stage needs none of its own)
+            if (c > 0) store_tm(c - 1);
+        } else if constexpr (TRANS) {
             // ---- stage 0 of the transition: this chunk's k and v in LDS, prefetch of the next
-            //      (kTransTm: the previous chunk's Tm out of LDS)
             with_norm(put_kv);
             if (c + 1 < nchunks) prefetch_kv(c + 1);
-            if constexpr (TMW)
-                if (c > 0) store_tm(c - 1);
             lds_barrier();
         } else {
             // ---- stage 0: stage this chunk's q in LDS, store the previous chunk's output, prefetch
@@ -966,8 +968,12 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             }
             lds_barrier();
 
-            // ---- kTransTm stage 4: Delta_N = Tm R_N, Delta_M = Tm R_M, then N and M through
-            //      K^T diag(e^(gamma_last - gamma)) as in the other transition
+            // ---- kTransTm stage 4: the next chunk's k and v into LDS (nothing here reads them)
+            //      and the prefetch of the chunk after it; Delta_N = Tm R_N, Delta_M = Tm R_M,
+            //      then N and M through K^T diag(e^(gamma_last - gamma)) as in the other
+            //      transition
+            with_norm(put_kv);
+            prefetch_kv(c + 2);
             f32x4 DN[NR], DM[NR];
 #pragma unroll
             for (int a = 0; a < NR; ++a) {

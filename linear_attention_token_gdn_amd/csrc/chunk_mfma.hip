@@ -478,9 +478,20 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     // stored, in the -A array that kOutTm leaves unused.
     using SmemT = Smem<D, C>;
     f16(*tmrow)[F::PA] = reinterpret_cast<f16(*)[F::PA]>(&sm.ost[0][0]);
-    f16 *tmf = &sm.an[0][0];
-    static_assert(sizeof(sm.ost) >= sizeof(f16) * C * F::PA && sizeof(sm.an) >= 2 * TMH &&
-                      offsetof(SmemT, ost) % 16 == 0 && offsetof(SmemT, an) % 16 == 0,
+    auto tmfb = [&](int buf) -> f16 * {  // kOutTm: two buffers, by chunk parity
+        return buf ? &sm.wn[0][0] : &sm.an[0][0];
+    };
+    auto put_tm = [&](int buf) {
+        f16 *dst = tmfb(buf);
+#pragma unroll
+        for (int n = 0; n < NTP; ++n) {
+            const int idx = tid + n * NT;
+            if (idx < NB * 32) *reinterpret_cast<u16x8 *>(dst + idx * 8) = ptm[n];
+        }
+    };
+    static_assert(sizeof(sm.ost) >= sizeof(f16) * C * F::PA && sizeof(sm.an) >= 2 * TMH && sizeof(sm.wn) >= 2 * TMH &&
+                      offsetof(SmemT, ost) % 16 == 0 && offsetof(SmemT, an) % 16 == 0 &&
+                      offsetof(SmemT, wn) % 16 == 0,
                   "Tm staging");
     auto store_tm = [&](int cidx) {  // 16-byte pieces: the fragments of lanes 2p', 2p' + 1
         uint16_t *dst = tm + tm_slot(cidx);
@@ -497,8 +508,14 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         prefetch_q(0);
         prefetch_kv(0);
         if constexpr (!TRANS || TMW) with_norm(put_kv);  // chunk 0's k, v (LDS is not in use yet)
+        if constexpr (TMR) {  // and q, Tm
+            with_norm(put_q);
+            put_tm(0);
+        }
         if (wave == GW) gates(0);
         if constexpr (!TRANS || TMW) prefetch_kv(1);
+        if constexpr (TMR)
+            if (nchunks > 1) prefetch_q(1);
     }
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = c * C, cb = c & 1;
@@ -516,14 +533,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         } else {
             // ---- stage 0: stage this chunk's q in LDS, store the previous chunk's output, prefetch
             //      the next q (this chunk's k and v were staged during the previous chunk)
-            with_norm(put_q);
-            if constexpr (TMR) {
-#pragma unroll
-                for (int n = 0; n < NTP; ++n) {
-                    const int idx = tid + n * NT;
-                    if (idx < NB * 32) *reinterpret_cast<u16x8 *>(tmf + idx * 8) = ptm[n];
-                }
-            }
+            if constexpr (!TMR) with_norm(put_q);  // (kOutTm: staged in stage 4 of the last chunk)
             if (c > 0) {
                 const int tp = t0 - C;  // the previous chunk is always a full one
 #pragma unroll
@@ -533,8 +543,12 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                     store4<TO>(o + ((base + tp + r) * Hv + hv) * D + cc * 4, x);
                 }
             }
-            if (c + 1 < nchunks) prefetch_q(c + 1);
-            lds_barrier();
+            if constexpr (!TMR) {
+                if (c + 1 < nchunks) prefetch_q(c + 1);
+                lds_barrier();
+            }
+            // (kOutTm: no barrier -- the stores only read the output staging, which stage 4
+            // writes two barriers on)
         }
 
         if constexpr (TMR) {
@@ -661,6 +675,10 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             //      the prefetch of the chunk after it; Delta = Tm R, O += P Delta, next state
             with_norm(put_kv);
             prefetch_kv(c + 2);
+            with_norm(put_q);       // q and Tm of the next chunk: stage 1 was the last reader of
+            put_tm((c + 1) & 1);    // this chunk's q; its Tm is in the other buffer
+            if (c + 2 < nchunks) prefetch_q(c + 2);
+            const f16 *tmf = tmfb(c & 1);
             f32x4 Dl[NR];
 #pragma unroll
             for (int a = 0; a < NR; ++a) {

@@ -53,7 +53,8 @@
 // output pass (kOutTm) reads it back.  Neither pass then forms U or W: since U - W S =
 // Tm (diag(beta) V - diag(beta e^gamma) K S), the state products run on K (already in LDS)
 // and Delta = Tm R is one dense product; the output pass also skips K K^T, the diagonal-block
-// inverses and the substitution, and needs 3 barriers per chunk instead of 5.
+// inverses and the substitution, and needs 2 barriers per chunk instead of 5 (both passes
+// stage the next chunk's inputs in stage 4, so neither needs a barrier after stage 0).
 #include <algorithm>
 #include <stddef.h>
 #include <stdlib.h>

@@ -106,8 +106,10 @@ const char *gdn_status_string(gdn_status_t status);
  * WY/UT transform) as fp16, its (chunk/16)(chunk/16 + 1)/2 lower 16 x 16 blocks of 512 B
  * (5 KiB at chunk 64), in ceil(rows / chunk) + B slots per value head (rows = B T, or T for
  * packed sequences): the transition pass stores it and the output pass reads it instead of
- * forming it again (320 MiB for 262,144 tokens x 16 heads).  With the environment variable
- * GDN_SEG_NO_TM=1 both passes form it and the size is the maps' alone.
+ * forming it again (320 MiB for 262,144 tokens x 16 heads).  Where those records would exceed
+ * 2 GiB (beyond about 1.7 million tokens x 16 heads at chunk 64), or with the environment variable
+ * GDN_SEG_NO_TM=1, both passes form it and the size is the maps' alone: the segmented plan's
+ * workspace stays bounded for any T.
  */
 size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int chunk,
                                     gdn_dtype_t in_dtype);

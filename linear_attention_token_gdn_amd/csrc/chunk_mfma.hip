@@ -1375,11 +1375,15 @@ int seg_tm_slots(const PrefillArgs &a) {
     const long rows = a.cu != nullptr ? a.T : static_cast<long>(a.B) * a.T;
     return static_cast<int>((rows + a.chunk - 1) / a.chunk + a.B);
 }
+// At most this many bytes of records (the split plan's bound on its own): longer inputs form
+// Tm in both passes, so the workspace stays bounded for any T.
+constexpr size_t kSegTmMaxBytes = size_t(2) << 30;
 size_t seg_tm_bytes(const PrefillArgs &a) {
     const char *env = getenv("GDN_SEG_NO_TM");  // A/B switch: form Tm in both passes
     if (env != nullptr && atoi(env) != 0) return 0;
     const size_t nr = a.chunk / 16;
-    return static_cast<size_t>(a.Hv) * seg_tm_slots(a) * (nr * (nr + 1) / 2) * 512;
+    const size_t bytes = static_cast<size_t>(a.Hv) * seg_tm_slots(a) * (nr * (nr + 1) / 2) * 512;
+    return bytes <= kSegTmMaxBytes ? bytes : 0;
 }
 
 template <int D, int C, typename TO, int MODE>

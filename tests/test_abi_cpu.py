@@ -70,6 +70,10 @@ def test_workspace_of_the_segmented_plan(lib, monkeypatch):
         monkeypatch.setenv("GDN_SEG_NO_TM", "1")
         assert gdn.gdn_chunk_fwd_workspace_size(B, T, H, H, 128, 128, 64, gdn.GDN_BF16) == maps
         monkeypatch.delenv("GDN_SEG_NO_TM")
+    # records beyond 2 GiB (16 heads x 8 M tokens: 10 GiB): the maps alone, both passes form Tm
+    maps = (2 * 15 + 16) * 16 * D2
+    assert _tm_records(1, 1 << 23, 16, 64) > 2 << 30
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 1 << 23, 16, 16, 128, 128, 64, gdn.GDN_BF16) == maps
     # the largest maps: 256 units at d = 128 fit the allocation-free entry point's scratch (it
     # runs without the records when they do not fit beside them)
     monkeypatch.setenv("GDN_SEG_NO_TM", "1")

@@ -23,7 +23,9 @@ from parity import check
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-PLANS = ["fused", "split", "segmented"]
+# "segmented_formed": the segmented plan with GDN_SEG_NO_TM, both passes forming every chunk's
+# (I + A)^-1 instead of the output pass reading the transition pass's records
+PLANS = ["fused", "split", "segmented", "segmented_formed"]
 ALL = 1 | 2 | 4  # GDN_QK_L2NORM | GDN_BETA_LOGIT | GDN_G_LOGIT
 
 
@@ -38,9 +40,11 @@ def _gpu():
 def use_plan(monkeypatch, plan):
     """Pin the prefill plan; the segmented one with one chunk per segment, so that every chunk
     boundary is a segment boundary (transition, combine and entry state all exercised)."""
-    monkeypatch.setenv("GDN_FORCE_VARIANT", plan)
-    if plan == "segmented":
+    monkeypatch.setenv("GDN_FORCE_VARIANT", plan.replace("_formed", ""))
+    if plan.startswith("segmented"):
         monkeypatch.setenv("GDN_SEG_CHUNKS", "1")
+    if plan == "segmented_formed":
+        monkeypatch.setenv("GDN_SEG_NO_TM", "1")
 
 
 def gdn_mod():

@@ -476,7 +476,8 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     // Tm in LDS.  kTransTm: as rows (row r, column s at tmrow[r][s]), written by the panel
     // solves of stage 3 into the output staging area that kTrans leaves unused, and stored as
     // A-operand fragments by store_tm after the next barrier.  kOutTm: the fragments as
-    // stored, in the -A array that kOutTm leaves unused.
+    // stored, double-buffered by chunk parity in the -A and -W arrays that kOutTm leaves
+    // unused (tmfb).
     using SmemT = Smem<D, C>;
     f16(*tmrow)[F::PA] = reinterpret_cast<f16(*)[F::PA]>(&sm.ost[0][0]);
     auto tmfb = [&](int buf) -> f16 * {  // kOutTm: two buffers, by chunk parity
@@ -533,7 +534,8 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             lds_barrier();
         } else {
             // ---- stage 0: stage this chunk's q in LDS, store the previous chunk's output, prefetch
-            //      the next q (this chunk's k and v were staged during the previous chunk)
+            //      the next q (this chunk's k and v were staged during the previous chunk; kOutTm:
+            //      q and Tm too, so this stage only stores)
             if constexpr (!TMR) with_norm(put_q);  // (kOutTm: staged in stage 4 of the last chunk)
             if (c > 0) {
                 const int tp = t0 - C;  // the previous chunk is always a full one
@@ -549,7 +551,7 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                 lds_barrier();
             }
             // (kOutTm: no barrier -- the stores only read the output staging, which stage 4
-            // writes two barriers on)
+            // writes one barrier on, after every wavefront's LDS reads here have completed)
         }
 
         if constexpr (TMR) {

@@ -294,6 +294,8 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     // and 7 take two tiles of row 3 each on one Q operand instead.  K^T is built by the
     // wavefronts w in [KTW, KTE), those with one tile.
     constexpr bool PAIRP = NB == 10 && F::NW == 8;
+    // kTransTm with C = 64 and 8 wavefronts: K^T and the gates in stage 1 (see there)
+    constexpr bool KT1 = TMW && NR == 4 && F::NW == 8;
     constexpr int KTW = PAIRP ? 0 : NB % F::NW, KTE = PAIRP ? 6 : F::NW;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     Smem<D, C> &sm = *reinterpret_cast<Smem<D, C> *>(smem_raw);
@@ -806,6 +808,24 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                     sm.p[16 * rt + 4 * lg + rr][kperm(16 * (rt + 1) + li)] = f16(0.f);
             }
         }
+        if constexpr (KT1) {
+            // kTransTm, C = 64, 8 wavefronts: the wavefronts with at most one K K^T tile here
+            // (0, 1, 5, 6 and 7) build K^T, and 7 forms the next chunk's gates, so that stage 2
+            // holds only the diagonal-block inverses
+            settle(pg);
+            settle(pb);
+            if (wave == GW && c + 1 < nchunks) gates(c + 1);  // its inputs came with the prefetch
+            const int kw = wave < 2 ? wave : wave - 3;  // 0, 1, 2, 3, 4 for waves 0, 1, 5, 6, 7
+            if (wave < 2 || wave >= 5) {
+                for (int idx = 64 * kw + lane; idx < D * (C / 8); idx += 320) {
+                    const int i = idx % D, s8 = idx / D, ki = kperm(i);
+                    f16x8 x;  // stored positions 8 s8 .. 8 s8 + 7 of row i of K^T
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = sm.k[kunperm(s8 * 8 + e)][ki];
+                    *reinterpret_cast<f16x8 *>(&sm.kt[i][s8 * 8]) = x;
+                }
+            }
+        }
         }
         lds_barrier();
 
@@ -841,10 +861,10 @@ chunk_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sm.td[bb][4 * q + i][j] = f16(x[i]);
             }
-            if (wave == GW && c + 1 < nchunks) gates(c + 1);  // its inputs came with the prefetch
-            // K^T by the wavefronts that invert nothing (0 .. 3 and 4 + NR ..)
+            if (!KT1 && wave == GW && c + 1 < nchunks) gates(c + 1);  // its inputs came with the prefetch
+            // K^T by the wavefronts that invert nothing (0 .. 3 and 4 + NR ..; KT1: in stage 1)
             const int kb = wave < 4 ? tid : tid - 64 * NR;
-            for (int idx = kb; (wave < 4 || wave >= 4 + NR) && idx < D * (C / 8);
+            for (int idx = kb; !KT1 && (wave < 4 || wave >= 4 + NR) && idx < D * (C / 8);
                  idx += NT - 64 * NR) {
                 const int i = idx % D, s8 = idx / D, ki = kperm(i);
                 f16x8 x;  // stored positions 8 s8 .. 8 s8 + 7 of row i of K^T
